@@ -1,0 +1,262 @@
+"""Seeded synthetic inputs for the MoE-layer path.
+
+Draws activations, router weights, the optional Zipf router bias and expert
+weights, and stores expert weights in the library's layouts (q4_1, NVFP4,
+bf16).  It holds no forward arithmetic; the oracle and the HIP library both
+read the arrays it returns and neither imports the other.
+
+Recipe (all draws are SplitMix64 streams keyed by (seed, tag, a, b), normals by
+Box-Muller; see synth.c):
+  * activations  x  ~ bf16(fp32(N(0, 1)))                  key (xseed, X, 0, 0)
+  * router       Wr ~ bf16(fp32(N(0, 0.02)))  [E][d]        key (seed, ROUTER, 0, 0)
+  * router bias  b[e] = fp32(-s * ln(1 + pi(e))), pi a random permutation of
+                 the expert ids (Zipf(s) over a random ranking)  key (seed, BIAS, 0, 0)
+  * expert e, matrix j (0 gate [f][d], 1 up [f][d], 2 down [d][f]):
+                 fp32(N(0, 0.02)), then the format's encoder   key (seed, EXPERT, e, j)
+    the shared expert uses e = SHARED_ID.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass, field
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "synth.c")
+_LIB = os.path.join(_HERE, "libsynth.so")
+
+TAG_X, TAG_ROUTER, TAG_BIAS, TAG_EXPERT = 1, 2, 3, 4
+SHARED_ID = 1_000_000
+FMT_CODE = {"bf16": 0, "q4_1": 1, "nvfp4": 2}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile synth.c into libsynth.so (gcc, OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared", "-o", _LIB + ".tmp", _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        u64, i64, dbl, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+        L.synth_key.restype = u64
+        L.synth_key.argtypes = [u64, u64, u64, u64]
+        L.synth_u64.restype = u64
+        L.synth_u64.argtypes = [u64, u64]
+        L.synth_normal_f32.argtypes = [u64, dbl, vp, i64]
+        L.synth_normal_bf16.argtypes = [u64, dbl, vp, i64]
+        L.synth_permutation.argtypes = [u64, vp, ctypes.c_int32]
+        L.synth_q4_1_encode.argtypes = [vp, i64, i64, vp, vp]
+        L.synth_nvfp4_encode.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.synth_f32_to_bf16.argtypes = [vp, vp, i64]
+        L.synth_matrix.argtypes = [u64, dbl, ctypes.c_int, i64, i64, vp, vp, vp]
+        L.synth_f64_to_f16.restype = ctypes.c_uint16
+        L.synth_f64_to_f16.argtypes = [dbl]
+        L.synth_f64_to_e4m3_sat.restype = ctypes.c_uint8
+        L.synth_f64_to_e4m3_sat.argtypes = [dbl]
+        L.synth_f64_to_e2m1.restype = ctypes.c_uint8
+        L.synth_f64_to_e2m1.argtypes = [dbl]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def key(seed: int, tag: int, a: int = 0, b: int = 0) -> int:
+    return int(lib().synth_key(seed, tag, a, b))
+
+
+# ---- raw draws --------------------------------------------------------------
+
+def normal_f32(k: int, sigma: float, n: int) -> np.ndarray:
+    out = np.empty(n, np.float32)
+    lib().synth_normal_f32(k, sigma, _p(out), n)
+    return out
+
+
+def normal_bf16(k: int, sigma: float, n: int) -> np.ndarray:
+    out = np.empty(n, np.uint16)
+    lib().synth_normal_bf16(k, sigma, _p(out), n)
+    return out
+
+
+def permutation(k: int, n: int) -> np.ndarray:
+    out = np.empty(n, np.int32)
+    lib().synth_permutation(k, _p(out), n)
+    return out
+
+
+# ---- encoders (arrays in, packed arrays out) ------------------------------------
+
+def encode_q4_1(w: np.ndarray):
+    """w: fp32 [rows][cols] -> (codes u8 [rows][cols/2], dm fp16-bits u16 [rows][cols/32][2])."""
+    w = np.ascontiguousarray(w, np.float32)
+    rows, cols = w.shape
+    assert cols % 32 == 0
+    codes = np.empty((rows, cols // 2), np.uint8)
+    dm = np.empty((rows, cols // 32, 2), np.uint16)
+    lib().synth_q4_1_encode(_p(w), rows, cols, _p(codes), _p(dm))
+    return codes, dm
+
+
+def encode_nvfp4(w: np.ndarray):
+    """w: fp32 [rows][cols] -> (codes u8 [rows][cols/2], scales u8 [rows][cols/16], ts fp32)."""
+    w = np.ascontiguousarray(w, np.float32)
+    rows, cols = w.shape
+    assert cols % 16 == 0
+    codes = np.empty((rows, cols // 2), np.uint8)
+    scales = np.empty((rows, cols // 16), np.uint8)
+    ts = np.zeros(1, np.float32)
+    lib().synth_nvfp4_encode(_p(w), rows, cols, _p(codes), _p(scales), _p(ts))
+    return codes, scales, float(ts[0])
+
+
+def encode_bf16(w: np.ndarray) -> np.ndarray:
+    w = np.ascontiguousarray(w, np.float32)
+    out = np.empty(w.shape, np.uint16)
+    lib().synth_f32_to_bf16(_p(w), _p(out), w.size)
+    return out
+
+
+# ---- layer containers ---------------------------------------------------------
+
+@dataclass
+class QMat:
+    """A stored matrix set [n][rows][cols] in one format.
+
+    codes : q4_1/nvfp4 u8 [n][rows][cols/2]; bf16 u16 [n][rows][cols]
+    scales: q4_1 u16 (fp16 bits) [n][rows][cols/32][2] = {d, m};
+            nvfp4 u8 (E4M3) [n][rows][cols/16]; bf16 None
+    tensor_scale: nvfp4 fp32 [n]; else None
+    """
+    fmt: str
+    n: int
+    rows: int
+    cols: int
+    codes: np.ndarray
+    scales: np.ndarray | None = None
+    tensor_scale: np.ndarray | None = None
+
+    def nbytes(self, count: int = 1) -> int:
+        """Stored bytes of `count` matrices of this set."""
+        per = self.rows * self.cols
+        if self.fmt == "bf16":
+            return count * per * 2
+        if self.fmt == "q4_1":
+            return count * (per // 2 + per // 32 * 4)
+        return count * (per // 2 + per // 16 + 4)
+
+
+def alloc_qmat(fmt: str, n: int, rows: int, cols: int) -> QMat:
+    if fmt == "bf16":
+        return QMat(fmt, n, rows, cols, np.empty((n, rows, cols), np.uint16))
+    if fmt == "q4_1":
+        return QMat(fmt, n, rows, cols, np.empty((n, rows, cols // 2), np.uint8),
+                    np.empty((n, rows, cols // 32, 2), np.uint16))
+    if fmt == "nvfp4":
+        return QMat(fmt, n, rows, cols, np.empty((n, rows, cols // 2), np.uint8),
+                    np.empty((n, rows, cols // 16), np.uint8), np.zeros(n, np.float32))
+    raise ValueError(fmt)
+
+
+def fill_matrix(q: QMat, i: int, k: int, sigma: float) -> None:
+    """Draw matrix i of q from stream k (N(0, sigma)) and encode it in place."""
+    codes = q.codes[i]
+    scales = q.scales[i] if q.scales is not None else None
+    ts = q.tensor_scale[i:i + 1] if q.tensor_scale is not None else None
+    lib().synth_matrix(k, sigma, FMT_CODE[q.fmt], q.rows, q.cols, _p(codes),
+                       _p(scales) if scales is not None else None,
+                       _p(ts) if ts is not None else None)
+
+
+@dataclass
+class Layer:
+    fmt: str
+    d: int
+    E: int
+    k: int
+    f: int
+    n_shared: int
+    shared_scale: float
+    renorm: int
+    router_w: np.ndarray                 # u16 bf16 bits [E][d]
+    router_b: np.ndarray | None          # fp32 [E] or None
+    gate: QMat
+    up: QMat
+    down: QMat
+    sh_gate: QMat | None = None
+    sh_up: QMat | None = None
+    sh_down: QMat | None = None
+    meta: dict = field(default_factory=dict)
+
+    def expert_bytes(self) -> int:
+        return self.gate.nbytes() + self.up.nbytes() + self.down.nbytes()
+
+
+def make_layer(seed: int = 0, fmt: str = "q4_1", E: int = 256, d: int = 2048, f: int = 512, k: int = 6,
+               n_shared: int = 1, shared_scale: float = 1.0, zipf: float | None = None, renorm: int = 1,
+               sigma: float = 0.02, router_sigma: float = 0.02) -> Layer:
+    """One MoE layer drawn from `seed` (see the module recipe)."""
+    router_w = normal_bf16(key(seed, TAG_ROUTER), router_sigma, E * d).reshape(E, d)
+    router_b = None
+    if zipf is not None:
+        pi = permutation(key(seed, TAG_BIAS), E)
+        router_b = (-zipf * np.log1p(pi.astype(np.float64))).astype(np.float32)
+    gate, up, down = alloc_qmat(fmt, E, f, d), alloc_qmat(fmt, E, f, d), alloc_qmat(fmt, E, d, f)
+    for e in range(E):
+        fill_matrix(gate, e, key(seed, TAG_EXPERT, e, 0), sigma)
+        fill_matrix(up, e, key(seed, TAG_EXPERT, e, 1), sigma)
+        fill_matrix(down, e, key(seed, TAG_EXPERT, e, 2), sigma)
+    L = Layer(fmt, d, E, k, f, n_shared, shared_scale, renorm, router_w, router_b, gate, up, down,
+              meta=dict(seed=seed, zipf=zipf))
+    if n_shared:
+        L.sh_gate, L.sh_up, L.sh_down = alloc_qmat(fmt, 1, f, d), alloc_qmat(fmt, 1, f, d), alloc_qmat(fmt, 1, d, f)
+        fill_matrix(L.sh_gate, 0, key(seed, TAG_EXPERT, SHARED_ID, 0), sigma)
+        fill_matrix(L.sh_up, 0, key(seed, TAG_EXPERT, SHARED_ID, 1), sigma)
+        fill_matrix(L.sh_down, 0, key(seed, TAG_EXPERT, SHARED_ID, 2), sigma)
+    return L
+
+
+def make_x(T: int, d: int = 2048, xseed: int = 0, sigma: float = 1.0) -> np.ndarray:
+    """bf16 bits [T][d] of fp32(N(0, sigma))."""
+    return normal_bf16(key(xseed, TAG_X), sigma, T * d).reshape(T, d)
+
+
+def bf16_to_f32(b: np.ndarray) -> np.ndarray:
+    """bf16 bits -> fp32 values (bit placement; exact)."""
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ---- the five workloads -----------------------------------------------------------
+
+CONFIGS = {
+    # name: T, format, router skew, layers
+    "decode_t4_q4_1": dict(T=4, fmt="q4_1", zipf=None, layers=1),
+    "decode_t64_q4_1": dict(T=64, fmt="q4_1", zipf=None, layers=1),
+    "decode_t256_nvfp4_zipf1.1": dict(T=256, fmt="nvfp4", zipf=1.1, layers=1),
+    "prefill_t4096_bf16": dict(T=4096, fmt="bf16", zipf=None, layers=1),
+    "stack47_decode_t32_q4_1_zipf0.8": dict(T=32, fmt="q4_1", zipf=0.8, layers=47),
+}
+
+
+def make_workload(name: str, layers: int | None = None):
+    """(list of Layer, x) for a named workload.  Layer l of a stack is drawn
+    from seed l; activations from seed 0.  `layers` truncates a stack."""
+    c = CONFIGS[name]
+    nl = c["layers"] if layers is None else layers
+    Ls = [make_layer(seed=l, fmt=c["fmt"], zipf=c["zipf"]) for l in range(nl)]
+    return Ls, make_x(c["T"])
