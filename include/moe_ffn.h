@@ -1,0 +1,161 @@
+/*
+ * moe_ffn.h -- C ABI of the MI355X (gfx950) sparse mixture-of-experts layer.
+ *
+ * The operation is the MoE layer of the open-weight coding model reviewed on
+ * orcarouter.ai as "Recursive Flint 40B-A2.5B", section "The architecture is
+ * an argument about memory bandwidth": per MoE layer, 256 routed experts of
+ * which each token uses 6, plus one shared expert that every token uses, with
+ * 47 such layers in the model; the same section states that decoding is bound
+ * by moving weights from memory.  The 4-bit storage formats (q4_1 and NVFP4)
+ * and the 16-bit checkpoint are the artefacts listed in "What actually
+ * shipped".  The page does not give the expert width, the activation or the
+ * router form; this library computes, per token x (bf16, d_model wide):
+ *
+ *   logits = x Wr^T + b                     (bf16 operands, fp32 accumulate)
+ *   ids    = the top_k largest logits, ties to the lower expert id
+ *   w      = softmax over the chosen logits (renorm_topk = 1), or the chosen
+ *            entries of the softmax over all experts (renorm_topk = 0)
+ *   E_e(x) = Wd_e (silu(Wg_e x) * (Wu_e x))  (SwiGLU, silu(g) = g/(1+e^-g))
+ *   y      = sum_j w_j E_{ids_j}(x) + shared_scale * E_shared(x)   -> bf16
+ *
+ * and moe_stack_forward chains layers as a pre-norm residual stack:
+ *   r <- x;  for each layer: r <- r + bf16(layer(bf16(RMSNorm(r))));  x <- bf16(r)
+ * with RMSNorm(r) = r / sqrt(mean(r^2) + eps) (gain 1) and r kept in fp32.
+ *
+ * Conventions for every call:
+ *   - returns a moe_status; never aborts or throws; moe_last_error() gives a
+ *     thread-local message for the last non-OK status of the calling thread;
+ *   - every argument is checked on the host before any work is enqueued;
+ *   - all device memory (weights, activations, workspace, route outputs) is
+ *     owned by the caller; the library never allocates device memory, and the
+ *     weight arrays are borrowed by a layer handle and must outlive it;
+ *   - forward calls are asynchronous on the given HIP stream (a hipStream_t
+ *     passed as void*, NULL = the default stream); MOE_OK means enqueued, the
+ *     results are valid once the caller synchronises that stream; no call
+ *     synchronises the host and data-dependent sizes stay on the device, so a
+ *     forward can be captured in a HIP graph;
+ *   - a layer handle is immutable after create; concurrent forwards on one
+ *     handle are safe when each uses its own workspace and outputs.
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* a NULL/misaligned pointer, a bad size or shape, T > max_tokens */
+  MOE_ERR_UNSUPPORTED = 2, /* not a gfx950 device, or a shape/format this build has no kernels for */
+  MOE_ERR_WORKSPACE = 3,   /* workspace NULL, misaligned (256 B) or smaller than the size query returns */
+  MOE_ERR_HIP = 4          /* a HIP runtime call failed (no device, launch failure); message has its name */
+} moe_status;
+
+/* Storage format of the expert weights (routed and shared alike). */
+typedef enum {
+  MOE_W_BF16 = 0,  /* plain bf16, the 16-bit checkpoint ("What actually shipped", BF16 bullet) */
+  MOE_W_Q4_1 = 1,  /* q4_1 ("What actually shipped", Int4 GGUF bullet): blocks of 32 along a row,
+                      w = d*q + m, q unsigned 4-bit, d and m fp16 */
+  MOE_W_NVFP4 = 2  /* NVFP4 ("What actually shipped", NVFP4 GGUF bullet): blocks of 16 along a row,
+                      w = E2M1(c) * E4M3(s) * ts, one OCP E4M3FN scale s per block, fp32 ts per matrix */
+} moe_wfmt;
+
+/* Shape and options of one MoE layer.  This build has kernels for
+ * d_model = 2048 and d_expert = d_shared = 512 (the reviewed model's MoE
+ * layer shape); other widths return MOE_ERR_UNSUPPORTED. */
+typedef struct {
+  int32_t d_model;      /* hidden size: 2048 */
+  int32_t n_experts;    /* routed experts: multiple of 16, 16..256 (the model: 256) */
+  int32_t top_k;        /* experts chosen per token: 1..8, <= n_experts (the model: 6) */
+  int32_t d_expert;     /* routed expert width: 512 */
+  int32_t n_shared;     /* always-on shared experts: 0 or 1 (the model: 1) */
+  int32_t d_shared;     /* shared expert width: must equal d_expert */
+  float shared_scale;   /* weight of the shared expert's output (1.0) */
+  int32_t renorm_topk;  /* 1: chosen weights sum to 1; 0: plain softmax entries */
+  int32_t wfmt;         /* a moe_wfmt */
+  int32_t max_tokens;   /* capacity: forwards accept 0 <= T <= max_tokens (1..65536) */
+} moe_layer_desc;
+
+/* One stored matrix set [n][rows][cols] (device pointers, row-major, the
+ * reduction dimension `cols` contiguous).  Element 2i of a row is the LOW
+ * nibble of byte i for the 4-bit formats.
+ *   codes : q4_1 / NVFP4: uint8 [n][rows][cols/2]; bf16: bf16 [n][rows][cols]  (16 B aligned)
+ *   scales: q4_1: fp16 pairs {d, m} [n][rows][cols/32][2]                      (4 B aligned)
+ *           NVFP4: E4M3 bytes [n][rows][cols/16]                               (2 B aligned)
+ *           bf16: NULL
+ *   tensor_scale: NVFP4: fp32 [n]; otherwise NULL */
+typedef struct {
+  const void* codes;
+  const void* scales;
+  const float* tensor_scale;
+} moe_qmat;
+
+/* Weights of one layer (device pointers, borrowed by the handle). */
+typedef struct {
+  const void* router_w;   /* bf16 [n_experts][d_model] (16 B aligned) */
+  const float* router_b;  /* fp32 [n_experts], or NULL for no router bias */
+  moe_qmat gate, up;      /* routed: n = n_experts, rows = d_expert, cols = d_model */
+  moe_qmat down;          /* routed: n = n_experts, rows = d_model, cols = d_expert */
+  moe_qmat sh_gate, sh_up, sh_down; /* shared (n = 1, same shapes); ignored when n_shared = 0 */
+} moe_layer_weights;
+
+/* Optional copies of intermediate results (device pointers; each may be NULL).
+ * T tokens, k = top_k, E = n_experts, S = T*k slots, slot s = t*k + j. */
+typedef struct {
+  int32_t* topk_ids; /* [T][k] chosen experts, logit-descending (ties: lower id first) */
+  float* topk_w;     /* [T][k] routing weights, same order */
+  float* logits;     /* [T][E] router logits (fp32, bias included) */
+  int32_t* counts;   /* [E] slots per expert */
+  int32_t* offsets;  /* [E+1] exclusive prefix sum of counts; offsets[E] = S */
+  int32_t* perm;     /* [S] expert-sorted position -> slot; stable (token order inside a bucket) */
+  void* x_in;        /* bf16 [T][d_model]: the layer's input (in a stack: bf16(RMSNorm(r))) */
+  void* y_out;       /* bf16 [T][d_model]: the layer's output */
+} moe_route_out;
+
+typedef struct moe_layer moe_layer; /* opaque, host memory only */
+
+/* Validate desc and weights (pointers, alignment), check that the current
+ * device is gfx950, and return a handle.  No device memory is allocated and
+ * no weight is repacked: the layouts above are the device layouts. */
+moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights* weights, moe_layer** out);
+
+/* Free a handle (NULL-safe). */
+void moe_layer_destroy(moe_layer* layer);
+
+/* Workspace bytes a forward of T tokens needs (T <= max_tokens). */
+moe_status moe_layer_workspace_size(const moe_layer* layer, int32_t T, size_t* bytes);
+
+/* The same, from a descriptor alone (host-only; no device needed). */
+moe_status moe_desc_workspace_size(const moe_layer_desc* desc, int32_t T, size_t* bytes);
+
+/* One layer: y = MoE(x).  x, y: bf16 [T][d_model] device arrays (16 B aligned,
+ * not overlapping).  route may be NULL.  workspace: device memory of at least
+ * moe_layer_workspace_size bytes, 256 B aligned, used for this call only.
+ * T = 0 is a no-op. */
+moe_status moe_layer_forward(const moe_layer* layer, const void* x, int32_t T, void* y, const moe_route_out* route,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for moe_stack_forward over these layers at T tokens. */
+moe_status moe_stack_workspace_size(const moe_layer* const* layers, int32_t n_layers, int32_t T, size_t* bytes);
+
+/* Pre-norm residual stack of n_layers layers (all with the same d_model and
+ * format), updating x (bf16 [T][d_model]) in place.  routes: NULL or an array
+ * of n_layers moe_route_out (each entry's pointers may be NULL). */
+moe_status moe_stack_forward(const moe_layer* const* layers, int32_t n_layers, void* x, int32_t T, float rms_eps,
+                             const moe_route_out* routes, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Library version string. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FFN_H */

@@ -1,0 +1,260 @@
+"""Python binding of libmoe_ffn.so, the gfx950 MoE-layer library.
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels behind the C ABI of include/moe_ffn.h.  torch is used for device
+memory and the current stream.  The library must be built
+(``python -m quantized_expert_ffn_wave_amd.build``); importing this package
+without it raises ImportError -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_ffn.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE",
+                4: "MOE_ERR_HIP"}
+WFMT = {"bf16": 0, "q4_1": 1, "nvfp4": 2}
+EXPORTED = ["moe_layer_create", "moe_layer_destroy", "moe_layer_workspace_size", "moe_desc_workspace_size",
+            "moe_layer_forward", "moe_stack_workspace_size", "moe_stack_forward", "moe_last_error", "moe_version"]
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m quantized_expert_ffn_wave_amd.build`")
+
+
+class moe_layer_desc(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("d_expert", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("d_shared", ctypes.c_int32),
+                ("shared_scale", ctypes.c_float), ("renorm_topk", ctypes.c_int32), ("wfmt", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32)]
+
+
+class moe_qmat(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("tensor_scale", ctypes.c_void_p)]
+
+
+class moe_layer_weights(ctypes.Structure):
+    _fields_ = [("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
+                ("gate", moe_qmat), ("up", moe_qmat), ("down", moe_qmat),
+                ("sh_gate", moe_qmat), ("sh_up", moe_qmat), ("sh_down", moe_qmat)]
+
+
+class moe_route_out(ctypes.Structure):
+    _fields_ = [("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("logits", ctypes.c_void_p),
+                ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p),
+                ("x_in", ctypes.c_void_p), ("y_out", ctypes.c_void_p)]
+
+
+_lib = ctypes.CDLL(LIB_PATH)
+_vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+_lib.moe_layer_create.argtypes = [ctypes.POINTER(moe_layer_desc), ctypes.POINTER(moe_layer_weights),
+                                  ctypes.POINTER(_vp)]
+_lib.moe_layer_create.restype = ctypes.c_int
+_lib.moe_layer_destroy.argtypes = [_vp]
+_lib.moe_layer_destroy.restype = None
+_lib.moe_layer_workspace_size.argtypes = [_vp, _i32, ctypes.POINTER(_sz)]
+_lib.moe_layer_workspace_size.restype = ctypes.c_int
+_lib.moe_desc_workspace_size.argtypes = [ctypes.POINTER(moe_layer_desc), _i32, ctypes.POINTER(_sz)]
+_lib.moe_desc_workspace_size.restype = ctypes.c_int
+_lib.moe_layer_forward.argtypes = [_vp, _vp, _i32, _vp, ctypes.POINTER(moe_route_out), _vp, _sz, _vp]
+_lib.moe_layer_forward.restype = ctypes.c_int
+_lib.moe_stack_workspace_size.argtypes = [ctypes.POINTER(_vp), _i32, _i32, ctypes.POINTER(_sz)]
+_lib.moe_stack_workspace_size.restype = ctypes.c_int
+_lib.moe_stack_forward.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _i32, ctypes.c_float,
+                                   ctypes.POINTER(moe_route_out), _vp, _sz, _vp]
+_lib.moe_stack_forward.restype = ctypes.c_int
+_lib.moe_last_error.restype = ctypes.c_char_p
+_lib.moe_version.restype = ctypes.c_char_p
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.moe_last_error().decode()
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def lib():
+    return _lib
+
+
+def version() -> str:
+    return _lib.moe_version().decode()
+
+
+def last_error() -> str:
+    return _lib.moe_last_error().decode()
+
+
+# ---- raw C-ABI calls (same names as include/moe_ffn.h) ------------------------------------
+
+def moe_desc_workspace_size(desc: moe_layer_desc, T: int) -> int:
+    n = _sz(0)
+    _check(_lib.moe_desc_workspace_size(ctypes.byref(desc), T, ctypes.byref(n)), "moe_desc_workspace_size")
+    return n.value
+
+
+def moe_layer_create(desc: moe_layer_desc, weights: moe_layer_weights) -> int:
+    h = _vp()
+    _check(_lib.moe_layer_create(ctypes.byref(desc), ctypes.byref(weights), ctypes.byref(h)), "moe_layer_create")
+    return h.value
+
+
+def moe_layer_destroy(handle: int) -> None:
+    _lib.moe_layer_destroy(handle)
+
+
+def moe_layer_workspace_size(handle: int, T: int) -> int:
+    n = _sz(0)
+    _check(_lib.moe_layer_workspace_size(handle, T, ctypes.byref(n)), "moe_layer_workspace_size")
+    return n.value
+
+
+def moe_layer_forward(handle: int, x_ptr: int, T: int, y_ptr: int, route: moe_route_out | None, ws_ptr: int,
+                      ws_bytes: int, stream: int) -> None:
+    _check(_lib.moe_layer_forward(handle, x_ptr, T, y_ptr, ctypes.byref(route) if route is not None else None,
+                                  ws_ptr, ws_bytes, stream), "moe_layer_forward")
+
+
+def moe_stack_workspace_size(handles, T: int) -> int:
+    arr = (_vp * len(handles))(*handles)
+    n = _sz(0)
+    _check(_lib.moe_stack_workspace_size(arr, len(handles), T, ctypes.byref(n)), "moe_stack_workspace_size")
+    return n.value
+
+
+def moe_stack_forward(handles, x_ptr: int, T: int, eps: float, routes, ws_ptr: int, ws_bytes: int,
+                      stream: int) -> None:
+    arr = (_vp * len(handles))(*handles)
+    rarr = None
+    if routes is not None:
+        rarr = (moe_route_out * len(routes))(*routes)
+    _check(_lib.moe_stack_forward(arr, len(handles), x_ptr, T, eps, rarr, ws_ptr, ws_bytes, stream),
+           "moe_stack_forward")
+
+
+# ---- torch-level helpers -----------------------------------------------------------------
+
+def make_desc(fmt: str, E: int = 256, k: int = 6, d: int = 2048, f: int = 512, n_shared: int = 1,
+              shared_scale: float = 1.0, renorm: int = 1, max_tokens: int = 4096) -> moe_layer_desc:
+    return moe_layer_desc(d, E, k, f, n_shared, f, shared_scale, renorm, WFMT[fmt], max_tokens)
+
+
+def _to_dev(a: np.ndarray, device):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    elif a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a).to(device)
+
+
+class DeviceLayer:
+    """Weights of one layer copied to the device plus its library handle.
+
+    `host` is any object with the attributes of a stored layer: fmt, E, k,
+    n_shared, shared_scale, renorm, router_w (bf16 bits [E][d]), router_b
+    (fp32 [E] or None) and gate/up/down/sh_gate/sh_up/sh_down, each with
+    codes, scales, tensor_scale numpy arrays in the layouts of moe_ffn.h."""
+
+    def __init__(self, host, device="cuda", max_tokens: int = 4096):
+        self.keep = []
+        self.fmt = host.fmt
+        self.desc = make_desc(host.fmt, E=host.E, k=host.k, d=host.d, f=host.f, n_shared=host.n_shared,
+                              shared_scale=host.shared_scale, renorm=host.renorm, max_tokens=max_tokens)
+        w = moe_layer_weights()
+        w.router_w = self._ptr(host.router_w, device)
+        w.router_b = self._ptr(host.router_b, device) if host.router_b is not None else None
+        for name in ("gate", "up", "down", "sh_gate", "sh_up", "sh_down"):
+            q = getattr(host, name, None)
+            if q is None:
+                continue
+            m = moe_qmat(self._ptr(q.codes, device),
+                         self._ptr(q.scales, device) if q.scales is not None else None,
+                         self._ptr(q.tensor_scale, device) if q.tensor_scale is not None else None)
+            setattr(w, name, m)
+        self.weights = w
+        self.handle = moe_layer_create(self.desc, w)
+
+    def _ptr(self, a, device):
+        t = _to_dev(a, device)
+        self.keep.append(t)
+        return t.data_ptr()
+
+    def workspace_size(self, T: int) -> int:
+        return moe_layer_workspace_size(self.handle, T)
+
+    def close(self):
+        if self.handle:
+            moe_layer_destroy(self.handle)
+            self.handle = 0
+            self.keep = []
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def alloc_workspace(nbytes: int, device="cuda"):
+    """Caller-owned workspace (torch allocations are 256-byte aligned or better)."""
+    import torch
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def route_buffers(T: int, k: int, E: int, device="cuda", d: int = 2048):
+    """Device buffers for every moe_route_out field, and the struct pointing at them."""
+    import torch
+    b = dict(topk_ids=torch.empty((T, k), dtype=torch.int32, device=device),
+             topk_w=torch.empty((T, k), dtype=torch.float32, device=device),
+             logits=torch.empty((T, E), dtype=torch.float32, device=device),
+             counts=torch.empty(E, dtype=torch.int32, device=device),
+             offsets=torch.empty(E + 1, dtype=torch.int32, device=device),
+             perm=torch.empty(max(T * k, 1), dtype=torch.int32, device=device),
+             x_in=torch.empty((T, d), dtype=torch.bfloat16, device=device),
+             y_out=torch.empty((T, d), dtype=torch.bfloat16, device=device))
+    r = moe_route_out(*[b[n].data_ptr() for n, _ in moe_route_out._fields_])
+    return r, b
+
+
+def current_stream() -> int:
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def layer_forward(layer: DeviceLayer, x, y=None, route: moe_route_out | None = None, workspace=None):
+    """y = MoE(x) for a bf16 torch tensor x [T][d] on the device."""
+    import torch
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty_like(x)
+    nbytes = layer.workspace_size(T)
+    if workspace is None:
+        workspace = alloc_workspace(nbytes, x.device)
+    moe_layer_forward(layer.handle, x.data_ptr(), T, y.data_ptr(), route, workspace.data_ptr(), workspace.numel(),
+                      current_stream())
+    return y
+
+
+def stack_forward(layers, x, eps: float = 1e-6, routes=None, workspace=None):
+    """In-place pre-norm residual stack over bf16 x [T][d]."""
+    handles = [l.handle for l in layers]
+    T = x.shape[0]
+    nbytes = moe_stack_workspace_size(handles, T)
+    if workspace is None:
+        workspace = alloc_workspace(nbytes, x.device)
+    moe_stack_forward(handles, x.data_ptr(), T, eps, routes, workspace.data_ptr(), workspace.numel(),
+                      current_stream())
+    return x

@@ -1,0 +1,329 @@
+// C ABI of the MoE-layer library (declared in include/moe_ffn.h): argument
+// validation, workspace layout and kernel sequencing.  No device memory is
+// allocated here and nothing synchronises the host.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "common.hpp"
+#include "moe_ffn.h"
+
+struct moe_layer {
+  moe_layer_desc desc;
+  moe_layer_weights w;
+  int device;
+  int n_cu;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+moe_status hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+moe_status check_desc(const moe_layer_desc* d) {
+  if (!d) return fail(MOE_ERR_INVALID_ARG, "desc is NULL");
+  if (d->wfmt < MOE_W_BF16 || d->wfmt > MOE_W_NVFP4) return fail(MOE_ERR_INVALID_ARG, "unknown wfmt %d", d->wfmt);
+  if (d->n_experts < 16 || d->n_experts > moe::MAX_E || d->n_experts % 16)
+    return fail(MOE_ERR_INVALID_ARG, "n_experts must be a multiple of 16 in [16, 256], got %d", d->n_experts);
+  if (d->top_k < 1 || d->top_k > moe::MAX_K || d->top_k > d->n_experts)
+    return fail(MOE_ERR_INVALID_ARG, "top_k must be in [1, min(8, n_experts)], got %d", d->top_k);
+  if (d->n_shared != 0 && d->n_shared != 1) return fail(MOE_ERR_INVALID_ARG, "n_shared must be 0 or 1");
+  if (d->renorm_topk != 0 && d->renorm_topk != 1) return fail(MOE_ERR_INVALID_ARG, "renorm_topk must be 0 or 1");
+  if (d->max_tokens < 1 || d->max_tokens > 65536)
+    return fail(MOE_ERR_INVALID_ARG, "max_tokens must be in [1, 65536], got %d", d->max_tokens);
+  if (d->d_model <= 0 || d->d_expert <= 0) return fail(MOE_ERR_INVALID_ARG, "d_model and d_expert must be positive");
+  if (d->n_shared && d->d_shared != d->d_expert)
+    return fail(MOE_ERR_INVALID_ARG, "d_shared (%d) must equal d_expert (%d)", d->d_shared, d->d_expert);
+  if (d->d_model != moe::D_MODEL || d->d_expert != moe::D_FF)
+    return fail(MOE_ERR_UNSUPPORTED, "this build has kernels for d_model=%d, d_expert=%d (got %d, %d)", moe::D_MODEL,
+                moe::D_FF, d->d_model, d->d_expert);
+  return MOE_OK;
+}
+
+moe_status check_qmat(const moe_qmat& q, int fmt, const char* name) {
+  if (!q.codes || !aligned(q.codes, 16)) return fail(MOE_ERR_INVALID_ARG, "%s.codes is NULL or not 16-byte aligned", name);
+  if (fmt == MOE_W_Q4_1 && (!q.scales || !aligned(q.scales, 4)))
+    return fail(MOE_ERR_INVALID_ARG, "%s.scales (q4_1 {d,m}) is NULL or not 4-byte aligned", name);
+  if (fmt == MOE_W_NVFP4) {
+    if (!q.scales || !aligned(q.scales, 2))
+      return fail(MOE_ERR_INVALID_ARG, "%s.scales (NVFP4 E4M3) is NULL or not 2-byte aligned", name);
+    if (!q.tensor_scale || !aligned(q.tensor_scale, 4))
+      return fail(MOE_ERR_INVALID_ARG, "%s.tensor_scale is NULL or not 4-byte aligned", name);
+  }
+  return MOE_OK;
+}
+
+struct WsLayout {
+  size_t logit_part, logits, ids, w, counts, offsets, perm, inv_perm, items_up, items_dn, ctl, h, y, total;
+  int max_up, max_dn;
+};
+
+WsLayout ws_layout(const moe_layer_desc& d, int T) {
+  WsLayout L;
+  const int E = d.n_experts, K = d.top_k;
+  const size_t S = (size_t)T * K, R = S + (size_t)d.n_shared * T;
+  const int U = (int)((S < (size_t)E ? S : (size_t)E) + d.n_shared);
+  L.max_up = 40 * U + (int)(R / 8) + 8;
+  L.max_dn = 48 * U + (int)(R / 4) + 16;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes > 0 ? bytes : 1); return at; };
+  L.logit_part = take(sizeof(float) * 8 * T * E);
+  L.logits = take(sizeof(float) * (size_t)T * E);
+  L.ids = take(sizeof(int32_t) * S);
+  L.w = take(sizeof(float) * S);
+  L.counts = take(sizeof(int32_t) * E);
+  L.offsets = take(sizeof(int32_t) * (E + 1));
+  L.perm = take(sizeof(int32_t) * S);
+  L.inv_perm = take(sizeof(int32_t) * S);
+  L.items_up = take(sizeof(uint32_t) * L.max_up);
+  L.items_dn = take(sizeof(uint32_t) * L.max_dn);
+  L.ctl = take(sizeof(int32_t) * moe::CTL_WORDS);
+  L.h = take(sizeof(uint16_t) * R * moe::D_FF);
+  L.y = take(sizeof(float) * R * moe::D_MODEL);
+  L.total = o;
+  return L;
+}
+
+moe::QMat qm(const moe_qmat& q) {
+  moe::QMat r;
+  r.codes = (const uint8_t*)q.codes;
+  r.scales = q.scales;
+  r.ts = q.tensor_scale;
+  return r;
+}
+
+moe::LayerArgs make_args(const moe_layer* L, const void* x, int T, char* ws, const WsLayout& W) {
+  moe::LayerArgs a;
+  memset(&a, 0, sizeof a);
+  const moe_layer_desc& d = L->desc;
+  a.T = T;
+  a.E = d.n_experts;
+  a.K = d.top_k;
+  a.S = T * d.top_k;
+  a.n_shared = d.n_shared;
+  a.renorm = d.renorm_topk;
+  a.fmt = d.wfmt;
+  a.ks = 8;
+  a.shared_scale = d.shared_scale;
+  a.x = (const uint16_t*)x;
+  a.router_w = (const uint16_t*)L->w.router_w;
+  a.router_b = L->w.router_b;
+  a.gate = qm(L->w.gate);
+  a.up = qm(L->w.up);
+  a.down = qm(L->w.down);
+  if (d.n_shared) {
+    a.sh_gate = qm(L->w.sh_gate);
+    a.sh_up = qm(L->w.sh_up);
+    a.sh_down = qm(L->w.sh_down);
+  }
+  a.logit_part = (float*)(ws + W.logit_part);
+  a.logits = (float*)(ws + W.logits);
+  a.ids = (int32_t*)(ws + W.ids);
+  a.w = (float*)(ws + W.w);
+  a.counts = (int32_t*)(ws + W.counts);
+  a.offsets = (int32_t*)(ws + W.offsets);
+  a.perm = (int32_t*)(ws + W.perm);
+  a.inv_perm = (int32_t*)(ws + W.inv_perm);
+  a.items_up = (uint32_t*)(ws + W.items_up);
+  a.items_dn = (uint32_t*)(ws + W.items_dn);
+  a.ctl = (int32_t*)(ws + W.ctl);
+  a.h = (_Float16*)(ws + W.h);
+  a.y = (float*)(ws + W.y);
+  a.max_items_up = W.max_up;
+  a.max_items_dn = W.max_dn;
+  return a;
+}
+
+int ffn_grid(const moe_layer* L, int max_items) {
+  const int g = L->n_cu * 8;
+  return max_items < g ? max_items : g;
+}
+
+hipError_t copy_async(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  if (!dst || bytes == 0) return hipSuccess;
+  return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
+}
+
+// Router, top-k, buckets, both FFN projections; then route copies.
+moe_status run_layer_core(const moe_layer* L, moe::LayerArgs& a, const WsLayout& W, const moe_route_out* route,
+                          hipStream_t s) {
+  hipError_t e;
+  const bool want_logits = route && route->logits;
+  if (want_logits) a.logits = route->logits;
+  if ((e = moe::launch_router(a, s)) != hipSuccess) return hip_fail(e, "router launch");
+  if ((e = moe::launch_topk(a, want_logits, s)) != hipSuccess) return hip_fail(e, "top-k launch");
+  if ((e = moe::launch_bucket(a, s)) != hipSuccess) return hip_fail(e, "bucket launch");
+  if ((e = moe::launch_ffn_up(a, ffn_grid(L, W.max_up), s)) != hipSuccess) return hip_fail(e, "gate/up launch");
+  if ((e = moe::launch_ffn_down(a, ffn_grid(L, W.max_dn), s)) != hipSuccess) return hip_fail(e, "down launch");
+  if (route) {
+    const size_t S = (size_t)a.S;
+    const int E = a.E;
+    if ((e = copy_async(route->topk_ids, a.ids, S * 4, s)) != hipSuccess) return hip_fail(e, "route copy");
+    if ((e = copy_async(route->topk_w, a.w, S * 4, s)) != hipSuccess) return hip_fail(e, "route copy");
+    if ((e = copy_async(route->counts, a.counts, (size_t)E * 4, s)) != hipSuccess) return hip_fail(e, "route copy");
+    if ((e = copy_async(route->offsets, a.offsets, (size_t)(E + 1) * 4, s)) != hipSuccess)
+      return hip_fail(e, "route copy");
+    if ((e = copy_async(route->perm, a.perm, S * 4, s)) != hipSuccess) return hip_fail(e, "route copy");
+    if ((e = copy_async(route->x_in, a.x, (size_t)a.T * moe::D_MODEL * 2, s)) != hipSuccess)
+      return hip_fail(e, "route copy");
+  }
+  return MOE_OK;
+}
+
+moe_status check_ws(void* ws, size_t have, size_t need) {
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (have < need) return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, need);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights* w, moe_layer** out) {
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  if (!w->router_w || !aligned(w->router_w, 16))
+    return fail(MOE_ERR_INVALID_ARG, "router_w is NULL or not 16-byte aligned");
+  if (w->router_b && !aligned(w->router_b, 4)) return fail(MOE_ERR_INVALID_ARG, "router_b is not 4-byte aligned");
+  const int f = desc->wfmt;
+  if ((st = check_qmat(w->gate, f, "gate")) || (st = check_qmat(w->up, f, "up")) ||
+      (st = check_qmat(w->down, f, "down")))
+    return st;
+  if (desc->n_shared && ((st = check_qmat(w->sh_gate, f, "sh_gate")) || (st = check_qmat(w->sh_up, f, "sh_up")) ||
+                         (st = check_qmat(w->sh_down, f, "sh_down"))))
+    return st;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d is %s; this library runs on gfx950 only", dev, prop.gcnArchName);
+  moe_layer* L = new (std::nothrow) moe_layer;
+  if (!L) return fail(MOE_ERR_INVALID_ARG, "out of host memory");
+  L->desc = *desc;
+  L->w = *w;
+  L->device = dev;
+  L->n_cu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+  *out = L;
+  return MOE_OK;
+}
+
+void moe_layer_destroy(moe_layer* layer) { delete layer; }
+
+moe_status moe_desc_workspace_size(const moe_layer_desc* desc, int32_t T, size_t* bytes) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  if (T < 0 || T > desc->max_tokens) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, max_tokens=%d]", T, desc->max_tokens);
+  *bytes = ws_layout(*desc, T).total;
+  return MOE_OK;
+}
+
+moe_status moe_layer_workspace_size(const moe_layer* layer, int32_t T, size_t* bytes) {
+  if (!layer) return fail(MOE_ERR_INVALID_ARG, "layer is NULL");
+  return moe_desc_workspace_size(&layer->desc, T, bytes);
+}
+
+moe_status moe_layer_forward(const moe_layer* L, const void* x, int32_t T, void* y, const moe_route_out* route,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (!L) return fail(MOE_ERR_INVALID_ARG, "layer is NULL");
+  if (T < 0 || T > L->desc.max_tokens)
+    return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, max_tokens=%d]", T, L->desc.max_tokens);
+  if (T == 0) return MOE_OK;
+  if (!x || !aligned(x, 16)) return fail(MOE_ERR_INVALID_ARG, "x is NULL or not 16-byte aligned");
+  if (!y || !aligned(y, 16)) return fail(MOE_ERR_INVALID_ARG, "y is NULL or not 16-byte aligned");
+  const size_t xb = (size_t)T * moe::D_MODEL * 2;
+  if ((const char*)x < (const char*)y + xb && (const char*)y < (const char*)x + xb)
+    return fail(MOE_ERR_INVALID_ARG, "x and y overlap");
+  const WsLayout W = ws_layout(L->desc, T);
+  moe_status st = check_ws(ws, ws_bytes, W.total);
+  if (st != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  moe::LayerArgs a = make_args(L, x, T, (char*)ws, W);
+  if ((st = run_layer_core(L, a, W, route, s)) != MOE_OK) return st;
+  hipError_t e = moe::launch_combine(a, (uint16_t*)y, s);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  if (route && (e = copy_async(route->y_out, y, xb, s)) != hipSuccess) return hip_fail(e, "route copy");
+  return MOE_OK;
+}
+
+moe_status moe_stack_workspace_size(const moe_layer* const* layers, int32_t n, int32_t T, size_t* bytes) {
+  if (!layers || n < 1) return fail(MOE_ERR_INVALID_ARG, "layers is NULL or n_layers < 1");
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  size_t mx = 0;
+  for (int l = 0; l < n; ++l) {
+    if (!layers[l]) return fail(MOE_ERR_INVALID_ARG, "layers[%d] is NULL", l);
+    if (T < 0 || T > layers[l]->desc.max_tokens)
+      return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, max_tokens] of layer %d", T, l);
+    const size_t b = ws_layout(layers[l]->desc, T).total;
+    if (b > mx) mx = b;
+  }
+  *bytes = mx + up256(sizeof(float) * (size_t)T * moe::D_MODEL) + up256(2 * (size_t)T * moe::D_MODEL);
+  return MOE_OK;
+}
+
+moe_status moe_stack_forward(const moe_layer* const* layers, int32_t n, void* x, int32_t T, float eps,
+                             const moe_route_out* routes, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  moe_status st = moe_stack_workspace_size(layers, n, T, &need);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !aligned(x, 16)) return fail(MOE_ERR_INVALID_ARG, "x is NULL or not 16-byte aligned");
+  if (!(eps >= 0.f)) return fail(MOE_ERR_INVALID_ARG, "rms_eps must be >= 0");
+  if ((st = check_ws(ws, ws_bytes, need)) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  size_t layer_ws = 0;
+  for (int l = 0; l < n; ++l) {
+    const size_t b = ws_layout(layers[l]->desc, T).total;
+    if (b > layer_ws) layer_ws = b;
+  }
+  char* base = (char*)ws;
+  float* r = (float*)(base + layer_ws);
+  uint16_t* xn = (uint16_t*)(base + layer_ws + up256(sizeof(float) * (size_t)T * moe::D_MODEL));
+  hipError_t e = moe::launch_stack_init((const uint16_t*)x, r, xn, T, eps, s);
+  if (e != hipSuccess) return hip_fail(e, "stack init launch");
+  for (int l = 0; l < n; ++l) {
+    const moe_layer* L = layers[l];
+    const WsLayout W = ws_layout(L->desc, T);
+    moe::LayerArgs a = make_args(L, xn, T, base, W);
+    const moe_route_out* route = routes ? &routes[l] : nullptr;
+    if ((st = run_layer_core(L, a, W, route, s)) != MOE_OK) return st;
+    const bool last = (l == n - 1);
+    e = moe::launch_combine_stack(a, r, last ? nullptr : xn, route ? (uint16_t*)route->y_out : nullptr,
+                                  last ? (uint16_t*)x : nullptr, eps, s);
+    if (e != hipSuccess) return hip_fail(e, "stack combine launch");
+  }
+  return MOE_OK;
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+const char* moe_version(void) { return "moe_ffn gfx950 0.1"; }
+
+}  // extern "C"

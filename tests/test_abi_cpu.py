@@ -1,0 +1,118 @@
+"""The C-ABI library loads and exports every symbol include/moe_ffn.h declares;
+host-side argument checks and workspace sizing (no GPU needed, no kernel runs)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_expert_ffn_wave_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_ffn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(moe.EXPORTED)
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_library_is_built_for_gfx950_only():
+    blob = open(moe.LIB_PATH, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa-+(gfx[0-9a-z]+)", blob))
+    assert targets == {b"gfx950"}
+
+
+def desc(**kw):
+    d = moe.make_desc("q4_1")
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_experts=8), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_experts=257), moe.MOE_ERR_INVALID_ARG),
+    (dict(top_k=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(top_k=9), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_shared=2), moe.MOE_ERR_INVALID_ARG),
+    (dict(wfmt=7), moe.MOE_ERR_INVALID_ARG),
+    (dict(max_tokens=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(d_shared=256), moe.MOE_ERR_INVALID_ARG),
+    (dict(d_model=1024), moe.MOE_ERR_UNSUPPORTED),
+    (dict(d_expert=256, d_shared=256), moe.MOE_ERR_UNSUPPORTED),
+])
+def test_bad_descriptors_are_rejected(kw, status):
+    n = ctypes.c_size_t(0)
+    st = moe.lib().moe_desc_workspace_size(ctypes.byref(desc(**kw)), 4, ctypes.byref(n))
+    assert st == status
+    assert moe.last_error()
+
+
+def test_workspace_size_grows_with_tokens_and_rejects_bad_T():
+    d = desc(max_tokens=4096)
+    sizes = [moe.moe_desc_workspace_size(d, T) for T in (0, 1, 4, 64, 256, 4096)]
+    assert all(b > a for a, b in zip(sizes, sizes[1:]))
+    assert all(s % 256 == 0 for s in sizes)
+    # the big terms: fp32 expert outputs and fp16 SwiGLU rows for S + T rows
+    S = 64 * 6
+    assert sizes[3] >= (S + 64) * (2048 * 4 + 512 * 2)
+    n = ctypes.c_size_t(0)
+    assert moe.lib().moe_desc_workspace_size(ctypes.byref(d), 4097, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+    assert moe.lib().moe_desc_workspace_size(ctypes.byref(d), -1, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+
+
+def fake_weights(align=256):
+    base = 1 << 32
+    q = moe.moe_qmat(base, base + align, base + 2 * align)
+    return moe.moe_layer_weights(base, None, q, q, q, q, q, q)
+
+
+def test_create_checks_pointers_before_the_device():
+    out = ctypes.c_void_p()
+    d = desc()
+    w = fake_weights()
+    w.router_w = None
+    assert moe.lib().moe_layer_create(ctypes.byref(d), ctypes.byref(w), ctypes.byref(out)) == moe.MOE_ERR_INVALID_ARG
+    w = fake_weights()
+    w.gate = moe.moe_qmat((1 << 32) + 8, (1 << 32), None)  # codes not 16-byte aligned
+    assert moe.lib().moe_layer_create(ctypes.byref(d), ctypes.byref(w), ctypes.byref(out)) == moe.MOE_ERR_INVALID_ARG
+    assert "gate.codes" in moe.last_error()
+    dn = moe.make_desc("nvfp4")
+    w = fake_weights()
+    w.up = moe.moe_qmat(1 << 32, 1 << 32, None)  # NVFP4 needs the per-matrix scale
+    assert moe.lib().moe_layer_create(ctypes.byref(dn), ctypes.byref(w), ctypes.byref(out)) == moe.MOE_ERR_INVALID_ARG
+    assert moe.lib().moe_layer_create(ctypes.byref(d), None, ctypes.byref(out)) == moe.MOE_ERR_INVALID_ARG
+    assert moe.lib().moe_layer_create(None, ctypes.byref(fake_weights()), ctypes.byref(out)) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_create_without_a_device_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    out = ctypes.c_void_p()
+    st = moe.lib().moe_layer_create(ctypes.byref(desc()), ctypes.byref(fake_weights()), ctypes.byref(out))
+    assert st == moe.MOE_ERR_HIP
+    assert out.value is None
+    assert "hip" in moe.last_error().lower()
+
+
+def test_forward_argument_errors_without_a_layer():
+    lib = moe.lib()
+    assert lib.moe_layer_forward(None, None, 4, None, None, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    n = ctypes.c_size_t(0)
+    assert lib.moe_layer_workspace_size(None, 4, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+    arr = (ctypes.c_void_p * 1)(None)
+    assert lib.moe_stack_workspace_size(arr, 1, 4, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_stack_forward(None, 0, None, 4, 1e-6, None, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    lib.moe_layer_destroy(None)  # NULL-safe
+    assert moe.version().startswith("moe_ffn gfx950")

@@ -1,0 +1,166 @@
+"""GPU parity of one MoE layer (through the C ABI) against the CPU oracle.
+
+Workloads: the decode layers of 4 and 64 tokens (q4_1, near-uniform routing),
+256 tokens with NVFP4 weights and a Zipf(1.1) router bias, the 4096-token
+bf16 prefill layer (outputs on a token sample), ragged token counts on both
+sides of the small-bucket/large-bucket boundary, reduced expert counts,
+top-k 1 and 8, no shared expert, unnormalised weights, determinism and T=0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_expert_ffn_wave_amd as moe
+import synth
+from parity import bits_of, check_layer, gpu_forward, say, x_to_dev
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+@pytest.fixture(scope="module")
+def q4_layer():
+    host = synth.make_layer(seed=0, fmt="q4_1")
+    return host, moe.DeviceLayer(host, max_tokens=4096)
+
+
+@pytest.fixture(scope="module")
+def nvfp4_layer():
+    host = synth.make_layer(seed=0, fmt="nvfp4", zipf=1.1)
+    return host, moe.DeviceLayer(host, max_tokens=4096)
+
+
+@pytest.fixture(scope="module")
+def bf16_layer():
+    host = synth.make_layer(seed=0, fmt="bf16")
+    return host, moe.DeviceLayer(host, max_tokens=4096)
+
+
+def test_decode_t4_q4_1(q4_layer):
+    host, dl = q4_layer
+    say("case decode_t4_q4_1")
+    info = check_layer(host, synth.make_x(4), dl)
+    say(f"  max row err {info['max_err']:.2e}")
+
+
+def test_decode_t64_q4_1(q4_layer):
+    host, dl = q4_layer
+    say("case decode_t64_q4_1")
+    info = check_layer(host, synth.make_x(64), dl)
+    assert info["counts"].max() <= 8  # near-uniform load: small buckets
+    say(f"  max row err {info['max_err']:.2e}, ties {info['ties']}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 7, 17, 63, 65, 100, 130])
+def test_ragged_token_counts_q4_1(q4_layer, T):
+    host, dl = q4_layer
+    say(f"case q4_1 T={T}")
+    check_layer(host, synth.make_x(T, xseed=100 + T), dl)
+
+
+def test_decode_t256_nvfp4_zipf(nvfp4_layer):
+    host, dl = nvfp4_layer
+    say("case decode_t256_nvfp4_zipf1.1")
+    info = check_layer(host, synth.make_x(256), dl)
+    c = np.sort(info["counts"])[::-1]
+    assert c[0] > 64 and (info["counts"] == 0).sum() > 100  # hot buckets, many empty experts
+    say(f"  max row err {info['max_err']:.2e}, top buckets {c[:6].tolist()}")
+
+
+@pytest.mark.parametrize("T", [1, 4, 33])
+def test_nvfp4_small(nvfp4_layer, T):
+    host, dl = nvfp4_layer
+    say(f"case nvfp4 T={T}")
+    check_layer(host, synth.make_x(T, xseed=200 + T), dl)
+
+
+@pytest.mark.parametrize("T", [2, 64, 300])
+def test_bf16_layer(bf16_layer, T):
+    host, dl = bf16_layer
+    say(f"case bf16 T={T}")
+    check_layer(host, synth.make_x(T, xseed=300 + T), dl)
+
+
+def test_prefill_t4096_bf16(bf16_layer):
+    host, dl = bf16_layer
+    say("case prefill_t4096_bf16 (outputs on 96 sampled tokens)")
+    x = synth.make_x(4096)
+    rng = np.random.default_rng(0)
+    sample = np.concatenate([[0, 1, 4095], rng.choice(4096, 93, replace=False)])
+    info = check_layer(host, x, dl, sample=sample)
+    assert info["counts"].min() > 0 and 60 < info["counts"].mean() < 130
+    say(f"  max row err {info['max_err']:.2e}")
+
+
+@pytest.mark.parametrize("E,k,n_shared,renorm,scale,fmt,T", [
+    (16, 1, 1, 1, 1.0, "q4_1", 9),
+    (16, 8, 1, 1, 1.0, "q4_1", 12),
+    (32, 6, 0, 1, 1.0, "q4_1", 21),
+    (32, 6, 1, 0, 2.5, "nvfp4", 19),
+    (16, 6, 1, 1, 1.0, "bf16", 70),
+])
+def test_layer_options(E, k, n_shared, renorm, scale, fmt, T):
+    say(f"case options E={E} k={k} shared={n_shared} renorm={renorm} scale={scale} {fmt} T={T}")
+    host = synth.make_layer(seed=7, fmt=fmt, E=E, k=k, n_shared=n_shared, renorm=renorm, shared_scale=scale,
+                            zipf=0.5)
+    check_layer(host, synth.make_x(T, xseed=400 + T), moe.DeviceLayer(host, max_tokens=T))
+
+
+def test_small_and_large_bucket_boundary():
+    """With 16 experts and top-6, token counts 8..14 give buckets of every size
+    around the switch between the vector path (<= 4 tokens) and the matrix
+    path (>= 5 tokens)."""
+    host = synth.make_layer(seed=3, fmt="q4_1", E=16, k=6)
+    dl = moe.DeviceLayer(host, max_tokens=64)
+    seen = set()
+    for T in range(8, 15):
+        say(f"case boundary T={T}")
+        info = check_layer(host, synth.make_x(T, xseed=500 + T), dl)
+        seen |= set(info["counts"].tolist())
+    assert {3, 4, 5, 6} <= seen
+
+
+def test_deterministic_bits(q4_layer):
+    host, dl = q4_layer
+    say("case determinism T=64")
+    x = synth.make_x(64, xseed=9)
+    a = gpu_forward(dl, x, host.E, host.k)
+    b = gpu_forward(dl, x, host.E, host.k)
+    for n in ("topk_ids", "topk_w", "logits", "perm", "y_bits"):
+        assert np.array_equal(a[n], b[n]), n
+
+
+def test_zero_tokens_is_a_noop(q4_layer):
+    host, dl = q4_layer
+    say("case T=0")
+    y = torch.full((1, 2048), 7.0, dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros((1, 2048), dtype=torch.bfloat16, device="cuda")
+    ws = moe.alloc_workspace(dl.workspace_size(0))
+    moe.moe_layer_forward(dl.handle, x.data_ptr(), 0, y.data_ptr(), None, ws.data_ptr(), ws.numel(),
+                          moe.current_stream())
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+
+
+def test_forward_rejects_small_workspace_and_overlap(q4_layer):
+    host, dl = q4_layer
+    say("case argument errors")
+    x = x_to_dev(synth.make_x(4))
+    y = torch.empty_like(x)
+    need = dl.workspace_size(4)
+    ws = moe.alloc_workspace(need)
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_layer_forward(dl.handle, x.data_ptr(), 4, y.data_ptr(), None, ws.data_ptr(), need - 256,
+                              moe.current_stream())
+    assert e.value.status == moe.MOE_ERR_WORKSPACE
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_layer_forward(dl.handle, x.data_ptr(), 4, x.data_ptr(), None, ws.data_ptr(), need,
+                              moe.current_stream())
+    assert e.value.status == moe.MOE_ERR_INVALID_ARG
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_layer_forward(dl.handle, x.data_ptr(), 4097, y.data_ptr(), None, ws.data_ptr(), need,
+                              moe.current_stream())
+    assert e.value.status == moe.MOE_ERR_INVALID_ARG
