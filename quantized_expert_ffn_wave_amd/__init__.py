@@ -21,7 +21,10 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
                 4: "MOE_ERR_HIP"}
 WFMT = {"bf16": 0, "q4_1": 1, "nvfp4": 2}
 EXPORTED = ["moe_layer_create", "moe_layer_destroy", "moe_layer_workspace_size", "moe_desc_workspace_size",
-            "moe_layer_forward", "moe_stack_workspace_size", "moe_stack_forward", "moe_last_error", "moe_version"]
+            "moe_layer_forward", "moe_layer_forward_staged", "moe_stack_workspace_size", "moe_stack_forward",
+            "moe_last_error", "moe_version"]
+N_STAGE_EVENTS = 7
+STAGES = ["router", "topk", "bucket", "gate_up", "down", "combine"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m quantized_expert_ffn_wave_amd.build`")
@@ -63,6 +66,9 @@ _lib.moe_desc_workspace_size.argtypes = [ctypes.POINTER(moe_layer_desc), _i32, c
 _lib.moe_desc_workspace_size.restype = ctypes.c_int
 _lib.moe_layer_forward.argtypes = [_vp, _vp, _i32, _vp, ctypes.POINTER(moe_route_out), _vp, _sz, _vp]
 _lib.moe_layer_forward.restype = ctypes.c_int
+_lib.moe_layer_forward_staged.argtypes = [_vp, _vp, _i32, _vp, ctypes.POINTER(moe_route_out), _vp, _sz, _vp,
+                                          ctypes.POINTER(_vp), _i32]
+_lib.moe_layer_forward_staged.restype = ctypes.c_int
 _lib.moe_stack_workspace_size.argtypes = [ctypes.POINTER(_vp), _i32, _i32, ctypes.POINTER(_sz)]
 _lib.moe_stack_workspace_size.restype = ctypes.c_int
 _lib.moe_stack_forward.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _i32, ctypes.c_float,
@@ -124,6 +130,14 @@ def moe_layer_forward(handle: int, x_ptr: int, T: int, y_ptr: int, route: moe_ro
                       ws_bytes: int, stream: int) -> None:
     _check(_lib.moe_layer_forward(handle, x_ptr, T, y_ptr, ctypes.byref(route) if route is not None else None,
                                   ws_ptr, ws_bytes, stream), "moe_layer_forward")
+
+
+def moe_layer_forward_staged(handle: int, x_ptr: int, T: int, y_ptr: int, route: moe_route_out | None, ws_ptr: int,
+                             ws_bytes: int, stream: int, events) -> None:
+    """events: N_STAGE_EVENTS raw hipEvent_t handles (ints)."""
+    arr = (_vp * len(events))(*events)
+    _check(_lib.moe_layer_forward_staged(handle, x_ptr, T, y_ptr, ctypes.byref(route) if route is not None else None,
+                                         ws_ptr, ws_bytes, stream, arr, len(events)), "moe_layer_forward_staged")
 
 
 def moe_stack_workspace_size(handles, T: int) -> int:

@@ -5,16 +5,23 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "common.hpp"
 #include "moe_ffn.h"
 
+// Handle: the borrowed weights plus a second stream on which the shared expert
+// (which does not depend on routing) runs concurrently with the router, joined
+// back before the routed down projection combines its output.
 struct moe_layer {
   moe_layer_desc desc;
   moe_layer_weights w;
   int device;
   int n_cu;
+  hipStream_t side;
+  hipEvent_t fork, join;
+  std::mutex mu;  // fork/join sequences of concurrent callers must not interleave
 };
 
 namespace {
@@ -81,9 +88,10 @@ WsLayout ws_layout(const moe_layer_desc& d, int T) {
   WsLayout L;
   const int E = d.n_experts, K = d.top_k;
   const size_t S = (size_t)T * K, R = S + (size_t)d.n_shared * T;
-  const int U = (int)((S < (size_t)E ? S : (size_t)E) + d.n_shared);
-  L.max_up = 40 * U + (int)(R / 8) + 8;
-  L.max_dn = 48 * U + (int)(R / 4) + 16;
+  // token tiles of the routed buckets: sum_e ceil(m_e / GV_GROUP) <= touched + S / GV_GROUP
+  const int tiles = (int)((S < (size_t)E ? S : (size_t)E) + S / moe::GV_GROUP + 1);
+  L.max_up = tiles * moe::N_UP_CHUNKS;
+  L.max_dn = tiles * moe::N_DN_CHUNKS;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes > 0 ? bytes : 1); return at; };
   L.logit_part = take(sizeof(float) * 8 * T * E);
@@ -94,8 +102,8 @@ WsLayout ws_layout(const moe_layer_desc& d, int T) {
   L.offsets = take(sizeof(int32_t) * (E + 1));
   L.perm = take(sizeof(int32_t) * S);
   L.inv_perm = take(sizeof(int32_t) * S);
-  L.items_up = take(sizeof(uint32_t) * L.max_up);
-  L.items_dn = take(sizeof(uint32_t) * L.max_dn);
+  L.items_up = take(sizeof(moe::Item) * L.max_up);
+  L.items_dn = take(sizeof(moe::Item) * L.max_dn);
   L.ctl = take(sizeof(int32_t) * moe::CTL_WORDS);
   L.h = take(sizeof(uint16_t) * R * moe::D_FF);
   L.y = take(sizeof(float) * R * moe::D_MODEL);
@@ -122,7 +130,6 @@ moe::LayerArgs make_args(const moe_layer* L, const void* x, int T, char* ws, con
   a.n_shared = d.n_shared;
   a.renorm = d.renorm_topk;
   a.fmt = d.wfmt;
-  a.ks = 8;
   a.shared_scale = d.shared_scale;
   a.x = (const uint16_t*)x;
   a.router_w = (const uint16_t*)L->w.router_w;
@@ -143,10 +150,10 @@ moe::LayerArgs make_args(const moe_layer* L, const void* x, int T, char* ws, con
   a.offsets = (int32_t*)(ws + W.offsets);
   a.perm = (int32_t*)(ws + W.perm);
   a.inv_perm = (int32_t*)(ws + W.inv_perm);
-  a.items_up = (uint32_t*)(ws + W.items_up);
-  a.items_dn = (uint32_t*)(ws + W.items_dn);
+  a.items_up = (moe::Item*)(ws + W.items_up);
+  a.items_dn = (moe::Item*)(ws + W.items_dn);
   a.ctl = (int32_t*)(ws + W.ctl);
-  a.h = (_Float16*)(ws + W.h);
+  a.h = (uint16_t*)(ws + W.h);
   a.y = (float*)(ws + W.y);
   a.max_items_up = W.max_up;
   a.max_items_dn = W.max_dn;
@@ -163,29 +170,61 @@ hipError_t copy_async(void* dst, const void* src, size_t bytes, hipStream_t s) {
   return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
 }
 
-// Router, top-k, buckets, both FFN projections; then route copies.
-moe_status run_layer_core(const moe_layer* L, moe::LayerArgs& a, const WsLayout& W, const moe_route_out* route,
-                          hipStream_t s) {
+hipError_t mark(void* const* ev, int i, hipStream_t s) {
+  return ev ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess;
+}
+
+int shared_grid(const moe_layer* L, int T, int chunks) {
+  const int items = moe::bucket_tiles(T) * chunks;
+  const int g = L->n_cu * 4;
+  return items < g ? items : g;
+}
+
+// One layer on stream s: the shared expert forks onto the handle's side stream
+// right away; router, top-k, buckets and the routed gate/up and down run on s;
+// the side stream joins before the combine.  Route copies (except the output)
+// are enqueued before the combine, which in a stack overwrites the layer
+// input.  ev (optional): stage records.
+moe_status run_layer(moe_layer* L, moe::LayerArgs& a, const WsLayout& W, const moe_route_out* route, hipStream_t s,
+                     void* const* ev) {
+  std::lock_guard<std::mutex> lock(L->mu);
   hipError_t e;
-  const bool want_logits = route && route->logits;
-  if (want_logits) a.logits = route->logits;
+  a.write_logits = (route && route->logits) ? 1 : 0;
+  if (a.write_logits) a.logits = route->logits;
+  if (a.n_shared) {
+    if ((e = hipEventRecord(L->fork, s)) != hipSuccess) return hip_fail(e, "fork record");
+    if ((e = hipStreamWaitEvent(L->side, L->fork, 0)) != hipSuccess) return hip_fail(e, "fork wait");
+    if ((e = moe::launch_ffn_up(a, true, shared_grid(L, a.T, moe::N_UP_CHUNKS), L->side)) != hipSuccess)
+      return hip_fail(e, "shared gate/up launch");
+    if ((e = moe::launch_ffn_down(a, true, shared_grid(L, a.T, moe::N_DN_CHUNKS), L->side)) != hipSuccess)
+      return hip_fail(e, "shared down launch");
+    if ((e = hipEventRecord(L->join, L->side)) != hipSuccess) return hip_fail(e, "join record");
+  }
+  if ((e = mark(ev, 0, s)) != hipSuccess) return hip_fail(e, "event record");
   if ((e = moe::launch_router(a, s)) != hipSuccess) return hip_fail(e, "router launch");
-  if ((e = moe::launch_topk(a, want_logits, s)) != hipSuccess) return hip_fail(e, "top-k launch");
+  if ((e = mark(ev, 1, s)) != hipSuccess) return hip_fail(e, "event record");
+  if ((e = moe::launch_topk(a, s)) != hipSuccess) return hip_fail(e, "top-k launch");
+  if ((e = mark(ev, 2, s)) != hipSuccess) return hip_fail(e, "event record");
   if ((e = moe::launch_bucket(a, s)) != hipSuccess) return hip_fail(e, "bucket launch");
-  if ((e = moe::launch_ffn_up(a, ffn_grid(L, W.max_up), s)) != hipSuccess) return hip_fail(e, "gate/up launch");
-  if ((e = moe::launch_ffn_down(a, ffn_grid(L, W.max_dn), s)) != hipSuccess) return hip_fail(e, "down launch");
   if (route) {
     const size_t S = (size_t)a.S;
     const int E = a.E;
-    if ((e = copy_async(route->topk_ids, a.ids, S * 4, s)) != hipSuccess) return hip_fail(e, "route copy");
-    if ((e = copy_async(route->topk_w, a.w, S * 4, s)) != hipSuccess) return hip_fail(e, "route copy");
-    if ((e = copy_async(route->counts, a.counts, (size_t)E * 4, s)) != hipSuccess) return hip_fail(e, "route copy");
-    if ((e = copy_async(route->offsets, a.offsets, (size_t)(E + 1) * 4, s)) != hipSuccess)
-      return hip_fail(e, "route copy");
-    if ((e = copy_async(route->perm, a.perm, S * 4, s)) != hipSuccess) return hip_fail(e, "route copy");
-    if ((e = copy_async(route->x_in, a.x, (size_t)a.T * moe::D_MODEL * 2, s)) != hipSuccess)
+    if ((e = copy_async(route->topk_ids, a.ids, S * 4, s)) != hipSuccess ||
+        (e = copy_async(route->topk_w, a.w, S * 4, s)) != hipSuccess ||
+        (e = copy_async(route->counts, a.counts, (size_t)E * 4, s)) != hipSuccess ||
+        (e = copy_async(route->offsets, a.offsets, (size_t)(E + 1) * 4, s)) != hipSuccess ||
+        (e = copy_async(route->perm, a.perm, S * 4, s)) != hipSuccess ||
+        (e = copy_async(route->x_in, a.x, (size_t)a.T * moe::D_MODEL * 2, s)) != hipSuccess)
       return hip_fail(e, "route copy");
   }
+  if ((e = mark(ev, 3, s)) != hipSuccess) return hip_fail(e, "event record");
+  if ((e = moe::launch_ffn_up(a, false, ffn_grid(L, W.max_up), s)) != hipSuccess) return hip_fail(e, "gate/up launch");
+  if ((e = mark(ev, 4, s)) != hipSuccess) return hip_fail(e, "event record");
+  if ((e = moe::launch_ffn_down(a, false, ffn_grid(L, W.max_dn), s)) != hipSuccess) return hip_fail(e, "down launch");
+  if (a.n_shared && (e = hipStreamWaitEvent(s, L->join, 0)) != hipSuccess) return hip_fail(e, "join wait");
+  if ((e = mark(ev, 5, s)) != hipSuccess) return hip_fail(e, "event record");
+  if ((e = moe::launch_combine(a, s)) != hipSuccess) return hip_fail(e, "combine launch");
+  if ((e = mark(ev, 6, s)) != hipSuccess) return hip_fail(e, "event record");
   return MOE_OK;
 }
 
@@ -230,11 +269,25 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
   L->w = *w;
   L->device = dev;
   L->n_cu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+  L->side = nullptr;
+  L->fork = L->join = nullptr;
+  if ((e = hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking)) != hipSuccess ||
+      (e = hipEventCreateWithFlags(&L->fork, hipEventDisableTiming)) != hipSuccess ||
+      (e = hipEventCreateWithFlags(&L->join, hipEventDisableTiming)) != hipSuccess) {
+    moe_layer_destroy(L);
+    return hip_fail(e, "side stream/event creation");
+  }
   *out = L;
   return MOE_OK;
 }
 
-void moe_layer_destroy(moe_layer* layer) { delete layer; }
+void moe_layer_destroy(moe_layer* layer) {
+  if (!layer) return;
+  if (layer->fork) (void)hipEventDestroy(layer->fork);
+  if (layer->join) (void)hipEventDestroy(layer->join);
+  if (layer->side) (void)hipStreamDestroy(layer->side);
+  delete layer;
+}
 
 moe_status moe_desc_workspace_size(const moe_layer_desc* desc, int32_t T, size_t* bytes) {
   moe_status st = check_desc(desc);
@@ -250,8 +303,9 @@ moe_status moe_layer_workspace_size(const moe_layer* layer, int32_t T, size_t* b
   return moe_desc_workspace_size(&layer->desc, T, bytes);
 }
 
-moe_status moe_layer_forward(const moe_layer* L, const void* x, int32_t T, void* y, const moe_route_out* route,
-                             void* ws, size_t ws_bytes, void* stream) {
+static moe_status layer_forward_impl(const moe_layer* L, const void* x, int32_t T, void* y,
+                                     const moe_route_out* route, void* ws, size_t ws_bytes, void* stream,
+                                     void* const* ev) {
   if (!L) return fail(MOE_ERR_INVALID_ARG, "layer is NULL");
   if (T < 0 || T > L->desc.max_tokens)
     return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, max_tokens=%d]", T, L->desc.max_tokens);
@@ -266,11 +320,26 @@ moe_status moe_layer_forward(const moe_layer* L, const void* x, int32_t T, void*
   if (st != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   moe::LayerArgs a = make_args(L, x, T, (char*)ws, W);
-  if ((st = run_layer_core(L, a, W, route, s)) != MOE_OK) return st;
-  hipError_t e = moe::launch_combine(a, (uint16_t*)y, s);
-  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  a.out = (uint16_t*)y;
+  if ((st = run_layer(const_cast<moe_layer*>(L), a, W, route, s, ev)) != MOE_OK) return st;
+  hipError_t e;
   if (route && (e = copy_async(route->y_out, y, xb, s)) != hipSuccess) return hip_fail(e, "route copy");
   return MOE_OK;
+}
+
+moe_status moe_layer_forward(const moe_layer* L, const void* x, int32_t T, void* y, const moe_route_out* route,
+                             void* ws, size_t ws_bytes, void* stream) {
+  return layer_forward_impl(L, x, T, y, route, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_layer_forward_staged(const moe_layer* L, const void* x, int32_t T, void* y,
+                                    const moe_route_out* route, void* ws, size_t ws_bytes, void* stream,
+                                    void* const* events, int32_t n_events) {
+  if (!events || n_events != MOE_N_STAGE_EVENTS)
+    return fail(MOE_ERR_INVALID_ARG, "events must hold %d hipEvent_t", MOE_N_STAGE_EVENTS);
+  for (int i = 0; i < n_events; ++i)
+    if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "events[%d] is NULL", i);
+  return layer_forward_impl(L, x, T, y, route, ws, ws_bytes, stream, events);
 }
 
 moe_status moe_stack_workspace_size(const moe_layer* const* layers, int32_t n, int32_t T, size_t* bytes) {
@@ -313,11 +382,13 @@ moe_status moe_stack_forward(const moe_layer* const* layers, int32_t n, void* x,
     const WsLayout W = ws_layout(L->desc, T);
     moe::LayerArgs a = make_args(L, xn, T, base, W);
     const moe_route_out* route = routes ? &routes[l] : nullptr;
-    if ((st = run_layer_core(L, a, W, route, s)) != MOE_OK) return st;
     const bool last = (l == n - 1);
-    e = moe::launch_combine_stack(a, r, last ? nullptr : xn, route ? (uint16_t*)route->y_out : nullptr,
-                                  last ? (uint16_t*)x : nullptr, eps, s);
-    if (e != hipSuccess) return hip_fail(e, "stack combine launch");
+    a.r = r;
+    a.eps = eps;
+    a.y_rec = route ? (uint16_t*)route->y_out : nullptr;
+    a.xn_next = last ? nullptr : xn;
+    a.x_final = last ? (uint16_t*)x : nullptr;
+    if ((st = run_layer(const_cast<moe_layer*>(L), a, W, route, s, nullptr)) != MOE_OK) return st;
   }
   return MOE_OK;
 }

@@ -14,29 +14,45 @@ constexpr int MAX_K = 8;       // experts per token
 
 enum Fmt : int { FMT_BF16 = 0, FMT_Q4_1 = 1, FMT_NVFP4 = 2 };
 
-// ---- work items ---------------------------------------------------------------
-// A work item names (expert, token tile, row chunk, path).  Expert value
-// MAX_E means the shared expert.  The bucket kernel writes the lists; the FFN
-// kernels decode them.
-constexpr uint32_t ITEM_MFMA = 0x80000000u;
-__host__ __device__ inline uint32_t make_item(int e, int chunk, int tile, bool mfma) {
-  return (uint32_t)e | ((uint32_t)chunk << 9) | ((uint32_t)tile << 16) | (mfma ? ITEM_MFMA : 0u);
+// ---- work decomposition ---------------------------------------------------------
+// A bucket of m tokens is split into token groups of GV_GROUP (vector path) when
+// m < MFMA_MIN, else into token tiles of MFMA_BN (matrix-core path).  Both paths
+// cover UP_ROWS gate/up row pairs or DN_ROWS down rows per work item; DN_ROWS is
+// also the chunk the combine works on.
+constexpr int GV_GROUP = 4;
+constexpr int MFMA_MIN = 65;
+constexpr int MFMA_BN = 64;
+constexpr int UP_ROWS = 64;
+constexpr int DN_ROWS = 128;
+constexpr int N_UP_CHUNKS = D_FF / UP_ROWS;      // 8
+constexpr int N_DN_CHUNKS = D_MODEL / DN_ROWS;   // 16
+
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+// token groups/tiles of a bucket of m tokens
+__host__ __device__ inline bool bucket_mfma(int m) { return m >= MFMA_MIN; }
+__host__ __device__ inline int bucket_tiles(int m) {
+  return m <= 0 ? 0 : (bucket_mfma(m) ? ceil_div(m, MFMA_BN) : ceil_div(m, GV_GROUP));
 }
-__device__ inline int item_expert(uint32_t it) { return (int)(it & 511u); }
-__device__ inline int item_chunk(uint32_t it) { return (int)((it >> 9) & 127u); }
-__device__ inline int item_tile(uint32_t it) { return (int)((it >> 16) & 0x7FFFu); }
-__device__ inline bool item_mfma(uint32_t it) { return (it & ITEM_MFMA) != 0; }
 
-// GEMV path: buckets of at most GEMV_MAX tokens.  Rows per item.
-constexpr int GEMV_MAX = 4;
-constexpr int UP_GEMV_ROWS = 16;    // gate/up row pairs per GEMV item (4 waves x 4)
-constexpr int DN_GEMV_ROWS = 64;    // down rows per GEMV item (4 waves x 16)
-// MFMA path: token tile and row chunk per item.
-constexpr int MFMA_BN = 64;         // tokens per MFMA item (two 32-token tiles)
-constexpr int UP_MFMA_ROWS = 64;    // gate/up row pairs per MFMA item (4 waves x 16)
-constexpr int DN_MFMA_ROWS = 128;   // down rows per MFMA item (4 waves x 32)
+// Work item (16 bytes, so that a kernel needs one load to start streaming):
+//   head: expert (9 bits; MAX_E = shared) | row chunk << 9 (5 bits) |
+//         token count << 14 (7 bits) | matrix-core path << 31
+//   p0:   first bucket position (routed) or first token (shared); the expert
+//         output rows of the item are p0.. (routed) or S + p0.. (shared)
+//   t01, t23: token ids of a vector-path item (16 bits each)
+struct Item {
+  uint32_t head, p0, t01, t23;
+};
+constexpr uint32_t ITEM_MFMA = 0x80000000u;
+__host__ __device__ inline uint32_t item_head(int e, int chunk, int cnt, bool mfma) {
+  return (uint32_t)e | ((uint32_t)chunk << 9) | ((uint32_t)cnt << 14) | (mfma ? ITEM_MFMA : 0u);
+}
+__device__ inline int item_expert(uint32_t h) { return (int)(h & 511u); }
+__device__ inline int item_chunk(uint32_t h) { return (int)((h >> 9) & 31u); }
+__device__ inline int item_count(uint32_t h) { return (int)((h >> 14) & 127u); }
+__device__ inline bool item_mfma(uint32_t h) { return (h & ITEM_MFMA) != 0; }
 
-// ---- control block and pointers handed to kernels -----------------------------
+// ---- control block ------------------------------------------------------------------
 enum Ctl : int { CTL_N_UP = 0, CTL_N_DN = 1, CTL_WORDS = 16 };
 
 struct QMat {
@@ -47,27 +63,35 @@ struct QMat {
 
 // Everything one layer forward needs on the device (passed by value).
 struct LayerArgs {
-  int T, E, K, S, n_shared, renorm, fmt, ks;  // ks = router K-splits
+  int T, E, K, S, n_shared, renorm, fmt;
   float shared_scale;
   const uint16_t* x;        // bf16 [T][D_MODEL]
   const uint16_t* router_w; // bf16 [E][D_MODEL]
   const float* router_b;    // [E] or null
   QMat gate, up, down, sh_gate, sh_up, sh_down;
   // workspace
-  float* logit_part;        // [ks][T][E]
-  float* logits;            // [T][E] (written only if requested)
+  float* logit_part;        // [8][T][E] router partial sums
+  float* logits;            // [T][E] (written only if write_logits)
+  int write_logits;
   int32_t* ids;             // [T][K]
   float* w;                 // [T][K]
   int32_t* counts;          // [E]
   int32_t* offsets;         // [E+1]
   int32_t* perm;            // [S]
   int32_t* inv_perm;        // [S]
-  uint32_t* items_up;       // work list, gate/up
-  uint32_t* items_dn;       // work list, down
+  Item* items_up;           // routed work list, gate/up
+  Item* items_dn;           // routed work list, down
   int32_t* ctl;             // [CTL_WORDS]
-  _Float16* h;              // [S + n_shared*T][D_FF] SwiGLU output, fp16
-  float* y;                 // [S + n_shared*T][D_MODEL] expert outputs, fp32
+  uint16_t* h;              // [S + n_shared*T][D_FF] SwiGLU output (fp16 or bf16 bits)
+  float* y;                 // [S + n_shared*T][D_MODEL] expert outputs
   int max_items_up, max_items_dn;
+  // combine targets
+  uint16_t* out;            // bf16 [T][D_MODEL] layer output (single layer), or null
+  float* r;                 // fp32 [T][D_MODEL] residual (stack), or null
+  uint16_t* y_rec;          // bf16 [T][D_MODEL] record of the layer output (stack), or null
+  uint16_t* xn_next;        // bf16 [T][D_MODEL] next layer input (stack), or null
+  uint16_t* x_final;        // bf16 [T][D_MODEL] final output (stack, last layer), or null
+  float eps;
 };
 
 // ---- small helpers ---------------------------------------------------------------
@@ -83,20 +107,15 @@ __device__ inline uint16_t f32_to_bf16(float f) {
 
 __device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
-constexpr int WAVE = 64;
-
 }  // namespace moe
 
 // Host-side launchers (defined in the .hip files, called by the ABI layer).
 namespace moe {
 hipError_t launch_router(const LayerArgs& a, hipStream_t s);
-hipError_t launch_topk(const LayerArgs& a, bool write_logits, hipStream_t s);
+hipError_t launch_topk(const LayerArgs& a, hipStream_t s);
 hipError_t launch_bucket(const LayerArgs& a, hipStream_t s);
-hipError_t launch_ffn_up(const LayerArgs& a, int grid, hipStream_t s);
-hipError_t launch_ffn_down(const LayerArgs& a, int grid, hipStream_t s);
-hipError_t launch_combine(const LayerArgs& a, uint16_t* out_bf16, hipStream_t s);
-// stack glue: r (fp32 [T][D]) and xn (bf16 [T][D])
+hipError_t launch_combine(const LayerArgs& a, hipStream_t s);
+hipError_t launch_ffn_up(const LayerArgs& a, bool shared, int grid, hipStream_t s);
+hipError_t launch_ffn_down(const LayerArgs& a, bool shared, int grid, hipStream_t s);
 hipError_t launch_stack_init(const uint16_t* x, float* r, uint16_t* xn, int T, float eps, hipStream_t s);
-hipError_t launch_combine_stack(const LayerArgs& a, float* r, uint16_t* xn_next, uint16_t* y_rec, uint16_t* x_final,
-                                float eps, hipStream_t s);
 }  // namespace moe

@@ -1,17 +1,28 @@
-// Expert FFN: gate/up projection with fused SwiGLU, and down projection, over
-// the expert buckets.  Both kernels are persistent: each workgroup walks the
-// device-side work list written by the bucket kernel.  Items of small buckets
-// (<= GEMV_MAX tokens) run on the vector ALUs, streaming packed weight rows
-// with 16-byte loads and decoding them in registers; items of large buckets
-// run on the matrix cores, decoding a weight tile into LDS once and
-// multiplying it with every token tile.
+// Expert FFN over the buckets: gate/up projection with fused SwiGLU, down
+// projection with the weighted combine fused into its epilogue, and the
+// residual/RMSNorm glue of stacked layers.
 //
 // The review "Recursive Flint 40B-A2.5B" (orcarouter.ai), section "The
 // architecture is an argument about memory bandwidth", argues that decoding
-// this model is a weight-movement problem; the small-bucket path is therefore
-// built to move each touched weight byte from HBM exactly once, with the
-// arithmetic kept under the HBM time.  Expert form (SwiGLU, width 512) and
-// the 4-bit layouts are the readings documented in include/moe_ffn.h.
+// this model is a weight-movement problem: each token touches 6 routed experts
+// and the shared one out of 257 per layer.  So the work is organised around
+// streaming each touched expert's packed weights from HBM once:
+//   * buckets below MFMA_MIN tokens run on the vector ALUs in token groups of
+//     up to 4 (two per pass): a lane owns one 32-element chunk of a weight row
+//     (16 bytes of 4-bit codes), decodes it in registers to fp16 pairs and uses
+//     v_dot2; each wave keeps a ring of row loads in flight and sums across
+//     lanes with permlane swaps and DPP moves;
+//   * buckets of MFMA_MIN or more tokens run on the matrix cores: a weight
+//     tile is decoded into LDS once per 64-token tile (v_mfma 32x32x16), with
+//     the next K-chunk prefetched into registers during the MFMAs.
+// Both kernels are persistent and walk device-side work lists, so no host
+// synchronisation is needed.  The shared expert does not depend on routing and
+// runs as its own launches (on a second stream, overlapping the router).
+//
+// Combine: a separate kernel sums, per token, the K weighted expert rows in
+// the fixed order j = 0..K-1 and the shared expert row, and rounds once to
+// bf16 (in a stack it also updates the fp32 residual and writes the next
+// layer's RMSNorm input).
 #include "common.hpp"
 
 namespace moe {
@@ -23,13 +34,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Streaming 16-byte load of weight bytes that are read once (non-temporal hint).
-__device__ inline u32x4 ld_stream(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
-__device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-
-// E2M1 pair (byte B of w) -> fp16 pair, unscaled.
-template <int B> __device__ inline uint32_t fp4x2_to_f16x2(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, B));
+// 16-byte loads: streaming (read once, non-temporal hint) or cached.
+template <bool NT> __device__ inline u32x4 ld16(const void* p) {
+  if (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return *reinterpret_cast<const u32x4*>(p);
+}
+template <bool NT> __device__ inline uint32_t ld4(const void* p) {
+  if (NT) return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  return *reinterpret_cast<const uint32_t*>(p);
+}
+template <bool NT> __device__ inline uint32_t ld2(const void* p) {
+  if (NT) return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+  return *reinterpret_cast<const uint16_t*>(p);
 }
 
 constexpr uint32_t MAGIC = 0x64006400u;  // fp16 pair (1024, 1024): ORing a nibble into the
@@ -46,9 +62,15 @@ __device__ inline float dot2b(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(b), c, false);
 }
 
+// E2M1 pair (byte B of w) -> fp16 pair, unscaled (exact).
+template <int B> __device__ inline uint32_t fp4x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, B));
+}
+
 // two bf16 (lo, hi halves of v) -> packed fp16 pair (exact for normal-range values)
 __device__ inline uint32_t bf16x2_to_f16x2(uint32_t v) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v << 16), __uint_as_float(v & 0xFFFF0000u)));
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v << 16), __uint_as_float(v & 0xFFFF0000u)));
 }
 
 // natural pairs N0=(e0,e1) N1=(e2,e3) N2=(e4,e5) N3=(e6,e7) -> the order the
@@ -63,36 +85,34 @@ __device__ inline void q4_order(uint32_t n0, uint32_t n1, uint32_t n2, uint32_t 
 __device__ inline float f16lo(uint32_t v) { return (float)as_f16x2(v)[0]; }
 __device__ inline float f16hi(uint32_t v) { return (float)as_f16x2(v)[1]; }
 
-// Saturating fp32 -> fp16 pair (the SwiGLU output is stored as fp16).
-__device__ inline uint32_t pack_h16(float a, float b) {
-  a = fminf(fmaxf(a, -65504.f), 65504.f);
-  b = fminf(fmaxf(b, -65504.f), 65504.f);
-  f16x2 r = {(_Float16)a, (_Float16)b};
-  return as_u32(r);
+// fp32 -> stored SwiGLU element: fp16 (saturated) for the 4-bit formats, bf16 otherwise.
+template <int FMT> __device__ inline uint16_t h_store(float v);
+template <> __device__ inline uint16_t h_store<FMT_Q4_1>(float v) {
+  v = fminf(fmaxf(v, -65504.f), 65504.f);
+  return __builtin_bit_cast(uint16_t, (_Float16)v);
 }
-__device__ inline uint32_t pack_b16(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-}
+template <> __device__ inline uint16_t h_store<FMT_NVFP4>(float v) { return h_store<FMT_Q4_1>(v); }
+template <> __device__ inline uint16_t h_store<FMT_BF16>(float v) { return f32_to_bf16(v); }
+
+// Operand precision of the expert GEMMs: fp16 for the 4-bit formats (their
+// decoded values are exact in fp16), bf16 for bf16 weights.
+template <int FMT> constexpr bool OPER_F16 = FMT != FMT_BF16;
 
 // ======================================================================================
-// Format traits for the vector (GEMV) path.  Each lane owns one 32-element chunk
-// of a row: 16 bytes of 4-bit codes (or 64 bytes of bf16).
+// Per-format chunk of a weight row: 32 consecutive elements owned by one lane.
 // ======================================================================================
 template <int FMT> struct GV;
 
 template <> struct GV<FMT_Q4_1> {
-  // raw chunk: 16 B codes + {d, m}
-  struct Raw { u32x4 c; uint32_t dm; };
-  // activations for one chunk: fp16 pairs in nibble order + even/odd sums
-  struct X { uint32_t p[16]; float se, so; };
-  static __device__ Raw load(const QMat& q, size_t row, int chunk, int cols) {
+  struct Raw { u32x4 c; uint32_t dm; };                // 16 B codes + fp16 {d, m}
+  struct X { uint32_t p[16]; float se, so; };          // fp16 pairs in nibble order + even/odd sums
+  template <bool NT> static __device__ Raw load(const QMat& q, size_t row, int chunk, int cols) {
     Raw r;
-    r.c = ld_stream(q.codes + row * (cols / 2) + 16 * chunk);
-    r.dm = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(q.scales) + row * (cols / 32) + chunk);
+    r.c = ld16<NT>(q.codes + row * (cols / 2) + 16 * chunk);
+    r.dm = ld4<NT>(reinterpret_cast<const uint32_t*>(q.scales) + row * (cols / 32) + chunk);
     return r;
   }
-  // src: 16 dwords of fp16 pairs, natural order
-  static __device__ void prep(X& x, const uint32_t* src) {
+  static __device__ void prep(X& x, const uint32_t* src) {  // src: 16 fp16 pairs, natural order
     float se = 0.f, so = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -103,116 +123,136 @@ template <> struct GV<FMT_Q4_1> {
     x.se = se;
     x.so = so;
   }
-  struct U { uint32_t A[4], B[4], C[4], D[4]; float c1, c2, c3, c4; };
-  static __device__ void unpack(U& u, const Raw& r, float /*ts*/) {
-    const uint32_t w[4] = {r.c[0], r.c[1], r.c[2], r.c[3]};
+  // out[t] = sum_i w_i x_t,i over the chunk.  With the nibbles ORed into the
+  // mantissa of 1024: lo = sum_even (1024+q) x, hi = sum_odd (1024+16q) x, so
+  // the block dot d*sum q x + m*sum x = d lo + (d/16) hi + (m-1024d) se + (m-64d) so.
+  template <int M> static __device__ void dot(const Raw& r, const X* x, float* out, float) {
+    float lo[M], hi[M];
+#pragma unroll
+    for (int t = 0; t < M; ++t) { lo[t] = 0.f; hi[t] = 0.f; }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t w8 = w[j] >> 8;
-      u.A[j] = (w[j] & 0x000F000Fu) | MAGIC;   // (1024+q0, 1024+q4)
-      u.B[j] = (w[j] & 0x00F000F0u) | MAGIC;   // (1024+16q1, 1024+16q5)
-      u.C[j] = (w8 & 0x000F000Fu) | MAGIC;     // (1024+q2, 1024+q6)
-      u.D[j] = (w8 & 0x00F000F0u) | MAGIC;     // (1024+16q3, 1024+16q7)
+      const uint32_t w = r.c[j], w8 = w >> 8;
+      const uint32_t A = (w & 0x000F000Fu) | MAGIC, B = (w & 0x00F000F0u) | MAGIC;
+      const uint32_t C = (w8 & 0x000F000Fu) | MAGIC, D = (w8 & 0x00F000F0u) | MAGIC;
+#pragma unroll
+      for (int t = 0; t < M; ++t) {
+        lo[t] = dot2h(A, x[t].p[4 * j + 0], lo[t]);
+        hi[t] = dot2h(B, x[t].p[4 * j + 1], hi[t]);
+        lo[t] = dot2h(C, x[t].p[4 * j + 2], lo[t]);
+        hi[t] = dot2h(D, x[t].p[4 * j + 3], hi[t]);
+      }
     }
     const float d = f16lo(r.dm), m = f16hi(r.dm);
-    // block dot = d*lo + (d/16)*hi + (m - 1024 d)*sum_even + (m - 64 d)*sum_odd
-    u.c1 = d;
-    u.c2 = d * 0.0625f;
-    u.c3 = m - 1024.f * d;
-    u.c4 = m - 64.f * d;
+    const float c2 = d * 0.0625f, c3 = m - 1024.f * d, c4 = m - 64.f * d;
+#pragma unroll
+    for (int t = 0; t < M; ++t) out[t] = d * lo[t] + c2 * hi[t] + c3 * x[t].se + c4 * x[t].so;
   }
-  static __device__ float dot(const U& u, const X& x) {
-    float lo = 0.f, hi = 0.f;
+  // 32 decoded weights as 16 fp16 pairs in nibble order (matrix-core path):
+  // fp16(d*q + m), rounded once.
+  static __device__ void decode(const Raw& r, uint32_t* o) {
+    const f16x2 d2 = {as_f16x2(r.dm)[0], as_f16x2(r.dm)[0]};
+    const f16x2 m2 = {as_f16x2(r.dm)[1], as_f16x2(r.dm)[1]};
+    const f16x2 off = {(_Float16)(-1024.f), (_Float16)(-1024.f)};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      lo = dot2h(u.A[j], x.p[4 * j + 0], lo);
-      hi = dot2h(u.B[j], x.p[4 * j + 1], hi);
-      lo = dot2h(u.C[j], x.p[4 * j + 2], lo);
-      hi = dot2h(u.D[j], x.p[4 * j + 3], hi);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t bits = ((r.c[j] >> (4 * s)) & 0x000F000Fu) | MAGIC;  // (q_s, q_{s+4})
+        const f16x2 qv = as_f16x2(bits) + off;                             // exact small integers
+        o[4 * j + s] = as_u32(__builtin_elementwise_fma(qv, d2, m2));
+      }
     }
-    return u.c1 * lo + u.c2 * hi + u.c3 * x.se + u.c4 * x.so;
   }
 };
 
 template <> struct GV<FMT_NVFP4> {
-  struct Raw { u32x4 c; uint32_t s; };
-  struct X { uint32_t p[16]; };
-  static __device__ Raw load(const QMat& q, size_t row, int chunk, int cols) {
+  struct Raw { u32x4 c; uint32_t s; };                 // 16 B codes + 2 E4M3 block scales
+  struct X { uint32_t p[16]; };                        // fp16 pairs, natural order
+  template <bool NT> static __device__ Raw load(const QMat& q, size_t row, int chunk, int cols) {
     Raw r;
-    r.c = ld_stream(q.codes + row * (cols / 2) + 16 * chunk);
-    r.s = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(q.scales) +
-                                                                        row * (cols / 16)) + chunk);
+    r.c = ld16<NT>(q.codes + row * (cols / 2) + 16 * chunk);
+    r.s = ld2<NT>(reinterpret_cast<const uint8_t*>(q.scales) + row * (cols / 16) + 2 * chunk);
     return r;
   }
   static __device__ void prep(X& x, const uint32_t* src) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) x.p[i] = src[i];
   }
-  struct U { uint32_t P[16]; float s0, s1; };
-  static __device__ void unpack(U& u, const Raw& r, float ts) {
-    const uint32_t w[4] = {r.c[0], r.c[1], r.c[2], r.c[3]};
+  template <int M> static __device__ void dot(const Raw& r, const X* x, float* out, float ts) {
+    float a0[M], a1[M];
+#pragma unroll
+    for (int t = 0; t < M; ++t) { a0[t] = 0.f; a1[t] = 0.f; }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      u.P[4 * j + 0] = fp4x2_to_f16x2<0>(w[j]);
-      u.P[4 * j + 1] = fp4x2_to_f16x2<1>(w[j]);
-      u.P[4 * j + 2] = fp4x2_to_f16x2<2>(w[j]);
-      u.P[4 * j + 3] = fp4x2_to_f16x2<3>(w[j]);
+      const uint32_t w = r.c[j];
+      const uint32_t P0 = fp4x2_to_f16x2<0>(w), P1 = fp4x2_to_f16x2<1>(w);
+      const uint32_t P2 = fp4x2_to_f16x2<2>(w), P3 = fp4x2_to_f16x2<3>(w);
+#pragma unroll
+      for (int t = 0; t < M; ++t) {
+        float& acc = (j < 2) ? a0[t] : a1[t];
+        acc = dot2h(P0, x[t].p[4 * j + 0], acc);
+        acc = dot2h(P1, x[t].p[4 * j + 1], acc);
+        acc = dot2h(P2, x[t].p[4 * j + 2], acc);
+        acc = dot2h(P3, x[t].p[4 * j + 3], acc);
+      }
     }
-    u.s0 = __builtin_amdgcn_cvt_f32_fp8(r.s, 0) * ts;
-    u.s1 = __builtin_amdgcn_cvt_f32_fp8(r.s, 1) * ts;
+    const float s0 = __builtin_amdgcn_cvt_f32_fp8(r.s, 0) * ts;
+    const float s1 = __builtin_amdgcn_cvt_f32_fp8(r.s, 1) * ts;
+#pragma unroll
+    for (int t = 0; t < M; ++t) out[t] = s0 * a0[t] + s1 * a1[t];
   }
-  static __device__ float dot(const U& u, const X& x) {
-    float a0 = 0.f, a1 = 0.f;
+  // E2M1 * E4M3 is exact in fp16; the per-matrix scale is applied after the MFMA.
+  static __device__ void decode(const Raw& r, uint32_t* o) {
+    const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8(r.s, 0);
+    const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8(r.s, 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a0 = dot2h(u.P[i], x.p[i], a0);
-#pragma unroll
-    for (int i = 8; i < 16; ++i) a1 = dot2h(u.P[i], x.p[i], a1);
-    return u.s0 * a0 + u.s1 * a1;
+    for (int j = 0; j < 4; ++j) {
+      const f16x2 s = (j < 2) ? f16x2{s0, s0} : f16x2{s1, s1};
+      o[4 * j + 0] = as_u32(as_f16x2(fp4x2_to_f16x2<0>(r.c[j])) * s);
+      o[4 * j + 1] = as_u32(as_f16x2(fp4x2_to_f16x2<1>(r.c[j])) * s);
+      o[4 * j + 2] = as_u32(as_f16x2(fp4x2_to_f16x2<2>(r.c[j])) * s);
+      o[4 * j + 3] = as_u32(as_f16x2(fp4x2_to_f16x2<3>(r.c[j])) * s);
+    }
   }
 };
 
 template <> struct GV<FMT_BF16> {
-  struct Raw { u32x4 c[4]; };
-  struct X { uint32_t p[16]; };
-  static __device__ Raw load(const QMat& q, size_t row, int chunk, int cols) {
+  struct Raw { u32x4 c[4]; };                          // 64 B of bf16
+  struct X { uint32_t p[16]; };                        // bf16 pairs, natural order
+  template <bool NT> static __device__ Raw load(const QMat& q, size_t row, int chunk, int cols) {
     Raw r;
     const uint8_t* p = q.codes + row * cols * 2 + 64 * chunk;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.c[i] = ld_stream(p + 16 * i);
+    for (int i = 0; i < 4; ++i) r.c[i] = ld16<NT>(p + 16 * i);
     return r;
   }
   static __device__ void prep(X& x, const uint32_t* src) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) x.p[i] = src[i];
   }
-  struct U { uint32_t P[16]; };
-  static __device__ void unpack(U& u, const Raw& r, float) {
+  template <int M> static __device__ void dot(const Raw& r, const X* x, float* out, float) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u.P[4 * i] = r.c[i][0]; u.P[4 * i + 1] = r.c[i][1]; u.P[4 * i + 2] = r.c[i][2]; u.P[4 * i + 3] = r.c[i][3];
+    for (int t = 0; t < M; ++t) {
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) a = dot2b(r.c[i >> 2][i & 3], x[t].p[i], a);
+      out[t] = a;
     }
   }
-  static __device__ float dot(const U& u, const X& x) {
-    float a = 0.f;
+  static __device__ void decode(const Raw& r, uint32_t* o) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) a = dot2b(u.P[i], x.p[i], a);
-    return a;
+    for (int i = 0; i < 16; ++i) o[i] = r.c[i >> 2][i & 3];
   }
 };
 
-// Operand precision of the expert GEMMs: fp16 for the 4-bit formats (their
-// decoded values are exact in fp16), bf16 for bf16 weights.
-template <int FMT> constexpr bool OPER_F16 = FMT != FMT_BF16;
-
-// 32 activation elements of one lane as 16 dwords of operand pairs, natural
-// order.  src points at bf16 (x) or at the stored SwiGLU output (fp16 for the
-// 4-bit formats, bf16 otherwise).
+// 32 activation elements of one lane as 16 operand pairs, natural order.  src
+// points at bf16 (x) or at the stored SwiGLU output (already operand typed).
 template <int FMT> __device__ inline void load_act(uint32_t* d, const uint16_t* src, bool src_bf16) {
-  const uint4* p = reinterpret_cast<const uint4*>(src);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint4 v = p[i];
-    d[4 * i] = v.x; d[4 * i + 1] = v.y; d[4 * i + 2] = v.z; d[4 * i + 3] = v.w;
+    const u32x4 v = ld16<false>(src + 8 * i);
+    d[4 * i] = v[0]; d[4 * i + 1] = v[1]; d[4 * i + 2] = v[2]; d[4 * i + 3] = v[3];
   }
   if (OPER_F16<FMT> && src_bf16) {
 #pragma unroll
@@ -220,37 +260,50 @@ template <int FMT> __device__ inline void load_act(uint32_t* d, const uint16_t* 
   }
 }
 
-// Transposing wave reduction: P partials per lane, summed over groups of G
-// lanes (xor masks G/2 .. 1).  While more than one value is left, each step
-// halves the count: lanes with the mask bit clear keep the first half, lanes
-// with it set the second half.  Afterwards v[0] of a lane holds the total of
-// index idx(lane) = sum over halving steps s of bit(lane, G>>(s+1)) * P>>(s+1).
-template <int P, int G>
+// Lane exchange for reduction step `m` (partner lane = lane ^ m, except m = 4
+// which pairs lane i with 7 - i inside each group of 8).  Steps 32 and 16 use
+// the gfx950 permlane swaps: swap(a, b).x + .y holds a's pair sum in the lanes
+// whose bit m is clear and b's pair sum in the others.  Steps below 16 use DPP.
+template <int M> __device__ inline float dpp_partner(float v) {
+  constexpr int ctrl = (M == 8) ? 0x128 : (M == 4) ? 0x141 : (M == 2) ? 0x4E : 0xB1;  // ror8, half-mirror, quad perms
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, false));
+}
+template <int M> __device__ inline float halve_step(float a, float b) {
+  if constexpr (M == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    const bool hi = (threadIdx.x & M) != 0;
+    const float sa = a + dpp_partner<M>(a), sb = b + dpp_partner<M>(b);
+    return hi ? sb : sa;
+  }
+}
+template <int M> __device__ inline float plain_step(float a) { return halve_step<M>(a, a); }
+
+// Transposing reduction: P partials per lane, summed over groups of G lanes
+// (steps G/2 .. 1).  While more than one value is left, each step halves the
+// count: lanes with bit m clear keep the first half, the others the second.
+// Afterwards v[0] of a lane holds the total of index
+// idx(lane) = sum over halving steps s of bit(lane, G >> (s+1)) * P >> (s+1).
+template <int P, int G, int M = G / 2>
 __device__ inline void xreduce(float* v) {
-  const int lane = threadIdx.x & 63;
-  int n = P;
+  if constexpr (M >= 1) {
+    if constexpr (P > 1) {
 #pragma unroll
-  for (int m = G / 2; m >= 1; m >>= 1) {
-    if (n > 1) {
-      const bool hi = (lane & m) != 0;
-      const int h = n / 2;
-#pragma unroll
-      for (int i = 0; i < P / 2; ++i) {
-        if (i < h) {
-          const float keep = hi ? v[i + h] : v[i];
-          const float send = hi ? v[i] : v[i + h];
-          v[i] = keep + __shfl_xor(send, m);
-        }
-      }
-      n = h;
+      for (int i = 0; i < P / 2; ++i) v[i] = halve_step<M>(v[i], v[i + P / 2]);
+      xreduce<P / 2, G, M / 2>(v);
     } else {
-      v[0] += __shfl_xor(v[0], m);
+      v[0] = plain_step<M>(v[0]);
+      xreduce<1, G, M / 2>(v);
     }
   }
 }
 
 // Index a lane holds after xreduce<P, G>, and whether it is the lane of its
-// group that should write it (the bits of the non-halving steps are zero).
+// group that writes it (the bits of the non-halving steps are zero).
 template <int P, int G>
 __device__ inline int xreduce_index(int lane, bool& writer) {
   int idx = 0, n = P, plain_mask = 0;
@@ -267,53 +320,84 @@ __device__ inline int xreduce_index(int lane, bool& writer) {
   return idx;
 }
 
-// Tokens of an item: bucket positions p0 .. p0+cnt-1 of a routed expert (token
-// = perm[p] / K, output row p), or tokens t0 .. t0+cnt-1 for the shared expert
-// (output row S + t).
+// Tokens of an item: bucket positions p0 .. p0+cnt-1 of a routed expert
+// (expert-output row p), or tokens p0 .. p0+cnt-1 of the shared expert
+// (expert-output row S + t).  Vector-path items carry their token ids.
 struct ItemTok {
   int p0, cnt;
-  bool shared;
+  bool shared, mfma;
+  int tok[GV_GROUP];
 };
 
-__device__ inline ItemTok item_tokens(const LayerArgs& a, int e, int tile) {
+__device__ inline ItemTok item_tokens(const Item& item, bool shared) {
   ItemTok r;
-  if (e >= a.E) {
-    r.shared = true;
-    r.p0 = tile * MFMA_BN;
-    r.cnt = a.T - r.p0;
-  } else {
-    r.shared = false;
-    const int c = a.counts[e];
-    r.p0 = a.offsets[e] + tile * MFMA_BN;
-    r.cnt = c - tile * MFMA_BN;
-  }
-  if (r.cnt > MFMA_BN) r.cnt = MFMA_BN;
+  r.shared = shared;
+  r.mfma = item_mfma(item.head);
+  r.p0 = (int)item.p0;
+  r.cnt = item_count(item.head);
+  r.tok[0] = (int)(item.t01 & 0xFFFFu);
+  r.tok[1] = (int)(item.t01 >> 16);
+  r.tok[2] = (int)(item.t23 & 0xFFFFu);
+  r.tok[3] = (int)(item.t23 >> 16);
   return r;
 }
+// token of entry i: shared -> p0 + i; vector path -> carried id; matrix path -> perm
 __device__ inline int tok_of(const LayerArgs& a, const ItemTok& it, int i) {
-  return it.shared ? it.p0 + i : a.perm[it.p0 + i] / a.K;
+  if (it.shared) return it.p0 + i;
+  if (!it.mfma) return it.tok[i];
+  return a.perm[it.p0 + i] / a.K;
 }
 __device__ inline int row_of(const LayerArgs& a, const ItemTok& it, int i) {
   return it.shared ? a.S + it.p0 + i : it.p0 + i;
 }
 
+// Shared-expert items are implicit: item i -> tile i / chunks, chunk i % chunks.
+__device__ inline Item shared_item(int T, int E, int i, int chunks) {
+  const bool mf = bucket_mfma(T);
+  const int per = mf ? MFMA_BN : GV_GROUP;
+  const int tile = i / chunks;
+  Item it;
+  it.p0 = (uint32_t)(tile * per);
+  it.head = item_head(E, i % chunks, min(per, T - tile * per), mf);
+  it.t01 = it.p0 | ((it.p0 + 1) << 16);
+  it.t23 = (it.p0 + 2) | ((it.p0 + 3) << 16);
+  return it;
+}
+__device__ inline int shared_items(int T, int chunks) { return bucket_tiles(T) * chunks; }
+
 // ======================================================================================
-// GEMV items
+// Vector-path items
 // ======================================================================================
 
-// gate/up + SwiGLU: each wave handles NR row pairs; a lane owns 32-element chunk
-// `lane` of the 2048-long rows.
-template <int FMT, int M, int NR>
-__device__ void gemv_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int mat, const ItemTok& it, int n0) {
+// Rows in flight per wave (a ring of register buffers): one row pair (up) or
+// one 4-row group (down) per slot.
+template <int FMT> constexpr int UP_RING = (FMT == FMT_BF16) ? 2 : 4;
+template <int FMT> constexpr int DN_RING = (FMT == FMT_BF16) ? 4 : 8;
+
+// gate/up + SwiGLU for NRW row pairs from n0 of one wave; lane owns chunk
+// `lane` of the 2048-long rows.  A ring of D row pairs is in flight: the
+// first D are issued before the activations are read; each step consumes one
+// slot and then refills that same slot (so no register copies and no full
+// drain of the load counter happen between steps); the last D steps only drain.
+template <int FMT, int M, int NRW>
+__device__ void gemv_up_wave(const LayerArgs& a, const QMat& G, const QMat& Uq, int mat, const ItemTok& it, int n0) {
   using F = GV<FMT>;
+  constexpr int D = UP_RING<FMT>;
+  static_assert(NRW % D == 0 && NRW >= D, "ring must divide the rows of a wave");
   const int lane = threadIdx.x & 63;
+  const size_t rbase = (size_t)mat * D_FF + n0;
+  typename F::Raw rg[D], ru[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    rg[i] = F::template load<true>(G, rbase + i, lane, D_MODEL);
+    ru[i] = F::template load<true>(Uq, rbase + i, lane, D_MODEL);
+  }
   typename F::X x[M];
 #pragma unroll
   for (int t = 0; t < M; ++t) {
     uint32_t src[16];
     if (t < it.cnt) {
-      const int tok = tok_of(a, it, t);
-      load_act<FMT>(src, a.x + (size_t)tok * D_MODEL + 32 * lane, true);
+      load_act<FMT>(src, a.x + (size_t)tok_of(a, it, t) * D_MODEL + 32 * lane, true);
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) src[i] = 0u;
@@ -322,56 +406,52 @@ __device__ void gemv_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int m
   }
   const float tsg = (FMT == FMT_NVFP4) ? G.ts[mat] : 1.f;
   const float tsu = (FMT == FMT_NVFP4) ? Uq.ts[mat] : 1.f;
-  typename F::Raw rg[NR], ru[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const size_t row = (size_t)mat * D_FF + n0 + r;
-    rg[r] = F::load(G, row, lane, D_MODEL);
-    ru[r] = F::load(Uq, row, lane, D_MODEL);
-  }
-  constexpr int P = 2 * NR * M;
-  float v[P];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    typename F::U ug, uu;
-    F::unpack(ug, rg[r], tsg);
-    F::unpack(uu, ru[r], tsu);
-#pragma unroll
-    for (int t = 0; t < M; ++t) {
-      v[r * M + t] = F::dot(ug, x[t]);
-      v[NR * M + r * M + t] = F::dot(uu, x[t]);
-    }
-  }
-  xreduce<P, 64>(v);
-  // lanes < 32 hold gate sums, lane+32 the matching up sums
-  const float u = __shfl_xor(v[0], 32);
   bool wr;
-  const int idx = xreduce_index<P, 64>(lane, wr);
-  if (lane < 32 && wr) {
-    const int r = idx / M, t = idx % M;
-    if (t < it.cnt) {
-      const float h = silu_mul(v[0], u);
-      uint16_t* hp = reinterpret_cast<uint16_t*>(a.h) + (size_t)row_of(a, it, t) * D_FF + n0 + r;
-      if (OPER_F16<FMT>) *hp = (uint16_t)(pack_h16(h, 0.f) & 0xFFFFu);
-      else *hp = f32_to_bf16(h);
+  const int idx = xreduce_index<2 * M, 64>(lane, wr);
+  const int my_t = idx % M;  // lanes < 32 hold gate sums of token my_t, lane + 32 the up sums
+  uint16_t* hrow = a.h + (size_t)row_of(a, it, my_t < it.cnt ? my_t : 0) * D_FF + n0;
+  const bool writer = lane < 32 && wr && my_t < it.cnt;
+  auto step = [&](int i, int r) {
+    float v[2 * M];
+    F::template dot<M>(rg[i], x, v, tsg);
+    F::template dot<M>(ru[i], x, v + M, tsu);
+    xreduce<2 * M, 64>(v);
+    const float u = __shfl_xor(v[0], 32);
+    if (writer) hrow[r] = h_store<FMT>(silu_mul(v[0], u));
+  };
+#pragma unroll 1
+  for (int b = 0; b < NRW - D; b += D) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      step(i, b + i);
+      rg[i] = F::template load<true>(G, rbase + b + i + D, lane, D_MODEL);
+      ru[i] = F::template load<true>(Uq, rbase + b + i + D, lane, D_MODEL);
     }
   }
+#pragma unroll
+  for (int i = 0; i < D; ++i) step(i, NRW - D + i);
 }
 
-// down: rows of 512; 16 lanes per row, a wave covers 4 rows per load and
-// NRG such groups; lane owns chunk (lane & 15) of its row.
-template <int FMT, int M, int NRG>
-__device__ void gemv_down(const LayerArgs& a, const QMat& D, int mat, const ItemTok& it, int r0) {
+// down rows r0 .. r0+4*NG-1 of one wave: 16 lanes per 512-long row, 4 rows per
+// load (one ring slot); lane owns chunk (lane & 15) of its row.  Same ring
+// discipline as the gate/up wave.
+template <int FMT, int M, int NG>
+__device__ void gemv_down_wave(const LayerArgs& a, const QMat& D, int mat, const ItemTok& it, int r0) {
   using F = GV<FMT>;
+  constexpr int R = DN_RING<FMT> < NG ? DN_RING<FMT> : NG;
+  static_assert(NG % R == 0, "ring must divide the row groups of a wave");
   const int lane = threadIdx.x & 63;
   const int chunk = lane & 15, rsub = lane >> 4;
+  const size_t rbase = (size_t)mat * D_MODEL + r0 + rsub;
+  typename F::Raw ring[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) ring[i] = F::template load<true>(D, rbase + 4 * i, chunk, D_FF);
   typename F::X x[M];
 #pragma unroll
   for (int t = 0; t < M; ++t) {
     uint32_t src[16];
     if (t < it.cnt) {
-      load_act<FMT>(src, reinterpret_cast<const uint16_t*>(a.h) + (size_t)row_of(a, it, t) * D_FF + 32 * chunk,
-                    false);
+      load_act<FMT>(src, a.h + (size_t)row_of(a, it, t) * D_FF + 32 * chunk, false);
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) src[i] = 0u;
@@ -379,93 +459,43 @@ __device__ void gemv_down(const LayerArgs& a, const QMat& D, int mat, const Item
     F::prep(x[t], src);
   }
   const float ts = (FMT == FMT_NVFP4) ? D.ts[mat] : 1.f;
-  typename F::Raw rr[NRG];
-#pragma unroll
-  for (int g = 0; g < NRG; ++g) rr[g] = F::load(D, (size_t)mat * D_MODEL + r0 + 4 * g + rsub, chunk, D_FF);
-  constexpr int P = NRG * M;
-  float v[P];
-#pragma unroll
-  for (int g = 0; g < NRG; ++g) {
-    typename F::U u;
-    F::unpack(u, rr[g], ts);
-#pragma unroll
-    for (int t = 0; t < M; ++t) v[g * M + t] = F::dot(u, x[t]);
-  }
-  xreduce<P, 16>(v);
   bool wr;
-  const int idx = xreduce_index<P, 16>(lane & 15, wr);
-  if (wr) {
-    const int g = idx / M, t = idx % M;
-    if (t < it.cnt) a.y[(size_t)row_of(a, it, t) * D_MODEL + r0 + 4 * g + rsub] = v[0];
+  const int my_t = xreduce_index<M, 16>(lane & 15, wr) % M;
+  float* yrow = a.y + (size_t)row_of(a, it, my_t < it.cnt ? my_t : 0) * D_MODEL + r0 + rsub;
+  const bool writer = wr && my_t < it.cnt;
+  auto step = [&](int i, int g) {
+    float v[M];
+    F::template dot<M>(ring[i], x, v, ts);
+    xreduce<M, 16>(v);
+    if (writer) yrow[4 * g] = v[0];
+  };
+#pragma unroll 1
+  for (int b = 0; b < NG - R; b += R) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      step(i, b + i);
+      ring[i] = F::template load<true>(D, rbase + 4 * (b + i + R), chunk, D_FF);
+    }
   }
+#pragma unroll
+  for (int i = 0; i < R; ++i) step(i, NG - R + i);
 }
 
 // ======================================================================================
-// MFMA items: weight tile of 128 rows x 64 k decoded into LDS, activation tile of
-// 64 tokens x 64 k staged into LDS, v_mfma_f32_32x32x16_{f16,bf16}.
+// Matrix-core items: weight tile of 128 rows x 64 k decoded into LDS, activation
+// tile of 64 tokens x 64 k staged into LDS, v_mfma_f32_32x32x16_{f16,bf16}; the
+// next K-chunk is loaded into registers while the current one is multiplied.
 // ======================================================================================
 constexpr int TS = 72;  // LDS row stride in 16-bit elements (64 + 8 pad)
 
-struct MfmaSmem {
+struct FfnSmem {
   uint16_t w[128 * TS];
   uint16_t x[MFMA_BN * TS];
   int tok[MFMA_BN];
   int row[MFMA_BN];
 };
 
-// Decode 32 consecutive weights (k0 .. k0+31 of one row) into 16 dwords of
-// operand pairs, in the order the activation tile uses for this format.
-template <int FMT> __device__ inline void mfma_decode_row32(const QMat& q, size_t row, int k0, int cols, uint32_t* o);
-
-template <> __device__ inline void mfma_decode_row32<FMT_Q4_1>(const QMat& q, size_t row, int k0, int cols,
-                                                               uint32_t* o) {
-  const u32x4 c = ld16(q.codes + row * (cols / 2) + k0 / 2);
-  const uint32_t dm = reinterpret_cast<const uint32_t*>(q.scales)[row * (cols / 32) + k0 / 32];
-  const f16x2 d2 = {as_f16x2(dm)[0], as_f16x2(dm)[0]};
-  const f16x2 m2 = {as_f16x2(dm)[1], as_f16x2(dm)[1]};
-  const f16x2 off = {(_Float16)(-1024.f), (_Float16)(-1024.f)};
-  const uint32_t w[4] = {c[0], c[1], c[2], c[3]};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      // s = 0..3 -> pairs (q_s, q_{s+4}) of this 8-element group
-      const uint32_t bits = ((w[j] >> (4 * s)) & 0x000F000Fu) | MAGIC;
-      const f16x2 qv = as_f16x2(bits) + off;                  // exact small integers
-      o[4 * j + s] = as_u32(__builtin_elementwise_fma(qv, d2, m2));  // fp16(d*q + m), one rounding
-    }
-  }
-}
-
-template <> __device__ inline void mfma_decode_row32<FMT_NVFP4>(const QMat& q, size_t row, int k0, int cols,
-                                                                uint32_t* o) {
-  const u32x4 c = ld16(q.codes + row * (cols / 2) + k0 / 2);
-  const uint32_t sb = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(q.scales) +
-                                                         row * (cols / 16) + k0 / 16);
-  const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sb, 0);
-  const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sb, 1);
-  const uint32_t w[4] = {c[0], c[1], c[2], c[3]};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const f16x2 s = (j < 2) ? f16x2{s0, s0} : f16x2{s1, s1};
-    o[4 * j + 0] = as_u32(as_f16x2(fp4x2_to_f16x2<0>(w[j])) * s);
-    o[4 * j + 1] = as_u32(as_f16x2(fp4x2_to_f16x2<1>(w[j])) * s);
-    o[4 * j + 2] = as_u32(as_f16x2(fp4x2_to_f16x2<2>(w[j])) * s);
-    o[4 * j + 3] = as_u32(as_f16x2(fp4x2_to_f16x2<3>(w[j])) * s);
-  }
-}
-
-template <> __device__ inline void mfma_decode_row32<FMT_BF16>(const QMat& q, size_t row, int k0, int cols,
-                                                               uint32_t* o) {
-  const uint8_t* p = q.codes + (row * cols + k0) * 2;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const u32x4 v = ld16(p + 16 * i);
-    o[4 * i] = v[0]; o[4 * i + 1] = v[1]; o[4 * i + 2] = v[2]; o[4 * i + 3] = v[3];
-  }
-}
-
-// Stage 16 activation elements (natural order pairs in src[8]) into LDS in the
+// Store 16 activation elements (natural-order pairs src[8]) into LDS in the
 // format's k order.
 template <int FMT> __device__ inline void stage_x16(uint16_t* dst, const uint32_t* src) {
   uint32_t o[8];
@@ -476,15 +506,15 @@ template <int FMT> __device__ inline void stage_x16(uint16_t* dst, const uint32_
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = src[i];
   }
-  uint4* d = reinterpret_cast<uint4*>(dst);
-  d[0] = make_uint4(o[0], o[1], o[2], o[3]);
-  d[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+  d[0] = u32x4{o[0], o[1], o[2], o[3]};
+  d[1] = u32x4{o[4], o[5], o[6], o[7]};
 }
 
 template <int FMT>
 __device__ inline f32x16 mfma32(const uint16_t* a, const uint16_t* b, f32x16 c) {
-  const uint4 av = *reinterpret_cast<const uint4*>(a);
-  const uint4 bv = *reinterpret_cast<const uint4*>(b);
+  const u32x4 av = *reinterpret_cast<const u32x4*>(a);
+  const u32x4 bv = *reinterpret_cast<const u32x4*>(b);
   if (OPER_F16<FMT>)
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av), __builtin_bit_cast(f16x8, bv), c, 0,
                                                   0, 0);
@@ -492,8 +522,7 @@ __device__ inline f32x16 mfma32(const uint16_t* a, const uint16_t* b, f32x16 c) 
                                                  0, 0);
 }
 
-// Fill the item's token/row tables in LDS (threads 0..63).
-__device__ inline void mfma_tables(const LayerArgs& a, const ItemTok& it, MfmaSmem& sm) {
+__device__ inline void mfma_tables(const LayerArgs& a, const ItemTok& it, FfnSmem& sm) {
   const int i = threadIdx.x;
   if (i < MFMA_BN) {
     sm.tok[i] = (i < it.cnt) ? tok_of(a, it, i) : -1;
@@ -501,135 +530,135 @@ __device__ inline void mfma_tables(const LayerArgs& a, const ItemTok& it, MfmaSm
   }
 }
 
-// gate/up item: 64 row pairs (n0 ..) x 64 tokens; LDS w rows 0..63 gate, 64..127 up.
+// One K-chunk of a 128-row x 64-token tile: thread (wr_row = tid/2, half = tid%2)
+// owns 32 weights of one row; thread (xt = tid/4, xs = tid%4) owns 16
+// activation elements of one token.
+template <int FMT> struct MfmaStage {
+  typename GV<FMT>::Raw w;
+  u32x4 x0, x1;
+};
+
 template <int FMT>
-__device__ void mfma_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int mat, const ItemTok& it, int n0,
-                        MfmaSmem& sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  mfma_tables(a, it, sm);
-  __syncthreads();
-  f32x16 acc[2] = {};
-  // staging roles
-  const int wr_row = tid >> 1, wr_half = tid & 1;  // 128 rows x 2 blocks of 32
-  const QMat& wq = (wr_row < 64) ? G : Uq;
-  const size_t wrow = (size_t)mat * D_FF + n0 + (wr_row & 63);
-  const int xt = tid >> 2, xs = tid & 3;           // 64 tokens x 4 parts of 16
-  const int xtok = sm.tok[xt];
-  // MFMA roles: A-row r -> LDS row (r < 16 ? 16w + r : 64 + 16w + r - 16)
-  const int ar = lane & 31;
-  const int arow = (ar < 16) ? (16 * wave + ar) : (64 + 16 * wave + ar - 16);
-  const int kh = 8 * (lane >> 5);
-  for (int kc = 0; kc < D_MODEL; kc += 64) {
-    uint32_t wv[16];
-    mfma_decode_row32<FMT>(wq, wrow, kc + 32 * wr_half, D_MODEL, wv);
-    uint32_t xv[8];
-    if (xtok >= 0) {
-      const uint4* p = reinterpret_cast<const uint4*>(a.x + (size_t)xtok * D_MODEL + kc + 16 * xs);
-      const uint4 v0 = p[0], v1 = p[1];
-      xv[0] = v0.x; xv[1] = v0.y; xv[2] = v0.z; xv[3] = v0.w; xv[4] = v1.x; xv[5] = v1.y; xv[6] = v1.z; xv[7] = v1.w;
-      if (OPER_F16<FMT>) {
+__device__ inline void mfma_fetch(MfmaStage<FMT>& st, const QMat& wq, size_t wrow, int kw, const uint16_t* xsrc,
+                                  int cols) {
+  st.w = GV<FMT>::template load<false>(wq, wrow, kw / 32, cols);
+  if (xsrc) {
+    st.x0 = ld16<false>(xsrc);
+    st.x1 = ld16<false>(xsrc + 8);
+  } else {
+    st.x0 = u32x4{0u, 0u, 0u, 0u};
+    st.x1 = st.x0;
+  }
+}
+
+template <int FMT>
+__device__ inline void mfma_stage_store(const MfmaStage<FMT>& st, FfnSmem& sm, int wr_row, int wr_half, int xt, int xs,
+                                        bool x_bf16) {
+  uint32_t wv[16];
+  GV<FMT>::decode(st.w, wv);
+  u32x4* d = reinterpret_cast<u32x4*>(sm.w + wr_row * TS + 32 * wr_half);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xv[i] = bf16x2_to_f16x2(xv[i]);
-      }
-    } else {
+  for (int i = 0; i < 4; ++i) d[i] = u32x4{wv[4 * i], wv[4 * i + 1], wv[4 * i + 2], wv[4 * i + 3]};
+  uint32_t xv[8] = {st.x0[0], st.x0[1], st.x0[2], st.x0[3], st.x1[0], st.x1[1], st.x1[2], st.x1[3]};
+  if (OPER_F16<FMT> && x_bf16) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) xv[i] = 0u;
-    }
-    __syncthreads();  // previous chunk's MFMAs are done with the tiles
-    {
-      uint4* d = reinterpret_cast<uint4*>(sm.w + wr_row * TS + 32 * wr_half);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) d[i] = make_uint4(wv[4 * i], wv[4 * i + 1], wv[4 * i + 2], wv[4 * i + 3]);
-      stage_x16<FMT>(sm.x + xt * TS + 16 * xs, xv);
-    }
+    for (int i = 0; i < 8; ++i) xv[i] = bf16x2_to_f16x2(xv[i]);
+  }
+  stage_x16<FMT>(sm.x + xt * TS + 16 * xs, xv);
+}
+
+// acc[tt] += W_tile(rows arow..) x X_tile(tokens 32tt..) over K = kdim.
+// wq/wrow: this thread's weight row; xrow_ptr: this thread's activation row (or null).
+template <int FMT>
+__device__ inline void mfma_kloop(f32x16* acc, FfnSmem& sm, const QMat& wq, size_t wrow, const uint16_t* xrow_ptr,
+                                  bool x_bf16, int kdim, int arow) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wr_row = tid >> 1, wr_half = tid & 1;
+  const int xt = tid >> 2, xs = tid & 3;
+  const int ar = lane & 31, kh = 8 * (lane >> 5);
+  MfmaStage<FMT> st;
+  mfma_fetch<FMT>(st, wq, wrow, 32 * wr_half, xrow_ptr ? xrow_ptr + 16 * xs : nullptr, kdim);
+#pragma unroll 1
+  for (int kc = 0; kc < kdim; kc += 64) {
+    __syncthreads();  // the previous chunk's MFMAs are done with the tiles
+    mfma_stage_store<FMT>(st, sm, wr_row, wr_half, xt, xs, x_bf16);
     __syncthreads();
+    if (kc + 64 < kdim)
+      mfma_fetch<FMT>(st, wq, wrow, kc + 64 + 32 * wr_half, xrow_ptr ? xrow_ptr + kc + 64 + 16 * xs : nullptr, kdim);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const uint16_t* ap = sm.w + arow * TS + 16 * s + kh;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-        acc[tt] = mfma32<FMT>(ap, sm.x + (32 * tt + ar) * TS + 16 * s + kh, acc[tt]);
+      for (int tt = 0; tt < 2; ++tt) acc[tt] = mfma32<FMT>(ap, sm.x + (32 * tt + ar) * TS + 16 * s + kh, acc[tt]);
     }
   }
-  // epilogue: acc[tt][4i+j] = A-row 8i + 4(lane/32) + j, token 32tt + lane%32.
-  // A-rows 0..15 gate, 16..31 up of the same n: gate i in {0,1}, up i+2.
+}
+
+// gate/up item: 64 row pairs (n0 ..) x 64 tokens; LDS rows 0..63 gate, 64..127 up.
+template <int FMT>
+__device__ void mfma_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int mat, const ItemTok& it, int n0,
+                        FfnSmem& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  mfma_tables(a, it, sm);
+  __syncthreads();
+  const int wr_row = tid >> 1;
+  QMat wq;
+  wq.codes = (wr_row < 64) ? G.codes : Uq.codes;
+  wq.scales = (wr_row < 64) ? G.scales : Uq.scales;
+  wq.ts = nullptr;
+  const size_t wrow = (size_t)mat * D_FF + n0 + (wr_row & 63);
+  const int xtok = sm.tok[tid >> 2];
+  const uint16_t* xrow = xtok >= 0 ? a.x + (size_t)xtok * D_MODEL : nullptr;
+  // A-row r -> LDS row (r < 16 ? 16w + r : 64 + 16w + r - 16): gate and up of the same n
+  const int ar = lane & 31;
+  const int arow = (ar < 16) ? (16 * wave + ar) : (64 + 16 * wave + ar - 16);
+  f32x16 acc[2] = {};
+  mfma_kloop<FMT>(acc, sm, wq, wrow, xrow, true, D_MODEL, arow);
+  // acc[tt][4i+j] = A-row 8i + 4(lane/32) + j, token 32tt + lane%32:
+  // gate for i in {0,1}, the matching up at i+2.
   const float tsg = (FMT == FMT_NVFP4) ? G.ts[mat] : 1.f;
   const float tsu = (FMT == FMT_NVFP4) ? Uq.ts[mat] : 1.f;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    const int ti = 32 * tt + (lane & 31);
-    const int hrow = sm.row[ti];
+    const int hrow = sm.row[32 * tt + ar];
     if (hrow < 0) continue;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      float hv[4];
+      uint16_t hv[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) hv[j] = silu_mul(acc[tt][4 * i + j] * tsg, acc[tt][4 * (i + 2) + j] * tsu);
+      for (int j = 0; j < 4; ++j) hv[j] = h_store<FMT>(silu_mul(acc[tt][4 * i + j] * tsg, acc[tt][4 * (i + 2) + j] * tsu));
       const int n = n0 + 16 * wave + 8 * i + 4 * (lane >> 5);
       uint2 pk;
-      if (OPER_F16<FMT>) { pk.x = pack_h16(hv[0], hv[1]); pk.y = pack_h16(hv[2], hv[3]); }
-      else { pk.x = pack_b16(hv[0], hv[1]); pk.y = pack_b16(hv[2], hv[3]); }
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.h) + (size_t)hrow * D_FF + n) = pk;
+      pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+      pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+      *reinterpret_cast<uint2*>(a.h + (size_t)hrow * D_FF + n) = pk;
     }
   }
-  __syncthreads();  // tables/tiles reused by the next item
+  __syncthreads();  // tables and tiles are reused by the next item
 }
 
 // down item: 128 rows (r0 ..) x 64 tokens, K = 512.
 template <int FMT>
-__device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const ItemTok& it, int r0, MfmaSmem& sm) {
+__device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const ItemTok& it, int r0, FfnSmem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   mfma_tables(a, it, sm);
   __syncthreads();
-  f32x16 acc[2] = {};
-  const int wr_row = tid >> 1, wr_half = tid & 1;
-  const size_t wrow = (size_t)mat * D_MODEL + r0 + wr_row;
-  const int xt = tid >> 2, xs = tid & 3;
-  const int xrow = sm.row[xt];
+  const size_t wrow = (size_t)mat * D_MODEL + r0 + (tid >> 1);
+  const int hrow_x = sm.row[tid >> 2];
+  const uint16_t* xrow = hrow_x >= 0 ? a.h + (size_t)hrow_x * D_FF : nullptr;
   const int ar = lane & 31;
-  const int arow = 32 * wave + ar;
-  const int kh = 8 * (lane >> 5);
-  for (int kc = 0; kc < D_FF; kc += 64) {
-    uint32_t wv[16];
-    mfma_decode_row32<FMT>(D, wrow, kc + 32 * wr_half, D_FF, wv);
-    uint32_t xv[8];
-    if (xrow >= 0) {
-      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.h) + (size_t)xrow * D_FF +
-                                                      kc + 16 * xs);
-      const uint4 v0 = p[0], v1 = p[1];
-      xv[0] = v0.x; xv[1] = v0.y; xv[2] = v0.z; xv[3] = v0.w; xv[4] = v1.x; xv[5] = v1.y; xv[6] = v1.z; xv[7] = v1.w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xv[i] = 0u;
-    }
-    __syncthreads();
-    {
-      uint4* d = reinterpret_cast<uint4*>(sm.w + wr_row * TS + 32 * wr_half);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) d[i] = make_uint4(wv[4 * i], wv[4 * i + 1], wv[4 * i + 2], wv[4 * i + 3]);
-      stage_x16<FMT>(sm.x + xt * TS + 16 * xs, xv);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint16_t* ap = sm.w + arow * TS + 16 * s + kh;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-        acc[tt] = mfma32<FMT>(ap, sm.x + (32 * tt + ar) * TS + 16 * s + kh, acc[tt]);
-    }
-  }
+  f32x16 acc[2] = {};
+  mfma_kloop<FMT>(acc, sm, D, wrow, xrow, false, D_FF, 32 * wave + ar);
   const float ts = (FMT == FMT_NVFP4) ? D.ts[mat] : 1.f;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    const int ti = 32 * tt + (lane & 31);
-    const int yrow = sm.row[ti];
+    const int yrow = sm.row[32 * tt + ar];
     if (yrow < 0) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = r0 + 32 * wave + 8 * i + 4 * (lane >> 5);
-      float4 o = make_float4(acc[tt][4 * i] * ts, acc[tt][4 * i + 1] * ts, acc[tt][4 * i + 2] * ts,
-                             acc[tt][4 * i + 3] * ts);
-      *reinterpret_cast<float4*>(a.y + (size_t)yrow * D_MODEL + r) = o;
+      *reinterpret_cast<float4*>(a.y + (size_t)yrow * D_MODEL + r) =
+          make_float4(acc[tt][4 * i] * ts, acc[tt][4 * i + 1] * ts, acc[tt][4 * i + 2] * ts, acc[tt][4 * i + 3] * ts);
     }
   }
   __syncthreads();
@@ -638,78 +667,195 @@ __device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const Item
 // ======================================================================================
 // Persistent kernels
 // ======================================================================================
-template <int FMT> constexpr int UP_NR = (FMT == FMT_BF16) ? 2 : 4;   // row pairs per wave per step
-template <int FMT> constexpr int DN_NRG = (FMT == FMT_BF16) ? 2 : 4;  // 4-row groups per wave per step
-
-template <int FMT>
+template <int FMT, bool SHARED>
 __global__ __launch_bounds__(256) void ffn_up_kernel(LayerArgs a) {
-  __shared__ MfmaSmem sm;
-  const int n_items = a.ctl[CTL_N_UP];
+  __shared__ FfnSmem sm;
+  const int n_items = SHARED ? shared_items(a.T, N_UP_CHUNKS) : a.ctl[CTL_N_UP];
   const int wave = threadIdx.x >> 6;
   for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
-    const uint32_t item = a.items_up[i];
-    const int e = item_expert(item);
-    const bool shared = e >= a.E;
-    const QMat& G = shared ? a.sh_gate : a.gate;
-    const QMat& U = shared ? a.sh_up : a.up;
-    const int mat = shared ? 0 : e;
-    const ItemTok it = item_tokens(a, e, item_tile(item));
-    if (item_mfma(item)) {
-      mfma_up<FMT>(a, G, U, mat, it, item_chunk(item) * UP_MFMA_ROWS, sm);
+    const Item item = SHARED ? shared_item(a.T, a.E, i, N_UP_CHUNKS) : a.items_up[i];
+    const int e = SHARED ? a.E : item_expert(item.head);
+    const QMat& G = SHARED ? a.sh_gate : a.gate;
+    const QMat& U = SHARED ? a.sh_up : a.up;
+    const int mat = SHARED ? 0 : e;
+    const ItemTok it = item_tokens(item, SHARED);
+    const int n0 = item_chunk(item.head) * UP_ROWS;
+    if (it.mfma) {
+      mfma_up<FMT>(a, G, U, mat, it, n0, sm);
     } else {
-      constexpr int NR = UP_NR<FMT>;
-      // an item covers UP_GEMV_ROWS row pairs: 4 waves x (UP_GEMV_ROWS/4) rows, NR per step
-      for (int r = 0; r < UP_GEMV_ROWS / 4; r += NR) {
-        const int n0 = item_chunk(item) * UP_GEMV_ROWS + wave * (UP_GEMV_ROWS / 4) + r;
-        if (it.cnt <= 1) gemv_up<FMT, 1, NR>(a, G, U, mat, it, n0);
-        else if (it.cnt <= 2) gemv_up<FMT, 2, NR>(a, G, U, mat, it, n0);
-        else gemv_up<FMT, 4, NR>(a, G, U, mat, it, n0);
+      constexpr int NRW = UP_ROWS / 4;  // row pairs per wave
+      // up to two tokens per pass; a second pass re-reads the rows from cache
+#pragma unroll 1
+      for (int tp = 0; tp < it.cnt; tp += 2) {
+        ItemTok sub = it;
+        sub.p0 += tp;
+        sub.cnt = min(2, it.cnt - tp);
+        sub.tok[0] = tp ? it.tok[2] : it.tok[0];
+        sub.tok[1] = tp ? it.tok[3] : it.tok[1];
+        if (sub.cnt == 1) gemv_up_wave<FMT, 1, NRW>(a, G, U, mat, sub, n0 + wave * NRW);
+        else gemv_up_wave<FMT, 2, NRW>(a, G, U, mat, sub, n0 + wave * NRW);
+      }
+    }
+  }
+}
+
+template <int FMT, bool SHARED>
+__global__ __launch_bounds__(256) void ffn_down_kernel(LayerArgs a) {
+  __shared__ FfnSmem sm;
+  const int n_items = SHARED ? shared_items(a.T, N_DN_CHUNKS) : a.ctl[CTL_N_DN];
+  const int wave = threadIdx.x >> 6;
+  for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
+    const Item item = SHARED ? shared_item(a.T, a.E, i, N_DN_CHUNKS) : a.items_dn[i];
+    const int e = SHARED ? a.E : item_expert(item.head);
+    const QMat& D = SHARED ? a.sh_down : a.down;
+    const int mat = SHARED ? 0 : e;
+    const ItemTok it = item_tokens(item, SHARED);
+    const int chunk = item_chunk(item.head);
+    const int r0 = chunk * DN_ROWS;
+    if (it.mfma) {
+      mfma_down<FMT>(a, D, mat, it, r0, sm);
+    } else {
+      constexpr int NRW = DN_ROWS / 4;  // rows per wave
+#pragma unroll 1
+      for (int tp = 0; tp < it.cnt; tp += 2) {
+        ItemTok sub = it;
+        sub.p0 += tp;
+        sub.cnt = min(2, it.cnt - tp);
+        sub.tok[0] = tp ? it.tok[2] : it.tok[0];
+        sub.tok[1] = tp ? it.tok[3] : it.tok[1];
+        if (sub.cnt == 1) gemv_down_wave<FMT, 1, NRW / 4>(a, D, mat, sub, r0 + wave * NRW);
+        else gemv_down_wave<FMT, 2, NRW / 4>(a, D, mat, sub, r0 + wave * NRW);
       }
     }
   }
 }
 
 template <int FMT>
-__global__ __launch_bounds__(256) void ffn_down_kernel(LayerArgs a) {
-  __shared__ MfmaSmem sm;
-  const int n_items = a.ctl[CTL_N_DN];
-  const int wave = threadIdx.x >> 6;
-  for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
-    const uint32_t item = a.items_dn[i];
-    const int e = item_expert(item);
-    const bool shared = e >= a.E;
-    const QMat& D = shared ? a.sh_down : a.down;
-    const int mat = shared ? 0 : e;
-    const ItemTok it = item_tokens(a, e, item_tile(item));
-    if (item_mfma(item)) {
-      mfma_down<FMT>(a, D, mat, it, item_chunk(item) * DN_MFMA_ROWS, sm);
-    } else {
-      constexpr int NRG = DN_NRG<FMT>;
-      for (int g = 0; g < DN_GEMV_ROWS / 16; g += NRG) {
-        const int r0 = item_chunk(item) * DN_GEMV_ROWS + wave * (DN_GEMV_ROWS / 4) + 4 * g;
-        if (it.cnt <= 1) gemv_down<FMT, 1, NRG>(a, D, mat, it, r0);
-        else if (it.cnt <= 2) gemv_down<FMT, 2, NRG>(a, D, mat, it, r0);
-        else gemv_down<FMT, 4, NRG>(a, D, mat, it, r0);
-      }
-    }
-  }
+hipError_t launch_up_fmt(const LayerArgs& a, bool shared, int grid, hipStream_t s) {
+  if (shared) hipLaunchKernelGGL((ffn_up_kernel<FMT, true>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((ffn_up_kernel<FMT, false>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
-
-hipError_t launch_ffn_up(const LayerArgs& a, int grid, hipStream_t s) {
-  switch (a.fmt) {
-    case FMT_Q4_1: hipLaunchKernelGGL(ffn_up_kernel<FMT_Q4_1>, dim3(grid), dim3(256), 0, s, a); break;
-    case FMT_NVFP4: hipLaunchKernelGGL(ffn_up_kernel<FMT_NVFP4>, dim3(grid), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL(ffn_up_kernel<FMT_BF16>, dim3(grid), dim3(256), 0, s, a); break;
-  }
+template <int FMT>
+hipError_t launch_down_fmt(const LayerArgs& a, bool shared, int grid, hipStream_t s) {
+  if (shared) hipLaunchKernelGGL((ffn_down_kernel<FMT, true>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((ffn_down_kernel<FMT, false>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_down(const LayerArgs& a, int grid, hipStream_t s) {
+hipError_t launch_ffn_up(const LayerArgs& a, bool shared, int grid, hipStream_t s) {
   switch (a.fmt) {
-    case FMT_Q4_1: hipLaunchKernelGGL(ffn_down_kernel<FMT_Q4_1>, dim3(grid), dim3(256), 0, s, a); break;
-    case FMT_NVFP4: hipLaunchKernelGGL(ffn_down_kernel<FMT_NVFP4>, dim3(grid), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL(ffn_down_kernel<FMT_BF16>, dim3(grid), dim3(256), 0, s, a); break;
+    case FMT_Q4_1: return launch_up_fmt<FMT_Q4_1>(a, shared, grid, s);
+    case FMT_NVFP4: return launch_up_fmt<FMT_NVFP4>(a, shared, grid, s);
+    default: return launch_up_fmt<FMT_BF16>(a, shared, grid, s);
   }
+}
+
+hipError_t launch_ffn_down(const LayerArgs& a, bool shared, int grid, hipStream_t s) {
+  switch (a.fmt) {
+    case FMT_Q4_1: return launch_down_fmt<FMT_Q4_1>(a, shared, grid, s);
+    case FMT_NVFP4: return launch_down_fmt<FMT_NVFP4>(a, shared, grid, s);
+    default: return launch_down_fmt<FMT_BF16>(a, shared, grid, s);
+  }
+}
+
+// ======================================================================================
+// Combine and stack glue: one workgroup per token, 8 consecutive columns per thread.
+// ======================================================================================
+__device__ inline float block_sum256(float v) {
+  __shared__ float red[4];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+__device__ inline void store_bf16x8(uint16_t* dst, const float* v) {
+  u32x4 pk;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) pk[q] = (uint32_t)f32_to_bf16(v[2 * q]) | ((uint32_t)f32_to_bf16(v[2 * q + 1]) << 16);
+  *reinterpret_cast<u32x4*>(dst) = pk;
+}
+
+// xn = bf16(v / sqrt(mean(v^2) + eps)) over the token's 2048 values.
+__device__ inline void rmsnorm_store(const float* v, uint16_t* dst, float eps) {
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) ss += v[q] * v[q];
+  ss = block_sum256(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)D_MODEL + eps);
+  float o[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) o[q] = v[q] * inv;
+  store_bf16x8(dst, o);
+}
+
+// out = sum_j w_j y[slot j] + shared_scale y[shared], in the order j = 0..K-1
+// then the shared expert, rounded once to bf16.  Single layer: written to
+// a.out.  Stack: recorded to a.y_rec (if any), r += out, then the next
+// layer's input bf16(RMSNorm(r)) or, after the last layer, bf16(r).
+__global__ __launch_bounds__(256) void combine_kernel(LayerArgs a) {
+  const int t = blockIdx.x;
+  const int i0 = 8 * threadIdx.x;
+  float o[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) o[q] = 0.f;
+  for (int j = 0; j < a.K; ++j) {
+    const float wj = a.w[(size_t)t * a.K + j];
+    const float4* p = reinterpret_cast<const float4*>(a.y + (size_t)a.inv_perm[(size_t)t * a.K + j] * D_MODEL + i0);
+    const float4 v0 = p[0], v1 = p[1];
+    o[0] += wj * v0.x; o[1] += wj * v0.y; o[2] += wj * v0.z; o[3] += wj * v0.w;
+    o[4] += wj * v1.x; o[5] += wj * v1.y; o[6] += wj * v1.z; o[7] += wj * v1.w;
+  }
+  if (a.n_shared) {
+    const float s = a.shared_scale;
+    const float4* p = reinterpret_cast<const float4*>(a.y + (size_t)(a.S + t) * D_MODEL + i0);
+    const float4 v0 = p[0], v1 = p[1];
+    o[0] += s * v0.x; o[1] += s * v0.y; o[2] += s * v0.z; o[3] += s * v0.w;
+    o[4] += s * v1.x; o[5] += s * v1.y; o[6] += s * v1.z; o[7] += s * v1.w;
+  }
+  if (!a.r) {
+    store_bf16x8(a.out + (size_t)t * D_MODEL + i0, o);
+    return;
+  }
+  float yb[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) yb[q] = bf16_to_f32(f32_to_bf16(o[q]));
+  if (a.y_rec) store_bf16x8(a.y_rec + (size_t)t * D_MODEL + i0, yb);
+  float4* rp = reinterpret_cast<float4*>(a.r + (size_t)t * D_MODEL + i0);
+  const float4 r0 = rp[0], r1 = rp[1];
+  float rv[8] = {r0.x + yb[0], r0.y + yb[1], r0.z + yb[2], r0.w + yb[3],
+                 r1.x + yb[4], r1.y + yb[5], r1.z + yb[6], r1.w + yb[7]};
+  rp[0] = make_float4(rv[0], rv[1], rv[2], rv[3]);
+  rp[1] = make_float4(rv[4], rv[5], rv[6], rv[7]);
+  if (a.x_final) store_bf16x8(a.x_final + (size_t)t * D_MODEL + i0, rv);
+  if (a.xn_next) rmsnorm_store(rv, a.xn_next + (size_t)t * D_MODEL + i0, a.eps);
+}
+
+hipError_t launch_combine(const LayerArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(combine_kernel, dim3(a.T), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Stack entry: r = x (fp32), xn = bf16(RMSNorm(r)).
+__global__ __launch_bounds__(256) void stack_init_kernel(const uint16_t* __restrict__ x, float* __restrict__ r,
+                                                         uint16_t* __restrict__ xn, float eps) {
+  const int t = blockIdx.x;
+  const int i0 = 8 * threadIdx.x;
+  const u32x4 pk = *reinterpret_cast<const u32x4*>(x + (size_t)t * D_MODEL + i0);
+  float v[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) { v[2 * q] = __uint_as_float(pk[q] << 16); v[2 * q + 1] = __uint_as_float(pk[q] & 0xFFFF0000u); }
+  float4* rp = reinterpret_cast<float4*>(r + (size_t)t * D_MODEL + i0);
+  rp[0] = make_float4(v[0], v[1], v[2], v[3]);
+  rp[1] = make_float4(v[4], v[5], v[6], v[7]);
+  rmsnorm_store(v, xn + (size_t)t * D_MODEL + i0, eps);
+}
+
+hipError_t launch_stack_init(const uint16_t* x, float* r, uint16_t* xn, int T, float eps, hipStream_t s) {
+  hipLaunchKernelGGL(stack_init_kernel, dim3(T), dim3(256), 0, s, x, r, xn, eps);
   return hipGetLastError();
 }
 

@@ -1,0 +1,376 @@
+// Routing: router logits on the matrix cores, top-k selection with softmax
+// weights (one wavefront per token), and the expert buckets and work lists.
+//
+// The review "Recursive Flint 40B-A2.5B" (orcarouter.ai), section "The
+// architecture is an argument about memory bandwidth", gives the selection
+// structure: 6 of 256 routed experts per token plus an always-on shared
+// expert.  The router form (bf16 Linear d_model -> experts, fp32 softmax over
+// the chosen experts) is this library's reading of that statement.
+//
+// Three launches (kernel boundaries order the steps; no device-scope fences):
+//   router        partial logits part[ks][t][e] over 8 K-splits (MFMA 16x16x32 bf16);
+//   topk          one wave per token sums the 8 partials in split order, selects
+//                 the top k (ties to the lower id) and writes the weights;
+//   bucket        one workgroup: histogram, exclusive prefix sum, a stable slot
+//                 permutation from per-expert token bitmasks and popcounts, its
+//                 inverse, and the FFN work lists.
+#include "common.hpp"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int ROUTER_KR = 256;                  // K range per split
+constexpr int ROUTER_KS = D_MODEL / ROUTER_KR;  // 8 splits
+constexpr int ROUTER_TG = 256;                  // tokens per workgroup on the large-T path
+
+// Decode-sized T: one wave per (16-token tile, 16-expert tile, K-split); the
+// workgroup's 4 waves take 4 consecutive expert tiles.  grid (ceil(T/16) *
+// ceil(E/64), ROUTER_KS).  MFMA 16x16x32 bf16: A = x rows, B = router rows.
+__global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ wr, float* __restrict__ part,
+                                                           int T, int E) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int egroups = (E + 63) / 64;
+  const int t0 = (blockIdx.x / egroups) * 16;
+  const int e0 = ((blockIdx.x % egroups) * 4 + wave) * 16;
+  if (e0 >= E) return;
+  const int ks = blockIdx.y;
+  const int kbase = ks * ROUTER_KR + 8 * (lane >> 4);
+  const int col = lane & 15;
+  const int t = t0 + col;
+  bf16x8 a[ROUTER_KR / 32], b[ROUTER_KR / 32];
+  const uint16_t* wrow = wr + (size_t)(e0 + col) * D_MODEL + kbase;
+  const uint16_t* xrow = x + (size_t)(t < T ? t : 0) * D_MODEL + kbase;
+#pragma unroll
+  for (int s = 0; s < ROUTER_KR / 32; ++s) {
+    b[s] = *reinterpret_cast<const bf16x8*>(wrow + 32 * s);
+    a[s] = (t < T) ? *reinterpret_cast<const bf16x8*>(xrow + 32 * s) : bf16x8{};
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < ROUTER_KR / 32; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[s], acc, 0, 0, 0);
+  // acc[j] = D[row 4*(lane/16)+j][col lane%16]: token t0 + 4*(lane>>4) + j, expert e0 + col
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tt = t0 + 4 * (lane >> 4) + j;
+    if (tt < T) part[((size_t)ks * T + tt) * E + e0 + col] = acc[j];
+  }
+}
+
+// Large T: a wave keeps its 16 router rows x 256 k in registers and loops over
+// the 16-token tiles of a 256-token group.  grid (ceil(E/64), ROUTER_KS, ceil(T/256)).
+__global__ __launch_bounds__(256) void router_large_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ wr, float* __restrict__ part,
+                                                           int T, int E) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e0 = (blockIdx.x * 4 + wave) * 16;
+  if (e0 >= E) return;
+  const int ks = blockIdx.y;
+  const int kbase = ks * ROUTER_KR + 8 * (lane >> 4);
+  const int col = lane & 15;
+  bf16x8 b[ROUTER_KR / 32];
+  const uint16_t* wrow = wr + (size_t)(e0 + col) * D_MODEL + kbase;
+#pragma unroll
+  for (int s = 0; s < ROUTER_KR / 32; ++s) b[s] = *reinterpret_cast<const bf16x8*>(wrow + 32 * s);
+  const int tg0 = blockIdx.z * ROUTER_TG;
+  for (int t0 = tg0; t0 < min(T, tg0 + ROUTER_TG); t0 += 16) {
+    const int t = t0 + col;
+    bf16x8 a[ROUTER_KR / 32];
+    const uint16_t* xrow = x + (size_t)(t < T ? t : 0) * D_MODEL + kbase;
+#pragma unroll
+    for (int s = 0; s < ROUTER_KR / 32; ++s) a[s] = (t < T) ? *reinterpret_cast<const bf16x8*>(xrow + 32 * s) : bf16x8{};
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < ROUTER_KR / 32; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[s], acc, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tt = t0 + 4 * (lane >> 4) + j;
+      if (tt < T) part[((size_t)ks * T + tt) * E + e0 + col] = acc[j];
+    }
+  }
+}
+
+hipError_t launch_router(const LayerArgs& a, hipStream_t s) {
+  if (a.T <= ROUTER_TG) {
+    dim3 grid(ceil_div(a.T, 16) * ceil_div(a.E, 64), ROUTER_KS);
+    hipLaunchKernelGGL(router_small_kernel, grid, dim3(256), 0, s, a.x, a.router_w, a.logit_part, a.T, a.E);
+  } else {
+    dim3 grid(ceil_div(a.E, 64), ROUTER_KS, ceil_div(a.T, ROUTER_TG));
+    hipLaunchKernelGGL(router_large_kernel, grid, dim3(256), 0, s, a.x, a.router_w, a.logit_part, a.T, a.E);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// top-k + buckets
+// ---------------------------------------------------------------------------------------
+constexpr int TK_THREADS = 256;             // 4 waves: 4 tokens per workgroup
+constexpr int BK_THREADS = 1024;
+constexpr int BK_TC = 1024;                 // tokens per bitmask chunk
+constexpr int BK_WORDS = BK_TC / 32;        // mask words per expert
+
+// Candidate order: a live candidate beats a dead one (taken, or no such
+// expert); among live ones the larger logit wins, ties to the lower id.  NaN
+// logits are ordered as -inf, so k distinct valid ids always come out.
+__device__ inline bool better(bool al, float av, int ae, bool bl, float bv, int be) {
+  if (al != bl) return al;
+  return av > bv || (av == bv && ae < be);
+}
+
+__device__ void topk_token(const LayerArgs& a, int t) {
+  const int lane = threadIdx.x & 63;
+  const int T = a.T, E = a.E, K = a.K;
+  float v[4];
+  bool live[4];
+  float mx = -INFINITY;
+  float raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    live[i] = e < E;
+    v[i] = -INFINITY;
+    if (live[i]) {
+      float p[ROUTER_KS];
+#pragma unroll
+      for (int ks = 0; ks < ROUTER_KS; ++ks) p[ks] = a.logit_part[((size_t)ks * T + t) * E + e];
+      float s = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < ROUTER_KS; ++ks) s += p[ks];
+      if (a.router_b) s += a.router_b[e];
+      raw[i] = s;
+      v[i] = (s != s) ? -INFINITY : s;
+      mx = fmaxf(mx, v[i]);
+    }
+  }
+  if (a.write_logits) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (live[i]) a.logits[(size_t)t * E + lane + 64 * i] = raw[i];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  float den_all = 0.f;
+  if (!a.renorm) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (live[i]) den_all += expf(v[i] - mx);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) den_all += __shfl_xor(den_all, off);
+  }
+  float sel_v[MAX_K];
+  int sel_e[MAX_K];
+#pragma unroll
+  for (int j = 0; j < MAX_K; ++j) {
+    sel_v[j] = -INFINITY;
+    sel_e[j] = 0;
+    if (j >= K) continue;
+    bool bl = live[0];
+    float bv = v[0];
+    int be = lane;
+#pragma unroll
+    for (int i = 1; i < 4; ++i)
+      if (better(live[i], v[i], lane + 64 * i, bl, bv, be)) { bl = live[i]; bv = v[i]; be = lane + 64 * i; }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const bool ol = __shfl_xor((int)bl, off) != 0;
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      if (better(ol, ov, oe, bl, bv, be)) { bl = ol; bv = ov; be = oe; }
+    }
+    sel_v[j] = bv;
+    sel_e[j] = be;
+    if ((be & 63) == lane) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (lane + 64 * i == be) live[i] = false;
+    }
+  }
+  if (lane < K) {
+    float wv;
+    int me = 0;
+    float mv = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAX_K; ++j)
+      if (j == lane) { me = sel_e[j]; mv = sel_v[j]; }
+    if (a.renorm) {
+      float den = 0.f;
+#pragma unroll
+      for (int j = 0; j < MAX_K; ++j)
+        if (j < K) den += expf(sel_v[j] - sel_v[0]);
+      wv = expf(mv - sel_v[0]) / den;
+    } else {
+      wv = expf(mv - mx) / den_all;
+    }
+    a.ids[(size_t)t * K + lane] = me;
+    a.w[(size_t)t * K + lane] = wv;
+  }
+}
+
+// Exclusive scan of v over n <= 320 entries by wave 0 (5 per lane); returns total.
+__device__ int wave0_scan(int* v, int n) {
+  const int lane = threadIdx.x & 63;
+  int loc[5], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int idx = lane * 5 + i;
+    loc[i] = (idx < n) ? v[idx] : 0;
+    sum += loc[i];
+  }
+  int inc = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  int run = inc - sum;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int idx = lane * 5 + i;
+    if (idx < n) v[idx] = run;
+    run += loc[i];
+  }
+  return __shfl(inc, 63);
+}
+
+struct BucketSmem {
+  int cnt[MAX_E + 1];
+  int off[MAX_E + 1];
+  int base[MAX_E];
+  uint32_t mask[MAX_E * BK_WORDS];
+  int it_m[MAX_E + 2];   // MFMA items per expert (up), then prefix
+  int it_g[MAX_E + 2];   // vector items per expert (up), then prefix
+  int tot[2];
+};
+
+// Buckets and work lists of the routed experts (one workgroup).
+__device__ void build_buckets(const LayerArgs& a, BucketSmem& sm) {
+  const int tid = threadIdx.x, nth = blockDim.x;
+  const int E = a.E, K = a.K, T = a.T, S = a.S;
+  const int32_t* ids = a.ids;
+
+  for (int e = tid; e < E; e += nth) { sm.cnt[e] = 0; sm.base[e] = 0; }
+  __syncthreads();
+  for (int s = tid; s < S; s += nth) atomicAdd(&sm.cnt[ids[s]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += nth) sm.off[e] = sm.cnt[e];
+  __syncthreads();
+  if (tid < 64) {
+    const int total = wave0_scan(sm.off, E);
+    if (tid == 0) sm.off[E] = total;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += nth) a.counts[e] = sm.cnt[e];
+  for (int e = tid; e <= E; e += nth) a.offsets[e] = sm.off[e];
+
+  for (int t0 = 0; t0 < T; t0 += BK_TC) {
+    const int words = min(BK_WORDS, ceil_div(T - t0, 32));
+    for (int i = tid; i < E * BK_WORDS; i += nth) sm.mask[i] = 0u;
+    __syncthreads();
+    const int s0 = t0 * K, s1 = min(T, t0 + BK_TC) * K;
+    for (int s = s0 + tid; s < s1; s += nth) {
+      const int tt = s / K - t0;
+      atomicOr(&sm.mask[ids[s] * BK_WORDS + (tt >> 5)], 1u << (tt & 31));
+    }
+    __syncthreads();
+    for (int s = s0 + tid; s < s1; s += nth) {
+      const int e = ids[s], tt = s / K - t0;
+      const uint32_t* me = sm.mask + e * BK_WORDS;
+      int r = sm.base[e];
+      for (int wd = 0; wd < (tt >> 5); ++wd) r += __popc(me[wd]);
+      r += __popc(me[tt >> 5] & ((1u << (tt & 31)) - 1u));
+      const int pos = sm.off[e] + r;
+      a.perm[pos] = s;
+      a.inv_perm[s] = pos;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += nth) {
+      int c = 0;
+      for (int wd = 0; wd < words; ++wd) c += __popc(sm.mask[e * BK_WORDS + wd]);
+      sm.base[e] += c;
+    }
+    __syncthreads();
+  }
+
+  // work lists (routed experts only): MFMA items first, then vector items.  Both
+  // lists use the same expert/tile order; the down list has N_DN_CHUNKS chunks
+  // per tile where the gate/up list has N_UP_CHUNKS.
+  for (int e = tid; e < E; e += nth) {
+    const int m = sm.cnt[e];
+    const int tiles = bucket_tiles(m);
+    sm.it_m[e] = bucket_mfma(m) ? tiles : 0;
+    sm.it_g[e] = bucket_mfma(m) ? 0 : tiles;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int a0 = wave0_scan(sm.it_m, E);
+    const int a1 = wave0_scan(sm.it_g, E);
+    if (tid == 0) {
+      sm.it_m[E] = a0;
+      sm.it_g[E] = a1;
+      sm.tot[0] = a0;
+      sm.tot[1] = a1;
+    }
+  }
+  __syncthreads();
+  const int tiles_m = sm.tot[0], tiles_g = sm.tot[1];
+  const int n_up = min((tiles_m + tiles_g) * N_UP_CHUNKS, a.max_items_up);
+  const int n_dn = min((tiles_m + tiles_g) * N_DN_CHUNKS, a.max_items_dn);
+  if (tid == 0) {
+    a.ctl[CTL_N_UP] = n_up;
+    a.ctl[CTL_N_DN] = n_dn;
+  }
+  for (int pass = 0; pass < 2; ++pass) {
+    const int nch = pass ? N_DN_CHUNKS : N_UP_CHUNKS;
+    const int n = pass ? n_dn : n_up;
+    Item* out = pass ? a.items_dn : a.items_up;
+    for (int i = tid; i < n; i += nth) {
+      const int ti = i / nch, chunk = i % nch;
+      const bool mf = ti < tiles_m;
+      const int* o = mf ? sm.it_m : sm.it_g;
+      const int li = mf ? ti : ti - tiles_m;
+      int lo = 0, hi = E;  // the expert e with o[e] <= li < o[e+1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (o[mid] <= li) lo = mid; else hi = mid;
+      }
+      const int tile = li - o[lo];
+      const int per = mf ? MFMA_BN : GV_GROUP;
+      const int p0 = sm.off[lo] + tile * per;
+      const int cnt = min(per, sm.cnt[lo] - tile * per);
+      uint32_t tk[GV_GROUP] = {0u, 0u, 0u, 0u};
+      if (!mf) {
+        for (int j = 0; j < cnt; ++j) tk[j] = (uint32_t)(a.perm[p0 + j] / K);
+      }
+      Item it;
+      it.head = item_head(lo, chunk, cnt, mf);
+      it.p0 = (uint32_t)p0;
+      it.t01 = tk[0] | (tk[1] << 16);
+      it.t23 = tk[2] | (tk[3] << 16);
+      out[i] = it;
+    }
+  }
+}
+
+__global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayerArgs a) {
+  const int t = blockIdx.x * (TK_THREADS / 64) + (threadIdx.x >> 6);
+  if (t < a.T) topk_token(a, t);
+}
+
+__global__ __launch_bounds__(BK_THREADS) void bucket_kernel(LayerArgs a) {
+  __shared__ BucketSmem sm;
+  build_buckets(a, sm);
+}
+
+hipError_t launch_topk(const LayerArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(topk_kernel, dim3(ceil_div(a.T, TK_THREADS / 64)), dim3(TK_THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bucket(const LayerArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(BK_THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -164,3 +164,26 @@ def test_forward_rejects_small_workspace_and_overlap(q4_layer):
         moe.moe_layer_forward(dl.handle, x.data_ptr(), 4097, y.data_ptr(), None, ws.data_ptr(), need,
                               moe.current_stream())
     assert e.value.status == moe.MOE_ERR_INVALID_ARG
+
+
+def test_staged_forward_matches_plain_forward(q4_layer):
+    """moe_layer_forward_staged records the stage events and computes the same bits."""
+    host, dl = q4_layer
+    say("case staged forward T=64")
+    x = x_to_dev(synth.make_x(64, xseed=11))
+    y0 = moe.layer_forward(dl, x)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(moe.N_STAGE_EVENTS)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    y1 = torch.empty_like(x)
+    ws = moe.alloc_workspace(dl.workspace_size(64))
+    moe.moe_layer_forward_staged(dl.handle, x.data_ptr(), 64, y1.data_ptr(), None, ws.data_ptr(), ws.numel(),
+                                 moe.current_stream(), [e.cuda_event for e in ev])
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    t = [ev[i].elapsed_time(ev[i + 1]) for i in range(moe.N_STAGE_EVENTS - 1)]
+    assert all(v >= 0 for v in t) and sum(t) > 0
+    with pytest.raises(moe.MoeError):
+        moe.moe_layer_forward_staged(dl.handle, x.data_ptr(), 64, y1.data_ptr(), None, ws.data_ptr(), ws.numel(),
+                                     moe.current_stream(), [e.cuda_event for e in ev[:3]])
