@@ -26,7 +26,10 @@ def build(verbose: bool = False) -> str:
                "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True, stderr=subprocess.PIPE if not verbose else None)
+        res = subprocess.run(cmd, stderr=subprocess.PIPE, text=True)
+        if res.returncode != 0:
+            print(res.stderr, flush=True)
+            raise RuntimeError(f"hipcc failed on {src}")
         objs.append(obj)
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]

@@ -17,8 +17,7 @@ enum Fmt : int { FMT_BF16 = 0, FMT_Q4_1 = 1, FMT_NVFP4 = 2 };
 // ---- work decomposition ---------------------------------------------------------
 // A bucket of m tokens is split into token groups of GV_GROUP (vector path) when
 // m < MFMA_MIN, else into token tiles of MFMA_BN (matrix-core path).  Both paths
-// cover UP_ROWS gate/up row pairs or DN_ROWS down rows per work item; DN_ROWS is
-// also the chunk the combine works on.
+// cover UP_ROWS gate/up row pairs or DN_ROWS down rows per work item.
 constexpr int GV_GROUP = 4;
 constexpr int MFMA_MIN = 65;
 constexpr int MFMA_BN = 64;

@@ -713,7 +713,8 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(LayerArgs a) {
     const int chunk = item_chunk(item.head);
     const int r0 = chunk * DN_ROWS;
     if (it.mfma) {
-      mfma_down<FMT>(a, D, mat, it, r0, sm);
+#pragma unroll 1
+      for (int rb = 0; rb < DN_ROWS; rb += 128) mfma_down<FMT>(a, D, mat, it, r0 + rb, sm);
     } else {
       constexpr int NRW = DN_ROWS / 4;  // rows per wave
 #pragma unroll 1

@@ -7,10 +7,11 @@
 // expert.  The router form (bf16 Linear d_model -> experts, fp32 softmax over
 // the chosen experts) is this library's reading of that statement.
 //
-// Three launches (kernel boundaries order the steps; no device-scope fences):
+// Kernel boundaries order the steps (no device-scope fences):
 //   router        partial logits part[ks][t][e] over 8 K-splits (MFMA 16x16x32 bf16);
 //   topk          one wave per token sums the 8 partials in split order, selects
-//                 the top k (ties to the lower id) and writes the weights;
+//                 the top k (ties to the lower id, wave-wide maximum of 64-bit
+//                 keys with permlane swaps and DPP) and writes the weights;
 //   bucket        one workgroup: histogram, exclusive prefix sum, a stable slot
 //                 permutation from per-expert token bitmasks and popcounts, its
 //                 inverse, and the FFN work lists.
@@ -111,27 +112,63 @@ constexpr int BK_THREADS = 1024;
 constexpr int BK_TC = 1024;                 // tokens per bitmask chunk
 constexpr int BK_WORDS = BK_TC / 32;        // mask words per expert
 
-// Candidate order: a live candidate beats a dead one (taken, or no such
-// expert); among live ones the larger logit wins, ties to the lower id.  NaN
-// logits are ordered as -inf, so k distinct valid ids always come out.
-__device__ inline bool better(bool al, float av, int ae, bool bl, float bv, int be) {
-  if (al != bl) return al;
-  return av > bv || (av == bv && ae < be);
+// Selection keys: (order-preserving bits of the logit) << 32 | (0xFFFF - id),
+// so the larger logit wins and equal logits go to the lower id.  NaN logits
+// are ordered as -inf; key 0 marks a taken candidate or a missing expert.
+__device__ inline uint32_t ordered_bits(float v) {
+  if (v != v) v = -INFINITY;
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ inline float from_ordered(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
+// Lane exchange for the wave-wide maximum: step m pairs lane i with i ^ m
+// (m = 4: with 7 - i inside groups of 8, which reaches the same set).
+template <int M> __device__ inline uint32_t xchg(uint32_t v) {
+  if constexpr (M == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
+  } else {
+    constexpr int ctrl = (M == 8) ? 0x128 : (M == 4) ? 0x141 : (M == 2) ? 0x4E : 0xB1;
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, ctrl, 0xF, 0xF, false);
+  }
+}
+template <int M> __device__ inline void max_step(uint32_t& hi, uint32_t& lo) {
+  const uint32_t ohi = xchg<M>(hi), olo = xchg<M>(lo);
+  const bool take = (ohi > hi) || (ohi == hi && olo > lo);
+  hi = take ? ohi : hi;
+  lo = take ? olo : lo;
+}
+__device__ inline uint64_t wave_max_key(uint64_t k) {
+  uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
+  max_step<32>(hi, lo);
+  max_step<16>(hi, lo);
+  max_step<8>(hi, lo);
+  max_step<4>(hi, lo);
+  max_step<2>(hi, lo);
+  max_step<1>(hi, lo);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// One wave: logits of token t (sum of the 8 partials in split order + bias),
+// the top k ids and their weights.
 __device__ void topk_token(const LayerArgs& a, int t) {
   const int lane = threadIdx.x & 63;
   const int T = a.T, E = a.E, K = a.K;
-  float v[4];
-  bool live[4];
+  uint64_t key[4];
   float mx = -INFINITY;
-  float raw[4];
+  float v[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    live[i] = e < E;
+    key[i] = 0;
     v[i] = -INFINITY;
-    if (live[i]) {
+    if (e < E) {
       float p[ROUTER_KS];
 #pragma unroll
       for (int ks = 0; ks < ROUTER_KS; ++ks) p[ks] = a.logit_part[((size_t)ks * T + t) * E + e];
@@ -139,23 +176,19 @@ __device__ void topk_token(const LayerArgs& a, int t) {
 #pragma unroll
       for (int ks = 0; ks < ROUTER_KS; ++ks) s += p[ks];
       if (a.router_b) s += a.router_b[e];
-      raw[i] = s;
+      if (a.write_logits) a.logits[(size_t)t * E + e] = s;
       v[i] = (s != s) ? -INFINITY : s;
+      key[i] = ((uint64_t)ordered_bits(s) << 32) | (uint64_t)(0xFFFFu - (uint32_t)e);
       mx = fmaxf(mx, v[i]);
     }
   }
-  if (a.write_logits) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (live[i]) a.logits[(size_t)t * E + lane + 64 * i] = raw[i];
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   float den_all = 0.f;
   if (!a.renorm) {
+    const uint64_t mk = wave_max_key(((uint64_t)ordered_bits(mx) << 32));
+    mx = from_ordered((uint32_t)(mk >> 32));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (live[i]) den_all += expf(v[i] - mx);
+      if (lane + 64 * i < E) den_all += expf(v[i] - mx);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) den_all += __shfl_xor(den_all, off);
   }
@@ -166,26 +199,16 @@ __device__ void topk_token(const LayerArgs& a, int t) {
     sel_v[j] = -INFINITY;
     sel_e[j] = 0;
     if (j >= K) continue;
-    bool bl = live[0];
-    float bv = v[0];
-    int be = lane;
+    uint64_t best = key[0];
 #pragma unroll
-    for (int i = 1; i < 4; ++i)
-      if (better(live[i], v[i], lane + 64 * i, bl, bv, be)) { bl = live[i]; bv = v[i]; be = lane + 64 * i; }
+    for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_key(best);
+    const int e = (int)(0xFFFFu - (uint32_t)(best & 0xFFFFu));
+    sel_e[j] = e;
+    sel_v[j] = from_ordered((uint32_t)(best >> 32));
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const bool ol = __shfl_xor((int)bl, off) != 0;
-      const float ov = __shfl_xor(bv, off);
-      const int oe = __shfl_xor(be, off);
-      if (better(ol, ov, oe, bl, bv, be)) { bl = ol; bv = ov; be = oe; }
-    }
-    sel_v[j] = bv;
-    sel_e[j] = be;
-    if ((be & 63) == lane) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (lane + 64 * i == be) live[i] = false;
-    }
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i == e) key[i] = 0;
   }
   if (lane < K) {
     float wv;
@@ -266,7 +289,7 @@ __device__ void build_buckets(const LayerArgs& a, BucketSmem& sm) {
 
   for (int t0 = 0; t0 < T; t0 += BK_TC) {
     const int words = min(BK_WORDS, ceil_div(T - t0, 32));
-    for (int i = tid; i < E * BK_WORDS; i += nth) sm.mask[i] = 0u;
+    for (int i = tid; i < E * words; i += nth) sm.mask[(i / words) * BK_WORDS + i % words] = 0u;
     __syncthreads();
     const int s0 = t0 * K, s1 = min(T, t0 + BK_TC) * K;
     for (int s = s0 + tid; s < s1; s += nth) {
@@ -315,40 +338,44 @@ __device__ void build_buckets(const LayerArgs& a, BucketSmem& sm) {
   }
   __syncthreads();
   const int tiles_m = sm.tot[0], tiles_g = sm.tot[1];
-  const int n_up = min((tiles_m + tiles_g) * N_UP_CHUNKS, a.max_items_up);
-  const int n_dn = min((tiles_m + tiles_g) * N_DN_CHUNKS, a.max_items_dn);
+  const int n_up = min((tiles_m + tiles_g) * N_UP_CHUNKS, a.max_items_up - a.max_items_up % N_UP_CHUNKS);
+  const int n_dn = min((tiles_m + tiles_g) * N_DN_CHUNKS, a.max_items_dn - a.max_items_dn % N_DN_CHUNKS);
   if (tid == 0) {
     a.ctl[CTL_N_UP] = n_up;
     a.ctl[CTL_N_DN] = n_dn;
   }
-  for (int pass = 0; pass < 2; ++pass) {
-    const int nch = pass ? N_DN_CHUNKS : N_UP_CHUNKS;
-    const int n = pass ? n_dn : n_up;
-    Item* out = pass ? a.items_dn : a.items_up;
-    for (int i = tid; i < n; i += nth) {
-      const int ti = i / nch, chunk = i % nch;
-      const bool mf = ti < tiles_m;
-      const int* o = mf ? sm.it_m : sm.it_g;
-      const int li = mf ? ti : ti - tiles_m;
-      int lo = 0, hi = E;  // the expert e with o[e] <= li < o[e+1]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (o[mid] <= li) lo = mid; else hi = mid;
-      }
-      const int tile = li - o[lo];
-      const int per = mf ? MFMA_BN : GV_GROUP;
-      const int p0 = sm.off[lo] + tile * per;
-      const int cnt = min(per, sm.cnt[lo] - tile * per);
-      uint32_t tk[GV_GROUP] = {0u, 0u, 0u, 0u};
-      if (!mf) {
-        for (int j = 0; j < cnt; ++j) tk[j] = (uint32_t)(a.perm[p0 + j] / K);
-      }
-      Item it;
-      it.head = item_head(lo, chunk, cnt, mf);
-      it.p0 = (uint32_t)p0;
-      it.t01 = tk[0] | (tk[1] << 16);
-      it.t23 = tk[2] | (tk[3] << 16);
-      out[i] = it;
+  // one thread per token tile: its N_UP_CHUNKS gate/up items and N_DN_CHUNKS down items
+  const int n_tiles = min(tiles_m + tiles_g, min(a.max_items_up / N_UP_CHUNKS, a.max_items_dn / N_DN_CHUNKS));
+  for (int ti = tid; ti < n_tiles; ti += nth) {
+    const bool mf = ti < tiles_m;
+    const int* o = mf ? sm.it_m : sm.it_g;
+    const int li = mf ? ti : ti - tiles_m;
+    int lo = 0, hi = E;  // the expert e with o[e] <= li < o[e+1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (o[mid] <= li) lo = mid; else hi = mid;
+    }
+    const int tile = li - o[lo];
+    const int per = mf ? MFMA_BN : GV_GROUP;
+    const int p0 = sm.off[lo] + tile * per;
+    const int cnt = min(per, sm.cnt[lo] - tile * per);
+    uint32_t tk[GV_GROUP] = {0u, 0u, 0u, 0u};
+    if (!mf) {
+      for (int j = 0; j < cnt; ++j) tk[j] = (uint32_t)(a.perm[p0 + j] / K);
+    }
+    Item it;
+    it.p0 = (uint32_t)p0;
+    it.t01 = tk[0] | (tk[1] << 16);
+    it.t23 = tk[2] | (tk[3] << 16);
+#pragma unroll
+    for (int c = 0; c < N_UP_CHUNKS; ++c) {
+      it.head = item_head(lo, c, cnt, mf);
+      a.items_up[ti * N_UP_CHUNKS + c] = it;
+    }
+#pragma unroll
+    for (int c = 0; c < N_DN_CHUNKS; ++c) {
+      it.head = item_head(lo, c, cnt, mf);
+      a.items_dn[ti * N_DN_CHUNKS + c] = it;
     }
   }
 }
