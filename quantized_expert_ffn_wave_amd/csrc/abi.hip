@@ -160,11 +160,6 @@ moe::LayerArgs make_args(const moe_layer* L, const void* x, int T, char* ws, con
   return a;
 }
 
-int ffn_grid(const moe_layer* L, int max_items) {
-  const int g = L->n_cu * 8;
-  return max_items < g ? max_items : g;
-}
-
 hipError_t copy_async(void* dst, const void* src, size_t bytes, hipStream_t s) {
   if (!dst || bytes == 0) return hipSuccess;
   return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
@@ -172,12 +167,6 @@ hipError_t copy_async(void* dst, const void* src, size_t bytes, hipStream_t s) {
 
 hipError_t mark(void* const* ev, int i, hipStream_t s) {
   return ev ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess;
-}
-
-int shared_grid(const moe_layer* L, int T, int chunks) {
-  const int items = moe::bucket_tiles(T) * chunks;
-  const int g = L->n_cu * 4;
-  return items < g ? items : g;
 }
 
 // One layer on stream s: the shared expert forks onto the handle's side stream
@@ -194,9 +183,10 @@ moe_status run_layer(moe_layer* L, moe::LayerArgs& a, const WsLayout& W, const m
   if (a.n_shared) {
     if ((e = hipEventRecord(L->fork, s)) != hipSuccess) return hip_fail(e, "fork record");
     if ((e = hipStreamWaitEvent(L->side, L->fork, 0)) != hipSuccess) return hip_fail(e, "fork wait");
-    if ((e = moe::launch_ffn_up(a, true, shared_grid(L, a.T, moe::N_UP_CHUNKS), L->side)) != hipSuccess)
+    const int tiles = moe::bucket_tiles(a.T);
+    if ((e = moe::launch_ffn(a, true, true, L->n_cu, tiles * moe::N_UP_CHUNKS, L->side)) != hipSuccess)
       return hip_fail(e, "shared gate/up launch");
-    if ((e = moe::launch_ffn_down(a, true, shared_grid(L, a.T, moe::N_DN_CHUNKS), L->side)) != hipSuccess)
+    if ((e = moe::launch_ffn(a, false, true, L->n_cu, tiles * moe::N_DN_CHUNKS, L->side)) != hipSuccess)
       return hip_fail(e, "shared down launch");
     if ((e = hipEventRecord(L->join, L->side)) != hipSuccess) return hip_fail(e, "join record");
   }
@@ -218,9 +208,9 @@ moe_status run_layer(moe_layer* L, moe::LayerArgs& a, const WsLayout& W, const m
       return hip_fail(e, "route copy");
   }
   if ((e = mark(ev, 3, s)) != hipSuccess) return hip_fail(e, "event record");
-  if ((e = moe::launch_ffn_up(a, false, ffn_grid(L, W.max_up), s)) != hipSuccess) return hip_fail(e, "gate/up launch");
+  if ((e = moe::launch_ffn(a, true, false, L->n_cu, W.max_up, s)) != hipSuccess) return hip_fail(e, "gate/up launch");
   if ((e = mark(ev, 4, s)) != hipSuccess) return hip_fail(e, "event record");
-  if ((e = moe::launch_ffn_down(a, false, ffn_grid(L, W.max_dn), s)) != hipSuccess) return hip_fail(e, "down launch");
+  if ((e = moe::launch_ffn(a, false, false, L->n_cu, W.max_dn, s)) != hipSuccess) return hip_fail(e, "down launch");
   if (a.n_shared && (e = hipStreamWaitEvent(s, L->join, 0)) != hipSuccess) return hip_fail(e, "join wait");
   if ((e = mark(ev, 5, s)) != hipSuccess) return hip_fail(e, "event record");
   if ((e = moe::launch_combine(a, s)) != hipSuccess) return hip_fail(e, "combine launch");

@@ -52,7 +52,7 @@ __device__ inline int item_count(uint32_t h) { return (int)((h >> 14) & 127u); }
 __device__ inline bool item_mfma(uint32_t h) { return (h & ITEM_MFMA) != 0; }
 
 // ---- control block ------------------------------------------------------------------
-enum Ctl : int { CTL_N_UP = 0, CTL_N_DN = 1, CTL_WORDS = 16 };
+enum Ctl : int { CTL_N_UP = 0, CTL_N_DN = 1, CTL_N_UP_MF = 2, CTL_N_DN_MF = 3, CTL_WORDS = 16 };
 
 struct QMat {
   const uint8_t* codes;   // q4_1/nvfp4 nibbles or bf16 elements
@@ -114,7 +114,8 @@ hipError_t launch_router(const LayerArgs& a, hipStream_t s);
 hipError_t launch_topk(const LayerArgs& a, hipStream_t s);
 hipError_t launch_bucket(const LayerArgs& a, hipStream_t s);
 hipError_t launch_combine(const LayerArgs& a, hipStream_t s);
-hipError_t launch_ffn_up(const LayerArgs& a, bool shared, int grid, hipStream_t s);
-hipError_t launch_ffn_down(const LayerArgs& a, bool shared, int grid, hipStream_t s);
+// gate/up (up) or down over the routed work list or the shared expert; at most
+// max_wgs workgroups, else as many as are resident on n_cu CUs at once
+hipError_t launch_ffn(const LayerArgs& a, bool up, bool shared, int n_cu, int max_wgs, hipStream_t s);
 hipError_t launch_stack_init(const uint16_t* x, float* r, uint16_t* xn, int T, float eps, hipStream_t s);
 }  // namespace moe

@@ -148,6 +148,46 @@ template <> struct GV<FMT_Q4_1> {
 #pragma unroll
     for (int t = 0; t < M; ++t) out[t] = d * lo[t] + c2 * hi[t] + c3 * x[t].se + c4 * x[t].so;
   }
+  // single-token form: nibbles unpacked once per row, then one dot per token
+  struct U { uint32_t A[4], B[4], C[4], D[4]; float d, c2, c3, c4; };
+  static __device__ void unpack(U& u, const Raw& r, float) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = r.c[j], w8 = w >> 8;
+      u.A[j] = (w & 0x000F000Fu) | MAGIC;
+      u.B[j] = (w & 0x00F000F0u) | MAGIC;
+      u.C[j] = (w8 & 0x000F000Fu) | MAGIC;
+      u.D[j] = (w8 & 0x00F000F0u) | MAGIC;
+    }
+    const float d = f16lo(r.dm), m = f16hi(r.dm);
+    u.d = d;
+    u.c2 = d * 0.0625f;
+    u.c3 = m - 1024.f * d;
+    u.c4 = m - 64.f * d;
+  }
+  static __device__ float dot1(const U& u, const X& x) {
+    float lo = 0.f, hi = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo = dot2h(u.A[j], x.p[4 * j + 0], lo);
+      hi = dot2h(u.B[j], x.p[4 * j + 1], hi);
+      lo = dot2h(u.C[j], x.p[4 * j + 2], lo);
+      hi = dot2h(u.D[j], x.p[4 * j + 3], hi);
+    }
+    return u.d * lo + u.c2 * hi + u.c3 * x.se + u.c4 * x.so;
+  }
+  // even/odd sums of a chunk stored in nibble order: pairs 0 and 2 of each group
+  // of four hold even elements, pairs 1 and 3 odd ones
+  static __device__ void sums(X& x) {
+    float se = 0.f, so = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      se += f16lo(x.p[4 * j]) + f16hi(x.p[4 * j]) + f16lo(x.p[4 * j + 2]) + f16hi(x.p[4 * j + 2]);
+      so += f16lo(x.p[4 * j + 1]) + f16hi(x.p[4 * j + 1]) + f16lo(x.p[4 * j + 3]) + f16hi(x.p[4 * j + 3]);
+    }
+    x.se = se;
+    x.so = so;
+  }
   // 32 decoded weights as 16 fp16 pairs in nibble order (matrix-core path):
   // fp16(d*q + m), rounded once.
   static __device__ void decode(const Raw& r, uint32_t* o) {
@@ -202,6 +242,27 @@ template <> struct GV<FMT_NVFP4> {
 #pragma unroll
     for (int t = 0; t < M; ++t) out[t] = s0 * a0[t] + s1 * a1[t];
   }
+  struct U { uint32_t P[16]; float s0, s1; };
+  static __device__ void unpack(U& u, const Raw& r, float ts) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u.P[4 * j + 0] = fp4x2_to_f16x2<0>(r.c[j]);
+      u.P[4 * j + 1] = fp4x2_to_f16x2<1>(r.c[j]);
+      u.P[4 * j + 2] = fp4x2_to_f16x2<2>(r.c[j]);
+      u.P[4 * j + 3] = fp4x2_to_f16x2<3>(r.c[j]);
+    }
+    u.s0 = __builtin_amdgcn_cvt_f32_fp8(r.s, 0) * ts;
+    u.s1 = __builtin_amdgcn_cvt_f32_fp8(r.s, 1) * ts;
+  }
+  static __device__ float dot1(const U& u, const X& x) {
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a0 = dot2h(u.P[i], x.p[i], a0);
+#pragma unroll
+    for (int i = 8; i < 16; ++i) a1 = dot2h(u.P[i], x.p[i], a1);
+    return u.s0 * a0 + u.s1 * a1;
+  }
+  static __device__ void sums(X&) {}
   // E2M1 * E4M3 is exact in fp16; the per-matrix scale is applied after the MFMA.
   static __device__ void decode(const Raw& r, uint32_t* o) {
     const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8(r.s, 0);
@@ -240,6 +301,18 @@ template <> struct GV<FMT_BF16> {
       out[t] = a;
     }
   }
+  struct U { uint32_t P[16]; };
+  static __device__ void unpack(U& u, const Raw& r, float) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u.P[i] = r.c[i >> 2][i & 3];
+  }
+  static __device__ float dot1(const U& u, const X& x) {
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = dot2b(u.P[i], x.p[i], a);
+    return a;
+  }
+  static __device__ void sums(X&) {}
   static __device__ void decode(const Raw& r, uint32_t* o) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[i] = r.c[i >> 2][i & 3];
@@ -369,116 +442,316 @@ __device__ inline int shared_items(int T, int chunks) { return bucket_tiles(T) *
 // Vector-path items
 // ======================================================================================
 
-// Rows in flight per wave (a ring of register buffers): one row pair (up) or
-// one 4-row group (down) per slot.
-template <int FMT> constexpr int UP_RING = (FMT == FMT_BF16) ? 2 : 4;
-template <int FMT> constexpr int DN_RING = (FMT == FMT_BF16) ? 4 : 8;
+// ======================================================================================
+// Vector path as a continuous stream.  A persistent workgroup walks its chunks
+// c, c + G, c + 2G, ... (G = grid size).  A chunk is one token group (<= 4
+// tokens) of one expert times UP_ROWS row pairs (gate/up) or DN_ROWS rows
+// (down); each wave owns a fixed quarter of the chunk's rows.  The activations
+// of the chunk's tokens sit in LDS (double buffered: the next chunk's are
+// loaded during this one), and every wave keeps a ring of weight-row loads in
+// flight that runs on into the next chunk, so the weight stream never drains
+// between chunks.
+// ======================================================================================
+template <int FMT> constexpr int UP_RING = (FMT == FMT_BF16) ? 2 : 4;  // row pairs in flight per wave
+template <int FMT> constexpr int DN_RING = (FMT == FMT_BF16) ? 4 : 8;  // 4-row groups in flight per wave
+constexpr int UP_STEPS = UP_ROWS / 4;        // row pairs per wave per chunk (16)
+constexpr int DN_STEPS = DN_ROWS / 16;       // 4-row groups per wave per chunk (8)
 
-// gate/up + SwiGLU for NRW row pairs from n0 of one wave; lane owns chunk
-// `lane` of the 2048-long rows.  A ring of D row pairs is in flight: the
-// first D are issued before the activations are read; each step consumes one
-// slot and then refills that same slot (so no register copies and no full
-// drain of the load counter happen between steps); the last D steps only drain.
-template <int FMT, int M, int NRW>
-__device__ void gemv_up_wave(const LayerArgs& a, const QMat& G, const QMat& Uq, int mat, const ItemTok& it, int n0) {
+// Activations of a chunk in LDS: [buffer][token][piece j][slot][16 B]; piece j
+// of a slot holds elements 8j..8j+7 of that slot's 32-element chunk (already in
+// the format's operand type and k order).  Gate/up: slot = lane (2048-long
+// rows); down: slot = lane & 15 (512-long rows).
+struct GvSmem {
+  u32x4 x[2][GV_GROUP][4][64];
+};
+
+// Loads of one chunk's activations into registers: thread (slot = tid / 4,
+// piece = tid % 4) takes 8 elements of each token (zeros for absent tokens).
+struct XStage {
+  u32x4 v[GV_GROUP];
+};
+
+template <int FMT, bool UP>
+__device__ inline void xstage_load(const LayerArgs& a, const ItemTok& it, XStage& st) {
+  const int tid = threadIdx.x;
+  const int slot = tid >> 2, piece = tid & 3;
+#pragma unroll
+  for (int t = 0; t < GV_GROUP; ++t) {
+    st.v[t] = u32x4{0u, 0u, 0u, 0u};
+    if (t < it.cnt && (UP || slot < 16)) {
+      const uint16_t* src = UP ? a.x + (size_t)tok_of(a, it, t) * D_MODEL + 32 * slot + 8 * piece
+                               : a.h + (size_t)row_of(a, it, t) * D_FF + 32 * slot + 8 * piece;
+      st.v[t] = ld16<false>(src);
+    }
+  }
+}
+
+template <int FMT, bool UP>
+__device__ inline void xstage_store(const XStage& st, GvSmem& sm, int buf) {
+  const int tid = threadIdx.x;
+  const int slot = tid >> 2, piece = tid & 3;
+  if (!UP && slot >= 16) return;
+#pragma unroll
+  for (int t = 0; t < GV_GROUP; ++t) {
+    uint32_t n[4] = {st.v[t][0], st.v[t][1], st.v[t][2], st.v[t][3]};
+    if (OPER_F16<FMT> && UP) {  // x arrives as bf16; the stored SwiGLU output is already operand typed
+#pragma unroll
+      for (int i = 0; i < 4; ++i) n[i] = bf16x2_to_f16x2(n[i]);
+    }
+    uint32_t o[4];
+    if (FMT == FMT_Q4_1) {
+      q4_order(n[0], n[1], n[2], n[3], o);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = n[i];
+    }
+    sm.x[buf][t][piece][slot] = u32x4{o[0], o[1], o[2], o[3]};
+  }
+}
+
+template <int FMT>
+__device__ inline void x_from_lds(typename GV<FMT>::X& x, const GvSmem& sm, int buf, int t, int slot) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4 v = sm.x[buf][t][j][slot];
+    x.p[4 * j] = v[0]; x.p[4 * j + 1] = v[1]; x.p[4 * j + 2] = v[2]; x.p[4 * j + 3] = v[3];
+  }
+}
+
+// Weight matrices of a chunk's expert (uniform across the workgroup).
+struct ChunkW {
+  QMat g, u;   // gate/up (or the down matrix in g)
+  int mat;
+  float tsg, tsu;
+};
+
+template <int FMT, bool SHARED, bool UP>
+__device__ inline ChunkW chunk_weights(const LayerArgs& a, const Item& item) {
+  ChunkW w;
+  const int e = SHARED ? 0 : item_expert(item.head);
+  w.mat = e;
+  if (UP) {
+    w.g = SHARED ? a.sh_gate : a.gate;
+    w.u = SHARED ? a.sh_up : a.up;
+  } else {
+    w.g = SHARED ? a.sh_down : a.down;
+    w.u = w.g;
+  }
+  w.tsg = (FMT == FMT_NVFP4) ? w.g.ts[e] : 1.f;
+  w.tsu = (FMT == FMT_NVFP4) ? w.u.ts[e] : 1.f;
+  return w;
+}
+
+template <bool SHARED>
+__device__ inline Item fetch_item(const LayerArgs& a, const Item* list, int idx, int chunks) {
+  return SHARED ? shared_item(a.T, a.E, idx, chunks) : list[idx];
+}
+
+// One chunk of gate/up for MT token slots (slots >= the item's count hold zero
+// activations): UP_STEPS row pairs per wave from the ring, each slot refilled
+// with the row UP_RING steps ahead, which past the chunk's end is a row of the
+// next chunk (nw, nr0) when there is one.
+template <int FMT, int MT>
+__device__ inline void up_chunk(typename GV<FMT>::Raw* rg, typename GV<FMT>::Raw* ru, const ChunkW& w, size_t r0,
+                                const ChunkW& nw, size_t nr0, bool has_next, const GvSmem& sm, int buf, int cnt,
+                                uint16_t* hbase) {
   using F = GV<FMT>;
   constexpr int D = UP_RING<FMT>;
-  static_assert(NRW % D == 0 && NRW >= D, "ring must divide the rows of a wave");
   const int lane = threadIdx.x & 63;
-  const size_t rbase = (size_t)mat * D_FF + n0;
+  typename F::X xs[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    x_from_lds<FMT>(xs[t], sm, buf, t, lane);
+    F::sums(xs[t]);
+  }
+  bool wr;
+  const int my_t = xreduce_index<2 * MT, 64>(lane, wr) % MT;
+  const bool writer = lane < 32 && wr && my_t < cnt;
+#pragma unroll
+  for (int s = 0; s < UP_STEPS; ++s) {
+    const int slot = s % D;
+    typename F::U ug, uu;
+    F::unpack(ug, rg[slot], w.tsg);
+    F::unpack(uu, ru[slot], w.tsu);
+    if (s + D < UP_STEPS) {
+      rg[slot] = F::template load<true>(w.g, r0 + s + D, lane, D_MODEL);
+      ru[slot] = F::template load<true>(w.u, r0 + s + D, lane, D_MODEL);
+    } else if (has_next) {
+      rg[slot] = F::template load<true>(nw.g, nr0 + s + D - UP_STEPS, lane, D_MODEL);
+      ru[slot] = F::template load<true>(nw.u, nr0 + s + D - UP_STEPS, lane, D_MODEL);
+    }
+    float v[2 * MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      v[t] = F::dot1(ug, xs[t]);
+      v[MT + t] = F::dot1(uu, xs[t]);
+    }
+    // gate sums land in lanes < 32, the matching up sums in lane ^ 32
+    xreduce<2 * MT, 64>(v);
+    const float u = __shfl_xor(v[0], 32);
+    if (writer) hbase[(size_t)my_t * D_FF + s] = h_store<FMT>(silu_mul(v[0], u));
+  }
+}
+
+// gate/up + SwiGLU over vector-path chunks [0, n) of `list` (or of the shared
+// expert), this workgroup taking c = blockIdx.x, +gridDim.x, ...
+template <int FMT, bool SHARED>
+__device__ void up_stream(const LayerArgs& a, const Item* list, int n, GvSmem& sm) {
+  using F = GV<FMT>;
+  constexpr int D = UP_RING<FMT>;
+  static_assert(UP_STEPS % D == 0, "ring must divide the steps of a chunk");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int c = blockIdx.x;
+  if (c >= n) return;
+  Item item = fetch_item<SHARED>(a, list, c, N_UP_CHUNKS);
+  ItemTok it = item_tokens(item, SHARED);
+  ChunkW w = chunk_weights<FMT, SHARED, true>(a, item);
+  // this wave's row pairs of a chunk: first_row + s, s = 0 .. UP_STEPS-1
+  auto first_row = [&](const Item& itm, const ChunkW& cw) {
+    return (size_t)cw.mat * D_FF + item_chunk(itm.head) * UP_ROWS + wave * UP_STEPS;
+  };
+  size_t r0 = first_row(item, w);
   typename F::Raw rg[D], ru[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
-    rg[i] = F::template load<true>(G, rbase + i, lane, D_MODEL);
-    ru[i] = F::template load<true>(Uq, rbase + i, lane, D_MODEL);
+    rg[i] = F::template load<true>(w.g, r0 + i, lane, D_MODEL);
+    ru[i] = F::template load<true>(w.u, r0 + i, lane, D_MODEL);
   }
-  typename F::X x[M];
-#pragma unroll
-  for (int t = 0; t < M; ++t) {
-    uint32_t src[16];
-    if (t < it.cnt) {
-      load_act<FMT>(src, a.x + (size_t)tok_of(a, it, t) * D_MODEL + 32 * lane, true);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) src[i] = 0u;
-    }
-    F::prep(x[t], src);
+  int buf = 0;
+  {
+    XStage st;
+    xstage_load<FMT, true>(a, it, st);
+    xstage_store<FMT, true>(st, sm, buf);
   }
-  const float tsg = (FMT == FMT_NVFP4) ? G.ts[mat] : 1.f;
-  const float tsu = (FMT == FMT_NVFP4) ? Uq.ts[mat] : 1.f;
-  bool wr;
-  const int idx = xreduce_index<2 * M, 64>(lane, wr);
-  const int my_t = idx % M;  // lanes < 32 hold gate sums of token my_t, lane + 32 the up sums
-  uint16_t* hrow = a.h + (size_t)row_of(a, it, my_t < it.cnt ? my_t : 0) * D_FF + n0;
-  const bool writer = lane < 32 && wr && my_t < it.cnt;
-  auto step = [&](int i, int r) {
-    float v[2 * M];
-    F::template dot<M>(rg[i], x, v, tsg);
-    F::template dot<M>(ru[i], x, v + M, tsu);
-    xreduce<2 * M, 64>(v);
-    const float u = __shfl_xor(v[0], 32);
-    if (writer) hrow[r] = h_store<FMT>(silu_mul(v[0], u));
-  };
+  __syncthreads();
 #pragma unroll 1
-  for (int b = 0; b < NRW - D; b += D) {
-#pragma unroll
-    for (int i = 0; i < D; ++i) {
-      step(i, b + i);
-      rg[i] = F::template load<true>(G, rbase + b + i + D, lane, D_MODEL);
-      ru[i] = F::template load<true>(Uq, rbase + b + i + D, lane, D_MODEL);
+  for (;;) {
+    const int nc = c + gridDim.x;
+    const bool has_next = nc < n;
+    Item nitem = item;
+    ItemTok nit = it;
+    ChunkW nw = w;
+    size_t nr0 = r0;
+    XStage st;
+    if (has_next) {
+      nitem = fetch_item<SHARED>(a, list, nc, N_UP_CHUNKS);
+      nit = item_tokens(nitem, SHARED);
+      nw = chunk_weights<FMT, SHARED, true>(a, nitem);
+      nr0 = first_row(nitem, nw);
+      xstage_load<FMT, true>(a, nit, st);
     }
+    const int cnt = it.cnt;
+    uint16_t* hbase = a.h + (size_t)row_of(a, it, 0) * D_FF + item_chunk(item.head) * UP_ROWS + wave * UP_STEPS;
+    if (cnt <= 1) up_chunk<FMT, 1>(rg, ru, w, r0, nw, nr0, has_next, sm, buf, cnt, hbase);
+    else if (cnt <= 2) up_chunk<FMT, 2>(rg, ru, w, r0, nw, nr0, has_next, sm, buf, cnt, hbase);
+    else up_chunk<FMT, GV_GROUP>(rg, ru, w, r0, nw, nr0, has_next, sm, buf, cnt, hbase);
+    if (!has_next) break;
+    xstage_store<FMT, true>(st, sm, buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    c = nc;
+    item = nitem;
+    it = nit;
+    w = nw;
+    r0 = nr0;
   }
-#pragma unroll
-  for (int i = 0; i < D; ++i) step(i, NRW - D + i);
 }
 
-// down rows r0 .. r0+4*NG-1 of one wave: 16 lanes per 512-long row, 4 rows per
-// load (one ring slot); lane owns chunk (lane & 15) of its row.  Same ring
-// discipline as the gate/up wave.
-template <int FMT, int M, int NG>
-__device__ void gemv_down_wave(const LayerArgs& a, const QMat& D, int mat, const ItemTok& it, int r0) {
+// One chunk of down for MT token slots: DN_STEPS groups of 4 rows per wave (16
+// lanes per 512-long row), ring refilled as in up_chunk.
+template <int FMT, int MT>
+__device__ inline void down_chunk(typename GV<FMT>::Raw* ring, const ChunkW& w, size_t r0, const ChunkW& nw,
+                                  size_t nr0, bool has_next, const GvSmem& sm, int buf, int cnt, float* ybase) {
   using F = GV<FMT>;
-  constexpr int R = DN_RING<FMT> < NG ? DN_RING<FMT> : NG;
-  static_assert(NG % R == 0, "ring must divide the row groups of a wave");
-  const int lane = threadIdx.x & 63;
-  const int chunk = lane & 15, rsub = lane >> 4;
-  const size_t rbase = (size_t)mat * D_MODEL + r0 + rsub;
+  constexpr int R = DN_RING<FMT> < DN_STEPS ? DN_RING<FMT> : DN_STEPS;
+  const int slot16 = threadIdx.x & 15;
+  typename F::X xs[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    x_from_lds<FMT>(xs[t], sm, buf, t, slot16);
+    F::sums(xs[t]);
+  }
+  bool wr;
+  const int my_t = xreduce_index<MT, 16>(slot16, wr) % MT;
+  const bool writer = wr && my_t < cnt;
+#pragma unroll
+  for (int g = 0; g < DN_STEPS; ++g) {
+    const int slot = g % R;
+    typename F::U u;
+    F::unpack(u, ring[slot], w.tsg);
+    if (g + R < DN_STEPS) {
+      ring[slot] = F::template load<true>(w.g, r0 + 4 * (g + R), slot16, D_FF);
+    } else if (has_next) {
+      ring[slot] = F::template load<true>(nw.g, nr0 + 4 * (g + R - DN_STEPS), slot16, D_FF);
+    }
+    float v[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) v[t] = F::dot1(u, xs[t]);
+    xreduce<MT, 16>(v);
+    if (writer) ybase[(size_t)my_t * D_MODEL + 4 * g] = v[0];
+  }
+}
+
+// down over vector-path chunks, workgroup-strided as up_stream
+template <int FMT, bool SHARED>
+__device__ void down_stream(const LayerArgs& a, const Item* list, int n, GvSmem& sm) {
+  using F = GV<FMT>;
+  constexpr int R = DN_RING<FMT> < DN_STEPS ? DN_RING<FMT> : DN_STEPS;
+  static_assert(DN_STEPS % R == 0, "ring must divide the steps of a chunk");
+  const int wave = threadIdx.x >> 6;
+  const int slot16 = threadIdx.x & 15, rsub = (threadIdx.x & 63) >> 4;
+  int c = blockIdx.x;
+  if (c >= n) return;
+  Item item = fetch_item<SHARED>(a, list, c, N_DN_CHUNKS);
+  ItemTok it = item_tokens(item, SHARED);
+  ChunkW w = chunk_weights<FMT, SHARED, false>(a, item);
+  // rows of this lane: first_row + 4 g, g = 0 .. DN_STEPS-1
+  auto first_row = [&](const Item& itm, const ChunkW& cw) {
+    return (size_t)cw.mat * D_MODEL + item_chunk(itm.head) * DN_ROWS + wave * (DN_ROWS / 4) + rsub;
+  };
+  size_t r0 = first_row(item, w);
   typename F::Raw ring[R];
 #pragma unroll
-  for (int i = 0; i < R; ++i) ring[i] = F::template load<true>(D, rbase + 4 * i, chunk, D_FF);
-  typename F::X x[M];
-#pragma unroll
-  for (int t = 0; t < M; ++t) {
-    uint32_t src[16];
-    if (t < it.cnt) {
-      load_act<FMT>(src, a.h + (size_t)row_of(a, it, t) * D_FF + 32 * chunk, false);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) src[i] = 0u;
-    }
-    F::prep(x[t], src);
+  for (int i = 0; i < R; ++i) ring[i] = F::template load<true>(w.g, r0 + 4 * i, slot16, D_FF);
+  int buf = 0;
+  {
+    XStage st;
+    xstage_load<FMT, false>(a, it, st);
+    xstage_store<FMT, false>(st, sm, buf);
   }
-  const float ts = (FMT == FMT_NVFP4) ? D.ts[mat] : 1.f;
-  bool wr;
-  const int my_t = xreduce_index<M, 16>(lane & 15, wr) % M;
-  float* yrow = a.y + (size_t)row_of(a, it, my_t < it.cnt ? my_t : 0) * D_MODEL + r0 + rsub;
-  const bool writer = wr && my_t < it.cnt;
-  auto step = [&](int i, int g) {
-    float v[M];
-    F::template dot<M>(ring[i], x, v, ts);
-    xreduce<M, 16>(v);
-    if (writer) yrow[4 * g] = v[0];
-  };
+  __syncthreads();
 #pragma unroll 1
-  for (int b = 0; b < NG - R; b += R) {
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      step(i, b + i);
-      ring[i] = F::template load<true>(D, rbase + 4 * (b + i + R), chunk, D_FF);
+  for (;;) {
+    const int nc = c + gridDim.x;
+    const bool has_next = nc < n;
+    Item nitem = item;
+    ItemTok nit = it;
+    ChunkW nw = w;
+    size_t nr0 = r0;
+    XStage st;
+    if (has_next) {
+      nitem = fetch_item<SHARED>(a, list, nc, N_DN_CHUNKS);
+      nit = item_tokens(nitem, SHARED);
+      nw = chunk_weights<FMT, SHARED, false>(a, nitem);
+      nr0 = first_row(nitem, nw);
+      xstage_load<FMT, false>(a, nit, st);
     }
+    const int cnt = it.cnt;
+    float* ybase =
+        a.y + (size_t)row_of(a, it, 0) * D_MODEL + item_chunk(item.head) * DN_ROWS + wave * (DN_ROWS / 4) + rsub;
+    if (cnt <= 1) down_chunk<FMT, 1>(ring, w, r0, nw, nr0, has_next, sm, buf, cnt, ybase);
+    else if (cnt <= 2) down_chunk<FMT, 2>(ring, w, r0, nw, nr0, has_next, sm, buf, cnt, ybase);
+    else down_chunk<FMT, GV_GROUP>(ring, w, r0, nw, nr0, has_next, sm, buf, cnt, ybase);
+    if (!has_next) break;
+    xstage_store<FMT, false>(st, sm, buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    c = nc;
+    item = nitem;
+    it = nit;
+    w = nw;
+    r0 = nr0;
   }
-#pragma unroll
-  for (int i = 0; i < R; ++i) step(i, NG - R + i);
 }
 
 // ======================================================================================
@@ -525,7 +798,8 @@ __device__ inline f32x16 mfma32(const uint16_t* a, const uint16_t* b, f32x16 c) 
 __device__ inline void mfma_tables(const LayerArgs& a, const ItemTok& it, FfnSmem& sm) {
   const int i = threadIdx.x;
   if (i < MFMA_BN) {
-    sm.tok[i] = (i < it.cnt) ? tok_of(a, it, i) : -1;
+    // matrix-core tiles are shared-expert tiles or routed buckets (tokens via perm)
+    sm.tok[i] = (i < it.cnt) ? (it.shared ? it.p0 + i : a.perm[it.p0 + i] / a.K) : -1;
     sm.row[i] = (i < it.cnt) ? row_of(a, it, i) : -1;
   }
 }
@@ -667,96 +941,89 @@ __device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const Item
 // ======================================================================================
 // Persistent kernels
 // ======================================================================================
+// Workgroups per CU the persistent kernels are compiled for: two for the 4-bit
+// formats (their rings fit in half the register file), one for bf16.
+template <int FMT> constexpr int FFN_WG_PER_CU = (FMT == FMT_BF16) ? 1 : 2;
+
+// Items of the matrix-core path come first; the vector-path chunks follow.
 template <int FMT, bool SHARED>
-__global__ __launch_bounds__(256) void ffn_up_kernel(LayerArgs a) {
-  __shared__ FfnSmem sm;
-  const int n_items = SHARED ? shared_items(a.T, N_UP_CHUNKS) : a.ctl[CTL_N_UP];
-  const int wave = threadIdx.x >> 6;
-  for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
-    const Item item = SHARED ? shared_item(a.T, a.E, i, N_UP_CHUNKS) : a.items_up[i];
-    const int e = SHARED ? a.E : item_expert(item.head);
-    const QMat& G = SHARED ? a.sh_gate : a.gate;
-    const QMat& U = SHARED ? a.sh_up : a.up;
-    const int mat = SHARED ? 0 : e;
-    const ItemTok it = item_tokens(item, SHARED);
-    const int n0 = item_chunk(item.head) * UP_ROWS;
-    if (it.mfma) {
-      mfma_up<FMT>(a, G, U, mat, it, n0, sm);
-    } else {
-      constexpr int NRW = UP_ROWS / 4;  // row pairs per wave
-      // up to two tokens per pass; a second pass re-reads the rows from cache
-#pragma unroll 1
-      for (int tp = 0; tp < it.cnt; tp += 2) {
-        ItemTok sub = it;
-        sub.p0 += tp;
-        sub.cnt = min(2, it.cnt - tp);
-        sub.tok[0] = tp ? it.tok[2] : it.tok[0];
-        sub.tok[1] = tp ? it.tok[3] : it.tok[1];
-        if (sub.cnt == 1) gemv_up_wave<FMT, 1, NRW>(a, G, U, mat, sub, n0 + wave * NRW);
-        else gemv_up_wave<FMT, 2, NRW>(a, G, U, mat, sub, n0 + wave * NRW);
-      }
-    }
+__global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_up_kernel(LayerArgs a) {
+  __shared__ union {
+    FfnSmem mf;
+    GvSmem gv;
+  } sm;
+  const bool shared_mfma = bucket_mfma(a.T);
+  const int n_all = SHARED ? shared_items(a.T, N_UP_CHUNKS) : a.ctl[CTL_N_UP];
+  const int n_mf = SHARED ? (shared_mfma ? n_all : 0) : a.ctl[CTL_N_UP_MF];
+  for (int i = blockIdx.x; i < n_mf; i += gridDim.x) {
+    const Item item = fetch_item<SHARED>(a, a.items_up, i, N_UP_CHUNKS);
+    const int e = SHARED ? 0 : item_expert(item.head);
+    mfma_up<FMT>(a, SHARED ? a.sh_gate : a.gate, SHARED ? a.sh_up : a.up, e, item_tokens(item, SHARED),
+                 item_chunk(item.head) * UP_ROWS, sm.mf);
+  }
+  if (SHARED) {
+    if (!shared_mfma) up_stream<FMT, true>(a, nullptr, n_all, sm.gv);
+  } else {
+    up_stream<FMT, false>(a, a.items_up + n_mf, n_all - n_mf, sm.gv);
   }
 }
 
 template <int FMT, bool SHARED>
-__global__ __launch_bounds__(256) void ffn_down_kernel(LayerArgs a) {
-  __shared__ FfnSmem sm;
-  const int n_items = SHARED ? shared_items(a.T, N_DN_CHUNKS) : a.ctl[CTL_N_DN];
-  const int wave = threadIdx.x >> 6;
-  for (int i = blockIdx.x; i < n_items; i += gridDim.x) {
-    const Item item = SHARED ? shared_item(a.T, a.E, i, N_DN_CHUNKS) : a.items_dn[i];
-    const int e = SHARED ? a.E : item_expert(item.head);
-    const QMat& D = SHARED ? a.sh_down : a.down;
-    const int mat = SHARED ? 0 : e;
+__global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_down_kernel(LayerArgs a) {
+  __shared__ union {
+    FfnSmem mf;
+    GvSmem gv;
+  } sm;
+  const bool shared_mfma = bucket_mfma(a.T);
+  const int n_all = SHARED ? shared_items(a.T, N_DN_CHUNKS) : a.ctl[CTL_N_DN];
+  const int n_mf = SHARED ? (shared_mfma ? n_all : 0) : a.ctl[CTL_N_DN_MF];
+  for (int i = blockIdx.x; i < n_mf; i += gridDim.x) {
+    const Item item = fetch_item<SHARED>(a, a.items_dn, i, N_DN_CHUNKS);
+    const int e = SHARED ? 0 : item_expert(item.head);
     const ItemTok it = item_tokens(item, SHARED);
-    const int chunk = item_chunk(item.head);
-    const int r0 = chunk * DN_ROWS;
-    if (it.mfma) {
+    const int r0 = item_chunk(item.head) * DN_ROWS;
 #pragma unroll 1
-      for (int rb = 0; rb < DN_ROWS; rb += 128) mfma_down<FMT>(a, D, mat, it, r0 + rb, sm);
-    } else {
-      constexpr int NRW = DN_ROWS / 4;  // rows per wave
-#pragma unroll 1
-      for (int tp = 0; tp < it.cnt; tp += 2) {
-        ItemTok sub = it;
-        sub.p0 += tp;
-        sub.cnt = min(2, it.cnt - tp);
-        sub.tok[0] = tp ? it.tok[2] : it.tok[0];
-        sub.tok[1] = tp ? it.tok[3] : it.tok[1];
-        if (sub.cnt == 1) gemv_down_wave<FMT, 1, NRW / 4>(a, D, mat, sub, r0 + wave * NRW);
-        else gemv_down_wave<FMT, 2, NRW / 4>(a, D, mat, sub, r0 + wave * NRW);
-      }
-    }
+    for (int rb = 0; rb < DN_ROWS; rb += 128) mfma_down<FMT>(a, SHARED ? a.sh_down : a.down, e, it, r0 + rb, sm.mf);
+  }
+  if (SHARED) {
+    if (!shared_mfma) down_stream<FMT, true>(a, nullptr, n_all, sm.gv);
+  } else {
+    down_stream<FMT, false>(a, a.items_dn + n_mf, n_all - n_mf, sm.gv);
   }
 }
 
-template <int FMT>
-hipError_t launch_up_fmt(const LayerArgs& a, bool shared, int grid, hipStream_t s) {
-  if (shared) hipLaunchKernelGGL((ffn_up_kernel<FMT, true>), dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((ffn_up_kernel<FMT, false>), dim3(grid), dim3(256), 0, s, a);
-  return hipGetLastError();
+// Workgroups of `kernel` that fit on one CU at once (the persistent kernels are
+// launched with exactly the resident count, so none waits for a free slot).
+template <typename Kern>
+int resident_per_cu(Kern kernel) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess || n < 1) n = 1;
+  return n;
 }
-template <int FMT>
-hipError_t launch_down_fmt(const LayerArgs& a, bool shared, int grid, hipStream_t s) {
-  if (shared) hipLaunchKernelGGL((ffn_down_kernel<FMT, true>), dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((ffn_down_kernel<FMT, false>), dim3(grid), dim3(256), 0, s, a);
+
+template <int FMT, bool SHARED>
+hipError_t launch_ffn_kernel(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s) {
+  static const int occ_up = resident_per_cu(ffn_up_kernel<FMT, SHARED>);
+  static const int occ_dn = resident_per_cu(ffn_down_kernel<FMT, SHARED>);
+  int grid = n_cu * (up ? occ_up : occ_dn);
+  if (max_wgs < grid) grid = max_wgs;
+  if (grid < 1) return hipSuccess;
+  if (up) hipLaunchKernelGGL((ffn_up_kernel<FMT, SHARED>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((ffn_down_kernel<FMT, SHARED>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_up(const LayerArgs& a, bool shared, int grid, hipStream_t s) {
-  switch (a.fmt) {
-    case FMT_Q4_1: return launch_up_fmt<FMT_Q4_1>(a, shared, grid, s);
-    case FMT_NVFP4: return launch_up_fmt<FMT_NVFP4>(a, shared, grid, s);
-    default: return launch_up_fmt<FMT_BF16>(a, shared, grid, s);
-  }
+template <int FMT>
+hipError_t launch_ffn_fmt(const LayerArgs& a, bool up, bool shared, int n_cu, int max_wgs, hipStream_t s) {
+  return shared ? launch_ffn_kernel<FMT, true>(a, up, n_cu, max_wgs, s)
+                : launch_ffn_kernel<FMT, false>(a, up, n_cu, max_wgs, s);
 }
 
-hipError_t launch_ffn_down(const LayerArgs& a, bool shared, int grid, hipStream_t s) {
+hipError_t launch_ffn(const LayerArgs& a, bool up, bool shared, int n_cu, int max_wgs, hipStream_t s) {
   switch (a.fmt) {
-    case FMT_Q4_1: return launch_down_fmt<FMT_Q4_1>(a, shared, grid, s);
-    case FMT_NVFP4: return launch_down_fmt<FMT_NVFP4>(a, shared, grid, s);
-    default: return launch_down_fmt<FMT_BF16>(a, shared, grid, s);
+    case FMT_Q4_1: return launch_ffn_fmt<FMT_Q4_1>(a, up, shared, n_cu, max_wgs, s);
+    case FMT_NVFP4: return launch_ffn_fmt<FMT_NVFP4>(a, up, shared, n_cu, max_wgs, s);
+    default: return launch_ffn_fmt<FMT_BF16>(a, up, shared, n_cu, max_wgs, s);
   }
 }
 

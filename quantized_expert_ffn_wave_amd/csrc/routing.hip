@@ -343,6 +343,8 @@ __device__ void build_buckets(const LayerArgs& a, BucketSmem& sm) {
   if (tid == 0) {
     a.ctl[CTL_N_UP] = n_up;
     a.ctl[CTL_N_DN] = n_dn;
+    a.ctl[CTL_N_UP_MF] = min(tiles_m * N_UP_CHUNKS, n_up);
+    a.ctl[CTL_N_DN_MF] = min(tiles_m * N_DN_CHUNKS, n_dn);
   }
   // one thread per token tile: its N_UP_CHUNKS gate/up items and N_DN_CHUNKS down items
   const int n_tiles = min(tiles_m + tiles_g, min(a.max_items_up / N_UP_CHUNKS, a.max_items_dn / N_DN_CHUNKS));
