@@ -104,7 +104,8 @@ __device__ inline uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-__device__ inline float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// silu(g) * u with the hardware reciprocal (1 ulp; the result is stored in 16 bits)
+__device__ inline float silu_mul(float g, float u) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u; }
 
 }  // namespace moe
 

@@ -51,6 +51,15 @@ template <bool NT> __device__ inline uint32_t ld2(const void* p) {
 constexpr uint32_t MAGIC = 0x64006400u;  // fp16 pair (1024, 1024): ORing a nibble into the
                                          // low mantissa bits gives 1024 + q exactly
 
+// (w & mask) | magic in one v_and_or_b32.  gfx950 VOP3 takes no literal
+// operands, so the mask rides in an SGPR and the magic in a VGPR; left to
+// itself the compiler splits this into an AND and an OR.
+__device__ inline uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic_v) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(magic_v));
+  return r;
+}
+
 __device__ inline uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ inline f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
 __device__ inline bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
@@ -106,10 +115,13 @@ template <int FMT> struct GV;
 template <> struct GV<FMT_Q4_1> {
   struct Raw { u32x4 c; uint32_t dm; };                // 16 B codes + fp16 {d, m}
   struct X { uint32_t p[16]; float se, so; };          // fp16 pairs in nibble order + even/odd sums
-  template <bool NT> static __device__ Raw load(const QMat& q, size_t row, int chunk, int cols) {
+  template <bool NT> static __device__ Raw load(const QMat& q, size_t row, uint32_t sub, int chunk, int cols) {
     Raw r;
-    r.c = ld16<NT>(q.codes + row * (cols / 2) + 16 * chunk);
-    r.dm = ld4<NT>(reinterpret_cast<const uint32_t*>(q.scales) + row * (cols / 32) + chunk);
+    // row terms are workgroup-uniform; the unsigned lane terms let the loads
+    // take the scalar-base + 32-bit vector-offset form
+    r.c = ld16<NT>(q.codes + row * (cols / 2) + (sub * (uint32_t)(cols / 2) + 16u * (uint32_t)chunk));
+    r.dm = ld4<NT>(reinterpret_cast<const uint32_t*>(q.scales) + row * (cols / 32) +
+                   (sub * (uint32_t)(cols / 32) + (uint32_t)chunk));
     return r;
   }
   static __device__ void prep(X& x, const uint32_t* src) {  // src: 16 fp16 pairs, natural order
@@ -154,10 +166,10 @@ template <> struct GV<FMT_Q4_1> {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t w = r.c[j], w8 = w >> 8;
-      u.A[j] = (w & 0x000F000Fu) | MAGIC;
-      u.B[j] = (w & 0x00F000F0u) | MAGIC;
-      u.C[j] = (w8 & 0x000F000Fu) | MAGIC;
-      u.D[j] = (w8 & 0x00F000F0u) | MAGIC;
+      u.A[j] = and_or(w, 0x000F000Fu, MAGIC);
+      u.B[j] = and_or(w, 0x00F000F0u, MAGIC);
+      u.C[j] = and_or(w8, 0x000F000Fu, MAGIC);
+      u.D[j] = and_or(w8, 0x00F000F0u, MAGIC);
     }
     const float d = f16lo(r.dm), m = f16hi(r.dm);
     u.d = d;
@@ -209,10 +221,11 @@ template <> struct GV<FMT_Q4_1> {
 template <> struct GV<FMT_NVFP4> {
   struct Raw { u32x4 c; uint32_t s; };                 // 16 B codes + 2 E4M3 block scales
   struct X { uint32_t p[16]; };                        // fp16 pairs, natural order
-  template <bool NT> static __device__ Raw load(const QMat& q, size_t row, int chunk, int cols) {
+  template <bool NT> static __device__ Raw load(const QMat& q, size_t row, uint32_t sub, int chunk, int cols) {
     Raw r;
-    r.c = ld16<NT>(q.codes + row * (cols / 2) + 16 * chunk);
-    r.s = ld2<NT>(reinterpret_cast<const uint8_t*>(q.scales) + row * (cols / 16) + 2 * chunk);
+    r.c = ld16<NT>(q.codes + row * (cols / 2) + (sub * (uint32_t)(cols / 2) + 16u * (uint32_t)chunk));
+    r.s = ld2<NT>(reinterpret_cast<const uint8_t*>(q.scales) + row * (cols / 16) +
+                  (sub * (uint32_t)(cols / 16) + 2u * (uint32_t)chunk));
     return r;
   }
   static __device__ void prep(X& x, const uint32_t* src) {
@@ -281,9 +294,9 @@ template <> struct GV<FMT_NVFP4> {
 template <> struct GV<FMT_BF16> {
   struct Raw { u32x4 c[4]; };                          // 64 B of bf16
   struct X { uint32_t p[16]; };                        // bf16 pairs, natural order
-  template <bool NT> static __device__ Raw load(const QMat& q, size_t row, int chunk, int cols) {
+  template <bool NT> static __device__ Raw load(const QMat& q, size_t row, uint32_t sub, int chunk, int cols) {
     Raw r;
-    const uint8_t* p = q.codes + row * cols * 2 + 64 * chunk;
+    const uint8_t* p = q.codes + row * cols * 2 + (sub * (uint32_t)(cols * 2) + 64u * (uint32_t)chunk);
 #pragma unroll
     for (int i = 0; i < 4; ++i) r.c[i] = ld16<NT>(p + 16 * i);
     return r;
@@ -542,21 +555,36 @@ __device__ inline ChunkW chunk_weights(const LayerArgs& a, const Item& item) {
   return w;
 }
 
+// The item of a chunk is the same for the whole workgroup: keep it in SGPRs so
+// that the row addresses derived from it are scalar.
 template <bool SHARED>
 __device__ inline Item fetch_item(const LayerArgs& a, const Item* list, int idx, int chunks) {
-  return SHARED ? shared_item(a.T, a.E, idx, chunks) : list[idx];
+  Item it = SHARED ? shared_item(a.T, a.E, idx, chunks) : list[idx];
+  it.head = __builtin_amdgcn_readfirstlane(it.head);
+  it.p0 = __builtin_amdgcn_readfirstlane(it.p0);
+  it.t01 = __builtin_amdgcn_readfirstlane(it.t01);
+  it.t23 = __builtin_amdgcn_readfirstlane(it.t23);
+  return it;
 }
 
 // One chunk of gate/up for MT token slots (slots >= the item's count hold zero
 // activations): UP_STEPS row pairs per wave from the ring, each slot refilled
 // with the row UP_RING steps ahead, which past the chunk's end is a row of the
 // next chunk (nw, nr0) when there is one.
+template <int MT> constexpr int POW2_UP = MT <= 1 ? 1 : MT <= 2 ? 2 : MT <= 4 ? 4 : 8;
+
+// value of lane ^ 32 in the lanes below 32
+__device__ inline float upper_half(float v) {
+  return __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false)[1]);
+}
+
 template <int FMT, int MT>
 __device__ inline void up_chunk(typename GV<FMT>::Raw* rg, typename GV<FMT>::Raw* ru, const ChunkW& w, size_t r0,
                                 const ChunkW& nw, size_t nr0, bool has_next, const GvSmem& sm, int buf, int cnt,
                                 uint16_t* hbase) {
   using F = GV<FMT>;
   constexpr int D = UP_RING<FMT>;
+  constexpr int RP = POW2_UP<MT>;  // reduction width (token slots padded to a power of two)
   const int lane = threadIdx.x & 63;
   typename F::X xs[MT];
 #pragma unroll
@@ -565,7 +593,7 @@ __device__ inline void up_chunk(typename GV<FMT>::Raw* rg, typename GV<FMT>::Raw
     F::sums(xs[t]);
   }
   bool wr;
-  const int my_t = xreduce_index<2 * MT, 64>(lane, wr) % MT;
+  const int my_t = xreduce_index<2 * RP, 64>(lane, wr) % RP;
   const bool writer = lane < 32 && wr && my_t < cnt;
 #pragma unroll
   for (int s = 0; s < UP_STEPS; ++s) {
@@ -574,21 +602,21 @@ __device__ inline void up_chunk(typename GV<FMT>::Raw* rg, typename GV<FMT>::Raw
     F::unpack(ug, rg[slot], w.tsg);
     F::unpack(uu, ru[slot], w.tsu);
     if (s + D < UP_STEPS) {
-      rg[slot] = F::template load<true>(w.g, r0 + s + D, lane, D_MODEL);
-      ru[slot] = F::template load<true>(w.u, r0 + s + D, lane, D_MODEL);
+      rg[slot] = F::template load<true>(w.g, r0 + s + D, 0u, lane, D_MODEL);
+      ru[slot] = F::template load<true>(w.u, r0 + s + D, 0u, lane, D_MODEL);
     } else if (has_next) {
-      rg[slot] = F::template load<true>(nw.g, nr0 + s + D - UP_STEPS, lane, D_MODEL);
-      ru[slot] = F::template load<true>(nw.u, nr0 + s + D - UP_STEPS, lane, D_MODEL);
+      rg[slot] = F::template load<true>(nw.g, nr0 + s + D - UP_STEPS, 0u, lane, D_MODEL);
+      ru[slot] = F::template load<true>(nw.u, nr0 + s + D - UP_STEPS, 0u, lane, D_MODEL);
     }
-    float v[2 * MT];
+    float v[2 * RP];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      v[t] = F::dot1(ug, xs[t]);
-      v[MT + t] = F::dot1(uu, xs[t]);
+    for (int t = 0; t < RP; ++t) {
+      v[t] = (t < MT) ? F::dot1(ug, xs[t < MT ? t : 0]) : 0.f;
+      v[RP + t] = (t < MT) ? F::dot1(uu, xs[t < MT ? t : 0]) : 0.f;
     }
     // gate sums land in lanes < 32, the matching up sums in lane ^ 32
-    xreduce<2 * MT, 64>(v);
-    const float u = __shfl_xor(v[0], 32);
+    xreduce<2 * RP, 64>(v);
+    const float u = upper_half(v[0]);
     if (writer) hbase[(size_t)my_t * D_FF + s] = h_store<FMT>(silu_mul(v[0], u));
   }
 }
@@ -600,7 +628,7 @@ __device__ void up_stream(const LayerArgs& a, const Item* list, int n, GvSmem& s
   using F = GV<FMT>;
   constexpr int D = UP_RING<FMT>;
   static_assert(UP_STEPS % D == 0, "ring must divide the steps of a chunk");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int c = blockIdx.x;
   if (c >= n) return;
   Item item = fetch_item<SHARED>(a, list, c, N_UP_CHUNKS);
@@ -614,8 +642,8 @@ __device__ void up_stream(const LayerArgs& a, const Item* list, int n, GvSmem& s
   typename F::Raw rg[D], ru[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
-    rg[i] = F::template load<true>(w.g, r0 + i, lane, D_MODEL);
-    ru[i] = F::template load<true>(w.u, r0 + i, lane, D_MODEL);
+    rg[i] = F::template load<true>(w.g, r0 + i, 0u, lane, D_MODEL);
+    ru[i] = F::template load<true>(w.u, r0 + i, 0u, lane, D_MODEL);
   }
   int buf = 0;
   {
@@ -643,7 +671,8 @@ __device__ void up_stream(const LayerArgs& a, const Item* list, int n, GvSmem& s
     const int cnt = it.cnt;
     uint16_t* hbase = a.h + (size_t)row_of(a, it, 0) * D_FF + item_chunk(item.head) * UP_ROWS + wave * UP_STEPS;
     if (cnt <= 1) up_chunk<FMT, 1>(rg, ru, w, r0, nw, nr0, has_next, sm, buf, cnt, hbase);
-    else if (cnt <= 2) up_chunk<FMT, 2>(rg, ru, w, r0, nw, nr0, has_next, sm, buf, cnt, hbase);
+    else if (cnt == 2) up_chunk<FMT, 2>(rg, ru, w, r0, nw, nr0, has_next, sm, buf, cnt, hbase);
+    else if (cnt == 3) up_chunk<FMT, 3>(rg, ru, w, r0, nw, nr0, has_next, sm, buf, cnt, hbase);
     else up_chunk<FMT, GV_GROUP>(rg, ru, w, r0, nw, nr0, has_next, sm, buf, cnt, hbase);
     if (!has_next) break;
     xstage_store<FMT, true>(st, sm, buf ^ 1);
@@ -664,7 +693,9 @@ __device__ inline void down_chunk(typename GV<FMT>::Raw* ring, const ChunkW& w, 
                                   size_t nr0, bool has_next, const GvSmem& sm, int buf, int cnt, float* ybase) {
   using F = GV<FMT>;
   constexpr int R = DN_RING<FMT> < DN_STEPS ? DN_RING<FMT> : DN_STEPS;
+  constexpr int RP = POW2_UP<MT>;
   const int slot16 = threadIdx.x & 15;
+  const uint32_t sub = (threadIdx.x & 63) >> 4;  // row of the lane within a 4-row group
   typename F::X xs[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
@@ -672,7 +703,7 @@ __device__ inline void down_chunk(typename GV<FMT>::Raw* ring, const ChunkW& w, 
     F::sums(xs[t]);
   }
   bool wr;
-  const int my_t = xreduce_index<MT, 16>(slot16, wr) % MT;
+  const int my_t = xreduce_index<RP, 16>(slot16, wr) % RP;
   const bool writer = wr && my_t < cnt;
 #pragma unroll
   for (int g = 0; g < DN_STEPS; ++g) {
@@ -680,14 +711,14 @@ __device__ inline void down_chunk(typename GV<FMT>::Raw* ring, const ChunkW& w, 
     typename F::U u;
     F::unpack(u, ring[slot], w.tsg);
     if (g + R < DN_STEPS) {
-      ring[slot] = F::template load<true>(w.g, r0 + 4 * (g + R), slot16, D_FF);
+      ring[slot] = F::template load<true>(w.g, r0 + 4 * (g + R), sub, slot16, D_FF);
     } else if (has_next) {
-      ring[slot] = F::template load<true>(nw.g, nr0 + 4 * (g + R - DN_STEPS), slot16, D_FF);
+      ring[slot] = F::template load<true>(nw.g, nr0 + 4 * (g + R - DN_STEPS), sub, slot16, D_FF);
     }
-    float v[MT];
+    float v[RP];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) v[t] = F::dot1(u, xs[t]);
-    xreduce<MT, 16>(v);
+    for (int t = 0; t < RP; ++t) v[t] = (t < MT) ? F::dot1(u, xs[t < MT ? t : 0]) : 0.f;
+    xreduce<RP, 16>(v);
     if (writer) ybase[(size_t)my_t * D_MODEL + 4 * g] = v[0];
   }
 }
@@ -698,21 +729,22 @@ __device__ void down_stream(const LayerArgs& a, const Item* list, int n, GvSmem&
   using F = GV<FMT>;
   constexpr int R = DN_RING<FMT> < DN_STEPS ? DN_RING<FMT> : DN_STEPS;
   static_assert(DN_STEPS % R == 0, "ring must divide the steps of a chunk");
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int slot16 = threadIdx.x & 15, rsub = (threadIdx.x & 63) >> 4;
   int c = blockIdx.x;
   if (c >= n) return;
   Item item = fetch_item<SHARED>(a, list, c, N_DN_CHUNKS);
   ItemTok it = item_tokens(item, SHARED);
   ChunkW w = chunk_weights<FMT, SHARED, false>(a, item);
-  // rows of this lane: first_row + 4 g, g = 0 .. DN_STEPS-1
+  // rows of this lane: first_row + rsub + 4 g, g = 0 .. DN_STEPS-1 (first_row is
+  // workgroup-uniform, rsub the lane's row within a 4-row group)
   auto first_row = [&](const Item& itm, const ChunkW& cw) {
-    return (size_t)cw.mat * D_MODEL + item_chunk(itm.head) * DN_ROWS + wave * (DN_ROWS / 4) + rsub;
+    return (size_t)cw.mat * D_MODEL + item_chunk(itm.head) * DN_ROWS + wave * (DN_ROWS / 4);
   };
   size_t r0 = first_row(item, w);
   typename F::Raw ring[R];
 #pragma unroll
-  for (int i = 0; i < R; ++i) ring[i] = F::template load<true>(w.g, r0 + 4 * i, slot16, D_FF);
+  for (int i = 0; i < R; ++i) ring[i] = F::template load<true>(w.g, r0 + 4 * i, (uint32_t)rsub, slot16, D_FF);
   int buf = 0;
   {
     XStage st;
@@ -740,7 +772,8 @@ __device__ void down_stream(const LayerArgs& a, const Item* list, int n, GvSmem&
     float* ybase =
         a.y + (size_t)row_of(a, it, 0) * D_MODEL + item_chunk(item.head) * DN_ROWS + wave * (DN_ROWS / 4) + rsub;
     if (cnt <= 1) down_chunk<FMT, 1>(ring, w, r0, nw, nr0, has_next, sm, buf, cnt, ybase);
-    else if (cnt <= 2) down_chunk<FMT, 2>(ring, w, r0, nw, nr0, has_next, sm, buf, cnt, ybase);
+    else if (cnt == 2) down_chunk<FMT, 2>(ring, w, r0, nw, nr0, has_next, sm, buf, cnt, ybase);
+    else if (cnt == 3) down_chunk<FMT, 3>(ring, w, r0, nw, nr0, has_next, sm, buf, cnt, ybase);
     else down_chunk<FMT, GV_GROUP>(ring, w, r0, nw, nr0, has_next, sm, buf, cnt, ybase);
     if (!has_next) break;
     xstage_store<FMT, false>(st, sm, buf ^ 1);
@@ -815,7 +848,7 @@ template <int FMT> struct MfmaStage {
 template <int FMT>
 __device__ inline void mfma_fetch(MfmaStage<FMT>& st, const QMat& wq, size_t wrow, int kw, const uint16_t* xsrc,
                                   int cols) {
-  st.w = GV<FMT>::template load<false>(wq, wrow, kw / 32, cols);
+  st.w = GV<FMT>::template load<false>(wq, wrow, 0u, kw / 32, cols);
   if (xsrc) {
     st.x0 = ld16<false>(xsrc);
     st.x1 = ld16<false>(xsrc + 8);
