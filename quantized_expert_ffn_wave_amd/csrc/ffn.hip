@@ -567,10 +567,6 @@ __device__ inline Item fetch_item(const LayerArgs& a, const Item* list, int idx,
   return it;
 }
 
-// One chunk of gate/up for MT token slots (slots >= the item's count hold zero
-// activations): UP_STEPS row pairs per wave from the ring, each slot refilled
-// with the row UP_RING steps ahead, which past the chunk's end is a row of the
-// next chunk (nw, nr0) when there is one.
 template <int MT> constexpr int POW2_UP = MT <= 1 ? 1 : MT <= 2 ? 2 : MT <= 4 ? 4 : 8;
 
 // value of lane ^ 32 in the lanes below 32
@@ -578,13 +574,20 @@ __device__ inline float upper_half(float v) {
   return __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false)[1]);
 }
 
+// One chunk of gate/up for MT token slots (slots >= the item's count hold zero
+// activations): UP_STEPS row pairs per wave from the ring, each slot refilled
+// with the row UP_RING steps ahead, which past the chunk's end is a row of the
+// next chunk (nw, nr0) when there is one.
 template <int FMT, int MT>
 __device__ inline void up_chunk(typename GV<FMT>::Raw* rg, typename GV<FMT>::Raw* ru, const ChunkW& w, size_t r0,
                                 const ChunkW& nw, size_t nr0, bool has_next, const GvSmem& sm, int buf, int cnt,
                                 uint16_t* hbase) {
   using F = GV<FMT>;
   constexpr int D = UP_RING<FMT>;
-  constexpr int RP = POW2_UP<MT>;  // reduction width (token slots padded to a power of two)
+  constexpr int RP = POW2_UP<MT>;          // token slots padded to a power of two
+  constexpr int EPI = 4 / RP;              // steps whose sums are reduced together (8 sums per lane)
+  constexpr int P = 2 * EPI * RP;          // partial sums per lane: [gate/up][step][token]
+  static_assert(UP_STEPS % EPI == 0 && P <= 64, "reduction batch");
   const int lane = threadIdx.x & 63;
   typename F::X xs[MT];
 #pragma unroll
@@ -592,12 +595,17 @@ __device__ inline void up_chunk(typename GV<FMT>::Raw* rg, typename GV<FMT>::Raw
     x_from_lds<FMT>(xs[t], sm, buf, t, lane);
     F::sums(xs[t]);
   }
+  // after the transposing reduction a lane holds one (gate/up, step, token)
+  // total; the gate totals sit in lanes < 32 and the matching up totals in lane ^ 32
   bool wr;
-  const int my_t = xreduce_index<2 * RP, 64>(lane, wr) % RP;
+  const int my_idx = xreduce_index<P, 64>(lane, wr);
+  const int my_t = my_idx % RP, my_r = (my_idx / RP) % EPI;
   const bool writer = lane < 32 && wr && my_t < cnt;
+  uint16_t* hdst = hbase + (size_t)my_t * D_FF + my_r;
+  float v[P];
 #pragma unroll
   for (int s = 0; s < UP_STEPS; ++s) {
-    const int slot = s % D;
+    const int slot = s % D, r = s % EPI;
     typename F::U ug, uu;
     F::unpack(ug, rg[slot], w.tsg);
     F::unpack(uu, ru[slot], w.tsu);
@@ -608,16 +616,16 @@ __device__ inline void up_chunk(typename GV<FMT>::Raw* rg, typename GV<FMT>::Raw
       rg[slot] = F::template load<true>(nw.g, nr0 + s + D - UP_STEPS, 0u, lane, D_MODEL);
       ru[slot] = F::template load<true>(nw.u, nr0 + s + D - UP_STEPS, 0u, lane, D_MODEL);
     }
-    float v[2 * RP];
 #pragma unroll
     for (int t = 0; t < RP; ++t) {
-      v[t] = (t < MT) ? F::dot1(ug, xs[t < MT ? t : 0]) : 0.f;
-      v[RP + t] = (t < MT) ? F::dot1(uu, xs[t < MT ? t : 0]) : 0.f;
+      v[r * RP + t] = (t < MT) ? F::dot1(ug, xs[t < MT ? t : 0]) : 0.f;
+      v[(EPI + r) * RP + t] = (t < MT) ? F::dot1(uu, xs[t < MT ? t : 0]) : 0.f;
     }
-    // gate sums land in lanes < 32, the matching up sums in lane ^ 32
-    xreduce<2 * RP, 64>(v);
-    const float u = upper_half(v[0]);
-    if (writer) hbase[(size_t)my_t * D_FF + s] = h_store<FMT>(silu_mul(v[0], u));
+    if (r == EPI - 1) {
+      xreduce<P, 64>(v);
+      const float u = upper_half(v[0]);
+      if (writer) hdst[s - r] = h_store<FMT>(silu_mul(v[0], u));
+    }
   }
 }
 
@@ -694,6 +702,9 @@ __device__ inline void down_chunk(typename GV<FMT>::Raw* ring, const ChunkW& w, 
   using F = GV<FMT>;
   constexpr int R = DN_RING<FMT> < DN_STEPS ? DN_RING<FMT> : DN_STEPS;
   constexpr int RP = POW2_UP<MT>;
+  constexpr int EPI = 8 / RP;                              // row groups reduced together (8 sums per lane)
+  constexpr int P = EPI * RP;                              // partial sums per lane: [group][token]
+  static_assert(DN_STEPS % EPI == 0 && P <= 16, "reduction batch");
   const int slot16 = threadIdx.x & 15;
   const uint32_t sub = (threadIdx.x & 63) >> 4;  // row of the lane within a 4-row group
   typename F::X xs[MT];
@@ -703,11 +714,14 @@ __device__ inline void down_chunk(typename GV<FMT>::Raw* ring, const ChunkW& w, 
     F::sums(xs[t]);
   }
   bool wr;
-  const int my_t = xreduce_index<RP, 16>(slot16, wr) % RP;
+  const int my_idx = xreduce_index<P, 16>(slot16, wr);
+  const int my_t = my_idx % RP, my_g = my_idx / RP;
   const bool writer = wr && my_t < cnt;
+  float* ydst = ybase + (size_t)my_t * D_MODEL + 4 * my_g;
+  float v[P];
 #pragma unroll
   for (int g = 0; g < DN_STEPS; ++g) {
-    const int slot = g % R;
+    const int slot = g % R, r = g % EPI;
     typename F::U u;
     F::unpack(u, ring[slot], w.tsg);
     if (g + R < DN_STEPS) {
@@ -715,11 +729,12 @@ __device__ inline void down_chunk(typename GV<FMT>::Raw* ring, const ChunkW& w, 
     } else if (has_next) {
       ring[slot] = F::template load<true>(nw.g, nr0 + 4 * (g + R - DN_STEPS), sub, slot16, D_FF);
     }
-    float v[RP];
 #pragma unroll
-    for (int t = 0; t < RP; ++t) v[t] = (t < MT) ? F::dot1(u, xs[t < MT ? t : 0]) : 0.f;
-    xreduce<RP, 16>(v);
-    if (writer) ybase[(size_t)my_t * D_MODEL + 4 * g] = v[0];
+    for (int t = 0; t < RP; ++t) v[r * RP + t] = (t < MT) ? F::dot1(u, xs[t < MT ? t : 0]) : 0.f;
+    if (r == EPI - 1) {
+      xreduce<P, 16>(v);
+      if (writer) ydst[4 * (g - r)] = v[0];
+    }
   }
 }
 
