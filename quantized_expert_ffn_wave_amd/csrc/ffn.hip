@@ -52,24 +52,20 @@ constexpr uint32_t MAGIC = 0x64006400u;  // fp16 pair (1024, 1024): ORing a nibb
                                          // low mantissa bits gives 1024 + q exactly
 
 // (w & mask) | magic in one v_and_or_b32.  gfx950 VOP3 takes no literal
-// operands, so the mask rides in an SGPR and the magic in a VGPR; left to
-// itself the compiler splits this into an AND and an OR.
-__device__ inline uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic_v) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(magic_v));
-  return r;
+// operands, so the mask rides in an SGPR and the magic must sit in a VGPR;
+// with both as literals the compiler splits this into an AND and an OR.  The
+// empty asm hides the constant (it emits no instruction), so it is kept in a
+// VGPR and the compiler itself selects v_and_or_b32 and tracks its hazards.
+__device__ inline uint32_t magic_vgpr() {
+  uint32_t m = MAGIC;
+  asm volatile("" : "+v"(m));
+  return m;
 }
+__device__ inline uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic_v) { return (w & mask) | magic_v; }
 
 __device__ inline uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ inline f16x2 as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
 __device__ inline bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
-
-__device__ inline float dot2h(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(as_f16x2(a), as_f16x2(b), c, false);
-}
-__device__ inline float dot2b(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(b), c, false);
-}
 
 // E2M1 pair (byte B of w) -> fp16 pair, unscaled (exact).
 template <int B> __device__ inline uint32_t fp4x2_to_f16x2(uint32_t w) {
@@ -108,100 +104,24 @@ template <> __device__ inline uint16_t h_store<FMT_BF16>(float v) { return f32_t
 template <int FMT> constexpr bool OPER_F16 = FMT != FMT_BF16;
 
 // ======================================================================================
-// Per-format chunk of a weight row: 32 consecutive elements owned by one lane.
+// Per-format chunk of a weight row: 32 consecutive elements of one row, the
+// unit one lane loads (16 bytes of 4-bit codes plus the block scales, or 64
+// bytes of bf16), and its decode to fp16/bf16 pairs for the matrix-core tiles.
 // ======================================================================================
 template <int FMT> struct GV;
 
 template <> struct GV<FMT_Q4_1> {
   struct Raw { u32x4 c; uint32_t dm; };                // 16 B codes + fp16 {d, m}
-  struct X { uint32_t p[16]; float se, so; };          // fp16 pairs in nibble order + even/odd sums
+  // chunk `chunk` of row (row + sub); the row terms are workgroup-uniform, the
+  // unsigned lane terms let the loads take the scalar-base + vector-offset form
   template <bool NT> static __device__ Raw load(const QMat& q, size_t row, uint32_t sub, int chunk, int cols) {
     Raw r;
-    // row terms are workgroup-uniform; the unsigned lane terms let the loads
-    // take the scalar-base + 32-bit vector-offset form
     r.c = ld16<NT>(q.codes + row * (cols / 2) + (sub * (uint32_t)(cols / 2) + 16u * (uint32_t)chunk));
     r.dm = ld4<NT>(reinterpret_cast<const uint32_t*>(q.scales) + row * (cols / 32) +
                    (sub * (uint32_t)(cols / 32) + (uint32_t)chunk));
     return r;
   }
-  static __device__ void prep(X& x, const uint32_t* src) {  // src: 16 fp16 pairs, natural order
-    float se = 0.f, so = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      q4_order(src[4 * j], src[4 * j + 1], src[4 * j + 2], src[4 * j + 3], &x.p[4 * j]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { se += f16lo(src[4 * j + i]); so += f16hi(src[4 * j + i]); }
-    }
-    x.se = se;
-    x.so = so;
-  }
-  // out[t] = sum_i w_i x_t,i over the chunk.  With the nibbles ORed into the
-  // mantissa of 1024: lo = sum_even (1024+q) x, hi = sum_odd (1024+16q) x, so
-  // the block dot d*sum q x + m*sum x = d lo + (d/16) hi + (m-1024d) se + (m-64d) so.
-  template <int M> static __device__ void dot(const Raw& r, const X* x, float* out, float) {
-    float lo[M], hi[M];
-#pragma unroll
-    for (int t = 0; t < M; ++t) { lo[t] = 0.f; hi[t] = 0.f; }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t w = r.c[j], w8 = w >> 8;
-      const uint32_t A = (w & 0x000F000Fu) | MAGIC, B = (w & 0x00F000F0u) | MAGIC;
-      const uint32_t C = (w8 & 0x000F000Fu) | MAGIC, D = (w8 & 0x00F000F0u) | MAGIC;
-#pragma unroll
-      for (int t = 0; t < M; ++t) {
-        lo[t] = dot2h(A, x[t].p[4 * j + 0], lo[t]);
-        hi[t] = dot2h(B, x[t].p[4 * j + 1], hi[t]);
-        lo[t] = dot2h(C, x[t].p[4 * j + 2], lo[t]);
-        hi[t] = dot2h(D, x[t].p[4 * j + 3], hi[t]);
-      }
-    }
-    const float d = f16lo(r.dm), m = f16hi(r.dm);
-    const float c2 = d * 0.0625f, c3 = m - 1024.f * d, c4 = m - 64.f * d;
-#pragma unroll
-    for (int t = 0; t < M; ++t) out[t] = d * lo[t] + c2 * hi[t] + c3 * x[t].se + c4 * x[t].so;
-  }
-  // single-token form: nibbles unpacked once per row, then one dot per token
-  struct U { uint32_t A[4], B[4], C[4], D[4]; float d, c2, c3, c4; };
-  static __device__ void unpack(U& u, const Raw& r, float) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t w = r.c[j], w8 = w >> 8;
-      u.A[j] = and_or(w, 0x000F000Fu, MAGIC);
-      u.B[j] = and_or(w, 0x00F000F0u, MAGIC);
-      u.C[j] = and_or(w8, 0x000F000Fu, MAGIC);
-      u.D[j] = and_or(w8, 0x00F000F0u, MAGIC);
-    }
-    const float d = f16lo(r.dm), m = f16hi(r.dm);
-    u.d = d;
-    u.c2 = d * 0.0625f;
-    u.c3 = m - 1024.f * d;
-    u.c4 = m - 64.f * d;
-  }
-  static __device__ float dot1(const U& u, const X& x) {
-    float lo = 0.f, hi = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lo = dot2h(u.A[j], x.p[4 * j + 0], lo);
-      hi = dot2h(u.B[j], x.p[4 * j + 1], hi);
-      lo = dot2h(u.C[j], x.p[4 * j + 2], lo);
-      hi = dot2h(u.D[j], x.p[4 * j + 3], hi);
-    }
-    return u.d * lo + u.c2 * hi + u.c3 * x.se + u.c4 * x.so;
-  }
-  // even/odd sums of a chunk stored in nibble order: pairs 0 and 2 of each group
-  // of four hold even elements, pairs 1 and 3 odd ones
-  static __device__ void sums(X& x) {
-    float se = 0.f, so = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      se += f16lo(x.p[4 * j]) + f16hi(x.p[4 * j]) + f16lo(x.p[4 * j + 2]) + f16hi(x.p[4 * j + 2]);
-      so += f16lo(x.p[4 * j + 1]) + f16hi(x.p[4 * j + 1]) + f16lo(x.p[4 * j + 3]) + f16hi(x.p[4 * j + 3]);
-    }
-    x.se = se;
-    x.so = so;
-  }
-  // 32 decoded weights as 16 fp16 pairs in nibble order (matrix-core path):
-  // fp16(d*q + m), rounded once.
+  // 32 decoded weights as 16 fp16 pairs in nibble order: fp16(d*q + m), rounded once.
   static __device__ void decode(const Raw& r, uint32_t* o) {
     const f16x2 d2 = {as_f16x2(r.dm)[0], as_f16x2(r.dm)[0]};
     const f16x2 m2 = {as_f16x2(r.dm)[1], as_f16x2(r.dm)[1]};
@@ -220,7 +140,6 @@ template <> struct GV<FMT_Q4_1> {
 
 template <> struct GV<FMT_NVFP4> {
   struct Raw { u32x4 c; uint32_t s; };                 // 16 B codes + 2 E4M3 block scales
-  struct X { uint32_t p[16]; };                        // fp16 pairs, natural order
   template <bool NT> static __device__ Raw load(const QMat& q, size_t row, uint32_t sub, int chunk, int cols) {
     Raw r;
     r.c = ld16<NT>(q.codes + row * (cols / 2) + (sub * (uint32_t)(cols / 2) + 16u * (uint32_t)chunk));
@@ -228,54 +147,6 @@ template <> struct GV<FMT_NVFP4> {
                   (sub * (uint32_t)(cols / 16) + 2u * (uint32_t)chunk));
     return r;
   }
-  static __device__ void prep(X& x, const uint32_t* src) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x.p[i] = src[i];
-  }
-  template <int M> static __device__ void dot(const Raw& r, const X* x, float* out, float ts) {
-    float a0[M], a1[M];
-#pragma unroll
-    for (int t = 0; t < M; ++t) { a0[t] = 0.f; a1[t] = 0.f; }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t w = r.c[j];
-      const uint32_t P0 = fp4x2_to_f16x2<0>(w), P1 = fp4x2_to_f16x2<1>(w);
-      const uint32_t P2 = fp4x2_to_f16x2<2>(w), P3 = fp4x2_to_f16x2<3>(w);
-#pragma unroll
-      for (int t = 0; t < M; ++t) {
-        float& acc = (j < 2) ? a0[t] : a1[t];
-        acc = dot2h(P0, x[t].p[4 * j + 0], acc);
-        acc = dot2h(P1, x[t].p[4 * j + 1], acc);
-        acc = dot2h(P2, x[t].p[4 * j + 2], acc);
-        acc = dot2h(P3, x[t].p[4 * j + 3], acc);
-      }
-    }
-    const float s0 = __builtin_amdgcn_cvt_f32_fp8(r.s, 0) * ts;
-    const float s1 = __builtin_amdgcn_cvt_f32_fp8(r.s, 1) * ts;
-#pragma unroll
-    for (int t = 0; t < M; ++t) out[t] = s0 * a0[t] + s1 * a1[t];
-  }
-  struct U { uint32_t P[16]; float s0, s1; };
-  static __device__ void unpack(U& u, const Raw& r, float ts) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u.P[4 * j + 0] = fp4x2_to_f16x2<0>(r.c[j]);
-      u.P[4 * j + 1] = fp4x2_to_f16x2<1>(r.c[j]);
-      u.P[4 * j + 2] = fp4x2_to_f16x2<2>(r.c[j]);
-      u.P[4 * j + 3] = fp4x2_to_f16x2<3>(r.c[j]);
-    }
-    u.s0 = __builtin_amdgcn_cvt_f32_fp8(r.s, 0) * ts;
-    u.s1 = __builtin_amdgcn_cvt_f32_fp8(r.s, 1) * ts;
-  }
-  static __device__ float dot1(const U& u, const X& x) {
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a0 = dot2h(u.P[i], x.p[i], a0);
-#pragma unroll
-    for (int i = 8; i < 16; ++i) a1 = dot2h(u.P[i], x.p[i], a1);
-    return u.s0 * a0 + u.s1 * a1;
-  }
-  static __device__ void sums(X&) {}
   // E2M1 * E4M3 is exact in fp16; the per-matrix scale is applied after the MFMA.
   static __device__ void decode(const Raw& r, uint32_t* o) {
     const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8(r.s, 0);
@@ -293,7 +164,6 @@ template <> struct GV<FMT_NVFP4> {
 
 template <> struct GV<FMT_BF16> {
   struct Raw { u32x4 c[4]; };                          // 64 B of bf16
-  struct X { uint32_t p[16]; };                        // bf16 pairs, natural order
   template <bool NT> static __device__ Raw load(const QMat& q, size_t row, uint32_t sub, int chunk, int cols) {
     Raw r;
     const uint8_t* p = q.codes + row * cols * 2 + (sub * (uint32_t)(cols * 2) + 64u * (uint32_t)chunk);
@@ -301,50 +171,11 @@ template <> struct GV<FMT_BF16> {
     for (int i = 0; i < 4; ++i) r.c[i] = ld16<NT>(p + 16 * i);
     return r;
   }
-  static __device__ void prep(X& x, const uint32_t* src) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x.p[i] = src[i];
-  }
-  template <int M> static __device__ void dot(const Raw& r, const X* x, float* out, float) {
-#pragma unroll
-    for (int t = 0; t < M; ++t) {
-      float a = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) a = dot2b(r.c[i >> 2][i & 3], x[t].p[i], a);
-      out[t] = a;
-    }
-  }
-  struct U { uint32_t P[16]; };
-  static __device__ void unpack(U& u, const Raw& r, float) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) u.P[i] = r.c[i >> 2][i & 3];
-  }
-  static __device__ float dot1(const U& u, const X& x) {
-    float a = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) a = dot2b(u.P[i], x.p[i], a);
-    return a;
-  }
-  static __device__ void sums(X&) {}
   static __device__ void decode(const Raw& r, uint32_t* o) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[i] = r.c[i >> 2][i & 3];
   }
 };
-
-// 32 activation elements of one lane as 16 operand pairs, natural order.  src
-// points at bf16 (x) or at the stored SwiGLU output (already operand typed).
-template <int FMT> __device__ inline void load_act(uint32_t* d, const uint16_t* src, bool src_bf16) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const u32x4 v = ld16<false>(src + 8 * i);
-    d[4 * i] = v[0]; d[4 * i + 1] = v[1]; d[4 * i + 2] = v[2]; d[4 * i + 3] = v[3];
-  }
-  if (OPER_F16<FMT> && src_bf16) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) d[i] = bf16x2_to_f16x2(d[i]);
-  }
-}
 
 // Lane exchange for reduction step `m` (partner lane = lane ^ m, except m = 4
 // which pairs lane i with 7 - i inside each group of 8).  Steps 32 and 16 use
@@ -367,52 +198,12 @@ template <int M> __device__ inline float halve_step(float a, float b) {
     return hi ? sb : sa;
   }
 }
-template <int M> __device__ inline float plain_step(float a) { return halve_step<M>(a, a); }
-
-// Transposing reduction: P partials per lane, summed over groups of G lanes
-// (steps G/2 .. 1).  While more than one value is left, each step halves the
-// count: lanes with bit m clear keep the first half, the others the second.
-// Afterwards v[0] of a lane holds the total of index
-// idx(lane) = sum over halving steps s of bit(lane, G >> (s+1)) * P >> (s+1).
-template <int P, int G, int M = G / 2>
-__device__ inline void xreduce(float* v) {
-  if constexpr (M >= 1) {
-    if constexpr (P > 1) {
-#pragma unroll
-      for (int i = 0; i < P / 2; ++i) v[i] = halve_step<M>(v[i], v[i + P / 2]);
-      xreduce<P / 2, G, M / 2>(v);
-    } else {
-      v[0] = plain_step<M>(v[0]);
-      xreduce<1, G, M / 2>(v);
-    }
-  }
-}
-
-// Index a lane holds after xreduce<P, G>, and whether it is the lane of its
-// group that writes it (the bits of the non-halving steps are zero).
-template <int P, int G>
-__device__ inline int xreduce_index(int lane, bool& writer) {
-  int idx = 0, n = P, plain_mask = 0;
-#pragma unroll
-  for (int m = G / 2; m >= 1; m >>= 1) {
-    if (n > 1) {
-      n /= 2;
-      if (lane & m) idx += n;
-    } else {
-      plain_mask |= m;
-    }
-  }
-  writer = (lane & plain_mask) == 0;
-  return idx;
-}
-
 // Tokens of an item: bucket positions p0 .. p0+cnt-1 of a routed expert
 // (expert-output row p), or tokens p0 .. p0+cnt-1 of the shared expert
 // (expert-output row S + t).  Vector-path items carry their token ids.
 struct ItemTok {
   int p0, cnt;
   bool shared, mfma;
-  int tok[GV_GROUP];
 };
 
 __device__ inline ItemTok item_tokens(const Item& item, bool shared) {
@@ -421,17 +212,7 @@ __device__ inline ItemTok item_tokens(const Item& item, bool shared) {
   r.mfma = item_mfma(item.head);
   r.p0 = (int)item.p0;
   r.cnt = item_count(item.head);
-  r.tok[0] = (int)(item.t01 & 0xFFFFu);
-  r.tok[1] = (int)(item.t01 >> 16);
-  r.tok[2] = (int)(item.t23 & 0xFFFFu);
-  r.tok[3] = (int)(item.t23 >> 16);
   return r;
-}
-// token of entry i: shared -> p0 + i; vector path -> carried id; matrix path -> perm
-__device__ inline int tok_of(const LayerArgs& a, const ItemTok& it, int i) {
-  if (it.shared) return it.p0 + i;
-  if (!it.mfma) return it.tok[i];
-  return a.perm[it.p0 + i] / a.K;
 }
 __device__ inline int row_of(const LayerArgs& a, const ItemTok& it, int i) {
   return it.shared ? a.S + it.p0 + i : it.p0 + i;
@@ -456,79 +237,202 @@ __device__ inline int shared_items(int T, int chunks) { return bucket_tiles(T) *
 // ======================================================================================
 
 // ======================================================================================
-// Vector path as a continuous stream.  A persistent workgroup walks its chunks
-// c, c + G, c + 2G, ... (G = grid size).  A chunk is one token group (<= 4
-// tokens) of one expert times UP_ROWS row pairs (gate/up) or DN_ROWS rows
-// (down); each wave owns a fixed quarter of the chunk's rows.  The activations
-// of the chunk's tokens sit in LDS (double buffered: the next chunk's are
-// loaded during this one), and every wave keeps a ring of weight-row loads in
-// flight that runs on into the next chunk, so the weight stream never drains
+// Vector path (buckets below MFMA_MIN tokens) on the matrix cores.
+//
+// v_mfma_f32_4x4x4_16b_{f16,bf16} performs 16 independent 4x4x4 products per
+// wave: lane l = 4b + j supplies row j of block b's first operand and column j
+// of its second one, and receives column j of block b's result.  Here block b
+// is one 32-element chunk of the reduction dimension, the first operand holds
+// the activations of the item's tokens (up to 4) and the second one 4 weight
+// rows.  So lane 4b + j streams chunk b of weight row j -- one 16-byte code
+// load plus the block scale, as a plain GEMV lane would -- and gets back the
+// 4 tokens' partial sums of its own row: the block scale applies inside the
+// lane, and a row's total is the sum over the 16 chunk lanes, taken once per
+// 4-row group.  The matrix cores take the token dimension, so the vector ALUs
+// only decode weights, whatever the item's token count.
+//
+// A persistent workgroup walks its chunks c = blockIdx.x, +gridDim.x, ...: a
+// chunk is one token group of one expert times UP_ROWS row pairs (gate/up) or
+// DN_ROWS rows (down), and each wave takes a quarter of the rows.  The chunk's
+// activations sit in LDS in operand order (double buffered: the next chunk's
+// are loaded during this one), and each wave keeps a ring of weight loads in
+// flight that runs on into the next chunk, so the weight stream does not drain
 // between chunks.
 // ======================================================================================
-template <int FMT> constexpr int UP_RING = (FMT == FMT_BF16) ? 2 : 4;  // row pairs in flight per wave
-template <int FMT> constexpr int DN_RING = (FMT == FMT_BF16) ? 4 : 8;  // 4-row groups in flight per wave
-constexpr int UP_STEPS = UP_ROWS / 4;        // row pairs per wave per chunk (16)
-constexpr int DN_STEPS = DN_ROWS / 16;       // 4-row groups per wave per chunk (8)
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Activations of a chunk in LDS: [buffer][token][piece j][slot][16 B]; piece j
-// of a slot holds elements 8j..8j+7 of that slot's 32-element chunk (already in
-// the format's operand type and k order).  Gate/up: slot = lane (2048-long
-// rows); down: slot = lane & 15 (512-long rows).
-struct GvSmem {
-  u32x4 x[2][GV_GROUP][4][64];
+template <int FMT> __device__ inline f32x4 mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c) {
+  const u32x2 x = {a0, a1}, w = {b0, b1};
+  if constexpr (FMT == FMT_BF16)
+    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(i16x4, x), __builtin_bit_cast(i16x4, w), c, 0, 0,
+                                                  0);
+  else
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(f16x4, x), __builtin_bit_cast(f16x4, w), c, 0, 0, 0);
+}
+
+template <int FMT> constexpr int MV_UP_RING = (FMT == FMT_BF16) ? 4 : 8;  // weight loads in flight per wave
+template <int FMT> constexpr int MV_DN_RING = (FMT == FMT_BF16) ? 4 : 8;
+constexpr int MV_UP_UNITS = 32;            // loads per wave per gate/up chunk: 4 row groups x 4 K-quarters x 2 matrices
+constexpr int MV_DN_UNITS = DN_ROWS / 16;  // loads per wave per down chunk: 8 row groups (K = 512 in one load)
+constexpr int MV_CHUNKS = D_MODEL / 32;    // 32-element chunks of the longest reduction
+constexpr int MV_TOKW = MV_CHUNKS * 16 + 4;  // dwords per token in LDS (16 B of padding against bank conflicts)
+
+// q4_1 per (chunk, token): -1024 * sum(x') seeds the accumulator, S = sum(x)
+// weighs the block minimum.
+struct MvKS {
+  float negK[GV_GROUP];
+  float S[GV_GROUP];
+};
+struct MvSmem {
+  uint32_t x[2][GV_GROUP * MV_TOKW];
+  MvKS ks[2][MV_CHUNKS];
 };
 
-// Loads of one chunk's activations into registers: thread (slot = tid / 4,
-// piece = tid % 4) takes 8 elements of each token (zeros for absent tokens).
-struct XStage {
-  u32x4 v[GV_GROUP];
+// token t of a vector-path item, from its packed ids (no indexed array)
+__device__ inline int item_token(const Item& item, int t) {
+  const uint32_t pair = (t & 2) ? item.t23 : item.t01;
+  return (int)((pair >> (16 * (t & 1))) & 0xFFFFu);
+}
+
+// One thread per (token, chunk): the chunk's 32 activation elements.
+struct MvStage {
+  u32x4 v[4];
 };
 
-template <int FMT, bool UP>
-__device__ inline void xstage_load(const LayerArgs& a, const ItemTok& it, XStage& st) {
-  const int tid = threadIdx.x;
-  const int slot = tid >> 2, piece = tid & 3;
+template <bool UP>
+__device__ inline void mv_stage_load(const LayerArgs& a, const Item& item, const ItemTok& it, MvStage& st) {
+  constexpr int NCH = UP ? D_MODEL / 32 : D_FF / 32;
+  const int t = threadIdx.x / NCH, c = threadIdx.x % NCH;
 #pragma unroll
-  for (int t = 0; t < GV_GROUP; ++t) {
-    st.v[t] = u32x4{0u, 0u, 0u, 0u};
-    if (t < it.cnt && (UP || slot < 16)) {
-      const uint16_t* src = UP ? a.x + (size_t)tok_of(a, it, t) * D_MODEL + 32 * slot + 8 * piece
-                               : a.h + (size_t)row_of(a, it, t) * D_FF + 32 * slot + 8 * piece;
-      st.v[t] = ld16<false>(src);
-    }
+  for (int i = 0; i < 4; ++i) st.v[i] = u32x4{0u, 0u, 0u, 0u};
+  if (t < GV_GROUP && t < it.cnt) {
+    const uint16_t* src = UP ? a.x + (size_t)item_token(item, t) * D_MODEL + 32 * c
+                             : a.h + (size_t)row_of(a, it, t) * D_FF + 32 * c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.v[i] = ld16<false>(src + 8 * i);
   }
 }
 
+// Activations into LDS in the operand order of the weights' decode: q4_1 in
+// nibble order with the odd elements divided by 16 (exact) to match the
+// 16 * q in which the high nibbles arrive; the other formats in natural order.
 template <int FMT, bool UP>
-__device__ inline void xstage_store(const XStage& st, GvSmem& sm, int buf) {
-  const int tid = threadIdx.x;
-  const int slot = tid >> 2, piece = tid & 3;
-  if (!UP && slot >= 16) return;
+__device__ inline void mv_stage_store(const MvStage& st, MvSmem& sm, int buf) {
+  constexpr int NCH = UP ? D_MODEL / 32 : D_FF / 32;
+  const int t = threadIdx.x / NCH, c = threadIdx.x % NCH;
+  if (t >= GV_GROUP) return;
+  uint32_t n[16], o[16];
 #pragma unroll
-  for (int t = 0; t < GV_GROUP; ++t) {
-    uint32_t n[4] = {st.v[t][0], st.v[t][1], st.v[t][2], st.v[t][3]};
-    if (OPER_F16<FMT> && UP) {  // x arrives as bf16; the stored SwiGLU output is already operand typed
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) n[i] = bf16x2_to_f16x2(n[i]);
-    }
-    uint32_t o[4];
-    if (FMT == FMT_Q4_1) {
-      q4_order(n[0], n[1], n[2], n[3], o);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = n[i];
-    }
-    sm.x[buf][t][piece][slot] = u32x4{o[0], o[1], o[2], o[3]};
+    for (int e = 0; e < 4; ++e) n[4 * i + e] = st.v[i][e];
   }
+  if (OPER_F16<FMT> && UP) {  // x arrives as bf16; the stored SwiGLU output is already operand typed
+#pragma unroll
+    for (int i = 0; i < 16; ++i) n[i] = bf16x2_to_f16x2(n[i]);
+  }
+  if constexpr (FMT == FMT_Q4_1) {
+    const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    float se = 0.f, so = 0.f;  // sums of x' over the even and the odd elements
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      q4_order(n[4 * p], n[4 * p + 1], n[4 * p + 2], n[4 * p + 3], &o[4 * p]);
+      o[4 * p + 1] = as_u32(as_f16x2(o[4 * p + 1]) * sixteenth);
+      o[4 * p + 3] = as_u32(as_f16x2(o[4 * p + 3]) * sixteenth);
+      se += (f16lo(o[4 * p]) + f16hi(o[4 * p])) + (f16lo(o[4 * p + 2]) + f16hi(o[4 * p + 2]));
+      so += (f16lo(o[4 * p + 1]) + f16hi(o[4 * p + 1])) + (f16lo(o[4 * p + 3]) + f16hi(o[4 * p + 3]));
+    }
+    sm.ks[buf][c].negK[t] = -1024.f * (se + so);
+    sm.ks[buf][c].S[t] = se + 16.f * so;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[i] = n[i];
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(sm.x[buf] + t * MV_TOKW + c * 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
 }
 
+// The lane's activations for one K-chunk (token j = lane & 3) and, for q4_1,
+// the 4 tokens' accumulator seeds and sums of that chunk.
 template <int FMT>
-__device__ inline void x_from_lds(typename GV<FMT>::X& x, const GvSmem& sm, int buf, int t, int slot) {
+__device__ inline void mv_acts(const MvSmem& sm, int buf, int chunk, int j, uint32_t* xq, f32x4& negK, f32x4& S) {
+  const u32x4* src = reinterpret_cast<const u32x4*>(sm.x[buf] + j * MV_TOKW + chunk * 16);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const u32x4 v = sm.x[buf][t][j][slot];
-    x.p[4 * j] = v[0]; x.p[4 * j + 1] = v[1]; x.p[4 * j + 2] = v[2]; x.p[4 * j + 3] = v[3];
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 v = src[i];
+    xq[4 * i] = v[0]; xq[4 * i + 1] = v[1]; xq[4 * i + 2] = v[2]; xq[4 * i + 3] = v[3];
   }
+  if (FMT == FMT_Q4_1) {
+    const MvKS& k = sm.ks[buf][chunk];
+    negK = f32x4{k.negK[0], k.negK[1], k.negK[2], k.negK[3]};
+    S = f32x4{k.S[0], k.S[1], k.S[2], k.S[3]};
+  }
+}
+
+// One weight load (32 elements of one row) against the 4 tokens' activations:
+// acc[t] += sum_k x_tk w_k.
+template <int FMT> struct MV;
+
+template <> struct MV<FMT_Q4_1> {
+  // With the nibbles ORed into fp16 1024, the products give
+  // sum(x' w') = K + sum(q x), K = 1024 sum(x'); the block dot is
+  // d (sum(x' w') - K) + m sum(x).
+  static __device__ void unit(const GV<FMT_Q4_1>::Raw& r, const uint32_t* xq, f32x4 negK, f32x4 S, f32x4& acc) {
+    const uint32_t mg = magic_vgpr();
+    f32x4 d = negK;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t w = r.c[p], w8 = w >> 8;
+      d = mfma4<FMT_Q4_1>(xq[4 * p], xq[4 * p + 1], and_or(w, 0x000F000Fu, mg), and_or(w, 0x00F000F0u, mg), d);
+      d = mfma4<FMT_Q4_1>(xq[4 * p + 2], xq[4 * p + 3], and_or(w8, 0x000F000Fu, mg), and_or(w8, 0x00F000F0u, mg),
+                          d);
+    }
+    const float sc = f16lo(r.dm), mn = f16hi(r.dm);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = fmaf(sc, d[t], fmaf(mn, S[t], acc[t]));
+  }
+};
+
+template <> struct MV<FMT_NVFP4> {
+  // E2M1 * E4M3 is exact in fp16, so the block scales go into the operand and
+  // the products accumulate straight on; the per-matrix scale comes after.
+  static __device__ void unit(const GV<FMT_NVFP4>::Raw& r, const uint32_t* xq, f32x4, f32x4, f32x4& acc) {
+    const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8(r.s, 0);
+    const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8(r.s, 1);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const f16x2 s = (p < 2) ? f16x2{s0, s0} : f16x2{s1, s1};
+      const uint32_t w = r.c[p];
+      acc = mfma4<FMT_NVFP4>(xq[4 * p], xq[4 * p + 1], as_u32(as_f16x2(fp4x2_to_f16x2<0>(w)) * s),
+                             as_u32(as_f16x2(fp4x2_to_f16x2<1>(w)) * s), acc);
+      acc = mfma4<FMT_NVFP4>(xq[4 * p + 2], xq[4 * p + 3], as_u32(as_f16x2(fp4x2_to_f16x2<2>(w)) * s),
+                             as_u32(as_f16x2(fp4x2_to_f16x2<3>(w)) * s), acc);
+    }
+  }
+};
+
+template <> struct MV<FMT_BF16> {
+  static __device__ void unit(const GV<FMT_BF16>::Raw& r, const uint32_t* xq, f32x4, f32x4, f32x4& acc) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      acc = mfma4<FMT_BF16>(xq[2 * m], xq[2 * m + 1], r.c[m >> 1][2 * (m & 1)], r.c[m >> 1][2 * (m & 1) + 1], acc);
+  }
+};
+
+// Sum over the 16 chunk lanes (lane bits 2..5) of 8 values per lane, lo[t]
+// and hi[t].  Afterwards a lane with bit 2 clear holds, for its row (lane
+// bits 0..1), value (bit 5 ? hi : lo)[2 * bit 4 + bit 3].
+__device__ inline float mv_reduce8(f32x4 lo, f32x4 hi) {
+  const float a0 = halve_step<32>(lo[0], hi[0]), a1 = halve_step<32>(lo[1], hi[1]);
+  const float a2 = halve_step<32>(lo[2], hi[2]), a3 = halve_step<32>(lo[3], hi[3]);
+  const float b0 = halve_step<16>(a0, a2), b1 = halve_step<16>(a1, a3);
+  const float c0 = halve_step<8>(b0, b1);
+  // partner lane + 4 inside the row of 16 lanes (DPP row_ror 12)
+  return c0 + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(c0), 0x12C, 0xF, 0xF, false));
 }
 
 // Weight matrices of a chunk's expert (uniform across the workgroup).
@@ -567,99 +471,47 @@ __device__ inline Item fetch_item(const LayerArgs& a, const Item* list, int idx,
   return it;
 }
 
-template <int MT> constexpr int POW2_UP = MT <= 1 ? 1 : MT <= 2 ? 2 : MT <= 4 ? 4 : 8;
-
 // value of lane ^ 32 in the lanes below 32
 __device__ inline float upper_half(float v) {
   return __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false)[1]);
 }
 
-// One chunk of gate/up for MT token slots (slots >= the item's count hold zero
-// activations): UP_STEPS row pairs per wave from the ring, each slot refilled
-// with the row UP_RING steps ahead, which past the chunk's end is a row of the
-// next chunk (nw, nr0) when there is one.
-template <int FMT, int MT>
-__device__ inline void up_chunk(typename GV<FMT>::Raw* rg, typename GV<FMT>::Raw* ru, const ChunkW& w, size_t r0,
-                                const ChunkW& nw, size_t nr0, bool has_next, const GvSmem& sm, int buf, int cnt,
-                                uint16_t* hbase) {
-  using F = GV<FMT>;
-  constexpr int D = UP_RING<FMT>;
-  constexpr int RP = POW2_UP<MT>;          // token slots padded to a power of two
-  constexpr int EPI = 4 / RP;              // steps whose sums are reduced together (8 sums per lane)
-  constexpr int P = 2 * EPI * RP;          // partial sums per lane: [gate/up][step][token]
-  static_assert(UP_STEPS % EPI == 0 && P <= 64, "reduction batch");
-  const int lane = threadIdx.x & 63;
-  typename F::X xs[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    x_from_lds<FMT>(xs[t], sm, buf, t, lane);
-    F::sums(xs[t]);
-  }
-  // after the transposing reduction a lane holds one (gate/up, step, token)
-  // total; the gate totals sit in lanes < 32 and the matching up totals in lane ^ 32
-  bool wr;
-  const int my_idx = xreduce_index<P, 64>(lane, wr);
-  const int my_t = my_idx % RP, my_r = (my_idx / RP) % EPI;
-  const bool writer = lane < 32 && wr && my_t < cnt;
-  uint16_t* hdst = hbase + (size_t)my_t * D_FF + my_r;
-  float v[P];
-#pragma unroll
-  for (int s = 0; s < UP_STEPS; ++s) {
-    const int slot = s % D, r = s % EPI;
-    typename F::U ug, uu;
-    F::unpack(ug, rg[slot], w.tsg);
-    F::unpack(uu, ru[slot], w.tsu);
-    if (s + D < UP_STEPS) {
-      rg[slot] = F::template load<true>(w.g, r0 + s + D, 0u, lane, D_MODEL);
-      ru[slot] = F::template load<true>(w.u, r0 + s + D, 0u, lane, D_MODEL);
-    } else if (has_next) {
-      rg[slot] = F::template load<true>(nw.g, nr0 + s + D - UP_STEPS, 0u, lane, D_MODEL);
-      ru[slot] = F::template load<true>(nw.u, nr0 + s + D - UP_STEPS, 0u, lane, D_MODEL);
-    }
-#pragma unroll
-    for (int t = 0; t < RP; ++t) {
-      v[r * RP + t] = (t < MT) ? F::dot1(ug, xs[t < MT ? t : 0]) : 0.f;
-      v[(EPI + r) * RP + t] = (t < MT) ? F::dot1(uu, xs[t < MT ? t : 0]) : 0.f;
-    }
-    if (r == EPI - 1) {
-      xreduce<P, 64>(v);
-      const float u = upper_half(v[0]);
-      if (writer) hdst[s - r] = h_store<FMT>(silu_mul(v[0], u));
-    }
-  }
-}
-
 // gate/up + SwiGLU over vector-path chunks [0, n) of `list` (or of the shared
 // expert), this workgroup taking c = blockIdx.x, +gridDim.x, ...
 template <int FMT, bool SHARED>
-__device__ void up_stream(const LayerArgs& a, const Item* list, int n, GvSmem& sm) {
-  using F = GV<FMT>;
-  constexpr int D = UP_RING<FMT>;
-  static_assert(UP_STEPS % D == 0, "ring must divide the steps of a chunk");
+__device__ void up_stream(const LayerArgs& a, const Item* list, int n, MvSmem& sm) {
+  using G = GV<FMT>;
+  constexpr int D = MV_UP_RING<FMT>, NU = MV_UP_UNITS;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 3, b = lane >> 2;
   int c = blockIdx.x;
   if (c >= n) return;
   Item item = fetch_item<SHARED>(a, list, c, N_UP_CHUNKS);
   ItemTok it = item_tokens(item, SHARED);
   ChunkW w = chunk_weights<FMT, SHARED, true>(a, item);
-  // this wave's row pairs of a chunk: first_row + s, s = 0 .. UP_STEPS-1
+  // load u of a chunk: row group g = u / 8, K-quarter q = (u / 2) % 4, matrix
+  // u % 2 (gate, up); lane (b, j) reads chunk 16 q + b of row first_row + 4 g + j
   auto first_row = [&](const Item& itm, const ChunkW& cw) {
-    return (size_t)cw.mat * D_FF + item_chunk(itm.head) * UP_ROWS + wave * UP_STEPS;
+    return (size_t)cw.mat * D_FF + item_chunk(itm.head) * UP_ROWS + wave * (UP_ROWS / 4);
+  };
+  auto load_unit = [&](const ChunkW& cw, size_t r0, int u) {
+    return G::template load<true>((u & 1) ? cw.u : cw.g, r0 + 4 * (u >> 3), (uint32_t)j, 16 * ((u >> 1) & 3) + b,
+                                  D_MODEL);
   };
   size_t r0 = first_row(item, w);
-  typename F::Raw rg[D], ru[D];
+  typename G::Raw ring[D];
 #pragma unroll
-  for (int i = 0; i < D; ++i) {
-    rg[i] = F::template load<true>(w.g, r0 + i, 0u, lane, D_MODEL);
-    ru[i] = F::template load<true>(w.u, r0 + i, 0u, lane, D_MODEL);
-  }
+  for (int i = 0; i < D; ++i) ring[i] = load_unit(w, r0, i);
   int buf = 0;
   {
-    XStage st;
-    xstage_load<FMT, true>(a, it, st);
-    xstage_store<FMT, true>(st, sm, buf);
+    MvStage st;
+    mv_stage_load<true>(a, item, it, st);
+    mv_stage_store<FMT, true>(st, sm, buf);
   }
   __syncthreads();
+  // after each group's reduction, lanes with bits 5 and 2 clear hold gate
+  // sums of token 2 * bit 4 + bit 3 (the matching up sums sit in lane + 32)
+  const int my_t = ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
 #pragma unroll 1
   for (;;) {
     const int nc = c + gridDim.x;
@@ -668,22 +520,39 @@ __device__ void up_stream(const LayerArgs& a, const Item* list, int n, GvSmem& s
     ItemTok nit = it;
     ChunkW nw = w;
     size_t nr0 = r0;
-    XStage st;
+    MvStage st;
     if (has_next) {
       nitem = fetch_item<SHARED>(a, list, nc, N_UP_CHUNKS);
       nit = item_tokens(nitem, SHARED);
       nw = chunk_weights<FMT, SHARED, true>(a, nitem);
       nr0 = first_row(nitem, nw);
-      xstage_load<FMT, true>(a, nit, st);
+      mv_stage_load<true>(a, nitem, nit, st);
     }
-    const int cnt = it.cnt;
-    uint16_t* hbase = a.h + (size_t)row_of(a, it, 0) * D_FF + item_chunk(item.head) * UP_ROWS + wave * UP_STEPS;
-    if (cnt <= 1) up_chunk<FMT, 1>(rg, ru, w, r0, nw, nr0, has_next, sm, buf, cnt, hbase);
-    else if (cnt == 2) up_chunk<FMT, 2>(rg, ru, w, r0, nw, nr0, has_next, sm, buf, cnt, hbase);
-    else if (cnt == 3) up_chunk<FMT, 3>(rg, ru, w, r0, nw, nr0, has_next, sm, buf, cnt, hbase);
-    else up_chunk<FMT, GV_GROUP>(rg, ru, w, r0, nw, nr0, has_next, sm, buf, cnt, hbase);
+    const bool writer = (lane & 36) == 0 && my_t < it.cnt;
+    uint16_t* hdst = a.h + (size_t)(row_of(a, it, 0) + my_t) * D_FF + item_chunk(item.head) * UP_ROWS +
+                     wave * (UP_ROWS / 4) + j;
+    f32x4 acc[2] = {}, negK = {}, S = {};
+    uint32_t xq[16];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int g = u >> 3, q = (u >> 1) & 3, m = u & 1;
+      if (m == 0) {
+        mv_acts<FMT>(sm, buf, 16 * q + b, j, xq, negK, S);
+        if (q == 0) acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      const typename G::Raw cur = ring[u % D];
+      if (u + D < NU) ring[u % D] = load_unit(w, r0, u + D);
+      else if (has_next) ring[u % D] = load_unit(nw, nr0, u + D - NU);
+      MV<FMT>::unit(cur, xq, negK, S, acc[m]);
+      if (u % 8 == 7) {
+        float v = mv_reduce8(acc[0], acc[1]);
+        if (FMT == FMT_NVFP4) v *= (lane & 32) ? w.tsu : w.tsg;
+        const float up = upper_half(v);
+        if (writer) hdst[4 * g] = h_store<FMT>(silu_mul(v, up));
+      }
+    }
     if (!has_next) break;
-    xstage_store<FMT, true>(st, sm, buf ^ 1);
+    mv_stage_store<FMT, true>(st, sm, buf ^ 1);
     __syncthreads();
     buf ^= 1;
     c = nc;
@@ -694,79 +563,39 @@ __device__ void up_stream(const LayerArgs& a, const Item* list, int n, GvSmem& s
   }
 }
 
-// One chunk of down for MT token slots: DN_STEPS groups of 4 rows per wave (16
-// lanes per 512-long row), ring refilled as in up_chunk.
-template <int FMT, int MT>
-__device__ inline void down_chunk(typename GV<FMT>::Raw* ring, const ChunkW& w, size_t r0, const ChunkW& nw,
-                                  size_t nr0, bool has_next, const GvSmem& sm, int buf, int cnt, float* ybase) {
-  using F = GV<FMT>;
-  constexpr int R = DN_RING<FMT> < DN_STEPS ? DN_RING<FMT> : DN_STEPS;
-  constexpr int RP = POW2_UP<MT>;
-  constexpr int EPI = 8 / RP;                              // row groups reduced together (8 sums per lane)
-  constexpr int P = EPI * RP;                              // partial sums per lane: [group][token]
-  static_assert(DN_STEPS % EPI == 0 && P <= 16, "reduction batch");
-  const int slot16 = threadIdx.x & 15;
-  const uint32_t sub = (threadIdx.x & 63) >> 4;  // row of the lane within a 4-row group
-  typename F::X xs[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    x_from_lds<FMT>(xs[t], sm, buf, t, slot16);
-    F::sums(xs[t]);
-  }
-  bool wr;
-  const int my_idx = xreduce_index<P, 16>(slot16, wr);
-  const int my_t = my_idx % RP, my_g = my_idx / RP;
-  const bool writer = wr && my_t < cnt;
-  float* ydst = ybase + (size_t)my_t * D_MODEL + 4 * my_g;
-  float v[P];
-#pragma unroll
-  for (int g = 0; g < DN_STEPS; ++g) {
-    const int slot = g % R, r = g % EPI;
-    typename F::U u;
-    F::unpack(u, ring[slot], w.tsg);
-    if (g + R < DN_STEPS) {
-      ring[slot] = F::template load<true>(w.g, r0 + 4 * (g + R), sub, slot16, D_FF);
-    } else if (has_next) {
-      ring[slot] = F::template load<true>(nw.g, nr0 + 4 * (g + R - DN_STEPS), sub, slot16, D_FF);
-    }
-#pragma unroll
-    for (int t = 0; t < RP; ++t) v[r * RP + t] = (t < MT) ? F::dot1(u, xs[t < MT ? t : 0]) : 0.f;
-    if (r == EPI - 1) {
-      xreduce<P, 16>(v);
-      if (writer) ydst[4 * (g - r)] = v[0];
-    }
-  }
-}
-
-// down over vector-path chunks, workgroup-strided as up_stream
+// down over vector-path chunks, workgroup-strided as up_stream: load u of a
+// chunk covers rows first_row + 4 u + j over the whole K = 512 (chunk b per lane)
 template <int FMT, bool SHARED>
-__device__ void down_stream(const LayerArgs& a, const Item* list, int n, GvSmem& sm) {
-  using F = GV<FMT>;
-  constexpr int R = DN_RING<FMT> < DN_STEPS ? DN_RING<FMT> : DN_STEPS;
-  static_assert(DN_STEPS % R == 0, "ring must divide the steps of a chunk");
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int slot16 = threadIdx.x & 15, rsub = (threadIdx.x & 63) >> 4;
+__device__ void down_stream(const LayerArgs& a, const Item* list, int n, MvSmem& sm) {
+  using G = GV<FMT>;
+  constexpr int D = MV_DN_RING<FMT>, NU = MV_DN_UNITS;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 3, b = lane >> 2;
   int c = blockIdx.x;
   if (c >= n) return;
   Item item = fetch_item<SHARED>(a, list, c, N_DN_CHUNKS);
   ItemTok it = item_tokens(item, SHARED);
   ChunkW w = chunk_weights<FMT, SHARED, false>(a, item);
-  // rows of this lane: first_row + rsub + 4 g, g = 0 .. DN_STEPS-1 (first_row is
-  // workgroup-uniform, rsub the lane's row within a 4-row group)
   auto first_row = [&](const Item& itm, const ChunkW& cw) {
     return (size_t)cw.mat * D_MODEL + item_chunk(itm.head) * DN_ROWS + wave * (DN_ROWS / 4);
   };
+  auto load_unit = [&](const ChunkW& cw, size_t r0, int u) {
+    return G::template load<true>(cw.g, r0 + 4 * u, (uint32_t)j, b, D_FF);
+  };
   size_t r0 = first_row(item, w);
-  typename F::Raw ring[R];
+  typename G::Raw ring[D];
 #pragma unroll
-  for (int i = 0; i < R; ++i) ring[i] = F::template load<true>(w.g, r0 + 4 * i, (uint32_t)rsub, slot16, D_FF);
+  for (int i = 0; i < D; ++i) ring[i] = load_unit(w, r0, i);
   int buf = 0;
   {
-    XStage st;
-    xstage_load<FMT, false>(a, it, st);
-    xstage_store<FMT, false>(st, sm, buf);
+    MvStage st;
+    mv_stage_load<false>(a, item, it, st);
+    mv_stage_store<FMT, false>(st, sm, buf);
   }
   __syncthreads();
+  // after a reduction over two row groups, lanes with bit 2 clear hold row
+  // group (2 p + bit 5)'s sum for token 2 * bit 4 + bit 3
+  const int my_t = ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
 #pragma unroll 1
   for (;;) {
     const int nc = c + gridDim.x;
@@ -775,23 +604,36 @@ __device__ void down_stream(const LayerArgs& a, const Item* list, int n, GvSmem&
     ItemTok nit = it;
     ChunkW nw = w;
     size_t nr0 = r0;
-    XStage st;
+    MvStage st;
     if (has_next) {
       nitem = fetch_item<SHARED>(a, list, nc, N_DN_CHUNKS);
       nit = item_tokens(nitem, SHARED);
       nw = chunk_weights<FMT, SHARED, false>(a, nitem);
       nr0 = first_row(nitem, nw);
-      xstage_load<FMT, false>(a, nit, st);
+      mv_stage_load<false>(a, nitem, nit, st);
     }
-    const int cnt = it.cnt;
-    float* ybase =
-        a.y + (size_t)row_of(a, it, 0) * D_MODEL + item_chunk(item.head) * DN_ROWS + wave * (DN_ROWS / 4) + rsub;
-    if (cnt <= 1) down_chunk<FMT, 1>(ring, w, r0, nw, nr0, has_next, sm, buf, cnt, ybase);
-    else if (cnt == 2) down_chunk<FMT, 2>(ring, w, r0, nw, nr0, has_next, sm, buf, cnt, ybase);
-    else if (cnt == 3) down_chunk<FMT, 3>(ring, w, r0, nw, nr0, has_next, sm, buf, cnt, ybase);
-    else down_chunk<FMT, GV_GROUP>(ring, w, r0, nw, nr0, has_next, sm, buf, cnt, ybase);
+    const bool writer = (lane & 4) == 0 && my_t < it.cnt;
+    float* ydst = a.y + (size_t)(row_of(a, it, 0) + my_t) * D_MODEL + item_chunk(item.head) * DN_ROWS +
+                  wave * (DN_ROWS / 4) + 4 * ((lane >> 5) & 1) + j;
+    uint32_t xq[16];
+    f32x4 negK = {}, S = {};
+    mv_acts<FMT>(sm, buf, b, j, xq, negK, S);
+    f32x4 acc[2];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const typename G::Raw cur = ring[u % D];
+      if (u + D < NU) ring[u % D] = load_unit(w, r0, u + D);
+      else if (has_next) ring[u % D] = load_unit(nw, nr0, u + D - NU);
+      acc[u & 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      MV<FMT>::unit(cur, xq, negK, S, acc[u & 1]);
+      if (u & 1) {
+        float v = mv_reduce8(acc[0], acc[1]);
+        if (FMT == FMT_NVFP4) v *= w.tsg;
+        if (writer) ydst[4 * (u - 1)] = v;
+      }
+    }
     if (!has_next) break;
-    xstage_store<FMT, false>(st, sm, buf ^ 1);
+    mv_stage_store<FMT, false>(st, sm, buf ^ 1);
     __syncthreads();
     buf ^= 1;
     c = nc;
@@ -998,7 +840,7 @@ template <int FMT, bool SHARED>
 __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_up_kernel(LayerArgs a) {
   __shared__ union {
     FfnSmem mf;
-    GvSmem gv;
+    MvSmem gv;
   } sm;
   const bool shared_mfma = bucket_mfma(a.T);
   const int n_all = SHARED ? shared_items(a.T, N_UP_CHUNKS) : a.ctl[CTL_N_UP];
@@ -1020,7 +862,7 @@ template <int FMT, bool SHARED>
 __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_down_kernel(LayerArgs a) {
   __shared__ union {
     FfnSmem mf;
-    GvSmem gv;
+    MvSmem gv;
   } sm;
   const bool shared_mfma = bucket_mfma(a.T);
   const int n_all = SHARED ? shared_items(a.T, N_DN_CHUNKS) : a.ctl[CTL_N_DN];
