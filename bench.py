@@ -2,7 +2,7 @@
 """Throughput of the MoE-layer forward on one MI355X.
 
 A step is one pass of the whole layer (router, top-k, buckets, gate/up +
-SwiGLU, down, combine; the shared expert on the library's side stream) over
+SwiGLU, down, combine; the shared expert in the same work lists) over
 one batch of synthetic tokens.  Steps are timed as HIP-graph replays of the
 library's forward (one captured graph per layer instance; the forward is
 capturable because it never synchronises the host), which is how a decode
@@ -129,10 +129,9 @@ def main() -> int:
         U = int((bufs["counts"].cpu().numpy() > 0).sum())
         touched.append(U)
         step_w_bytes.append((U + 1) * exp_b)
-        # routed gate/up launch: the touched experts' gate and up matrices, the
-        # tokens once, the SwiGLU rows of the S slots (the shared expert is a
-        # launch of its own on the side stream)
-        up_bytes.append(U * gu_b + T * 2048 * 2 + S * 512 * 2)
+        # gate/up launch: the gate and up matrices of the touched experts and
+        # the shared one, the tokens once, the SwiGLU rows of the S + T slots
+        up_bytes.append((U + 1) * gu_b + T * 2048 * 2 + (S + T) * 512 * 2)
     router_b = E * 2048 * 2
 
     def step(i, events=None, on=None):

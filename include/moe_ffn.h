@@ -34,10 +34,11 @@
  *     results are valid once the caller synchronises that stream; no call
  *     synchronises the host and data-dependent sizes stay on the device, so a
  *     forward can be captured in a HIP graph;
- *   - a layer handle is immutable after create; it owns one HIP stream and two
- *     events (no device memory), on which the shared expert overlaps the
- *     router; concurrent forwards on one handle are safe when each uses its
- *     own workspace and outputs (their shared-expert work is serialised).
+ *   - a layer handle is immutable after create and holds no GPU resources;
+ *     every forward runs as one chain of kernels on the caller's stream (the
+ *     shared expert's work sits in the same work lists as the routed
+ *     experts'); concurrent forwards on one handle are safe when each uses
+ *     its own workspace and outputs.
  */
 #ifndef MOE_FFN_H
 #define MOE_FFN_H
@@ -121,9 +122,8 @@ typedef struct {
 typedef struct moe_layer moe_layer; /* opaque, host memory only */
 
 /* Validate desc and weights (pointers, alignment), check that the current
- * device is gfx950, create the handle's side stream and events on it, and
- * return the handle.  No device memory is allocated and no weight is
- * repacked: the layouts above are the device layouts. */
+ * device is gfx950, and return the handle.  No device memory is allocated and
+ * no weight is repacked: the layouts above are the device layouts. */
 moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights* weights, moe_layer** out);
 
 /* Free a handle (NULL-safe). */
@@ -144,10 +144,9 @@ moe_status moe_layer_forward(const moe_layer* layer, const void* x, int32_t T, v
 
 /* moe_layer_forward that also records caller-created HIP events (hipEvent_t
  * passed as void*) on the caller's stream: events[i] just before stage i is
- * enqueued -- 0 router logits, 1 top-k, 2 buckets, 3 routed gate/up + SwiGLU,
- * 4 routed down, 5 combine (after the join with the shared expert, which runs
- * on the handle's side stream overlapping stages 0-4) -- and events[6] after
- * the last stage.  n_events must be MOE_N_STAGE_EVENTS.  Used to time each
+ * enqueued -- 0 router logits, 1 top-k, 2 buckets and work lists, 3 gate/up
+ * + SwiGLU (routed and shared experts), 4 down, 5 combine -- and events[6]
+ * after the last stage.  n_events must be MOE_N_STAGE_EVENTS.  Used to time each
  * kernel on the stream it runs on; results are identical to
  * moe_layer_forward.  Event record failures return MOE_ERR_HIP. */
 #define MOE_N_STAGE_EVENTS 7

@@ -5,23 +5,17 @@
 #include <stdio.h>
 #include <string.h>
 
-#include <mutex>
 #include <string>
 
 #include "common.hpp"
 #include "moe_ffn.h"
 
-// Handle: the borrowed weights plus a second stream on which the shared expert
-// (which does not depend on routing) runs concurrently with the router, joined
-// back before the routed down projection combines its output.
+// Handle: the checked descriptor and the borrowed weights (no GPU resources).
 struct moe_layer {
   moe_layer_desc desc;
   moe_layer_weights w;
   int device;
   int n_cu;
-  hipStream_t side;
-  hipEvent_t fork, join;
-  std::mutex mu;  // fork/join sequences of concurrent callers must not interleave
 };
 
 namespace {
@@ -88,8 +82,10 @@ WsLayout ws_layout(const moe_layer_desc& d, int T) {
   WsLayout L;
   const int E = d.n_experts, K = d.top_k;
   const size_t S = (size_t)T * K, R = S + (size_t)d.n_shared * T;
-  // token tiles of the routed buckets: sum_e ceil(m_e / GV_GROUP) <= touched + S / GV_GROUP
-  const int tiles = (int)((S < (size_t)E ? S : (size_t)E) + S / moe::GV_GROUP + 1);
+  // token tiles of the routed buckets, sum_e ceil(m_e / GV_GROUP) <= touched + S / GV_GROUP,
+  // plus those of the shared expert
+  const int tiles = (int)((S < (size_t)E ? S : (size_t)E) + S / moe::GV_GROUP + 1) +
+                    (d.n_shared ? moe::bucket_tiles(T) : 0);
   L.max_up = tiles * moe::N_UP_CHUNKS;
   L.max_dn = tiles * moe::N_DN_CHUNKS;
   size_t o = 0;
@@ -169,27 +165,15 @@ hipError_t mark(void* const* ev, int i, hipStream_t s) {
   return ev ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess;
 }
 
-// One layer on stream s: the shared expert forks onto the handle's side stream
-// right away; router, top-k, buckets and the routed gate/up and down run on s;
-// the side stream joins before the combine.  Route copies (except the output)
-// are enqueued before the combine, which in a stack overwrites the layer
-// input.  ev (optional): stage records.
-moe_status run_layer(moe_layer* L, moe::LayerArgs& a, const WsLayout& W, const moe_route_out* route, hipStream_t s,
-                     void* const* ev) {
-  std::lock_guard<std::mutex> lock(L->mu);
+// One layer on stream s: router, top-k, buckets and work lists, gate/up +
+// SwiGLU and down over the routed and shared experts, combine.  Route copies
+// (except the output) are enqueued before the combine, which in a stack
+// overwrites the layer input.  ev (optional): stage records.
+moe_status run_layer(const moe_layer* L, moe::LayerArgs& a, const WsLayout& W, const moe_route_out* route,
+                     hipStream_t s, void* const* ev) {
   hipError_t e;
   a.write_logits = (route && route->logits) ? 1 : 0;
   if (a.write_logits) a.logits = route->logits;
-  if (a.n_shared) {
-    if ((e = hipEventRecord(L->fork, s)) != hipSuccess) return hip_fail(e, "fork record");
-    if ((e = hipStreamWaitEvent(L->side, L->fork, 0)) != hipSuccess) return hip_fail(e, "fork wait");
-    const int tiles = moe::bucket_tiles(a.T);
-    if ((e = moe::launch_ffn(a, true, true, L->n_cu, tiles * moe::N_UP_CHUNKS, L->side)) != hipSuccess)
-      return hip_fail(e, "shared gate/up launch");
-    if ((e = moe::launch_ffn(a, false, true, L->n_cu, tiles * moe::N_DN_CHUNKS, L->side)) != hipSuccess)
-      return hip_fail(e, "shared down launch");
-    if ((e = hipEventRecord(L->join, L->side)) != hipSuccess) return hip_fail(e, "join record");
-  }
   if ((e = mark(ev, 0, s)) != hipSuccess) return hip_fail(e, "event record");
   if ((e = moe::launch_router(a, s)) != hipSuccess) return hip_fail(e, "router launch");
   if ((e = mark(ev, 1, s)) != hipSuccess) return hip_fail(e, "event record");
@@ -208,10 +192,9 @@ moe_status run_layer(moe_layer* L, moe::LayerArgs& a, const WsLayout& W, const m
       return hip_fail(e, "route copy");
   }
   if ((e = mark(ev, 3, s)) != hipSuccess) return hip_fail(e, "event record");
-  if ((e = moe::launch_ffn(a, true, false, L->n_cu, W.max_up, s)) != hipSuccess) return hip_fail(e, "gate/up launch");
+  if ((e = moe::launch_ffn(a, true, L->n_cu, W.max_up, s)) != hipSuccess) return hip_fail(e, "gate/up launch");
   if ((e = mark(ev, 4, s)) != hipSuccess) return hip_fail(e, "event record");
-  if ((e = moe::launch_ffn(a, false, false, L->n_cu, W.max_dn, s)) != hipSuccess) return hip_fail(e, "down launch");
-  if (a.n_shared && (e = hipStreamWaitEvent(s, L->join, 0)) != hipSuccess) return hip_fail(e, "join wait");
+  if ((e = moe::launch_ffn(a, false, L->n_cu, W.max_dn, s)) != hipSuccess) return hip_fail(e, "down launch");
   if ((e = mark(ev, 5, s)) != hipSuccess) return hip_fail(e, "event record");
   if ((e = moe::launch_combine(a, s)) != hipSuccess) return hip_fail(e, "combine launch");
   if ((e = mark(ev, 6, s)) != hipSuccess) return hip_fail(e, "event record");
@@ -259,25 +242,11 @@ moe_status moe_layer_create(const moe_layer_desc* desc, const moe_layer_weights*
   L->w = *w;
   L->device = dev;
   L->n_cu = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
-  L->side = nullptr;
-  L->fork = L->join = nullptr;
-  if ((e = hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking)) != hipSuccess ||
-      (e = hipEventCreateWithFlags(&L->fork, hipEventDisableTiming)) != hipSuccess ||
-      (e = hipEventCreateWithFlags(&L->join, hipEventDisableTiming)) != hipSuccess) {
-    moe_layer_destroy(L);
-    return hip_fail(e, "side stream/event creation");
-  }
   *out = L;
   return MOE_OK;
 }
 
-void moe_layer_destroy(moe_layer* layer) {
-  if (!layer) return;
-  if (layer->fork) (void)hipEventDestroy(layer->fork);
-  if (layer->join) (void)hipEventDestroy(layer->join);
-  if (layer->side) (void)hipStreamDestroy(layer->side);
-  delete layer;
-}
+void moe_layer_destroy(moe_layer* layer) { delete layer; }
 
 moe_status moe_desc_workspace_size(const moe_layer_desc* desc, int32_t T, size_t* bytes) {
   moe_status st = check_desc(desc);
@@ -311,7 +280,7 @@ static moe_status layer_forward_impl(const moe_layer* L, const void* x, int32_t 
   hipStream_t s = (hipStream_t)stream;
   moe::LayerArgs a = make_args(L, x, T, (char*)ws, W);
   a.out = (uint16_t*)y;
-  if ((st = run_layer(const_cast<moe_layer*>(L), a, W, route, s, ev)) != MOE_OK) return st;
+  if ((st = run_layer(L, a, W, route, s, ev)) != MOE_OK) return st;
   hipError_t e;
   if (route && (e = copy_async(route->y_out, y, xb, s)) != hipSuccess) return hip_fail(e, "route copy");
   return MOE_OK;
@@ -378,7 +347,7 @@ moe_status moe_stack_forward(const moe_layer* const* layers, int32_t n, void* x,
     a.y_rec = route ? (uint16_t*)route->y_out : nullptr;
     a.xn_next = last ? nullptr : xn;
     a.x_final = last ? (uint16_t*)x : nullptr;
-    if ((st = run_layer(const_cast<moe_layer*>(L), a, W, route, s, nullptr)) != MOE_OK) return st;
+    if ((st = run_layer(L, a, W, route, s, nullptr)) != MOE_OK) return st;
   }
   return MOE_OK;
 }

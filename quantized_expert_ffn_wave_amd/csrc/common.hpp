@@ -11,6 +11,7 @@ constexpr int D_MODEL = 2048;  // hidden size
 constexpr int D_FF = 512;      // expert width (routed and shared)
 constexpr int MAX_E = 256;     // routed experts
 constexpr int MAX_K = 8;       // experts per token
+constexpr int SHARED_ID = MAX_E;  // expert id of the shared expert in the work lists
 
 enum Fmt : int { FMT_BF16 = 0, FMT_Q4_1 = 1, FMT_NVFP4 = 2 };
 
@@ -34,7 +35,7 @@ __host__ __device__ inline int bucket_tiles(int m) {
 }
 
 // Work item (16 bytes, so that a kernel needs one load to start streaming):
-//   head: expert (9 bits; MAX_E = shared) | row chunk << 9 (5 bits) |
+//   head: expert (9 bits; SHARED_ID = the shared expert) | row chunk << 9 (5 bits) |
 //         token count << 14 (7 bits) | matrix-core path << 31
 //   p0:   first bucket position (routed) or first token (shared); the expert
 //         output rows of the item are p0.. (routed) or S + p0.. (shared)
@@ -47,6 +48,7 @@ __host__ __device__ inline uint32_t item_head(int e, int chunk, int cnt, bool mf
   return (uint32_t)e | ((uint32_t)chunk << 9) | ((uint32_t)cnt << 14) | (mfma ? ITEM_MFMA : 0u);
 }
 __device__ inline int item_expert(uint32_t h) { return (int)(h & 511u); }
+__device__ inline bool item_shared(uint32_t h) { return item_expert(h) == SHARED_ID; }
 __device__ inline int item_chunk(uint32_t h) { return (int)((h >> 9) & 31u); }
 __device__ inline int item_count(uint32_t h) { return (int)((h >> 14) & 127u); }
 __device__ inline bool item_mfma(uint32_t h) { return (h & ITEM_MFMA) != 0; }
@@ -115,8 +117,8 @@ hipError_t launch_router(const LayerArgs& a, hipStream_t s);
 hipError_t launch_topk(const LayerArgs& a, hipStream_t s);
 hipError_t launch_bucket(const LayerArgs& a, hipStream_t s);
 hipError_t launch_combine(const LayerArgs& a, hipStream_t s);
-// gate/up (up) or down over the routed work list or the shared expert; at most
+// gate/up (up) or down over the work list (routed and shared experts); at most
 // max_wgs workgroups, else as many as are resident on n_cu CUs at once
-hipError_t launch_ffn(const LayerArgs& a, bool up, bool shared, int n_cu, int max_wgs, hipStream_t s);
+hipError_t launch_ffn(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s);
 hipError_t launch_stack_init(const uint16_t* x, float* r, uint16_t* xn, int T, float eps, hipStream_t s);
 }  // namespace moe

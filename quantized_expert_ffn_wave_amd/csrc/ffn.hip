@@ -1,23 +1,22 @@
-// Expert FFN over the buckets: gate/up projection with fused SwiGLU, down
-// projection with the weighted combine fused into its epilogue, and the
-// residual/RMSNorm glue of stacked layers.
+// Expert FFN over the work lists: gate/up projection with fused SwiGLU, down
+// projection, the weighted combine, and the residual/RMSNorm glue of stacked
+// layers.
 //
 // The review "Recursive Flint 40B-A2.5B" (orcarouter.ai), section "The
 // architecture is an argument about memory bandwidth", argues that decoding
 // this model is a weight-movement problem: each token touches 6 routed experts
 // and the shared one out of 257 per layer.  So the work is organised around
 // streaming each touched expert's packed weights from HBM once:
-//   * buckets below MFMA_MIN tokens run on the vector ALUs in token groups of
-//     up to 4 (two per pass): a lane owns one 32-element chunk of a weight row
-//     (16 bytes of 4-bit codes), decodes it in registers to fp16 pairs and uses
-//     v_dot2; each wave keeps a ring of row loads in flight and sums across
-//     lanes with permlane swaps and DPP moves;
-//   * buckets of MFMA_MIN or more tokens run on the matrix cores: a weight
-//     tile is decoded into LDS once per 64-token tile (v_mfma 32x32x16), with
-//     the next K-chunk prefetched into registers during the MFMAs.
-// Both kernels are persistent and walk device-side work lists, so no host
-// synchronisation is needed.  The shared expert does not depend on routing and
-// runs as its own launches (on a second stream, overlapping the router).
+//   * buckets below MFMA_MIN tokens (groups of up to 4 tokens) run as a GEMV on
+//     v_mfma_f32_4x4x4_16b: a lane loads one 32-element chunk of a weight row
+//     (16 bytes of 4-bit codes and the block scale), unpacks it in registers,
+//     and the 16 independent 4x4x4 products return it the group's partial sums
+//     of its own row; each wave keeps a ring of loads in flight across chunks;
+//   * buckets of MFMA_MIN or more tokens run as 128-row x 64-token tiles: the
+//     weight tile is decoded into LDS once per tile (v_mfma 32x32x16), with the
+//     next K-chunk prefetched into registers during the MFMAs.
+// Both kernels are persistent and walk device-side work lists that hold the
+// routed and the shared expert alike, so no host synchronisation is needed.
 //
 // Combine: a separate kernel sums, per token, the K weighted expert rows in
 // the fixed order j = 0..K-1 and the shared expert row, and rounds once to
@@ -206,9 +205,9 @@ struct ItemTok {
   bool shared, mfma;
 };
 
-__device__ inline ItemTok item_tokens(const Item& item, bool shared) {
+__device__ inline ItemTok item_tokens(const Item& item) {
   ItemTok r;
-  r.shared = shared;
+  r.shared = item_shared(item.head);
   r.mfma = item_mfma(item.head);
   r.p0 = (int)item.p0;
   r.cnt = item_count(item.head);
@@ -218,19 +217,6 @@ __device__ inline int row_of(const LayerArgs& a, const ItemTok& it, int i) {
   return it.shared ? a.S + it.p0 + i : it.p0 + i;
 }
 
-// Shared-expert items are implicit: item i -> tile i / chunks, chunk i % chunks.
-__device__ inline Item shared_item(int T, int E, int i, int chunks) {
-  const bool mf = bucket_mfma(T);
-  const int per = mf ? MFMA_BN : GV_GROUP;
-  const int tile = i / chunks;
-  Item it;
-  it.p0 = (uint32_t)(tile * per);
-  it.head = item_head(E, i % chunks, min(per, T - tile * per), mf);
-  it.t01 = it.p0 | ((it.p0 + 1) << 16);
-  it.t23 = (it.p0 + 2) | ((it.p0 + 3) << 16);
-  return it;
-}
-__device__ inline int shared_items(int T, int chunks) { return bucket_tiles(T) * chunks; }
 
 // ======================================================================================
 // Vector-path items
@@ -442,16 +428,26 @@ struct ChunkW {
   float tsg, tsu;
 };
 
-template <int FMT, bool SHARED, bool UP>
+// a or b, chosen field by field (a chosen reference would live in scratch)
+__device__ inline QMat sel_qmat(bool first, const QMat& x, const QMat& y) {
+  QMat q;
+  q.codes = first ? x.codes : y.codes;
+  q.scales = first ? x.scales : y.scales;
+  q.ts = first ? x.ts : y.ts;
+  return q;
+}
+
+template <int FMT, bool UP>
 __device__ inline ChunkW chunk_weights(const LayerArgs& a, const Item& item) {
   ChunkW w;
-  const int e = SHARED ? 0 : item_expert(item.head);
+  const bool sh = item_shared(item.head);
+  const int e = sh ? 0 : item_expert(item.head);
   w.mat = e;
   if (UP) {
-    w.g = SHARED ? a.sh_gate : a.gate;
-    w.u = SHARED ? a.sh_up : a.up;
+    w.g = sel_qmat(sh, a.sh_gate, a.gate);
+    w.u = sel_qmat(sh, a.sh_up, a.up);
   } else {
-    w.g = SHARED ? a.sh_down : a.down;
+    w.g = sel_qmat(sh, a.sh_down, a.down);
     w.u = w.g;
   }
   w.tsg = (FMT == FMT_NVFP4) ? w.g.ts[e] : 1.f;
@@ -461,9 +457,8 @@ __device__ inline ChunkW chunk_weights(const LayerArgs& a, const Item& item) {
 
 // The item of a chunk is the same for the whole workgroup: keep it in SGPRs so
 // that the row addresses derived from it are scalar.
-template <bool SHARED>
-__device__ inline Item fetch_item(const LayerArgs& a, const Item* list, int idx, int chunks) {
-  Item it = SHARED ? shared_item(a.T, a.E, idx, chunks) : list[idx];
+__device__ inline Item fetch_item(const Item* list, int idx) {
+  Item it = list[idx];
   it.head = __builtin_amdgcn_readfirstlane(it.head);
   it.p0 = __builtin_amdgcn_readfirstlane(it.p0);
   it.t01 = __builtin_amdgcn_readfirstlane(it.t01);
@@ -476,9 +471,9 @@ __device__ inline float upper_half(float v) {
   return __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false)[1]);
 }
 
-// gate/up + SwiGLU over vector-path chunks [0, n) of `list` (or of the shared
-// expert), this workgroup taking c = blockIdx.x, +gridDim.x, ...
-template <int FMT, bool SHARED>
+// gate/up + SwiGLU over vector-path chunks [0, n) of `list`, this workgroup
+// taking c = blockIdx.x, +gridDim.x, ...
+template <int FMT>
 __device__ void up_stream(const LayerArgs& a, const Item* list, int n, MvSmem& sm) {
   using G = GV<FMT>;
   constexpr int D = MV_UP_RING<FMT>, NU = MV_UP_UNITS;
@@ -486,9 +481,9 @@ __device__ void up_stream(const LayerArgs& a, const Item* list, int n, MvSmem& s
   const int j = lane & 3, b = lane >> 2;
   int c = blockIdx.x;
   if (c >= n) return;
-  Item item = fetch_item<SHARED>(a, list, c, N_UP_CHUNKS);
-  ItemTok it = item_tokens(item, SHARED);
-  ChunkW w = chunk_weights<FMT, SHARED, true>(a, item);
+  Item item = fetch_item(list, c);
+  ItemTok it = item_tokens(item);
+  ChunkW w = chunk_weights<FMT, true>(a, item);
   // load u of a chunk: row group g = u / 8, K-quarter q = (u / 2) % 4, matrix
   // u % 2 (gate, up); lane (b, j) reads chunk 16 q + b of row first_row + 4 g + j
   auto first_row = [&](const Item& itm, const ChunkW& cw) {
@@ -522,9 +517,9 @@ __device__ void up_stream(const LayerArgs& a, const Item* list, int n, MvSmem& s
     size_t nr0 = r0;
     MvStage st;
     if (has_next) {
-      nitem = fetch_item<SHARED>(a, list, nc, N_UP_CHUNKS);
-      nit = item_tokens(nitem, SHARED);
-      nw = chunk_weights<FMT, SHARED, true>(a, nitem);
+      nitem = fetch_item(list, nc);
+      nit = item_tokens(nitem);
+      nw = chunk_weights<FMT, true>(a, nitem);
       nr0 = first_row(nitem, nw);
       mv_stage_load<true>(a, nitem, nit, st);
     }
@@ -565,7 +560,7 @@ __device__ void up_stream(const LayerArgs& a, const Item* list, int n, MvSmem& s
 
 // down over vector-path chunks, workgroup-strided as up_stream: load u of a
 // chunk covers rows first_row + 4 u + j over the whole K = 512 (chunk b per lane)
-template <int FMT, bool SHARED>
+template <int FMT>
 __device__ void down_stream(const LayerArgs& a, const Item* list, int n, MvSmem& sm) {
   using G = GV<FMT>;
   constexpr int D = MV_DN_RING<FMT>, NU = MV_DN_UNITS;
@@ -573,9 +568,9 @@ __device__ void down_stream(const LayerArgs& a, const Item* list, int n, MvSmem&
   const int j = lane & 3, b = lane >> 2;
   int c = blockIdx.x;
   if (c >= n) return;
-  Item item = fetch_item<SHARED>(a, list, c, N_DN_CHUNKS);
-  ItemTok it = item_tokens(item, SHARED);
-  ChunkW w = chunk_weights<FMT, SHARED, false>(a, item);
+  Item item = fetch_item(list, c);
+  ItemTok it = item_tokens(item);
+  ChunkW w = chunk_weights<FMT, false>(a, item);
   auto first_row = [&](const Item& itm, const ChunkW& cw) {
     return (size_t)cw.mat * D_MODEL + item_chunk(itm.head) * DN_ROWS + wave * (DN_ROWS / 4);
   };
@@ -606,9 +601,9 @@ __device__ void down_stream(const LayerArgs& a, const Item* list, int n, MvSmem&
     size_t nr0 = r0;
     MvStage st;
     if (has_next) {
-      nitem = fetch_item<SHARED>(a, list, nc, N_DN_CHUNKS);
-      nit = item_tokens(nitem, SHARED);
-      nw = chunk_weights<FMT, SHARED, false>(a, nitem);
+      nitem = fetch_item(list, nc);
+      nit = item_tokens(nitem);
+      nw = chunk_weights<FMT, false>(a, nitem);
       nr0 = first_row(nitem, nw);
       mv_stage_load<false>(a, nitem, nit, st);
     }
@@ -836,50 +831,39 @@ __device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const Item
 template <int FMT> constexpr int FFN_WG_PER_CU = (FMT == FMT_BF16) ? 1 : 2;
 
 // Items of the matrix-core path come first; the vector-path chunks follow.
-template <int FMT, bool SHARED>
+template <int FMT>
 __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_up_kernel(LayerArgs a) {
   __shared__ union {
     FfnSmem mf;
     MvSmem gv;
   } sm;
-  const bool shared_mfma = bucket_mfma(a.T);
-  const int n_all = SHARED ? shared_items(a.T, N_UP_CHUNKS) : a.ctl[CTL_N_UP];
-  const int n_mf = SHARED ? (shared_mfma ? n_all : 0) : a.ctl[CTL_N_UP_MF];
+  const int n_all = a.ctl[CTL_N_UP], n_mf = a.ctl[CTL_N_UP_MF];
   for (int i = blockIdx.x; i < n_mf; i += gridDim.x) {
-    const Item item = fetch_item<SHARED>(a, a.items_up, i, N_UP_CHUNKS);
-    const int e = SHARED ? 0 : item_expert(item.head);
-    mfma_up<FMT>(a, SHARED ? a.sh_gate : a.gate, SHARED ? a.sh_up : a.up, e, item_tokens(item, SHARED),
-                 item_chunk(item.head) * UP_ROWS, sm.mf);
+    const Item item = fetch_item(a.items_up, i);
+    const bool sh = item_shared(item.head);
+    mfma_up<FMT>(a, sel_qmat(sh, a.sh_gate, a.gate), sel_qmat(sh, a.sh_up, a.up), sh ? 0 : item_expert(item.head),
+                 item_tokens(item), item_chunk(item.head) * UP_ROWS, sm.mf);
   }
-  if (SHARED) {
-    if (!shared_mfma) up_stream<FMT, true>(a, nullptr, n_all, sm.gv);
-  } else {
-    up_stream<FMT, false>(a, a.items_up + n_mf, n_all - n_mf, sm.gv);
-  }
+  up_stream<FMT>(a, a.items_up + n_mf, n_all - n_mf, sm.gv);
 }
 
-template <int FMT, bool SHARED>
+template <int FMT>
 __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_down_kernel(LayerArgs a) {
   __shared__ union {
     FfnSmem mf;
     MvSmem gv;
   } sm;
-  const bool shared_mfma = bucket_mfma(a.T);
-  const int n_all = SHARED ? shared_items(a.T, N_DN_CHUNKS) : a.ctl[CTL_N_DN];
-  const int n_mf = SHARED ? (shared_mfma ? n_all : 0) : a.ctl[CTL_N_DN_MF];
+  const int n_all = a.ctl[CTL_N_DN], n_mf = a.ctl[CTL_N_DN_MF];
   for (int i = blockIdx.x; i < n_mf; i += gridDim.x) {
-    const Item item = fetch_item<SHARED>(a, a.items_dn, i, N_DN_CHUNKS);
-    const int e = SHARED ? 0 : item_expert(item.head);
-    const ItemTok it = item_tokens(item, SHARED);
+    const Item item = fetch_item(a.items_dn, i);
+    const bool sh = item_shared(item.head);
+    const ItemTok it = item_tokens(item);
     const int r0 = item_chunk(item.head) * DN_ROWS;
 #pragma unroll 1
-    for (int rb = 0; rb < DN_ROWS; rb += 128) mfma_down<FMT>(a, SHARED ? a.sh_down : a.down, e, it, r0 + rb, sm.mf);
+    for (int rb = 0; rb < DN_ROWS; rb += 128)
+      mfma_down<FMT>(a, sel_qmat(sh, a.sh_down, a.down), sh ? 0 : item_expert(item.head), it, r0 + rb, sm.mf);
   }
-  if (SHARED) {
-    if (!shared_mfma) down_stream<FMT, true>(a, nullptr, n_all, sm.gv);
-  } else {
-    down_stream<FMT, false>(a, a.items_dn + n_mf, n_all - n_mf, sm.gv);
-  }
+  down_stream<FMT>(a, a.items_dn + n_mf, n_all - n_mf, sm.gv);
 }
 
 // Workgroups of `kernel` that fit on one CU at once (the persistent kernels are
@@ -891,29 +875,23 @@ int resident_per_cu(Kern kernel) {
   return n;
 }
 
-template <int FMT, bool SHARED>
-hipError_t launch_ffn_kernel(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s) {
-  static const int occ_up = resident_per_cu(ffn_up_kernel<FMT, SHARED>);
-  static const int occ_dn = resident_per_cu(ffn_down_kernel<FMT, SHARED>);
+template <int FMT>
+hipError_t launch_ffn_fmt(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s) {
+  static const int occ_up = resident_per_cu(ffn_up_kernel<FMT>);
+  static const int occ_dn = resident_per_cu(ffn_down_kernel<FMT>);
   int grid = n_cu * (up ? occ_up : occ_dn);
   if (max_wgs < grid) grid = max_wgs;
   if (grid < 1) return hipSuccess;
-  if (up) hipLaunchKernelGGL((ffn_up_kernel<FMT, SHARED>), dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((ffn_down_kernel<FMT, SHARED>), dim3(grid), dim3(256), 0, s, a);
+  if (up) hipLaunchKernelGGL((ffn_up_kernel<FMT>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((ffn_down_kernel<FMT>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <int FMT>
-hipError_t launch_ffn_fmt(const LayerArgs& a, bool up, bool shared, int n_cu, int max_wgs, hipStream_t s) {
-  return shared ? launch_ffn_kernel<FMT, true>(a, up, n_cu, max_wgs, s)
-                : launch_ffn_kernel<FMT, false>(a, up, n_cu, max_wgs, s);
-}
-
-hipError_t launch_ffn(const LayerArgs& a, bool up, bool shared, int n_cu, int max_wgs, hipStream_t s) {
+hipError_t launch_ffn(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s) {
   switch (a.fmt) {
-    case FMT_Q4_1: return launch_ffn_fmt<FMT_Q4_1>(a, up, shared, n_cu, max_wgs, s);
-    case FMT_NVFP4: return launch_ffn_fmt<FMT_NVFP4>(a, up, shared, n_cu, max_wgs, s);
-    default: return launch_ffn_fmt<FMT_BF16>(a, up, shared, n_cu, max_wgs, s);
+    case FMT_Q4_1: return launch_ffn_fmt<FMT_Q4_1>(a, up, n_cu, max_wgs, s);
+    case FMT_NVFP4: return launch_ffn_fmt<FMT_NVFP4>(a, up, n_cu, max_wgs, s);
+    default: return launch_ffn_fmt<FMT_BF16>(a, up, n_cu, max_wgs, s);
   }
 }
 

@@ -316,9 +316,9 @@ __device__ void build_buckets(const LayerArgs& a, BucketSmem& sm) {
     __syncthreads();
   }
 
-  // work lists (routed experts only): MFMA items first, then vector items.  Both
-  // lists use the same expert/tile order; the down list has N_DN_CHUNKS chunks
-  // per tile where the gate/up list has N_UP_CHUNKS.
+  // work lists: matrix-core items first, then vector items.  Both lists use
+  // the same tile order; the down list has N_DN_CHUNKS chunks per tile where
+  // the gate/up list has N_UP_CHUNKS.
   for (int e = tid; e < E; e += nth) {
     const int m = sm.cnt[e];
     const int tiles = bucket_tiles(m);
@@ -338,32 +338,51 @@ __device__ void build_buckets(const LayerArgs& a, BucketSmem& sm) {
   }
   __syncthreads();
   const int tiles_m = sm.tot[0], tiles_g = sm.tot[1];
-  const int n_up = min((tiles_m + tiles_g) * N_UP_CHUNKS, a.max_items_up - a.max_items_up % N_UP_CHUNKS);
-  const int n_dn = min((tiles_m + tiles_g) * N_DN_CHUNKS, a.max_items_dn - a.max_items_dn % N_DN_CHUNKS);
+  // The shared expert takes every token: 64-token matrix-core tiles from
+  // MFMA_MIN tokens on, else groups of GV_GROUP tokens, in the same lists.
+  // Tile order: routed matrix-core, shared matrix-core, routed vector, shared
+  // vector (the kernels take the matrix-core items first).
+  const int sh_tiles = a.n_shared ? bucket_tiles(T) : 0;
+  const bool sh_mf = bucket_mfma(T);
+  const int mf_tiles = tiles_m + (sh_mf ? sh_tiles : 0);
+  const int all_tiles = tiles_m + tiles_g + sh_tiles;
+  const int n_up = min(all_tiles * N_UP_CHUNKS, a.max_items_up - a.max_items_up % N_UP_CHUNKS);
+  const int n_dn = min(all_tiles * N_DN_CHUNKS, a.max_items_dn - a.max_items_dn % N_DN_CHUNKS);
   if (tid == 0) {
     a.ctl[CTL_N_UP] = n_up;
     a.ctl[CTL_N_DN] = n_dn;
-    a.ctl[CTL_N_UP_MF] = min(tiles_m * N_UP_CHUNKS, n_up);
-    a.ctl[CTL_N_DN_MF] = min(tiles_m * N_DN_CHUNKS, n_dn);
+    a.ctl[CTL_N_UP_MF] = min(mf_tiles * N_UP_CHUNKS, n_up);
+    a.ctl[CTL_N_DN_MF] = min(mf_tiles * N_DN_CHUNKS, n_dn);
   }
   // one thread per token tile: its N_UP_CHUNKS gate/up items and N_DN_CHUNKS down items
-  const int n_tiles = min(tiles_m + tiles_g, min(a.max_items_up / N_UP_CHUNKS, a.max_items_dn / N_DN_CHUNKS));
+  const int n_tiles = min(all_tiles, min(a.max_items_up / N_UP_CHUNKS, a.max_items_dn / N_DN_CHUNKS));
   for (int ti = tid; ti < n_tiles; ti += nth) {
-    const bool mf = ti < tiles_m;
-    const int* o = mf ? sm.it_m : sm.it_g;
-    const int li = mf ? ti : ti - tiles_m;
-    int lo = 0, hi = E;  // the expert e with o[e] <= li < o[e+1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (o[mid] <= li) lo = mid; else hi = mid;
-    }
-    const int tile = li - o[lo];
+    const bool shared = (ti >= tiles_m && ti < mf_tiles) || ti >= mf_tiles + tiles_g;
+    const bool mf = ti < mf_tiles;
     const int per = mf ? MFMA_BN : GV_GROUP;
-    const int p0 = sm.off[lo] + tile * per;
-    const int cnt = min(per, sm.cnt[lo] - tile * per);
+    int expert, p0, cnt;
     uint32_t tk[GV_GROUP] = {0u, 0u, 0u, 0u};
-    if (!mf) {
-      for (int j = 0; j < cnt; ++j) tk[j] = (uint32_t)(a.perm[p0 + j] / K);
+    if (shared) {
+      const int tile = mf ? ti - tiles_m : ti - mf_tiles - tiles_g;
+      expert = SHARED_ID;
+      p0 = tile * per;
+      cnt = min(per, T - p0);
+      for (int j = 0; j < cnt && j < GV_GROUP; ++j) tk[j] = (uint32_t)(p0 + j);
+    } else {
+      const int* o = mf ? sm.it_m : sm.it_g;
+      const int li = mf ? ti : ti - mf_tiles;
+      int lo = 0, hi = E;  // the expert e with o[e] <= li < o[e+1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (o[mid] <= li) lo = mid; else hi = mid;
+      }
+      const int tile = li - o[lo];
+      expert = lo;
+      p0 = sm.off[lo] + tile * per;
+      cnt = min(per, sm.cnt[lo] - tile * per);
+      if (!mf) {
+        for (int j = 0; j < cnt; ++j) tk[j] = (uint32_t)(a.perm[p0 + j] / K);
+      }
     }
     Item it;
     it.p0 = (uint32_t)p0;
@@ -371,12 +390,12 @@ __device__ void build_buckets(const LayerArgs& a, BucketSmem& sm) {
     it.t23 = tk[2] | (tk[3] << 16);
 #pragma unroll
     for (int c = 0; c < N_UP_CHUNKS; ++c) {
-      it.head = item_head(lo, c, cnt, mf);
+      it.head = item_head(expert, c, cnt, mf);
       a.items_up[ti * N_UP_CHUNKS + c] = it;
     }
 #pragma unroll
     for (int c = 0; c < N_DN_CHUNKS; ++c) {
-      it.head = item_head(lo, c, cnt, mf);
+      it.head = item_head(expert, c, cnt, mf);
       a.items_dn[ti * N_DN_CHUNKS + c] = it;
     }
   }
