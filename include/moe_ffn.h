@@ -144,9 +144,10 @@ moe_status moe_layer_forward(const moe_layer* layer, const void* x, int32_t T, v
 
 /* moe_layer_forward that also records caller-created HIP events (hipEvent_t
  * passed as void*) on the caller's stream: events[i] just before stage i is
- * enqueued -- 0 router logits, 1 top-k, 2 buckets and work lists, 3 gate/up
- * + SwiGLU (routed and shared experts), 4 down, 5 combine -- and events[6]
- * after the last stage.  n_events must be MOE_N_STAGE_EVENTS.  Used to time each
+ * enqueued -- 0 router logits, 1 top-k, 2 buckets and work lists (for T <=
+ * 16 built by stage 1's kernel, so stage 2 is empty), 3 gate/up + SwiGLU
+ * (routed and shared experts), 4 down, 5 combine -- and events[6] after the
+ * last stage.  n_events must be MOE_N_STAGE_EVENTS.  Used to time each
  * kernel on the stream it runs on; results are identical to
  * moe_layer_forward.  Event record failures return MOE_ERR_HIP. */
 #define MOE_N_STAGE_EVENTS 7

@@ -74,8 +74,8 @@ moe_status check_qmat(const moe_qmat& q, int fmt, const char* name) {
 }
 
 struct WsLayout {
-  size_t logit_part, logits, ids, w, counts, offsets, perm, inv_perm, items_up, items_dn, ctl, h, y, total;
-  int max_up, max_dn;
+  size_t logit_part, logits, ids, w, counts, offsets, perm, inv_perm, tiles, ctl, h, y, total;
+  int max_tiles;
 };
 
 WsLayout ws_layout(const moe_layer_desc& d, int T) {
@@ -86,8 +86,7 @@ WsLayout ws_layout(const moe_layer_desc& d, int T) {
   // plus those of the shared expert
   const int tiles = (int)((S < (size_t)E ? S : (size_t)E) + S / moe::GV_GROUP + 1) +
                     (d.n_shared ? moe::bucket_tiles(T) : 0);
-  L.max_up = tiles * moe::N_UP_CHUNKS;
-  L.max_dn = tiles * moe::N_DN_CHUNKS;
+  L.max_tiles = tiles;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes > 0 ? bytes : 1); return at; };
   L.logit_part = take(sizeof(float) * 8 * T * E);
@@ -98,8 +97,7 @@ WsLayout ws_layout(const moe_layer_desc& d, int T) {
   L.offsets = take(sizeof(int32_t) * (E + 1));
   L.perm = take(sizeof(int32_t) * S);
   L.inv_perm = take(sizeof(int32_t) * S);
-  L.items_up = take(sizeof(moe::Item) * L.max_up);
-  L.items_dn = take(sizeof(moe::Item) * L.max_dn);
+  L.tiles = take(sizeof(moe::Item) * L.max_tiles);
   L.ctl = take(sizeof(int32_t) * moe::CTL_WORDS);
   L.h = take(sizeof(uint16_t) * R * moe::D_FF);
   L.y = take(sizeof(float) * R * moe::D_MODEL);
@@ -146,13 +144,11 @@ moe::LayerArgs make_args(const moe_layer* L, const void* x, int T, char* ws, con
   a.offsets = (int32_t*)(ws + W.offsets);
   a.perm = (int32_t*)(ws + W.perm);
   a.inv_perm = (int32_t*)(ws + W.inv_perm);
-  a.items_up = (moe::Item*)(ws + W.items_up);
-  a.items_dn = (moe::Item*)(ws + W.items_dn);
+  a.tiles = (moe::Item*)(ws + W.tiles);
   a.ctl = (int32_t*)(ws + W.ctl);
   a.h = (uint16_t*)(ws + W.h);
   a.y = (float*)(ws + W.y);
-  a.max_items_up = W.max_up;
-  a.max_items_dn = W.max_dn;
+  a.max_tiles = W.max_tiles;
   return a;
 }
 
@@ -192,9 +188,9 @@ moe_status run_layer(const moe_layer* L, moe::LayerArgs& a, const WsLayout& W, c
       return hip_fail(e, "route copy");
   }
   if ((e = mark(ev, 3, s)) != hipSuccess) return hip_fail(e, "event record");
-  if ((e = moe::launch_ffn(a, true, L->n_cu, W.max_up, s)) != hipSuccess) return hip_fail(e, "gate/up launch");
+  if ((e = moe::launch_ffn(a, true, L->n_cu, W.max_tiles * moe::N_UP_CHUNKS, s)) != hipSuccess) return hip_fail(e, "gate/up launch");
   if ((e = mark(ev, 4, s)) != hipSuccess) return hip_fail(e, "event record");
-  if ((e = moe::launch_ffn(a, false, L->n_cu, W.max_dn, s)) != hipSuccess) return hip_fail(e, "down launch");
+  if ((e = moe::launch_ffn(a, false, L->n_cu, W.max_tiles * moe::N_DN_CHUNKS, s)) != hipSuccess) return hip_fail(e, "down launch");
   if ((e = mark(ev, 5, s)) != hipSuccess) return hip_fail(e, "event record");
   if ((e = moe::launch_combine(a, s)) != hipSuccess) return hip_fail(e, "combine launch");
   if ((e = mark(ev, 6, s)) != hipSuccess) return hip_fail(e, "event record");

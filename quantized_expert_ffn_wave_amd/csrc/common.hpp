@@ -80,12 +80,11 @@ struct LayerArgs {
   int32_t* offsets;         // [E+1]
   int32_t* perm;            // [S]
   int32_t* inv_perm;        // [S]
-  Item* items_up;           // routed work list, gate/up
-  Item* items_dn;           // routed work list, down
+  Item* tiles;              // work list: one entry per token tile (row chunk 0)
   int32_t* ctl;             // [CTL_WORDS]
   uint16_t* h;              // [S + n_shared*T][D_FF] SwiGLU output (fp16 or bf16 bits)
   float* y;                 // [S + n_shared*T][D_MODEL] expert outputs
-  int max_items_up, max_items_dn;
+  int max_tiles;
   // combine targets
   uint16_t* out;            // bf16 [T][D_MODEL] layer output (single layer), or null
   float* r;                 // fp32 [T][D_MODEL] residual (stack), or null

@@ -457,8 +457,10 @@ __device__ inline ChunkW chunk_weights(const LayerArgs& a, const Item& item) {
 
 // The item of a chunk is the same for the whole workgroup: keep it in SGPRs so
 // that the row addresses derived from it are scalar.
-__device__ inline Item fetch_item(const Item* list, int idx) {
-  Item it = list[idx];
+// Item idx of a list with `chunks` row chunks per tile.
+__device__ inline Item fetch_item(const Item* tiles, int idx, int chunks) {
+  Item it = tiles[idx / chunks];
+  it.head |= (uint32_t)(idx % chunks) << 9;
   it.head = __builtin_amdgcn_readfirstlane(it.head);
   it.p0 = __builtin_amdgcn_readfirstlane(it.p0);
   it.t01 = __builtin_amdgcn_readfirstlane(it.t01);
@@ -471,17 +473,18 @@ __device__ inline float upper_half(float v) {
   return __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false)[1]);
 }
 
-// gate/up + SwiGLU over vector-path chunks [0, n) of `list`, this workgroup
-// taking c = blockIdx.x, +gridDim.x, ...
+// gate/up + SwiGLU over the vector-path items base + c, c in [0, n), this
+// workgroup taking c = blockIdx.x, +gridDim.x, ...
 template <int FMT>
-__device__ void up_stream(const LayerArgs& a, const Item* list, int n, MvSmem& sm) {
+__device__ void up_stream(const LayerArgs& a, int base, int n, MvSmem& sm) {
   using G = GV<FMT>;
+  constexpr int CH = N_UP_CHUNKS;
   constexpr int D = MV_UP_RING<FMT>, NU = MV_UP_UNITS;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 3, b = lane >> 2;
   int c = blockIdx.x;
   if (c >= n) return;
-  Item item = fetch_item(list, c);
+  Item item = fetch_item(a.tiles, base + c, CH);
   ItemTok it = item_tokens(item);
   ChunkW w = chunk_weights<FMT, true>(a, item);
   // load u of a chunk: row group g = u / 8, K-quarter q = (u / 2) % 4, matrix
@@ -517,7 +520,7 @@ __device__ void up_stream(const LayerArgs& a, const Item* list, int n, MvSmem& s
     size_t nr0 = r0;
     MvStage st;
     if (has_next) {
-      nitem = fetch_item(list, nc);
+      nitem = fetch_item(a.tiles, base + nc, CH);
       nit = item_tokens(nitem);
       nw = chunk_weights<FMT, true>(a, nitem);
       nr0 = first_row(nitem, nw);
@@ -561,14 +564,15 @@ __device__ void up_stream(const LayerArgs& a, const Item* list, int n, MvSmem& s
 // down over vector-path chunks, workgroup-strided as up_stream: load u of a
 // chunk covers rows first_row + 4 u + j over the whole K = 512 (chunk b per lane)
 template <int FMT>
-__device__ void down_stream(const LayerArgs& a, const Item* list, int n, MvSmem& sm) {
+__device__ void down_stream(const LayerArgs& a, int base, int n, MvSmem& sm) {
   using G = GV<FMT>;
+  constexpr int CH = N_DN_CHUNKS;
   constexpr int D = MV_DN_RING<FMT>, NU = MV_DN_UNITS;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 3, b = lane >> 2;
   int c = blockIdx.x;
   if (c >= n) return;
-  Item item = fetch_item(list, c);
+  Item item = fetch_item(a.tiles, base + c, CH);
   ItemTok it = item_tokens(item);
   ChunkW w = chunk_weights<FMT, false>(a, item);
   auto first_row = [&](const Item& itm, const ChunkW& cw) {
@@ -601,7 +605,7 @@ __device__ void down_stream(const LayerArgs& a, const Item* list, int n, MvSmem&
     size_t nr0 = r0;
     MvStage st;
     if (has_next) {
-      nitem = fetch_item(list, nc);
+      nitem = fetch_item(a.tiles, base + nc, CH);
       nit = item_tokens(nitem);
       nw = chunk_weights<FMT, false>(a, nitem);
       nr0 = first_row(nitem, nw);
@@ -839,12 +843,12 @@ __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_up_kernel(LayerAr
   } sm;
   const int n_all = a.ctl[CTL_N_UP], n_mf = a.ctl[CTL_N_UP_MF];
   for (int i = blockIdx.x; i < n_mf; i += gridDim.x) {
-    const Item item = fetch_item(a.items_up, i);
+    const Item item = fetch_item(a.tiles, i, N_UP_CHUNKS);
     const bool sh = item_shared(item.head);
     mfma_up<FMT>(a, sel_qmat(sh, a.sh_gate, a.gate), sel_qmat(sh, a.sh_up, a.up), sh ? 0 : item_expert(item.head),
                  item_tokens(item), item_chunk(item.head) * UP_ROWS, sm.mf);
   }
-  up_stream<FMT>(a, a.items_up + n_mf, n_all - n_mf, sm.gv);
+  up_stream<FMT>(a, n_mf, n_all - n_mf, sm.gv);
 }
 
 template <int FMT>
@@ -855,7 +859,7 @@ __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_down_kernel(Layer
   } sm;
   const int n_all = a.ctl[CTL_N_DN], n_mf = a.ctl[CTL_N_DN_MF];
   for (int i = blockIdx.x; i < n_mf; i += gridDim.x) {
-    const Item item = fetch_item(a.items_dn, i);
+    const Item item = fetch_item(a.tiles, i, N_DN_CHUNKS);
     const bool sh = item_shared(item.head);
     const ItemTok it = item_tokens(item);
     const int r0 = item_chunk(item.head) * DN_ROWS;
@@ -863,7 +867,7 @@ __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_down_kernel(Layer
     for (int rb = 0; rb < DN_ROWS; rb += 128)
       mfma_down<FMT>(a, sel_qmat(sh, a.sh_down, a.down), sh ? 0 : item_expert(item.head), it, r0 + rb, sm.mf);
   }
-  down_stream<FMT>(a, a.items_dn + n_mf, n_all - n_mf, sm.gv);
+  down_stream<FMT>(a, n_mf, n_all - n_mf, sm.gv);
 }
 
 // Workgroups of `kernel` that fit on one CU at once (the persistent kernels are

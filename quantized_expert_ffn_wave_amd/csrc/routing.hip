@@ -30,7 +30,8 @@ constexpr int ROUTER_TG = 256;                  // tokens per workgroup on the l
 // workgroup's 4 waves take 4 consecutive expert tiles.  grid (ceil(T/16) *
 // ceil(E/64), ROUTER_KS).  MFMA 16x16x32 bf16: A = x rows, B = router rows.
 __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __restrict__ x,
-                                                           const uint16_t* __restrict__ wr, float* __restrict__ part,
+                                                           const uint16_t* __restrict__ wr,
+                                                           const float* __restrict__ bias, float* __restrict__ part,
                                                            int T, int E) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int egroups = (E + 63) / 64;
@@ -53,17 +54,19 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
 #pragma unroll
   for (int s = 0; s < ROUTER_KR / 32; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[s], acc, 0, 0, 0);
   // acc[j] = D[row 4*(lane/16)+j][col lane%16]: token t0 + 4*(lane>>4) + j, expert e0 + col
+  const float bz = (ks == 0 && bias) ? bias[e0 + col] : 0.f;  // the bias rides in split 0
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int tt = t0 + 4 * (lane >> 4) + j;
-    if (tt < T) part[((size_t)ks * T + tt) * E + e0 + col] = acc[j];
+    if (tt < T) part[((size_t)ks * T + tt) * E + e0 + col] = acc[j] + bz;
   }
 }
 
 // Large T: a wave keeps its 16 router rows x 256 k in registers and loops over
 // the 16-token tiles of a 256-token group.  grid (ceil(E/64), ROUTER_KS, ceil(T/256)).
 __global__ __launch_bounds__(256) void router_large_kernel(const uint16_t* __restrict__ x,
-                                                           const uint16_t* __restrict__ wr, float* __restrict__ part,
+                                                           const uint16_t* __restrict__ wr,
+                                                           const float* __restrict__ bias, float* __restrict__ part,
                                                            int T, int E) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int e0 = (blockIdx.x * 4 + wave) * 16;
@@ -75,6 +78,7 @@ __global__ __launch_bounds__(256) void router_large_kernel(const uint16_t* __res
   const uint16_t* wrow = wr + (size_t)(e0 + col) * D_MODEL + kbase;
 #pragma unroll
   for (int s = 0; s < ROUTER_KR / 32; ++s) b[s] = *reinterpret_cast<const bf16x8*>(wrow + 32 * s);
+  const float bz = (ks == 0 && bias) ? bias[e0 + col] : 0.f;  // the bias rides in split 0
   const int tg0 = blockIdx.z * ROUTER_TG;
   for (int t0 = tg0; t0 < min(T, tg0 + ROUTER_TG); t0 += 16) {
     const int t = t0 + col;
@@ -88,7 +92,7 @@ __global__ __launch_bounds__(256) void router_large_kernel(const uint16_t* __res
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int tt = t0 + 4 * (lane >> 4) + j;
-      if (tt < T) part[((size_t)ks * T + tt) * E + e0 + col] = acc[j];
+      if (tt < T) part[((size_t)ks * T + tt) * E + e0 + col] = acc[j] + bz;
     }
   }
 }
@@ -96,10 +100,10 @@ __global__ __launch_bounds__(256) void router_large_kernel(const uint16_t* __res
 hipError_t launch_router(const LayerArgs& a, hipStream_t s) {
   if (a.T <= ROUTER_TG) {
     dim3 grid(ceil_div(a.T, 16) * ceil_div(a.E, 64), ROUTER_KS);
-    hipLaunchKernelGGL(router_small_kernel, grid, dim3(256), 0, s, a.x, a.router_w, a.logit_part, a.T, a.E);
+    hipLaunchKernelGGL(router_small_kernel, grid, dim3(256), 0, s, a.x, a.router_w, a.router_b, a.logit_part, a.T, a.E);
   } else {
     dim3 grid(ceil_div(a.E, 64), ROUTER_KS, ceil_div(a.T, ROUTER_TG));
-    hipLaunchKernelGGL(router_large_kernel, grid, dim3(256), 0, s, a.x, a.router_w, a.logit_part, a.T, a.E);
+    hipLaunchKernelGGL(router_large_kernel, grid, dim3(256), 0, s, a.x, a.router_w, a.router_b, a.logit_part, a.T, a.E);
   }
   return hipGetLastError();
 }
@@ -112,11 +116,11 @@ constexpr int BK_THREADS = 1024;
 constexpr int BK_TC = 1024;                 // tokens per bitmask chunk
 constexpr int BK_WORDS = BK_TC / 32;        // mask words per expert
 
-// Selection keys: (order-preserving bits of the logit) << 32 | (0xFFFF - id),
-// so the larger logit wins and equal logits go to the lower id.  NaN logits
-// are ordered as -inf; key 0 marks a taken candidate or a missing expert.
+// Selection key: the order-preserving bits of a logit (NaN ordered as -inf,
+// -0 as +0); equal keys go to the lower expert id.
 __device__ inline uint32_t ordered_bits(float v) {
   if (v != v) v = -INFINITY;
+  if (v == 0.f) v = 0.f;  // -0 and +0 are one value
   const uint32_t b = __float_as_uint(v);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
@@ -138,60 +142,61 @@ template <int M> __device__ inline uint32_t xchg(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, ctrl, 0xF, 0xF, false);
   }
 }
-template <int M> __device__ inline void max_step(uint32_t& hi, uint32_t& lo) {
-  const uint32_t ohi = xchg<M>(hi), olo = xchg<M>(lo);
-  const bool take = (ohi > hi) || (ohi == hi && olo > lo);
-  hi = take ? ohi : hi;
-  lo = take ? olo : lo;
-}
-__device__ inline uint64_t wave_max_key(uint64_t k) {
-  uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
-  max_step<32>(hi, lo);
-  max_step<16>(hi, lo);
-  max_step<8>(hi, lo);
-  max_step<4>(hi, lo);
-  max_step<2>(hi, lo);
-  max_step<1>(hi, lo);
-  return ((uint64_t)hi << 32) | lo;
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, xchg<32>(v));
+  v = max(v, xchg<16>(v));
+  v = max(v, xchg<8>(v));
+  v = max(v, xchg<4>(v));
+  v = max(v, xchg<2>(v));
+  v = max(v, xchg<1>(v));
+  return v;
 }
 
 // One wave: logits of token t (sum of the 8 partials in split order + bias),
 // the top k ids and their weights.
-__device__ void topk_token(const LayerArgs& a, int t) {
+__device__ void topk_token(const LayerArgs& a, int t, int32_t* lds_ids) {
   const int lane = threadIdx.x & 63;
   const int T = a.T, E = a.E, K = a.K;
-  uint64_t key[4];
+  // all 8 x 4 partial sums in flight at once (lanes past E read a valid
+  // entry and are masked below); the bias is already in split 0
+  float p[4][ROUTER_KS];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = min(lane + 64 * i, E - 1);
+#pragma unroll
+    for (int ks = 0; ks < ROUTER_KS; ++ks) p[i][ks] = a.logit_part[((size_t)ks * T + t) * E + e];
+  }
+  uint32_t kk[4];
   float mx = -INFINITY;
   float v[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    key[i] = 0;
+    float s = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < ROUTER_KS; ++ks) s += p[i][ks];
+    kk[i] = 0u;
     v[i] = -INFINITY;
     if (e < E) {
-      float p[ROUTER_KS];
-#pragma unroll
-      for (int ks = 0; ks < ROUTER_KS; ++ks) p[ks] = a.logit_part[((size_t)ks * T + t) * E + e];
-      float s = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < ROUTER_KS; ++ks) s += p[ks];
-      if (a.router_b) s += a.router_b[e];
       if (a.write_logits) a.logits[(size_t)t * E + e] = s;
       v[i] = (s != s) ? -INFINITY : s;
-      key[i] = ((uint64_t)ordered_bits(s) << 32) | (uint64_t)(0xFFFFu - (uint32_t)e);
+      kk[i] = ordered_bits(s);
       mx = fmaxf(mx, v[i]);
     }
   }
   float den_all = 0.f;
   if (!a.renorm) {
-    const uint64_t mk = wave_max_key(((uint64_t)ordered_bits(mx) << 32));
-    mx = from_ordered((uint32_t)(mk >> 32));
+    mx = from_ordered(wave_max_u32(ordered_bits(mx)));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (lane + 64 * i < E) den_all += expf(v[i] - mx);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) den_all += __shfl_xor(den_all, off);
   }
+  // K rounds: the wave-wide maximum of the 32-bit order-preserving keys, then
+  // the lowest expert id holding it (a ballot per group of 64 ids), which is
+  // taken out.  Key 0 marks a taken or missing expert (every logit, -inf and
+  // NaN included, has a larger key).
   float sel_v[MAX_K];
   int sel_e[MAX_K];
 #pragma unroll
@@ -199,16 +204,23 @@ __device__ void topk_token(const LayerArgs& a, int t) {
     sel_v[j] = -INFINITY;
     sel_e[j] = 0;
     if (j >= K) continue;
-    uint64_t best = key[0];
-#pragma unroll
-    for (int i = 1; i < 4; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_key(best);
-    const int e = (int)(0xFFFFu - (uint32_t)(best & 0xFFFFu));
+    const uint32_t m = wave_max_u32(max(max(kk[0], kk[1]), max(kk[2], kk[3])));
+    uint64_t bal = __ballot(kk[0] == m);
+    int e = 0;
+    if (bal) {
+      e = __builtin_ctzll(bal);
+    } else if ((bal = __ballot(kk[1] == m))) {
+      e = 64 + __builtin_ctzll(bal);
+    } else if ((bal = __ballot(kk[2] == m))) {
+      e = 128 + __builtin_ctzll(bal);
+    } else {
+      e = 192 + __builtin_ctzll(__ballot(kk[3] == m));
+    }
     sel_e[j] = e;
-    sel_v[j] = from_ordered((uint32_t)(best >> 32));
+    sel_v[j] = from_ordered(m);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i == e) key[i] = 0;
+      if (lane + 64 * i == e) kk[i] = 0u;
   }
   if (lane < K) {
     float wv;
@@ -228,10 +240,11 @@ __device__ void topk_token(const LayerArgs& a, int t) {
     }
     a.ids[(size_t)t * K + lane] = me;
     a.w[(size_t)t * K + lane] = wv;
+    if (lds_ids) lds_ids[t * K + lane] = me;
   }
 }
 
-// Exclusive scan of v over n <= 320 entries by wave 0 (5 per lane); returns total.
+// Exclusive scan of v over n <= 320 entries by one wave (5 per lane); returns total.
 __device__ int wave0_scan(int* v, int n) {
   const int lane = threadIdx.x & 63;
   int loc[5], sum = 0;
@@ -257,15 +270,99 @@ __device__ int wave0_scan(int* v, int n) {
   return __shfl(inc, 63);
 }
 
+struct ListSmem {
+  int it_m[MAX_E + 2];   // matrix-core tiles per expert, then their exclusive prefix
+  int it_g[MAX_E + 2];   // vector tiles per expert, then their exclusive prefix
+  int tot[2];
+};
+
 struct BucketSmem {
   int cnt[MAX_E + 1];
   int off[MAX_E + 1];
   int base[MAX_E];
   uint32_t mask[MAX_E * BK_WORDS];
-  int it_m[MAX_E + 2];   // MFMA items per expert (up), then prefix
-  int it_g[MAX_E + 2];   // vector items per expert (up), then prefix
-  int tot[2];
+  ListSmem ls;
 };
+
+// Work lists from the bucket sizes cnt[e] and offsets off[e] (in LDS);
+// perm_at(p) gives the slot at bucket position p.
+template <typename PermAt>
+__device__ void write_lists(const LayerArgs& a, const int* bcnt, const int* boff, ListSmem& ls, PermAt perm_at) {
+  const int tid = threadIdx.x, nth = blockDim.x;
+  const int E = a.E, K = a.K, T = a.T;
+  // work list: matrix-core tiles first, then vector tiles.  Gate/up item i is
+  // row chunk i % N_UP_CHUNKS of tile i / N_UP_CHUNKS, down item i chunk
+  // i % N_DN_CHUNKS of tile i / N_DN_CHUNKS.
+  for (int e = tid; e < E; e += nth) {
+    const int m = bcnt[e];
+    const int tiles = bucket_tiles(m);
+    ls.it_m[e] = bucket_mfma(m) ? tiles : 0;
+    ls.it_g[e] = bucket_mfma(m) ? 0 : tiles;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int a0 = wave0_scan(ls.it_m, E);
+    if (tid == 0) ls.it_m[E] = ls.tot[0] = a0;
+  } else if (tid < 128) {
+    const int a1 = wave0_scan(ls.it_g, E);
+    if (tid == 64) ls.it_g[E] = ls.tot[1] = a1;
+  }
+  __syncthreads();
+  const int tiles_m = ls.tot[0], tiles_g = ls.tot[1];
+  // The shared expert takes every token: 64-token matrix-core tiles from
+  // MFMA_MIN tokens on, else groups of GV_GROUP tokens, in the same lists.
+  // Tile order: routed matrix-core, shared matrix-core, routed vector, shared
+  // vector (the kernels take the matrix-core items first).
+  const int sh_tiles = a.n_shared ? bucket_tiles(T) : 0;
+  const bool sh_mf = bucket_mfma(T);
+  const int mf_tiles = tiles_m + (sh_mf ? sh_tiles : 0);
+  const int all_tiles = tiles_m + tiles_g + sh_tiles;
+  const int n_tiles = min(all_tiles, a.max_tiles);
+  const int n_up = n_tiles * N_UP_CHUNKS, n_dn = n_tiles * N_DN_CHUNKS;
+  if (tid == 0) {
+    a.ctl[CTL_N_UP] = n_up;
+    a.ctl[CTL_N_DN] = n_dn;
+    a.ctl[CTL_N_UP_MF] = min(mf_tiles * N_UP_CHUNKS, n_up);
+    a.ctl[CTL_N_DN_MF] = min(mf_tiles * N_DN_CHUNKS, n_dn);
+  }
+  // one thread per token tile: its entry (row chunk 0; the kernels derive the
+  // chunk from the item index)
+  for (int ti = tid; ti < n_tiles; ti += nth) {
+    const bool shared = (ti >= tiles_m && ti < mf_tiles) || ti >= mf_tiles + tiles_g;
+    const bool mf = ti < mf_tiles;
+    const int per = mf ? MFMA_BN : GV_GROUP;
+    int expert, p0, cnt;
+    uint32_t tk[GV_GROUP] = {0u, 0u, 0u, 0u};
+    if (shared) {
+      const int tile = mf ? ti - tiles_m : ti - mf_tiles - tiles_g;
+      expert = SHARED_ID;
+      p0 = tile * per;
+      cnt = min(per, T - p0);
+      for (int j = 0; j < cnt && j < GV_GROUP; ++j) tk[j] = (uint32_t)(p0 + j);
+    } else {
+      const int* o = mf ? ls.it_m : ls.it_g;
+      const int li = mf ? ti : ti - mf_tiles;
+      int lo = 0, hi = E;  // the expert e with o[e] <= li < o[e+1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (o[mid] <= li) lo = mid; else hi = mid;
+      }
+      const int tile = li - o[lo];
+      expert = lo;
+      p0 = boff[lo] + tile * per;
+      cnt = min(per, bcnt[lo] - tile * per);
+      if (!mf) {
+        for (int j = 0; j < cnt; ++j) tk[j] = (uint32_t)(perm_at(p0 + j) / K);
+      }
+    }
+    Item it;
+    it.head = item_head(expert, 0, cnt, mf);
+    it.p0 = (uint32_t)p0;
+    it.t01 = tk[0] | (tk[1] << 16);
+    it.t23 = tk[2] | (tk[3] << 16);
+    a.tiles[ti] = it;
+  }
+}
 
 // Buckets and work lists of the routed experts (one workgroup).
 __device__ void build_buckets(const LayerArgs& a, BucketSmem& sm) {
@@ -316,94 +413,12 @@ __device__ void build_buckets(const LayerArgs& a, BucketSmem& sm) {
     __syncthreads();
   }
 
-  // work lists: matrix-core items first, then vector items.  Both lists use
-  // the same tile order; the down list has N_DN_CHUNKS chunks per tile where
-  // the gate/up list has N_UP_CHUNKS.
-  for (int e = tid; e < E; e += nth) {
-    const int m = sm.cnt[e];
-    const int tiles = bucket_tiles(m);
-    sm.it_m[e] = bucket_mfma(m) ? tiles : 0;
-    sm.it_g[e] = bucket_mfma(m) ? 0 : tiles;
-  }
-  __syncthreads();
-  if (tid < 64) {
-    const int a0 = wave0_scan(sm.it_m, E);
-    const int a1 = wave0_scan(sm.it_g, E);
-    if (tid == 0) {
-      sm.it_m[E] = a0;
-      sm.it_g[E] = a1;
-      sm.tot[0] = a0;
-      sm.tot[1] = a1;
-    }
-  }
-  __syncthreads();
-  const int tiles_m = sm.tot[0], tiles_g = sm.tot[1];
-  // The shared expert takes every token: 64-token matrix-core tiles from
-  // MFMA_MIN tokens on, else groups of GV_GROUP tokens, in the same lists.
-  // Tile order: routed matrix-core, shared matrix-core, routed vector, shared
-  // vector (the kernels take the matrix-core items first).
-  const int sh_tiles = a.n_shared ? bucket_tiles(T) : 0;
-  const bool sh_mf = bucket_mfma(T);
-  const int mf_tiles = tiles_m + (sh_mf ? sh_tiles : 0);
-  const int all_tiles = tiles_m + tiles_g + sh_tiles;
-  const int n_up = min(all_tiles * N_UP_CHUNKS, a.max_items_up - a.max_items_up % N_UP_CHUNKS);
-  const int n_dn = min(all_tiles * N_DN_CHUNKS, a.max_items_dn - a.max_items_dn % N_DN_CHUNKS);
-  if (tid == 0) {
-    a.ctl[CTL_N_UP] = n_up;
-    a.ctl[CTL_N_DN] = n_dn;
-    a.ctl[CTL_N_UP_MF] = min(mf_tiles * N_UP_CHUNKS, n_up);
-    a.ctl[CTL_N_DN_MF] = min(mf_tiles * N_DN_CHUNKS, n_dn);
-  }
-  // one thread per token tile: its N_UP_CHUNKS gate/up items and N_DN_CHUNKS down items
-  const int n_tiles = min(all_tiles, min(a.max_items_up / N_UP_CHUNKS, a.max_items_dn / N_DN_CHUNKS));
-  for (int ti = tid; ti < n_tiles; ti += nth) {
-    const bool shared = (ti >= tiles_m && ti < mf_tiles) || ti >= mf_tiles + tiles_g;
-    const bool mf = ti < mf_tiles;
-    const int per = mf ? MFMA_BN : GV_GROUP;
-    int expert, p0, cnt;
-    uint32_t tk[GV_GROUP] = {0u, 0u, 0u, 0u};
-    if (shared) {
-      const int tile = mf ? ti - tiles_m : ti - mf_tiles - tiles_g;
-      expert = SHARED_ID;
-      p0 = tile * per;
-      cnt = min(per, T - p0);
-      for (int j = 0; j < cnt && j < GV_GROUP; ++j) tk[j] = (uint32_t)(p0 + j);
-    } else {
-      const int* o = mf ? sm.it_m : sm.it_g;
-      const int li = mf ? ti : ti - mf_tiles;
-      int lo = 0, hi = E;  // the expert e with o[e] <= li < o[e+1]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (o[mid] <= li) lo = mid; else hi = mid;
-      }
-      const int tile = li - o[lo];
-      expert = lo;
-      p0 = sm.off[lo] + tile * per;
-      cnt = min(per, sm.cnt[lo] - tile * per);
-      if (!mf) {
-        for (int j = 0; j < cnt; ++j) tk[j] = (uint32_t)(a.perm[p0 + j] / K);
-      }
-    }
-    Item it;
-    it.p0 = (uint32_t)p0;
-    it.t01 = tk[0] | (tk[1] << 16);
-    it.t23 = tk[2] | (tk[3] << 16);
-#pragma unroll
-    for (int c = 0; c < N_UP_CHUNKS; ++c) {
-      it.head = item_head(expert, c, cnt, mf);
-      a.items_up[ti * N_UP_CHUNKS + c] = it;
-    }
-#pragma unroll
-    for (int c = 0; c < N_DN_CHUNKS; ++c) {
-      it.head = item_head(expert, c, cnt, mf);
-      a.items_dn[ti * N_DN_CHUNKS + c] = it;
-    }
-  }
+  write_lists(a, sm.cnt, sm.off, sm.ls, [&](int p) { return a.perm[p]; });
 }
 
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayerArgs a) {
   const int t = blockIdx.x * (TK_THREADS / 64) + (threadIdx.x >> 6);
-  if (t < a.T) topk_token(a, t);
+  if (t < a.T) topk_token(a, t, nullptr);
 }
 
 __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(LayerArgs a) {
@@ -411,13 +426,85 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(LayerArgs a) {
   build_buckets(a, sm);
 }
 
+// ---------------------------------------------------------------------------------------
+// Decode-sized batches (T <= RS_MAX_T): buckets and work lists in one
+// workgroup with the ids, token masks and the permutation in LDS.  Up to
+// RS_FUSED_T tokens (one per wave) the same workgroup also runs the top-k.
+// ---------------------------------------------------------------------------------------
+constexpr int RS_THREADS = 1024;
+constexpr int RS_MAX_T = 256;
+constexpr int RS_FUSED_T = RS_THREADS / 64;
+constexpr int RS_WORDS = RS_MAX_T / 32;
+
+struct RouteSmallSmem {
+  int32_t ids[RS_MAX_T * MAX_K];
+  int32_t perm[RS_MAX_T * MAX_K];
+  uint32_t mask[MAX_E * RS_WORDS];
+  int cnt[MAX_E + 1];
+  int off[MAX_E + 1];
+  ListSmem ls;
+};
+
+template <bool TOPK>
+__global__ __launch_bounds__(RS_THREADS) void route_small_kernel(LayerArgs a) {
+  __shared__ RouteSmallSmem sm;
+  const int tid = threadIdx.x, nth = blockDim.x, wave = tid >> 6;
+  const int E = a.E, K = a.K, T = a.T, S = a.S;
+  const int W = ceil_div(T, 32);
+  if (TOPK) {  // one wave per token
+    for (int t = wave; t < T; t += RS_THREADS / 64) topk_token(a, t, sm.ids);
+  } else {
+    for (int s = tid; s < S; s += nth) sm.ids[s] = a.ids[s];
+  }
+  for (int i = tid; i < E * W; i += nth) sm.mask[i] = 0u;
+  __syncthreads();
+  // per-expert token masks (a token holds at most one slot of an expert)
+  for (int s = tid; s < S; s += nth) {
+    const int t = s / K;
+    atomicOr(&sm.mask[sm.ids[s] * W + (t >> 5)], 1u << (t & 31));
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += nth) {
+    int c = 0;
+    for (int w = 0; w < W; ++w) c += __popc(sm.mask[e * W + w]);
+    sm.cnt[e] = sm.off[e] = c;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int total = wave0_scan(sm.off, E);
+    if (tid == 0) sm.off[E] = total;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += nth) a.counts[e] = sm.cnt[e];
+  for (int e = tid; e <= E; e += nth) a.offsets[e] = sm.off[e];
+  // stable permutation: a slot's rank in its bucket = tokens of that expert before it
+  for (int s = tid; s < S; s += nth) {
+    const int e = sm.ids[s], t = s / K;
+    const uint32_t* me = sm.mask + e * W;
+    int r = 0;
+    for (int w = 0; w < (t >> 5); ++w) r += __popc(me[w]);
+    r += __popc(me[t >> 5] & ((1u << (t & 31)) - 1u));
+    const int pos = sm.off[e] + r;
+    sm.perm[pos] = s;
+    a.perm[pos] = s;
+    a.inv_perm[s] = pos;
+  }
+  __syncthreads();
+  write_lists(a, sm.cnt, sm.off, sm.ls, [&](int p) { return sm.perm[p]; });
+}
+
+// top-k (with the buckets too, for up to RS_FUSED_T tokens)
 hipError_t launch_topk(const LayerArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3(ceil_div(a.T, TK_THREADS / 64)), dim3(TK_THREADS), 0, s, a);
+  if (a.T <= RS_FUSED_T) hipLaunchKernelGGL(route_small_kernel<true>, dim3(1), dim3(RS_THREADS), 0, s, a);
+  else hipLaunchKernelGGL(topk_kernel, dim3(ceil_div(a.T, TK_THREADS / 64)), dim3(TK_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
+// buckets and work lists (done by the top-k launch for up to RS_FUSED_T tokens)
 hipError_t launch_bucket(const LayerArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(BK_THREADS), 0, s, a);
+  if (a.T <= RS_FUSED_T) return hipSuccess;
+  if (a.T <= RS_MAX_T) hipLaunchKernelGGL(route_small_kernel<false>, dim3(1), dim3(RS_THREADS), 0, s, a);
+  else hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(BK_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
