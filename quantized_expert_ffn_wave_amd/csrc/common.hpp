@@ -23,9 +23,9 @@ constexpr int GV_GROUP = 4;
 constexpr int MFMA_MIN = 65;
 constexpr int MFMA_BN = 64;
 constexpr int UP_ROWS = 64;
-constexpr int DN_ROWS = 128;
+constexpr int DN_ROWS = 256;
 constexpr int N_UP_CHUNKS = D_FF / UP_ROWS;      // 8
-constexpr int N_DN_CHUNKS = D_MODEL / DN_ROWS;   // 16
+constexpr int N_DN_CHUNKS = D_MODEL / DN_ROWS;   // 8
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // token groups/tiles of a bucket of m tokens

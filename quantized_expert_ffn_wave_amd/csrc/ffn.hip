@@ -262,7 +262,7 @@ template <int FMT> __device__ inline f32x4 mfma4(uint32_t a0, uint32_t a1, uint3
 template <int FMT> constexpr int MV_UP_RING = (FMT == FMT_BF16) ? 4 : 8;  // weight loads in flight per wave
 template <int FMT> constexpr int MV_DN_RING = (FMT == FMT_BF16) ? 4 : 8;
 constexpr int MV_UP_UNITS = 32;            // loads per wave per gate/up chunk: 4 row groups x 4 K-quarters x 2 matrices
-constexpr int MV_DN_UNITS = DN_ROWS / 16;  // loads per wave per down chunk: 8 row groups (K = 512 in one load)
+constexpr int MV_DN_UNITS = DN_ROWS / 16;  // loads per wave per down chunk: one per 4-row group (K = 512 in one load)
 constexpr int MV_CHUNKS = D_MODEL / 32;    // 32-element chunks of the longest reduction
 constexpr int MV_TOKW = MV_CHUNKS * 16 + 4;  // dwords per token in LDS (16 B of padding against bank conflicts)
 
