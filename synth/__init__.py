@@ -253,10 +253,25 @@ CONFIGS = {
 }
 
 
-def make_workload(name: str, layers: int | None = None):
+def make_workload(name: str, layers: int | None = None, workers: int = 1, progress=None):
     """(list of Layer, x) for a named workload.  Layer l of a stack is drawn
-    from seed l; activations from seed 0.  `layers` truncates a stack."""
+    from seed l; activations from seed 0.  `layers` truncates a stack.
+    `workers` > 1 draws layers on threads (the C encoders release the GIL);
+    `progress(l)` is called as layer l is ready.  The result does not depend
+    on either."""
     c = CONFIGS[name]
     nl = c["layers"] if layers is None else layers
-    Ls = [make_layer(seed=l, fmt=c["fmt"], zipf=c["zipf"]) for l in range(nl)]
+
+    def one(l):
+        L = make_layer(seed=l, fmt=c["fmt"], zipf=c["zipf"])
+        if progress is not None:
+            progress(l)
+        return L
+
+    if workers > 1 and nl > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            Ls = list(ex.map(one, range(nl)))
+    else:
+        Ls = [one(l) for l in range(nl)]
     return Ls, make_x(c["T"])

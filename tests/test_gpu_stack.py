@@ -112,7 +112,8 @@ def test_stack_2_layers_nvfp4_and_bf16():
 def test_stack47_decode_t32_q4_1_zipf():
     """The 47-layer stack at its full size: ~23.7 GB of q4_1 experts resident."""
     say("case stack47_decode_t32_q4_1_zipf0.8: generating 47 layers")
-    layers, x = synth.make_workload("stack47_decode_t32_q4_1_zipf0.8")
+    layers, x = synth.make_workload("stack47_decode_t32_q4_1_zipf0.8", workers=16,
+                                    progress=lambda l: say(f"  layer {l} ready"))
     say("  running the stack on the GPU")
     out, rec = run_stack(layers, x)
     say("  teacher-forced check, every layer")
