@@ -650,9 +650,12 @@ __device__ void down_stream(const LayerArgs& a, int base, int n, MvSmem& sm) {
 // ======================================================================================
 constexpr int TS = 72;  // LDS row stride in 16-bit elements (64 + 8 pad)
 
-struct FfnSmem {
+struct FfnBuf {
   uint16_t w[128 * TS];
   uint16_t x[MFMA_BN * TS];
+};
+struct FfnSmem {
+  FfnBuf buf[2];  // K-chunks alternate between the two, so one barrier per chunk suffices
   int tok[MFMA_BN];
   int row[MFMA_BN];
 };
@@ -715,7 +718,7 @@ __device__ inline void mfma_fetch(MfmaStage<FMT>& st, const QMat& wq, size_t wro
 }
 
 template <int FMT>
-__device__ inline void mfma_stage_store(const MfmaStage<FMT>& st, FfnSmem& sm, int wr_row, int wr_half, int xt, int xs,
+__device__ inline void mfma_stage_store(const MfmaStage<FMT>& st, FfnBuf& sm, int wr_row, int wr_half, int xt, int xs,
                                         bool x_bf16) {
   uint32_t wv[16];
   GV<FMT>::decode(st.w, wv);
@@ -730,30 +733,46 @@ __device__ inline void mfma_stage_store(const MfmaStage<FMT>& st, FfnSmem& sm, i
   stage_x16<FMT>(sm.x + xt * TS + 16 * xs, xv);
 }
 
-// acc[tt] += W_tile(rows arow..) x X_tile(tokens 32tt..) over K = kdim.
-// wq/wrow: this thread's weight row; xrow_ptr: this thread's activation row (or null).
+// acc[tt] += W_tile(rows arow..) x X_tile(tokens 32tt..) of one K-chunk in LDS.
+template <int FMT>
+__device__ inline void mfma_chunk(f32x16* acc, const FfnBuf& sm, int arow) {
+  const int lane = threadIdx.x & 63;
+  const int ar = lane & 31, kh = 8 * (lane >> 5);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint16_t* ap = sm.w + arow * TS + 16 * s + kh;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) acc[tt] = mfma32<FMT>(ap, sm.x + (32 * tt + ar) * TS + 16 * s + kh, acc[tt]);
+  }
+}
+
+// acc[tt] += W_tile x X_tile over K = kdim (a multiple of 128), 64 at a time.
+// wq/wrow: this thread's weight row; xrow_ptr: this thread's activation row (or
+// null).  Two K-chunks are loaded ahead into registers; even chunks are staged
+// in LDS buffer 0 and odd ones in buffer 1, so the barrier after a chunk's
+// stores also tells that every wave is done with the chunk before it.
 template <int FMT>
 __device__ inline void mfma_kloop(f32x16* acc, FfnSmem& sm, const QMat& wq, size_t wrow, const uint16_t* xrow_ptr,
                                   bool x_bf16, int kdim, int arow) {
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int wr_row = tid >> 1, wr_half = tid & 1;
   const int xt = tid >> 2, xs = tid & 3;
-  const int ar = lane & 31, kh = 8 * (lane >> 5);
-  MfmaStage<FMT> st;
-  mfma_fetch<FMT>(st, wq, wrow, 32 * wr_half, xrow_ptr ? xrow_ptr + 16 * xs : nullptr, kdim);
+  auto fetch = [&](MfmaStage<FMT>& st, int kc) {
+    mfma_fetch<FMT>(st, wq, wrow, kc + 32 * wr_half, xrow_ptr ? xrow_ptr + kc + 16 * xs : nullptr, kdim);
+  };
+  MfmaStage<FMT> st0, st1;
+  fetch(st0, 0);
+  fetch(st1, 64);
 #pragma unroll 1
-  for (int kc = 0; kc < kdim; kc += 64) {
-    __syncthreads();  // the previous chunk's MFMAs are done with the tiles
-    mfma_stage_store<FMT>(st, sm, wr_row, wr_half, xt, xs, x_bf16);
+  for (int kc = 0; kc < kdim; kc += 128) {
+    mfma_stage_store<FMT>(st0, sm.buf[0], wr_row, wr_half, xt, xs, x_bf16);
     __syncthreads();
-    if (kc + 64 < kdim)
-      mfma_fetch<FMT>(st, wq, wrow, kc + 64 + 32 * wr_half, xrow_ptr ? xrow_ptr + kc + 64 + 16 * xs : nullptr, kdim);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint16_t* ap = sm.w + arow * TS + 16 * s + kh;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) acc[tt] = mfma32<FMT>(ap, sm.x + (32 * tt + ar) * TS + 16 * s + kh, acc[tt]);
-    }
+    if (kc + 128 < kdim) fetch(st0, kc + 128);
+    mfma_chunk<FMT>(acc, sm.buf[0], arow);
+    mfma_stage_store<FMT>(st1, sm.buf[1], wr_row, wr_half, xt, xs, x_bf16);
+    __syncthreads();
+    if (kc + 192 < kdim) fetch(st1, kc + 192);
+    mfma_chunk<FMT>(acc, sm.buf[1], arow);
   }
 }
 
@@ -834,38 +853,50 @@ __device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const Item
 // formats (their rings fit in half the register file), one for bf16.
 template <int FMT> constexpr int FFN_WG_PER_CU = (FMT == FMT_BF16) ? 1 : 2;
 
-// Items of the matrix-core path come first; the vector-path chunks follow.
-template <int FMT>
-__global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_up_kernel(LayerArgs a) {
-  __shared__ union {
+// LDS of the persistent kernels: the matrix-core tiles only where the batch
+// can have them (MF: T >= MFMA_MIN), since their double buffer would otherwise
+// cost the vector path occupancy.
+template <bool MF> struct FfnKernelSmem;
+template <> struct FfnKernelSmem<true> {
+  union {
     FfnSmem mf;
     MvSmem gv;
-  } sm;
+  };
+};
+template <> struct FfnKernelSmem<false> {
+  MvSmem gv;
+};
+
+// Items of the matrix-core path come first; the vector-path chunks follow.
+template <int FMT, bool MF>
+__global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_up_kernel(LayerArgs a) {
+  __shared__ FfnKernelSmem<MF> sm;
   const int n_all = a.ctl[CTL_N_UP], n_mf = a.ctl[CTL_N_UP_MF];
-  for (int i = blockIdx.x; i < n_mf; i += gridDim.x) {
-    const Item item = fetch_item(a.tiles, i, N_UP_CHUNKS);
-    const bool sh = item_shared(item.head);
-    mfma_up<FMT>(a, sel_qmat(sh, a.sh_gate, a.gate), sel_qmat(sh, a.sh_up, a.up), sh ? 0 : item_expert(item.head),
-                 item_tokens(item), item_chunk(item.head) * UP_ROWS, sm.mf);
+  if constexpr (MF) {
+    for (int i = blockIdx.x; i < n_mf; i += gridDim.x) {
+      const Item item = fetch_item(a.tiles, i, N_UP_CHUNKS);
+      const bool sh = item_shared(item.head);
+      mfma_up<FMT>(a, sel_qmat(sh, a.sh_gate, a.gate), sel_qmat(sh, a.sh_up, a.up), sh ? 0 : item_expert(item.head),
+                   item_tokens(item), item_chunk(item.head) * UP_ROWS, sm.mf);
+    }
   }
   up_stream<FMT>(a, n_mf, n_all - n_mf, sm.gv);
 }
 
-template <int FMT>
+template <int FMT, bool MF>
 __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_down_kernel(LayerArgs a) {
-  __shared__ union {
-    FfnSmem mf;
-    MvSmem gv;
-  } sm;
+  __shared__ FfnKernelSmem<MF> sm;
   const int n_all = a.ctl[CTL_N_DN], n_mf = a.ctl[CTL_N_DN_MF];
-  for (int i = blockIdx.x; i < n_mf; i += gridDim.x) {
-    const Item item = fetch_item(a.tiles, i, N_DN_CHUNKS);
-    const bool sh = item_shared(item.head);
-    const ItemTok it = item_tokens(item);
-    const int r0 = item_chunk(item.head) * DN_ROWS;
+  if constexpr (MF) {
+    for (int i = blockIdx.x; i < n_mf; i += gridDim.x) {
+      const Item item = fetch_item(a.tiles, i, N_DN_CHUNKS);
+      const bool sh = item_shared(item.head);
+      const ItemTok it = item_tokens(item);
+      const int r0 = item_chunk(item.head) * DN_ROWS;
 #pragma unroll 1
-    for (int rb = 0; rb < DN_ROWS; rb += 128)
-      mfma_down<FMT>(a, sel_qmat(sh, a.sh_down, a.down), sh ? 0 : item_expert(item.head), it, r0 + rb, sm.mf);
+      for (int rb = 0; rb < DN_ROWS; rb += 128)
+        mfma_down<FMT>(a, sel_qmat(sh, a.sh_down, a.down), sh ? 0 : item_expert(item.head), it, r0 + rb, sm.mf);
+    }
   }
   down_stream<FMT>(a, n_mf, n_all - n_mf, sm.gv);
 }
@@ -879,16 +910,24 @@ int resident_per_cu(Kern kernel) {
   return n;
 }
 
-template <int FMT>
-hipError_t launch_ffn_fmt(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s) {
-  static const int occ_up = resident_per_cu(ffn_up_kernel<FMT>);
-  static const int occ_dn = resident_per_cu(ffn_down_kernel<FMT>);
+template <int FMT, bool MF>
+hipError_t launch_ffn_var(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s) {
+  static const int occ_up = resident_per_cu(ffn_up_kernel<FMT, MF>);
+  static const int occ_dn = resident_per_cu(ffn_down_kernel<FMT, MF>);
   int grid = n_cu * (up ? occ_up : occ_dn);
   if (max_wgs < grid) grid = max_wgs;
   if (grid < 1) return hipSuccess;
-  if (up) hipLaunchKernelGGL((ffn_up_kernel<FMT>), dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((ffn_down_kernel<FMT>), dim3(grid), dim3(256), 0, s, a);
+  if (up) hipLaunchKernelGGL((ffn_up_kernel<FMT, MF>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((ffn_down_kernel<FMT, MF>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+// Matrix-core tiles exist only for buckets (or the shared expert) of
+// MFMA_MIN or more tokens, so below that the leaner kernel runs.
+template <int FMT>
+hipError_t launch_ffn_fmt(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s) {
+  return bucket_mfma(a.T) ? launch_ffn_var<FMT, true>(a, up, n_cu, max_wgs, s)
+                          : launch_ffn_var<FMT, false>(a, up, n_cu, max_wgs, s);
 }
 
 hipError_t launch_ffn(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s) {
