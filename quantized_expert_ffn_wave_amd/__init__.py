@@ -53,6 +53,13 @@ class moe_route_out(ctypes.Structure):
                 ("x_in", ctypes.c_void_p), ("y_out", ctypes.c_void_p)]
 
 
+# torch is imported before the library is loaded so that one HIP runtime serves
+# the process: torch brings its own libamdhip64 (soname libamdhip64.so.7), which
+# then satisfies this library's dependency.  Loaded the other way round, the
+# library would pull in the system runtime and torch a second one beside it,
+# and the library's runtime then finds no device.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 _vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
 _lib.moe_layer_create.argtypes = [ctypes.POINTER(moe_layer_desc), ctypes.POINTER(moe_layer_weights),

@@ -263,6 +263,10 @@ template <int FMT> constexpr int MV_UP_RING = (FMT == FMT_BF16) ? 4 : 8;  // wei
 template <int FMT> constexpr int MV_DN_RING = (FMT == FMT_BF16) ? 4 : 8;
 constexpr int MV_UP_UNITS = 32;            // loads per wave per gate/up chunk: 4 row groups x 4 K-quarters x 2 matrices
 constexpr int MV_DN_UNITS = DN_ROWS / 16;  // loads per wave per down chunk: one per 4-row group (K = 512 in one load)
+// The ring carries loads across chunks in place: the next chunk's load i is
+// issued into the slot its predecessor load NU - D + i vacates, so D must divide NU.
+static_assert(MV_UP_UNITS % MV_UP_RING<FMT_Q4_1> == 0 && MV_UP_UNITS % MV_UP_RING<FMT_BF16> == 0, "ring");
+static_assert(MV_DN_UNITS % MV_DN_RING<FMT_Q4_1> == 0 && MV_DN_UNITS % MV_DN_RING<FMT_BF16> == 0, "ring");
 constexpr int MV_CHUNKS = D_MODEL / 32;    // 32-element chunks of the longest reduction
 constexpr int MV_TOKW = MV_CHUNKS * 16 + 4;  // dwords per token in LDS (16 B of padding against bank conflicts)
 

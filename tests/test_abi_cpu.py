@@ -116,3 +116,23 @@ def test_forward_argument_errors_without_a_layer():
     assert lib.moe_stack_forward(None, 0, None, 4, 1e-6, None, None, 0, None) == moe.MOE_ERR_INVALID_ARG
     lib.moe_layer_destroy(None)  # NULL-safe
     assert moe.version().startswith("moe_ffn gfx950")
+
+
+def test_one_hip_runtime_per_process():
+    """Importing the binding alone leaves one libamdhip64 mapped (torch's), so
+    that the library and torch share a runtime whatever is imported first."""
+    import subprocess
+    import sys
+    code = ("import quantized_expert_ffn_wave_amd\n"
+            "paths = set()\n"
+            "for line in open('/proc/self/maps'):\n"
+            "    p = line.split()[-1]\n"
+            "    if 'libamdhip64' in p:\n"
+            "        paths.add(os.path.realpath(p))\n"
+            "print(len(paths), sorted(paths))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", "import os\n" + code], cwd=root, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr
+    n = int(r.stdout.split()[0])
+    assert n == 1, r.stdout
