@@ -10,11 +10,13 @@
 // Kernel boundaries order the steps (no device-scope fences):
 //   router        partial logits part[ks][t][e] over 8 K-splits (MFMA 16x16x32 bf16);
 //   topk          one wave per token sums the 8 partials in split order, selects
-//                 the top k (ties to the lower id, wave-wide maximum of 64-bit
-//                 keys with permlane swaps and DPP) and writes the weights;
-//   bucket        one workgroup: histogram, exclusive prefix sum, a stable slot
-//                 permutation from per-expert token bitmasks and popcounts, its
-//                 inverse, and the FFN work lists.
+//                 the top k (ties to the lower id: wave-wide maxima of 32-bit
+//                 order-preserving keys with permlane swaps and DPP, then a
+//                 ballot) and writes the weights;
+//   bucket        histogram, exclusive prefix sum, a stable slot permutation from
+//                 per-expert token bitmasks and popcounts, its inverse, and the
+//                 FFN work lists: one workgroup up to 256 tokens, else three
+//                 launches over 256-token chunks.
 #include "common.hpp"
 
 namespace moe {
@@ -113,8 +115,6 @@ hipError_t launch_router(const LayerArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------------------
 constexpr int TK_THREADS = 256;             // 4 waves: 4 tokens per workgroup
 constexpr int BK_THREADS = 1024;
-constexpr int BK_TC = 1024;                 // tokens per bitmask chunk
-constexpr int BK_WORDS = BK_TC / 32;        // mask words per expert
 
 // Selection key: the order-preserving bits of a logit (NaN ordered as -inf,
 // -0 as +0); equal keys go to the lower expert id.
@@ -276,13 +276,6 @@ struct ListSmem {
   int tot[2];
 };
 
-struct BucketSmem {
-  int cnt[MAX_E + 1];
-  int off[MAX_E + 1];
-  int base[MAX_E];
-  uint32_t mask[MAX_E * BK_WORDS];
-  ListSmem ls;
-};
 
 // Work lists from the bucket sizes cnt[e] and offsets off[e] (in LDS);
 // perm_at(p) gives the slot at bucket position p.
@@ -364,66 +357,113 @@ __device__ void write_lists(const LayerArgs& a, const int* bcnt, const int* boff
   }
 }
 
-// Buckets and work lists of the routed experts (one workgroup).
-__device__ void build_buckets(const LayerArgs& a, BucketSmem& sm) {
-  const int tid = threadIdx.x, nth = blockDim.x;
-  const int E = a.E, K = a.K, T = a.T, S = a.S;
-  const int32_t* ids = a.ids;
-
-  for (int e = tid; e < E; e += nth) { sm.cnt[e] = 0; sm.base[e] = 0; }
-  __syncthreads();
-  for (int s = tid; s < S; s += nth) atomicAdd(&sm.cnt[ids[s]], 1);
-  __syncthreads();
-  for (int e = tid; e < E; e += nth) sm.off[e] = sm.cnt[e];
-  __syncthreads();
-  if (tid < 64) {
-    const int total = wave0_scan(sm.off, E);
-    if (tid == 0) sm.off[E] = total;
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += nth) a.counts[e] = sm.cnt[e];
-  for (int e = tid; e <= E; e += nth) a.offsets[e] = sm.off[e];
-
-  for (int t0 = 0; t0 < T; t0 += BK_TC) {
-    const int words = min(BK_WORDS, ceil_div(T - t0, 32));
-    for (int i = tid; i < E * words; i += nth) sm.mask[(i / words) * BK_WORDS + i % words] = 0u;
-    __syncthreads();
-    const int s0 = t0 * K, s1 = min(T, t0 + BK_TC) * K;
-    for (int s = s0 + tid; s < s1; s += nth) {
-      const int tt = s / K - t0;
-      atomicOr(&sm.mask[ids[s] * BK_WORDS + (tt >> 5)], 1u << (tt & 31));
-    }
-    __syncthreads();
-    for (int s = s0 + tid; s < s1; s += nth) {
-      const int e = ids[s], tt = s / K - t0;
-      const uint32_t* me = sm.mask + e * BK_WORDS;
-      int r = sm.base[e];
-      for (int wd = 0; wd < (tt >> 5); ++wd) r += __popc(me[wd]);
-      r += __popc(me[tt >> 5] & ((1u << (tt & 31)) - 1u));
-      const int pos = sm.off[e] + r;
-      a.perm[pos] = s;
-      a.inv_perm[s] = pos;
-    }
-    __syncthreads();
-    for (int e = tid; e < E; e += nth) {
-      int c = 0;
-      for (int wd = 0; wd < words; ++wd) c += __popc(sm.mask[e * BK_WORDS + wd]);
-      sm.base[e] += c;
-    }
-    __syncthreads();
-  }
-
-  write_lists(a, sm.cnt, sm.off, sm.ls, [&](int p) { return a.perm[p]; });
-}
-
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayerArgs a) {
   const int t = blockIdx.x * (TK_THREADS / 64) + (threadIdx.x >> 6);
   if (t < a.T) topk_token(a, t, nullptr);
 }
 
-__global__ __launch_bounds__(BK_THREADS) void bucket_kernel(LayerArgs a) {
-  __shared__ BucketSmem sm;
-  build_buckets(a, sm);
+// ---------------------------------------------------------------------------------------
+// Large batches (T > RS_MAX_T): buckets in chunks of BK_CT tokens, three launches.
+//   chunk_hist   one workgroup per chunk: slots per expert in the chunk;
+//   chunk_scan   one workgroup: bucket sizes and offsets, each chunk's first
+//                position in every bucket, and the work lists (vector-path
+//                items without their token ids);
+//   chunk_perm   one workgroup per chunk: a slot's rank among the chunk's slots
+//                of its expert (token bitmasks and popcounts), hence its bucket
+//                position, the permutation and its inverse, and the token ids of
+//                the vector-path items.
+// The partial-logit region, consumed by the top-k, holds the chunk table
+// base[chunk][e] and, after it, each expert's first vector-path tile (or -1).
+// ---------------------------------------------------------------------------------------
+constexpr int BK_CT = 256;
+constexpr int BK_CW = BK_CT / 32;
+
+__device__ inline int32_t* chunk_table(const LayerArgs& a) { return reinterpret_cast<int32_t*>(a.logit_part); }
+
+__global__ __launch_bounds__(BK_THREADS) void chunk_hist_kernel(LayerArgs a) {
+  __shared__ int cnt[MAX_E];
+  const int tid = threadIdx.x, E = a.E, K = a.K;
+  const int t0 = blockIdx.x * BK_CT, t1 = min(a.T, t0 + BK_CT);
+  for (int e = tid; e < E; e += BK_THREADS) cnt[e] = 0;
+  __syncthreads();
+  for (int s = t0 * K + tid; s < t1 * K; s += BK_THREADS) atomicAdd(&cnt[a.ids[s]], 1);
+  __syncthreads();
+  int32_t* base = chunk_table(a) + (size_t)blockIdx.x * E;
+  for (int e = tid; e < E; e += BK_THREADS) base[e] = cnt[e];
+}
+
+__global__ __launch_bounds__(BK_THREADS) void chunk_scan_kernel(LayerArgs a) {
+  __shared__ int cnt[MAX_E + 1];
+  __shared__ int off[MAX_E + 1];
+  __shared__ ListSmem ls;
+  const int tid = threadIdx.x, E = a.E;
+  const int nch = ceil_div(a.T, BK_CT);
+  int32_t* tab = chunk_table(a);
+  // per expert: exclusive running sum over the chunks (in place), then the total
+  for (int e = tid; e < E; e += BK_THREADS) {
+    int run = 0;
+    for (int c0 = 0; c0 < nch; c0 += 8) {
+      int h[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = (c0 + i < nch) ? tab[(size_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (c0 + i < nch) tab[(size_t)(c0 + i) * E + e] = run;
+        run += h[i];
+      }
+    }
+    cnt[e] = off[e] = run;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int total = wave0_scan(off, E);
+    if (tid == 0) off[E] = total;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += BK_THREADS) a.counts[e] = cnt[e];
+  for (int e = tid; e <= E; e += BK_THREADS) a.offsets[e] = off[e];
+  for (int i = tid; i < nch * E; i += BK_THREADS) tab[i] += off[i % E];
+  write_lists(a, cnt, off, ls, [](int) { return 0; });
+  // first vector-path tile of each expert (tile order: routed matrix-core,
+  // shared matrix-core, routed vector, shared vector)
+  const int sh_mf = (a.n_shared && bucket_mfma(a.T)) ? bucket_tiles(a.T) : 0;
+  int32_t* vt = tab + (size_t)nch * E;
+  for (int e = tid; e < E; e += BK_THREADS) vt[e] = bucket_mfma(cnt[e]) ? -1 : ls.tot[0] + sh_mf + ls.it_g[e];
+}
+
+__global__ __launch_bounds__(BK_THREADS) void chunk_perm_kernel(LayerArgs a) {
+  __shared__ int32_t ids[BK_CT * MAX_K];
+  __shared__ uint32_t mask[MAX_E * BK_CW];
+  const int tid = threadIdx.x, E = a.E, K = a.K;
+  const int t0 = blockIdx.x * BK_CT, t1 = min(a.T, t0 + BK_CT);
+  const int s0 = t0 * K, ns = (t1 - t0) * K;
+  const int nch = ceil_div(a.T, BK_CT);
+  const int32_t* base = chunk_table(a) + (size_t)blockIdx.x * E;
+  const int32_t* vt = chunk_table(a) + (size_t)nch * E;
+  const int n_tiles = a.ctl[CTL_N_UP] / N_UP_CHUNKS;
+  for (int i = tid; i < ns; i += BK_THREADS) ids[i] = a.ids[s0 + i];
+  for (int i = tid; i < E * BK_CW; i += BK_THREADS) mask[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < ns; i += BK_THREADS) {
+    const int tt = i / K;
+    atomicOr(&mask[ids[i] * BK_CW + (tt >> 5)], 1u << (tt & 31));
+  }
+  __syncthreads();
+  for (int i = tid; i < ns; i += BK_THREADS) {
+    const int e = ids[i], tt = i / K;
+    const uint32_t* me = mask + e * BK_CW;
+    int r = 0;
+    for (int w = 0; w < (tt >> 5); ++w) r += __popc(me[w]);
+    r += __popc(me[tt >> 5] & ((1u << (tt & 31)) - 1u));
+    const int pos = base[e] + r;
+    a.perm[pos] = s0 + i;
+    a.inv_perm[s0 + i] = pos;
+    if (vt[e] >= 0) {  // a vector-path bucket: the token's id goes into its item
+      const int g = pos - a.offsets[e];
+      const int ti = vt[e] + g / GV_GROUP;
+      if (ti < n_tiles) reinterpret_cast<uint16_t*>(a.tiles + ti)[4 + g % GV_GROUP] = (uint16_t)(t0 + tt);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -503,8 +543,14 @@ hipError_t launch_topk(const LayerArgs& a, hipStream_t s) {
 // buckets and work lists (done by the top-k launch for up to RS_FUSED_T tokens)
 hipError_t launch_bucket(const LayerArgs& a, hipStream_t s) {
   if (a.T <= RS_FUSED_T) return hipSuccess;
-  if (a.T <= RS_MAX_T) hipLaunchKernelGGL(route_small_kernel<false>, dim3(1), dim3(RS_THREADS), 0, s, a);
-  else hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(BK_THREADS), 0, s, a);
+  if (a.T <= RS_MAX_T) {
+    hipLaunchKernelGGL(route_small_kernel<false>, dim3(1), dim3(RS_THREADS), 0, s, a);
+    return hipGetLastError();
+  }
+  const int nch = ceil_div(a.T, BK_CT);
+  hipLaunchKernelGGL(chunk_hist_kernel, dim3(nch), dim3(BK_THREADS), 0, s, a);
+  hipLaunchKernelGGL(chunk_scan_kernel, dim3(1), dim3(BK_THREADS), 0, s, a);
+  hipLaunchKernelGGL(chunk_perm_kernel, dim3(nch), dim3(BK_THREADS), 0, s, a);
   return hipGetLastError();
 }
 

@@ -111,8 +111,7 @@ def test_layer_options(E, k, n_shared, renorm, scale, fmt, T):
 
 def test_small_and_large_bucket_boundary():
     """With 16 experts and top-6, token counts 8..14 give buckets of every size
-    around the switch between the vector path (<= 4 tokens) and the matrix
-    path (>= 5 tokens)."""
+    around the vector path's 4-token groups (one group, then two)."""
     host = synth.make_layer(seed=3, fmt="q4_1", E=16, k=6)
     dl = moe.DeviceLayer(host, max_tokens=64)
     seen = set()
@@ -187,3 +186,27 @@ def test_staged_forward_matches_plain_forward(q4_layer):
     with pytest.raises(moe.MoeError):
         moe.moe_layer_forward_staged(dl.handle, x.data_ptr(), 64, y1.data_ptr(), None, ws.data_ptr(), ws.numel(),
                                      moe.current_stream(), [e.cuda_event for e in ev[:3]])
+
+
+def test_matrix_core_bucket_boundary():
+    """16 experts, top-6, 168..180 tokens: buckets on both sides of the switch
+    from 4-token vector groups (<= 64 tokens) to 64-token matrix-core tiles."""
+    host = synth.make_layer(seed=5, fmt="q4_1", E=16, k=6)
+    dl = moe.DeviceLayer(host, max_tokens=256)
+    seen = set()
+    for T in (168, 172, 176, 180):
+        say(f"case matrix-core boundary T={T}")
+        info = check_layer(host, synth.make_x(T, xseed=600 + T), dl)
+        seen |= set(info["counts"].tolist())
+    assert any(55 <= c <= 64 for c in seen) and any(65 <= c <= 75 for c in seen), sorted(seen)
+
+
+def test_chunked_buckets_mixed(nvfp4_layer):
+    """520 tokens: the 256-token chunked bucket build (last chunk ragged) with
+    hot matrix-core buckets and cold vector-path buckets in one batch."""
+    host, dl = nvfp4_layer
+    say("case chunked buckets nvfp4 zipf T=520")
+    info = check_layer(host, synth.make_x(520, xseed=700), dl)
+    c = info["counts"]
+    assert c.max() >= 65 and ((c > 0) & (c < 65)).sum() > 20
+    say(f"  max row err {info['max_err']:.2e}")
