@@ -17,26 +17,30 @@ enum Fmt : int { FMT_BF16 = 0, FMT_Q4_1 = 1, FMT_NVFP4 = 2 };
 
 // ---- work decomposition ---------------------------------------------------------
 // A bucket of m tokens is split into token groups of GV_GROUP (vector path) when
-// m < MFMA_MIN, else into token tiles of MFMA_BN (matrix-core path).  Both paths
-// cover UP_ROWS gate/up row pairs or DN_ROWS down rows per work item.
+// m < MFMA_MIN, else into token tiles of mfma_bn(T) tokens (matrix-core path):
+// 64 in batches of up to MFMA_WIDE_T tokens, 128 in larger ones (where buckets
+// are large, a wider tile streams an expert's weights fewer times; where they
+// are not, narrower tiles make more and shorter items).  Both paths cover
+// UP_ROWS gate/up row pairs or DN_ROWS down rows per work item.
 constexpr int GV_GROUP = 4;
 constexpr int MFMA_MIN = 65;
-constexpr int MFMA_BN = 64;
+constexpr int MFMA_WIDE_T = 256;
 constexpr int UP_ROWS = 64;
 constexpr int DN_ROWS = 256;
 constexpr int N_UP_CHUNKS = D_FF / UP_ROWS;      // 8
 constexpr int N_DN_CHUNKS = D_MODEL / DN_ROWS;   // 8
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
-// token groups/tiles of a bucket of m tokens
+__host__ __device__ inline int mfma_bn(int T) { return T > MFMA_WIDE_T ? 128 : 64; }
+// token groups/tiles of a bucket of m tokens (bn: the batch's tile width)
 __host__ __device__ inline bool bucket_mfma(int m) { return m >= MFMA_MIN; }
-__host__ __device__ inline int bucket_tiles(int m) {
-  return m <= 0 ? 0 : (bucket_mfma(m) ? ceil_div(m, MFMA_BN) : ceil_div(m, GV_GROUP));
+__host__ __device__ inline int bucket_tiles(int m, int bn) {
+  return m <= 0 ? 0 : (bucket_mfma(m) ? ceil_div(m, bn) : ceil_div(m, GV_GROUP));
 }
 
 // Work item (16 bytes, so that a kernel needs one load to start streaming):
 //   head: expert (9 bits; SHARED_ID = the shared expert) | row chunk << 9 (5 bits) |
-//         token count << 14 (7 bits) | matrix-core path << 31
+//         token count << 14 (8 bits) | matrix-core path << 31
 //   p0:   first bucket position (routed) or first token (shared); the expert
 //         output rows of the item are p0.. (routed) or S + p0.. (shared)
 //   t01, t23: token ids of a vector-path item (16 bits each)
@@ -50,7 +54,7 @@ __host__ __device__ inline uint32_t item_head(int e, int chunk, int cnt, bool mf
 __device__ inline int item_expert(uint32_t h) { return (int)(h & 511u); }
 __device__ inline bool item_shared(uint32_t h) { return item_expert(h) == SHARED_ID; }
 __device__ inline int item_chunk(uint32_t h) { return (int)((h >> 9) & 31u); }
-__device__ inline int item_count(uint32_t h) { return (int)((h >> 14) & 127u); }
+__device__ inline int item_count(uint32_t h) { return (int)((h >> 14) & 255u); }
 __device__ inline bool item_mfma(uint32_t h) { return (h & ITEM_MFMA) != 0; }
 
 // ---- control block ------------------------------------------------------------------

@@ -12,9 +12,10 @@
 //     (16 bytes of 4-bit codes and the block scale), unpacks it in registers,
 //     and the 16 independent 4x4x4 products return it the group's partial sums
 //     of its own row; each wave keeps a ring of loads in flight across chunks;
-//   * buckets of MFMA_MIN or more tokens run as 128-row x 64-token tiles: the
-//     weight tile is decoded into LDS once per tile (v_mfma 32x32x16), with the
-//     next K-chunk prefetched into registers during the MFMAs.
+//   * buckets of MFMA_MIN or more tokens run as 128-row x 128-token tiles (one
+//     tile covers a bucket of up to 128 tokens, so its expert's weights stream
+//     once): the weight tile is decoded into LDS (v_mfma 32x32x16), with the
+//     next K-chunks prefetched into registers during the MFMAs.
 // Both kernels are persistent and walk device-side work lists that hold the
 // routed and the shared expert alike, so no host synchronisation is needed.
 //
@@ -649,19 +650,23 @@ __device__ void down_stream(const LayerArgs& a, int base, int n, MvSmem& sm) {
 
 // ======================================================================================
 // Matrix-core items: weight tile of 128 rows x 64 k decoded into LDS, activation
-// tile of 64 tokens x 64 k staged into LDS, v_mfma_f32_32x32x16_{f16,bf16}; the
-// next K-chunk is loaded into registers while the current one is multiplied.
+// tile of BN tokens x 64 k staged into LDS, v_mfma_f32_32x32x16_{f16,bf16};
+// the next K-chunks are loaded into registers while the current one is multiplied.
 // ======================================================================================
 constexpr int TS = 72;  // LDS row stride in 16-bit elements (64 + 8 pad)
+template <int BN> constexpr int MF_TT = BN / 32;   // 32-token blocks of a tile (accumulators per wave)
+template <int BN> constexpr int MF_XT = 256 / BN;  // threads per token when staging activations
+template <int BN> constexpr int MF_XK = 64 / MF_XT<BN>;  // activation elements per thread and K-chunk
+static_assert(MF_XK<64> % 16 == 0 && MF_XK<128> % 16 == 0, "activations are staged 16 elements at a time");
 
-struct FfnBuf {
+template <int BN> struct FfnBuf {
   uint16_t w[128 * TS];
-  uint16_t x[MFMA_BN * TS];
+  uint16_t x[BN * TS];
 };
-struct FfnSmem {
-  FfnBuf buf[2];  // K-chunks alternate between the two, so one barrier per chunk suffices
-  int tok[MFMA_BN];
-  int row[MFMA_BN];
+template <int BN> struct FfnSmem {
+  FfnBuf<BN> buf[2];  // K-chunks alternate between the two, so one barrier per chunk suffices
+  int tok[BN];
+  int row[BN];
 };
 
 // Store 16 activation elements (natural-order pairs src[8]) into LDS in the
@@ -691,62 +696,62 @@ __device__ inline f32x16 mfma32(const uint16_t* a, const uint16_t* b, f32x16 c) 
                                                  0, 0);
 }
 
-__device__ inline void mfma_tables(const LayerArgs& a, const ItemTok& it, FfnSmem& sm) {
+template <int BN> __device__ inline void mfma_tables(const LayerArgs& a, const ItemTok& it, FfnSmem<BN>& sm) {
   const int i = threadIdx.x;
-  if (i < MFMA_BN) {
+  if (i < BN) {
     // matrix-core tiles are shared-expert tiles or routed buckets (tokens via perm)
     sm.tok[i] = (i < it.cnt) ? (it.shared ? it.p0 + i : a.perm[it.p0 + i] / a.K) : -1;
     sm.row[i] = (i < it.cnt) ? row_of(a, it, i) : -1;
   }
 }
 
-// One K-chunk of a 128-row x 64-token tile: thread (wr_row = tid/2, half = tid%2)
-// owns 32 weights of one row; thread (xt = tid/4, xs = tid%4) owns 16
-// activation elements of one token.
-template <int FMT> struct MfmaStage {
+// One K-chunk of a 128-row x BN-token tile: thread (wr_row = tid/2,
+// half = tid%2) owns 32 weights of one row; thread (xt = tid/MF_XT,
+// xs = tid%MF_XT) owns MF_XK activation elements of one token.
+template <int FMT, int BN> struct MfmaStage {
   typename GV<FMT>::Raw w;
-  u32x4 x0, x1;
+  u32x4 x[MF_XK<BN> / 8];
 };
 
-template <int FMT>
-__device__ inline void mfma_fetch(MfmaStage<FMT>& st, const QMat& wq, size_t wrow, int kw, const uint16_t* xsrc,
+template <int FMT, int BN>
+__device__ inline void mfma_fetch(MfmaStage<FMT, BN>& st, const QMat& wq, size_t wrow, int kw, const uint16_t* xsrc,
                                   int cols) {
   st.w = GV<FMT>::template load<false>(wq, wrow, 0u, kw / 32, cols);
-  if (xsrc) {
-    st.x0 = ld16<false>(xsrc);
-    st.x1 = ld16<false>(xsrc + 8);
-  } else {
-    st.x0 = u32x4{0u, 0u, 0u, 0u};
-    st.x1 = st.x0;
-  }
+#pragma unroll
+  for (int i = 0; i < MF_XK<BN> / 8; ++i) st.x[i] = xsrc ? ld16<false>(xsrc + 8 * i) : u32x4{0u, 0u, 0u, 0u};
 }
 
-template <int FMT>
-__device__ inline void mfma_stage_store(const MfmaStage<FMT>& st, FfnBuf& sm, int wr_row, int wr_half, int xt, int xs,
-                                        bool x_bf16) {
+template <int FMT, int BN>
+__device__ inline void mfma_stage_store(const MfmaStage<FMT, BN>& st, FfnBuf<BN>& sm, int wr_row, int wr_half, int xt,
+                                        int xs, bool x_bf16) {
   uint32_t wv[16];
   GV<FMT>::decode(st.w, wv);
   u32x4* d = reinterpret_cast<u32x4*>(sm.w + wr_row * TS + 32 * wr_half);
 #pragma unroll
   for (int i = 0; i < 4; ++i) d[i] = u32x4{wv[4 * i], wv[4 * i + 1], wv[4 * i + 2], wv[4 * i + 3]};
-  uint32_t xv[8] = {st.x0[0], st.x0[1], st.x0[2], st.x0[3], st.x1[0], st.x1[1], st.x1[2], st.x1[3]};
-  if (OPER_F16<FMT> && x_bf16) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xv[i] = bf16x2_to_f16x2(xv[i]);
+  for (int g = 0; g < MF_XK<BN> / 16; ++g) {
+    uint32_t xv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xv[i] = st.x[2 * g + i / 4][i % 4];
+    if (OPER_F16<FMT> && x_bf16) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xv[i] = bf16x2_to_f16x2(xv[i]);
+    }
+    stage_x16<FMT>(sm.x + xt * TS + MF_XK<BN> * xs + 16 * g, xv);
   }
-  stage_x16<FMT>(sm.x + xt * TS + 16 * xs, xv);
 }
 
 // acc[tt] += W_tile(rows arow..) x X_tile(tokens 32tt..) of one K-chunk in LDS.
-template <int FMT>
-__device__ inline void mfma_chunk(f32x16* acc, const FfnBuf& sm, int arow) {
+template <int FMT, int BN>
+__device__ inline void mfma_chunk(f32x16* acc, const FfnBuf<BN>& sm, int arow) {
   const int lane = threadIdx.x & 63;
   const int ar = lane & 31, kh = 8 * (lane >> 5);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const uint16_t* ap = sm.w + arow * TS + 16 * s + kh;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) acc[tt] = mfma32<FMT>(ap, sm.x + (32 * tt + ar) * TS + 16 * s + kh, acc[tt]);
+    for (int tt = 0; tt < MF_TT<BN>; ++tt) acc[tt] = mfma32<FMT>(ap, sm.x + (32 * tt + ar) * TS + 16 * s + kh, acc[tt]);
   }
 }
 
@@ -755,35 +760,35 @@ __device__ inline void mfma_chunk(f32x16* acc, const FfnBuf& sm, int arow) {
 // null).  Two K-chunks are loaded ahead into registers; even chunks are staged
 // in LDS buffer 0 and odd ones in buffer 1, so the barrier after a chunk's
 // stores also tells that every wave is done with the chunk before it.
-template <int FMT>
-__device__ inline void mfma_kloop(f32x16* acc, FfnSmem& sm, const QMat& wq, size_t wrow, const uint16_t* xrow_ptr,
+template <int FMT, int BN>
+__device__ inline void mfma_kloop(f32x16* acc, FfnSmem<BN>& sm, const QMat& wq, size_t wrow, const uint16_t* xrow_ptr,
                                   bool x_bf16, int kdim, int arow) {
   const int tid = threadIdx.x;
   const int wr_row = tid >> 1, wr_half = tid & 1;
-  const int xt = tid >> 2, xs = tid & 3;
-  auto fetch = [&](MfmaStage<FMT>& st, int kc) {
-    mfma_fetch<FMT>(st, wq, wrow, kc + 32 * wr_half, xrow_ptr ? xrow_ptr + kc + 16 * xs : nullptr, kdim);
+  const int xt = tid / MF_XT<BN>, xs = tid % MF_XT<BN>;
+  auto fetch = [&](MfmaStage<FMT, BN>& st, int kc) {
+    mfma_fetch<FMT, BN>(st, wq, wrow, kc + 32 * wr_half, xrow_ptr ? xrow_ptr + kc + MF_XK<BN> * xs : nullptr, kdim);
   };
-  MfmaStage<FMT> st0, st1;
+  MfmaStage<FMT, BN> st0, st1;
   fetch(st0, 0);
   fetch(st1, 64);
 #pragma unroll 1
   for (int kc = 0; kc < kdim; kc += 128) {
-    mfma_stage_store<FMT>(st0, sm.buf[0], wr_row, wr_half, xt, xs, x_bf16);
+    mfma_stage_store<FMT, BN>(st0, sm.buf[0], wr_row, wr_half, xt, xs, x_bf16);
     __syncthreads();
     if (kc + 128 < kdim) fetch(st0, kc + 128);
-    mfma_chunk<FMT>(acc, sm.buf[0], arow);
-    mfma_stage_store<FMT>(st1, sm.buf[1], wr_row, wr_half, xt, xs, x_bf16);
+    mfma_chunk<FMT, BN>(acc, sm.buf[0], arow);
+    mfma_stage_store<FMT, BN>(st1, sm.buf[1], wr_row, wr_half, xt, xs, x_bf16);
     __syncthreads();
     if (kc + 192 < kdim) fetch(st1, kc + 192);
-    mfma_chunk<FMT>(acc, sm.buf[1], arow);
+    mfma_chunk<FMT, BN>(acc, sm.buf[1], arow);
   }
 }
 
-// gate/up item: 64 row pairs (n0 ..) x 64 tokens; LDS rows 0..63 gate, 64..127 up.
-template <int FMT>
+// gate/up item: 64 row pairs (n0 ..) x BN tokens; LDS rows 0..63 gate, 64..127 up.
+template <int FMT, int BN>
 __device__ void mfma_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int mat, const ItemTok& it, int n0,
-                        FfnSmem& sm) {
+                        FfnSmem<BN>& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   mfma_tables(a, it, sm);
   __syncthreads();
@@ -793,19 +798,19 @@ __device__ void mfma_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int m
   wq.scales = (wr_row < 64) ? G.scales : Uq.scales;
   wq.ts = nullptr;
   const size_t wrow = (size_t)mat * D_FF + n0 + (wr_row & 63);
-  const int xtok = sm.tok[tid >> 2];
+  const int xtok = sm.tok[tid / MF_XT<BN>];
   const uint16_t* xrow = xtok >= 0 ? a.x + (size_t)xtok * D_MODEL : nullptr;
   // A-row r -> LDS row (r < 16 ? 16w + r : 64 + 16w + r - 16): gate and up of the same n
   const int ar = lane & 31;
   const int arow = (ar < 16) ? (16 * wave + ar) : (64 + 16 * wave + ar - 16);
-  f32x16 acc[2] = {};
-  mfma_kloop<FMT>(acc, sm, wq, wrow, xrow, true, D_MODEL, arow);
+  f32x16 acc[MF_TT<BN>] = {};
+  mfma_kloop<FMT, BN>(acc, sm, wq, wrow, xrow, true, D_MODEL, arow);
   // acc[tt][4i+j] = A-row 8i + 4(lane/32) + j, token 32tt + lane%32:
   // gate for i in {0,1}, the matching up at i+2.
   const float tsg = (FMT == FMT_NVFP4) ? G.ts[mat] : 1.f;
   const float tsu = (FMT == FMT_NVFP4) ? Uq.ts[mat] : 1.f;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int tt = 0; tt < MF_TT<BN>; ++tt) {
     const int hrow = sm.row[32 * tt + ar];
     if (hrow < 0) continue;
 #pragma unroll
@@ -823,21 +828,21 @@ __device__ void mfma_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int m
   __syncthreads();  // tables and tiles are reused by the next item
 }
 
-// down item: 128 rows (r0 ..) x 64 tokens, K = 512.
-template <int FMT>
-__device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const ItemTok& it, int r0, FfnSmem& sm) {
+// down item: 128 rows (r0 ..) x BN tokens, K = 512.
+template <int FMT, int BN>
+__device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const ItemTok& it, int r0, FfnSmem<BN>& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   mfma_tables(a, it, sm);
   __syncthreads();
   const size_t wrow = (size_t)mat * D_MODEL + r0 + (tid >> 1);
-  const int hrow_x = sm.row[tid >> 2];
+  const int hrow_x = sm.row[tid / MF_XT<BN>];
   const uint16_t* xrow = hrow_x >= 0 ? a.h + (size_t)hrow_x * D_FF : nullptr;
   const int ar = lane & 31;
-  f32x16 acc[2] = {};
-  mfma_kloop<FMT>(acc, sm, D, wrow, xrow, false, D_FF, 32 * wave + ar);
+  f32x16 acc[MF_TT<BN>] = {};
+  mfma_kloop<FMT, BN>(acc, sm, D, wrow, xrow, false, D_FF, 32 * wave + ar);
   const float ts = (FMT == FMT_NVFP4) ? D.ts[mat] : 1.f;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int tt = 0; tt < MF_TT<BN>; ++tt) {
     const int yrow = sm.row[32 * tt + ar];
     if (yrow < 0) continue;
 #pragma unroll
@@ -857,49 +862,61 @@ __device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const Item
 // formats (their rings fit in half the register file), one for bf16.
 template <int FMT> constexpr int FFN_WG_PER_CU = (FMT == FMT_BF16) ? 1 : 2;
 
-// LDS of the persistent kernels: the matrix-core tiles only where the batch
-// can have them (MF: T >= MFMA_MIN), since their double buffer would otherwise
-// cost the vector path occupancy.
-template <bool MF> struct FfnKernelSmem;
-template <> struct FfnKernelSmem<true> {
+// LDS of the persistent kernels: the matrix-core tiles (BN tokens wide) only
+// where the batch can have them (BN > 0: T >= MFMA_MIN), since their double
+// buffer would otherwise cost the vector path occupancy.
+template <int BN> struct FfnKernelSmem {
   union {
-    FfnSmem mf;
+    FfnSmem<BN> mf;
     MvSmem gv;
   };
 };
-template <> struct FfnKernelSmem<false> {
+template <> struct FfnKernelSmem<0> {
   MvSmem gv;
 };
 
+// Matrix-core items in an XCD-aware order.  Workgroups are dispatched to the 8
+// XCDs round-robin by blockIdx, and workgroup c takes items c, c + gridDim.x,
+// ... (gridDim.x a multiple of 8), so item i runs on XCD i % 8.  In groups of 8
+// tiles, position i = 64 g + 8 ch + tl holds row chunk ch of tile 8 g + tl:
+// the 8 chunks of a tile run on one XCD at about the same time and read its
+// activation tile through that XCD's L2 instead of once per XCD.
+__device__ inline int mf_item(int i, int n) {
+  if (i >= (n / 64) * 64) return i;
+  const int g = i >> 6, ch = (i >> 3) & 7, tl = i & 7;
+  return (8 * g + tl) * 8 + ch;
+}
+static_assert(N_UP_CHUNKS == 8 && N_DN_CHUNKS == 8, "mf_item assumes 8 row chunks per tile");
+
 // Items of the matrix-core path come first; the vector-path chunks follow.
-template <int FMT, bool MF>
+template <int FMT, int BN>
 __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_up_kernel(LayerArgs a) {
-  __shared__ FfnKernelSmem<MF> sm;
+  __shared__ FfnKernelSmem<BN> sm;
   const int n_all = a.ctl[CTL_N_UP], n_mf = a.ctl[CTL_N_UP_MF];
-  if constexpr (MF) {
+  if constexpr (BN > 0) {
     for (int i = blockIdx.x; i < n_mf; i += gridDim.x) {
-      const Item item = fetch_item(a.tiles, i, N_UP_CHUNKS);
+      const Item item = fetch_item(a.tiles, mf_item(i, n_mf), N_UP_CHUNKS);
       const bool sh = item_shared(item.head);
-      mfma_up<FMT>(a, sel_qmat(sh, a.sh_gate, a.gate), sel_qmat(sh, a.sh_up, a.up), sh ? 0 : item_expert(item.head),
+      mfma_up<FMT, BN>(a, sel_qmat(sh, a.sh_gate, a.gate), sel_qmat(sh, a.sh_up, a.up), sh ? 0 : item_expert(item.head),
                    item_tokens(item), item_chunk(item.head) * UP_ROWS, sm.mf);
     }
   }
   up_stream<FMT>(a, n_mf, n_all - n_mf, sm.gv);
 }
 
-template <int FMT, bool MF>
+template <int FMT, int BN>
 __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_down_kernel(LayerArgs a) {
-  __shared__ FfnKernelSmem<MF> sm;
+  __shared__ FfnKernelSmem<BN> sm;
   const int n_all = a.ctl[CTL_N_DN], n_mf = a.ctl[CTL_N_DN_MF];
-  if constexpr (MF) {
+  if constexpr (BN > 0) {
     for (int i = blockIdx.x; i < n_mf; i += gridDim.x) {
-      const Item item = fetch_item(a.tiles, i, N_DN_CHUNKS);
+      const Item item = fetch_item(a.tiles, mf_item(i, n_mf), N_DN_CHUNKS);
       const bool sh = item_shared(item.head);
       const ItemTok it = item_tokens(item);
       const int r0 = item_chunk(item.head) * DN_ROWS;
 #pragma unroll 1
       for (int rb = 0; rb < DN_ROWS; rb += 128)
-        mfma_down<FMT>(a, sel_qmat(sh, a.sh_down, a.down), sh ? 0 : item_expert(item.head), it, r0 + rb, sm.mf);
+        mfma_down<FMT, BN>(a, sel_qmat(sh, a.sh_down, a.down), sh ? 0 : item_expert(item.head), it, r0 + rb, sm.mf);
     }
   }
   down_stream<FMT>(a, n_mf, n_all - n_mf, sm.gv);
@@ -914,24 +931,26 @@ int resident_per_cu(Kern kernel) {
   return n;
 }
 
-template <int FMT, bool MF>
+template <int FMT, int BN>
 hipError_t launch_ffn_var(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s) {
-  static const int occ_up = resident_per_cu(ffn_up_kernel<FMT, MF>);
-  static const int occ_dn = resident_per_cu(ffn_down_kernel<FMT, MF>);
+  static const int occ_up = resident_per_cu(ffn_up_kernel<FMT, BN>);
+  static const int occ_dn = resident_per_cu(ffn_down_kernel<FMT, BN>);
   int grid = n_cu * (up ? occ_up : occ_dn);
   if (max_wgs < grid) grid = max_wgs;
   if (grid < 1) return hipSuccess;
-  if (up) hipLaunchKernelGGL((ffn_up_kernel<FMT, MF>), dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((ffn_down_kernel<FMT, MF>), dim3(grid), dim3(256), 0, s, a);
+  if (up) hipLaunchKernelGGL((ffn_up_kernel<FMT, BN>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((ffn_down_kernel<FMT, BN>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 // Matrix-core tiles exist only for buckets (or the shared expert) of
-// MFMA_MIN or more tokens, so below that the leaner kernel runs.
+// MFMA_MIN or more tokens, so below that the leaner kernel runs; above, the
+// kernel for the batch's tile width.
 template <int FMT>
 hipError_t launch_ffn_fmt(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s) {
-  return bucket_mfma(a.T) ? launch_ffn_var<FMT, true>(a, up, n_cu, max_wgs, s)
-                          : launch_ffn_var<FMT, false>(a, up, n_cu, max_wgs, s);
+  if (!bucket_mfma(a.T)) return launch_ffn_var<FMT, 0>(a, up, n_cu, max_wgs, s);
+  return mfma_bn(a.T) == 64 ? launch_ffn_var<FMT, 64>(a, up, n_cu, max_wgs, s)
+                            : launch_ffn_var<FMT, 128>(a, up, n_cu, max_wgs, s);
 }
 
 hipError_t launch_ffn(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s) {
@@ -980,24 +999,40 @@ __device__ inline void rmsnorm_store(const float* v, uint16_t* dst, float eps) {
 // a.out.  Stack: recorded to a.y_rec (if any), r += out, then the next
 // layer's input bf16(RMSNorm(r)) or, after the last layer, bf16(r).
 __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a) {
-  const int t = blockIdx.x;
+  const int t = blockIdx.x, K = a.K;
   const int i0 = 8 * threadIdx.x;
+  // every load is issued before the first sum: the slots' rows, then the rows
+  int pos[MAX_K];
+  float wj[MAX_K];
+#pragma unroll
+  for (int j = 0; j < MAX_K; ++j) {
+    pos[j] = 0;
+    wj[j] = 0.f;
+    if (j < K) {
+      pos[j] = a.inv_perm[(size_t)t * K + j];
+      wj[j] = a.w[(size_t)t * K + j];
+    }
+  }
+  float4 v[MAX_K + 1][2];
+#pragma unroll
+  for (int j = 0; j <= MAX_K; ++j) {
+    const bool sh = (j == MAX_K);
+    if (sh ? a.n_shared != 0 : j < K) {
+      const float4* p = reinterpret_cast<const float4*>(a.y + (size_t)(sh ? a.S + t : pos[j]) * D_MODEL + i0);
+      v[j][0] = p[0];
+      v[j][1] = p[1];
+    }
+  }
   float o[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) o[q] = 0.f;
-  for (int j = 0; j < a.K; ++j) {
-    const float wj = a.w[(size_t)t * a.K + j];
-    const float4* p = reinterpret_cast<const float4*>(a.y + (size_t)a.inv_perm[(size_t)t * a.K + j] * D_MODEL + i0);
-    const float4 v0 = p[0], v1 = p[1];
-    o[0] += wj * v0.x; o[1] += wj * v0.y; o[2] += wj * v0.z; o[3] += wj * v0.w;
-    o[4] += wj * v1.x; o[5] += wj * v1.y; o[6] += wj * v1.z; o[7] += wj * v1.w;
-  }
-  if (a.n_shared) {
-    const float s = a.shared_scale;
-    const float4* p = reinterpret_cast<const float4*>(a.y + (size_t)(a.S + t) * D_MODEL + i0);
-    const float4 v0 = p[0], v1 = p[1];
-    o[0] += s * v0.x; o[1] += s * v0.y; o[2] += s * v0.z; o[3] += s * v0.w;
-    o[4] += s * v1.x; o[5] += s * v1.y; o[6] += s * v1.z; o[7] += s * v1.w;
+#pragma unroll
+  for (int j = 0; j <= MAX_K; ++j) {
+    const bool sh = (j == MAX_K);
+    if (sh ? a.n_shared == 0 : j >= K) continue;
+    const float c = sh ? a.shared_scale : wj[j];
+    o[0] += c * v[j][0].x; o[1] += c * v[j][0].y; o[2] += c * v[j][0].z; o[3] += c * v[j][0].w;
+    o[4] += c * v[j][1].x; o[5] += c * v[j][1].y; o[6] += c * v[j][1].z; o[7] += c * v[j][1].w;
   }
   if (!a.r) {
     store_bf16x8(a.out + (size_t)t * D_MODEL + i0, o);

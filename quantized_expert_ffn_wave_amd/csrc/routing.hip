@@ -26,6 +26,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int ROUTER_KR = 256;                  // K range per split
 constexpr int ROUTER_KS = D_MODEL / ROUTER_KR;  // 8 splits
+constexpr int ROUTER_SMALL_T = 256;             // largest T for one 16-token tile per wave
 constexpr int ROUTER_TG = 256;                  // tokens per workgroup on the large-T path
 
 // Decode-sized T: one wave per (16-token tile, 16-expert tile, K-split); the
@@ -65,7 +66,9 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
 }
 
 // Large T: a wave keeps its 16 router rows x 256 k in registers and loops over
-// the 16-token tiles of a 256-token group.  grid (ceil(E/64), ROUTER_KS, ceil(T/256)).
+// the 16-token tiles of a ROUTER_TG-token group, loading the next tile's
+// activations while the current one is multiplied.
+// grid (ceil(E/64), ROUTER_KS, ceil(T/ROUTER_TG)).
 __global__ __launch_bounds__(256) void router_large_kernel(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ wr,
                                                            const float* __restrict__ bias, float* __restrict__ part,
@@ -81,13 +84,17 @@ __global__ __launch_bounds__(256) void router_large_kernel(const uint16_t* __res
 #pragma unroll
   for (int s = 0; s < ROUTER_KR / 32; ++s) b[s] = *reinterpret_cast<const bf16x8*>(wrow + 32 * s);
   const float bz = (ks == 0 && bias) ? bias[e0 + col] : 0.f;  // the bias rides in split 0
-  const int tg0 = blockIdx.z * ROUTER_TG;
-  for (int t0 = tg0; t0 < min(T, tg0 + ROUTER_TG); t0 += 16) {
+  const int tg0 = blockIdx.z * ROUTER_TG, tg1 = min(T, tg0 + ROUTER_TG);
+  auto load_tile = [&](bf16x8* a, int t0) {
     const int t = t0 + col;
-    bf16x8 a[ROUTER_KR / 32];
-    const uint16_t* xrow = x + (size_t)(t < T ? t : 0) * D_MODEL + kbase;
+    const uint16_t* xrow = x + (size_t)(t < T ? t : T - 1) * D_MODEL + kbase;
 #pragma unroll
-    for (int s = 0; s < ROUTER_KR / 32; ++s) a[s] = (t < T) ? *reinterpret_cast<const bf16x8*>(xrow + 32 * s) : bf16x8{};
+    for (int s = 0; s < ROUTER_KR / 32; ++s) a[s] = *reinterpret_cast<const bf16x8*>(xrow + 32 * s);
+  };
+  bf16x8 a[ROUTER_KR / 32], an[ROUTER_KR / 32];
+  load_tile(a, tg0);
+  for (int t0 = tg0; t0 < tg1; t0 += 16) {
+    load_tile(an, (t0 + 16 < tg1) ? t0 + 16 : t0);  // always issued; the last one repeats the tile
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < ROUTER_KR / 32; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[s], acc, 0, 0, 0);
@@ -96,11 +103,13 @@ __global__ __launch_bounds__(256) void router_large_kernel(const uint16_t* __res
       const int tt = t0 + 4 * (lane >> 4) + j;
       if (tt < T) part[((size_t)ks * T + tt) * E + e0 + col] = acc[j] + bz;
     }
+#pragma unroll
+    for (int s = 0; s < ROUTER_KR / 32; ++s) a[s] = an[s];
   }
 }
 
 hipError_t launch_router(const LayerArgs& a, hipStream_t s) {
-  if (a.T <= ROUTER_TG) {
+  if (a.T <= ROUTER_SMALL_T) {
     dim3 grid(ceil_div(a.T, 16) * ceil_div(a.E, 64), ROUTER_KS);
     hipLaunchKernelGGL(router_small_kernel, grid, dim3(256), 0, s, a.x, a.router_w, a.router_b, a.logit_part, a.T, a.E);
   } else {
@@ -286,9 +295,10 @@ __device__ void write_lists(const LayerArgs& a, const int* bcnt, const int* boff
   // work list: matrix-core tiles first, then vector tiles.  Gate/up item i is
   // row chunk i % N_UP_CHUNKS of tile i / N_UP_CHUNKS, down item i chunk
   // i % N_DN_CHUNKS of tile i / N_DN_CHUNKS.
+  const int bn = mfma_bn(T);
   for (int e = tid; e < E; e += nth) {
     const int m = bcnt[e];
-    const int tiles = bucket_tiles(m);
+    const int tiles = bucket_tiles(m, bn);
     ls.it_m[e] = bucket_mfma(m) ? tiles : 0;
     ls.it_g[e] = bucket_mfma(m) ? 0 : tiles;
   }
@@ -302,11 +312,11 @@ __device__ void write_lists(const LayerArgs& a, const int* bcnt, const int* boff
   }
   __syncthreads();
   const int tiles_m = ls.tot[0], tiles_g = ls.tot[1];
-  // The shared expert takes every token: 64-token matrix-core tiles from
+  // The shared expert takes every token: bn-token matrix-core tiles from
   // MFMA_MIN tokens on, else groups of GV_GROUP tokens, in the same lists.
   // Tile order: routed matrix-core, shared matrix-core, routed vector, shared
   // vector (the kernels take the matrix-core items first).
-  const int sh_tiles = a.n_shared ? bucket_tiles(T) : 0;
+  const int sh_tiles = a.n_shared ? bucket_tiles(T, bn) : 0;
   const bool sh_mf = bucket_mfma(T);
   const int mf_tiles = tiles_m + (sh_mf ? sh_tiles : 0);
   const int all_tiles = tiles_m + tiles_g + sh_tiles;
@@ -323,7 +333,7 @@ __device__ void write_lists(const LayerArgs& a, const int* bcnt, const int* boff
   for (int ti = tid; ti < n_tiles; ti += nth) {
     const bool shared = (ti >= tiles_m && ti < mf_tiles) || ti >= mf_tiles + tiles_g;
     const bool mf = ti < mf_tiles;
-    const int per = mf ? MFMA_BN : GV_GROUP;
+    const int per = mf ? bn : GV_GROUP;
     int expert, p0, cnt;
     uint32_t tk[GV_GROUP] = {0u, 0u, 0u, 0u};
     if (shared) {
@@ -426,7 +436,7 @@ __global__ __launch_bounds__(BK_THREADS) void chunk_scan_kernel(LayerArgs a) {
   write_lists(a, cnt, off, ls, [](int) { return 0; });
   // first vector-path tile of each expert (tile order: routed matrix-core,
   // shared matrix-core, routed vector, shared vector)
-  const int sh_mf = (a.n_shared && bucket_mfma(a.T)) ? bucket_tiles(a.T) : 0;
+  const int sh_mf = (a.n_shared && bucket_mfma(a.T)) ? bucket_tiles(a.T, mfma_bn(a.T)) : 0;
   int32_t* vt = tab + (size_t)nch * E;
   for (int e = tid; e < E; e += BK_THREADS) vt[e] = bucket_mfma(cnt[e]) ? -1 : ls.tot[0] + sh_mf + ls.it_g[e];
 }
