@@ -21,7 +21,8 @@ enum Fmt : int { FMT_BF16 = 0, FMT_Q4_1 = 1, FMT_NVFP4 = 2 };
 // 64 in batches of up to MFMA_WIDE_T tokens, 128 in larger ones (where buckets
 // are large, a wider tile streams an expert's weights fewer times; where they
 // are not, narrower tiles make more and shorter items).  Both paths cover
-// UP_ROWS gate/up row pairs or DN_ROWS down rows per work item.
+// UP_ROWS gate/up row pairs (vector path; matrix-core path: D_FF / mf_up_chunks
+// of the tile width), or DN_ROWS down rows, per work item.
 constexpr int GV_GROUP = 4;
 constexpr int MFMA_MIN = 65;
 constexpr int MFMA_WIDE_T = 256;
@@ -32,6 +33,9 @@ constexpr int N_DN_CHUNKS = D_MODEL / DN_ROWS;   // 8
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ inline int mfma_bn(int T) { return T > MFMA_WIDE_T ? 128 : 64; }
+// gate/up items per matrix-core tile of width bn: 128 row pairs each for
+// 128-token tiles, 64 for 64-token ones
+__host__ __device__ constexpr int mf_up_chunks(int bn) { return bn == 128 ? 4 : 8; }
 // token groups/tiles of a bucket of m tokens (bn: the batch's tile width)
 __host__ __device__ inline bool bucket_mfma(int m) { return m >= MFMA_MIN; }
 __host__ __device__ inline int bucket_tiles(int m, int bn) {

@@ -649,22 +649,38 @@ __device__ void down_stream(const LayerArgs& a, int base, int n, MvSmem& sm) {
 }
 
 // ======================================================================================
-// Matrix-core items: weight tile of 128 rows x 64 k decoded into LDS, activation
-// tile of BN tokens x 64 k staged into LDS, v_mfma_f32_32x32x16_{f16,bf16};
-// the next K-chunks are loaded into registers while the current one is multiplied.
+// Matrix-core items.  Each wave owns RB blocks of 32 weight rows and loads them
+// straight from global memory into the A operand of v_mfma_f32_32x32x16_{f16,bf16}:
+// lane (r = lane % 32, h = lane / 32) holds, for each 64-wide K-chunk and row
+// block, the 32 weights k = 32 h .. 32 h + 31 of its row (one block of the 4-bit
+// formats), decoded into the chunk's 4 MFMA steps of 8 weights.  The chunk's
+// BN-token activation tile is staged in LDS (double buffered, one barrier per
+// chunk) in the decode's k order, and lane (token c = lane % 32, h) reads the
+// same k of its token as the B operand.  NS K-chunks are held in registers: the
+// one multiplied and the NS - 1 loads in flight behind it.
+//   gate/up item (4 waves x 32 RB row pairs from n0): with RB = 2 a wave's block
+//     0 holds gate rows n0 + 32 w + r and block 1 the up rows of the same n; with
+//     RB = 1 its one block holds gate rows n0 + 16 w + r (r < 16) and the up rows
+//     of the same n (r >= 16).  Either way a lane holds both inputs of its SwiGLU
+//     outputs.  RB = 2 for 128-token tiles (fewer passes over the activation
+//     tile when the batch is large), 1 for 64-token ones (more, shorter items);
+//   down item: DN_ROWS rows from r0; wave w's block b = rows r0 + 64 w + 32 b + r.
 // ======================================================================================
 constexpr int TS = 72;  // LDS row stride in 16-bit elements (64 + 8 pad)
-template <int BN> constexpr int MF_TT = BN / 32;   // 32-token blocks of a tile (accumulators per wave)
-template <int BN> constexpr int MF_XT = 256 / BN;  // threads per token when staging activations
+template <int BN> constexpr int MF_TT = BN / 32;         // 32-token blocks of a tile
+template <int BN> constexpr int MF_XT = 256 / BN;        // threads per token when staging activations
 template <int BN> constexpr int MF_XK = 64 / MF_XT<BN>;  // activation elements per thread and K-chunk
+template <int BN> constexpr int MF_UP_RB = (BN == 128) ? 2 : 1;
+// K-chunks held in registers: gate/up (K = 2048) 4, or 2 where 4 would not fit
+// two waves per SIMD (128-token tiles); down (K = 512, 8 chunks) 2
+template <int FMT, int BN> constexpr int MF_NS_UP = (BN == 128) ? 2 : 4;
+template <int FMT, int BN> constexpr int MF_NS_DN = 2;
 static_assert(MF_XK<64> % 16 == 0 && MF_XK<128> % 16 == 0, "activations are staged 16 elements at a time");
+static_assert(DN_ROWS == 4 * 64, "down items: 4 waves x 2 row blocks of 32 rows");
+static_assert(D_MODEL % (64 * 4) == 0 && D_FF % (64 * 4) == 0, "the chunk loop is unrolled by up to 4");
 
-template <int BN> struct FfnBuf {
-  uint16_t w[128 * TS];
-  uint16_t x[BN * TS];
-};
 template <int BN> struct FfnSmem {
-  FfnBuf<BN> buf[2];  // K-chunks alternate between the two, so one barrier per chunk suffices
+  uint16_t x[2][BN * TS];  // K-chunks alternate between the two, so one barrier per chunk suffices
   int tok[BN];
   int row[BN];
 };
@@ -686,9 +702,7 @@ template <int FMT> __device__ inline void stage_x16(uint16_t* dst, const uint32_
 }
 
 template <int FMT>
-__device__ inline f32x16 mfma32(const uint16_t* a, const uint16_t* b, f32x16 c) {
-  const u32x4 av = *reinterpret_cast<const u32x4*>(a);
-  const u32x4 bv = *reinterpret_cast<const u32x4*>(b);
+__device__ inline f32x16 mfma32(u32x4 av, u32x4 bv, f32x16 c) {
   if (OPER_F16<FMT>)
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, av), __builtin_bit_cast(f16x8, bv), c, 0,
                                                   0, 0);
@@ -705,120 +719,121 @@ template <int BN> __device__ inline void mfma_tables(const LayerArgs& a, const I
   }
 }
 
-// One K-chunk of a 128-row x BN-token tile: thread (wr_row = tid/2,
-// half = tid%2) owns 32 weights of one row; thread (xt = tid/MF_XT,
-// xs = tid%MF_XT) owns MF_XK activation elements of one token.
-template <int FMT, int BN> struct MfmaStage {
-  typename GV<FMT>::Raw w;
+// One K-chunk in registers: the lane's 32 weights of each row block, and the
+// thread's MF_XK activations of token tid / MF_XT (elements MF_XK * (tid % MF_XT) ..).
+template <int FMT, int BN, int RB> struct MfStage {
+  typename GV<FMT>::Raw w[RB];
   u32x4 x[MF_XK<BN> / 8];
 };
 
-template <int FMT, int BN>
-__device__ inline void mfma_fetch(MfmaStage<FMT, BN>& st, const QMat& wq, size_t wrow, int kw, const uint16_t* xsrc,
-                                  int cols) {
-  st.w = GV<FMT>::template load<false>(wq, wrow, 0u, kw / 32, cols);
-#pragma unroll
-  for (int i = 0; i < MF_XK<BN> / 8; ++i) st.x[i] = xsrc ? ld16<false>(xsrc + 8 * i) : u32x4{0u, 0u, 0u, 0u};
-}
-
-template <int FMT, int BN>
-__device__ inline void mfma_stage_store(const MfmaStage<FMT, BN>& st, FfnBuf<BN>& sm, int wr_row, int wr_half, int xt,
-                                        int xs, bool x_bf16) {
-  uint32_t wv[16];
-  GV<FMT>::decode(st.w, wv);
-  u32x4* d = reinterpret_cast<u32x4*>(sm.w + wr_row * TS + 32 * wr_half);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) d[i] = u32x4{wv[4 * i], wv[4 * i + 1], wv[4 * i + 2], wv[4 * i + 3]};
-#pragma unroll
-  for (int g = 0; g < MF_XK<BN> / 16; ++g) {
-    uint32_t xv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) xv[i] = st.x[2 * g + i / 4][i % 4];
-    if (OPER_F16<FMT> && x_bf16) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xv[i] = bf16x2_to_f16x2(xv[i]);
-    }
-    stage_x16<FMT>(sm.x + xt * TS + MF_XK<BN> * xs + 16 * g, xv);
-  }
-}
-
-// acc[tt] += W_tile(rows arow..) x X_tile(tokens 32tt..) of one K-chunk in LDS.
-template <int FMT, int BN>
-__device__ inline void mfma_chunk(f32x16* acc, const FfnBuf<BN>& sm, int arow) {
-  const int lane = threadIdx.x & 63;
-  const int ar = lane & 31, kh = 8 * (lane >> 5);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const uint16_t* ap = sm.w + arow * TS + 16 * s + kh;
-#pragma unroll
-    for (int tt = 0; tt < MF_TT<BN>; ++tt) acc[tt] = mfma32<FMT>(ap, sm.x + (32 * tt + ar) * TS + 16 * s + kh, acc[tt]);
-  }
-}
-
-// acc[tt] += W_tile x X_tile over K = kdim (a multiple of 128), 64 at a time.
-// wq/wrow: this thread's weight row; xrow_ptr: this thread's activation row (or
-// null).  Two K-chunks are loaded ahead into registers; even chunks are staged
-// in LDS buffer 0 and odd ones in buffer 1, so the barrier after a chunk's
-// stores also tells that every wave is done with the chunk before it.
-template <int FMT, int BN>
-__device__ inline void mfma_kloop(f32x16* acc, FfnSmem<BN>& sm, const QMat& wq, size_t wrow, const uint16_t* xrow_ptr,
-                                  bool x_bf16, int kdim, int arow) {
-  const int tid = threadIdx.x;
-  const int wr_row = tid >> 1, wr_half = tid & 1;
+// acc[b][tt] += W_block_b (this wave's rows) x X (tokens 32 tt ..) over K = kdim.
+// q[b], wrow[b]: the matrix and the lane's weight row of block b; xsrc: the
+// thread's activation row and offset (a valid row also for tokens past the
+// tile's count: their columns are never stored, and a column only meets its
+// own activations).
+template <int FMT, int BN, int RB, int NS>
+__device__ inline void mf_kloop(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<BN>& sm, const QMat (&q)[RB],
+                                const size_t (&wrow)[RB], const uint16_t* xsrc, bool x_bf16, int kdim) {
+  static_assert(NS % 2 == 0, "chunk j uses LDS buffer j % 2");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int h = lane >> 5, c = lane & 31;
   const int xt = tid / MF_XT<BN>, xs = tid % MF_XT<BN>;
-  auto fetch = [&](MfmaStage<FMT, BN>& st, int kc) {
-    mfma_fetch<FMT, BN>(st, wq, wrow, kc + 32 * wr_half, xrow_ptr ? xrow_ptr + kc + MF_XK<BN> * xs : nullptr, kdim);
+  const int nc = kdim / 64;
+  // every load is issued unconditionally (past the last chunk the last one is
+  // loaded again), so that the compiler's wait counts stay exact
+  auto fetch = [&](MfStage<FMT, BN, RB>& st, int ck) {
+    ck = min(ck, nc - 1);
+#pragma unroll
+    for (int b = 0; b < RB; ++b) st.w[b] = GV<FMT>::template load<false>(q[b], wrow[b], 0u, 2 * ck + h, kdim);
+#pragma unroll
+    for (int i = 0; i < MF_XK<BN> / 8; ++i) st.x[i] = ld16<false>(xsrc + 64 * ck + 8 * i);
   };
-  MfmaStage<FMT, BN> st0, st1;
-  fetch(st0, 0);
-  fetch(st1, 64);
+  auto stage = [&](const MfStage<FMT, BN, RB>& st, uint16_t* buf) {
+#pragma unroll
+    for (int g = 0; g < MF_XK<BN> / 16; ++g) {
+      uint32_t xv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xv[i] = st.x[2 * g + i / 4][i % 4];
+      if (OPER_F16<FMT> && x_bf16) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xv[i] = bf16x2_to_f16x2(xv[i]);
+      }
+      stage_x16<FMT>(buf + xt * TS + MF_XK<BN> * xs + 16 * g, xv);
+    }
+  };
+  auto multiply = [&](const MfStage<FMT, BN, RB>& st, const uint16_t* buf) {
+    uint32_t wv[RB][16];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) GV<FMT>::decode(st.w[b], wv[b]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int tt = 0; tt < MF_TT<BN>; ++tt) {
+        const u32x4 bv = *reinterpret_cast<const u32x4*>(buf + (32 * tt + c) * TS + 32 * h + 8 * s);
+#pragma unroll
+        for (int b = 0; b < RB; ++b)
+          acc[b][tt] = mfma32<FMT>(u32x4{wv[b][4 * s], wv[b][4 * s + 1], wv[b][4 * s + 2], wv[b][4 * s + 3]}, bv,
+                                   acc[b][tt]);
+      }
+    }
+  };
+  MfStage<FMT, BN, RB> st[NS];
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) fetch(st[i], i);
 #pragma unroll 1
-  for (int kc = 0; kc < kdim; kc += 128) {
-    mfma_stage_store<FMT, BN>(st0, sm.buf[0], wr_row, wr_half, xt, xs, x_bf16);
-    __syncthreads();
-    if (kc + 128 < kdim) fetch(st0, kc + 128);
-    mfma_chunk<FMT, BN>(acc, sm.buf[0], arow);
-    mfma_stage_store<FMT, BN>(st1, sm.buf[1], wr_row, wr_half, xt, xs, x_bf16);
-    __syncthreads();
-    if (kc + 192 < kdim) fetch(st1, kc + 192);
-    mfma_chunk<FMT, BN>(acc, sm.buf[1], arow);
+  for (int ck0 = 0; ck0 < nc; ck0 += NS) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      stage(st[j], sm.x[j & 1]);
+      fetch(st[(j + NS - 1) % NS], ck0 + j + NS - 1);
+      __syncthreads();
+      multiply(st[j], sm.x[j & 1]);
+    }
   }
 }
 
-// gate/up item: 64 row pairs (n0 ..) x BN tokens; LDS rows 0..63 gate, 64..127 up.
+// gate/up item: 32 MF_UP_RB row pairs per wave (n0 ..) x BN tokens.
 template <int FMT, int BN>
 __device__ void mfma_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int mat, const ItemTok& it, int n0,
                         FfnSmem<BN>& sm) {
+  constexpr int RB = MF_UP_RB<BN>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, c = lane & 31;
   mfma_tables(a, it, sm);
   __syncthreads();
-  const int wr_row = tid >> 1;
-  QMat wq;
-  wq.codes = (wr_row < 64) ? G.codes : Uq.codes;
-  wq.scales = (wr_row < 64) ? G.scales : Uq.scales;
-  wq.ts = nullptr;
-  const size_t wrow = (size_t)mat * D_FF + n0 + (wr_row & 63);
-  const int xtok = sm.tok[tid / MF_XT<BN>];
-  const uint16_t* xrow = xtok >= 0 ? a.x + (size_t)xtok * D_MODEL : nullptr;
-  // A-row r -> LDS row (r < 16 ? 16w + r : 64 + 16w + r - 16): gate and up of the same n
-  const int ar = lane & 31;
-  const int arow = (ar < 16) ? (16 * wave + ar) : (64 + 16 * wave + ar - 16);
-  f32x16 acc[MF_TT<BN>] = {};
-  mfma_kloop<FMT, BN>(acc, sm, wq, wrow, xrow, true, D_MODEL, arow);
-  // acc[tt][4i+j] = A-row 8i + 4(lane/32) + j, token 32tt + lane%32:
-  // gate for i in {0,1}, the matching up at i+2.
+  QMat q[RB];
+  size_t wrow[RB];
+  if constexpr (RB == 2) {
+    q[0] = G;
+    q[1] = Uq;
+    wrow[0] = wrow[1] = (size_t)mat * D_FF + n0 + 32 * wave + c;
+  } else {
+    q[0] = sel_qmat(c < 16, G, Uq);
+    wrow[0] = (size_t)mat * D_FF + n0 + 16 * wave + (c & 15);
+  }
+  const int xtok = sm.tok[min(tid / MF_XT<BN>, it.cnt - 1)];
+  const uint16_t* xsrc = a.x + (size_t)xtok * D_MODEL + MF_XK<BN> * (tid % MF_XT<BN>);
+  f32x16 acc[RB][MF_TT<BN>] = {};
+  mf_kloop<FMT, BN, RB, MF_NS_UP<FMT, BN>>(acc, sm, q, wrow, xsrc, true, D_MODEL);
+  // acc[b][tt][4i+j] = row 8i + 4h + j of block b, token 32tt + c.  The gate
+  // value of a lane's output (block 0 / rows below 16) sits at gi, its up at ui.
   const float tsg = (FMT == FMT_NVFP4) ? G.ts[mat] : 1.f;
   const float tsu = (FMT == FMT_NVFP4) ? Uq.ts[mat] : 1.f;
+  constexpr int NI = (RB == 2) ? 4 : 2;  // groups of 4 outputs per lane and token block
 #pragma unroll
   for (int tt = 0; tt < MF_TT<BN>; ++tt) {
-    const int hrow = sm.row[32 * tt + ar];
+    const int hrow = sm.row[32 * tt + c];
     if (hrow < 0) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NI; ++i) {
       uint16_t hv[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) hv[j] = h_store<FMT>(silu_mul(acc[tt][4 * i + j] * tsg, acc[tt][4 * (i + 2) + j] * tsu));
-      const int n = n0 + 16 * wave + 8 * i + 4 * (lane >> 5);
+      for (int j = 0; j < 4; ++j) {
+        const float g = (RB == 2) ? acc[0][tt][4 * i + j] : acc[0][tt][4 * i + j];
+        const float u = (RB == 2) ? acc[RB - 1][tt][4 * i + j] : acc[0][tt][4 * (i + 2) + j];
+        hv[j] = h_store<FMT>(silu_mul(g * tsg, u * tsu));
+      }
+      const int n = n0 + 32 * RB / 2 * wave + 8 * i + 4 * h;
       uint2 pk;
       pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
       pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
@@ -828,28 +843,34 @@ __device__ void mfma_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int m
   __syncthreads();  // tables and tiles are reused by the next item
 }
 
-// down item: 128 rows (r0 ..) x BN tokens, K = 512.
+// down item: DN_ROWS rows (r0 ..) x BN tokens, K = 512.
 template <int FMT, int BN>
 __device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const ItemTok& it, int r0, FfnSmem<BN>& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, c = lane & 31;
   mfma_tables(a, it, sm);
   __syncthreads();
-  const size_t wrow = (size_t)mat * D_MODEL + r0 + (tid >> 1);
-  const int hrow_x = sm.row[tid / MF_XT<BN>];
-  const uint16_t* xrow = hrow_x >= 0 ? a.h + (size_t)hrow_x * D_FF : nullptr;
-  const int ar = lane & 31;
-  f32x16 acc[MF_TT<BN>] = {};
-  mfma_kloop<FMT, BN>(acc, sm, D, wrow, xrow, false, D_FF, 32 * wave + ar);
+  const QMat q[2] = {D, D};
+  const size_t wr = (size_t)mat * D_MODEL + r0 + 64 * wave + c;
+  const size_t wrow[2] = {wr, wr + 32};
+  const int hrow_x = sm.row[min(tid / MF_XT<BN>, it.cnt - 1)];
+  const uint16_t* xsrc = a.h + (size_t)hrow_x * D_FF + MF_XK<BN> * (tid % MF_XT<BN>);
+  f32x16 acc[2][MF_TT<BN>] = {};
+  mf_kloop<FMT, BN, 2, MF_NS_DN<FMT, BN>>(acc, sm, q, wrow, xsrc, false, D_FF);
   const float ts = (FMT == FMT_NVFP4) ? D.ts[mat] : 1.f;
 #pragma unroll
   for (int tt = 0; tt < MF_TT<BN>; ++tt) {
-    const int yrow = sm.row[32 * tt + ar];
+    const int yrow = sm.row[32 * tt + c];
     if (yrow < 0) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = r0 + 32 * wave + 8 * i + 4 * (lane >> 5);
-      *reinterpret_cast<float4*>(a.y + (size_t)yrow * D_MODEL + r) =
-          make_float4(acc[tt][4 * i] * ts, acc[tt][4 * i + 1] * ts, acc[tt][4 * i + 2] * ts, acc[tt][4 * i + 3] * ts);
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 64 * wave + 32 * b + 8 * i + 4 * h;
+        *reinterpret_cast<float4*>(a.y + (size_t)yrow * D_MODEL + r) =
+            make_float4(acc[b][tt][4 * i] * ts, acc[b][tt][4 * i + 1] * ts, acc[b][tt][4 * i + 2] * ts,
+                        acc[b][tt][4 * i + 3] * ts);
+      }
     }
   }
   __syncthreads();
@@ -858,9 +879,9 @@ __device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const Item
 // ======================================================================================
 // Persistent kernels
 // ======================================================================================
-// Workgroups per CU the persistent kernels are compiled for: two for the 4-bit
-// formats (their rings fit in half the register file), one for bf16.
-template <int FMT> constexpr int FFN_WG_PER_CU = (FMT == FMT_BF16) ? 1 : 2;
+// Workgroups per CU the persistent kernels are compiled for: two (their rings
+// and tiles fit in half the register file).
+template <int FMT> constexpr int FFN_WG_PER_CU = 2;
 
 // LDS of the persistent kernels: the matrix-core tiles (BN tokens wide) only
 // where the batch can have them (BN > 0: T >= MFMA_MIN), since their double
@@ -878,30 +899,33 @@ template <> struct FfnKernelSmem<0> {
 // Matrix-core items in an XCD-aware order.  Workgroups are dispatched to the 8
 // XCDs round-robin by blockIdx, and workgroup c takes items c, c + gridDim.x,
 // ... (gridDim.x a multiple of 8), so item i runs on XCD i % 8.  In groups of 8
-// tiles, position i = 64 g + 8 ch + tl holds row chunk ch of tile 8 g + tl:
-// the 8 chunks of a tile run on one XCD at about the same time and read its
+// tiles of C items, position i = 8 C g + 8 ch + tl holds item ch of tile 8 g + tl:
+// the items of a tile run on one XCD at about the same time and read its
 // activation tile through that XCD's L2 instead of once per XCD.
-__device__ inline int mf_item(int i, int n) {
-  if (i >= (n / 64) * 64) return i;
-  const int g = i >> 6, ch = (i >> 3) & 7, tl = i & 7;
-  return (8 * g + tl) * 8 + ch;
+__device__ inline int mf_item(int i, int n, int C) {
+  const int G = 8 * C;
+  if (i >= (n / G) * G) return i;
+  const int g = i / G, r = i % G, ch = r >> 3, tl = r & 7;
+  return (8 * g + tl) * C + ch;
 }
-static_assert(N_UP_CHUNKS == 8 && N_DN_CHUNKS == 8, "mf_item assumes 8 row chunks per tile");
 
 // Items of the matrix-core path come first; the vector-path chunks follow.
 template <int FMT, int BN>
 __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_up_kernel(LayerArgs a) {
   __shared__ FfnKernelSmem<BN> sm;
+  // matrix-core items: mf_up_chunks(BN) per tile; vector-path items: N_UP_CHUNKS per tile
   const int n_all = a.ctl[CTL_N_UP], n_mf = a.ctl[CTL_N_UP_MF];
+  constexpr int UC = (BN > 0) ? mf_up_chunks(BN) : 1;
+  const int base = (n_mf / UC) * N_UP_CHUNKS;
   if constexpr (BN > 0) {
     for (int i = blockIdx.x; i < n_mf; i += gridDim.x) {
-      const Item item = fetch_item(a.tiles, mf_item(i, n_mf), N_UP_CHUNKS);
+      const Item item = fetch_item(a.tiles, mf_item(i, n_mf, UC), UC);
       const bool sh = item_shared(item.head);
       mfma_up<FMT, BN>(a, sel_qmat(sh, a.sh_gate, a.gate), sel_qmat(sh, a.sh_up, a.up), sh ? 0 : item_expert(item.head),
-                   item_tokens(item), item_chunk(item.head) * UP_ROWS, sm.mf);
+                       item_tokens(item), item_chunk(item.head) * (D_FF / UC), sm.mf);
     }
   }
-  up_stream<FMT>(a, n_mf, n_all - n_mf, sm.gv);
+  up_stream<FMT>(a, base, n_all - base, sm.gv);
 }
 
 template <int FMT, int BN>
@@ -910,13 +934,10 @@ __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_down_kernel(Layer
   const int n_all = a.ctl[CTL_N_DN], n_mf = a.ctl[CTL_N_DN_MF];
   if constexpr (BN > 0) {
     for (int i = blockIdx.x; i < n_mf; i += gridDim.x) {
-      const Item item = fetch_item(a.tiles, mf_item(i, n_mf), N_DN_CHUNKS);
+      const Item item = fetch_item(a.tiles, mf_item(i, n_mf, N_DN_CHUNKS), N_DN_CHUNKS);
       const bool sh = item_shared(item.head);
-      const ItemTok it = item_tokens(item);
-      const int r0 = item_chunk(item.head) * DN_ROWS;
-#pragma unroll 1
-      for (int rb = 0; rb < DN_ROWS; rb += 128)
-        mfma_down<FMT, BN>(a, sel_qmat(sh, a.sh_down, a.down), sh ? 0 : item_expert(item.head), it, r0 + rb, sm.mf);
+      mfma_down<FMT, BN>(a, sel_qmat(sh, a.sh_down, a.down), sh ? 0 : item_expert(item.head), item_tokens(item),
+                         item_chunk(item.head) * DN_ROWS, sm.mf);
     }
   }
   down_stream<FMT>(a, n_mf, n_all - n_mf, sm.gv);

@@ -292,9 +292,10 @@ template <typename PermAt>
 __device__ void write_lists(const LayerArgs& a, const int* bcnt, const int* boff, ListSmem& ls, PermAt perm_at) {
   const int tid = threadIdx.x, nth = blockDim.x;
   const int E = a.E, K = a.K, T = a.T;
-  // work list: matrix-core tiles first, then vector tiles.  Gate/up item i is
-  // row chunk i % N_UP_CHUNKS of tile i / N_UP_CHUNKS, down item i chunk
-  // i % N_DN_CHUNKS of tile i / N_DN_CHUNKS.
+  // work list: matrix-core tiles first, then vector tiles.  A matrix-core tile
+  // makes mf_up_chunks(bn) gate/up items and N_DN_CHUNKS down items, a vector tile
+  // N_UP_CHUNKS and N_DN_CHUNKS; item i of a kind is chunk i % chunks of its
+  // tile i / chunks (vector items counted from the first vector tile).
   const int bn = mfma_bn(T);
   for (int e = tid; e < E; e += nth) {
     const int m = bcnt[e];
@@ -325,8 +326,8 @@ __device__ void write_lists(const LayerArgs& a, const int* bcnt, const int* boff
   if (tid == 0) {
     a.ctl[CTL_N_UP] = n_up;
     a.ctl[CTL_N_DN] = n_dn;
-    a.ctl[CTL_N_UP_MF] = min(mf_tiles * N_UP_CHUNKS, n_up);
-    a.ctl[CTL_N_DN_MF] = min(mf_tiles * N_DN_CHUNKS, n_dn);
+    a.ctl[CTL_N_UP_MF] = min(mf_tiles, n_tiles) * mf_up_chunks(bn);
+    a.ctl[CTL_N_DN_MF] = min(mf_tiles, n_tiles) * N_DN_CHUNKS;
   }
   // one thread per token tile: its entry (row chunk 0; the kernels derive the
   // chunk from the item index)
