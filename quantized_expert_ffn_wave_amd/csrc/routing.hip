@@ -315,11 +315,14 @@ __device__ void write_lists(const LayerArgs& a, const int* bcnt, const int* boff
   const int tiles_m = ls.tot[0], tiles_g = ls.tot[1];
   // The shared expert takes every token: bn-token matrix-core tiles from
   // MFMA_MIN tokens on, else groups of GV_GROUP tokens, in the same lists.
-  // Tile order: routed matrix-core, shared matrix-core, routed vector, shared
-  // vector (the kernels take the matrix-core items first).
+  // Tile order: routed matrix-core, shared matrix-core, shared vector, routed
+  // vector (the kernels take the matrix-core items first; the shared expert's
+  // vector items, which mostly read its weights from L2, go before the routed
+  // ones so that they do not fall into the last, partial round).
   const int sh_tiles = a.n_shared ? bucket_tiles(T, bn) : 0;
   const bool sh_mf = bucket_mfma(T);
   const int mf_tiles = tiles_m + (sh_mf ? sh_tiles : 0);
+  const int sh_vec = sh_mf ? 0 : sh_tiles;
   const int all_tiles = tiles_m + tiles_g + sh_tiles;
   const int n_tiles = min(all_tiles, a.max_tiles);
   const int n_up = n_tiles * N_UP_CHUNKS, n_dn = n_tiles * N_DN_CHUNKS;
@@ -332,20 +335,20 @@ __device__ void write_lists(const LayerArgs& a, const int* bcnt, const int* boff
   // one thread per token tile: its entry (row chunk 0; the kernels derive the
   // chunk from the item index)
   for (int ti = tid; ti < n_tiles; ti += nth) {
-    const bool shared = (ti >= tiles_m && ti < mf_tiles) || ti >= mf_tiles + tiles_g;
+    const bool shared = (ti >= tiles_m && ti < mf_tiles + sh_vec);
     const bool mf = ti < mf_tiles;
     const int per = mf ? bn : GV_GROUP;
     int expert, p0, cnt;
     uint32_t tk[GV_GROUP] = {0u, 0u, 0u, 0u};
     if (shared) {
-      const int tile = mf ? ti - tiles_m : ti - mf_tiles - tiles_g;
+      const int tile = mf ? ti - tiles_m : ti - mf_tiles;
       expert = SHARED_ID;
       p0 = tile * per;
       cnt = min(per, T - p0);
       for (int j = 0; j < cnt && j < GV_GROUP; ++j) tk[j] = (uint32_t)(p0 + j);
     } else {
       const int* o = mf ? ls.it_m : ls.it_g;
-      const int li = mf ? ti : ti - mf_tiles;
+      const int li = mf ? ti : ti - mf_tiles - sh_vec;
       int lo = 0, hi = E;  // the expert e with o[e] <= li < o[e+1]
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -436,10 +439,10 @@ __global__ __launch_bounds__(BK_THREADS) void chunk_scan_kernel(LayerArgs a) {
   for (int i = tid; i < nch * E; i += BK_THREADS) tab[i] += off[i % E];
   write_lists(a, cnt, off, ls, [](int) { return 0; });
   // first vector-path tile of each expert (tile order: routed matrix-core,
-  // shared matrix-core, routed vector, shared vector)
-  const int sh_mf = (a.n_shared && bucket_mfma(a.T)) ? bucket_tiles(a.T, mfma_bn(a.T)) : 0;
+  // shared matrix-core, shared vector, routed vector)
+  const int sh_all = a.n_shared ? bucket_tiles(a.T, mfma_bn(a.T)) : 0;  // matrix-core or vector, first either way
   int32_t* vt = tab + (size_t)nch * E;
-  for (int e = tid; e < E; e += BK_THREADS) vt[e] = bucket_mfma(cnt[e]) ? -1 : ls.tot[0] + sh_mf + ls.it_g[e];
+  for (int e = tid; e < E; e += BK_THREADS) vt[e] = bucket_mfma(cnt[e]) ? -1 : ls.tot[0] + sh_all + ls.it_g[e];
 }
 
 __global__ __launch_bounds__(BK_THREADS) void chunk_perm_kernel(LayerArgs a) {
