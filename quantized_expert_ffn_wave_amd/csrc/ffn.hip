@@ -479,15 +479,18 @@ __device__ inline float upper_half(float v) {
 }
 
 // gate/up + SwiGLU over the vector-path items base + c, c in [0, n), this
-// workgroup taking c = blockIdx.x, +gridDim.x, ...
+// workgroup taking c = (blockIdx.x - rot) mod gridDim.x, + gridDim.x, ...  The
+// kernels rotate by their matrix-core item count, so that the workgroups which
+// took a (heavier) matrix-core item are the last to get a vector item of the
+// partial round.
 template <int FMT>
-__device__ void up_stream(const LayerArgs& a, int base, int n, MvSmem& sm) {
+__device__ void up_stream(const LayerArgs& a, int base, int n, int rot, MvSmem& sm) {
   using G = GV<FMT>;
   constexpr int CH = N_UP_CHUNKS;
   constexpr int D = MV_UP_RING<FMT>, NU = MV_UP_UNITS;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 3, b = lane >> 2;
-  int c = blockIdx.x;
+  int c = (int)((blockIdx.x + gridDim.x - rot) % gridDim.x);
   if (c >= n) return;
   Item item = fetch_item(a.tiles, base + c, CH);
   ItemTok it = item_tokens(item);
@@ -569,13 +572,13 @@ __device__ void up_stream(const LayerArgs& a, int base, int n, MvSmem& sm) {
 // down over vector-path chunks, workgroup-strided as up_stream: load u of a
 // chunk covers rows first_row + 4 u + j over the whole K = 512 (chunk b per lane)
 template <int FMT>
-__device__ void down_stream(const LayerArgs& a, int base, int n, MvSmem& sm) {
+__device__ void down_stream(const LayerArgs& a, int base, int n, int rot, MvSmem& sm) {
   using G = GV<FMT>;
   constexpr int CH = N_DN_CHUNKS;
   constexpr int D = MV_DN_RING<FMT>, NU = MV_DN_UNITS;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 3, b = lane >> 2;
-  int c = blockIdx.x;
+  int c = (int)((blockIdx.x + gridDim.x - rot) % gridDim.x);
   if (c >= n) return;
   Item item = fetch_item(a.tiles, base + c, CH);
   ItemTok it = item_tokens(item);
@@ -925,7 +928,7 @@ __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_up_kernel(LayerAr
                        item_tokens(item), item_chunk(item.head) * (D_FF / UC), sm.mf);
     }
   }
-  up_stream<FMT>(a, base, n_all - base, sm.gv);
+  up_stream<FMT>(a, base, n_all - base, n_mf % gridDim.x, sm.gv);
 }
 
 template <int FMT, int BN>
@@ -940,7 +943,7 @@ __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_down_kernel(Layer
                          item_chunk(item.head) * DN_ROWS, sm.mf);
     }
   }
-  down_stream<FMT>(a, n_mf, n_all - n_mf, sm.gv);
+  down_stream<FMT>(a, n_mf, n_all - n_mf, n_mf % gridDim.x, sm.gv);
 }
 
 // Workgroups of `kernel` that fit on one CU at once (the persistent kernels are
