@@ -8,8 +8,9 @@
 // the chosen experts) is this library's reading of that statement.
 //
 // Kernel boundaries order the steps (no device-scope fences):
-//   router        partial logits part[ks][t][e] over 8 K-splits (MFMA 16x16x32 bf16);
-//   topk          one wave per token sums the 8 partials in split order, selects
+//   router        partial logits part[ks][t][e] over 8 K-splits, or 4 beyond 256
+//                 tokens (MFMA 16x16x32 bf16);
+//   topk          one wave per token sums the partials in split order, selects
 //                 the top k (ties to the lower id: wave-wide maxima of 32-bit
 //                 order-preserving keys with permlane swaps and DPP, then a
 //                 ballot) and writes the weights;
@@ -24,10 +25,15 @@ namespace moe {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int ROUTER_KR = 256;                  // K range per split
+constexpr int ROUTER_KR = 256;                  // K range per split (T <= ROUTER_SMALL_T)
 constexpr int ROUTER_KS = D_MODEL / ROUTER_KR;  // 8 splits
 constexpr int ROUTER_SMALL_T = 256;             // largest T for one 16-token tile per wave
-constexpr int ROUTER_TG = 256;                  // tokens per workgroup on the large-T path
+constexpr int ROUTER_KS_L = 4;                  // K-splits for larger T
+constexpr int ROUTER_KR_L = D_MODEL / ROUTER_KS_L;
+constexpr int ROUTER_TG = 64;                   // tokens per workgroup for larger T
+constexpr int ROUTER_XS = ROUTER_KR_L + 8;      // LDS row stride of the staged activations
+// partial logit splits the top-k sums for a batch of T tokens
+__host__ __device__ inline int router_splits(int T) { return T <= ROUTER_SMALL_T ? ROUTER_KS : ROUTER_KS_L; }
 
 // Decode-sized T: one wave per (16-token tile, 16-expert tile, K-split); the
 // workgroup's 4 waves take 4 consecutive expert tiles.  grid (ceil(T/16) *
@@ -65,46 +71,52 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
   }
 }
 
-// Large T: a wave keeps its 16 router rows x 256 k in registers and loops over
-// the 16-token tiles of a ROUTER_TG-token group, loading the next tile's
-// activations while the current one is multiplied.
-// grid (ceil(E/64), ROUTER_KS, ceil(T/ROUTER_TG)).
-__global__ __launch_bounds__(256) void router_large_kernel(const uint16_t* __restrict__ x,
-                                                           const uint16_t* __restrict__ wr,
-                                                           const float* __restrict__ bias, float* __restrict__ part,
-                                                           int T, int E) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e0 = (blockIdx.x * 4 + wave) * 16;
-  if (e0 >= E) return;
-  const int ks = blockIdx.y;
-  const int kbase = ks * ROUTER_KR + 8 * (lane >> 4);
-  const int col = lane & 15;
-  bf16x8 b[ROUTER_KR / 32];
-  const uint16_t* wrow = wr + (size_t)(e0 + col) * D_MODEL + kbase;
+// Larger T: one 1024-thread workgroup per (64-token group, K-split of 512).
+// Wave w keeps router rows 16 w .. 16 w + 15 of the split in registers, so the
+// 16 waves cover 256 experts, and the 16-token activation tiles are staged once
+// in LDS for all of them (double buffered, one barrier per tile): the
+// activations are read once, not once per group of experts.
+// grid (ceil(T/ROUTER_TG), ROUTER_KS_L).
+__global__ __launch_bounds__(1024) void router_large_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ wr,
+                                                            const float* __restrict__ bias, float* __restrict__ part,
+                                                            int T, int E) {
+  __shared__ uint16_t xs[2][16 * ROUTER_XS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ks = blockIdx.y, k0 = ks * ROUTER_KR_L;
+  const int col = lane & 15, kq = lane >> 4;
+  const int e = 16 * wave + col;  // this lane's expert (B column / output column)
+  const bool ev = e < E;
+  bf16x8 b[ROUTER_KR_L / 32];
+  const uint16_t* wrow = wr + (size_t)(ev ? e : 0) * D_MODEL + k0 + 8 * kq;
 #pragma unroll
-  for (int s = 0; s < ROUTER_KR / 32; ++s) b[s] = *reinterpret_cast<const bf16x8*>(wrow + 32 * s);
-  const float bz = (ks == 0 && bias) ? bias[e0 + col] : 0.f;  // the bias rides in split 0
-  const int tg0 = blockIdx.z * ROUTER_TG, tg1 = min(T, tg0 + ROUTER_TG);
-  auto load_tile = [&](bf16x8* a, int t0) {
-    const int t = t0 + col;
-    const uint16_t* xrow = x + (size_t)(t < T ? t : T - 1) * D_MODEL + kbase;
-#pragma unroll
-    for (int s = 0; s < ROUTER_KR / 32; ++s) a[s] = *reinterpret_cast<const bf16x8*>(xrow + 32 * s);
+  for (int s = 0; s < ROUTER_KR_L / 32; ++s) b[s] = *reinterpret_cast<const bf16x8*>(wrow + 32 * s);
+  const float bz = (ks == 0 && bias && ev) ? bias[e] : 0.f;  // the bias rides in split 0
+  const int tg0 = blockIdx.x * ROUTER_TG, tg1 = min(T, tg0 + ROUTER_TG);
+  // staging: thread tid holds 8 activations (16 B) of row tid / 64 of a tile
+  const int sr = tid >> 6, sc = 8 * (tid & 63);
+  auto stage_load = [&](int t0) {
+    return *reinterpret_cast<const bf16x8*>(x + (size_t)min(t0 + sr, T - 1) * D_MODEL + k0 + sc);
   };
-  bf16x8 a[ROUTER_KR / 32], an[ROUTER_KR / 32];
-  load_tile(a, tg0);
+  bf16x8 v = stage_load(tg0);
+  int buf = 0;
   for (int t0 = tg0; t0 < tg1; t0 += 16) {
-    load_tile(an, (t0 + 16 < tg1) ? t0 + 16 : t0);  // always issued; the last one repeats the tile
+    *reinterpret_cast<bf16x8*>(&xs[buf][sr * ROUTER_XS + sc]) = v;
+    __syncthreads();
+    v = stage_load(min(t0 + 16, tg1 - 1));  // always issued; the last one is not stored
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < ROUTER_KR / 32; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[s], acc, 0, 0, 0);
+    for (int s = 0; s < ROUTER_KR_L / 32; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&xs[buf][col * ROUTER_XS + 32 * s + 8 * kq]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[s], acc, 0, 0, 0);
+    }
+    // acc[j] = token t0 + 4 kq + j, expert e
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int tt = t0 + 4 * (lane >> 4) + j;
-      if (tt < T) part[((size_t)ks * T + tt) * E + e0 + col] = acc[j] + bz;
+      const int tt = t0 + 4 * kq + j;
+      if (tt < tg1 && ev) part[((size_t)ks * T + tt) * E + e] = acc[j] + bz;
     }
-#pragma unroll
-    for (int s = 0; s < ROUTER_KR / 32; ++s) a[s] = an[s];
+    buf ^= 1;
   }
 }
 
@@ -113,8 +125,9 @@ hipError_t launch_router(const LayerArgs& a, hipStream_t s) {
     dim3 grid(ceil_div(a.T, 16) * ceil_div(a.E, 64), ROUTER_KS);
     hipLaunchKernelGGL(router_small_kernel, grid, dim3(256), 0, s, a.x, a.router_w, a.router_b, a.logit_part, a.T, a.E);
   } else {
-    dim3 grid(ceil_div(a.E, 64), ROUTER_KS, ceil_div(a.T, ROUTER_TG));
-    hipLaunchKernelGGL(router_large_kernel, grid, dim3(256), 0, s, a.x, a.router_w, a.router_b, a.logit_part, a.T, a.E);
+    dim3 grid(ceil_div(a.T, ROUTER_TG), ROUTER_KS_L);
+    hipLaunchKernelGGL(router_large_kernel, grid, dim3(1024), 0, s, a.x, a.router_w, a.router_b, a.logit_part, a.T,
+                       a.E);
   }
   return hipGetLastError();
 }
@@ -161,19 +174,20 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
-// One wave: logits of token t (sum of the 8 partials in split order + bias),
+// One wave: logits of token t (sum of the KS partials in split order + bias),
 // the top k ids and their weights.
+template <int KS>
 __device__ void topk_token(const LayerArgs& a, int t, int32_t* lds_ids) {
   const int lane = threadIdx.x & 63;
   const int T = a.T, E = a.E, K = a.K;
   // all 8 x 4 partial sums in flight at once (lanes past E read a valid
   // entry and are masked below); the bias is already in split 0
-  float p[4][ROUTER_KS];
+  float p[4][KS];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = min(lane + 64 * i, E - 1);
 #pragma unroll
-    for (int ks = 0; ks < ROUTER_KS; ++ks) p[i][ks] = a.logit_part[((size_t)ks * T + t) * E + e];
+    for (int ks = 0; ks < KS; ++ks) p[i][ks] = a.logit_part[((size_t)ks * T + t) * E + e];
   }
   uint32_t kk[4];
   float mx = -INFINITY;
@@ -183,7 +197,7 @@ __device__ void topk_token(const LayerArgs& a, int t, int32_t* lds_ids) {
     const int e = lane + 64 * i;
     float s = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < ROUTER_KS; ++ks) s += p[i][ks];
+    for (int ks = 0; ks < KS; ++ks) s += p[i][ks];
     kk[i] = 0u;
     v[i] = -INFINITY;
     if (e < E) {
@@ -371,9 +385,11 @@ __device__ void write_lists(const LayerArgs& a, const int* bcnt, const int* boff
   }
 }
 
+// KS: the router's partial splits for this batch size (router_splits(T))
+template <int KS>
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayerArgs a) {
   const int t = blockIdx.x * (TK_THREADS / 64) + (threadIdx.x >> 6);
-  if (t < a.T) topk_token(a, t, nullptr);
+  if (t < a.T) topk_token<KS>(a, t, nullptr);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -506,7 +522,7 @@ __global__ __launch_bounds__(RS_THREADS) void route_small_kernel(LayerArgs a) {
   const int E = a.E, K = a.K, T = a.T, S = a.S;
   const int W = ceil_div(T, 32);
   if (TOPK) {  // one wave per token
-    for (int t = wave; t < T; t += RS_THREADS / 64) topk_token(a, t, sm.ids);
+    for (int t = wave; t < T; t += RS_THREADS / 64) topk_token<ROUTER_KS>(a, t, sm.ids);
   } else {
     for (int s = tid; s < S; s += nth) sm.ids[s] = a.ids[s];
   }
@@ -550,7 +566,9 @@ __global__ __launch_bounds__(RS_THREADS) void route_small_kernel(LayerArgs a) {
 // top-k (with the buckets too, for up to RS_FUSED_T tokens)
 hipError_t launch_topk(const LayerArgs& a, hipStream_t s) {
   if (a.T <= RS_FUSED_T) hipLaunchKernelGGL(route_small_kernel<true>, dim3(1), dim3(RS_THREADS), 0, s, a);
-  else hipLaunchKernelGGL(topk_kernel, dim3(ceil_div(a.T, TK_THREADS / 64)), dim3(TK_THREADS), 0, s, a);
+  else if (router_splits(a.T) == ROUTER_KS)
+    hipLaunchKernelGGL(topk_kernel<ROUTER_KS>, dim3(ceil_div(a.T, TK_THREADS / 64)), dim3(TK_THREADS), 0, s, a);
+  else hipLaunchKernelGGL(topk_kernel<ROUTER_KS_L>, dim3(ceil_div(a.T, TK_THREADS / 64)), dim3(TK_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
