@@ -101,6 +101,7 @@ def test_prefill_t4096_bf16(bf16_layer):
     (32, 6, 0, 1, 1.0, "q4_1", 21),
     (32, 6, 1, 0, 2.5, "nvfp4", 19),
     (16, 6, 1, 1, 1.0, "bf16", 70),
+    (32, 6, 1, 1, 1.0, "q4_1", 300),  # large-batch router and chunked buckets with fewer experts than waves
 ])
 def test_layer_options(E, k, n_shared, renorm, scale, fmt, T):
     say(f"case options E={E} k={k} shared={n_shared} renorm={renorm} scale={scale} {fmt} T={T}")
