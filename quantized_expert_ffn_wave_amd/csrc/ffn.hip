@@ -478,19 +478,44 @@ __device__ inline float upper_half(float v) {
   return __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false)[1]);
 }
 
+// Order of the vector-path items c in [0, n) over the G workgroups, given that
+// workgroups 0 .. m-1 first took matrix-core items (each worth about two vector
+// items at the batch sizes that have both): the first P = R (G - m) items go
+// round-robin to the other G - m workgroups only (R rounds), the rest to all
+// workgroups round-robin.  With no matrix-core items this is c = blockIdx.x,
+// + G, ...
+struct VecOrder {
+  int G, m, P;
+  __device__ VecOrder(int n_mf) {
+    G = (int)gridDim.x;
+    m = min(n_mf, G);
+    const int R = (n_mf > 0 && m < G) ? 2 * ceil_div(n_mf, G) : 0;
+    P = R * (G - m);
+  }
+  __device__ int first() const {
+    const int w = (int)blockIdx.x;
+    return (w >= m && P > 0) ? w - m : P + w;
+  }
+  __device__ int next(int c) const {
+    if (c < P) {
+      const int nc = c + (G - m);
+      return nc < P ? nc : P + (int)blockIdx.x;
+    }
+    return c + G;
+  }
+};
+
 // gate/up + SwiGLU over the vector-path items base + c, c in [0, n), this
-// workgroup taking c = (blockIdx.x - rot) mod gridDim.x, + gridDim.x, ...  The
-// kernels rotate by their matrix-core item count, so that the workgroups which
-// took a (heavier) matrix-core item are the last to get a vector item of the
-// partial round.
+// workgroup taking its items in VecOrder.
 template <int FMT>
-__device__ void up_stream(const LayerArgs& a, int base, int n, int rot, MvSmem& sm) {
+__device__ void up_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem& sm) {
   using G = GV<FMT>;
   constexpr int CH = N_UP_CHUNKS;
   constexpr int D = MV_UP_RING<FMT>, NU = MV_UP_UNITS;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 3, b = lane >> 2;
-  int c = (int)((blockIdx.x + gridDim.x - rot) % gridDim.x);
+  const VecOrder order(n_mf);
+  int c = order.first();
   if (c >= n) return;
   Item item = fetch_item(a.tiles, base + c, CH);
   ItemTok it = item_tokens(item);
@@ -520,7 +545,7 @@ __device__ void up_stream(const LayerArgs& a, int base, int n, int rot, MvSmem& 
   const int my_t = ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
 #pragma unroll 1
   for (;;) {
-    const int nc = c + gridDim.x;
+    const int nc = order.next(c);
     const bool has_next = nc < n;
     Item nitem = item;
     ItemTok nit = it;
@@ -569,16 +594,17 @@ __device__ void up_stream(const LayerArgs& a, int base, int n, int rot, MvSmem& 
   }
 }
 
-// down over vector-path chunks, workgroup-strided as up_stream: load u of a
+// down over vector-path chunks, ordered and loaded as in up_stream: load u of a
 // chunk covers rows first_row + 4 u + j over the whole K = 512 (chunk b per lane)
 template <int FMT>
-__device__ void down_stream(const LayerArgs& a, int base, int n, int rot, MvSmem& sm) {
+__device__ void down_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem& sm) {
   using G = GV<FMT>;
   constexpr int CH = N_DN_CHUNKS;
   constexpr int D = MV_DN_RING<FMT>, NU = MV_DN_UNITS;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 3, b = lane >> 2;
-  int c = (int)((blockIdx.x + gridDim.x - rot) % gridDim.x);
+  const VecOrder order(n_mf);
+  int c = order.first();
   if (c >= n) return;
   Item item = fetch_item(a.tiles, base + c, CH);
   ItemTok it = item_tokens(item);
@@ -605,7 +631,7 @@ __device__ void down_stream(const LayerArgs& a, int base, int n, int rot, MvSmem
   const int my_t = ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
 #pragma unroll 1
   for (;;) {
-    const int nc = c + gridDim.x;
+    const int nc = order.next(c);
     const bool has_next = nc < n;
     Item nitem = item;
     ItemTok nit = it;
@@ -928,7 +954,7 @@ __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_up_kernel(LayerAr
                        item_tokens(item), item_chunk(item.head) * (D_FF / UC), sm.mf);
     }
   }
-  up_stream<FMT>(a, base, n_all - base, n_mf % gridDim.x, sm.gv);
+  up_stream<FMT>(a, base, n_all - base, n_mf, sm.gv);
 }
 
 template <int FMT, int BN>
@@ -943,7 +969,7 @@ __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_down_kernel(Layer
                          item_chunk(item.head) * DN_ROWS, sm.mf);
     }
   }
-  down_stream<FMT>(a, n_mf, n_all - n_mf, n_mf % gridDim.x, sm.gv);
+  down_stream<FMT>(a, n_mf, n_all - n_mf, n_mf, sm.gv);
 }
 
 // Workgroups of `kernel` that fit on one CU at once (the persistent kernels are
