@@ -16,6 +16,18 @@ width 512, d_model 2048, top-6, near-uniform routing).  Steps rotate over
 so that every step reads its expert weights from HBM, not from the 256 MB
 last-level cache.
 
+The 47-layer workload (`--workload stack47_decode_t32_q4_1_zipf0.8`) times the
+pre-norm residual stack instead: a step is 32 tokens through all 47 layers
+(23.75 GB of q4_1 weights resident), replayed as one captured graph from the
+same input each time; its roofline entry times the gate/up kernel of every
+layer on the layer inputs the stack produced.
+
+Also measured, outside the timed steps: the attainable HBM read rate (a plain
+streaming read of 4 GiB through the library's moe_stream_read, best of a few
+launch shapes), the spread of single graph replays (p10/p50/p90), and for the
+64-token q4_1 workload a token-count sweep 1, 2, 4, ..., 256 with the same
+generator (`--no-sweep` skips it).
+
 Prints one JSON line: tokens/s (the metric), the achieved HBM bandwidth on the
 expert-weight bytes the step touches, a roofline entry for the dominant kernel
 (gate/up + SwiGLU) timed with HIP events on the library's stream, and the CPU
@@ -35,6 +47,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
+STREAM_BYTES = 4 << 30
+SWEEP_T = [1, 2, 4, 8, 16, 32, 64, 128, 256]
+STACK_EPS = 1e-6
 
 
 def log(msg: str) -> None:
@@ -68,39 +83,68 @@ def read_traffic(workload: str):
         return None
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_t64_q4_1")
-    ap.add_argument("--layers", type=int, default=8, help="layer instances the steps rotate over")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true", help="time plain launches instead of HIP-graph replays")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="after timing, run a plain 1 GiB device copy (reference for HBM byte counters)")
-    args = ap.parse_args()
-
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
-              "run with --gpus 1", file=sys.stderr)
-        return 2
-
+def pct(a, q):
     import numpy as np
-    import torch
+    return round(float(np.percentile(np.asarray(a), q)), 5)
 
-    import quantized_expert_ffn_wave_amd as moe
-    import synth
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 2
+def stream_reference(moe, torch):
+    """Attainable HBM read rate: best of a few launch shapes of a plain 4 GiB read."""
+    src = torch.empty(STREAM_BYTES, dtype=torch.uint8, device="cuda")
+    src.fill_(7)
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = moe.current_stream()
+    best = None
+    for wg_per_cu in (1, 2, 4, 8):
+        grid = n_cu * wg_per_cu
+        moe.moe_stream_read(src.data_ptr(), STREAM_BYTES, sink.data_ptr(), grid, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            moe.moe_stream_read(src.data_ptr(), STREAM_BYTES, sink.data_ptr(), grid, stream)
+        e1.record()
+        torch.cuda.synchronize()
+        gbps = STREAM_BYTES * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        log(f"stream read 4 GiB, {grid} workgroups: {gbps:.0f} GB/s")
+        if best is None or gbps > best[0]:
+            best = (gbps, grid)
+    del src, sink
+    torch.cuda.empty_cache()
+    return {"gbps": round(best[0], 1), "bytes": STREAM_BYTES, "workgroups": best[1],
+            "kernel": "moe_stream_read (16 B nontemporal loads, 8 in flight per thread)"}
+
+
+def replay_spread(torch, replay, n):
+    """Per-replay durations (ms) with an event pair around each replay."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        evs[i][0].record()
+        replay(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def copy_calibration(torch):
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 3 copies of {n} bytes")
+    del src, dst
+
+
+def bench_layer(args, moe, synth, torch, np):
     cfg = synth.CONFIGS[args.workload]
-    if cfg["layers"] != 1:
-        print("bench.py times single-layer workloads", file=sys.stderr)
-        return 2
     T, fmt = cfg["T"], cfg["fmt"]
     NL = max(1, args.layers)
+    do_sweep = (not args.no_sweep) and args.workload == "decode_t64_q4_1"
+    max_tokens = max(T, SWEEP_T[-1]) if do_sweep else T
 
     log(f"generating {NL} layer instances of {args.workload}")
     t0 = time.time()
@@ -109,29 +153,33 @@ def main() -> int:
         hosts.append(synth.make_layer(seed=s, fmt=fmt, zipf=cfg["zipf"]))
         log(f"  layer {s} ready ({time.time() - t0:.1f} s)")
     x_bits = synth.make_x(T)
-    dls = [moe.DeviceLayer(h, max_tokens=T) for h in hosts]
+    dls = [moe.DeviceLayer(h, max_tokens=max_tokens) for h in hosts]
     x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
     y = torch.empty_like(x)
     ws = moe.alloc_workspace(dls[0].workspace_size(T))
     stream = moe.current_stream()
     E, K = hosts[0].E, hosts[0].k
 
-    # routing of each instance (untimed): touched experts -> algorithmic bytes
     exp_b = hosts[0].expert_bytes()
     gu_b = hosts[0].gate.nbytes() + hosts[0].up.nbytes()
-    dn_b = hosts[0].down.nbytes()
-    S = T * K
-    touched, step_w_bytes, up_bytes = [], [], []
-    for dl in dls:
-        route, bufs = moe.route_buffers(T, K, E)
-        moe.layer_forward(dl, x, y, route=route, workspace=ws)
+
+    def touched_bytes(dl, xt, wst):
+        """Routing of one instance (untimed): touched experts -> algorithmic bytes."""
+        n = xt.shape[0]
+        route, bufs = moe.route_buffers(n, K, E)
+        moe.layer_forward(dl, xt, torch.empty_like(xt), route=route, workspace=wst)
         torch.cuda.synchronize()
         U = int((bufs["counts"].cpu().numpy() > 0).sum())
-        touched.append(U)
-        step_w_bytes.append((U + 1) * exp_b)
         # gate/up launch: the gate and up matrices of the touched experts and
         # the shared one, the tokens once, the SwiGLU rows of the S + T slots
-        up_bytes.append((U + 1) * gu_b + T * 2048 * 2 + (S + T) * 512 * 2)
+        return U, (U + 1) * exp_b, (U + 1) * gu_b + n * 2048 * 2 + (n * K + n) * 512 * 2
+
+    touched, step_w_bytes, up_bytes = [], [], []
+    for dl in dls:
+        U, wb, ub = touched_bytes(dl, x, ws)
+        touched.append(U)
+        step_w_bytes.append(wb)
+        up_bytes.append(ub)
     router_b = E * 2048 * 2
 
     def step(i, events=None, on=None):
@@ -164,10 +212,9 @@ def main() -> int:
         step(args.warmup + i, handles[i])
     stop.record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms = total_ms / args.steps
+    ms = start.elapsed_time(stop) / args.steps
 
-    graph_ms = None
+    graph_ms, spread = None, None
     if not args.no_graph:
         graphs = []
         for i in range(NL):
@@ -186,6 +233,9 @@ def main() -> int:
         torch.cuda.synchronize()
         graph_ms = g0.elapsed_time(g1) / args.steps
         log(f"graph replay: {graph_ms * 1e3:.1f} us per step")
+        sp = replay_spread(torch, lambda i: graphs[i % NL].replay(), args.steps)
+        spread = {"p10": pct(sp, 10), "p50": pct(sp, 50), "p90": pct(sp, 90)}
+        del graphs
 
     stage_ms = np.array([[row[j].elapsed_time(row[j + 1]) for j in range(moe.N_STAGE_EVENTS - 1)] for row in evs])
     idx = [(args.warmup + i) % NL for i in range(args.steps)]
@@ -198,17 +248,42 @@ def main() -> int:
     stage_means = {n: round(float(v), 4) for n, v in zip(moe.STAGES, stage_ms.mean(0))}
     log(f"stage means (ms): {stage_means}")
 
+    sweep = None
+    if do_sweep:
+        sweep = []
+        x_all = torch.from_numpy(synth.make_x(SWEEP_T[-1]).view(np.int16)).cuda().view(torch.bfloat16)
+        ws_all = moe.alloc_workspace(max(dls[0].workspace_size(t) for t in SWEEP_T))
+        for t in SWEEP_T:
+            xt, yt = x_all[:t].contiguous(), torch.empty((t, 2048), dtype=torch.bfloat16, device="cuda")
+            tb = [touched_bytes(dl, xt, ws_all) for dl in dls]
+            gs = []
+            for dl in dls:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    moe.moe_layer_forward(dl.handle, xt.data_ptr(), t, yt.data_ptr(), None, ws_all.data_ptr(),
+                                          ws_all.numel(), moe.current_stream())
+                gs.append(g)
+            for i in range(args.warmup):
+                gs[i % NL].replay()
+            torch.cuda.synchronize()
+            n = max(args.steps // 2, 10)
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record()
+            for i in range(n):
+                gs[(args.warmup + i) % NL].replay()
+            a1.record()
+            torch.cuda.synchronize()
+            t_ms = a0.elapsed_time(a1) / n
+            wb = float(np.mean([tb[(args.warmup + i) % NL][1] for i in range(n)]))
+            sweep.append({"tokens": t, "us_per_step": round(t_ms * 1e3, 2), "tokens_per_s": round(t / (t_ms * 1e-3), 1),
+                          "touched_experts_mean": round(float(np.mean([u for u, _, _ in tb])), 1),
+                          "hbm_gbps_expert_weights": round(wb / (t_ms * 1e-3) / 1e9, 1)})
+            log(f"sweep T={t}: {t_ms * 1e3:.1f} us, {sweep[-1]['hbm_gbps_expert_weights']} GB/s")
+            del gs
+        del x_all, ws_all
+
     if args.copy_calibration:
-        n = 1 << 30
-        src = torch.empty(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"copy calibration: 3 copies of {n} bytes")
-        del src, dst
+        copy_calibration(torch)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -226,8 +301,14 @@ def main() -> int:
                "sample": f"{n_cpu} steps of the same workload (the full {T}-token batch through one layer "
                          f"instance each; fp64 routing and 7 experts per token), {dt:.1f} s wall"}
 
+    for d in dls:
+        d.close()
+    del dls, ws, x, y
+    torch.cuda.empty_cache()
+    stream_ref = None if args.no_stream_reference else stream_reference(moe, torch)
+
     out = {
-        "metric": "MoE-layer tokens/s + achieved HBM GB/s (% of peak), decode batch 1\u2013256, 1 GPU",
+        "metric": "MoE-layer tokens/s + achieved HBM GB/s (% of peak), decode batch 1–256, 1 GPU",
         "value": round(T / (step_ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -241,21 +322,226 @@ def main() -> int:
         "data": "synthetic",
         "hbm_gbps_expert_weights": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "hbm_frac_of_stream_read": round(gbps / stream_ref["gbps"], 4) if stream_ref else None,
+        "stream_read": stream_ref,
         "config": {"workload": f"moe_layer_{args.workload}", "tokens": T, "d_model": 2048, "routed_experts": E,
                    "top_k": K, "shared_experts": 1, "d_expert": 512, "weights": fmt, "router_bias_zipf": cfg["zipf"],
                    "layer_instances": NL, "touched_experts_mean": round(float(np.mean(touched)), 1),
                    "expert_weight_bytes_per_step": int(w_bytes), "router_bytes_per_step": router_b,
                    "launch": "hip_graph_replay" if graph_ms is not None else "plain",
-                   "plain_launch_ms_per_step": round(ms, 5), "stage_ms": stage_means},
+                   "plain_launch_ms_per_step": round(ms, 5), "graph_replay_ms": spread, "stage_ms": stage_means},
         "roofline": {"bound": "hbm", "kernel": "ffn_up_kernel (gate/up + SwiGLU)",
                      "achieved": round(up_achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(up_achieved / HBM_PEAK_GBPS, 4),
+                     "frac_of_stream_read": round(up_achieved / stream_ref["gbps"], 4) if stream_ref else None,
                      "traffic": traffic},
         "cpu_baseline": cpu,
     }
-    print(json.dumps(out), flush=True)
+    if sweep is not None:
+        out["token_sweep"] = sweep
+    return out
+
+
+def bench_stack(args, moe, synth, torch, np):
+    cfg = synth.CONFIGS[args.workload]
+    T, fmt, NLAY = cfg["T"], cfg["fmt"], cfg["layers"]
+    log(f"generating the {NLAY} layers of {args.workload}")
+    t0 = time.time()
+    hosts, x_bits = synth.make_workload(args.workload, workers=16,
+                                        progress=lambda l: log(f"  layer {l} ready ({time.time() - t0:.1f} s)"))
+    dls = []
+    for l, h in enumerate(hosts):
+        dls.append(moe.DeviceLayer(h, max_tokens=T))
+        if l % 8 == 7:
+            log(f"  {l + 1} layers on the device")
+    handles = [d.handle for d in dls]
+    E, K = hosts[0].E, hosts[0].k
+    exp_b = hosts[0].expert_bytes()
+    gu_b = hosts[0].gate.nbytes() + hosts[0].up.nbytes()
+    x0 = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    x = x0.clone()
+    ws = moe.alloc_workspace(moe.moe_stack_workspace_size(handles, T))
+    stream = moe.current_stream()
+
+    # one untimed pass recording every layer's routing and normalised input
+    rb = [moe.route_buffers(T, K, E) for _ in range(NLAY)]
+    moe.moe_stack_forward(handles, x.data_ptr(), T, STACK_EPS, [r for r, _ in rb], ws.data_ptr(), ws.numel(), stream)
+    torch.cuda.synchronize()
+    touched = [int((b["counts"].cpu().numpy() > 0).sum()) for _, b in rb]
+    w_bytes = float(sum((u + 1) * exp_b for u in touched))
+    up_bytes = [(u + 1) * gu_b + T * 2048 * 2 + (T * K + T) * 512 * 2 for u in touched]
+    xin = [b["x_in"] for _, b in rb]
+    log(f"touched experts per layer: mean {np.mean(touched):.1f}; expert bytes per step {w_bytes / 1e6:.1f} MB")
+
+    def run(on):
+        moe.moe_stack_forward(handles, x.data_ptr(), T, STACK_EPS, None, ws.data_ptr(), ws.numel(), on)
+
+    for _ in range(args.warmup):
+        x.copy_(x0)
+        run(stream)
+    torch.cuda.synchronize()
+
+    def plain(i):
+        run(stream)
+
+    # restore outside the event pair so that only the stack pass is timed
+    def timed(f, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            x.copy_(x0)
+            evs[i][0].record()
+            f(i)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
+
+    log(f"timing {args.steps} plain-launch stack steps")
+    plain_ms = timed(plain, args.steps)
+    ms = float(np.mean(plain_ms))
+
+    graph_ms, spread = None, None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        x.copy_(x0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            run(moe.current_stream())
+        for _ in range(args.warmup):
+            x.copy_(x0)
+            g.replay()
+        torch.cuda.synchronize()
+        log(f"timing {args.steps} graph replays of the stack")
+        gm = timed(lambda i: g.replay(), args.steps)
+        graph_ms = float(np.mean(gm))
+        spread = {"p10": pct(gm, 10), "p50": pct(gm, 50), "p90": pct(gm, 90)}
+        log(f"graph replay: {graph_ms * 1e3:.1f} us per 47-layer step")
+        # the replay reproduces the recorded pass (same input, same routing)
+        x_chk = x.clone()
+        x.copy_(x0)
+        run(stream)
+        torch.cuda.synchronize()
+        if not torch.equal(x_chk, x):
+            raise RuntimeError("graph replay of the stack differs from a plain pass")
+        del g
+
+    # roofline: the gate/up stage of every layer on the inputs the stack produced,
+    # one layer after another so that each reads its weights from HBM
+    y = torch.empty_like(x)
+    wsl = moe.alloc_workspace(dls[0].workspace_size(T))
+    n_rep = max(1, args.steps // 10)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.N_STAGE_EVENTS)] for _ in range(NLAY * n_rep)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for r in range(n_rep):
+        for l in range(NLAY):
+            row = [e.cuda_event for e in evs[r * NLAY + l]]
+            moe.moe_layer_forward_staged(handles[l], xin[l].data_ptr(), T, y.data_ptr(), None, wsl.data_ptr(),
+                                         wsl.numel(), stream, row)
+    torch.cuda.synchronize()
+    stage_ms = np.array([[row[j].elapsed_time(row[j + 1]) for j in range(moe.N_STAGE_EVENTS - 1)] for row in evs])
+    up_ms = stage_ms[:, moe.STAGES.index("gate_up")]
+    up_achieved = n_rep * sum(up_bytes) / (up_ms.sum() * 1e-3) / 1e9
+    stage_means = {n: round(float(v), 4) for n, v in zip(moe.STAGES, stage_ms.mean(0))}
+    log(f"per-layer stage means (ms): {stage_means}")
+
+    step_ms = graph_ms if graph_ms is not None else ms
+    gbps = w_bytes / (step_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        th = oracle.max_threads()
+        n_tok = 8
+        log(f"cpu baseline: oracle stack on {th} threads, {n_tok} tokens through all {NLAY} layers, about 10 s")
+        n_cpu, c0 = 0, time.time()
+        while n_cpu < 1 or (time.time() - c0 < 10.0 and n_cpu < 16):
+            sl = slice((n_cpu * n_tok) % T, (n_cpu * n_tok) % T + n_tok)
+            oracle.stack_forward(hosts, x_bits[sl], eps=STACK_EPS, threads=th, record=False)
+            n_cpu += 1
+        dt = time.time() - c0
+        cpu = {"value": round(n_cpu * n_tok / dt, 3), "unit": "tokens/s", "cores": th, "kind": "oracle",
+               "sample": f"{n_cpu} passes of {n_tok} of the 32 tokens through all {NLAY} layers of the same "
+                         f"stack (tokens are independent within a layer), {dt:.1f} s wall"}
+
     for d in dls:
         d.close()
+    del dls, ws, wsl, x, x0, y, xin, rb
+    torch.cuda.empty_cache()
+    stream_ref = None if args.no_stream_reference else stream_reference(moe, torch)
+
+    return {
+        "metric": "MoE-layer tokens/s + achieved HBM GB/s (% of peak), decode batch 1–256, 1 GPU",
+        "value": round(T / (step_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"{fmt} weights, f16 operands, f32 accumulate",
+        "data": "synthetic",
+        "hbm_gbps_expert_weights": round(gbps, 1),
+        "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "hbm_frac_of_stream_read": round(gbps / stream_ref["gbps"], 4) if stream_ref else None,
+        "stream_read": stream_ref,
+        "config": {"workload": f"moe_stack_{args.workload}", "tokens": T, "layers": NLAY, "d_model": 2048,
+                   "routed_experts": E, "top_k": K, "shared_experts": 1, "d_expert": 512, "weights": fmt,
+                   "router_bias_zipf": cfg["zipf"], "rms_eps": STACK_EPS,
+                   "touched_experts_mean": round(float(np.mean(touched)), 1),
+                   "expert_weight_bytes_per_step": int(w_bytes), "router_bytes_per_step": NLAY * E * 2048 * 2,
+                   "launch": "hip_graph_replay" if graph_ms is not None else "plain",
+                   "plain_launch_ms_per_step": round(ms, 5), "graph_replay_ms": spread,
+                   "per_layer_stage_ms": stage_means},
+        "roofline": {"bound": "hbm", "kernel": "ffn_up_kernel (gate/up + SwiGLU), every layer of the stack",
+                     "achieved": round(up_achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(up_achieved / HBM_PEAK_GBPS, 4),
+                     "frac_of_stream_read": round(up_achieved / stream_ref["gbps"], 4) if stream_ref else None,
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_t64_q4_1")
+    ap.add_argument("--layers", type=int, default=8, help="layer instances the steps rotate over (single layer)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time plain launches instead of HIP-graph replays")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the token-count sweep")
+    ap.add_argument("--no-stream-reference", action="store_true", help="skip the 4 GiB streaming-read reference")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run a plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import quantized_expert_ffn_wave_amd as moe
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    if args.workload not in synth.CONFIGS:
+        print(f"unknown workload {args.workload}; one of {sorted(synth.CONFIGS)}", file=sys.stderr)
+        return 2
+    if synth.CONFIGS[args.workload]["layers"] == 1:
+        out = bench_layer(args, moe, synth, torch, np)
+    else:
+        out = bench_stack(args, moe, synth, torch, np)
+    print(json.dumps(out), flush=True)
     return 0
 
 

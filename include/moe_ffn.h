@@ -164,6 +164,18 @@ moe_status moe_stack_workspace_size(const moe_layer* const* layers, int32_t n_la
 moe_status moe_stack_forward(const moe_layer* const* layers, int32_t n_layers, void* x, int32_t T, float rms_eps,
                              const moe_route_out* routes, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Measurement helper, not part of the layer: a plain streaming read of
+ * `bytes` bytes of device memory at src, 16 bytes per load with eight loads in
+ * flight per thread, on `grid` workgroups of 256 threads (0 = one per compute
+ * unit) on the given stream.  It computes nothing and gives the attainable HBM
+ * read rate that the layer's weight streams are measured against: the review's
+ * section "The architecture is an argument about memory bandwidth" states that
+ * decoding is bound by moving weights from memory.  src must be 16 B aligned
+ * and bytes a positive multiple of 16; sink is caller-owned device memory of
+ * 256 uint32 that the kernel may write (its contents are meaningless).
+ * Invalid arguments return MOE_ERR_INVALID_ARG before anything is enqueued. */
+moe_status moe_stream_read(const void* src, size_t bytes, void* sink, int32_t grid, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* moe_last_error(void);
 

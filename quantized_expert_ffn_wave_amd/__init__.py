@@ -22,7 +22,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
 WFMT = {"bf16": 0, "q4_1": 1, "nvfp4": 2}
 EXPORTED = ["moe_layer_create", "moe_layer_destroy", "moe_layer_workspace_size", "moe_desc_workspace_size",
             "moe_layer_forward", "moe_layer_forward_staged", "moe_stack_workspace_size", "moe_stack_forward",
-            "moe_last_error", "moe_version"]
+            "moe_stream_read", "moe_last_error", "moe_version"]
 N_STAGE_EVENTS = 7
 STAGES = ["router", "topk", "bucket", "gate_up", "down", "combine"]
 
@@ -81,6 +81,8 @@ _lib.moe_stack_workspace_size.restype = ctypes.c_int
 _lib.moe_stack_forward.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _i32, ctypes.c_float,
                                    ctypes.POINTER(moe_route_out), _vp, _sz, _vp]
 _lib.moe_stack_forward.restype = ctypes.c_int
+_lib.moe_stream_read.argtypes = [_vp, _sz, _vp, _i32, _vp]
+_lib.moe_stream_read.restype = ctypes.c_int
 _lib.moe_last_error.restype = ctypes.c_char_p
 _lib.moe_version.restype = ctypes.c_char_p
 
@@ -162,6 +164,11 @@ def moe_stack_forward(handles, x_ptr: int, T: int, eps: float, routes, ws_ptr: i
         rarr = (moe_route_out * len(routes))(*routes)
     _check(_lib.moe_stack_forward(arr, len(handles), x_ptr, T, eps, rarr, ws_ptr, ws_bytes, stream),
            "moe_stack_forward")
+
+
+
+def moe_stream_read(src_ptr: int, nbytes: int, sink_ptr: int, grid: int, stream: int) -> None:
+    _check(_lib.moe_stream_read(src_ptr, nbytes, sink_ptr, grid, stream), "moe_stream_read")
 
 
 # ---- torch-level helpers -----------------------------------------------------------------

@@ -348,6 +348,21 @@ moe_status moe_stack_forward(const moe_layer* const* layers, int32_t n, void* x,
   return MOE_OK;
 }
 
+moe_status moe_stream_read(const void* src, size_t bytes, void* sink, int32_t grid, void* stream) {
+  if (!src || !aligned(src, 16)) return fail(MOE_ERR_INVALID_ARG, "src must be a 16 B aligned device pointer");
+  if (bytes == 0 || bytes % 16) return fail(MOE_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  if (!sink || !aligned(sink, 4)) return fail(MOE_ERR_INVALID_ARG, "sink must be a 4 B aligned device pointer");
+  if (grid < 0 || grid > 65536) return fail(MOE_ERR_INVALID_ARG, "grid must be in [0, 65536], got %d", grid);
+  int dev = 0, n_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "device query");
+  if ((e = moe::launch_stream_read(src, bytes, static_cast<uint32_t*>(sink), grid ? grid : n_cu,
+                                   static_cast<hipStream_t>(stream))) != hipSuccess)
+    return hip_fail(e, "stream read launch");
+  return MOE_OK;
+}
+
 const char* moe_last_error(void) { return g_err.c_str(); }
 
 const char* moe_version(void) { return "moe_ffn gfx950 0.1"; }

@@ -128,4 +128,6 @@ hipError_t launch_combine(const LayerArgs& a, hipStream_t s);
 // max_wgs workgroups, else as many as are resident on n_cu CUs at once
 hipError_t launch_ffn(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s);
 hipError_t launch_stack_init(const uint16_t* x, float* r, uint16_t* xn, int T, float eps, hipStream_t s);
+// plain streaming read of bytes (a multiple of 16) from src on grid workgroups
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int grid, hipStream_t s);
 }  // namespace moe

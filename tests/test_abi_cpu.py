@@ -115,6 +115,12 @@ def test_forward_argument_errors_without_a_layer():
     assert lib.moe_stack_workspace_size(arr, 1, 4, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_stack_forward(None, 0, None, 4, 1e-6, None, None, 0, None) == moe.MOE_ERR_INVALID_ARG
     lib.moe_layer_destroy(None)  # NULL-safe
+    # the streaming-read helper checks its arguments before touching a device
+    assert lib.moe_stream_read(None, 4096, 0x1000, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_stream_read(0x1008, 4096, 0x1000, 0, None) == moe.MOE_ERR_INVALID_ARG  # misaligned src
+    assert lib.moe_stream_read(0x1000, 4100, 0x1000, 0, None) == moe.MOE_ERR_INVALID_ARG  # not 16 B multiple
+    assert lib.moe_stream_read(0x1000, 4096, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_stream_read(0x1000, 4096, 0x1000, -1, None) == moe.MOE_ERR_INVALID_ARG
     assert moe.version().startswith("moe_ffn gfx950")
 
 
