@@ -17,14 +17,20 @@ enum Fmt : int { FMT_BF16 = 0, FMT_Q4_1 = 1, FMT_NVFP4 = 2 };
 
 // ---- work decomposition ---------------------------------------------------------
 // A bucket of m tokens is split into token groups of GV_GROUP (vector path) when
-// m < MFMA_MIN, else into token tiles of mfma_bn(T) tokens (matrix-core path):
-// 64 in batches of up to MFMA_WIDE_T tokens, 128 in larger ones (where buckets
-// are large, a wider tile streams an expert's weights fewer times; where they
-// are not, narrower tiles make more and shorter items).  Both paths cover
+// m < mfma_min(T), else into token tiles of mfma_bn(T) tokens (matrix-core
+// path): 64 in batches of up to MFMA_WIDE_T tokens, 128 in larger ones (where
+// buckets are large, a wider tile streams an expert's weights fewer times;
+// where they are not, narrower tiles make more and shorter items).  The
+// threshold is MFMA_MIN up to MFMA_MID_T tokens, where most buckets are small
+// and a tile item is slower than the vector items it replaces, and
+// MFMA_MIN_WIDE above, where mid-size buckets would otherwise stream their
+// expert's weights once per 4 tokens.  Both paths cover
 // UP_ROWS gate/up row pairs (vector path; matrix-core path: D_FF / mf_up_chunks
 // of the tile width), or DN_ROWS down rows, per work item.
 constexpr int GV_GROUP = 4;
 constexpr int MFMA_MIN = 65;
+constexpr int MFMA_MIN_WIDE = 16;
+constexpr int MFMA_MID_T = 128;
 constexpr int MFMA_WIDE_T = 256;
 constexpr int UP_ROWS = 64;
 constexpr int DN_ROWS = 256;
@@ -36,10 +42,11 @@ __host__ __device__ inline int mfma_bn(int T) { return T > MFMA_WIDE_T ? 128 : 6
 // gate/up items per matrix-core tile of width bn: 128 row pairs each for
 // 128-token tiles, 64 for 64-token ones
 __host__ __device__ constexpr int mf_up_chunks(int bn) { return bn == 128 ? 4 : 8; }
-// token groups/tiles of a bucket of m tokens (bn: the batch's tile width)
-__host__ __device__ inline bool bucket_mfma(int m) { return m >= MFMA_MIN; }
-__host__ __device__ inline int bucket_tiles(int m, int bn) {
-  return m <= 0 ? 0 : (bucket_mfma(m) ? ceil_div(m, bn) : ceil_div(m, GV_GROUP));
+// path and token groups/tiles of a bucket of m tokens in a batch of T tokens
+__host__ __device__ inline int mfma_min(int T) { return T > MFMA_MID_T ? MFMA_MIN_WIDE : MFMA_MIN; }
+__host__ __device__ inline bool bucket_mfma(int m, int T) { return m >= mfma_min(T); }
+__host__ __device__ inline int bucket_tiles(int m, int T) {
+  return m <= 0 ? 0 : (bucket_mfma(m, T) ? ceil_div(m, mfma_bn(T)) : ceil_div(m, GV_GROUP));
 }
 
 // Work item (16 bytes, so that a kernel needs one load to start streaming):

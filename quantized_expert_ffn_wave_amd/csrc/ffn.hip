@@ -7,15 +7,17 @@
 // this model is a weight-movement problem: each token touches 6 routed experts
 // and the shared one out of 257 per layer.  So the work is organised around
 // streaming each touched expert's packed weights from HBM once:
-//   * buckets below MFMA_MIN tokens (groups of up to 4 tokens) run as a GEMV on
+//   * buckets below mfma_min(T) tokens (groups of up to 4 tokens) run as a GEMV on
 //     v_mfma_f32_4x4x4_16b: a lane loads one 32-element chunk of a weight row
 //     (16 bytes of 4-bit codes and the block scale), unpacks it in registers,
 //     and the 16 independent 4x4x4 products return it the group's partial sums
 //     of its own row; each wave keeps a ring of loads in flight across chunks;
-//   * buckets of MFMA_MIN or more tokens run as 128-row x 128-token tiles (one
-//     tile covers a bucket of up to 128 tokens, so its expert's weights stream
-//     once): the weight tile is decoded into LDS (v_mfma 32x32x16), with the
-//     next K-chunks prefetched into registers during the MFMAs.
+//   * larger buckets (65 tokens on in batches of up to 128 tokens, 16 on in
+//     larger ones) run as token tiles of 64 (batches of up to 256 tokens) or
+//     128 tokens, so that an expert's weights stream once per tile: each lane
+//     loads and decodes its weights straight into the A operand of
+//     v_mfma_f32_32x32x16, the tile's activations are staged in LDS, and the
+//     next K-chunks are prefetched into registers during the MFMAs.
 // Both kernels are persistent and walk device-side work lists that hold the
 // routed and the shared expert alike, so no host synchronisation is needed.
 //
@@ -224,7 +226,7 @@ __device__ inline int row_of(const LayerArgs& a, const ItemTok& it, int i) {
 // ======================================================================================
 
 // ======================================================================================
-// Vector path (buckets below MFMA_MIN tokens) on the matrix cores.
+// Vector path (buckets below mfma_min(T) tokens) on the matrix cores.
 //
 // v_mfma_f32_4x4x4_16b_{f16,bf16} performs 16 independent 4x4x4 products per
 // wave: lane l = 4b + j supplies row j of block b's first operand and column j
@@ -913,7 +915,7 @@ __device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const Item
 template <int FMT> constexpr int FFN_WG_PER_CU = 2;
 
 // LDS of the persistent kernels: the matrix-core tiles (BN tokens wide) only
-// where the batch can have them (BN > 0: T >= MFMA_MIN), since their double
+// where the batch can have them (BN > 0: T >= mfma_min(T)), since their double
 // buffer would otherwise cost the vector path occupancy.
 template <int BN> struct FfnKernelSmem {
   union {
@@ -994,11 +996,11 @@ hipError_t launch_ffn_var(const LayerArgs& a, bool up, int n_cu, int max_wgs, hi
 }
 
 // Matrix-core tiles exist only for buckets (or the shared expert) of
-// MFMA_MIN or more tokens, so below that the leaner kernel runs; above, the
+// mfma_min(T) or more tokens, so below that the leaner kernel runs; above, the
 // kernel for the batch's tile width.
 template <int FMT>
 hipError_t launch_ffn_fmt(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s) {
-  if (!bucket_mfma(a.T)) return launch_ffn_var<FMT, 0>(a, up, n_cu, max_wgs, s);
+  if (!bucket_mfma(a.T, a.T)) return launch_ffn_var<FMT, 0>(a, up, n_cu, max_wgs, s);
   return mfma_bn(a.T) == 64 ? launch_ffn_var<FMT, 64>(a, up, n_cu, max_wgs, s)
                             : launch_ffn_var<FMT, 128>(a, up, n_cu, max_wgs, s);
 }

@@ -313,9 +313,9 @@ __device__ void write_lists(const LayerArgs& a, const int* bcnt, const int* boff
   const int bn = mfma_bn(T);
   for (int e = tid; e < E; e += nth) {
     const int m = bcnt[e];
-    const int tiles = bucket_tiles(m, bn);
-    ls.it_m[e] = bucket_mfma(m) ? tiles : 0;
-    ls.it_g[e] = bucket_mfma(m) ? 0 : tiles;
+    const int tiles = bucket_tiles(m, T);
+    ls.it_m[e] = bucket_mfma(m, T) ? tiles : 0;
+    ls.it_g[e] = bucket_mfma(m, T) ? 0 : tiles;
   }
   __syncthreads();
   if (tid < 64) {
@@ -328,13 +328,13 @@ __device__ void write_lists(const LayerArgs& a, const int* bcnt, const int* boff
   __syncthreads();
   const int tiles_m = ls.tot[0], tiles_g = ls.tot[1];
   // The shared expert takes every token: bn-token matrix-core tiles from
-  // MFMA_MIN tokens on, else groups of GV_GROUP tokens, in the same lists.
+  // mfma_min(T) tokens on, else groups of GV_GROUP tokens, in the same lists.
   // Tile order: routed matrix-core, shared matrix-core, shared vector, routed
   // vector (the kernels take the matrix-core items first; the shared expert's
   // vector items, which mostly read its weights from L2, go before the routed
   // ones so that they do not fall into the last, partial round).
-  const int sh_tiles = a.n_shared ? bucket_tiles(T, bn) : 0;
-  const bool sh_mf = bucket_mfma(T);
+  const int sh_tiles = a.n_shared ? bucket_tiles(T, T) : 0;
+  const bool sh_mf = bucket_mfma(T, T);
   const int mf_tiles = tiles_m + (sh_mf ? sh_tiles : 0);
   const int sh_vec = sh_mf ? 0 : sh_tiles;
   const int all_tiles = tiles_m + tiles_g + sh_tiles;
@@ -456,9 +456,10 @@ __global__ __launch_bounds__(BK_THREADS) void chunk_scan_kernel(LayerArgs a) {
   write_lists(a, cnt, off, ls, [](int) { return 0; });
   // first vector-path tile of each expert (tile order: routed matrix-core,
   // shared matrix-core, shared vector, routed vector)
-  const int sh_all = a.n_shared ? bucket_tiles(a.T, mfma_bn(a.T)) : 0;  // matrix-core or vector, first either way
+  const int sh_all = a.n_shared ? bucket_tiles(a.T, a.T) : 0;  // matrix-core or vector, first either way
   int32_t* vt = tab + (size_t)nch * E;
-  for (int e = tid; e < E; e += BK_THREADS) vt[e] = bucket_mfma(cnt[e]) ? -1 : ls.tot[0] + sh_all + ls.it_g[e];
+  for (int e = tid; e < E; e += BK_THREADS)
+    vt[e] = bucket_mfma(cnt[e], a.T) ? -1 : ls.tot[0] + sh_all + ls.it_g[e];
 }
 
 __global__ __launch_bounds__(BK_THREADS) void chunk_perm_kernel(LayerArgs a) {

@@ -190,24 +190,28 @@ def test_staged_forward_matches_plain_forward(q4_layer):
 
 
 def test_matrix_core_bucket_boundary():
-    """16 experts, top-6, 168..180 tokens: buckets on both sides of the switch
-    from 4-token vector groups (<= 64 tokens) to 64-token matrix-core tiles."""
-    host = synth.make_layer(seed=5, fmt="q4_1", E=16, k=6)
-    dl = moe.DeviceLayer(host, max_tokens=256)
-    seen = set()
-    for T in (168, 172, 176, 180):
-        say(f"case matrix-core boundary T={T}")
-        info = check_layer(host, synth.make_x(T, xseed=600 + T), dl)
-        seen |= set(info["counts"].tolist())
-    assert any(55 <= c <= 64 for c in seen) and any(65 <= c <= 75 for c in seen), sorted(seen)
+    """Buckets on both sides of the switch from 4-token vector groups to
+    64-token matrix-core tiles: at 65 tokens in batches of up to 128 tokens
+    (16 experts, top-8, 116..128 tokens), at 16 tokens in larger ones (64
+    experts, top-6, 150..170 tokens)."""
+    for E, k, Ts, lo, hi in ((16, 8, (116, 120, 124, 128), 64, 65), (64, 6, (150, 160, 170), 15, 16)):
+        host = synth.make_layer(seed=5, fmt="q4_1", E=E, k=k)
+        dl = moe.DeviceLayer(host, max_tokens=256)
+        seen = set()
+        for T in Ts:
+            say(f"case matrix-core boundary E={E} k={k} T={T}")
+            info = check_layer(host, synth.make_x(T, xseed=600 + T), dl)
+            seen |= set(info["counts"].tolist())
+        assert any(lo - 8 <= c <= lo for c in seen) and any(hi <= c <= hi + 8 for c in seen), sorted(seen)
 
 
 def test_chunked_buckets_mixed(nvfp4_layer):
     """520 tokens: the 256-token chunked bucket build (last chunk ragged) with
-    hot matrix-core buckets and cold vector-path buckets in one batch."""
+    hot and mid-size matrix-core buckets and cold vector-path buckets (below 16
+    tokens) in one batch."""
     host, dl = nvfp4_layer
     say("case chunked buckets nvfp4 zipf T=520")
     info = check_layer(host, synth.make_x(520, xseed=700), dl)
     c = info["counts"]
-    assert c.max() >= 65 and ((c > 0) & (c < 65)).sum() > 20
+    assert c.max() >= 65 and ((c >= 16) & (c <= 64)).sum() > 5 and ((c > 0) & (c < 16)).sum() > 20
     say(f"  max row err {info['max_err']:.2e}")
