@@ -85,7 +85,7 @@ WsLayout ws_layout(const moe_layer_desc& d, int T) {
   // token tiles of the routed buckets, sum_e ceil(m_e / GV_GROUP) <= touched + S / GV_GROUP,
   // plus those of the shared expert
   const int tiles = (int)((S < (size_t)E ? S : (size_t)E) + S / moe::GV_GROUP + 1) +
-                    (d.n_shared ? moe::bucket_tiles(T, T) : 0);
+                    (d.n_shared ? moe::shared_tiles(T) : 0);
   L.max_tiles = tiles;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += up256(bytes > 0 ? bytes : 1); return at; };

@@ -48,6 +48,14 @@ __host__ __device__ inline bool bucket_mfma(int m, int T) { return m >= mfma_min
 __host__ __device__ inline int bucket_tiles(int m, int T) {
   return m <= 0 ? 0 : (bucket_mfma(m, T) ? ceil_div(m, mfma_bn(T)) : ceil_div(m, GV_GROUP));
 }
+// The shared expert (all T tokens) takes tiles from MFMA_MIN tokens on at every
+// batch size: a tile holding a few dozen tokens is slower than its vector groups.
+__host__ __device__ inline bool shared_mfma(int T) { return T >= MFMA_MIN; }
+__host__ __device__ inline int shared_tiles(int T) {
+  return T <= 0 ? 0 : (shared_mfma(T) ? ceil_div(T, mfma_bn(T)) : ceil_div(T, GV_GROUP));
+}
+// whether a batch of T tokens can have matrix-core tiles at all
+__host__ __device__ inline bool batch_mfma(int T) { return bucket_mfma(T, T) || shared_mfma(T); }
 
 // Work item (16 bytes, so that a kernel needs one load to start streaming):
 //   head: expert (9 bits; SHARED_ID = the shared expert) | row chunk << 9 (5 bits) |

@@ -1000,7 +1000,7 @@ hipError_t launch_ffn_var(const LayerArgs& a, bool up, int n_cu, int max_wgs, hi
 // kernel for the batch's tile width.
 template <int FMT>
 hipError_t launch_ffn_fmt(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s) {
-  if (!bucket_mfma(a.T, a.T)) return launch_ffn_var<FMT, 0>(a, up, n_cu, max_wgs, s);
+  if (!batch_mfma(a.T)) return launch_ffn_var<FMT, 0>(a, up, n_cu, max_wgs, s);
   return mfma_bn(a.T) == 64 ? launch_ffn_var<FMT, 64>(a, up, n_cu, max_wgs, s)
                             : launch_ffn_var<FMT, 128>(a, up, n_cu, max_wgs, s);
 }

@@ -333,8 +333,8 @@ __device__ void write_lists(const LayerArgs& a, const int* bcnt, const int* boff
   // vector (the kernels take the matrix-core items first; the shared expert's
   // vector items, which mostly read its weights from L2, go before the routed
   // ones so that they do not fall into the last, partial round).
-  const int sh_tiles = a.n_shared ? bucket_tiles(T, T) : 0;
-  const bool sh_mf = bucket_mfma(T, T);
+  const int sh_tiles = a.n_shared ? shared_tiles(T) : 0;
+  const bool sh_mf = shared_mfma(T);
   const int mf_tiles = tiles_m + (sh_mf ? sh_tiles : 0);
   const int sh_vec = sh_mf ? 0 : sh_tiles;
   const int all_tiles = tiles_m + tiles_g + sh_tiles;
@@ -456,7 +456,7 @@ __global__ __launch_bounds__(BK_THREADS) void chunk_scan_kernel(LayerArgs a) {
   write_lists(a, cnt, off, ls, [](int) { return 0; });
   // first vector-path tile of each expert (tile order: routed matrix-core,
   // shared matrix-core, shared vector, routed vector)
-  const int sh_all = a.n_shared ? bucket_tiles(a.T, a.T) : 0;  // matrix-core or vector, first either way
+  const int sh_all = a.n_shared ? shared_tiles(a.T) : 0;  // matrix-core or vector, first either way
   int32_t* vt = tab + (size_t)nch * E;
   for (int e = tid; e < E; e += BK_THREADS)
     vt[e] = bucket_mfma(cnt[e], a.T) ? -1 : ls.tot[0] + sh_all + ls.it_g[e];
