@@ -3,8 +3,9 @@
 Workloads: the decode layers of 4 and 64 tokens (q4_1, near-uniform routing),
 256 tokens with NVFP4 weights and a Zipf(1.1) router bias, the 4096-token
 bf16 prefill layer (outputs on a token sample), ragged token counts on both
-sides of the small-bucket/large-bucket boundary, reduced expert counts,
-top-k 1 and 8, no shared expert, unnormalised weights, determinism and T=0.
+sides of the small-bucket/large-bucket boundary, the largest accepted batch
+(65536 tokens), reduced expert counts, top-k 1 and 8, no shared expert,
+unnormalised weights, determinism and T=0.
 """
 import numpy as np
 import pytest
@@ -93,6 +94,23 @@ def test_prefill_t4096_bf16(bf16_layer):
     info = check_layer(host, x, dl, sample=sample)
     assert info["counts"].min() > 0 and 60 < info["counts"].mean() < 130
     say(f"  max row err {info['max_err']:.2e}")
+
+
+def test_maximum_token_count_q4_1():
+    """The largest batch a layer accepts (max_tokens = 65536): 16-bit token ids
+    at their limit, 256 chunks in the bucket build, 128-token tiles only.  Routing
+    is compared on every token, outputs on 64 sampled ones."""
+    T = 65536
+    host = synth.make_layer(seed=11, fmt="q4_1")
+    dl = moe.DeviceLayer(host, max_tokens=T)
+    say("case maximum token count q4_1 T=65536 (outputs on 64 sampled tokens)")
+    x = synth.make_x(T, xseed=T)
+    rng = np.random.default_rng(1)
+    sample = np.concatenate([[0, 1, 32767, 65534, T - 1], rng.choice(T, 59, replace=False)])
+    info = check_layer(host, x, dl, sample=sample)
+    assert info["counts"].sum() == 6 * T and info["counts"].min() > 0
+    say(f"  max row err {info['max_err']:.2e}")
+    dl.close()
 
 
 @pytest.mark.parametrize("E,k,n_shared,renorm,scale,fmt,T", [
