@@ -4,9 +4,10 @@
 A step is one pass of the whole layer (router, top-k, buckets, gate/up +
 SwiGLU, down, combine; the shared expert in the same work lists) over
 one batch of synthetic tokens.  Steps are timed as HIP-graph replays of the
-library's forward (one captured graph per layer instance; the forward is
-capturable because it never synchronises the host), which is how a decode
-loop launches it; `--no-graph` times plain launches instead.  Per-kernel
+library's forward (one captured graph holds a forward of each layer instance
+in turn, as a decode loop captures its whole step; the forward is capturable
+because it never synchronises the host); `--no-graph` times plain launches
+instead.  Per-kernel
 durations for the roofline come from a second timed region of plain
 launches with HIP events recorded between the kernels on the library's
 stream (event records inside a captured graph do not time kernels).  The default
@@ -216,33 +217,44 @@ def bench_layer(args, moe, synth, torch, np):
 
     graph_ms, spread = None, None
     if not args.no_graph:
-        graphs = []
-        for i in range(NL):
+        # One graph holds a forward of every layer instance in turn, as a decode
+        # loop captures its whole step rather than one graph per layer (a graph
+        # launch costs about 5 us of idle GPU between graphs); a second graph
+        # holds the first K % NL instances, so that exactly K steps are timed.
+        def capture(n):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(i, on=moe.current_stream())
-            graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % NL].replay()
+                for i in range(n):
+                    step(i, on=moe.current_stream())
+            return g
+        n_full, n_rest = divmod(args.steps, NL)
+        g_all = capture(NL)
+        g_rest = capture(n_rest) if n_rest else None
+        for _ in range(max(1, args.warmup // NL)):
+            g_all.replay()
         torch.cuda.synchronize()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g0.record()
-        for i in range(args.steps):
-            graphs[(args.warmup + i) % NL].replay()
+        for _ in range(n_full):
+            g_all.replay()
+        if g_rest is not None:
+            g_rest.replay()
         g1.record()
         torch.cuda.synchronize()
         graph_ms = g0.elapsed_time(g1) / args.steps
         log(f"graph replay: {graph_ms * 1e3:.1f} us per step")
-        sp = replay_spread(torch, lambda i: graphs[i % NL].replay(), args.steps)
-        spread = {"p10": pct(sp, 10), "p50": pct(sp, 50), "p90": pct(sp, 90)}
-        del graphs
+        sp = [v / NL for v in replay_spread(torch, lambda i: g_all.replay(), max(n_full, 10))]
+        spread = {"p10": pct(sp, 10), "p50": pct(sp, 50), "p90": pct(sp, 90), "steps_per_replay": NL}
+        del g_all, g_rest
 
     stage_ms = np.array([[row[j].elapsed_time(row[j + 1]) for j in range(moe.N_STAGE_EVENTS - 1)] for row in evs])
     idx = [(args.warmup + i) % NL for i in range(args.steps)]
     up_ms = stage_ms[:, moe.STAGES.index("gate_up")]
     up_achieved = sum(up_bytes[j] for j in idx) / (up_ms.sum() * 1e-3) / 1e9
-    w_bytes = float(np.mean([step_w_bytes[j] for j in idx]))
     step_ms = graph_ms if graph_ms is not None else ms
+    # the timed steps: instances 0, 1, ... in the graph, warmup, warmup + 1, ... in plain launches
+    first = 0 if graph_ms is not None else args.warmup
+    w_bytes = float(np.mean([step_w_bytes[(first + i) % NL] for i in range(args.steps)]))
     gbps = w_bytes / (step_ms * 1e-3) / 1e9
     traffic = read_traffic(args.workload)
     stage_means = {n: round(float(v), 4) for n, v in zip(moe.STAGES, stage_ms.mean(0))}
@@ -256,30 +268,28 @@ def bench_layer(args, moe, synth, torch, np):
         for t in SWEEP_T:
             xt, yt = x_all[:t].contiguous(), torch.empty((t, 2048), dtype=torch.bfloat16, device="cuda")
             tb = [touched_bytes(dl, xt, ws_all) for dl in dls]
-            gs = []
-            for dl in dls:
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
+            g = torch.cuda.CUDAGraph()  # every instance in turn, as for the timed steps above
+            with torch.cuda.graph(g):
+                for dl in dls:
                     moe.moe_layer_forward(dl.handle, xt.data_ptr(), t, yt.data_ptr(), None, ws_all.data_ptr(),
                                           ws_all.numel(), moe.current_stream())
-                gs.append(g)
-            for i in range(args.warmup):
-                gs[i % NL].replay()
+            for _ in range(max(1, args.warmup // NL)):
+                g.replay()
             torch.cuda.synchronize()
-            n = max(args.steps // 2, 10)
+            reps = max(2, args.steps // (2 * NL))
             a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a0.record()
-            for i in range(n):
-                gs[(args.warmup + i) % NL].replay()
+            for _ in range(reps):
+                g.replay()
             a1.record()
             torch.cuda.synchronize()
-            t_ms = a0.elapsed_time(a1) / n
-            wb = float(np.mean([tb[(args.warmup + i) % NL][1] for i in range(n)]))
+            t_ms = a0.elapsed_time(a1) / (reps * NL)
+            wb = float(np.mean([b for _, b, _ in tb]))
             sweep.append({"tokens": t, "us_per_step": round(t_ms * 1e3, 2), "tokens_per_s": round(t / (t_ms * 1e-3), 1),
                           "touched_experts_mean": round(float(np.mean([u for u, _, _ in tb])), 1),
                           "hbm_gbps_expert_weights": round(wb / (t_ms * 1e-3) / 1e9, 1)})
             log(f"sweep T={t}: {t_ms * 1e3:.1f} us, {sweep[-1]['hbm_gbps_expert_weights']} GB/s")
-            del gs
+            del g
         del x_all, ws_all
 
     if args.copy_calibration:

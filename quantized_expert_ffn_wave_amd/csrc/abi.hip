@@ -188,9 +188,11 @@ moe_status run_layer(const moe_layer* L, moe::LayerArgs& a, const WsLayout& W, c
       return hip_fail(e, "route copy");
   }
   if ((e = mark(ev, 3, s)) != hipSuccess) return hip_fail(e, "event record");
-  if ((e = moe::launch_ffn(a, true, L->n_cu, W.max_tiles * moe::N_UP_CHUNKS, s)) != hipSuccess) return hip_fail(e, "gate/up launch");
+  if ((e = moe::launch_ffn(a, true, L->n_cu, W.max_tiles * moe::vec_up_chunks(a.T), s)) != hipSuccess)
+    return hip_fail(e, "gate/up launch");
   if ((e = mark(ev, 4, s)) != hipSuccess) return hip_fail(e, "event record");
-  if ((e = moe::launch_ffn(a, false, L->n_cu, W.max_tiles * moe::N_DN_CHUNKS, s)) != hipSuccess) return hip_fail(e, "down launch");
+  if ((e = moe::launch_ffn(a, false, L->n_cu, W.max_tiles * moe::vec_dn_chunks(a.T), s)) != hipSuccess)
+    return hip_fail(e, "down launch");
   if ((e = mark(ev, 5, s)) != hipSuccess) return hip_fail(e, "event record");
   if ((e = moe::launch_combine(a, s)) != hipSuccess) return hip_fail(e, "combine launch");
   if ((e = mark(ev, 6, s)) != hipSuccess) return hip_fail(e, "event record");

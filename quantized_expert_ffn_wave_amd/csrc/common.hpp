@@ -36,6 +36,15 @@ constexpr int UP_ROWS = 64;
 constexpr int DN_ROWS = 256;
 constexpr int N_UP_CHUNKS = D_FF / UP_ROWS;      // 8
 constexpr int N_DN_CHUNKS = D_MODEL / DN_ROWS;   // 8
+// In batches of up to VEC_SMALL_T tokens (7 experts a token, no matrix-core
+// tiles) the standard vector items would leave most workgroups idle, so they
+// are cut smaller: gate/up items of 16 row pairs for one token and 32 up to
+// VEC_SMALL_T, down items of 128 rows.
+constexpr int VEC_SMALL_T = 8;
+__host__ __device__ constexpr int vec_up_rows(int T) { return T <= 1 ? 16 : T <= VEC_SMALL_T ? 32 : UP_ROWS; }
+__host__ __device__ constexpr int vec_dn_rows(int T) { return T <= VEC_SMALL_T ? 128 : DN_ROWS; }
+__host__ __device__ constexpr int vec_up_chunks(int T) { return D_FF / vec_up_rows(T); }
+__host__ __device__ constexpr int vec_dn_chunks(int T) { return D_MODEL / vec_dn_rows(T); }
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ inline int mfma_bn(int T) { return T > MFMA_WIDE_T ? 128 : 64; }

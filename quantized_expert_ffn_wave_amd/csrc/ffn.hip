@@ -264,12 +264,14 @@ template <int FMT> __device__ inline f32x4 mfma4(uint32_t a0, uint32_t a1, uint3
 
 template <int FMT> constexpr int MV_UP_RING = (FMT == FMT_BF16) ? 4 : 8;  // weight loads in flight per wave
 template <int FMT> constexpr int MV_DN_RING = (FMT == FMT_BF16) ? 4 : 8;
-constexpr int MV_UP_UNITS = 32;            // loads per wave per gate/up chunk: 4 row groups x 4 K-quarters x 2 matrices
-constexpr int MV_DN_UNITS = DN_ROWS / 16;  // loads per wave per down chunk: one per 4-row group (K = 512 in one load)
-// The ring carries loads across chunks in place: the next chunk's load i is
+// loads per wave per gate/up item of VR row pairs: VR / 16 row groups x 4 K-quarters x 2 matrices
+template <int VR> constexpr int MV_UP_UNITS = VR / 2;
+// loads per wave per down item of VDR rows: one per 4-row group (K = 512 in one load)
+template <int VDR> constexpr int MV_DN_UNITS = VDR / 16;
+// The ring carries loads across items in place: the next item's load i is
 // issued into the slot its predecessor load NU - D + i vacates, so D must divide NU.
-static_assert(MV_UP_UNITS % MV_UP_RING<FMT_Q4_1> == 0 && MV_UP_UNITS % MV_UP_RING<FMT_BF16> == 0, "ring");
-static_assert(MV_DN_UNITS % MV_DN_RING<FMT_Q4_1> == 0 && MV_DN_UNITS % MV_DN_RING<FMT_BF16> == 0, "ring");
+static_assert(MV_UP_UNITS<16> % MV_UP_RING<FMT_Q4_1> == 0 && MV_UP_UNITS<16> % MV_UP_RING<FMT_BF16> == 0, "ring");
+static_assert(MV_DN_UNITS<128> % MV_DN_RING<FMT_Q4_1> == 0 && MV_DN_UNITS<128> % MV_DN_RING<FMT_BF16> == 0, "ring");
 constexpr int MV_CHUNKS = D_MODEL / 32;    // 32-element chunks of the longest reduction
 constexpr int MV_TOKW = MV_CHUNKS * 16 + 4;  // dwords per token in LDS (16 B of padding against bank conflicts)
 
@@ -509,11 +511,11 @@ struct VecOrder {
 
 // gate/up + SwiGLU over the vector-path items base + c, c in [0, n), this
 // workgroup taking its items in VecOrder.
-template <int FMT>
+template <int FMT, int VR>
 __device__ void up_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem& sm) {
   using G = GV<FMT>;
-  constexpr int CH = N_UP_CHUNKS;
-  constexpr int D = MV_UP_RING<FMT>, NU = MV_UP_UNITS;
+  constexpr int CH = D_FF / VR;
+  constexpr int D = MV_UP_RING<FMT>, NU = MV_UP_UNITS<VR>;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 3, b = lane >> 2;
   const VecOrder order(n_mf);
@@ -525,7 +527,7 @@ __device__ void up_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem&
   // load u of a chunk: row group g = u / 8, K-quarter q = (u / 2) % 4, matrix
   // u % 2 (gate, up); lane (b, j) reads chunk 16 q + b of row first_row + 4 g + j
   auto first_row = [&](const Item& itm, const ChunkW& cw) {
-    return (size_t)cw.mat * D_FF + item_chunk(itm.head) * UP_ROWS + wave * (UP_ROWS / 4);
+    return (size_t)cw.mat * D_FF + item_chunk(itm.head) * VR + wave * (VR / 4);
   };
   auto load_unit = [&](const ChunkW& cw, size_t r0, int u) {
     return G::template load<true>((u & 1) ? cw.u : cw.g, r0 + 4 * (u >> 3), (uint32_t)j, 16 * ((u >> 1) & 3) + b,
@@ -562,8 +564,7 @@ __device__ void up_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem&
       mv_stage_load<true>(a, nitem, nit, st);
     }
     const bool writer = (lane & 36) == 0 && my_t < it.cnt;
-    uint16_t* hdst = a.h + (size_t)(row_of(a, it, 0) + my_t) * D_FF + item_chunk(item.head) * UP_ROWS +
-                     wave * (UP_ROWS / 4) + j;
+    uint16_t* hdst = a.h + (size_t)(row_of(a, it, 0) + my_t) * D_FF + item_chunk(item.head) * VR + wave * (VR / 4) + j;
     f32x4 acc[2] = {}, negK = {}, S = {};
     uint32_t xq[16];
 #pragma unroll
@@ -598,11 +599,11 @@ __device__ void up_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem&
 
 // down over vector-path chunks, ordered and loaded as in up_stream: load u of a
 // chunk covers rows first_row + 4 u + j over the whole K = 512 (chunk b per lane)
-template <int FMT>
+template <int FMT, int VDR>
 __device__ void down_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem& sm) {
   using G = GV<FMT>;
-  constexpr int CH = N_DN_CHUNKS;
-  constexpr int D = MV_DN_RING<FMT>, NU = MV_DN_UNITS;
+  constexpr int CH = D_MODEL / VDR;
+  constexpr int D = MV_DN_RING<FMT>, NU = MV_DN_UNITS<VDR>;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 3, b = lane >> 2;
   const VecOrder order(n_mf);
@@ -612,7 +613,7 @@ __device__ void down_stream(const LayerArgs& a, int base, int n, int n_mf, MvSme
   ItemTok it = item_tokens(item);
   ChunkW w = chunk_weights<FMT, false>(a, item);
   auto first_row = [&](const Item& itm, const ChunkW& cw) {
-    return (size_t)cw.mat * D_MODEL + item_chunk(itm.head) * DN_ROWS + wave * (DN_ROWS / 4);
+    return (size_t)cw.mat * D_MODEL + item_chunk(itm.head) * VDR + wave * (VDR / 4);
   };
   auto load_unit = [&](const ChunkW& cw, size_t r0, int u) {
     return G::template load<true>(cw.g, r0 + 4 * u, (uint32_t)j, b, D_FF);
@@ -648,8 +649,8 @@ __device__ void down_stream(const LayerArgs& a, int base, int n, int n_mf, MvSme
       mv_stage_load<false>(a, nitem, nit, st);
     }
     const bool writer = (lane & 4) == 0 && my_t < it.cnt;
-    float* ydst = a.y + (size_t)(row_of(a, it, 0) + my_t) * D_MODEL + item_chunk(item.head) * DN_ROWS +
-                  wave * (DN_ROWS / 4) + 4 * ((lane >> 5) & 1) + j;
+    float* ydst = a.y + (size_t)(row_of(a, it, 0) + my_t) * D_MODEL + item_chunk(item.head) * VDR + wave * (VDR / 4) +
+                  4 * ((lane >> 5) & 1) + j;
     uint32_t xq[16];
     f32x4 negK = {}, S = {};
     mv_acts<FMT>(sm, buf, b, j, xq, negK, S);
@@ -941,13 +942,17 @@ __device__ inline int mf_item(int i, int n, int C) {
 }
 
 // Items of the matrix-core path come first; the vector-path chunks follow.
-template <int FMT, int BN>
+// VR, VDR: rows of the vector-path gate/up and down items (vec_up_rows and
+// vec_dn_rows of the batch size).
+static_assert(MFMA_MIN > VEC_SMALL_T && MFMA_MIN_WIDE > VEC_SMALL_T,
+              "batches with smaller vector items have no matrix-core tiles");
+template <int FMT, int BN, int VR>
 __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_up_kernel(LayerArgs a) {
   __shared__ FfnKernelSmem<BN> sm;
-  // matrix-core items: mf_up_chunks(BN) per tile; vector-path items: N_UP_CHUNKS per tile
+  // matrix-core items: mf_up_chunks(BN) per tile; vector-path items: D_FF / VR per tile
   const int n_all = a.ctl[CTL_N_UP], n_mf = a.ctl[CTL_N_UP_MF];
   constexpr int UC = (BN > 0) ? mf_up_chunks(BN) : 1;
-  const int base = (n_mf / UC) * N_UP_CHUNKS;
+  const int base = (n_mf / UC) * (D_FF / VR);
   if constexpr (BN > 0) {
     for (int i = blockIdx.x; i < n_mf; i += gridDim.x) {
       const Item item = fetch_item(a.tiles, mf_item(i, n_mf, UC), UC);
@@ -956,10 +961,10 @@ __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_up_kernel(LayerAr
                        item_tokens(item), item_chunk(item.head) * (D_FF / UC), sm.mf);
     }
   }
-  up_stream<FMT>(a, base, n_all - base, n_mf, sm.gv);
+  up_stream<FMT, VR>(a, base, n_all - base, n_mf, sm.gv);
 }
 
-template <int FMT, int BN>
+template <int FMT, int BN, int VDR>
 __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_down_kernel(LayerArgs a) {
   __shared__ FfnKernelSmem<BN> sm;
   const int n_all = a.ctl[CTL_N_DN], n_mf = a.ctl[CTL_N_DN_MF];
@@ -971,7 +976,8 @@ __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_down_kernel(Layer
                          item_chunk(item.head) * DN_ROWS, sm.mf);
     }
   }
-  down_stream<FMT>(a, n_mf, n_all - n_mf, n_mf, sm.gv);
+  const int base = (n_mf / N_DN_CHUNKS) * (D_MODEL / VDR);
+  down_stream<FMT, VDR>(a, base, n_all - base, n_mf, sm.gv);
 }
 
 // Workgroups of `kernel` that fit on one CU at once (the persistent kernels are
@@ -983,26 +989,35 @@ int resident_per_cu(Kern kernel) {
   return n;
 }
 
-template <int FMT, int BN>
+template <int FMT, int BN, int VR, int VDR>
 hipError_t launch_ffn_var(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s) {
-  static const int occ_up = resident_per_cu(ffn_up_kernel<FMT, BN>);
-  static const int occ_dn = resident_per_cu(ffn_down_kernel<FMT, BN>);
+  static const int occ_up = resident_per_cu(ffn_up_kernel<FMT, BN, VR>);
+  static const int occ_dn = resident_per_cu(ffn_down_kernel<FMT, BN, VDR>);
   int grid = n_cu * (up ? occ_up : occ_dn);
   if (max_wgs < grid) grid = max_wgs;
   if (grid < 1) return hipSuccess;
-  if (up) hipLaunchKernelGGL((ffn_up_kernel<FMT, BN>), dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((ffn_down_kernel<FMT, BN>), dim3(grid), dim3(256), 0, s, a);
+  if (up) hipLaunchKernelGGL((ffn_up_kernel<FMT, BN, VR>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((ffn_down_kernel<FMT, BN, VDR>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 // Matrix-core tiles exist only for buckets (or the shared expert) of
 // mfma_min(T) or more tokens, so below that the leaner kernel runs; above, the
 // kernel for the batch's tile width.
+// The vector item sizes follow vec_up_rows / vec_dn_rows of the batch.
+static_assert(vec_up_rows(1) == 16 && vec_up_rows(2) == 32 && vec_up_rows(VEC_SMALL_T) == 32 &&
+                  vec_up_rows(VEC_SMALL_T + 1) == UP_ROWS && vec_dn_rows(VEC_SMALL_T) == 128 &&
+                  vec_dn_rows(VEC_SMALL_T + 1) == DN_ROWS,
+              "the launch below instantiates these item sizes");
 template <int FMT>
 hipError_t launch_ffn_fmt(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s) {
-  if (!batch_mfma(a.T)) return launch_ffn_var<FMT, 0>(a, up, n_cu, max_wgs, s);
-  return mfma_bn(a.T) == 64 ? launch_ffn_var<FMT, 64>(a, up, n_cu, max_wgs, s)
-                            : launch_ffn_var<FMT, 128>(a, up, n_cu, max_wgs, s);
+  if (!batch_mfma(a.T)) {
+    if (a.T <= 1) return launch_ffn_var<FMT, 0, 16, 128>(a, up, n_cu, max_wgs, s);
+    if (a.T <= VEC_SMALL_T) return launch_ffn_var<FMT, 0, 32, 128>(a, up, n_cu, max_wgs, s);
+    return launch_ffn_var<FMT, 0, UP_ROWS, DN_ROWS>(a, up, n_cu, max_wgs, s);
+  }
+  return mfma_bn(a.T) == 64 ? launch_ffn_var<FMT, 64, UP_ROWS, DN_ROWS>(a, up, n_cu, max_wgs, s)
+                            : launch_ffn_var<FMT, 128, UP_ROWS, DN_ROWS>(a, up, n_cu, max_wgs, s);
 }
 
 hipError_t launch_ffn(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s) {

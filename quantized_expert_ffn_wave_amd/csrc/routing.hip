@@ -339,7 +339,8 @@ __device__ void write_lists(const LayerArgs& a, const int* bcnt, const int* boff
   const int sh_vec = sh_mf ? 0 : sh_tiles;
   const int all_tiles = tiles_m + tiles_g + sh_tiles;
   const int n_tiles = min(all_tiles, a.max_tiles);
-  const int n_up = n_tiles * N_UP_CHUNKS, n_dn = n_tiles * N_DN_CHUNKS;
+  // (batches with matrix-core tiles have the standard vector items)
+  const int n_up = n_tiles * vec_up_chunks(T), n_dn = n_tiles * vec_dn_chunks(T);
   if (tid == 0) {
     a.ctl[CTL_N_UP] = n_up;
     a.ctl[CTL_N_DN] = n_dn;
