@@ -510,21 +510,46 @@ constexpr int RS_WORDS = RS_MAX_T / 32;
 
 struct RouteSmallSmem {
   int32_t ids[RS_MAX_T * MAX_K];
-  int32_t perm[RS_MAX_T * MAX_K];
   uint32_t mask[MAX_E * RS_WORDS];
-  int cnt[MAX_E + 1];
-  int off[MAX_E + 1];
-  ListSmem ls;
+  int off[MAX_E + 1];    // bucket offsets (exclusive prefix of the sizes)
+  int it_m[MAX_E];       // first routed matrix-core tile of each expert
+  int vt[MAX_E];         // its first vector tile (an index into the list), or -1
+  int wtot[4][3];        // per wave of experts: sizes, matrix-core tiles, vector tiles
 };
 
+// inclusive prefix sum over the wave's lanes
+__device__ inline int wave_inclusive(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Buckets and work lists of T <= RS_MAX_T tokens in one 1024-thread
+// workgroup, in four barrier-separated phases: ids into LDS (TOPK: the
+// workgroup runs the top-k itself, one wave per token); per-expert token
+// bitmasks; per expert (one thread each, E <= 256) its bucket size and tile
+// counts, prefix-summed within each wave and then across the four waves; and
+// the outputs: the bucket sizes and offsets, the stable slot permutation and
+// its inverse (a slot's rank r in its bucket = tokens of that expert before
+// it), and the tile entries: a slot of a vector-path bucket writes its token
+// id into tile r / 4 (and slot 4 k the tile's head), each expert its
+// matrix-core tiles, and the threads past the experts the shared expert's
+// tiles.  Tile order: routed
+// matrix-core, shared matrix-core, shared vector, routed vector (the kernels
+// take the matrix-core items first; the shared expert's vector items, which
+// mostly read its weights from L2, go before the routed ones so that they do
+// not fall into the last, partial round).
 template <bool TOPK>
-__global__ __launch_bounds__(RS_THREADS) void route_small_kernel(LayerArgs a) {
-  __shared__ RouteSmallSmem sm;
-  const int tid = threadIdx.x, nth = blockDim.x, wave = tid >> 6;
+__device__ void route_small(const LayerArgs& a, RouteSmallSmem& sm) {
+  const int tid = threadIdx.x, nth = blockDim.x, wave = tid >> 6, lane = tid & 63;
   const int E = a.E, K = a.K, T = a.T, S = a.S;
   const int W = ceil_div(T, 32);
-  if (TOPK) {  // one wave per token
-    for (int t = wave; t < T; t += RS_THREADS / 64) topk_token<ROUTER_KS>(a, t, sm.ids);
+  if (TOPK) {
+    for (int t = wave; t < T; t += nth / 64) topk_token<ROUTER_KS>(a, t, sm.ids);
   } else {
     for (int s = tid; s < S; s += nth) sm.ids[s] = a.ids[s];
   }
@@ -536,33 +561,124 @@ __global__ __launch_bounds__(RS_THREADS) void route_small_kernel(LayerArgs a) {
     atomicOr(&sm.mask[sm.ids[s] * W + (t >> 5)], 1u << (t & 31));
   }
   __syncthreads();
-  for (int e = tid; e < E; e += nth) {
-    int c = 0;
-    for (int w = 0; w < W; ++w) c += __popc(sm.mask[e * W + w]);
-    sm.cnt[e] = sm.off[e] = c;
+  // thread e < E: bucket size and tiles, prefix sums within its wave
+  const int bn = mfma_bn(T);
+  int c = 0, tm = 0, tg = 0, c_in = 0, tm_in = 0, tg_in = 0;
+  if (wave < 4) {
+    if (tid < E) {
+      for (int w = 0; w < W; ++w) c += __popc(sm.mask[tid * W + w]);
+      const int tiles = bucket_tiles(c, T);
+      tm = bucket_mfma(c, T) ? tiles : 0;
+      tg = bucket_mfma(c, T) ? 0 : tiles;
+    }
+    c_in = wave_inclusive(c);
+    tm_in = wave_inclusive(tm);
+    tg_in = wave_inclusive(tg);
+    if (lane == 63) {
+      sm.wtot[wave][0] = c_in;
+      sm.wtot[wave][1] = tm_in;
+      sm.wtot[wave][2] = tg_in;
+    }
   }
   __syncthreads();
-  if (tid < 64) {
-    const int total = wave0_scan(sm.off, E);
-    if (tid == 0) sm.off[E] = total;
+  // totals over the waves of experts, and each expert's exclusive prefixes
+  int tot_c = 0, tiles_m = 0, tiles_g = 0, pre_c = 0, pre_m = 0, pre_g = 0;
+  for (int v = 0; v < 4; ++v) {
+    if (v < wave) {
+      pre_c += sm.wtot[v][0];
+      pre_m += sm.wtot[v][1];
+      pre_g += sm.wtot[v][2];
+    }
+    tot_c += sm.wtot[v][0];
+    tiles_m += sm.wtot[v][1];
+    tiles_g += sm.wtot[v][2];
+  }
+  const int sh_tiles = a.n_shared ? shared_tiles(T) : 0;
+  const bool sh_mf = shared_mfma(T);
+  const int mf_tiles = tiles_m + (sh_mf ? sh_tiles : 0);
+  const int sh_vec = sh_mf ? 0 : sh_tiles;
+  const int n_tiles = min(tiles_m + tiles_g + sh_tiles, a.max_tiles);
+  if (tid < E) {
+    const int off = pre_c + c_in - c;
+    sm.off[tid] = off;
+    sm.it_m[tid] = pre_m + tm_in - tm;
+    sm.vt[tid] = (c > 0 && tm == 0) ? mf_tiles + sh_vec + pre_g + tg_in - tg : -1;
+    a.counts[tid] = c;
+    a.offsets[tid] = off;
+  }
+  if (tid == 0) {
+    sm.off[E] = tot_c;
+    a.offsets[E] = tot_c;
+  }
+  if (tid == 0) {
+    // (batches with matrix-core tiles have the standard vector items)
+    a.ctl[CTL_N_UP] = n_tiles * vec_up_chunks(T);
+    a.ctl[CTL_N_DN] = n_tiles * vec_dn_chunks(T);
+    a.ctl[CTL_N_UP_MF] = min(mf_tiles, n_tiles) * mf_up_chunks(bn);
+    a.ctl[CTL_N_DN_MF] = min(mf_tiles, n_tiles) * N_DN_CHUNKS;
   }
   __syncthreads();
-  for (int e = tid; e < E; e += nth) a.counts[e] = sm.cnt[e];
-  for (int e = tid; e <= E; e += nth) a.offsets[e] = sm.off[e];
-  // stable permutation: a slot's rank in its bucket = tokens of that expert before it
+  // stable permutation and its inverse
   for (int s = tid; s < S; s += nth) {
     const int e = sm.ids[s], t = s / K;
     const uint32_t* me = sm.mask + e * W;
     int r = 0;
     for (int w = 0; w < (t >> 5); ++w) r += __popc(me[w]);
     r += __popc(me[t >> 5] & ((1u << (t & 31)) - 1u));
-    const int pos = sm.off[e] + r;
-    sm.perm[pos] = s;
+    const int off = sm.off[e], pos = off + r;
     a.perm[pos] = s;
     a.inv_perm[s] = pos;
+    const int v0 = sm.vt[e];
+    if (v0 >= 0) {  // vector-path bucket: the token goes into slot r % 4 of tile r / 4
+      const int k = r / GV_GROUP, j = r % GV_GROUP, ti = v0 + k;
+      if (ti < n_tiles) {
+        uint16_t* entry = reinterpret_cast<uint16_t*>(a.tiles + ti);
+        entry[4 + j] = (uint16_t)t;
+        if (j == 0) {
+          uint32_t* w2 = reinterpret_cast<uint32_t*>(a.tiles + ti);
+          w2[0] = item_head(e, 0, min(GV_GROUP, sm.off[e + 1] - off - k * GV_GROUP), false);
+          w2[1] = (uint32_t)pos;
+        }
+      }
+    }
   }
-  __syncthreads();
-  write_lists(a, sm.cnt, sm.off, sm.ls, [&](int p) { return sm.perm[p]; });
+  // routed matrix-core tiles, one expert per thread (at most T / bn each)
+  if (tid < E && tm > 0) {
+    const int e = tid, off = sm.off[e];
+    for (int k = 0; k < tm; ++k) {
+      const int ti = sm.it_m[e] + k;
+      if (ti >= n_tiles) break;
+      Item it;
+      it.head = item_head(e, 0, min(bn, c - k * bn), true);
+      it.p0 = (uint32_t)(off + k * bn);
+      it.t01 = it.t23 = 0u;
+      a.tiles[ti] = it;
+    }
+  }
+  // the shared expert's tiles, on the threads past the experts
+  for (int i = tid - 256; i >= 0 && i < sh_tiles; i += nth - 256) {
+    const int ti = (sh_mf ? tiles_m : mf_tiles) + i;
+    if (ti >= n_tiles) break;
+    const int per = sh_mf ? bn : GV_GROUP;
+    const int p0 = i * per, cnt = min(per, T - p0);
+    uint32_t tk[GV_GROUP] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < GV_GROUP; ++j)
+      if (!sh_mf && j < cnt) tk[j] = (uint32_t)(p0 + j);
+    Item it;
+    it.head = item_head(SHARED_ID, 0, cnt, sh_mf);
+    it.p0 = (uint32_t)p0;
+    it.t01 = tk[0] | (tk[1] << 16);
+    it.t23 = tk[2] | (tk[3] << 16);
+    a.tiles[ti] = it;
+  }
+}
+
+template <bool TOPK>
+__global__ __launch_bounds__(RS_THREADS) void route_small_kernel(LayerArgs a) {
+  __shared__ RouteSmallSmem sm;
+  static_assert(RS_THREADS > 256 && MAX_E <= 256, "experts on the first four waves, shared tiles on the rest");
+  route_small<TOPK>(a, sm);
 }
 
 // top-k (with the buckets too, for up to RS_FUSED_T tokens)
