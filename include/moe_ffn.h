@@ -87,9 +87,15 @@ typedef struct {
  * reduction dimension `cols` contiguous).  Element 2i of a row is the LOW
  * nibble of byte i for the 4-bit formats.
  *   codes : q4_1 / NVFP4: uint8 [n][rows][cols/2]; bf16: bf16 [n][rows][cols]  (16 B aligned)
- *   scales: q4_1: fp16 pairs {d, m} [n][rows][cols/32][2]                      (4 B aligned)
- *           NVFP4: E4M3 bytes [n][rows][cols/16]                               (2 B aligned)
+ *   scales: q4_1: fp16 pairs {d, m} [n][rows][cols/32][2]                      (16 B aligned)
+ *           NVFP4: E4M3 bytes [n][rows][cols/16], a 32-element block's two     (8 B aligned)
+ *                  scales adjacent (its first 16 elements' first)
  *           bf16: NULL
+ *           Within a row of C = cols/32 blocks, block k's scales sit at block
+ *           position (k mod 16) * (C/16) + floor(k/16) (C a multiple of 16;
+ *           for cols = 512 that is the natural order), so that the 4 blocks
+ *           k, k+16, k+32, k+48 of a row of 2048 are adjacent: the vector path
+ *           reads them with one 16-byte (q4_1) or 8-byte (NVFP4) load.
  *   tensor_scale: NVFP4: fp32 [n]; otherwise NULL */
 typedef struct {
   const void* codes;

@@ -125,6 +125,14 @@ __attribute__((constructor)) static void orc_tables(void) {
   for (int i = 0; i < 16; ++i) T_E2M1[i] = orc_e2m1_value((uint8_t)i);
 }
 
+/* Position of the scales of 32-element block k within a row of C such blocks:
+ * blocks are stored in the order k mod G, then floor(k / G), with G = 16 where
+ * 16 divides C and G = C otherwise (the natural order). */
+static int64_t orc_scale_pos(int64_t k, int64_t C) {
+  const int64_t G = (C % 16 == 0) ? 16 : C;
+  return (k % G) * (C / G) + k / G;
+}
+
 /* Weight (r, c) of matrix `n` of a stored set, decoded to fp32:
  *   q4_1 : fp32(d) * fp32(q) + fp32(m)  (the product is exact, the add rounds once)
  *   NVFP4: fp32(E2M1 * E4M3) * ts        (the first product is exact)
@@ -138,14 +146,14 @@ float orc_weight(const orc_mat* M, int64_t n, int64_t r, int64_t c) {
   uint8_t byte = M->codes[((n * R + r) * C + c) / 2];
   uint8_t q = (c & 1) ? (byte >> 4) : (byte & 15);
   if (M->fmt == ORC_Q4_1) {
-    int64_t blk = (n * R + r) * (C / 32) + c / 32;
+    int64_t blk = (n * R + r) * (C / 32) + orc_scale_pos(c / 32, C / 32);
     float d = (float)T_FP16[M->dm[2 * blk]];
     float m = (float)T_FP16[M->dm[2 * blk + 1]];
     float p = d * (float)q;
     return p + m;
   }
   /* NVFP4 */
-  int64_t blk = (n * R + r) * (C / 16) + c / 16;
+  int64_t blk = (n * R + r) * (C / 16) + 2 * orc_scale_pos(c / 32, C / 32) + (c / 16) % 2;
   float p = (float)(T_E2M1[q] * T_E4M3[M->e4m3[blk]]);
   return p * M->ts[n];
 }

@@ -62,11 +62,11 @@ moe_status check_desc(const moe_layer_desc* d) {
 
 moe_status check_qmat(const moe_qmat& q, int fmt, const char* name) {
   if (!q.codes || !aligned(q.codes, 16)) return fail(MOE_ERR_INVALID_ARG, "%s.codes is NULL or not 16-byte aligned", name);
-  if (fmt == MOE_W_Q4_1 && (!q.scales || !aligned(q.scales, 4)))
-    return fail(MOE_ERR_INVALID_ARG, "%s.scales (q4_1 {d,m}) is NULL or not 4-byte aligned", name);
+  if (fmt == MOE_W_Q4_1 && (!q.scales || !aligned(q.scales, 16)))
+    return fail(MOE_ERR_INVALID_ARG, "%s.scales (q4_1 {d,m}) is NULL or not 16-byte aligned", name);
   if (fmt == MOE_W_NVFP4) {
-    if (!q.scales || !aligned(q.scales, 2))
-      return fail(MOE_ERR_INVALID_ARG, "%s.scales (NVFP4 E4M3) is NULL or not 2-byte aligned", name);
+    if (!q.scales || !aligned(q.scales, 8))
+      return fail(MOE_ERR_INVALID_ARG, "%s.scales (NVFP4 E4M3) is NULL or not 8-byte aligned", name);
     if (!q.tensor_scale || !aligned(q.tensor_scale, 4))
       return fail(MOE_ERR_INVALID_ARG, "%s.tensor_scale is NULL or not 4-byte aligned", name);
   }

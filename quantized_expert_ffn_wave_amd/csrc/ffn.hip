@@ -35,11 +35,16 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // 16-byte loads: streaming (read once, non-temporal hint) or cached.
 template <bool NT> __device__ inline u32x4 ld16(const void* p) {
   if (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return *reinterpret_cast<const u32x4*>(p);
+}
+template <bool NT> __device__ inline u32x2 ld8(const void* p) {
+  if (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return *reinterpret_cast<const u32x2*>(p);
 }
 template <bool NT> __device__ inline uint32_t ld4(const void* p) {
   if (NT) return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
@@ -112,17 +117,43 @@ template <int FMT> constexpr bool OPER_F16 = FMT != FMT_BF16;
 // ======================================================================================
 template <int FMT> struct GV;
 
+// Position of the scales of 32-element block `chunk` within a row of
+// cols / 32 blocks: (chunk mod 16) * (cols / 512) + chunk / 16 where 16 divides
+// the block count (the natural order for 512 columns).
+__device__ inline uint32_t scale_slot(int chunk, int cols) {
+  const int C = cols / 32, G = (C % 16 == 0) ? 16 : C;
+  return (uint32_t)((chunk % G) * (C / G) + chunk / G);
+}
+static_assert(D_MODEL / 32 == 64 && D_FF / 32 == 16,
+              "the matrix-core loop spells the order out for rows of 64 blocks; rows of 16 keep the natural order");
+
 template <> struct GV<FMT_Q4_1> {
   struct Raw { u32x4 c; uint32_t dm; };                // 16 B codes + fp16 {d, m}
+  using Scales4 = u32x4;                               // {d, m} of blocks b, b + 16, b + 32, b + 48
   // chunk `chunk` of row (row + sub); the row terms are workgroup-uniform, the
   // unsigned lane terms let the loads take the scalar-base + vector-offset form
   template <bool NT> static __device__ Raw load(const QMat& q, size_t row, uint32_t sub, int chunk, int cols) {
-    Raw r;
-    r.c = ld16<NT>(q.codes + row * (cols / 2) + (sub * (uint32_t)(cols / 2) + 16u * (uint32_t)chunk));
-    r.dm = ld4<NT>(reinterpret_cast<const uint32_t*>(q.scales) + row * (cols / 32) +
-                   (sub * (uint32_t)(cols / 32) + (uint32_t)chunk));
+    return load_slot<NT>(q, row, sub, chunk, scale_slot(chunk, cols), cols);
+  }
+  // with the block's scale position given (slot = scale_slot(chunk, cols))
+  template <bool NT>
+  static __device__ Raw load_slot(const QMat& q, size_t row, uint32_t sub, int chunk, uint32_t slot, int cols) {
+    Raw r = load_codes<NT>(q, row, sub, chunk, cols);
+    r.dm = ld4<NT>(reinterpret_cast<const uint32_t*>(q.scales) + row * (cols / 32) + (sub * (uint32_t)(cols / 32) + slot));
     return r;
   }
+  template <bool NT> static __device__ Raw load_codes(const QMat& q, size_t row, uint32_t sub, int chunk, int cols) {
+    Raw r;
+    r.c = ld16<NT>(q.codes + row * (cols / 2) + (sub * (uint32_t)(cols / 2) + 16u * (uint32_t)chunk));
+    r.dm = 0u;
+    return r;
+  }
+  // the scales of blocks b + 16 i, i < 4, of a row of 2048 (adjacent in storage)
+  template <bool NT> static __device__ Scales4 load_scales4(const QMat& q, size_t row, uint32_t sub, uint32_t b) {
+    return ld16<NT>(reinterpret_cast<const uint8_t*>(q.scales) + row * (D_MODEL / 32 * 4) +
+                    (sub * (uint32_t)(D_MODEL / 32 * 4) + 16u * b));
+  }
+  static __device__ void set_scale(Raw& r, const Scales4& s, int i) { r.dm = s[i]; }
   // 32 decoded weights as 16 fp16 pairs in nibble order: fp16(d*q + m), rounded once.
   static __device__ void decode(const Raw& r, uint32_t* o) {
     const f16x2 d2 = {as_f16x2(r.dm)[0], as_f16x2(r.dm)[0]};
@@ -142,13 +173,27 @@ template <> struct GV<FMT_Q4_1> {
 
 template <> struct GV<FMT_NVFP4> {
   struct Raw { u32x4 c; uint32_t s; };                 // 16 B codes + 2 E4M3 block scales
+  using Scales4 = u32x2;                               // the 2 scales of blocks b, b + 16, b + 32, b + 48
   template <bool NT> static __device__ Raw load(const QMat& q, size_t row, uint32_t sub, int chunk, int cols) {
-    Raw r;
-    r.c = ld16<NT>(q.codes + row * (cols / 2) + (sub * (uint32_t)(cols / 2) + 16u * (uint32_t)chunk));
-    r.s = ld2<NT>(reinterpret_cast<const uint8_t*>(q.scales) + row * (cols / 16) +
-                  (sub * (uint32_t)(cols / 16) + 2u * (uint32_t)chunk));
+    return load_slot<NT>(q, row, sub, chunk, scale_slot(chunk, cols), cols);
+  }
+  template <bool NT>
+  static __device__ Raw load_slot(const QMat& q, size_t row, uint32_t sub, int chunk, uint32_t slot, int cols) {
+    Raw r = load_codes<NT>(q, row, sub, chunk, cols);
+    r.s = ld2<NT>(reinterpret_cast<const uint8_t*>(q.scales) + row * (cols / 16) + (sub * (uint32_t)(cols / 16) + 2u * slot));
     return r;
   }
+  template <bool NT> static __device__ Raw load_codes(const QMat& q, size_t row, uint32_t sub, int chunk, int cols) {
+    Raw r;
+    r.c = ld16<NT>(q.codes + row * (cols / 2) + (sub * (uint32_t)(cols / 2) + 16u * (uint32_t)chunk));
+    r.s = 0u;
+    return r;
+  }
+  template <bool NT> static __device__ Scales4 load_scales4(const QMat& q, size_t row, uint32_t sub, uint32_t b) {
+    return ld8<NT>(reinterpret_cast<const uint8_t*>(q.scales) + row * (D_MODEL / 16) +
+                   (sub * (uint32_t)(D_MODEL / 16) + 8u * b));
+  }
+  static __device__ void set_scale(Raw& r, const Scales4& s, int i) { r.s = (s[i >> 1] >> (16 * (i & 1))) & 0xFFFFu; }
   // E2M1 * E4M3 is exact in fp16; the per-matrix scale is applied after the MFMA.
   static __device__ void decode(const Raw& r, uint32_t* o) {
     const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8(r.s, 0);
@@ -166,6 +211,13 @@ template <> struct GV<FMT_NVFP4> {
 
 template <> struct GV<FMT_BF16> {
   struct Raw { u32x4 c[4]; };                          // 64 B of bf16
+  using Scales4 = uint32_t;                            // (no scales)
+  template <bool NT>
+  static __device__ Raw load_slot(const QMat& q, size_t row, uint32_t sub, int chunk, uint32_t, int cols) {
+    return load<NT>(q, row, sub, chunk, cols);
+  }
+  template <bool NT> static __device__ Scales4 load_scales4(const QMat&, size_t, uint32_t, uint32_t) { return 0u; }
+  static __device__ void set_scale(Raw&, const Scales4&, int) {}
   template <bool NT> static __device__ Raw load(const QMat& q, size_t row, uint32_t sub, int chunk, int cols) {
     Raw r;
     const uint8_t* p = q.codes + row * cols * 2 + (sub * (uint32_t)(cols * 2) + 64u * (uint32_t)chunk);
@@ -251,7 +303,6 @@ __device__ inline int row_of(const LayerArgs& a, const ItemTok& it, int i) {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int FMT> __device__ inline f32x4 mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c) {
   const u32x2 x = {a0, a1}, w = {b0, b1};
@@ -529,14 +580,29 @@ __device__ void up_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem&
   auto first_row = [&](const Item& itm, const ChunkW& cw) {
     return (size_t)cw.mat * D_FF + item_chunk(itm.head) * VR + wave * (VR / 4);
   };
+  // 4-bit formats: the codes ride in the ring, the scales of a row group's 4
+  // K-quarters come in one load per matrix (adjacent in storage) and are
+  // handed to each unit as it is used
+  constexpr bool S4 = FMT != FMT_BF16;
+  static_assert(!S4 || D == 8, "scale loads follow the ring's 8-load row groups");
   auto load_unit = [&](const ChunkW& cw, size_t r0, int u) {
-    return G::template load<true>((u & 1) ? cw.u : cw.g, r0 + 4 * (u >> 3), (uint32_t)j, 16 * ((u >> 1) & 3) + b,
-                                  D_MODEL);
+    const QMat& q = (u & 1) ? cw.u : cw.g;
+    if constexpr (S4) return G::template load_codes<true>(q, r0 + 4 * (u >> 3), (uint32_t)j, 16 * ((u >> 1) & 3) + b, D_MODEL);
+    else return G::template load<true>(q, r0 + 4 * (u >> 3), (uint32_t)j, 16 * ((u >> 1) & 3) + b, D_MODEL);
+  };
+  // the scales of row group u / 8 of load u's matrix
+  auto load_sc = [&](const ChunkW& cw, size_t r0, int u) {
+    return G::template load_scales4<true>((u & 1) ? cw.u : cw.g, r0 + 4 * (u >> 3), (uint32_t)j, (uint32_t)b);
   };
   size_t r0 = first_row(item, w);
   typename G::Raw ring[D];
+  typename G::Scales4 s4c[2] = {}, s4n[2] = {};  // scales of the current / next row group, gate and up
 #pragma unroll
   for (int i = 0; i < D; ++i) ring[i] = load_unit(w, r0, i);
+  if constexpr (S4) {
+    s4c[0] = load_sc(w, r0, 0);
+    s4c[1] = load_sc(w, r0, 1);
+  }
   int buf = 0;
   {
     MvStage st;
@@ -574,11 +640,22 @@ __device__ void up_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem&
         mv_acts<FMT>(sm, buf, 16 * q + b, j, xq, negK, S);
         if (q == 0) acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      const typename G::Raw cur = ring[u % D];
-      if (u + D < NU) ring[u % D] = load_unit(w, r0, u + D);
-      else if (has_next) ring[u % D] = load_unit(nw, nr0, u + D - NU);
+      typename G::Raw cur = ring[u % D];
+      if constexpr (S4) G::set_scale(cur, s4c[m], q);
+      const int un = u + D;  // the load issued now
+      if (un < NU) {
+        ring[u % D] = load_unit(w, r0, un);
+        if (S4 && ((un >> 1) & 3) == 0) s4n[m] = load_sc(w, r0, un);
+      } else if (has_next) {
+        ring[u % D] = load_unit(nw, nr0, un - NU);
+        if (S4 && (((un - NU) >> 1) & 3) == 0) s4n[m] = load_sc(nw, nr0, un - NU);
+      }
       MV<FMT>::unit(cur, xq, negK, S, acc[m]);
       if (u % 8 == 7) {
+        if constexpr (S4) {
+          s4c[0] = s4n[0];
+          s4c[1] = s4n[1];
+        }
         float v = mv_reduce8(acc[0], acc[1]);
         if (FMT == FMT_NVFP4) v *= (lane & 32) ? w.tsu : w.tsg;
         const float up = upper_half(v);
@@ -775,8 +852,12 @@ __device__ inline void mf_kloop(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<BN>& sm, c
   // loaded again), so that the compiler's wait counts stay exact
   auto fetch = [&](MfStage<FMT, BN, RB>& st, int ck) {
     ck = min(ck, nc - 1);
+    // scale position of block 2 ck + h: with 2048 columns the blocks are stored
+    // in the order k mod 16, k / 16, i.e. at 8 (ck mod 8) + 4 h + ck / 8
+    const uint32_t slot = (kdim == D_MODEL) ? 8u * (uint32_t)(ck & 7) + 4u * (uint32_t)h + (uint32_t)(ck >> 3)
+                                            : 2u * (uint32_t)ck + (uint32_t)h;
 #pragma unroll
-    for (int b = 0; b < RB; ++b) st.w[b] = GV<FMT>::template load<false>(q[b], wrow[b], 0u, 2 * ck + h, kdim);
+    for (int b = 0; b < RB; ++b) st.w[b] = GV<FMT>::template load_slot<false>(q[b], wrow[b], 0u, 2 * ck + h, slot, kdim);
 #pragma unroll
     for (int i = 0; i < MF_XK<BN> / 8; ++i) st.x[i] = ld16<false>(xsrc + 64 * ck + 8 * i);
   };
@@ -911,9 +992,12 @@ __device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const Item
 // ======================================================================================
 // Persistent kernels
 // ======================================================================================
-// Workgroups per CU the persistent kernels are compiled for: two (their rings
-// and tiles fit in half the register file).
+// Workgroups per CU the persistent kernels are compiled for: at least two
+// (their rings and tiles fit in half the register file).  They are launched
+// with as many workgroups as are resident at once (three per CU for the lighter
+// vector-only kernels), at most MF_WG_PER_CU per CU where tiles are possible.
 template <int FMT> constexpr int FFN_WG_PER_CU = 2;
+constexpr int MF_WG_PER_CU = 2;
 
 // LDS of the persistent kernels: the matrix-core tiles (BN tokens wide) only
 // where the batch can have them (BN > 0: T >= mfma_min(T)), since their double
@@ -993,7 +1077,12 @@ template <int FMT, int BN, int VR, int VDR>
 hipError_t launch_ffn_var(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s) {
   static const int occ_up = resident_per_cu(ffn_up_kernel<FMT, BN, VR>);
   static const int occ_dn = resident_per_cu(ffn_down_kernel<FMT, BN, VDR>);
-  int grid = n_cu * (up ? occ_up : occ_dn);
+  // Kernels with matrix-core tiles run at most MF_WG_PER_CU workgroups per CU:
+  // with a third one resident the 256-token NVFP4 layer took 89 instead of 78
+  // us (its tile items then share a CU three ways); the vector-only kernels
+  // take every resident slot (capped at two they lost 3 us at 64 tokens).
+  const int occ = up ? occ_up : occ_dn;
+  int grid = n_cu * (BN > 0 ? min(occ, MF_WG_PER_CU) : occ);
   if (max_wgs < grid) grid = max_wgs;
   if (grid < 1) return hipSuccess;
   if (up) hipLaunchKernelGGL((ffn_up_kernel<FMT, BN, VR>), dim3(grid), dim3(256), 0, s, a);

@@ -140,7 +140,10 @@ class QMat:
 
     codes : q4_1/nvfp4 u8 [n][rows][cols/2]; bf16 u16 [n][rows][cols]
     scales: q4_1 u16 (fp16 bits) [n][rows][cols/32][2] = {d, m};
-            nvfp4 u8 (E4M3) [n][rows][cols/16]; bf16 None
+            nvfp4 u8 (E4M3) [n][rows][cols/16]; bf16 None.  Within a row the
+            32-element blocks' scales are stored in the order k mod 16, then
+            k // 16 (where 16 divides the block count; NVFP4 keeps a block's
+            two scales together)
     tensor_scale: nvfp4 fp32 [n]; else None
     """
     fmt: str

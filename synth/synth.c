@@ -20,6 +20,8 @@
  *   NVFP4 : blocks of 16 along a row; E2M1 codes (bit 3 = sign), one FP8 E4M3
  *           (OCP E4M3FN) scale per block, one fp32 scale per matrix.
  *   bf16  : plain bf16.
+ * The scales of a row are stored in the order of scale_pos() below (per
+ * 32-element block; NVFP4 keeps a block's two scales together).
  */
 #define _GNU_SOURCE
 #include <math.h>
@@ -188,6 +190,17 @@ void synth_permutation(uint64_t key, int32_t* perm, int32_t n) {
 /* ---- encoders -------------------------------------------------------------- */
 
 /* q4_1 encode of one row of `cols` fp32 values (cols % 32 == 0). */
+/* Storage order of the scales within a row of C blocks of 32 elements: block k
+ * at position (k mod G) * (C / G) + floor(k / G), G = 16 when 16 divides C
+ * (else G = C, the identity).  With C = 64 the 16 blocks a lane of the
+ * library's vector path reads in one pass of K = 512 lie 4 positions apart, and
+ * its 4 blocks k, k + 16, k + 32, k + 48 are adjacent; with C = 16 the order is
+ * the natural one. */
+static inline int64_t scale_pos(int64_t k, int64_t C) {
+  const int64_t G = (C % 16 == 0) ? 16 : C;
+  return (k % G) * (C / G) + k / G;
+}
+
 static void q4_1_row(const float* w, int64_t cols, uint8_t* codes, uint16_t* dm) {
   for (int64_t b = 0; b < cols / 32; ++b) {
     const float* x = w + 32 * b;
@@ -204,8 +217,9 @@ static void q4_1_row(const float* w, int64_t cols, uint8_t* codes, uint16_t* dm)
       q[i] = (uint8_t)t;
     }
     for (int i = 0; i < 16; ++i) codes[16 * b + i] = (uint8_t)(q[2 * i] | (q[2 * i + 1] << 4));
-    dm[2 * b] = dh;
-    dm[2 * b + 1] = mh;
+    const int64_t p = scale_pos(b, cols / 32);
+    dm[2 * p] = dh;
+    dm[2 * p + 1] = mh;
   }
 }
 
@@ -216,7 +230,8 @@ void synth_q4_1_encode(const float* w, int64_t rows, int64_t cols, uint8_t* code
   for (int64_t r = 0; r < rows; ++r) q4_1_row(w + r * cols, cols, codes + r * cols / 2, dm + r * (cols / 32) * 2);
 }
 
-/* NVFP4 encode of a rows x cols fp32 matrix (cols % 16 == 0).
+/* NVFP4 encode of a rows x cols fp32 matrix (cols % 32 == 0; the two scales
+ * of a 32-element block are stored together at that block's position).
  * ts = amax/(6*448) in fp32; block scale s = E4M3(amax_b / (6*ts)); code =
  * nearest E2M1 to w / (s*ts).  codes: rows*cols/2 bytes, scales: rows*cols/16. */
 void synth_nvfp4_encode(const float* w, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
@@ -232,7 +247,7 @@ void synth_nvfp4_encode(const float* w, int64_t rows, int64_t cols, uint8_t* cod
       double ab = 0;
       for (int i = 0; i < 16; ++i) { double a = fabs((double)x[i]); if (a > ab) ab = a; }
       uint8_t s = synth_f64_to_e4m3_sat(ab / (6.0 * (double)ts));
-      scales[r * (cols / 16) + b] = s;
+      scales[r * (cols / 16) + 2 * scale_pos(b / 2, cols / 32) + (b & 1)] = s;
       double sv = e4m3_bits_value(s) * (double)ts;
       uint8_t c[16];
       for (int i = 0; i < 16; ++i) c[i] = (sv == 0.0) ? 0 : synth_f64_to_e2m1((double)x[i] / sv);
@@ -295,7 +310,7 @@ void synth_matrix(uint64_t key, double sigma, int fmt, int64_t rows, int64_t col
         if (a > ab) ab = a;
       }
       uint8_t s = synth_f64_to_e4m3_sat(ab / (6.0 * (double)ts));
-      sc[r * (cols / 16) + b] = s;
+      sc[r * (cols / 16) + 2 * scale_pos(b / 2, cols / 32) + (b & 1)] = s;
       double sv = e4m3_bits_value(s) * (double)ts;
       uint8_t c[16];
       for (int i = 0; i < 16; ++i) c[i] = (sv == 0.0) ? 0 : synth_f64_to_e2m1((double)x[i] / sv);

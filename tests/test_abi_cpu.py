@@ -87,6 +87,10 @@ def test_create_checks_pointers_before_the_device():
     w.gate = moe.moe_qmat((1 << 32) + 8, (1 << 32), None)  # codes not 16-byte aligned
     assert moe.lib().moe_layer_create(ctypes.byref(d), ctypes.byref(w), ctypes.byref(out)) == moe.MOE_ERR_INVALID_ARG
     assert "gate.codes" in moe.last_error()
+    w = fake_weights()
+    w.down = moe.moe_qmat(1 << 32, (1 << 32) + 4, None)  # q4_1 scales are read 16 bytes at a time
+    assert moe.lib().moe_layer_create(ctypes.byref(d), ctypes.byref(w), ctypes.byref(out)) == moe.MOE_ERR_INVALID_ARG
+    assert "down.scales" in moe.last_error()
     dn = moe.make_desc("nvfp4")
     w = fake_weights()
     w.up = moe.moe_qmat(1 << 32, 1 << 32, None)  # NVFP4 needs the per-matrix scale

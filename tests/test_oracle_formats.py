@@ -146,6 +146,58 @@ def test_nvfp4_round_trip():
     assert np.array_equal(dec.astype(np.float32), ref)
 
 
+def _scale_pos(k, C):
+    """Storage position of block k's scales in a row of C blocks (the order the
+    weight layout documents: k mod 16, then k // 16, where 16 divides C)."""
+    G = 16 if C % 16 == 0 else C
+    return (k % G) * (C // G) + k // G
+
+
+def test_scale_order_is_a_permutation_pinned_at_2048_columns():
+    pos = [_scale_pos(k, 64) for k in range(64)]
+    assert sorted(pos) == list(range(64))
+    assert pos[:3] == [0, 4, 8] and pos[16] == 1 and pos[17] == 5 and pos[63] == 63
+    assert [_scale_pos(k, 16) for k in range(16)] == list(range(16))   # 512 columns: natural order
+    assert [_scale_pos(k, 2) for k in range(2)] == [0, 1]
+
+
+def test_q4_1_scales_of_2048_columns_follow_the_documented_order():
+    rows, cols = 4, 2048
+    w, q, codes, dm = _q4_1_matrix(rows, cols, 7)
+    dec = oracle.decode_matrix(q, 0)
+    pos = np.array([_scale_pos(k, cols // 32) for k in range(cols // 32)])
+    d = dm[..., 0].view(np.float16).astype(np.float64)[:, pos]   # [rows][block]
+    m = dm[..., 1].view(np.float16).astype(np.float64)[:, pos]
+    qn = np.empty((rows, cols), np.int64)
+    qn[:, 0::2] = codes & 15
+    qn[:, 1::2] = codes >> 4
+    ref = (d.repeat(32, 1).astype(np.float32) * qn.astype(np.float32)) + m.repeat(32, 1).astype(np.float32)
+    assert np.array_equal(dec, ref.astype(np.float32))
+    # the encoder stored each block's own scale there: the round trip is within half a step
+    err = np.abs(dec.astype(np.float64) - w.astype(np.float64)).reshape(rows, cols // 32, 32)
+    bound = d[..., None] / 2 + np.abs(m[..., None] - w.reshape(rows, cols // 32, 32).min(-1, keepdims=True)) + 1e-9
+    assert np.all(err <= bound)
+
+
+def test_nvfp4_scales_of_2048_columns_follow_the_documented_order():
+    rows, cols = 4, 2048
+    w = synth.normal_f32(synth.key(6, 99), 0.02, rows * cols).reshape(rows, cols)
+    codes, sc, ts = synth.encode_nvfp4(w)
+    q = synth.QMat("nvfp4", 1, rows, cols, codes[None], sc[None], np.array([ts], np.float32))
+    dec = oracle.decode_matrix(q, 0)
+    pos = np.array([_scale_pos(k, cols // 32) for k in range(cols // 32)])
+    idx = (2 * pos[:, None] + np.arange(2)[None, :]).reshape(-1)   # 16-element block b -> storage byte
+    s = np.array([[oracle.e4m3_value(int(v)) for v in row] for row in sc[:, idx]]) * ts
+    qn = np.empty((rows, cols), np.int64)
+    qn[:, 0::2] = codes & 15
+    qn[:, 1::2] = codes >> 4
+    e2 = np.array([oracle.e2m1_value(int(c)) for c in range(16)])[qn]
+    ref = (e2 * s.repeat(16, 1) / ts).astype(np.float32) * np.float32(ts)
+    assert np.array_equal(dec, ref)
+    amax_b = np.abs(w).reshape(rows, cols // 16, 16).max(-1)
+    assert np.all(np.abs(6 * s - amax_b) <= amax_b / 16 + 1e-12)
+
+
 def test_nvfp4_encoder_ties_and_clamp():
     assert synth.lib().synth_f64_to_e2m1(0.25) == 0       # tie 0 / 0.5 -> even code 0
     assert synth.lib().synth_f64_to_e2m1(0.75) == 2       # tie 0.5 / 1 -> code 2 (1.0)
