@@ -293,8 +293,9 @@ __device__ inline int row_of(const LayerArgs& a, const ItemTok& it, int i) {
 // only decode weights, whatever the item's token count.
 //
 // A persistent workgroup walks its chunks c = blockIdx.x, +gridDim.x, ...: a
-// chunk is one token group of one expert times UP_ROWS row pairs (gate/up) or
-// DN_ROWS rows (down), and each wave takes a quarter of the rows.  The chunk's
+// chunk is one token group of one expert times VR row pairs (gate/up; UP_ROWS,
+// or 16 / 32 in batches of 1 / up to 8 tokens) or VDR rows (down; DN_ROWS, or
+// 128 up to 8 tokens), and each wave takes a quarter of the rows.  The chunk's
 // activations sit in LDS in operand order (double buffered: the next chunk's
 // are loaded during this one), and each wave keeps a ring of weight loads in
 // flight that runs on into the next chunk, so the weight stream does not drain

@@ -308,7 +308,7 @@ __device__ void write_lists(const LayerArgs& a, const int* bcnt, const int* boff
   const int E = a.E, K = a.K, T = a.T;
   // work list: matrix-core tiles first, then vector tiles.  A matrix-core tile
   // makes mf_up_chunks(bn) gate/up items and N_DN_CHUNKS down items, a vector tile
-  // N_UP_CHUNKS and N_DN_CHUNKS; item i of a kind is chunk i % chunks of its
+  // vec_up_chunks(T) and vec_dn_chunks(T); item i of a kind is chunk i % chunks of its
   // tile i / chunks (vector items counted from the first vector tile).
   const int bn = mfma_bn(T);
   for (int e = tid; e < E; e += nth) {
