@@ -73,6 +73,7 @@ def lib():
         L.orc_expert.argtypes = [ctypes.POINTER(_Layer), ctypes.POINTER(_Mat), ctypes.POINTER(_Mat),
                                  ctypes.POINTER(_Mat), ctypes.c_int64, vp, vp]
         L.orc_max_threads.restype = i32
+        L.orc_head_logits.argtypes = [ctypes.POINTER(_Mat), vp, i32, vp, i32, vp, i32]
         _lib = L
     return _lib
 
@@ -270,6 +271,21 @@ def stack_forward(layers, x: np.ndarray, eps: float = 1e-6, threads: int = 0, re
     lib().orc_stack_forward(ctypes.cast(arr, ctypes.c_void_p), nl, _p(x), T, eps, _p(out), _p(xin), _p(yout),
                             _p(ids), threads)
     return dict(out=out, xin=xin, yout=yout, ids=ids)
+
+
+def head_logits(q, x: np.ndarray, rows: np.ndarray | None = None, threads: int = 0) -> np.ndarray:
+    """Output-head logits of bf16 tokens x [T][cols] against stored matrix 0 of
+    q ([vocab][cols]): fp64 [T][len(rows)] (rows None = every vocabulary row)."""
+    keep = []
+    m = _mat(q, keep)
+    x = np.ascontiguousarray(x, np.uint16)
+    T = x.shape[0]
+    r = None if rows is None else np.ascontiguousarray(rows, np.int32)
+    n = q.rows if r is None else r.size
+    out = np.empty((T, n), np.float64)
+    if T > 0 and n > 0:
+        lib().orc_head_logits(ctypes.byref(m), _p(x), T, _p(r), n, _p(out), threads)
+    return out
 
 
 def max_threads() -> int:

@@ -378,4 +378,32 @@ void orc_stack_forward(const orc_layer* const* layers, int n_layers, const uint1
   }
 }
 
+/* Output head (the 4-bit lm_head of "The quantisation recipe is the most
+ * transferable part"): logits[t][v] = sum_k x[t][k] w[v][k] for the stored
+ * matrix W (n = 0, rows = vocabulary, cols = d) and bf16 tokens x [T][cols].
+ * rows: the vocabulary rows to evaluate (n_rows of them; NULL = all rows in
+ * order); out: fp64 [T][n_rows].  Each row is decoded once, then dotted with
+ * every token in ascending k. */
+void orc_head_logits(const orc_mat* W, const uint16_t* x, int T, const int32_t* rows, int n_rows, double* out,
+                     int nthreads) {
+  int d = W->cols;
+  double* xd = (double*)malloc(sizeof(double) * ((int64_t)T * d + 1));
+  for (int64_t i = 0; i < (int64_t)T * d; ++i) xd[i] = T_BF16[x[i]];
+  int nt = orc_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nt)
+  for (int i = 0; i < n_rows; ++i) {
+    int64_t v = rows ? rows[i] : i;
+    double* wr = (double*)malloc(sizeof(double) * d);
+    for (int k = 0; k < d; ++k) wr[k] = (double)orc_weight(W, 0, v, k);
+    for (int t = 0; t < T; ++t) {
+      const double* xt = xd + (int64_t)t * d;
+      double s = 0.0;
+      for (int k = 0; k < d; ++k) s += wr[k] * xt[k];
+      out[(int64_t)t * n_rows + i] = s;
+    }
+    free(wr);
+  }
+  free(xd);
+}
+
 int orc_max_threads(void) { return orc_threads(0); }

@@ -14,6 +14,9 @@ Box-Muller; see synth.c):
   * expert e, matrix j (0 gate [f][d], 1 up [f][d], 2 down [d][f]):
                  fp32(N(0, 0.02)), then the format's encoder   key (seed, EXPERT, e, j)
     the shared expert uses e = SHARED_ID.
+  * output head  W  ~ fp32(N(0, 0.02)) [V][d], then the format's encoder
+                 key (seed, HEAD, 0, 0); the vocabulary V is synthetic (the
+                 pages do not give it; about 150 k)
 """
 from __future__ import annotations
 
@@ -28,7 +31,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "synth.c")
 _LIB = os.path.join(_HERE, "libsynth.so")
 
-TAG_X, TAG_ROUTER, TAG_BIAS, TAG_EXPERT = 1, 2, 3, 4
+TAG_X, TAG_ROUTER, TAG_BIAS, TAG_EXPERT, TAG_HEAD = 1, 2, 3, 4, 5
+HEAD_VOCAB = 151552  # synthetic vocabulary of the output-head workload
 SHARED_ID = 1_000_000
 FMT_CODE = {"bf16": 0, "q4_1": 1, "nvfp4": 2}
 
@@ -239,6 +243,13 @@ def make_x(T: int, d: int = 2048, xseed: int = 0, sigma: float = 1.0) -> np.ndar
     return normal_bf16(key(xseed, TAG_X), sigma, T * d).reshape(T, d)
 
 
+def make_head(V: int = HEAD_VOCAB, fmt: str = "q4_1", seed: int = 0, d: int = 2048, sigma: float = 0.02) -> QMat:
+    """Output-head matrix [V][d] (one stored matrix) drawn from `seed`."""
+    q = alloc_qmat(fmt, 1, V, d)
+    fill_matrix(q, 0, key(seed, TAG_HEAD), sigma)
+    return q
+
+
 def bf16_to_f32(b: np.ndarray) -> np.ndarray:
     """bf16 bits -> fp32 values (bit placement; exact)."""
     return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
@@ -253,6 +264,15 @@ CONFIGS = {
     "decode_t256_nvfp4_zipf1.1": dict(T=256, fmt="nvfp4", zipf=1.1, layers=1),
     "prefill_t4096_bf16": dict(T=4096, fmt="bf16", zipf=None, layers=1),
     "stack47_decode_t32_q4_1_zipf0.8": dict(T=32, fmt="q4_1", zipf=0.8, layers=47),
+}
+
+
+# output-head workloads: name -> T, format, vocabulary
+HEAD_CONFIGS = {
+    "head_v151552_t1_q4_1": dict(T=1, fmt="q4_1", V=HEAD_VOCAB),
+    "head_v151552_t4_q4_1": dict(T=4, fmt="q4_1", V=HEAD_VOCAB),
+    "head_v151552_t32_q4_1": dict(T=32, fmt="q4_1", V=HEAD_VOCAB),
+    "head_v151552_t4_nvfp4": dict(T=4, fmt="nvfp4", V=HEAD_VOCAB),
 }
 
 
