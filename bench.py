@@ -23,6 +23,11 @@ pre-norm residual stack instead: a step is 32 tokens through all 47 layers
 same input each time; its roofline entry times the gate/up kernel of every
 layer on the layer inputs the stack produced.
 
+The output-head workloads (`--workload head_v151552_t4_q4_1` and the others
+of synth.HEAD_CONFIGS) time the 4-bit output head instead: a step is the
+logits of T tokens against a synthetic 151552 x 2048 head, rotating over
+`--layers` drawn heads; its roofline entry is the head kernel itself.
+
 Also measured, outside the timed steps: the attainable HBM read rate (a plain
 streaming read of 4 GiB through the library's moe_stream_read, best of a few
 launch shapes), the spread of single graph replays (p10/p50/p90), and for the
@@ -515,6 +520,126 @@ def bench_stack(args, moe, synth, torch, np):
     }
 
 
+def head_row_bytes(fmt: str) -> int:
+    """Stored bytes of one vocabulary row of 2048 columns."""
+    return {"q4_1": 1024 + 64 * 4, "nvfp4": 1024 + 128, "bf16": 4096}[fmt]
+
+
+def bench_head(args, moe, synth, torch, np):
+    """Output-head GEMV: logits [T][V] of T tokens against a [V][2048] head.
+    Steps rotate over --layers independently drawn heads (each 194 MB in q4_1,
+    so that together they exceed the 256 MB last-level cache)."""
+    cfg = synth.HEAD_CONFIGS[args.workload]
+    T, fmt, V = cfg["T"], cfg["fmt"], cfg["V"]
+    NL = max(1, args.layers)
+    log(f"generating {NL} heads of {args.workload}")
+    hosts = [synth.make_head(V, fmt, seed=s) for s in range(NL)]
+    dms = [moe.DeviceMatrix(h) for h in hosts]
+    x_bits = synth.make_x(T)
+    x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    logits = torch.empty((T, V), dtype=torch.float32, device="cuda")
+    stream = moe.current_stream()
+    # algorithmic bytes of one launch: the head once, the tokens once, the logits once
+    step_bytes = V * head_row_bytes(fmt) + (4 if fmt == "nvfp4" else 0) + T * 2048 * 2 + T * V * 4
+
+    def step(i, on=None):
+        dm = dms[i % NL]
+        moe.moe_head_forward(x.data_ptr(), T, dm.qmat, moe.WFMT[fmt], V, 2048, logits.data_ptr(),
+                             stream if on is None else on)
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # per-launch durations: an event pair around each plain launch on the library's stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    log(f"timing {args.steps} plain launches")
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        evs[i][0].record()
+        step(args.warmup + i)
+        evs[i][1].record()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    graph_ms = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(NL):
+                step(i, on=moe.current_stream())
+        n_full, n_rest = divmod(args.steps, NL)
+        g_rest = None
+        if n_rest:
+            g_rest = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_rest):
+                for i in range(n_rest):
+                    step(i, on=moe.current_stream())
+        for _ in range(max(1, args.warmup // NL)):
+            g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(n_full):
+            g.replay()
+        if g_rest is not None:
+            g_rest.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+        log(f"graph replay: {graph_ms * 1e3:.1f} us per step; plain launches {ms * 1e3:.1f} us, "
+            f"kernel {kern_ms * 1e3:.1f} us")
+        del g, g_rest
+    step_ms = graph_ms if graph_ms is not None else ms
+    achieved = step_bytes / (kern_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        th = oracle.max_threads()
+        log(f"cpu baseline: oracle on {th} threads, whole {T}-token steps for about 10 s")
+        n_cpu, c0 = 0, time.time()
+        while n_cpu < 1 or (time.time() - c0 < 10.0 and n_cpu < 64):
+            oracle.head_logits(hosts[n_cpu % NL], x_bits, threads=th)
+            n_cpu += 1
+        dt = time.time() - c0
+        cpu = {"value": round(n_cpu * T / dt, 3), "unit": "tokens/s", "cores": th, "kind": "oracle",
+               "sample": f"{n_cpu} steps of the same workload (all {V} rows for the {T} tokens, fp64), "
+                         f"{dt:.1f} s wall"}
+
+    del dms, x, logits
+    torch.cuda.empty_cache()
+    stream_ref = None if args.no_stream_reference else stream_reference(moe, torch)
+    return {
+        "metric": "output-head tokens/s + achieved HBM GB/s (% of peak), 1 GPU",
+        "value": round(T / (step_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"{fmt} weights, {'bf16' if fmt == 'bf16' else 'f16'} operands, f32 accumulate",
+        "data": "synthetic",
+        "hbm_gbps": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
+        "stream_read": stream_ref,
+        "config": {"workload": f"output_head_{args.workload}", "tokens": T, "vocab": V, "d_model": 2048,
+                   "weights": fmt, "head_instances": NL, "bytes_per_step": step_bytes,
+                   "launch": "hip_graph_replay" if graph_ms is not None else "plain",
+                   "plain_launch_ms_per_step": round(ms, 5), "kernel_ms": round(kern_ms, 5)},
+        "roofline": {"bound": "hbm", "kernel": "head_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "frac_of_stream_read": round(achieved / stream_ref["gbps"], 4) if stream_ref else None,
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -544,10 +669,13 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
-    if args.workload not in synth.CONFIGS:
-        print(f"unknown workload {args.workload}; one of {sorted(synth.CONFIGS)}", file=sys.stderr)
+    if args.workload in synth.HEAD_CONFIGS:
+        out = bench_head(args, moe, synth, torch, np)
+    elif args.workload not in synth.CONFIGS:
+        print(f"unknown workload {args.workload}; one of {sorted(synth.CONFIGS) + sorted(synth.HEAD_CONFIGS)}",
+              file=sys.stderr)
         return 2
-    if synth.CONFIGS[args.workload]["layers"] == 1:
+    elif synth.CONFIGS[args.workload]["layers"] == 1:
         out = bench_layer(args, moe, synth, torch, np)
     else:
         out = bench_stack(args, moe, synth, torch, np)

@@ -170,6 +170,27 @@ moe_status moe_stack_workspace_size(const moe_layer* const* layers, int32_t n_la
 moe_status moe_stack_forward(const moe_layer* const* layers, int32_t n_layers, void* x, int32_t T, float rms_eps,
                              const moe_route_out* routes, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Output head (the step after the last MoE layer of a decode pass): logits
+ * over the vocabulary,
+ *   logits[t][v] = sum_k x[t][k] * W[v][k]      (fp32, K = d_model),
+ * with W stored like an expert matrix (moe_qmat with n = 1, rows = vocab,
+ * cols = d_model) in q4_1, NVFP4 or bf16.  The review's section "The
+ * quantisation recipe is the most transferable part" stores this head in 4
+ * bits because, with 2.5 B active parameters, it is a large share of the
+ * weights each token reads; the vocabulary size is not given there.
+ *   x      : bf16 [T][d_model] (16 B aligned), 0 <= T <= 65536
+ *   logits : fp32 [T][vocab] (4 B aligned), written in full
+ *   w, wfmt: the head matrix (device pointers, caller-owned, same alignment
+ *            rules as the experts') and its format, MOE_W_BF16 / MOE_W_Q4_1 /
+ *            MOE_W_NVFP4
+ *   vocab  : 1 .. MOE_HEAD_MAX_VOCAB; d_model must be 2048 in this build
+ * Asynchronous on `stream` like the layer forward; T = 0 is a no-op.  Bad
+ * arguments return MOE_ERR_INVALID_ARG (MOE_ERR_UNSUPPORTED for d_model)
+ * before anything is enqueued.  No workspace and no device allocation. */
+#define MOE_HEAD_MAX_VOCAB 1048576
+moe_status moe_head_forward(const void* x, int32_t T, const moe_qmat* w, int32_t wfmt, int32_t vocab,
+                            int32_t d_model, float* logits, void* stream);
+
 /* Measurement helper, not part of the layer: a plain streaming read of
  * `bytes` bytes of device memory at src, 16 bytes per load with eight loads in
  * flight per thread, on `grid` workgroups of 256 threads (0 = one per compute

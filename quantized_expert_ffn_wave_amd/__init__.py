@@ -22,7 +22,8 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
 WFMT = {"bf16": 0, "q4_1": 1, "nvfp4": 2}
 EXPORTED = ["moe_layer_create", "moe_layer_destroy", "moe_layer_workspace_size", "moe_desc_workspace_size",
             "moe_layer_forward", "moe_layer_forward_staged", "moe_stack_workspace_size", "moe_stack_forward",
-            "moe_stream_read", "moe_last_error", "moe_version"]
+            "moe_head_forward", "moe_stream_read", "moe_last_error", "moe_version"]
+HEAD_MAX_VOCAB = 1048576
 N_STAGE_EVENTS = 7
 STAGES = ["router", "topk", "bucket", "gate_up", "down", "combine"]
 
@@ -81,6 +82,8 @@ _lib.moe_stack_workspace_size.restype = ctypes.c_int
 _lib.moe_stack_forward.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _i32, ctypes.c_float,
                                    ctypes.POINTER(moe_route_out), _vp, _sz, _vp]
 _lib.moe_stack_forward.restype = ctypes.c_int
+_lib.moe_head_forward.argtypes = [_vp, _i32, ctypes.POINTER(moe_qmat), _i32, _i32, _i32, _vp, _vp]
+_lib.moe_head_forward.restype = ctypes.c_int
 _lib.moe_stream_read.argtypes = [_vp, _sz, _vp, _i32, _vp]
 _lib.moe_stream_read.restype = ctypes.c_int
 _lib.moe_last_error.restype = ctypes.c_char_p
@@ -167,6 +170,12 @@ def moe_stack_forward(handles, x_ptr: int, T: int, eps: float, routes, ws_ptr: i
 
 
 
+def moe_head_forward(x_ptr: int, T: int, w: moe_qmat, wfmt: int, vocab: int, d_model: int, logits_ptr: int,
+                     stream: int) -> None:
+    _check(_lib.moe_head_forward(x_ptr, T, ctypes.byref(w), wfmt, vocab, d_model, logits_ptr, stream),
+           "moe_head_forward")
+
+
 def moe_stream_read(src_ptr: int, nbytes: int, sink_ptr: int, grid: int, stream: int) -> None:
     _check(_lib.moe_stream_read(src_ptr, nbytes, sink_ptr, grid, stream), "moe_stream_read")
 
@@ -234,6 +243,36 @@ class DeviceLayer:
             self.close()
         except Exception:
             pass
+
+
+class DeviceMatrix:
+    """One stored matrix (matrix 0 of a host set with the attributes codes,
+    scales, tensor_scale, fmt, rows, cols) copied to the device, with the
+    moe_qmat that points at it."""
+
+    def __init__(self, host, device="cuda"):
+        self.fmt, self.rows, self.cols = host.fmt, host.rows, host.cols
+        self.keep = []
+
+        def ptr(a):
+            if a is None:
+                return None
+            t = _to_dev(a, device)
+            self.keep.append(t)
+            return t.data_ptr()
+
+        ts = host.tensor_scale[0:1] if host.tensor_scale is not None else None
+        self.qmat = moe_qmat(ptr(host.codes[0]), ptr(host.scales[0] if host.scales is not None else None), ptr(ts))
+
+
+def head_forward(m: DeviceMatrix, x, logits=None):
+    """logits = x W^T for a bf16 torch tensor x [T][d] and a head matrix on the device."""
+    import torch
+    T = x.shape[0]
+    if logits is None:
+        logits = torch.empty((T, m.rows), dtype=torch.float32, device=x.device)
+    moe_head_forward(x.data_ptr(), T, m.qmat, WFMT[m.fmt], m.rows, m.cols, logits.data_ptr(), current_stream())
+    return logits
 
 
 def alloc_workspace(nbytes: int, device="cuda"):

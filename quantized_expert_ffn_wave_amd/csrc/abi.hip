@@ -350,6 +350,38 @@ moe_status moe_stack_forward(const moe_layer* const* layers, int32_t n, void* x,
   return MOE_OK;
 }
 
+moe_status moe_head_forward(const void* x, int32_t T, const moe_qmat* w, int32_t wfmt, int32_t vocab,
+                            int32_t d_model, float* logits, void* stream) {
+  if (T < 0 || T > 65536) return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, 65536]", T);
+  if (vocab < 1 || vocab > MOE_HEAD_MAX_VOCAB)
+    return fail(MOE_ERR_INVALID_ARG, "vocab=%d outside [1, %d]", vocab, MOE_HEAD_MAX_VOCAB);
+  if (wfmt < MOE_W_BF16 || wfmt > MOE_W_NVFP4) return fail(MOE_ERR_INVALID_ARG, "unknown wfmt %d", wfmt);
+  if (d_model != moe::D_MODEL)
+    return fail(MOE_ERR_UNSUPPORTED, "this build has head kernels for d_model=%d (got %d)", moe::D_MODEL, d_model);
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "w is NULL");
+  moe_status st = check_qmat(*w, wfmt, "head");
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !aligned(x, 16)) return fail(MOE_ERR_INVALID_ARG, "x is NULL or not 16-byte aligned");
+  if (!logits || !aligned(logits, 4)) return fail(MOE_ERR_INVALID_ARG, "logits is NULL or not 4-byte aligned");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int n_cu = 0;
+  if ((e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+    return hip_fail(e, "device query");
+  moe::HeadArgs a;
+  a.x = (const uint16_t*)x;
+  a.w = qm(*w);
+  a.logits = logits;
+  a.T = T;
+  a.V = vocab;
+  a.fmt = wfmt;
+  if ((e = moe::launch_head(a, n_cu > 0 ? n_cu : 256, (hipStream_t)stream)) != hipSuccess)
+    return hip_fail(e, "head launch");
+  return MOE_OK;
+}
+
 moe_status moe_stream_read(const void* src, size_t bytes, void* sink, int32_t grid, void* stream) {
   if (!src || !aligned(src, 16)) return fail(MOE_ERR_INVALID_ARG, "src must be a 16 B aligned device pointer");
   if (bytes == 0 || bytes % 16) return fail(MOE_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");

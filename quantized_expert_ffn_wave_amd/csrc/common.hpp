@@ -144,6 +144,13 @@ __device__ inline float silu_mul(float g, float u) { return g * __builtin_amdgcn
 
 // Host-side launchers (defined in the .hip files, called by the ABI layer).
 namespace moe {
+// Output head GEMV: logits[t][v] = sum_k x[t][k] w[v][k], D_MODEL columns.
+struct HeadArgs {
+  const uint16_t* x;  // bf16 [T][D_MODEL]
+  QMat w;             // [V][D_MODEL] in `fmt`
+  float* logits;      // fp32 [T][V]
+  int T, V, fmt;
+};
 hipError_t launch_router(const LayerArgs& a, hipStream_t s);
 hipError_t launch_topk(const LayerArgs& a, hipStream_t s);
 hipError_t launch_bucket(const LayerArgs& a, hipStream_t s);
@@ -152,6 +159,8 @@ hipError_t launch_combine(const LayerArgs& a, hipStream_t s);
 // max_wgs workgroups, else as many as are resident on n_cu CUs at once
 hipError_t launch_ffn(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s);
 hipError_t launch_stack_init(const uint16_t* x, float* r, uint16_t* xn, int T, float eps, hipStream_t s);
+// output head over n_cu compute units
+hipError_t launch_head(const HeadArgs& a, int n_cu, hipStream_t s);
 // plain streaming read of bytes (a multiple of 16) from src on grid workgroups
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int grid, hipStream_t s);
 }  // namespace moe

@@ -1234,4 +1234,143 @@ hipError_t launch_stack_init(const uint16_t* x, float* r, uint16_t* xn, int T, f
   return hipGetLastError();
 }
 
+// ======================================================================================
+// Output head: logits[t][v] = sum_k x[t][k] W[v][k] over a vocabulary of V rows of
+// D_MODEL columns.  The review ("The quantisation recipe is the most transferable
+// part") stores this head in 4 bits because, with 2.5 B active parameters, it is a
+// large share of the bytes each token reads.  It is a pure streaming GEMV on the
+// vector path's units: persistent workgroups over items of HEAD_ROWS rows (a wave
+// takes a quarter: two pairs of 4-row groups), tokens in groups of 4 (one 4x4x4
+// operand, staged in LDS once per group), and each wave's ring of weight loads
+// running on from one item into the next.  Item c is row chunk c / ntg of token
+// group c % ntg, so with the grid a multiple of the group count a workgroup keeps
+// its tokens.
+// ======================================================================================
+constexpr int HEAD_ROWS = 64;
+
+template <int FMT>
+__global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void head_kernel(HeadArgs a) {
+  __shared__ MvSmem sm;
+  using G = GV<FMT>;
+  // unit u of an item: pair p = u / 8 of 4-row groups, K-quarter q = (u / 2) % 4,
+  // group m = u % 2 of the pair; lane (b, j) reads chunk 16 q + b of row
+  // r0 + 8 p + 4 m + j (clamped into the vocabulary; rows past it are read
+  // again and not stored)
+  constexpr int D = MV_UP_RING<FMT>, NU = 2 * 8;
+  static_assert(NU % D == 0 && HEAD_ROWS == 4 * 16, "4 waves x 2 pairs of 4-row groups per item");
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 3, b = lane >> 2;
+  const int ntg = ceil_div(a.T, GV_GROUP), n = ceil_div(a.V, HEAD_ROWS) * ntg, G_ = (int)gridDim.x;
+  int c = blockIdx.x;
+  if (c >= n) return;
+  auto first_row = [&](int cc) { return (cc / ntg) * HEAD_ROWS + wave * (HEAD_ROWS / 4); };
+  // first row of load u's 4-row group (wave-uniform) and the lane's row offset
+  // from it, both clamped into the vocabulary
+  auto group_base = [&](int r0_, int u) { return min(r0_ + 8 * (u >> 3) + 4 * (u & 1), a.V - 1); };
+  auto lane_sub = [&](int base) { return (uint32_t)min(j, a.V - 1 - base); };
+  // 4-bit formats: the codes ride in the ring; the scales of a row group's 4
+  // K-quarters (adjacent in storage) come in one load with the group's first
+  // unit and are handed to each unit as it is used
+  constexpr bool S4 = FMT != FMT_BF16;
+  static_assert(!S4 || D == 8, "scale loads follow the ring's 8-load row groups");
+  auto load_unit = [&](int r0_, int u) {
+    const int base = group_base(r0_, u);
+    if constexpr (S4) return G::template load_codes<true>(a.w, (size_t)base, lane_sub(base), 16 * ((u >> 1) & 3) + b, D_MODEL);
+    else return G::template load<true>(a.w, (size_t)base, lane_sub(base), 16 * ((u >> 1) & 3) + b, D_MODEL);
+  };
+  auto load_sc = [&](int r0_, int u) {
+    const int base = group_base(r0_, u);
+    return G::template load_scales4<true>(a.w, (size_t)base, lane_sub(base), (uint32_t)b);
+  };
+  // tokens 4 tg .. 4 tg + 3 into LDS (zeros past T), in the vector path's operand order
+  auto stage = [&](int tg) {
+    MvStage st;
+    const int t = 4 * tg + (int)threadIdx.x / 64, cc = threadIdx.x % 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.v[i] = u32x4{0u, 0u, 0u, 0u};
+    if (t < a.T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.v[i] = ld16<false>(a.x + (size_t)t * D_MODEL + 32 * cc + 8 * i);
+    }
+    mv_stage_store<FMT, true>(st, sm, 0);
+  };
+  int tg = c % ntg, r0 = first_row(c);
+  typename G::Raw ring[D];
+  typename G::Scales4 s4c[2] = {}, s4n[2] = {};  // scales of the current / next pair, row group m
+#pragma unroll
+  for (int i = 0; i < D; ++i) ring[i] = load_unit(r0, i);
+  if constexpr (S4) {
+    s4c[0] = load_sc(r0, 0);
+    s4c[1] = load_sc(r0, 1);
+  }
+  stage(tg);
+  __syncthreads();
+  const float ts = (FMT == FMT_NVFP4) ? a.w.ts[0] : 1.f;
+  // after a pair's reduction, lanes with bit 2 clear hold row group 2 p + bit 5
+  // of token 2 * bit 4 + bit 3, row j
+  const int my_t = ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
+#pragma unroll 1
+  for (;;) {
+    const int nc = c + G_;
+    const bool has_next = nc < n;
+    const int nr0 = has_next ? first_row(nc) : r0;
+    f32x4 acc[2] = {}, negK = {}, S = {};
+    uint32_t xq[16];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int p = u >> 3, q = (u >> 1) & 3, m = u & 1;
+      if (m == 0) {
+        mv_acts<FMT>(sm, 0, 16 * q + b, j, xq, negK, S);
+        if (q == 0) acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      typename G::Raw cur = ring[u % D];
+      if constexpr (S4) G::set_scale(cur, s4c[m], q);
+      const int un = u + D;  // the load issued now
+      if (un < NU) {
+        ring[u % D] = load_unit(r0, un);
+        if (S4 && ((un >> 1) & 3) == 0) s4n[m] = load_sc(r0, un);
+      } else if (has_next) {
+        ring[u % D] = load_unit(nr0, un - NU);
+        if (S4 && (((un - NU) >> 1) & 3) == 0) s4n[m] = load_sc(nr0, un - NU);
+      }
+      MV<FMT>::unit(cur, xq, negK, S, acc[m]);
+      if (u % 8 == 7) {
+        if constexpr (S4) {
+          s4c[0] = s4n[0];
+          s4c[1] = s4n[1];
+        }
+        const float v = mv_reduce8(acc[0], acc[1]) * ts;
+        const int row = r0 + 8 * p + 4 * ((lane >> 5) & 1) + j, t = 4 * tg + my_t;
+        if ((lane & 4) == 0 && row < a.V && t < a.T) a.logits[(size_t)t * a.V + row] = v;
+      }
+    }
+    if (!has_next) break;
+    const int ntgc = nc % ntg;
+    if (ntgc != tg) {  // another token group: every wave is done with the tile before it is replaced
+      __syncthreads();
+      stage(ntgc);
+      __syncthreads();
+      tg = ntgc;
+    }
+    c = nc;
+    r0 = nr0;
+  }
+}
+
+hipError_t launch_head(const HeadArgs& a, int n_cu, hipStream_t s) {
+  const int n = ceil_div(a.V, HEAD_ROWS) * ceil_div(a.T, GV_GROUP);
+  auto go = [&](auto kernel) {
+    static_assert(FFN_WG_PER_CU<FMT_Q4_1> == 2, "two workgroups per CU");
+    int grid = n_cu * 2;
+    if (n < grid) grid = n;
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+  };
+  switch (a.fmt) {
+    case FMT_Q4_1: return go(head_kernel<FMT_Q4_1>);
+    case FMT_NVFP4: return go(head_kernel<FMT_NVFP4>);
+    default: return go(head_kernel<FMT_BF16>);
+  }
+}
+
 }  // namespace moe

@@ -128,6 +128,33 @@ def test_forward_argument_errors_without_a_layer():
     assert moe.version().startswith("moe_ffn gfx950")
 
 
+def test_head_argument_errors_before_the_device():
+    """moe_head_forward checks every argument it can without a device; T = 0 is
+    a no-op that succeeds once the matrix pointers check out."""
+    lib = moe.lib()
+    Q, BF, NV = moe.WFMT["q4_1"], moe.WFMT["bf16"], moe.WFMT["nvfp4"]
+    good = moe.moe_qmat(0x1000, 0x2000, 0x3000)
+    ref = ctypes.byref(good)
+    X, L = 0x4000, 0x5000
+    inv, uns = moe.MOE_ERR_INVALID_ARG, moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_head_forward(X, -1, ref, Q, 100, 2048, L, None) == inv
+    assert lib.moe_head_forward(X, 65537, ref, Q, 100, 2048, L, None) == inv
+    assert lib.moe_head_forward(X, 1, ref, Q, 0, 2048, L, None) == inv
+    assert lib.moe_head_forward(X, 1, ref, Q, moe.HEAD_MAX_VOCAB + 1, 2048, L, None) == inv
+    assert lib.moe_head_forward(X, 1, ref, 3, 100, 2048, L, None) == inv
+    assert lib.moe_head_forward(X, 1, ref, Q, 100, 4096, L, None) == uns
+    assert lib.moe_head_forward(X, 1, None, Q, 100, 2048, L, None) == inv
+    assert lib.moe_head_forward(X, 1, ctypes.byref(moe.moe_qmat(0x1008, 0x2000, 0)), BF, 100, 2048, L, None) == inv
+    assert lib.moe_head_forward(X, 1, ctypes.byref(moe.moe_qmat(0x1000, 0x2008, 0)), Q, 100, 2048, L, None) == inv
+    assert lib.moe_head_forward(X, 1, ctypes.byref(moe.moe_qmat(0x1000, 0x2008, 0)), NV, 100, 2048, L, None) == inv
+    assert "tensor_scale" in moe.last_error()
+    assert lib.moe_head_forward(None, 1, ref, Q, 100, 2048, L, None) == inv
+    assert lib.moe_head_forward(X + 8, 1, ref, Q, 100, 2048, L, None) == inv
+    assert lib.moe_head_forward(X, 1, ref, Q, 100, 2048, None, None) == inv
+    assert lib.moe_head_forward(X, 1, ref, Q, 100, 2048, L + 2, None) == inv
+    assert lib.moe_head_forward(None, 0, ref, Q, 100, 2048, None, None) == moe.MOE_OK
+
+
 def test_one_hip_runtime_per_process():
     """Importing the binding alone leaves one libamdhip64 mapped (torch's), so
     that the library and torch share a runtime whatever is imported first."""
