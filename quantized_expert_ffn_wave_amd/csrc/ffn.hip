@@ -1238,13 +1238,12 @@ hipError_t launch_stack_init(const uint16_t* x, float* r, uint16_t* xn, int T, f
 // Output head: logits[t][v] = sum_k x[t][k] W[v][k] over a vocabulary of V rows of
 // D_MODEL columns.  The review ("The quantisation recipe is the most transferable
 // part") stores this head in 4 bits because, with 2.5 B active parameters, it is a
-// large share of the bytes each token reads.  It is a pure streaming GEMV on the
-// vector path's units: persistent workgroups over items of HEAD_ROWS rows (a wave
-// takes a quarter: two pairs of 4-row groups), tokens in groups of 4 (one 4x4x4
-// operand, staged in LDS once per group), and each wave's ring of weight loads
-// running on from one item into the next.  Item c is row chunk c / ntg of token
-// group c % ntg, so with the grid a multiple of the group count a workgroup keeps
-// its tokens.
+// large share of the bytes each token reads.
+//
+// Up to 4 tokens it is a streaming GEMV on the vector path's units: persistent
+// workgroups over items of HEAD_ROWS rows (a wave takes 16: two pairs of 4-row
+// groups), the 4 tokens in LDS in operand order, and each wave's ring of weight
+// loads running on from one item into the next.
 // ======================================================================================
 constexpr int HEAD_ROWS = 64;
 
@@ -1260,10 +1259,10 @@ __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void head_kernel(HeadArgs 
   static_assert(NU % D == 0 && HEAD_ROWS == 4 * 16, "4 waves x 2 pairs of 4-row groups per item");
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 3, b = lane >> 2;
-  const int ntg = ceil_div(a.T, GV_GROUP), n = ceil_div(a.V, HEAD_ROWS) * ntg, G_ = (int)gridDim.x;
+  const int n = ceil_div(a.V, HEAD_ROWS), G_ = (int)gridDim.x;
   int c = blockIdx.x;
   if (c >= n) return;
-  auto first_row = [&](int cc) { return (cc / ntg) * HEAD_ROWS + wave * (HEAD_ROWS / 4); };
+  auto first_row = [&](int cc) { return cc * HEAD_ROWS + wave * (HEAD_ROWS / 4); };
   // first row of load u's 4-row group (wave-uniform) and the lane's row offset
   // from it, both clamped into the vocabulary
   auto group_base = [&](int r0_, int u) { return min(r0_ + 8 * (u >> 3) + 4 * (u & 1), a.V - 1); };
@@ -1282,19 +1281,7 @@ __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void head_kernel(HeadArgs 
     const int base = group_base(r0_, u);
     return G::template load_scales4<true>(a.w, (size_t)base, lane_sub(base), (uint32_t)b);
   };
-  // tokens 4 tg .. 4 tg + 3 into LDS (zeros past T), in the vector path's operand order
-  auto stage = [&](int tg) {
-    MvStage st;
-    const int t = 4 * tg + (int)threadIdx.x / 64, cc = threadIdx.x % 64;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st.v[i] = u32x4{0u, 0u, 0u, 0u};
-    if (t < a.T) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st.v[i] = ld16<false>(a.x + (size_t)t * D_MODEL + 32 * cc + 8 * i);
-    }
-    mv_stage_store<FMT, true>(st, sm, 0);
-  };
-  int tg = c % ntg, r0 = first_row(c);
+  int r0 = first_row(c);
   typename G::Raw ring[D];
   typename G::Scales4 s4c[2] = {}, s4n[2] = {};  // scales of the current / next pair, row group m
 #pragma unroll
@@ -1303,7 +1290,17 @@ __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void head_kernel(HeadArgs 
     s4c[0] = load_sc(r0, 0);
     s4c[1] = load_sc(r0, 1);
   }
-  stage(tg);
+  {  // the tokens into LDS (zeros past T): a thread per (token, chunk)
+    const int t = (int)threadIdx.x >> 6, cc = (int)threadIdx.x & 63;
+    MvStage st;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.v[i] = u32x4{0u, 0u, 0u, 0u};
+    if (t < a.T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.v[i] = ld16<false>(a.x + (size_t)t * D_MODEL + 32 * cc + 8 * i);
+    }
+    mv_stage_store<FMT, true>(st, sm, 0);
+  }
   __syncthreads();
   const float ts = (FMT == FMT_NVFP4) ? a.w.ts[0] : 1.f;
   // after a pair's reduction, lanes with bit 2 clear hold row group 2 p + bit 5
@@ -1340,36 +1337,229 @@ __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void head_kernel(HeadArgs 
           s4c[1] = s4n[1];
         }
         const float v = mv_reduce8(acc[0], acc[1]) * ts;
-        const int row = r0 + 8 * p + 4 * ((lane >> 5) & 1) + j, t = 4 * tg + my_t;
+        const int row = r0 + 8 * p + 4 * ((lane >> 5) & 1) + j, t = my_t;
         if ((lane & 4) == 0 && row < a.V && t < a.T) a.logits[(size_t)t * a.V + row] = v;
       }
     }
     if (!has_next) break;
-    const int ntgc = nc % ntg;
-    if (ntgc != tg) {  // another token group: every wave is done with the tile before it is replaced
+    c = nc;
+    r0 = nr0;
+  }
+}
+
+// ---- the head on the matrix cores (batches of more than 4 tokens) -----------------
+// With more than one 4-token group the 4x4x4 products, not the weight stream,
+// set the vector kernel's pace.  Here the 16x16x32 MFMA multiplies 16 tokens
+// (A, from LDS) by 16 vocabulary rows (B, decoded in registers): lane (r, g)
+// holds row r of a 16-row block and k-group g, and each of its 16-byte weight
+// loads is one 32-element block that feeds 4 MFMAs per 16-token tile.  A pass
+// keeps NT tiles (16 NT tokens) resident in LDS for all of its items; a wave
+// takes RB blocks of 16 rows, its ring holds D loads, and an item is the
+// waves' rows.  K-step z = 4 i + a (a < 4) of a row reads block 16 i + 4 a + g:
+// four steps in a row read 256 contiguous bytes of it, and the scales of the
+// steps with one a are adjacent in storage (one load per a, per item).  The
+// x tile: [block][token][16-byte sub-block s XOR (token / 4) mod 4] in the weights'
+// decode order, so that the 16 lanes of a k-group read 16 tokens without bank
+// conflicts.  Batches beyond 32 tokens take passes of 32.  Item c is row chunk
+// rc of pass tp, numbered so that the passes of a row chunk fall on one XCD
+// (workgroup id mod 8 under round-robin dispatch, with the grid a multiple of 8)
+// and on workgroups that run at the same time, where their repeated reads of the
+// chunk can meet in that XCD's L2.
+template <int NT> constexpr int HMF_W = NT == 1 ? 4 : 8;  // waves per workgroup
+template <int NT> constexpr int HMF_RB = NT == 1 ? 2 : 1;  // 16-row blocks per wave
+// weight loads in flight per wave (a bf16 load is 64 bytes a lane, a 4-bit one 16)
+template <int FMT> constexpr int HMF_D = FMT == FMT_BF16 ? 4 : 8;
+template <int NT> constexpr int HMF_ROWS = HMF_W<NT> * 16 * HMF_RB<NT>;  // rows per item
+template <int NT> struct HeadMfSmem {
+  u32x4 x[MV_CHUNKS][16 * NT][4];
+};
+
+template <int FMT> __device__ inline f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (OPER_F16<FMT>)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                  0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+}
+
+template <int FMT, int NT>
+__global__ __launch_bounds__(64 * HMF_W<NT>, NT == 1 ? 2 : 1) void head_mf_kernel(HeadArgs a) {
+  constexpr int W = HMF_W<NT>, RB = HMF_RB<NT>, D = HMF_D<FMT>, NU = 16 * RB, TT = 16 * NT, ROWS = HMF_ROWS<NT>;
+  static_assert(NU % D == 0, "the ring holds whole items");
+  __shared__ HeadMfSmem<NT> sm;
+  using G = GV<FMT>;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int ntp = ceil_div(a.T, TT), nrc = ceil_div(a.V, ROWS);
+  // items: XCD slot c % 8, then k = c / 8 -> row chunk 8 (k / ntp) + slot, pass k % ntp
+  const int n = 8 * ntp * ceil_div(nrc, 8), G_ = (int)gridDim.x;
+  int c = blockIdx.x;
+  if (c >= n) return;
+  auto item_tp = [&](int cc) { return (cc >> 3) % ntp; };
+  auto first_row = [&](int cc) { return (8 * ((cc >> 3) / ntp) + (cc & 7)) * ROWS + wave * 16 * RB; };
+  // unit u: k-step z = u / RB of row block rb = u % RB; rows clamped into the
+  // vocabulary (read again, never stored)
+  auto row_base = [&](int r0_, int rb) { return min(r0_ + 16 * rb, a.V - 1); };
+  auto lane_sub = [&](int base) { return (uint32_t)min(r16, a.V - 1 - base); };
+  auto block_of = [&](int z) { return 16 * (z >> 2) + 4 * (z & 3) + g; };
+  constexpr bool S4 = FMT != FMT_BF16;
+  auto load_unit = [&](int r0_, int u) {
+    const int base = row_base(r0_, u % RB);
+    if constexpr (S4) return G::template load_codes<true>(a.w, (size_t)base, lane_sub(base), block_of(u / RB), D_MODEL);
+    else return G::template load<true>(a.w, (size_t)base, lane_sub(base), block_of(u / RB), D_MODEL);
+  };
+  // scales of blocks 4 s + g + 16 i (i < 4): the steps z = 4 i + s of row block rb
+  typename G::Scales4 sc[RB][4], sn[RB][4];
+  auto load_scales = [&](int r0_, typename G::Scales4 (&dst)[RB][4]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int base = row_base(r0_, rb);
+#pragma unroll
+      for (int s_ = 0; s_ < 4; ++s_)
+        dst[rb][s_] = G::template load_scales4<true>(a.w, (size_t)base, lane_sub(base), (uint32_t)(4 * s_ + g));
+    }
+  };
+  // the pass's tokens TT tp .. into LDS (zeros past T): thread (token, block)
+  // pairs, TT / W per thread, all loads in flight before the stores
+  static_assert(TT % W == 0, "whole tokens per wave");
+  auto stage = [&](int tp) {
+    const int blk = (int)threadIdx.x & 63, t0 = (int)threadIdx.x >> 6;
+    u32x4 v[TT / W][4];
+#pragma unroll
+    for (int k = 0; k < TT / W; ++k) {
+      const int t = TT * tp + t0 + W * k;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        v[k][i] = (t < a.T) ? ld16<false>(a.x + (size_t)t * D_MODEL + 32 * blk + 8 * i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < TT / W; ++k) {
+      const int tl = t0 + W * k;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t e[4] = {v[k][i][0], v[k][i][1], v[k][i][2], v[k][i][3]}, o[4];
+        if constexpr (OPER_F16<FMT>) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) e[q] = bf16x2_to_f16x2(e[q]);
+        }
+        if constexpr (FMT == FMT_Q4_1) q4_order(e[0], e[1], e[2], e[3], o);
+        else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[q] = e[q];
+        }
+        sm.x[blk][tl][i ^ ((tl >> 2) & 3)] = u32x4{o[0], o[1], o[2], o[3]};
+      }
+    }
+  };
+  int tp = item_tp(c), r0 = first_row(c);
+  typename G::Raw ring[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) ring[i] = load_unit(r0, i);
+  if constexpr (S4) load_scales(r0, sc);
+  stage(tp);
+  __syncthreads();
+  const float ts = (FMT == FMT_NVFP4) ? a.w.ts[0] : 1.f;
+  const int swz = (r16 >> 2) & 3;
+#pragma unroll 1
+  for (;;) {
+    const int nc = c + G_;
+    const bool has_next = nc < n;
+    const int nr0 = has_next ? first_row(nc) : r0;
+    f32x4 acc[RB][NT];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) acc[rb][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int z = 0; z < 16; ++z) {
+      u32x4 xa[NT][4];  // A operands: tokens 16 tt + r16 of block block_of(z), sub-blocks s
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int s_ = 0; s_ < 4; ++s_) xa[tt][s_] = sm.x[block_of(z)][16 * tt + r16][s_ ^ swz];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int u = z * RB + rb;
+        typename G::Raw cur = ring[u % D];
+        if constexpr (S4) G::set_scale(cur, sc[rb][z & 3], z >> 2);
+        const int un = u + D;  // the load issued now
+        if (un < NU) {
+          ring[u % D] = load_unit(r0, un);
+        } else if (has_next) {
+          ring[u % D] = load_unit(nr0, un - NU);
+          if (S4 && un == NU) load_scales(nr0, sn);
+        }
+        uint32_t w[16];
+        G::decode(cur, w);
+#pragma unroll
+        for (int s_ = 0; s_ < 4; ++s_)
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt)
+            acc[rb][tt] = mfma16<FMT>(xa[tt][s_], u32x4{w[4 * s_], w[4 * s_ + 1], w[4 * s_ + 2], w[4 * s_ + 3]},
+                                      acc[rb][tt]);
+      }
+    }
+    // acc[rb][tt][j]: token 16 tt + 4 g + j of the pass, row r0 + 16 rb + r16
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int row = r0 + 16 * rb + r16;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = TT * tp + 16 * tt + 4 * g + j;
+          if (row < a.V && t < a.T) a.logits[(size_t)t * a.V + row] = acc[rb][tt][j] * ts;
+        }
+    }
+    if (!has_next) break;
+    if constexpr (S4) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int s_ = 0; s_ < 4; ++s_) sc[rb][s_] = sn[rb][s_];
+    }
+    const int ntpc = item_tp(nc);
+    if (ntpc != tp) {  // another pass: every wave is done with the tile before it is replaced
       __syncthreads();
-      stage(ntgc);
+      stage(ntpc);
       __syncthreads();
-      tg = ntgc;
+      tp = ntpc;
     }
     c = nc;
     r0 = nr0;
   }
 }
 
+template <int FMT, int NT> hipError_t launch_head_mf(const HeadArgs& a, int n_cu, hipStream_t s) {
+  const int ntp = ceil_div(a.T, 16 * NT), nrc = ceil_div(a.V, HMF_ROWS<NT>);
+  const int n = 8 * ntp * ceil_div(nrc, 8);
+  int grid = n_cu * (NT == 1 ? 2 : 1);
+  grid -= grid % 8;
+  if (grid < 8) grid = 8;
+  if (n < grid) grid = n;
+  hipLaunchKernelGGL((head_mf_kernel<FMT, NT>), dim3(grid), dim3(64 * HMF_W<NT>), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int FMT> hipError_t launch_head_vec(const HeadArgs& a, int n_cu, hipStream_t s) {
+  const int n = ceil_div(a.V, HEAD_ROWS);
+  int grid = n_cu * FFN_WG_PER_CU<FMT>;
+  if (n < grid) grid = n;
+  hipLaunchKernelGGL(head_kernel<FMT>, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int FMT> hipError_t launch_head_fmt(const HeadArgs& a, int n_cu, hipStream_t s) {
+  if (a.T <= GV_GROUP) return launch_head_vec<FMT>(a, n_cu, s);
+  return a.T <= 16 ? launch_head_mf<FMT, 1>(a, n_cu, s) : launch_head_mf<FMT, 2>(a, n_cu, s);
+}
+
 hipError_t launch_head(const HeadArgs& a, int n_cu, hipStream_t s) {
-  const int n = ceil_div(a.V, HEAD_ROWS) * ceil_div(a.T, GV_GROUP);
-  auto go = [&](auto kernel) {
-    static_assert(FFN_WG_PER_CU<FMT_Q4_1> == 2, "two workgroups per CU");
-    int grid = n_cu * 2;
-    if (n < grid) grid = n;
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, a);
-    return hipGetLastError();
-  };
   switch (a.fmt) {
-    case FMT_Q4_1: return go(head_kernel<FMT_Q4_1>);
-    case FMT_NVFP4: return go(head_kernel<FMT_NVFP4>);
-    default: return go(head_kernel<FMT_BF16>);
+    case FMT_Q4_1: return launch_head_fmt<FMT_Q4_1>(a, n_cu, s);
+    case FMT_NVFP4: return launch_head_fmt<FMT_NVFP4>(a, n_cu, s);
+    default: return launch_head_fmt<FMT_BF16>(a, n_cu, s);
   }
 }
 

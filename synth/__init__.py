@@ -271,7 +271,10 @@ CONFIGS = {
 HEAD_CONFIGS = {
     "head_v151552_t1_q4_1": dict(T=1, fmt="q4_1", V=HEAD_VOCAB),
     "head_v151552_t4_q4_1": dict(T=4, fmt="q4_1", V=HEAD_VOCAB),
+    "head_v151552_t8_q4_1": dict(T=8, fmt="q4_1", V=HEAD_VOCAB),
+    "head_v151552_t16_q4_1": dict(T=16, fmt="q4_1", V=HEAD_VOCAB),
     "head_v151552_t32_q4_1": dict(T=32, fmt="q4_1", V=HEAD_VOCAB),
+    "head_v151552_t64_q4_1": dict(T=64, fmt="q4_1", V=HEAD_VOCAB),
     "head_v151552_t4_nvfp4": dict(T=4, fmt="nvfp4", V=HEAD_VOCAB),
 }
 
