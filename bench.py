@@ -70,10 +70,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """HBM bytes per gate/up launch from the committed counter summary, if it was
-    taken on the current kernel source (else None)."""
-    path = os.path.join(PROFILE_DIR, f"ffn_up_{workload}_traffic.txt")
+def read_traffic(workload: str, kernel: str = "ffn_up"):
+    """HBM bytes per launch of the roofline kernel (gate/up, or the head) from the
+    committed counter summary, if it was taken on the current kernel source
+    (else None)."""
+    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -595,6 +596,9 @@ def bench_head(args, moe, synth, torch, np):
         del g, g_rest
     step_ms = graph_ms if graph_ms is not None else ms
     achieved = step_bytes / (kern_ms * 1e-3) / 1e9
+    traffic = read_traffic(args.workload, "head")
+    if args.copy_calibration:
+        copy_calibration(torch)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -632,10 +636,10 @@ def bench_head(args, moe, synth, torch, np):
                    "weights": fmt, "head_instances": NL, "bytes_per_step": step_bytes,
                    "launch": "hip_graph_replay" if graph_ms is not None else "plain",
                    "plain_launch_ms_per_step": round(ms, 5), "kernel_ms": round(kern_ms, 5)},
-        "roofline": {"bound": "hbm", "kernel": "head_kernel", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": "head_kernel (T <= 4) / head_mf_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "frac_of_stream_read": round(achieved / stream_ref["gbps"], 4) if stream_ref else None,
-                     "traffic": None},
+                     "traffic": traffic},
         "cpu_baseline": cpu,
     }
 
