@@ -74,6 +74,8 @@ def lib():
                                  ctypes.POINTER(_Mat), ctypes.c_int64, vp, vp]
         L.orc_max_threads.restype = i32
         L.orc_head_logits.argtypes = [ctypes.POINTER(_Mat), vp, i32, vp, i32, vp, i32]
+        L.orc_attn_prep.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, i32, dbl, dbl, vp, vp]
+        L.orc_attn_decode.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, i32]
         _lib = L
     return _lib
 
@@ -285,6 +287,38 @@ def head_logits(q, x: np.ndarray, rows: np.ndarray | None = None, threads: int =
     out = np.empty((T, n), np.float64)
     if T > 0 and n > 0:
         lib().orc_head_logits(ctypes.byref(m), _p(x), T, _p(r), n, _p(out), threads)
+    return out
+
+
+def attn_prep(q: np.ndarray, k: np.ndarray, q_gain: np.ndarray, k_gain: np.ndarray, pos: np.ndarray, rope: bool,
+              theta: float = 10000.0, eps: float = 1e-6):
+    """The new token's q [B][HQ][D] and k [B][HK][D] (bf16 bits) normalised per
+    head, rotated if `rope`, rounded to bf16: returns (q', k') as bf16 bits."""
+    q = np.ascontiguousarray(q, np.uint16)
+    k = np.ascontiguousarray(k, np.uint16)
+    B, HQ, D = q.shape
+    HK = k.shape[1]
+    qo, ko = np.empty_like(q), np.empty_like(k)
+    g1, g2 = np.ascontiguousarray(q_gain, np.uint16), np.ascontiguousarray(k_gain, np.uint16)
+    p = np.ascontiguousarray(pos, np.int32)
+    lib().orc_attn_prep(_p(q), _p(k), B, HQ, HK, D, _p(g1), _p(g2), _p(p), int(rope), theta, eps, _p(qo), _p(ko))
+    return qo, ko
+
+
+def attn_decode(q: np.ndarray, kc: np.ndarray, vc: np.ndarray, lens: np.ndarray, window: int,
+                sinks: np.ndarray | None, threads: int = 0) -> np.ndarray:
+    """Attention of one token per sequence: q [B][HQ][D], caches [B][cap][HK][D]
+    (bf16 bits), lens [B]; window 0 = full.  Returns fp64 [B][HQ][D]."""
+    q = np.ascontiguousarray(q, np.uint16)
+    kc = np.ascontiguousarray(kc, np.uint16)
+    vc = np.ascontiguousarray(vc, np.uint16)
+    B, HQ, D = q.shape
+    cap, HK = kc.shape[1], kc.shape[2]
+    ln = np.ascontiguousarray(lens, np.int32)
+    sk = None if sinks is None else np.ascontiguousarray(sinks, np.float32)
+    out = np.empty((B, HQ, D), np.float64)
+    if B > 0:
+        lib().orc_attn_decode(_p(q), _p(kc), _p(vc), _p(ln), B, HQ, HK, D, cap, window, _p(sk), _p(out), threads)
     return out
 
 

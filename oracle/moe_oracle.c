@@ -406,4 +406,96 @@ void orc_head_logits(const orc_mat* W, const uint16_t* x, int T, const int32_t* 
   free(xd);
 }
 
+/* ---- decode attention ----------------------------------------------------------
+ * The attention layout of "The architecture is an argument about memory
+ * bandwidth": 32 query heads and 4 key-value heads of dimension 128 (query
+ * head h reads key-value head h / 8); sliding-window layers attend to the
+ * current token and the 512 before it (a window of 513), the other layers to
+ * every earlier token; rotary position embedding on the sliding-window layers
+ * only; an RMSNorm over each head of q and k; a learned sink per query head.
+ * Readings (the pages give no formulas): RMSNorm x / sqrt(mean(x^2) + eps) *
+ * gain; the norm comes before the rotation; the rotation pairs element i with
+ * i + D/2 at angle pos * theta^(-2i/D); scores q.k / sqrt(D); the sink z_h is
+ * one more logit in the softmax's denominator with no value. */
+
+/* Per-head RMSNorm then (if rope) rotation of one head vector x[D] at position
+ * pos; result in y (fp64). */
+static void orc_qk_head(const double* x, int D, const double* gain, double eps, int rope, double theta, int64_t pos,
+                        double* y) {
+  double ss = 0.0;
+  for (int i = 0; i < D; ++i) ss += x[i] * x[i];
+  const double r = 1.0 / sqrt(ss / D + eps);
+  for (int i = 0; i < D; ++i) y[i] = x[i] * r * gain[i];
+  if (!rope) return;
+  const int H = D / 2;
+  for (int i = 0; i < H; ++i) {
+    const double ang = (double)pos * pow(theta, -2.0 * i / D);
+    const double c = cos(ang), s = sin(ang), a = y[i], b = y[i + H];
+    y[i] = a * c - b * s;
+    y[i + H] = b * c + a * s;
+  }
+}
+
+/* The new token's q and k: normalised, rotated (if rope) and rounded to bf16.
+ * q [B][HQ][D], k [B][HK][D] bf16 in; gains [D] (bf16); pos [B]; outputs bf16. */
+void orc_attn_prep(const uint16_t* q, const uint16_t* k, int B, int HQ, int HK, int D, const uint16_t* q_gain,
+                   const uint16_t* k_gain, const int32_t* pos, int rope, double theta, double eps, uint16_t* q_out,
+                   uint16_t* k_out) {
+  double* x = (double*)malloc(sizeof(double) * D);
+  double* y = (double*)malloc(sizeof(double) * D);
+  double* gq = (double*)malloc(sizeof(double) * D);
+  double* gk = (double*)malloc(sizeof(double) * D);
+  for (int i = 0; i < D; ++i) { gq[i] = T_BF16[q_gain[i]]; gk[i] = T_BF16[k_gain[i]]; }
+  for (int b = 0; b < B; ++b) {
+    for (int h = 0; h < HQ + HK; ++h) {
+      const int isq = h < HQ;
+      const uint16_t* src = isq ? q + ((int64_t)b * HQ + h) * D : k + ((int64_t)b * HK + (h - HQ)) * D;
+      uint16_t* dst = isq ? q_out + ((int64_t)b * HQ + h) * D : k_out + ((int64_t)b * HK + (h - HQ)) * D;
+      for (int i = 0; i < D; ++i) x[i] = T_BF16[src[i]];
+      orc_qk_head(x, D, isq ? gq : gk, eps, rope, theta, pos[b], y);
+      for (int i = 0; i < D; ++i) dst[i] = orc_bf16_rne(y[i]);
+    }
+  }
+  free(x); free(y); free(gq); free(gk);
+}
+
+/* Attention of one new token per sequence over its cache.
+ * q [B][HQ][D] bf16 (prepared); kc, vc [B][cap][HK][D] bf16, positions 0 ..
+ * len[b]-1 valid; window 0 = every position, else the last `window` ones;
+ * sinks [HQ] fp32 or NULL (no sink); out [B][HQ][D] fp64.  Each (b, h) is an
+ * independent softmax; threads split them. */
+void orc_attn_decode(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, const int32_t* len, int B, int HQ,
+                     int HK, int D, int cap, int window, const float* sinks, double* out, int nthreads) {
+  int nt = orc_threads(nthreads);
+  const int G = HQ / HK;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+  for (int bh = 0; bh < B * HQ; ++bh) {
+    const int b = bh / HQ, h = bh % HQ, kv = h / G;
+    const int n = len[b];
+    const int lo = (window > 0 && n > window) ? n - window : 0;
+    double* s = (double*)malloc(sizeof(double) * (n > 0 ? n : 1));
+    const uint16_t* qh = q + ((int64_t)b * HQ + h) * D;
+    double m = -INFINITY;
+    for (int p = lo; p < n; ++p) {
+      const uint16_t* kp = kc + (((int64_t)b * cap + p) * HK + kv) * D;
+      double acc = 0.0;
+      for (int i = 0; i < D; ++i) acc += T_BF16[qh[i]] * T_BF16[kp[i]];
+      s[p - lo] = acc / sqrt((double)D);
+      if (s[p - lo] > m) m = s[p - lo];
+    }
+    const double z = sinks ? (double)sinks[h] : -INFINITY;
+    if (z > m) m = z;
+    double den = sinks ? exp(z - m) : 0.0;
+    for (int p = lo; p < n; ++p) den += exp(s[p - lo] - m);
+    double* o = out + ((int64_t)b * HQ + h) * D;
+    for (int i = 0; i < D; ++i) o[i] = 0.0;
+    for (int p = lo; p < n; ++p) {
+      const double w = exp(s[p - lo] - m) / den;
+      const uint16_t* vp = vc + (((int64_t)b * cap + p) * HK + kv) * D;
+      for (int i = 0; i < D; ++i) o[i] += w * T_BF16[vp[i]];
+    }
+    free(s);
+  }
+}
+
 int orc_max_threads(void) { return orc_threads(0); }

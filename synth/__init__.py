@@ -14,6 +14,9 @@ Box-Muller; see synth.c):
   * expert e, matrix j (0 gate [f][d], 1 up [f][d], 2 down [d][f]):
                  fp32(N(0, 0.02)), then the format's encoder   key (seed, EXPERT, e, j)
     the shared expert uses e = SHARED_ID.
+  * decode attention: new-token q [B][32][128], k and v [B][4][128], cached keys
+                 and values [B][cap][4][128] ~ bf16(fp32(N(0, 1))); q/k RMSNorm gains
+                 bf16(1 + N(0, 0.1)) [128]; sinks fp32(N(0, 1)) [32]   key (seed, ATTN, i, 0)
   * output head  W  ~ fp32(N(0, 0.02)) [V][d], then the format's encoder
                  key (seed, HEAD, 0, 0); the vocabulary V is synthetic (the
                  pages do not give it; about 150 k)
@@ -31,7 +34,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "synth.c")
 _LIB = os.path.join(_HERE, "libsynth.so")
 
-TAG_X, TAG_ROUTER, TAG_BIAS, TAG_EXPERT, TAG_HEAD = 1, 2, 3, 4, 5
+TAG_X, TAG_ROUTER, TAG_BIAS, TAG_EXPERT, TAG_HEAD, TAG_ATTN = 1, 2, 3, 4, 5, 6
 HEAD_VOCAB = 151552  # synthetic vocabulary of the output-head workload
 SHARED_ID = 1_000_000
 FMT_CODE = {"bf16": 0, "q4_1": 1, "nvfp4": 2}
@@ -248,6 +251,25 @@ def make_head(V: int = HEAD_VOCAB, fmt: str = "q4_1", seed: int = 0, d: int = 20
     q = alloc_qmat(fmt, 1, V, d)
     fill_matrix(q, 0, key(seed, TAG_HEAD), sigma)
     return q
+
+
+ATTN_HQ, ATTN_HK, ATTN_D = 32, 4, 128  # query heads, key-value heads, head dimension
+ATTN_WINDOW = 513                        # sliding window: the current token and the 512 before it
+
+
+def make_attn(B: int, cap: int, seed: int = 0, HQ: int = ATTN_HQ, HK: int = ATTN_HK, D: int = ATTN_D) -> dict:
+    """Inputs of one decode-attention step: the new token's q, k, v (bf16 bits),
+    a cache of `cap` positions per sequence in the plain layout [B][cap][HK][D]
+    (keys as stored: already normalised and rotated), the gains and the sinks."""
+    def bf(i, n, sigma=1.0):
+        return normal_bf16(key(seed, TAG_ATTN, i), sigma, n)
+    g = normal_f32(key(seed, TAG_ATTN, 5), 0.1, 2 * D) + np.float32(1.0)
+    return dict(q=bf(0, B * HQ * D).reshape(B, HQ, D), k=bf(1, B * HK * D).reshape(B, HK, D),
+                v=bf(2, B * HK * D).reshape(B, HK, D),
+                k_cache=bf(3, B * cap * HK * D).reshape(B, cap, HK, D),
+                v_cache=bf(4, B * cap * HK * D).reshape(B, cap, HK, D),
+                q_gain=encode_bf16(g[:D]), k_gain=encode_bf16(g[D:]),
+                sinks=normal_f32(key(seed, TAG_ATTN, 6), 1.0, HQ))
 
 
 def bf16_to_f32(b: np.ndarray) -> np.ndarray:
