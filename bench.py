@@ -26,7 +26,11 @@ layer on the layer inputs the stack produced.
 The output-head workloads (`--workload head_v151552_t4_q4_1` and the others
 of synth.HEAD_CONFIGS) time the 4-bit output head instead: a step is the
 logits of T tokens against a synthetic 151552 x 2048 head, rotating over
-`--layers` drawn heads; its roofline entry is the head kernel itself.
+`--layers` drawn heads; its roofline entry is the head kernel itself.  The
+decode-attention workloads (`--workload attn_full_b32_ctx8192`,
+`attn_swa_b32_ctx8192`) time one attention layer's step for 32 sequences with
+8192 cached positions (full attention, or the 513-token window with rotary
+embedding).
 
 Also measured, outside the timed steps: the attainable HBM read rate (a plain
 streaming read of 4 GiB through the library's moe_stream_read, best of a few
@@ -644,6 +648,145 @@ def bench_head(args, moe, synth, torch, np):
     }
 
 
+def bench_attn(args, moe, synth, torch, np):
+    """Decode attention: one new token for each of B sequences whose caches hold
+    ctx positions (the token at position ctx - 1).  Steps rotate over --layers
+    independently drawn caches (537 MB each at 32 x 8192), so that every step
+    reads its keys and values from HBM."""
+    cfg = synth.ATTN_CONFIGS[args.workload]
+    B, ctx, window, rope = cfg["B"], cfg["ctx"], cfg["window"], cfg["rope"]
+    NL = max(1, args.layers)
+    HQ, HK, D = synth.ATTN_HQ, synth.ATTN_HK, synth.ATTN_D
+    desc = moe.moe_attn_desc(window, int(rope), 10000.0, 1e-6)
+    log(f"generating {NL} caches of {args.workload}")
+    a = synth.make_attn(B, ctx, seed=0)
+
+    def dev(b):
+        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).cuda().view(torch.bfloat16)
+
+    caches = []
+    for i in range(NL):
+        c = moe.AttnCache(B, ctx)
+        if i == 0:
+            c.load(a["k_cache"], a["v_cache"])
+        else:  # further layers: a cheap device-side variant of the same draw
+            c.k.copy_(caches[0].k.roll(i, dims=2))
+            c.v_t.copy_(caches[0].v_t.roll(i, dims=4))
+        caches.append(c)
+    q, k, v = dev(a["q"]), dev(a["k"]), dev(a["v"])
+    qg, kg = dev(a["q_gain"]), dev(a["k_gain"])
+    sinks = torch.from_numpy(a["sinks"]).cuda()
+    pos = torch.full((B,), ctx - 1, dtype=torch.int32, device="cuda")
+    out = torch.empty((B, HQ, D), dtype=torch.bfloat16, device="cuda")
+    ws = moe.alloc_workspace(moe.attn_workspace_size(desc, B, ctx))
+    stream = moe.current_stream()
+    span = min(window, ctx) if window else ctx
+    # algorithmic bytes of one call: the attended keys and values once, the new
+    # token's q, k, v and gains in, k' and v appended, out written
+    step_bytes = B * HK * span * D * 2 * 2 + B * (HQ + 2 * HK) * D * 2 + 2 * D * 2 + B * HK * D * 2 * 2 + B * HQ * D * 2
+
+    def step(i, on=None):
+        c = caches[i % NL]
+        moe.moe_attn_decode(desc, B, ctx, q.data_ptr(), k.data_ptr(), v.data_ptr(), qg.data_ptr(), kg.data_ptr(),
+                            sinks.data_ptr(), pos.data_ptr(), c.k.data_ptr(), c.v_t.data_ptr(), ctx, out.data_ptr(),
+                            ws.data_ptr(), ws.numel(), stream if on is None else on)
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} plain calls")
+    start.record()
+    for i in range(args.steps):
+        evs[i][0].record()
+        step(args.warmup + i)
+        evs[i][1].record()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    call_ms = float(np.mean([x.elapsed_time(y) for x, y in evs]))
+    graph_ms = None
+    if not args.no_graph:
+        n_full, n_rest = divmod(args.steps, NL)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(NL):
+                step(i, on=moe.current_stream())
+        g_rest = None
+        if n_rest:
+            g_rest = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_rest):
+                for i in range(n_rest):
+                    step(i, on=moe.current_stream())
+        for _ in range(max(1, args.warmup // NL)):
+            g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(n_full):
+            g.replay()
+        if g_rest is not None:
+            g_rest.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+        log(f"graph replay: {graph_ms * 1e3:.1f} us per step; plain {ms * 1e3:.1f} us; call {call_ms * 1e3:.1f} us")
+        del g, g_rest
+    step_ms = graph_ms if graph_ms is not None else ms
+    achieved = step_bytes / (call_ms * 1e-3) / 1e9
+    if args.copy_calibration:
+        copy_calibration(torch)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        th = oracle.max_threads()
+        lens = np.full(B, ctx, np.int32)
+        log(f"cpu baseline: oracle on {th} threads, whole steps for about 10 s")
+        n_cpu, c0 = 0, time.time()
+        while n_cpu < 1 or (time.time() - c0 < 10.0 and n_cpu < 64):
+            qp, _ = oracle.attn_prep(a["q"], a["k"], a["q_gain"], a["k_gain"], lens - 1, rope)
+            oracle.attn_decode(qp, a["k_cache"], a["v_cache"], lens, window, a["sinks"], threads=th)
+            n_cpu += 1
+        dt = time.time() - c0
+        cpu = {"value": round(n_cpu * B / dt, 3), "unit": "tokens/s", "cores": th, "kind": "oracle",
+               "sample": f"{n_cpu} steps of the same workload ({B} sequences, {span} attended positions each, "
+                         f"fp64), {dt:.1f} s wall"}
+
+    del caches, q, k, v, out, ws
+    torch.cuda.empty_cache()
+    stream_ref = None if args.no_stream_reference else stream_reference(moe, torch)
+    return {
+        "metric": "decode-attention tokens/s + achieved HBM GB/s (% of peak), 1 GPU",
+        "value": round(B / (step_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 cache and operands, f32 accumulate and softmax",
+        "data": "synthetic",
+        "hbm_gbps": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
+        "stream_read": stream_ref,
+        "config": {"workload": f"decode_attention_{args.workload}", "sequences": B, "cached_positions": ctx,
+                   "attended_positions": span, "window": window, "rope": rope, "q_heads": HQ, "kv_heads": HK,
+                   "head_dim": D, "cache_instances": NL, "bytes_per_step": step_bytes,
+                   "launch": "hip_graph_replay" if graph_ms is not None else "plain",
+                   "plain_launch_ms_per_step": round(ms, 5), "call_ms": round(call_ms, 5)},
+        "roofline": {"bound": "hbm", "kernel": "attention call (prep + attn_decode_kernel + combine)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "frac_of_stream_read": round(achieved / stream_ref["gbps"], 4) if stream_ref else None,
+                     "traffic": read_traffic(args.workload, "attn")},
+        "cpu_baseline": cpu,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -675,8 +818,11 @@ def main() -> int:
         return 2
     if args.workload in synth.HEAD_CONFIGS:
         out = bench_head(args, moe, synth, torch, np)
+    elif args.workload in synth.ATTN_CONFIGS:
+        out = bench_attn(args, moe, synth, torch, np)
     elif args.workload not in synth.CONFIGS:
-        print(f"unknown workload {args.workload}; one of {sorted(synth.CONFIGS) + sorted(synth.HEAD_CONFIGS)}",
+        print(f"unknown workload {args.workload}; one of "
+              f"{sorted(synth.CONFIGS) + sorted(synth.HEAD_CONFIGS) + sorted(synth.ATTN_CONFIGS)}",
               file=sys.stderr)
         return 2
     elif synth.CONFIGS[args.workload]["layers"] == 1:

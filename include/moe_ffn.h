@@ -203,6 +203,62 @@ moe_status moe_head_forward(const void* x, int32_t T, const moe_qmat* w, int32_t
  * Invalid arguments return MOE_ERR_INVALID_ARG before anything is enqueued. */
 moe_status moe_stream_read(const void* src, size_t bytes, void* sink, int32_t grid, void* stream);
 
+/* ---- decode attention ----------------------------------------------------------
+ * One new token per sequence through one attention layer of the layout in the
+ * review's section "The architecture is an argument about memory bandwidth":
+ * 32 query heads share 4 key-value heads of dimension 128 (query head h reads
+ * key-value head h / 8); sliding-window layers attend to the current token and
+ * the 512 before it, the others to every earlier token; rotary position
+ * embedding on the sliding-window layers only; an RMSNorm over each head of q
+ * and k; a learned sink per query head.  Formulas (this library's reading):
+ *   q' = bf16(rot(RMSNorm(q) * q_gain)), k' likewise with k_gain, where
+ *   RMSNorm(x) = x / sqrt(mean(x^2) + rms_eps) over one head's 128 elements and
+ *   rot pairs element i with i + 64 at angle pos * rope_theta^(-i/64);
+ *   s_j = q'.k'_j / sqrt(128) over the attended positions j;
+ *   out = sum_j e^{s_j} v_j / (sum_j e^{s_j} + e^{sink_h})   (bf16).
+ * Cache layout (bf16, caller-owned device memory, cap positions per sequence,
+ * cap a multiple of 64):
+ *   k_cache   [B][4][cap][128]        keys as stored (normalised and rotated)
+ *   v_cache_t [B][4][cap/64][128][64] values, transposed in tiles of 64
+ *                                     positions: position p, dimension d of a
+ *                                     head at [p / 64][d][p % 64]
+ * The call appends the new token's k' and v at position pos[b] and attends to
+ * positions max(0, pos[b] + 1 - window) .. pos[b] (window 0: 0 .. pos[b]).
+ * Entries the call does not attend to are never used, so an unwritten cache may
+ * hold anything there. */
+#define MOE_ATTN_Q_HEADS 32
+#define MOE_ATTN_KV_HEADS 4
+#define MOE_ATTN_HEAD_DIM 128
+typedef struct {
+  int32_t window;   /* 0: full attention; else the last `window` positions (513 on sliding-window layers) */
+  int32_t rope;     /* 1: rotary embedding on q and k (sliding-window layers); 0: none */
+  float rope_theta; /* base of the rotation frequencies, > 0 when rope is set (10000 in the benchmarks) */
+  float rms_eps;    /* epsilon of the q/k RMSNorm, >= 0 (1e-6) */
+} moe_attn_desc;
+
+/* Workspace bytes for moe_attn_decode with B sequences of at most max_len
+ * positions each (1 <= max_len <= cap; it sets the number of position splits). */
+moe_status moe_attn_workspace_size(const moe_attn_desc* d, int32_t B, int32_t max_len, size_t* bytes);
+
+/* The decode-attention step (prep, split decode, combine: three kernels on
+ * `stream`, asynchronous, capturable).
+ *   q          bf16 [B][32][128] new token's queries (before norm and rotation)
+ *   k, v       bf16 [B][4][128]  new token's keys and values
+ *   q_gain, k_gain  bf16 [128]   RMSNorm gains
+ *   sinks      fp32 [32] per query head, or NULL for no sink
+ *   pos        int32 [B] device memory: the new token's position, 0 <= pos < cap
+ *              and pos + 1 <= max_len (values outside [0, cap) are clamped)
+ *   out        bf16 [B][32][128]
+ *   workspace  moe_attn_workspace_size(d, B, max_len) bytes, 256 B aligned
+ * All pointers are device pointers; q, k, v, the caches and the workspace 16 B
+ * aligned, the others aligned to their element.  0 <= B <= 65535; B = 0 is a
+ * no-op.  Bad arguments return MOE_ERR_INVALID_ARG (MOE_ERR_WORKSPACE for a
+ * short workspace) before anything is enqueued. */
+moe_status moe_attn_decode(const moe_attn_desc* d, int32_t B, int32_t max_len, const void* q, const void* k,
+                           const void* v, const void* q_gain, const void* k_gain, const float* sinks,
+                           const int32_t* pos, void* k_cache, void* v_cache_t, int32_t cap, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* moe_last_error(void);
 

@@ -22,7 +22,9 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
 WFMT = {"bf16": 0, "q4_1": 1, "nvfp4": 2}
 EXPORTED = ["moe_layer_create", "moe_layer_destroy", "moe_layer_workspace_size", "moe_desc_workspace_size",
             "moe_layer_forward", "moe_layer_forward_staged", "moe_stack_workspace_size", "moe_stack_forward",
-            "moe_head_forward", "moe_stream_read", "moe_last_error", "moe_version"]
+            "moe_head_forward", "moe_attn_workspace_size", "moe_attn_decode", "moe_stream_read", "moe_last_error",
+            "moe_version"]
+ATTN_HQ, ATTN_HK, ATTN_D = 32, 4, 128
 HEAD_MAX_VOCAB = 1048576
 N_STAGE_EVENTS = 7
 STAGES = ["router", "topk", "bucket", "gate_up", "down", "combine"]
@@ -46,6 +48,11 @@ class moe_layer_weights(ctypes.Structure):
     _fields_ = [("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
                 ("gate", moe_qmat), ("up", moe_qmat), ("down", moe_qmat),
                 ("sh_gate", moe_qmat), ("sh_up", moe_qmat), ("sh_down", moe_qmat)]
+
+
+class moe_attn_desc(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("rope", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+                ("rms_eps", ctypes.c_float)]
 
 
 class moe_route_out(ctypes.Structure):
@@ -84,6 +91,11 @@ _lib.moe_stack_forward.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _i32, ctypes.
 _lib.moe_stack_forward.restype = ctypes.c_int
 _lib.moe_head_forward.argtypes = [_vp, _i32, ctypes.POINTER(moe_qmat), _i32, _i32, _i32, _vp, _vp]
 _lib.moe_head_forward.restype = ctypes.c_int
+_lib.moe_attn_workspace_size.argtypes = [ctypes.POINTER(moe_attn_desc), _i32, _i32, ctypes.POINTER(_sz)]
+_lib.moe_attn_workspace_size.restype = ctypes.c_int
+_lib.moe_attn_decode.argtypes = [ctypes.POINTER(moe_attn_desc), _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _vp, _i32, _vp, _vp, _sz, _vp]
+_lib.moe_attn_decode.restype = ctypes.c_int
 _lib.moe_stream_read.argtypes = [_vp, _sz, _vp, _i32, _vp]
 _lib.moe_stream_read.restype = ctypes.c_int
 _lib.moe_last_error.restype = ctypes.c_char_p
@@ -273,6 +285,71 @@ def head_forward(m: DeviceMatrix, x, logits=None):
         logits = torch.empty((T, m.rows), dtype=torch.float32, device=x.device)
     moe_head_forward(x.data_ptr(), T, m.qmat, WFMT[m.fmt], m.rows, m.cols, logits.data_ptr(), current_stream())
     return logits
+
+
+def attn_workspace_size(desc: moe_attn_desc, B: int, max_len: int) -> int:
+    n = _sz(0)
+    _check(_lib.moe_attn_workspace_size(ctypes.byref(desc), B, max_len, ctypes.byref(n)), "moe_attn_workspace_size")
+    return n.value
+
+
+def moe_attn_decode(desc: moe_attn_desc, B: int, max_len: int, q: int, k: int, v: int, q_gain: int, k_gain: int,
+                    sinks, pos: int, k_cache: int, v_cache_t: int, cap: int, out: int, ws: int, ws_bytes: int,
+                    stream: int) -> None:
+    _check(_lib.moe_attn_decode(ctypes.byref(desc), B, max_len, q, k, v, q_gain, k_gain, sinks, pos, k_cache,
+                                v_cache_t, cap, out, ws, ws_bytes, stream), "moe_attn_decode")
+
+
+ATTN_TILE = 64  # positions per tile of the transposed value cache
+
+
+class AttnCache:
+    """Device key/value cache of B sequences x cap positions in the library's
+    layout: keys [B][4][cap][128], values transposed in 64-position tiles
+    [B][4][cap/64][128][64] (bf16)."""
+
+    def __init__(self, B: int, cap: int, device="cuda"):
+        import torch
+        self.B, self.cap = B, cap
+        self.k = torch.zeros((B, ATTN_HK, cap, ATTN_D), dtype=torch.bfloat16, device=device)
+        self.v_t = torch.zeros((B, ATTN_HK, cap // ATTN_TILE, ATTN_D, ATTN_TILE), dtype=torch.bfloat16,
+                               device=device)
+
+    def load(self, k_plain: np.ndarray, v_plain: np.ndarray) -> None:
+        """Fill from plain-layout bf16 bits [B][cap][4][128] (every position)."""
+        import torch
+        B, cap = self.B, self.cap
+        kt = torch.from_numpy(np.ascontiguousarray(k_plain).view(np.int16)).view(torch.bfloat16)
+        vt = torch.from_numpy(np.ascontiguousarray(v_plain).view(np.int16)).view(torch.bfloat16)
+        self.k.copy_(kt.permute(0, 2, 1, 3).to(self.k.device))
+        v5 = vt.reshape(B, cap // ATTN_TILE, ATTN_TILE, ATTN_HK, ATTN_D).permute(0, 3, 1, 4, 2)
+        self.v_t.copy_(v5.to(self.v_t.device))
+
+    def plain(self):
+        """(keys, values) as bf16 bits in the plain layout [B][cap][4][128]."""
+        import torch
+        k = self.k.permute(0, 2, 1, 3).contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        v = self.v_t.permute(0, 2, 4, 1, 3).reshape(self.B, self.cap, ATTN_HK, ATTN_D)
+        v = v.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return k, v
+
+
+def attn_decode(desc: moe_attn_desc, q, k, v, q_gain, k_gain, sinks, pos, cache: AttnCache, max_len: int,
+                out=None, workspace=None):
+    """One decode-attention step on torch device tensors (bf16 q [B][32][128],
+    k, v [B][4][128], gains [128]; fp32 sinks [32] or None; int32 pos [B]).
+    Appends k', v to the cache and returns out bf16 [B][32][128]."""
+    import torch
+    B = q.shape[0]
+    if out is None:
+        out = torch.empty((B, ATTN_HQ, ATTN_D), dtype=torch.bfloat16, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(attn_workspace_size(desc, B, max_len), device=q.device)
+    moe_attn_decode(desc, B, max_len, q.data_ptr(), k.data_ptr(), v.data_ptr(), q_gain.data_ptr(),
+                    k_gain.data_ptr(), None if sinks is None else sinks.data_ptr(), pos.data_ptr(),
+                    cache.k.data_ptr(), cache.v_t.data_ptr(), cache.cap, out.data_ptr(), workspace.data_ptr(),
+                    workspace.numel(), current_stream())
+    return out
 
 
 def alloc_workspace(nbytes: int, device="cuda"):

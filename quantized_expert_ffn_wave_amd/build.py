@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_ffn.so")
-SOURCES = ["abi.hip", "routing.hip", "ffn.hip", "stream_read.hip"]
+SOURCES = ["abi.hip", "routing.hip", "ffn.hip", "stream_read.hip", "attention.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

@@ -206,6 +206,36 @@ moe_status check_ws(void* ws, size_t have, size_t need) {
   return MOE_OK;
 }
 
+// Decode attention: positions per split and the split count for B sequences of
+// at most max_len positions (the splits cover the attended span and the
+// alignment of its start down to 64); smaller splits while there would be
+// fewer than 1024 waves.
+struct AttnPlan {
+  int chunk, splits;
+  size_t q_off, o_off, ml_off, total;
+};
+moe_status attn_plan(const moe_attn_desc* d, int32_t B, int32_t max_len, AttnPlan* P) {
+  if (!d) return fail(MOE_ERR_INVALID_ARG, "attention descriptor is NULL");
+  if (d->window < 0) return fail(MOE_ERR_INVALID_ARG, "window=%d must be >= 0", d->window);
+  if (d->rope != 0 && d->rope != 1) return fail(MOE_ERR_INVALID_ARG, "rope=%d must be 0 or 1", d->rope);
+  if (d->rope && !(d->rope_theta > 0.f)) return fail(MOE_ERR_INVALID_ARG, "rope_theta must be > 0");
+  if (!(d->rms_eps >= 0.f)) return fail(MOE_ERR_INVALID_ARG, "rms_eps must be >= 0");
+  if (B < 0 || B > 65535) return fail(MOE_ERR_INVALID_ARG, "B=%d outside [0, 65535]", B);
+  if (max_len < 1) return fail(MOE_ERR_INVALID_ARG, "max_len=%d must be >= 1", max_len);
+  // a split is 256 positions (a 64-position tile for each of the 4 waves of its
+  // workgroup), or a multiple of 256 that keeps the splits at 64 or fewer
+  const int span = (d->window > 0 && d->window < max_len ? d->window : max_len) + 63;
+  const int chunk = 256 * ((span + 256 * 64 - 1) / (256 * 64));
+  P->chunk = chunk;
+  P->splits = (span + chunk - 1) / chunk;
+  const size_t rows = (size_t)B * moe::ATTN_HQ;
+  P->q_off = 0;
+  P->o_off = up256(rows * moe::ATTN_D * 2);
+  P->ml_off = P->o_off + up256(rows * P->splits * moe::ATTN_D * 4);
+  P->total = P->ml_off + up256(rows * P->splits * 2 * 4);
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -402,3 +432,58 @@ const char* moe_last_error(void) { return g_err.c_str(); }
 const char* moe_version(void) { return "moe_ffn gfx950 0.1"; }
 
 }  // extern "C"
+
+moe_status moe_attn_workspace_size(const moe_attn_desc* d, int32_t B, int32_t max_len, size_t* bytes) {
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  AttnPlan P;
+  moe_status st = attn_plan(d, B, max_len, &P);
+  if (st != MOE_OK) return st;
+  *bytes = P.total;
+  return MOE_OK;
+}
+
+moe_status moe_attn_decode(const moe_attn_desc* d, int32_t B, int32_t max_len, const void* q, const void* k,
+                           const void* v, const void* q_gain, const void* k_gain, const float* sinks,
+                           const int32_t* pos, void* k_cache, void* v_cache_t, int32_t cap, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  AttnPlan P;
+  moe_status st = attn_plan(d, B, max_len, &P);
+  if (st != MOE_OK) return st;
+  if (cap < 64 || cap % 64) return fail(MOE_ERR_INVALID_ARG, "cap=%d must be a positive multiple of 64", cap);
+  if (max_len > cap) return fail(MOE_ERR_INVALID_ARG, "max_len=%d exceeds cap=%d", max_len, cap);
+  if (B == 0) return MOE_OK;
+  struct { const void* p; size_t al; const char* name; } ptrs[] = {
+      {q, 16, "q"}, {k, 16, "k"}, {v, 16, "v"}, {q_gain, 2, "q_gain"}, {k_gain, 2, "k_gain"}, {pos, 4, "pos"},
+      {k_cache, 16, "k_cache"}, {v_cache_t, 16, "v_cache_t"}, {out, 4, "out"}, {workspace, 256, "workspace"}};
+  for (const auto& e : ptrs)
+    if (!e.p || !aligned(e.p, e.al)) return fail(MOE_ERR_INVALID_ARG, "%s is NULL or not %zu-byte aligned", e.name, e.al);
+  if (sinks && !aligned(sinks, 4)) return fail(MOE_ERR_INVALID_ARG, "sinks is not 4-byte aligned");
+  if (workspace_bytes < P.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, P.total);
+  moe::AttnArgs a;
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.q_gain = (const uint16_t*)q_gain;
+  a.k_gain = (const uint16_t*)k_gain;
+  a.sinks = sinks;
+  a.pos = pos;
+  a.k_cache = (uint16_t*)k_cache;
+  a.v_cache = (uint16_t*)v_cache_t;
+  char* ws = (char*)workspace;
+  a.qbuf = (uint16_t*)(ws + P.q_off);
+  a.part_o = (float*)(ws + P.o_off);
+  a.part_ml = (float*)(ws + P.ml_off);
+  a.out = (uint16_t*)out;
+  a.cap = cap;
+  a.window = d->window;
+  a.rope = d->rope;
+  a.chunk = P.chunk;
+  a.splits = P.splits;
+  a.eps = d->rms_eps;
+  for (int i = 0; i < moe::ATTN_D / 2; ++i)
+    a.inv_freq[i] = d->rope ? pow((double)d->rope_theta, -2.0 * i / moe::ATTN_D) : 0.0;
+  hipError_t e = moe::launch_attn(a, B, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return MOE_OK;
+}

@@ -301,6 +301,13 @@ HEAD_CONFIGS = {
 }
 
 
+# decode-attention workloads: name -> sequences, cached positions, window, rotation
+ATTN_CONFIGS = {
+    "attn_full_b32_ctx8192": dict(B=32, ctx=8192, window=0, rope=False),
+    "attn_swa_b32_ctx8192": dict(B=32, ctx=8192, window=ATTN_WINDOW, rope=True),
+}
+
+
 def make_workload(name: str, layers: int | None = None, workers: int = 1, progress=None):
     """(list of Layer, x) for a named workload.  Layer l of a stack is drawn
     from seed l; activations from seed 0.  `layers` truncates a stack.

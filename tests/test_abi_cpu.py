@@ -155,6 +155,57 @@ def test_head_argument_errors_before_the_device():
     assert lib.moe_head_forward(None, 0, ref, Q, 100, 2048, None, None) == moe.MOE_OK
 
 
+def test_attention_argument_errors_before_the_device():
+    """moe_attn_workspace_size / moe_attn_decode reject bad descriptors, sizes
+    and pointers without touching a device; B = 0 is a no-op."""
+    lib = moe.lib()
+    inv, wsz = moe.MOE_ERR_INVALID_ARG, moe.MOE_ERR_WORKSPACE
+    d = moe.moe_attn_desc(513, 1, 10000.0, 1e-6)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_attn_workspace_size(ctypes.byref(d), 4, 1024, ctypes.byref(n)) == moe.MOE_OK
+    need = n.value
+    assert need > 0
+    assert lib.moe_attn_workspace_size(None, 4, 1024, ctypes.byref(n)) == inv
+    assert lib.moe_attn_workspace_size(ctypes.byref(d), 4, 1024, None) == inv
+    for bad in (moe.moe_attn_desc(-1, 0, 1.0, 1e-6), moe.moe_attn_desc(0, 2, 1.0, 1e-6),
+                moe.moe_attn_desc(0, 1, 0.0, 1e-6), moe.moe_attn_desc(0, 0, 1.0, -1.0)):
+        assert lib.moe_attn_workspace_size(ctypes.byref(bad), 4, 1024, ctypes.byref(n)) == inv
+    assert lib.moe_attn_workspace_size(ctypes.byref(d), -1, 1024, ctypes.byref(n)) == inv
+    assert lib.moe_attn_workspace_size(ctypes.byref(d), 65536, 1024, ctypes.byref(n)) == inv
+    assert lib.moe_attn_workspace_size(ctypes.byref(d), 4, 0, ctypes.byref(n)) == inv
+    # more positions, more splits: the workspace grows
+    big = ctypes.c_size_t(0)
+    full = moe.moe_attn_desc(0, 0, 10000.0, 1e-6)
+    assert lib.moe_attn_workspace_size(ctypes.byref(full), 4, 65536, ctypes.byref(big)) == moe.MOE_OK
+    assert big.value > need
+
+    P = [0x10000 + 0x1000 * i for i in range(12)]  # aligned fake device pointers
+
+    def call(B=4, max_len=1024, cap=1024, ptrs=None, ws_bytes=need, desc=d):
+        p = list(P) if ptrs is None else ptrs
+        return lib.moe_attn_decode(ctypes.byref(desc), B, max_len, p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7],
+                                   p[8], cap, p[9], p[10], ws_bytes, None)
+
+    assert call(cap=1000) == inv            # not a multiple of 64
+    assert call(cap=0) == inv
+    assert call(max_len=2048) == inv        # beyond cap
+    assert call(B=0) == moe.MOE_OK          # no-op, checked before the pointers
+    for i in (0, 1, 2, 3, 4, 6, 7, 8, 9, 10):  # every pointer but sinks is required
+        p = list(P)
+        p[i] = 0
+        assert call(ptrs=p) == inv, i
+    p = list(P)
+    p[0] += 8                                # q not 16-byte aligned
+    assert call(ptrs=p) == inv
+    p = list(P)
+    p[10] += 16                              # workspace not 256-byte aligned
+    assert call(ptrs=p) == inv
+    p = list(P)
+    p[5] += 2                                # sinks not 4-byte aligned
+    assert call(ptrs=p) == inv
+    assert call(ws_bytes=need - 1) == wsz
+
+
 def test_one_hip_runtime_per_process():
     """Importing the binding alone leaves one libamdhip64 mapped (torch's), so
     that the library and torch share a runtime whatever is imported first."""
