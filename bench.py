@@ -671,7 +671,7 @@ def bench_attn(args, moe, synth, torch, np):
             c.load(a["k_cache"], a["v_cache"])
         else:  # further layers: a cheap device-side variant of the same draw
             c.k.copy_(caches[0].k.roll(i, dims=2))
-            c.v_t.copy_(caches[0].v_t.roll(i, dims=4))
+            c.v_t.copy_(caches[0].v_t.roll(i, dims=2))
         caches.append(c)
     q, k, v = dev(a["q"]), dev(a["k"]), dev(a["v"])
     qg, kg = dev(a["q_gain"]), dev(a["k_gain"])

@@ -217,11 +217,13 @@ moe_status moe_stream_read(const void* src, size_t bytes, void* sink, int32_t gr
  *   s_j = q'.k'_j / sqrt(128) over the attended positions j;
  *   out = sum_j e^{s_j} v_j / (sum_j e^{s_j} + e^{sink_h})   (bf16).
  * Cache layout (bf16, caller-owned device memory, cap positions per sequence,
- * cap a multiple of 64):
- *   k_cache   [B][4][cap][128]        keys as stored (normalised and rotated)
- *   v_cache_t [B][4][cap/64][128][64] values, transposed in tiles of 64
- *                                     positions: position p, dimension d of a
- *                                     head at [p / 64][d][p % 64]
+ * cap a multiple of 64), one block of cap * 128 elements per (sequence b,
+ * key-value head h) at offset (b * 4 + h) * cap * 128, laid out in the order the
+ * matrix cores read it:
+ *   k_cache   keys as stored (normalised and rotated): position p, dimension d
+ *             at ((p / 16) * 16 + d / 8) * 128 + (p % 16) * 8 + d % 8
+ *   v_cache_t values: position p = 32 a + 16 h + 4 g + s (h < 2, g < 4, s < 4),
+ *             dimension d at (a * 8 + d / 16) * 512 + g * 128 + (d % 16) * 8 + 4 h + s
  * The call appends the new token's k' and v at position pos[b] and attends to
  * positions max(0, pos[b] + 1 - window) .. pos[b] (window 0: 0 .. pos[b]).
  * Entries the call does not attend to are never used, so an unwritten cache may

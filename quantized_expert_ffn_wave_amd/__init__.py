@@ -300,19 +300,19 @@ def moe_attn_decode(desc: moe_attn_desc, B: int, max_len: int, q: int, k: int, v
                                 v_cache_t, cap, out, ws, ws_bytes, stream), "moe_attn_decode")
 
 
-ATTN_TILE = 64  # positions per tile of the transposed value cache
-
-
 class AttnCache:
     """Device key/value cache of B sequences x cap positions in the library's
-    layout: keys [B][4][cap][128], values transposed in 64-position tiles
-    [B][4][cap/64][128][64] (bf16)."""
+    layout (bf16; per (sequence, key-value head) a block of cap x 128):
+    keys [cap/16][16 dimension groups][16 positions][8], values
+    [cap/32][8 dimension groups][4][16 dimensions][8 positions]: within a
+    32-position block, group g holds positions 4 g .. 4 g + 3 and 16 + 4 g ..
+    16 + 4 g + 3."""
 
     def __init__(self, B: int, cap: int, device="cuda"):
         import torch
         self.B, self.cap = B, cap
-        self.k = torch.zeros((B, ATTN_HK, cap, ATTN_D), dtype=torch.bfloat16, device=device)
-        self.v_t = torch.zeros((B, ATTN_HK, cap // ATTN_TILE, ATTN_D, ATTN_TILE), dtype=torch.bfloat16,
+        self.k = torch.zeros((B, ATTN_HK, cap // 16, ATTN_D // 8, 16, 8), dtype=torch.bfloat16, device=device)
+        self.v_t = torch.zeros((B, ATTN_HK, cap // 32, ATTN_D // 16, 4, 16, 8), dtype=torch.bfloat16,
                                device=device)
 
     def load(self, k_plain: np.ndarray, v_plain: np.ndarray) -> None:
@@ -321,15 +321,21 @@ class AttnCache:
         B, cap = self.B, self.cap
         kt = torch.from_numpy(np.ascontiguousarray(k_plain).view(np.int16)).view(torch.bfloat16)
         vt = torch.from_numpy(np.ascontiguousarray(v_plain).view(np.int16)).view(torch.bfloat16)
-        self.k.copy_(kt.permute(0, 2, 1, 3).to(self.k.device))
-        v5 = vt.reshape(B, cap // ATTN_TILE, ATTN_TILE, ATTN_HK, ATTN_D).permute(0, 3, 1, 4, 2)
-        self.v_t.copy_(v5.to(self.v_t.device))
+        # k[b][p][h][d], p = 16 pb + pi, d = 8 dg + di -> [b][h][pb][dg][pi][di]
+        k6 = kt.reshape(B, cap // 16, 16, ATTN_HK, ATTN_D // 8, 8).permute(0, 3, 1, 4, 2, 5)
+        self.k.copy_(k6.to(self.k.device))
+        # v[b][p][h][d], p = 32 pb + 16 ph + 4 pg + ps, d = 16 dg + di -> [b][h][pb][dg][pg][di][ph][ps]
+        v8 = vt.reshape(B, cap // 32, 2, 4, 4, ATTN_HK, ATTN_D // 16, 16).permute(0, 5, 1, 6, 3, 7, 2, 4)
+        self.v_t.copy_(v8.reshape(self.v_t.shape).to(self.v_t.device))
 
     def plain(self):
         """(keys, values) as bf16 bits in the plain layout [B][cap][4][128]."""
         import torch
-        k = self.k.permute(0, 2, 1, 3).contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-        v = self.v_t.permute(0, 2, 4, 1, 3).reshape(self.B, self.cap, ATTN_HK, ATTN_D)
+        B, cap = self.B, self.cap
+        k = self.k.permute(0, 2, 4, 1, 3, 5).reshape(B, cap, ATTN_HK, ATTN_D)
+        v8 = self.v_t.reshape(B, ATTN_HK, cap // 32, ATTN_D // 16, 4, 16, 2, 4)  # [b][h][pb][dg][pg][di][ph][ps]
+        v = v8.permute(0, 2, 6, 4, 7, 1, 3, 5).reshape(B, cap, ATTN_HK, ATTN_D)
+        k = k.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         v = v.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         return k, v
 

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 
 #include "common.hpp"
@@ -211,7 +212,7 @@ moe_status check_ws(void* ws, size_t have, size_t need) {
 // alignment of its start down to 64); smaller splits while there would be
 // fewer than 1024 waves.
 struct AttnPlan {
-  int chunk, splits;
+  int splits;
   size_t q_off, o_off, ml_off, total;
 };
 moe_status attn_plan(const moe_attn_desc* d, int32_t B, int32_t max_len, AttnPlan* P) {
@@ -222,12 +223,12 @@ moe_status attn_plan(const moe_attn_desc* d, int32_t B, int32_t max_len, AttnPla
   if (!(d->rms_eps >= 0.f)) return fail(MOE_ERR_INVALID_ARG, "rms_eps must be >= 0");
   if (B < 0 || B > 65535) return fail(MOE_ERR_INVALID_ARG, "B=%d outside [0, 65535]", B);
   if (max_len < 1) return fail(MOE_ERR_INVALID_ARG, "max_len=%d must be >= 1", max_len);
-  // a split is 256 positions (a 64-position tile for each of the 4 waves of its
-  // workgroup), or a multiple of 256 that keeps the splits at 64 or fewer
+  // about 512 / (4 B) splits of 4 waves, so that the workgroups fill the GPU
+  // about once and each wave streams several 32-position steps; at most 64, and
+  // no more than there are groups of 4 steps in the attended span
   const int span = (d->window > 0 && d->window < max_len ? d->window : max_len) + 63;
-  const int chunk = 256 * ((span + 256 * 64 - 1) / (256 * 64));
-  P->chunk = chunk;
-  P->splits = (span + chunk - 1) / chunk;
+  const int groups = (span + 32 * 4 - 1) / (32 * 4);
+  P->splits = std::min({std::max(1, (512 + 4 * B - 1) / (4 * std::max(B, 1))), 64, groups});
   const size_t rows = (size_t)B * moe::ATTN_HQ;
   P->q_off = 0;
   P->o_off = up256(rows * moe::ATTN_D * 2);
@@ -478,11 +479,12 @@ moe_status moe_attn_decode(const moe_attn_desc* d, int32_t B, int32_t max_len, c
   a.cap = cap;
   a.window = d->window;
   a.rope = d->rope;
-  a.chunk = P.chunk;
   a.splits = P.splits;
   a.eps = d->rms_eps;
-  for (int i = 0; i < moe::ATTN_D / 2; ++i)
-    a.inv_freq[i] = d->rope ? pow((double)d->rope_theta, -2.0 * i / moe::ATTN_D) : 0.0;
+  const double th = d->rope ? (double)d->rope_theta : 1.0;
+  for (int e = 0; e < 8; ++e) a.rot_e[e] = pow(th, -2.0 * e / moe::ATTN_D);
+  for (int g = 0; g < 4; ++g) a.rot_g[g] = pow(th, -2.0 * 8 * g / moe::ATTN_D);
+  a.rot_32 = pow(th, -2.0 * 32 / moe::ATTN_D);
   hipError_t e = moe::launch_attn(a, B, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return MOE_OK;

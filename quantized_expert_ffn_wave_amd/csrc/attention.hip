@@ -6,20 +6,25 @@
 // rotary embedding on the sliding-window layers only; an RMSNorm over each head
 // of q and k; a learned sink per query head.
 //
-// One new token per sequence, three kernels on the caller's stream:
-//   prep     per sequence: RMSNorm (and rotation) of the token's 32 q and 4 k
-//            heads, q' to the workspace, k' and v appended to the cache at the
-//            token's position;
-//   decode   per (sequence, key-value head, split of positions): the 8 query
-//            heads of the group against the split's keys and values on the
-//            16x16x32 bf16 MFMA, an online softmax, unnormalised partial outputs;
+// One new token per sequence, two kernels on the caller's stream:
+//   decode   per (sequence, key-value head, split of positions): RMSNorm (and
+//            rotation) of the group's 8 query heads straight into MFMA operands;
+//            the split that holds the new position also normalises (rotates)
+//            the new key and appends it and the value to the cache; then the
+//            8 query heads against the split's keys and values on the 16x16x32
+//            bf16 MFMA, an online softmax, unnormalised partial outputs;
 //   combine  per (sequence, query head): the splits and the sink merged.
 //
-// Cache layout (bf16): keys [B][HK][cap][D] (a position's 128 elements
-// contiguous), values transposed in tiles of 64 positions [B][HK][cap/64][D][64]
-// (within a tile, a dimension's positions contiguous, and the tile's 16 KB in
-// one piece), so that both products contract over contiguous memory: q.k over
-// d, p.v over positions.
+// Cache layout (bf16), per (sequence, key-value head), in the order the MFMA
+// operands read it, so that each quarter-wave's 16-byte loads are contiguous:
+//   keys   [cap/16][D/8][16][8]: position p, dimension d at
+//          ((p / 16) * 16 + d / 8) * 128 + (p % 16) * 8 + d % 8;
+//   values [cap/32][D/16][4][16][8]: position p = 32 a + 16 h + 4 g + s,
+//          dimension d at (a * 8 + d / 16) * 512 + g * 128 + (d % 16) * 8 + 4 h + s.
+// Both products contract over 16-byte runs (q.k over 8 dimensions of one
+// position, p.v over the 8 positions {4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3} of
+// a 32-position block, the positions whose scores one lane holds), and every
+// load instruction of a wave reads 1 KB in one piece.
 #include "common.hpp"
 
 namespace moe {
@@ -31,11 +36,21 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int AD = ATTN_D;            // head dimension
 constexpr int AGQ = ATTN_HQ / ATTN_HK;  // query heads per key-value head (8)
-constexpr int ATILE = 64;             // positions per tile of the decode loop
-constexpr int ADW = 4;                // waves per decode workgroup (a tile each, in turn)
+constexpr int ATILE = 64;             // positions per tile of the transposed value cache
+constexpr int ADW = 4;                // waves per decode workgroup
+constexpr int ASTEP = 32;             // positions per step of a decode wave
 constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ inline u32x4 ld16g(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// the cache is streamed once per step: nontemporal loads keep it from displacing
+// other lines in L2 and the last-level cache
+__device__ inline u32x4 ld16nt(const void* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); }
+
+// element offsets within one (sequence, key-value head) block of the caches
+__device__ inline size_t k_off(int p, int d) { return ((size_t)(p >> 4) * 16 + (d >> 3)) * 128 + (p & 15) * 8 + (d & 7); }
+__device__ inline size_t v_off(int p, int d) {
+  return ((size_t)(p >> 5) * 8 + (d >> 4)) * 512 + ((p >> 2) & 3) * 128 + (d & 15) * 8 + ((p >> 4) & 1) * 4 + (p & 3);
+}
 
 __device__ inline float wave_sum(float v) {
 #pragma unroll
@@ -43,62 +58,101 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
-// ---- prep --------------------------------------------------------------------------
-// One wave per head (grid B x 9 workgroups of 4 waves: 32 q heads, then 4 k
-// heads), lane l holding elements l and l + 64 (the rotation's pair), so that
-// every head's load, norm and store run side by side.  The rotation angle
-// pos * inv_freq[l] (inv_freq formed in fp64 on the host) is reduced modulo 2 pi
-// in fp64: positions reach 10^5, where an fp32 angle would be off by 10^-2 rad.
-__global__ __launch_bounds__(256) void attn_prep_kernel(AttnArgs a) {
-  const int b = blockIdx.x, lane = threadIdx.x & 63;
-  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
-  const int pos = min(max(a.pos[b], 0), a.cap - 1);
-  const bool isq = h < ATTN_HQ;
-  const uint16_t* src = isq ? a.q + ((size_t)b * ATTN_HQ + h) * AD : a.k + ((size_t)b * ATTN_HK + (h - ATTN_HQ)) * AD;
-  const uint16_t* gain = isq ? a.q_gain : a.k_gain;
-  const float x0 = bf16_to_f32(src[lane]), x1 = bf16_to_f32(src[lane + 64]);
-  const float g0 = bf16_to_f32(gain[lane]), g1 = bf16_to_f32(gain[lane + 64]);
-  const float r = rsqrtf(wave_sum(x0 * x0 + x1 * x1) * (1.f / AD) + a.eps);
-  float y0 = x0 * r * g0, y1 = x1 * r * g1;
-  if (a.rope) {
-    const double two_pi = 6.283185307179586;
-    const double ang = (double)pos * a.inv_freq[lane];
-    const float red = (float)fma(-rint(ang * (1.0 / two_pi)), two_pi, ang);  // in [-pi, pi]
-    float sn, cs;
-    sincosf(red, &sn, &cs);
-    const float t0 = y0 * cs - y1 * sn, t1 = y1 * cs + y0 * sn;
-    y0 = t0;
-    y1 = t1;
-  }
-  uint16_t* dst = isq ? a.qbuf + ((size_t)b * ATTN_HQ + h) * AD
-                      : a.k_cache + (((size_t)b * ATTN_HK + (h - ATTN_HQ)) * a.cap + pos) * AD;
-  dst[lane] = f32_to_bf16(y0);
-  dst[lane + 64] = f32_to_bf16(y1);
-  if (blockIdx.y == 0) {  // values as given, one element per (head, dimension), into the transposed tiles
-    for (int i = threadIdx.x; i < ATTN_HK * AD; i += 256) {
-      const int kv = i / AD, d = i % AD;
-      a.v_cache[(((size_t)b * ATTN_HK + kv) * (a.cap / ATILE) + pos / ATILE) * (AD * ATILE) + d * ATILE + pos % ATILE] =
-          a.v[((size_t)b * ATTN_HK + kv) * AD + d];
-    }
+// ---- decode ------------------------------------------------------------------------
+// One workgroup of 4 waves per (split, key-value head, sequence).  The attended
+// positions are cut into steps of 32 from the window's start rounded down to 64;
+// step q goes to split (q / 4) mod splits and wave q mod 4, so that the waves of
+// all splits stream adjacent steps together.  A wave keeps the next step's 16
+// loads in flight while it multiplies the current one, and the waves' running
+// maxima, sums and outputs are merged through LDS at the end.
+// Lane (c, g) = (lane % 16, lane / 16).  Step of 32 positions t0 ..:
+//   scores on 2 MFMA tiles (t < 2) x 4 K-steps: A = keys, row r of tile t is
+//   position t0 + 16 t + r, lane (r, g) supplying d = 32 i + 8 g .. + 7 of K-step
+//   i; B = q of head c (zero for c >= 8), the same d.  Output lane (c, g) holds
+//   the scores of head c at positions t0 + 16 t + 4 g + j, j < 4;
+//   values on 8 MFMA tiles of 16 dimensions: A = V^T, lane (r, g) supplying
+//   dimension 16 dt + r at those 8 positions (16 contiguous bytes); B = the
+//   lane's own 8 probabilities of head c.  Output
+//   lane (c, g) holds O[head c][16 dt + 4 g + j].
+// cos and sin of the rotation angle pos * inv_freq: the angle in revolutions is
+// formed and reduced to [-1/2, 1/2] in fp64 (positions reach 10^5, where an fp32
+// angle would be off by 10^-2 rad), then v_cos_f32 / v_sin_f32 take it in
+// revolutions (absolute error near 1e-6, against a bf16 step of 4e-3).
+__device__ inline void rotation(double inv_freq, int pos, float& cs, float& sn) {
+  const double rev = (double)pos * inv_freq * 0.15915494309189535;  // 1 / (2 pi)
+  const float fr = (float)(rev - rint(rev));
+  cs = __builtin_amdgcn_cosf(fr);
+  sn = __builtin_amdgcn_sinf(fr);
+}
+
+// The prepared head (query or key) in the decode's operand layout: lane (c, g)
+// holds d = 32 i + 8 g + e (i < 4, e < 8).  The 4 lanes of a head (g = 0 .. 3)
+// together hold its 128 elements, and element d and its rotation partner
+// d + 64 (i and i + 2) sit in the same lane.  Split in two so that the inputs'
+// loads can go out ahead of the cache's: loads, then the norm and rotation.
+struct QIn {
+  u32x4 x[4], gain[4];
+};
+
+// src: the head's 128 bf16 elements, or null for a lane that holds no head
+__device__ inline void prep_load(const uint16_t* src, const uint16_t* gain, int g, QIn& in) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    in.x[i] = src ? ld16g(src + 8 * g + 32 * i) : u32x4{0u, 0u, 0u, 0u};
+    in.gain[i] = ld16g(gain + 8 * g + 32 * i);
   }
 }
 
-// ---- decode ------------------------------------------------------------------------
-// One workgroup of 4 waves per (split, key-value head, sequence); wave w takes
-// the split's tiles w, w + 4, .. and the waves' running maxima, sums and outputs
-// are merged through LDS at the end.  Lane (c, g) = (lane % 16, lane / 16).
-// Tile of 64 positions t0 ..:
-//   scores on 4 MFMA tiles (t < 4) x 4 K-steps: A = keys, row r of tile t is
-//   position t0 + 32 (t / 2) + 8 (r / 4) + 4 (t % 2) + r % 4, lane (r, g)
-//   supplying d = 8 g + 32 i .. + 7 of step i; B = q of head c (zero for c >= 8),
-//   the same d.  Output lane (c, g) holds the scores of head c at positions
-//   t0 + 32 (t / 2) + 8 g + 4 (t % 2) + j, j < 4: for each 32-position half
-//   the 8 positions t0 + 32 h + 8 g .. + 7;
-//   values on 2 halves x 8 MFMA tiles of 16 dimensions: A = V^T, lane (r, g)
-//   supplying dimension 16 dt + r at the positions of its k-group, 8 g .. + 7 of
-//   the half (16 contiguous bytes of the tile); B = the lane's own 8
-//   probabilities of head c.  Output lane (c, g) holds O[head c][16 dt + 4 g + j].
-__global__ __launch_bounds__(64 * ADW) void attn_decode_kernel(AttnArgs a) {
+// The rotation frequency theta^(-d/64) of element d = 32 i + 8 g + e, as the
+// product of theta^(-e/64), theta^(-8g/64) and theta^(-32i/64) formed in fp64 on
+// the host (two fp64 roundings: a relative error near 2^-52)
+__device__ inline double freq(const AttnArgs& a, int i, int e, double fg) {
+  return (i ? a.rot_32 : 1.0) * a.rot_e[e] * fg;
+}
+
+__device__ inline void prep(const AttnArgs& a, const QIn& in, bool live, int g, int pos, u32x4 (&out)[4]) {
+  float y[4][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      y[i][e] = bf16_to_f32((uint16_t)(in.x[i][e >> 1] >> (16 * (e & 1))));
+      ss += y[i][e] * y[i][e];
+    }
+  ss += __shfl_xor(ss, 16);
+  ss += __shfl_xor(ss, 32);
+  const float r = live ? rsqrtf(ss * (1.f / AD) + a.eps) : 0.f;  // lanes without a head stay 0, even with eps = 0
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[i][e] *= r * bf16_to_f32((uint16_t)(in.gain[i][e >> 1] >> (16 * (e & 1))));
+  if (a.rope) {
+    const double fg = g == 0 ? a.rot_g[0] : g == 1 ? a.rot_g[1] : g == 2 ? a.rot_g[2] : a.rot_g[3];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float cs, sn;
+        rotation(freq(a, i, e, fg), pos, cs, sn);
+        const float t0 = y[i][e] * cs - y[i + 2][e] * sn, t1 = y[i + 2][e] * cs + y[i][e] * sn;
+        y[i][e] = t0;
+        y[i + 2][e] = t1;
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      out[i][e] = (uint32_t)f32_to_bf16(y[i][2 * e]) | ((uint32_t)f32_to_bf16(y[i][2 * e + 1]) << 16);
+}
+
+struct AStep {
+  u32x4 k[2][4];
+  u32x4 v[AD / 16];
+};
+
+__global__ __launch_bounds__(64 * ADW, 2) void attn_decode_kernel(AttnArgs a) {
   __shared__ float sm_ml[ADW][2][16];
   __shared__ f32x4 sm_o[ADW - 1][AD / 16][64];
   const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
@@ -106,92 +160,146 @@ __global__ __launch_bounds__(64 * ADW) void attn_decode_kernel(AttnArgs a) {
   const int len = min(max(a.pos[b], 0), a.cap - 1) + 1;
   const int lo = (a.window > 0 && len > a.window) ? len - a.window : 0;
   const int base = lo & ~(ATILE - 1);
-  const int p_begin = base + split * a.chunk, p_end = min(len, p_begin + a.chunk);
+  // steps of 32 positions from base; step q belongs to split (q / ADW) % splits
+  // and wave q % ADW, so that the splits' waves read adjacent steps at once
+  const int nst = (len - base + ASTEP - 1) / ASTEP;
+  const int first_step = split * ADW + wave, stride = a.splits * ADW;
+  const int nsteps = first_step < nst ? (nst - first_step + stride - 1) / stride : 0;
   const int hq = kv * AGQ + c;
+  const int pos = len - 1;
+  // the new token's key and value: appended by the one workgroup whose steps
+  // hold its position, before any of its cache loads (the barrier orders the
+  // stores before the loads; no other workgroup reads these cache lines)
+  const bool owner = ((pos - base) / ASTEP / ADW) % a.splits == split;
+  if (owner) {
+    if (wave == 0) {  // lanes (0, g) prepare the key; its 8-element runs are contiguous in the key cache
+      QIn kin;
+      prep_load(c == 0 ? a.k + ((size_t)b * ATTN_HK + kv) * AD : nullptr, a.k_gain, g, kin);
+      const uint16_t* vs = a.v + ((size_t)b * ATTN_HK + kv) * AD;
+      u32x4 vv[4];  // the value's same 32 elements, loaded with the key's inputs
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vv[i] = (c == 0) ? ld16g(vs + 32 * i + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 kp[4];
+      prep(a, kin, c == 0, g, pos, kp);
+      if (c == 0) {
+        uint16_t* kd = a.k_cache + ((size_t)b * ATTN_HK + kv) * (size_t)a.cap * AD;
+        uint16_t* vd = a.v_cache + ((size_t)b * ATTN_HK + kv) * (size_t)a.cap * AD;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          *reinterpret_cast<u32x4*>(kd + k_off(pos, 32 * i + 8 * g)) = kp[i];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            vd[v_off(pos, 32 * i + 8 * g + e)] = (uint16_t)(vv[i][e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+    __syncthreads();  // workgroup-uniform: owner is the same for all its waves
+  }
+  const uint16_t* kbase = a.k_cache + ((size_t)b * ATTN_HK + kv) * (size_t)a.cap * AD;
+  const uint16_t* vbase = a.v_cache + ((size_t)b * ATTN_HK + kv) * (size_t)AD * a.cap;
+  // start of the wave's step j; past its last step the last one is loaded
+  // again (never used), so that every load is issued and the waits stay exact
+  auto step_pos = [&](int j) { return base + ASTEP * (first_step + stride * min(j, nsteps - 1)); };
+  auto load = [&](AStep& st, int t0) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int p = t0 + 16 * t + c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.k[t][i] = ld16nt(kbase + k_off(p, 32 * i + 8 * g));
+    }
+#pragma unroll
+    for (int dt = 0; dt < AD / 16; ++dt) st.v[dt] = ld16nt(vbase + v_off(t0 + 4 * g, 16 * dt + c));
+  };
+  // the query's inputs, then the first two steps, are loaded before the query
+  // is prepared, so that its norm and rotation overlap the cache loads
+  QIn qin;
+  prep_load(c < AGQ ? a.q + ((size_t)b * ATTN_HQ + hq) * AD : nullptr, a.q_gain, g, qin);
+  AStep s0, s1;
+  if (nsteps > 0) {
+    load(s0, step_pos(0));
+    load(s1, step_pos(1));
+  }
+  u32x4 qv[4];  // this lane's prepared query operand: head c, d = 32 i + 8 g .. + 7
+  prep(a, qin, c < AGQ, g, pos, qv);
+  if (split == 0 && c < AGQ && wave == 0) {  // q' also to the workspace, for inspection
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(a.qbuf + ((size_t)b * ATTN_HQ + hq) * AD + 8 * g + 32 * i) = qv[i];
+  }
   float m = -INFINITY, l = 0.f;
   f32x4 o[AD / 16];
 #pragma unroll
   for (int dt = 0; dt < AD / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (p_begin + wave * ATILE < p_end) {
-    u32x4 qv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      qv[i] = (c < AGQ) ? ld16g(a.qbuf + ((size_t)b * ATTN_HQ + hq) * AD + 8 * g + 32 * i) : u32x4{0u, 0u, 0u, 0u};
-    const uint16_t* kbase = a.k_cache + ((size_t)b * ATTN_HK + kv) * (size_t)a.cap * AD;
-    const uint16_t* vbase = a.v_cache + ((size_t)b * ATTN_HK + kv) * (size_t)AD * a.cap;  // this head's tiles
+  if (nsteps > 0) {
     const float qscale = LOG2E * rsqrtf((float)AD);  // scores in the log2 domain
-    for (int t0 = p_begin + wave * ATILE; t0 < p_end; t0 += ADW * ATILE) {
-      // all loads of the tile first
-      u32x4 kv4[4][4], vt[2][AD / 16];
+    auto compute = [&](const AStep& st, int t0, bool valid) {
+      // scores of positions t0 + 8 g + e, masked outside [lo, len); an invalid
+      // step (past the wave's last, loaded again only to keep the waits exact)
+      // is masked whole
+      const int lo_v = valid ? lo : len;
+      float sc[8];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int p = t0 + 32 * (t >> 1) + 8 * (c >> 2) + 4 * (t & 1) + (c & 3);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kv4[t][i] = ld16g(kbase + (size_t)p * AD + 8 * g + 32 * i);
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int dt = 0; dt < AD / 16; ++dt)
-          vt[h][dt] = ld16g(vbase + (size_t)t0 * AD + (16 * dt + c) * ATILE + 32 * h + 8 * g);
-      // scores, masked outside [lo, len)
-      float sc[2][8];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < 2; ++t) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv4[t][i]),
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, st.k[t][i]),
                                                         __builtin_bit_cast(bf16x8, qv[i]), acc, 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int p = t0 + 32 * (t >> 1) + 8 * g + 4 * (t & 1) + j;
-          sc[t >> 1][4 * (t & 1) + j] = (p >= lo && p < len) ? acc[j] * qscale : -INFINITY;
+          const int p = t0 + 16 * t + 4 * g + j;
+          sc[4 * t + j] = (p >= lo_v && p < len) ? acc[j] * qscale : -INFINITY;
         }
       }
-      float mx = -INFINITY;
+      float mx = sc[0];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sc[h][e]);
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);  // finite: every tile holds at least one position in range
-      const float alpha = exp2f(m - m_new);
+      const float m_new = fmaxf(m, mx);
+      // a step wholly before the window's start leaves the maximum at -inf
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2f(m - m_use);
       m = m_new;
       l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < AD / 16; ++dt) o[dt] *= alpha;
+      uint32_t pk[4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t pk[4];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          // the denominator sums the same bf16 probabilities the products use
-          const uint16_t p0 = f32_to_bf16(exp2f(sc[h][e] - m_new)), p1 = f32_to_bf16(exp2f(sc[h][e + 1] - m_new));
-          l += bf16_to_f32(p0) + bf16_to_f32(p1);
-          pk[e / 2] = (uint32_t)p0 | ((uint32_t)p1 << 16);
-        }
-        // positions outside [lo, len) carry probability 0; their values are zeroed
-        // too, so that whatever the unwritten cache holds cannot turn into NaN
-        const int pv0 = t0 + 32 * h + 8 * g;
-        const bool whole = pv0 >= lo && pv0 + 8 <= len;
-        const u32x4 pb = u32x4{pk[0], pk[1], pk[2], pk[3]};
-#pragma unroll
-        for (int dt = 0; dt < AD / 16; ++dt) {
-          u32x4 v = vt[h][dt];
-          if (!whole) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int p = pv0 + 2 * e;
-              const uint32_t keep = ((p >= lo && p < len) ? 0x0000FFFFu : 0u) | ((p + 1 >= lo && p + 1 < len) ? 0xFFFF0000u : 0u);
-              v[e] &= keep;
-            }
-          }
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), __builtin_bit_cast(bf16x8, pb),
-                                                          o[dt], 0, 0, 0);
-        }
+      for (int e = 0; e < 8; e += 2) {
+        // the denominator sums the same bf16 probabilities the products use
+        const uint16_t p0 = f32_to_bf16(exp2f(sc[e] - m_use)), p1 = f32_to_bf16(exp2f(sc[e + 1] - m_use));
+        l += bf16_to_f32(p0) + bf16_to_f32(p1);
+        pk[e / 2] = (uint32_t)p0 | ((uint32_t)p1 << 16);
       }
+      // positions outside [lo, len) carry probability 0; their values are zeroed
+      // too, so that whatever the unwritten cache holds cannot turn into NaN
+      const int pv0 = t0 + 4 * g;  // element e of the lane's 8 is position pv0 + 16 (e / 4) + e % 4
+      const bool whole = pv0 >= lo_v && pv0 + 20 <= len;
+      const u32x4 pb = u32x4{pk[0], pk[1], pk[2], pk[3]};
+#pragma unroll
+      for (int dt = 0; dt < AD / 16; ++dt) {
+        u32x4 v = st.v[dt];
+        if (!whole) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int p = pv0 + 16 * (e >> 1) + 2 * (e & 1);  // elements 2 e, 2 e + 1
+            const uint32_t keep =
+                ((p >= lo_v && p < len) ? 0x0000FFFFu : 0u) | ((p + 1 >= lo_v && p + 1 < len) ? 0xFFFF0000u : 0u);
+            v[e] &= keep;
+          }
+        }
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), __builtin_bit_cast(bf16x8, pb),
+                                                        o[dt], 0, 0, 0);
+      }
+    };
+    // two steps in flight: the same loads outstanding at the loop's entry and at
+    // its back edge, so each compute waits only for its own step's loads
+    for (int j = 0; j < nsteps; j += 2) {
+      compute(s0, step_pos(j), true);
+      load(s0, step_pos(j + 2));
+      if (j + 1 < nsteps) compute(s1, step_pos(j + 1), true);  // (an odd count's last half is skipped)
+      load(s1, step_pos(j + 3));
     }
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
@@ -215,7 +323,7 @@ __global__ __launch_bounds__(64 * ADW) void attn_decode_kernel(AttnArgs a) {
 #pragma unroll
     for (int w = 0; w < ADW; ++w) {
       // waves without positions hold m = -inf, l = 0, o = 0
-      sc[w] = (M == -INFINITY) ? 0.f : exp2f(sm_ml[w][0][c] - M);
+      sc[w] = (M == -INFINITY || sm_ml[w][0][c] == -INFINITY) ? 0.f : exp2f(sm_ml[w][0][c] - M);
       L += sc[w] * sm_ml[w][1][c];
     }
     const size_t row = ((size_t)b * ATTN_HQ + hq) * a.splits + split;
@@ -272,7 +380,6 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn(const AttnArgs& a, int B, hipStream_t s) {
-  hipLaunchKernelGGL(attn_prep_kernel, dim3(B, (ATTN_HQ + ATTN_HK) / 4), dim3(256), 0, s, a);
   hipLaunchKernelGGL(attn_decode_kernel, dim3(a.splits, ATTN_HK, B), dim3(64 * ADW), 0, s, a);
   hipLaunchKernelGGL(attn_combine_kernel, dim3(B * ATTN_HQ), dim3(64), 0, s, a);
   return hipGetLastError();

@@ -167,9 +167,10 @@ struct AttnArgs {
   float* part_o;            // [B][HQ][splits][D] unnormalised partial outputs (workspace)
   float* part_ml;           // [B][HQ][splits][2] running maximum (log2 domain) and sum (workspace)
   uint16_t* out;            // bf16 [B][HQ][D]
-  int cap, window, rope, chunk, splits;
+  int cap, window, rope, splits;
   float eps;
-  double inv_freq[ATTN_D / 2];  // rotation frequencies theta^(-i/64)
+  // rotation frequencies: theta^(-d/64) = rot_32^(d / 32) * rot_g[(d / 8) % 4] * rot_e[d % 8]
+  double rot_e[8], rot_g[4], rot_32;
 };
 hipError_t launch_attn(const AttnArgs& a, int B, hipStream_t s);
 hipError_t launch_router(const LayerArgs& a, hipStream_t s);
