@@ -66,9 +66,11 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str = "ffn_up") -> str:
+    """Hash of the sources of the kernel a traffic summary was taken on."""
     h = hashlib.sha256()
-    for f in ("ffn.hip", "common.hpp"):
+    files = ("attention.hip", "attention.hpp", "common.hpp") if kernel == "attn" else ("ffn.hip", "common.hpp")
+    for f in files:
         with open(os.path.join(ROOT, "quantized_expert_ffn_wave_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -86,7 +88,7 @@ def read_traffic(workload: str, kernel: str = "ffn_up"):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha") != kernel_source_hash():
+    if kv.get("kernel_source_sha") != kernel_source_hash(kernel):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -778,7 +780,7 @@ def bench_attn(args, moe, synth, torch, np):
                    "head_dim": D, "cache_instances": NL, "bytes_per_step": step_bytes,
                    "launch": "hip_graph_replay" if graph_ms is not None else "plain",
                    "plain_launch_ms_per_step": round(ms, 5), "call_ms": round(call_ms, 5)},
-        "roofline": {"bound": "hbm", "kernel": "attention call (prep + attn_decode_kernel + combine)",
+        "roofline": {"bound": "hbm", "kernel": "attention call (attn_decode_kernel + attn_combine_kernel)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "frac_of_stream_read": round(achieved / stream_ref["gbps"], 4) if stream_ref else None,

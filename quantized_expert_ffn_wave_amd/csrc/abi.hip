@@ -9,6 +9,7 @@
 #include <string>
 
 #include "common.hpp"
+#include "attention.hpp"
 #include "moe_ffn.h"
 
 // Handle: the checked descriptor and the borrowed weights (no GPU resources).

@@ -26,6 +26,7 @@
 // a 32-position block, the positions whose scores one lane holds), and every
 // load instruction of a wave reads 1 KB in one piece.
 #include "common.hpp"
+#include "attention.hpp"
 
 namespace moe {
 namespace {
