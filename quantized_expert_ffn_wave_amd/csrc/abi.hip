@@ -226,10 +226,12 @@ moe_status attn_plan(const moe_attn_desc* d, int32_t B, int32_t max_len, AttnPla
   if (max_len < 1) return fail(MOE_ERR_INVALID_ARG, "max_len=%d must be >= 1", max_len);
   // about 512 / (4 B) splits of 4 waves, so that the workgroups fill the GPU
   // about once and each wave streams several 32-position steps; at most 64, and
-  // no more than there are groups of 4 steps in the attended span
+  // no more than there are groups of 4 steps in the attended span.  Spans of up
+  // to 1024 positions (the 513-token window among them) take one split: each
+  // wave then has at most 8 steps, and no combine kernel runs.
   const int span = (d->window > 0 && d->window < max_len ? d->window : max_len) + 63;
   const int groups = (span + 32 * 4 - 1) / (32 * 4);
-  P->splits = std::min({std::max(1, (512 + 4 * B - 1) / (4 * std::max(B, 1))), 64, groups});
+  P->splits = span <= 1024 + 63 ? 1 : std::min({std::max(1, (512 + 4 * B - 1) / (4 * std::max(B, 1))), 64, groups});
   const size_t rows = (size_t)B * moe::ATTN_HQ;
   P->q_off = 0;
   P->o_off = up256(rows * moe::ATTN_D * 2);

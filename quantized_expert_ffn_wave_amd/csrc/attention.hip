@@ -13,7 +13,8 @@
 //            the new key and appends it and the value to the cache; then the
 //            8 query heads against the split's keys and values on the 16x16x32
 //            bf16 MFMA, an online softmax, unnormalised partial outputs;
-//   combine  per (sequence, query head): the splits and the sink merged.
+//   combine  per (sequence, query head): the splits and the sink merged (with
+//            one split the decode kernel writes the output itself).
 //
 // Cache layout (bf16), per (sequence, key-value head), in the order the MFMA
 // operands read it, so that each quarter-wave's 16-byte loads are contiguous:
@@ -327,18 +328,39 @@ __global__ __launch_bounds__(64 * ADW, 2) void attn_decode_kernel(AttnArgs a) {
       sc[w] = (M == -INFINITY || sm_ml[w][0][c] == -INFINITY) ? 0.f : exp2f(sm_ml[w][0][c] - M);
       L += sc[w] * sm_ml[w][1][c];
     }
-    const size_t row = ((size_t)b * ATTN_HQ + hq) * a.splits + split;
-    float* po = a.part_o + row * AD;
+    if (a.splits == 1) {
+      // one split: the workgroup holds every attended position, so it adds the
+      // sink and writes the output itself (the launcher skips the combine)
+      const float z = a.sinks ? a.sinks[hq] * LOG2E : -INFINITY;
+      const float M2 = fmaxf(M, z);
+      const float wm = exp2f(M - M2);
+      const float inv = 1.f / (L * wm + (a.sinks ? exp2f(z - M2) : 0.f));
+      uint16_t* po = a.out + ((size_t)b * ATTN_HQ + hq) * AD;
 #pragma unroll
-    for (int dt = 0; dt < AD / 16; ++dt) {
-      f32x4 acc = o[dt] * sc[0];
+      for (int dt = 0; dt < AD / 16; ++dt) {
+        f32x4 acc = o[dt] * sc[0];
 #pragma unroll
-      for (int w = 1; w < ADW; ++w) acc += sm_o[w - 1][dt][lane] * sc[w];
-      *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) = acc;
-    }
-    if (g == 0) {
-      a.part_ml[2 * row] = M;
-      a.part_ml[2 * row + 1] = L;
+        for (int w = 1; w < ADW; ++w) acc += sm_o[w - 1][dt][lane] * sc[w];
+        const float f = wm * inv;
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(acc[0] * f) | ((uint32_t)f32_to_bf16(acc[1] * f) << 16);
+        pk.y = (uint32_t)f32_to_bf16(acc[2] * f) | ((uint32_t)f32_to_bf16(acc[3] * f) << 16);
+        *reinterpret_cast<uint2*>(po + 16 * dt + 4 * g) = pk;
+      }
+    } else {
+      const size_t row = ((size_t)b * ATTN_HQ + hq) * a.splits + split;
+      float* po = a.part_o + row * AD;
+#pragma unroll
+      for (int dt = 0; dt < AD / 16; ++dt) {
+        f32x4 acc = o[dt] * sc[0];
+#pragma unroll
+        for (int w = 1; w < ADW; ++w) acc += sm_o[w - 1][dt][lane] * sc[w];
+        *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) = acc;
+      }
+      if (g == 0) {
+        a.part_ml[2 * row] = M;
+        a.part_ml[2 * row + 1] = L;
+      }
     }
   }
 }
@@ -382,7 +404,7 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a) {
 
 hipError_t launch_attn(const AttnArgs& a, int B, hipStream_t s) {
   hipLaunchKernelGGL(attn_decode_kernel, dim3(a.splits, ATTN_HK, B), dim3(64 * ADW), 0, s, a);
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(B * ATTN_HQ), dim3(64), 0, s, a);
+  if (a.splits > 1) hipLaunchKernelGGL(attn_combine_kernel, dim3(B * ATTN_HQ), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
