@@ -169,33 +169,33 @@ __global__ __launch_bounds__(64 * ADW, 2) void attn_decode_kernel(AttnArgs a) {
   const int nsteps = first_step < nst ? (nst - first_step + stride - 1) / stride : 0;
   const int hq = kv * AGQ + c;
   const int pos = len - 1;
-  // the new token's key and value: appended by the one workgroup whose steps
-  // hold its position, before any of its cache loads (the barrier orders the
-  // stores before the loads; no other workgroup reads these cache lines)
-  const bool owner = ((pos - base) / ASTEP / ADW) % a.splits == split;
-  if (owner) {
-    if (wave == 0) {  // lanes (0, g) prepare the key; its 8-element runs are contiguous in the key cache
-      QIn kin;
-      prep_load(c == 0 ? a.k + ((size_t)b * ATTN_HK + kv) * AD : nullptr, a.k_gain, g, kin);
-      const uint16_t* vs = a.v + ((size_t)b * ATTN_HK + kv) * AD;
-      u32x4 vv[4];  // the value's same 32 elements, loaded with the key's inputs
+  // the new token's key and value: appended by the one wave whose step holds
+  // its position, before that wave's cache loads (a fence orders its stores
+  // before its loads; no other wave reads these cache lines: a 32-position step
+  // belongs to one wave, and its lines hold that step's positions only)
+  const int pos_step = (pos - base) / ASTEP;
+  if ((pos_step / ADW) % a.splits == split && pos_step % ADW == wave) {
+    // lanes (0, g) prepare the key; its 8-element runs are contiguous in the key cache
+    QIn kin;
+    prep_load(c == 0 ? a.k + ((size_t)b * ATTN_HK + kv) * AD : nullptr, a.k_gain, g, kin);
+    const uint16_t* vs = a.v + ((size_t)b * ATTN_HK + kv) * AD;
+    u32x4 vv[4];  // the value's same 32 elements, loaded with the key's inputs
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vv[i] = (c == 0) ? ld16g(vs + 32 * i + 8 * g) : u32x4{0u, 0u, 0u, 0u};
-      u32x4 kp[4];
-      prep(a, kin, c == 0, g, pos, kp);
-      if (c == 0) {
-        uint16_t* kd = a.k_cache + ((size_t)b * ATTN_HK + kv) * (size_t)a.cap * AD;
-        uint16_t* vd = a.v_cache + ((size_t)b * ATTN_HK + kv) * (size_t)a.cap * AD;
+    for (int i = 0; i < 4; ++i) vv[i] = (c == 0) ? ld16g(vs + 32 * i + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+    u32x4 kp[4];
+    prep(a, kin, c == 0, g, pos, kp);
+    if (c == 0) {
+      uint16_t* kd = a.k_cache + ((size_t)b * ATTN_HK + kv) * (size_t)a.cap * AD;
+      uint16_t* vd = a.v_cache + ((size_t)b * ATTN_HK + kv) * (size_t)a.cap * AD;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *reinterpret_cast<u32x4*>(kd + k_off(pos, 32 * i + 8 * g)) = kp[i];
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<u32x4*>(kd + k_off(pos, 32 * i + 8 * g)) = kp[i];
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            vd[v_off(pos, 32 * i + 8 * g + e)] = (uint16_t)(vv[i][e >> 1] >> (16 * (e & 1)));
-        }
+        for (int e = 0; e < 8; ++e)
+          vd[v_off(pos, 32 * i + 8 * g + e)] = (uint16_t)(vv[i][e >> 1] >> (16 * (e & 1)));
       }
     }
-    __syncthreads();  // workgroup-uniform: owner is the same for all its waves
+    __threadfence_block();  // the stores complete before this wave's loads
   }
   const uint16_t* kbase = a.k_cache + ((size_t)b * ATTN_HK + kv) * (size_t)a.cap * AD;
   const uint16_t* vbase = a.v_cache + ((size_t)b * ATTN_HK + kv) * (size_t)AD * a.cap;
