@@ -1243,12 +1243,14 @@ hipError_t launch_stack_init(const uint16_t* x, float* r, uint16_t* xn, int T, f
 // Up to 4 tokens it is a streaming GEMV on the vector path's units: persistent
 // workgroups over items of HEAD_ROWS rows (a wave takes 16: two pairs of 4-row
 // groups), the 4 tokens in LDS in operand order, and each wave's ring of weight
-// loads running on from one item into the next.
+// loads running on from one item into the next; three workgroups per CU.
 // ======================================================================================
 constexpr int HEAD_ROWS = 64;
+// three workgroups per CU: 35.2-35.5 against 36.7 us for one token (two per CU)
+constexpr int HEAD_WG_PER_CU = 3;
 
 template <int FMT>
-__global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void head_kernel(HeadArgs a) {
+__global__ __launch_bounds__(256, HEAD_WG_PER_CU) void head_kernel(HeadArgs a) {
   __shared__ MvSmem sm;
   using G = GV<FMT>;
   // unit u of an item: pair p = u / 8 of 4-row groups, K-quarter q = (u / 2) % 4,
@@ -1544,7 +1546,7 @@ template <int FMT, int NT> hipError_t launch_head_mf(const HeadArgs& a, int n_cu
 
 template <int FMT> hipError_t launch_head_vec(const HeadArgs& a, int n_cu, hipStream_t s) {
   const int n = ceil_div(a.V, HEAD_ROWS);
-  int grid = n_cu * FFN_WG_PER_CU<FMT>;
+  int grid = n_cu * HEAD_WG_PER_CU;
   if (n < grid) grid = n;
   hipLaunchKernelGGL(head_kernel<FMT>, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
