@@ -242,8 +242,9 @@ typedef struct {
  * positions each (1 <= max_len <= cap; it sets the number of position splits). */
 moe_status moe_attn_workspace_size(const moe_attn_desc* d, int32_t B, int32_t max_len, size_t* bytes);
 
-/* The decode-attention step (prep, split decode, combine: three kernels on
- * `stream`, asynchronous, capturable).
+/* The decode-attention step on `stream` (asynchronous, capturable): one
+ * decode kernel (norm and rotation of q and the new k, the append, the split
+ * attention) and, when the attended span is split, a combine kernel.
  *   q          bf16 [B][32][128] new token's queries (before norm and rotation)
  *   k, v       bf16 [B][4][128]  new token's keys and values
  *   q_gain, k_gain  bf16 [128]   RMSNorm gains

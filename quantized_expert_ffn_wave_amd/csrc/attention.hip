@@ -38,7 +38,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int AD = ATTN_D;            // head dimension
 constexpr int AGQ = ATTN_HQ / ATTN_HK;  // query heads per key-value head (8)
-constexpr int ATILE = 64;             // positions per tile of the transposed value cache
+constexpr int ATILE = 64;             // alignment of the attended span's start (positions)
 constexpr int ADW = 4;                // waves per decode workgroup
 constexpr int ASTEP = 32;             // positions per step of a decode wave
 constexpr float LOG2E = 1.4426950408889634f;
