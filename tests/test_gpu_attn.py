@@ -140,3 +140,36 @@ def test_positions_out_of_range_are_clamped():
     kc, vc = cache.plain()
     np.testing.assert_array_equal(vc[[0, 1], [0, cap - 1]], a["v"])
     assert np.isfinite(f(bits(out))).all()
+
+
+@pytest.mark.parametrize("window,lens", [(0, [5, 70, 130]), (synth.ATTN_WINDOW, [600, 514, 1000])])
+def test_unwritten_cache_entries_never_reach_the_output(window, lens):
+    """Every cache entry outside the attended positions holds a NaN; the output
+    must still equal the oracle's (masked scores are selected away, masked
+    values zeroed before their products)."""
+    B, cap = len(lens), 1024
+    lens = np.asarray(lens, np.int32)
+    say(f"case attn NaN-filled cache window={window} lens={lens.tolist()}")
+    a = synth.make_attn(B, cap, seed=11)
+    kc, vc = a["k_cache"].copy(), a["v_cache"].copy()
+    for b in range(B):
+        lo = max(0, lens[b] - window) if window else 0
+        keep = np.zeros(cap, bool)
+        keep[lo:lens[b] - 1] = True  # the new token's slot is written by the call
+        kc[b, ~keep] = 0x7FC0
+        vc[b, ~keep] = 0x7FC0
+    desc = moe.moe_attn_desc(window, int(window > 0), 10000.0, 1e-6)
+    cache = moe.AttnCache(B, cap)
+    cache.load(kc, vc)
+    sk = torch.from_numpy(a["sinks"]).cuda()
+    ws = moe.alloc_workspace(moe.attn_workspace_size(desc, B, cap))
+    out = moe.attn_decode(desc, dev(a["q"]), dev(a["k"]), dev(a["v"]), dev(a["q_gain"]), dev(a["k_gain"]), sk,
+                          torch.from_numpy(lens - 1).cuda(), cache, cap, workspace=ws)
+    torch.cuda.synchronize()
+    got = f(bits(out))
+    assert np.isfinite(got).all()
+    k2, v2 = cache.plain()
+    q_gpu = ws[:B * HQ * D * 2].view(torch.int16).cpu().numpy().view(np.uint16).reshape(B, HQ, D)
+    ref = oracle.attn_decode(q_gpu, k2, v2, lens, window, a["sinks"])
+    mag = oracle.attn_decode(q_gpu, k2, v2 & np.uint16(0x7FFF), lens, window, a["sinks"])
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 2.0 ** -7 * mag + 1e-6)
