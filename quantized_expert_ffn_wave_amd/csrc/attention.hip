@@ -9,10 +9,10 @@
 // One new token per sequence, two kernels on the caller's stream:
 //   decode   per (sequence, key-value head, split of positions): RMSNorm (and
 //            rotation) of the group's 8 query heads straight into MFMA operands;
-//            the split that holds the new position also normalises (rotates)
-//            the new key and appends it and the value to the cache; then the
-//            8 query heads against the split's keys and values on the 16x16x32
-//            bf16 MFMA, an online softmax, unnormalised partial outputs;
+//            the wave whose step holds the new position also normalises
+//            (rotates) the new key and appends it and the value to the cache;
+//            then the 8 query heads against the split's keys and values on the
+//            16x16x32 bf16 MFMA, an online softmax, unnormalised partial outputs;
 //   combine  per (sequence, query head): the splits and the sink merged (with
 //            one split the decode kernel writes the output itself).
 //
