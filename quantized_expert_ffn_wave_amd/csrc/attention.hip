@@ -199,8 +199,9 @@ __global__ __launch_bounds__(64 * ADW, 2) void attn_decode_kernel(AttnArgs a) {
   }
   const uint16_t* kbase = a.k_cache + ((size_t)b * ATTN_HK + kv) * (size_t)a.cap * AD;
   const uint16_t* vbase = a.v_cache + ((size_t)b * ATTN_HK + kv) * (size_t)AD * a.cap;
-  // start of the wave's step j; past its last step the last one is loaded
-  // again (never used), so that every load is issued and the waits stay exact
+  // start of the wave's step j, clamped to its last step: with an odd step
+  // count the second buffer of the last pair reloads that step (never used),
+  // so that every load is issued and the waits stay exact
   auto step_pos = [&](int j) { return base + ASTEP * (first_step + stride * min(j, nsteps - 1)); };
   auto load = [&](AStep& st, int t0) {
 #pragma unroll
@@ -295,14 +296,19 @@ __global__ __launch_bounds__(64 * ADW, 2) void attn_decode_kernel(AttnArgs a) {
                                                         o[dt], 0, 0, 0);
       }
     };
-    // two steps in flight: the same loads outstanding at the loop's entry and at
-    // its back edge, so each compute waits only for its own step's loads
-    for (int j = 0; j < nsteps; j += 2) {
+    // two steps in flight: the same loads outstanding at the loop's entry, at
+    // its back edge and after it, so each compute waits only for its own
+    // step's loads; the last pair (or single step) is computed after the loop
+    // and issues no loads
+    int j = 0;
+    for (; j + 2 < nsteps; j += 2) {
       compute(s0, step_pos(j), true);
       load(s0, step_pos(j + 2));
-      if (j + 1 < nsteps) compute(s1, step_pos(j + 1), true);  // (an odd count's last half is skipped)
+      compute(s1, step_pos(j + 1), true);
       load(s1, step_pos(j + 3));
     }
+    compute(s0, step_pos(j), true);
+    if (j + 1 < nsteps) compute(s1, step_pos(j + 1), true);
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
   }
