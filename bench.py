@@ -96,6 +96,13 @@ def read_traffic(workload: str, kernel: str = "ffn_up"):
         return None
 
 
+def operand_dtype(fmt: str) -> str:
+    """What the expert products compute in, for a weight format."""
+    if fmt == "bf16":
+        return "bf16 weights, bf16 operands, f32 accumulate"
+    return f"{fmt} weights, f16 operands (per-token power-of-two scaled), f32 accumulate"
+
+
 def pct(a, q):
     import numpy as np
     return round(float(np.percentile(np.asarray(a), q)), 5)
@@ -174,6 +181,7 @@ def bench_layer(args, moe, synth, torch, np):
     E, K = hosts[0].E, hosts[0].k
 
     exp_b = hosts[0].expert_bytes()
+    h_elem = 2 if fmt == "bf16" else 4
     gu_b = hosts[0].gate.nbytes() + hosts[0].up.nbytes()
 
     def touched_bytes(dl, xt, wst):
@@ -185,7 +193,8 @@ def bench_layer(args, moe, synth, torch, np):
         U = int((bufs["counts"].cpu().numpy() > 0).sum())
         # gate/up launch: the gate and up matrices of the touched experts and
         # the shared one, the tokens once, the SwiGLU rows of the S + T slots
-        return U, (U + 1) * exp_b, (U + 1) * gu_b + n * 2048 * 2 + (n * K + n) * 512 * 2
+        # (fp32 for the 4-bit formats, bf16 for bf16 weights)
+        return U, (U + 1) * exp_b, (U + 1) * gu_b + n * 2048 * 2 + (n * K + n) * 512 * h_elem
 
     touched, step_w_bytes, up_bytes = [], [], []
     for dl in dls:
@@ -340,7 +349,7 @@ def bench_layer(args, moe, synth, torch, np):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"{fmt} weights, f16 operands, f32 accumulate",
+        "dtype": operand_dtype(fmt),
         "data": "synthetic",
         "hbm_gbps_expert_weights": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
@@ -379,6 +388,7 @@ def bench_stack(args, moe, synth, torch, np):
     handles = [d.handle for d in dls]
     E, K = hosts[0].E, hosts[0].k
     exp_b = hosts[0].expert_bytes()
+    h_elem = 2 if fmt == "bf16" else 4
     gu_b = hosts[0].gate.nbytes() + hosts[0].up.nbytes()
     x0 = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
     x = x0.clone()
@@ -391,7 +401,7 @@ def bench_stack(args, moe, synth, torch, np):
     torch.cuda.synchronize()
     touched = [int((b["counts"].cpu().numpy() > 0).sum()) for _, b in rb]
     w_bytes = float(sum((u + 1) * exp_b for u in touched))
-    up_bytes = [(u + 1) * gu_b + T * 2048 * 2 + (T * K + T) * 512 * 2 for u in touched]
+    up_bytes = [(u + 1) * gu_b + T * 2048 * 2 + (T * K + T) * 512 * (2 if fmt == "bf16" else 4) for u in touched]
     xin = [b["x_in"] for _, b in rb]
     log(f"touched experts per layer: mean {np.mean(touched):.1f}; expert bytes per step {w_bytes / 1e6:.1f} MB")
 
@@ -504,7 +514,7 @@ def bench_stack(args, moe, synth, torch, np):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"{fmt} weights, f16 operands, f32 accumulate",
+        "dtype": operand_dtype(fmt),
         "data": "synthetic",
         "hbm_gbps_expert_weights": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),

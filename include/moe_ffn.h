@@ -18,6 +18,21 @@
  *   E_e(x) = Wd_e (silu(Wg_e x) * (Wu_e x))  (SwiGLU, silu(g) = g/(1+e^-g))
  *   y      = sum_j w_j E_{ids_j}(x) + shared_scale * E_shared(x)   -> bf16
  *
+ * Arithmetic: router logits accumulate in fp32 from bf16 operands; the SwiGLU
+ * output h is rounded to bf16 between the two expert products; expert outputs
+ * are summed in fp32 in the order j = 0..k-1, then the shared expert, and the
+ * result is rounded once to bf16.  With 4-bit weights both expert products run
+ * on fp16 operands (every q4_1 weight d*q + m rounded once to fp16, every
+ * NVFP4 E2M1 x E4M3 product exact in fp16, the tensor scale applied in fp32),
+ * and each token's activations (x, and h per expert-output row) enter them
+ * multiplied by a power of two that puts the row's largest magnitude in
+ * [2^14, 2^15), undone in fp32 afterwards: the size of a token row is then
+ * limited only by fp32, not by fp16's range.
+ * Supported inputs: finite x (NaN and infinity are outside the contract);
+ * finite weights with every q4_1 block satisfying |d*q + m| <= 65504 for
+ * q = 0..15; results whose intermediate values (logits, gate/up products, h,
+ * expert outputs) are finite in fp32.  The library does not check these.
+ *
  * and moe_stack_forward chains layers as a pre-norm residual stack:
  *   r <- x;  for each layer: r <- r + bf16(layer(bf16(RMSNorm(r))));  x <- bf16(r)
  * with RMSNorm(r) = r / sqrt(mean(r^2) + eps) (gain 1) and r kept in fp32.
@@ -123,6 +138,7 @@ typedef struct {
   int32_t* perm;     /* [S] expert-sorted position -> slot; stable (token order inside a bucket) */
   void* x_in;        /* bf16 [T][d_model]: the layer's input (in a stack: bf16(RMSNorm(r))) */
   void* y_out;       /* bf16 [T][d_model]: the layer's output */
+  int32_t* inv_perm; /* [S] slot -> its expert-sorted position (the inverse of perm) */
 } moe_route_out;
 
 typedef struct moe_layer moe_layer; /* opaque, host memory only */

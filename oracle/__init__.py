@@ -63,6 +63,8 @@ def lib():
         L.orc_bf16_rne.argtypes = [dbl]
         L.orc_weight.restype = ctypes.c_float
         L.orc_weight.argtypes = [ctypes.POINTER(_Mat), ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+        L.orc_decode_matrix.argtypes = [ctypes.POINTER(_Mat), ctypes.c_int64, ctypes.c_void_p]
+        L.orc_decode_matrix.restype = None
         L.orc_topk.argtypes = [vp, i32, i32, vp, vp]
         L.orc_route_weights.argtypes = [vp, i32, vp, i32, i32, vp]
         L.orc_layer_forward.argtypes = [ctypes.POINTER(_Layer), vp, i32, vp, vp, vp, vp, vp, vp, i32]
@@ -162,14 +164,11 @@ def weight(q, n: int, r: int, c: int) -> float:
 
 
 def decode_matrix(q, n: int) -> np.ndarray:
-    """All weights of matrix n of a stored set, decoded to fp32 (slow; small shapes)."""
+    """All weights of matrix n of a stored set, decoded to fp32."""
     keep = []
     m = _mat(q, keep)
     out = np.empty((q.rows, q.cols), np.float32)
-    f = lib().orc_weight
-    for r in range(q.rows):
-        for c in range(q.cols):
-            out[r, c] = f(ctypes.byref(m), n, r, c)
+    lib().orc_decode_matrix(ctypes.byref(m), n, _p(out))
     return out
 
 

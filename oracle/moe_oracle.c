@@ -161,6 +161,12 @@ float orc_weight(const orc_mat* M, int64_t n, int64_t r, int64_t c) {
 /* ---- the layer, step by step ------------------------------------------------ */
 
 /* logits[e] = sum_k x[k] * Wr[e][k] (+ b[e]), fp64, k ascending. */
+/* All weights of matrix n, decoded (O1), into out[rows][cols]. */
+void orc_decode_matrix(const orc_mat* M, int64_t n, float* out) {
+  for (int64_t r = 0; r < M->rows; ++r)
+    for (int64_t c = 0; c < M->cols; ++c) out[r * M->cols + c] = orc_weight(M, n, r, c);
+}
+
 void orc_router_logits(const orc_layer* L, const double* x, double* logits) {
   for (int e = 0; e < L->E; ++e) {
     double s = 0;

@@ -58,7 +58,7 @@ class moe_attn_desc(ctypes.Structure):
 class moe_route_out(ctypes.Structure):
     _fields_ = [("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("logits", ctypes.c_void_p),
                 ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p),
-                ("x_in", ctypes.c_void_p), ("y_out", ctypes.c_void_p)]
+                ("x_in", ctypes.c_void_p), ("y_out", ctypes.c_void_p), ("inv_perm", ctypes.c_void_p)]
 
 
 # torch is imported before the library is loaded so that one HIP runtime serves
@@ -374,7 +374,8 @@ def route_buffers(T: int, k: int, E: int, device="cuda", d: int = 2048):
              offsets=torch.empty(E + 1, dtype=torch.int32, device=device),
              perm=torch.empty(max(T * k, 1), dtype=torch.int32, device=device),
              x_in=torch.empty((T, d), dtype=torch.bfloat16, device=device),
-             y_out=torch.empty((T, d), dtype=torch.bfloat16, device=device))
+             y_out=torch.empty((T, d), dtype=torch.bfloat16, device=device),
+             inv_perm=torch.empty(max(T * k, 1), dtype=torch.int32, device=device))
     r = moe_route_out(*[b[n].data_ptr() for n, _ in moe_route_out._fields_])
     return r, b
 

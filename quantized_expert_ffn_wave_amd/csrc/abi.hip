@@ -76,7 +76,7 @@ moe_status check_qmat(const moe_qmat& q, int fmt, const char* name) {
 }
 
 struct WsLayout {
-  size_t logit_part, logits, ids, w, counts, offsets, perm, inv_perm, tiles, ctl, h, y, total;
+  size_t logit_part, logits, ids, w, counts, offsets, perm, inv_perm, tiles, ctl, h, y, xsc, hmax, total;
   int max_tiles;
 };
 
@@ -101,8 +101,12 @@ WsLayout ws_layout(const moe_layer_desc& d, int T) {
   L.inv_perm = take(sizeof(int32_t) * S);
   L.tiles = take(sizeof(moe::Item) * L.max_tiles);
   L.ctl = take(sizeof(int32_t) * moe::CTL_WORDS);
-  L.h = take(sizeof(uint16_t) * R * moe::D_FF);
+  // SwiGLU output: fp32 for the 4-bit formats (scaled into fp16 by the down
+  // kernel with the row's largest |h|), bf16 for bf16 weights
+  L.h = take((d.wfmt == MOE_W_BF16 ? sizeof(uint16_t) : sizeof(float)) * R * moe::D_FF);
   L.y = take(sizeof(float) * R * moe::D_MODEL);
+  L.xsc = take(sizeof(float) * (size_t)T);
+  L.hmax = take(sizeof(uint32_t) * R);
   L.total = o;
   return L;
 }
@@ -148,8 +152,10 @@ moe::LayerArgs make_args(const moe_layer* L, const void* x, int T, char* ws, con
   a.inv_perm = (int32_t*)(ws + W.inv_perm);
   a.tiles = (moe::Item*)(ws + W.tiles);
   a.ctl = (int32_t*)(ws + W.ctl);
-  a.h = (uint16_t*)(ws + W.h);
+  a.h = (void*)(ws + W.h);
   a.y = (float*)(ws + W.y);
+  a.xsc = (float*)(ws + W.xsc);
+  a.hmax = (uint32_t*)(ws + W.hmax);
   a.max_tiles = W.max_tiles;
   return a;
 }
@@ -186,6 +192,7 @@ moe_status run_layer(const moe_layer* L, moe::LayerArgs& a, const WsLayout& W, c
         (e = copy_async(route->counts, a.counts, (size_t)E * 4, s)) != hipSuccess ||
         (e = copy_async(route->offsets, a.offsets, (size_t)(E + 1) * 4, s)) != hipSuccess ||
         (e = copy_async(route->perm, a.perm, S * 4, s)) != hipSuccess ||
+        (e = copy_async(route->inv_perm, a.inv_perm, S * 4, s)) != hipSuccess ||
         (e = copy_async(route->x_in, a.x, (size_t)a.T * moe::D_MODEL * 2, s)) != hipSuccess)
       return hip_fail(e, "route copy");
   }

@@ -114,8 +114,13 @@ struct LayerArgs {
   int32_t* inv_perm;        // [S]
   Item* tiles;              // work list: one entry per token tile (row chunk 0)
   int32_t* ctl;             // [CTL_WORDS]
-  uint16_t* h;              // [S + n_shared*T][D_FF] SwiGLU output (fp16 or bf16 bits)
+  void* h;                  // [S + n_shared*T][D_FF] SwiGLU output: fp32 for the 4-bit formats, bf16 bits else
   float* y;                 // [S + n_shared*T][D_MODEL] expert outputs
+  // 4-bit formats only (their products run on fp16 operands): the power-of-two
+  // scale of each token's activations, and the bits of each expert-output
+  // row's largest |h| (fp32; raised with atomic max by gate/up, read by down)
+  float* xsc;               // [T]
+  uint32_t* hmax;           // [S + n_shared*T]
   int max_tiles;
   // combine targets
   uint16_t* out;            // bf16 [T][D_MODEL] layer output (single layer), or null
@@ -139,6 +144,43 @@ __device__ inline uint16_t f32_to_bf16(float f) {
 
 // silu(g) * u with the hardware reciprocal (1 ulp; the result is stored in 16 bits)
 __device__ inline float silu_mul(float g, float u) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u; }
+
+// Power-of-two scale for a row of activations whose largest magnitude has the
+// fp32 bit pattern `maxbits` (sign clear): the largest element lands in
+// [2^14, 2^15), so the row fits fp16 with its full 11-bit precision (the fp16
+// maximum is about 2^16).  The exponent is clamped to [-100, 100], which leaves
+// all-zero and tiny rows unscaled past 2^100.  Multiplying by it, and by its
+// inverse, is exact in fp32.
+__device__ inline float pow2_scale(uint32_t maxbits) {
+  const int e = (int)(maxbits >> 23);  // biased exponent of the row maximum
+  const int k = min(max(141 - e, -100), 100);
+  return __uint_as_float((uint32_t)(k + 127) << 23);
+}
+__device__ inline float pow2_inv(float s) { return __uint_as_float((254u << 23) - __float_as_uint(s)); }
+
+// Lane exchange for the wave-wide maximum: step m pairs lane i with i ^ m
+// (m = 4: with 7 - i inside groups of 8, which reaches the same set).
+template <int M> __device__ inline uint32_t xchg(uint32_t v) {
+  if constexpr (M == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
+  } else {
+    constexpr int ctrl = (M == 8) ? 0x128 : (M == 4) ? 0x141 : (M == 2) ? 0x4E : 0xB1;
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, ctrl, 0xF, 0xF, false);
+  }
+}
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, xchg<32>(v));
+  v = max(v, xchg<16>(v));
+  v = max(v, xchg<8>(v));
+  v = max(v, xchg<4>(v));
+  v = max(v, xchg<2>(v));
+  v = max(v, xchg<1>(v));
+  return v;
+}
 
 }  // namespace moe
 

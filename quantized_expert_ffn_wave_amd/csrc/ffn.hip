@@ -25,6 +25,8 @@
 // the fixed order j = 0..K-1 and the shared expert row, and rounds once to
 // bf16 (in a stack it also updates the fp32 residual and writes the next
 // layer's RMSNorm input).
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
@@ -79,10 +81,26 @@ template <int B> __device__ inline uint32_t fp4x2_to_f16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, B));
 }
 
-// two bf16 (lo, hi halves of v) -> packed fp16 pair (exact for normal-range values)
-__device__ inline uint32_t bf16x2_to_f16x2(uint32_t v) {
-  return __builtin_bit_cast(uint32_t,
-                            __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v << 16), __uint_as_float(v & 0xFFFF0000u)));
+// two bf16 (lo, hi halves of v) times a power of two sc -> packed fp16 pair.
+// Exact wherever the scaled value is an fp16 normal: with sc from pow2_scale
+// of the row maximum that is every element above 2^-28 of that maximum (a
+// bf16 significand has 8 bits, an fp16 one 11).
+__device__ inline uint32_t bf16x2_to_f16x2(uint32_t v, float sc) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(v << 16) * sc,
+                                                                  __uint_as_float(v & 0xFFFF0000u) * sc));
+}
+
+// two fp32 values times a power of two sc -> packed fp16 pair, rounded toward zero
+__device__ inline uint32_t f32x2_to_f16x2(uint32_t lo, uint32_t hi, float sc) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(lo) * sc, __uint_as_float(hi) * sc));
+}
+
+// largest |bf16| of the 8 elements in v, as bits (finite inputs)
+__device__ inline uint32_t bf16_absmax8(const u32x4& v) {
+  uint32_t m = 0u;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) m = max(m, max(v[q] & 0x7FFFu, (v[q] >> 16) & 0x7FFFu));
+  return m;
 }
 
 // natural pairs N0=(e0,e1) N1=(e2,e3) N2=(e4,e5) N3=(e6,e7) -> the order the
@@ -97,18 +115,17 @@ __device__ inline void q4_order(uint32_t n0, uint32_t n1, uint32_t n2, uint32_t 
 __device__ inline float f16lo(uint32_t v) { return (float)as_f16x2(v)[0]; }
 __device__ inline float f16hi(uint32_t v) { return (float)as_f16x2(v)[1]; }
 
-// fp32 -> stored SwiGLU element: fp16 (saturated) for the 4-bit formats, bf16 otherwise.
-template <int FMT> __device__ inline uint16_t h_store(float v);
-template <> __device__ inline uint16_t h_store<FMT_Q4_1>(float v) {
-  v = fminf(fmaxf(v, -65504.f), 65504.f);
-  return __builtin_bit_cast(uint16_t, (_Float16)v);
-}
-template <> __device__ inline uint16_t h_store<FMT_NVFP4>(float v) { return h_store<FMT_Q4_1>(v); }
-template <> __device__ inline uint16_t h_store<FMT_BF16>(float v) { return f32_to_bf16(v); }
-
 // Operand precision of the expert GEMMs: fp16 for the 4-bit formats (their
-// decoded values are exact in fp16), bf16 for bf16 weights.
+// decoded values are exact in fp16), bf16 for bf16 weights.  The activations
+// (x, and the SwiGLU output h, stored as bf16) enter the fp16 products scaled
+// per token by a power of two (pow2_scale of the row's largest magnitude),
+// which is undone in fp32 on the products' sums: fp16's 5-bit exponent then
+// never limits the range of a token row.
 template <int FMT> constexpr bool OPER_F16 = FMT != FMT_BF16;
+// Element of the stored SwiGLU output h: fp32 where the down product runs on
+// scaled fp16 operands (the scale is found from the whole row, after every
+// gate/up item has written it), bf16 for bf16 weights.
+template <int FMT> using HElem = std::conditional_t<OPER_F16<FMT>, float, uint16_t>;
 
 // ======================================================================================
 // Per-format chunk of a weight row: 32 consecutive elements of one row, the
@@ -336,6 +353,7 @@ struct MvKS {
 struct MvSmem {
   uint32_t x[2][GV_GROUP * MV_TOKW];
   MvKS ks[2][MV_CHUNKS];
+  float isc[2][GV_GROUP];  // 4-bit formats: inverse activation scale per token
 };
 
 // token t of a vector-path item, from its packed ids (no indexed array)
@@ -344,22 +362,36 @@ __device__ inline int item_token(const Item& item, int t) {
   return (int)((pair >> (16 * (t & 1))) & 0xFFFFu);
 }
 
-// One thread per (token, chunk): the chunk's 32 activation elements.
+// One thread per (token, chunk): the chunk's 32 activation elements and, for
+// the 4-bit formats, the token's activation scale (gate/up: from the top-k's
+// per-token maximum of x; down: from the gate/up kernel's maximum of |h| on
+// the expert-output row).
 struct MvStage {
-  u32x4 v[4];
+  u32x4 v[8];  // 32 bf16 (x, or bf16 h) in v[0..3], or 32 fp32 (h of the 4-bit formats)
+  float sc;
 };
 
-template <bool UP>
+template <int FMT, bool UP>
 __device__ inline void mv_stage_load(const LayerArgs& a, const Item& item, const ItemTok& it, MvStage& st) {
   constexpr int NCH = UP ? D_MODEL / 32 : D_FF / 32;
   const int t = threadIdx.x / NCH, c = threadIdx.x % NCH;
 #pragma unroll
   for (int i = 0; i < 4; ++i) st.v[i] = u32x4{0u, 0u, 0u, 0u};
+  st.sc = 1.f;
   if (t < GV_GROUP && t < it.cnt) {
-    const uint16_t* src = UP ? a.x + (size_t)item_token(item, t) * D_MODEL + 32 * c
-                             : a.h + (size_t)row_of(a, it, t) * D_FF + 32 * c;
+    const int tok = UP ? item_token(item, t) : 0;
+    const int row = UP ? 0 : row_of(a, it, t);
+    if constexpr (!UP && OPER_F16<FMT>) {
+      const float* src = static_cast<const float*>(a.h) + (size_t)row * D_FF + 32 * c;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st.v[i] = ld16<false>(src + 8 * i);
+      for (int i = 0; i < 8; ++i) st.v[i] = ld16<false>(src + 4 * i);
+    } else {
+      const uint16_t* src = UP ? a.x + (size_t)tok * D_MODEL + 32 * c
+                               : static_cast<const uint16_t*>(a.h) + (size_t)row * D_FF + 32 * c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.v[i] = ld16<false>(src + 8 * i);
+    }
+    if constexpr (OPER_F16<FMT>) st.sc = UP ? a.xsc[tok] : pow2_scale(a.hmax[row]);
   }
 }
 
@@ -372,15 +404,22 @@ __device__ inline void mv_stage_store(const MvStage& st, MvSmem& sm, int buf) {
   const int t = threadIdx.x / NCH, c = threadIdx.x % NCH;
   if (t >= GV_GROUP) return;
   uint32_t n[16], o[16];
+  if constexpr (!UP && OPER_F16<FMT>) {  // fp32 h, scaled into fp16 pairs
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 16; ++i) n[i] = f32x2_to_f16x2(st.v[i >> 1][2 * (i & 1)], st.v[i >> 1][2 * (i & 1) + 1], st.sc);
+  } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) n[4 * i + e] = st.v[i][e];
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) n[4 * i + e] = st.v[i][e];
+    }
+    if constexpr (OPER_F16<FMT>) {  // bf16 x, scaled into fp16
+#pragma unroll
+      for (int i = 0; i < 16; ++i) n[i] = bf16x2_to_f16x2(n[i], st.sc);
+    }
   }
-  if (OPER_F16<FMT> && UP) {  // x arrives as bf16; the stored SwiGLU output is already operand typed
-#pragma unroll
-    for (int i = 0; i < 16; ++i) n[i] = bf16x2_to_f16x2(n[i]);
-  }
+  if constexpr (OPER_F16<FMT>)
+    if (c == 0) sm.isc[buf][t] = pow2_inv(st.sc);
   if constexpr (FMT == FMT_Q4_1) {
     const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
     float se = 0.f, so = 0.f;  // sums of x' over the even and the odd elements
@@ -607,7 +646,7 @@ __device__ void up_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem&
   int buf = 0;
   {
     MvStage st;
-    mv_stage_load<true>(a, item, it, st);
+    mv_stage_load<FMT, true>(a, item, it, st);
     mv_stage_store<FMT, true>(st, sm, buf);
   }
   __syncthreads();
@@ -628,10 +667,14 @@ __device__ void up_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem&
       nit = item_tokens(nitem);
       nw = chunk_weights<FMT, true>(a, nitem);
       nr0 = first_row(nitem, nw);
-      mv_stage_load<true>(a, nitem, nit, st);
+      mv_stage_load<FMT, true>(a, nitem, nit, st);
     }
     const bool writer = (lane & 36) == 0 && my_t < it.cnt;
-    uint16_t* hdst = a.h + (size_t)(row_of(a, it, 0) + my_t) * D_FF + item_chunk(item.head) * VR + wave * (VR / 4) + j;
+    const int hrow = row_of(a, it, 0) + my_t;
+    HElem<FMT>* hdst = static_cast<HElem<FMT>*>(a.h) + (size_t)hrow * D_FF + item_chunk(item.head) * VR +
+                       wave * (VR / 4) + j;
+    const float isc = OPER_F16<FMT> ? sm.isc[buf][my_t] : 1.f;  // undoes the token's activation scale
+    float hm = 0.f;                                             // largest |h| this lane writes
     f32x4 acc[2] = {}, negK = {}, S = {};
     uint32_t xq[16];
 #pragma unroll
@@ -659,9 +702,20 @@ __device__ void up_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem&
         }
         float v = mv_reduce8(acc[0], acc[1]);
         if (FMT == FMT_NVFP4) v *= (lane & 32) ? w.tsu : w.tsg;
+        if constexpr (OPER_F16<FMT>) v *= isc;
         const float up = upper_half(v);
-        if (writer) hdst[4 * g] = h_store<FMT>(silu_mul(v, up));
+        const float hv = silu_mul(v, up);
+        if (writer) {
+          if constexpr (OPER_F16<FMT>) hdst[4 * g] = hv;
+          else hdst[4 * g] = f32_to_bf16(hv);
+          hm = fmaxf(hm, fabsf(hv));
+        }
       }
+    }
+    if constexpr (OPER_F16<FMT>) {  // the rows' largest |h| (a quad holds 4 rows of one token) for down
+      hm = fmaxf(hm, dpp_partner<1>(hm));
+      hm = fmaxf(hm, dpp_partner<2>(hm));
+      if (writer && (lane & 3) == 0) atomicMax(a.hmax + hrow, __float_as_uint(hm));
     }
     if (!has_next) break;
     mv_stage_store<FMT, true>(st, sm, buf ^ 1);
@@ -703,7 +757,7 @@ __device__ void down_stream(const LayerArgs& a, int base, int n, int n_mf, MvSme
   int buf = 0;
   {
     MvStage st;
-    mv_stage_load<false>(a, item, it, st);
+    mv_stage_load<FMT, false>(a, item, it, st);
     mv_stage_store<FMT, false>(st, sm, buf);
   }
   __syncthreads();
@@ -724,9 +778,10 @@ __device__ void down_stream(const LayerArgs& a, int base, int n, int n_mf, MvSme
       nit = item_tokens(nitem);
       nw = chunk_weights<FMT, false>(a, nitem);
       nr0 = first_row(nitem, nw);
-      mv_stage_load<false>(a, nitem, nit, st);
+      mv_stage_load<FMT, false>(a, nitem, nit, st);
     }
     const bool writer = (lane & 4) == 0 && my_t < it.cnt;
+    const float isc = OPER_F16<FMT> ? sm.isc[buf][my_t] : 1.f;  // undoes the row's h scale
     float* ydst = a.y + (size_t)(row_of(a, it, 0) + my_t) * D_MODEL + item_chunk(item.head) * VDR + wave * (VDR / 4) +
                   4 * ((lane >> 5) & 1) + j;
     uint32_t xq[16];
@@ -743,6 +798,7 @@ __device__ void down_stream(const LayerArgs& a, int base, int n, int n_mf, MvSme
       if (u & 1) {
         float v = mv_reduce8(acc[0], acc[1]);
         if (FMT == FMT_NVFP4) v *= w.tsg;
+        if constexpr (OPER_F16<FMT>) v *= isc;
         if (writer) ydst[4 * (u - 1)] = v;
       }
     }
@@ -793,6 +849,7 @@ template <int BN> struct FfnSmem {
   uint16_t x[2][BN * TS];  // K-chunks alternate between the two, so one barrier per chunk suffices
   int tok[BN];
   int row[BN];
+  float isc[BN];           // 4-bit formats: inverse activation scale per token column
 };
 
 // Store 16 activation elements (natural-order pairs src[8]) into LDS in the
@@ -820,30 +877,40 @@ __device__ inline f32x16 mfma32(u32x4 av, u32x4 bv, f32x16 c) {
                                                  0, 0);
 }
 
-template <int BN> __device__ inline void mfma_tables(const LayerArgs& a, const ItemTok& it, FfnSmem<BN>& sm) {
+// UP: the activation scale is the token's (x); down: the expert-output row's (h).
+template <int FMT, bool UP, int BN>
+__device__ inline void mfma_tables(const LayerArgs& a, const ItemTok& it, FfnSmem<BN>& sm) {
   const int i = threadIdx.x;
   if (i < BN) {
     // matrix-core tiles are shared-expert tiles or routed buckets (tokens via perm)
-    sm.tok[i] = (i < it.cnt) ? (it.shared ? it.p0 + i : a.perm[it.p0 + i] / a.K) : -1;
-    sm.row[i] = (i < it.cnt) ? row_of(a, it, i) : -1;
+    const int tok = (i < it.cnt) ? (it.shared ? it.p0 + i : a.perm[it.p0 + i] / a.K) : -1;
+    const int row = (i < it.cnt) ? row_of(a, it, i) : -1;
+    sm.tok[i] = tok;
+    sm.row[i] = row;
+    if constexpr (OPER_F16<FMT>)
+      sm.isc[i] = (i < it.cnt) ? pow2_inv(UP ? a.xsc[tok] : pow2_scale(a.hmax[row])) : 1.f;
   }
 }
 
 // One K-chunk in registers: the lane's 32 weights of each row block, and the
 // thread's MF_XK activations of token tid / MF_XT (elements MF_XK * (tid % MF_XT) ..).
-template <int FMT, int BN, int RB> struct MfStage {
+template <int FMT, int BN, int RB, bool XF32> struct MfStage {
   typename GV<FMT>::Raw w[RB];
-  u32x4 x[MF_XK<BN> / 8];
+  u32x4 x[MF_XK<BN> / (XF32 ? 4 : 8)];  // the thread's activations: bf16, or fp32 (h of the 4-bit formats)
 };
 
 // acc[b][tt] += W_block_b (this wave's rows) x X (tokens 32 tt ..) over K = kdim.
 // q[b], wrow[b]: the matrix and the lane's weight row of block b; xsrc: the
-// thread's activation row and offset (a valid row also for tokens past the
-// tile's count: their columns are never stored, and a column only meets its
-// own activations).
-template <int FMT, int BN, int RB, int NS>
+// thread's activation row (bf16, or fp32 with XF32) and offset (a valid row
+// also for tokens past the tile's count: their columns are never stored, and a
+// column only meets its own activations); xscale: that row's activation scale
+// (4-bit formats).
+template <int FMT, int BN, int RB, int NS, bool XF32 = false>
 __device__ inline void mf_kloop(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<BN>& sm, const QMat (&q)[RB],
-                                const size_t (&wrow)[RB], const uint16_t* xsrc, bool x_bf16, int kdim) {
+                                const size_t (&wrow)[RB], const void* xsrc, float xscale, int kdim) {
+  using Stage = MfStage<FMT, BN, RB, XF32>;
+  constexpr int NX = MF_XK<BN> / (XF32 ? 4 : 8);  // 16-byte activation loads per thread and chunk
+  static_assert(!XF32 || OPER_F16<FMT>, "fp32 activations feed the fp16 products only");
   static_assert(NS % 2 == 0, "chunk j uses LDS buffer j % 2");
   const int tid = threadIdx.x, lane = tid & 63;
   const int h = lane >> 5, c = lane & 31;
@@ -851,7 +918,7 @@ __device__ inline void mf_kloop(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<BN>& sm, c
   const int nc = kdim / 64;
   // every load is issued unconditionally (past the last chunk the last one is
   // loaded again), so that the compiler's wait counts stay exact
-  auto fetch = [&](MfStage<FMT, BN, RB>& st, int ck) {
+  auto fetch = [&](Stage& st, int ck) {
     ck = min(ck, nc - 1);
     // scale position of block 2 ck + h: with 2048 columns the blocks are stored
     // in the order k mod 16, k / 16, i.e. at 8 (ck mod 8) + 4 h + ck / 8
@@ -860,22 +927,29 @@ __device__ inline void mf_kloop(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<BN>& sm, c
 #pragma unroll
     for (int b = 0; b < RB; ++b) st.w[b] = GV<FMT>::template load_slot<false>(q[b], wrow[b], 0u, 2 * ck + h, slot, kdim);
 #pragma unroll
-    for (int i = 0; i < MF_XK<BN> / 8; ++i) st.x[i] = ld16<false>(xsrc + 64 * ck + 8 * i);
+    for (int i = 0; i < NX; ++i)
+      st.x[i] = ld16<false>(static_cast<const uint8_t*>(xsrc) + (XF32 ? 4 : 2) * 64 * ck + 16 * i);
   };
-  auto stage = [&](const MfStage<FMT, BN, RB>& st, uint16_t* buf) {
+  auto stage = [&](const Stage& st, uint16_t* buf) {
 #pragma unroll
     for (int g = 0; g < MF_XK<BN> / 16; ++g) {
       uint32_t xv[8];
+      if constexpr (XF32) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) xv[i] = st.x[2 * g + i / 4][i % 4];
-      if (OPER_F16<FMT> && x_bf16) {
+        for (int i = 0; i < 8; ++i)
+          xv[i] = f32x2_to_f16x2(st.x[4 * g + i / 2][2 * (i & 1)], st.x[4 * g + i / 2][2 * (i & 1) + 1], xscale);
+      } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xv[i] = bf16x2_to_f16x2(xv[i]);
+        for (int i = 0; i < 8; ++i) xv[i] = st.x[2 * g + i / 4][i % 4];
+        if constexpr (OPER_F16<FMT>) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) xv[i] = bf16x2_to_f16x2(xv[i], xscale);
+        }
       }
       stage_x16<FMT>(buf + xt * TS + MF_XK<BN> * xs + 16 * g, xv);
     }
   };
-  auto multiply = [&](const MfStage<FMT, BN, RB>& st, const uint16_t* buf) {
+  auto multiply = [&](const Stage& st, const uint16_t* buf) {
     uint32_t wv[RB][16];
 #pragma unroll
     for (int b = 0; b < RB; ++b) GV<FMT>::decode(st.w[b], wv[b]);
@@ -891,7 +965,7 @@ __device__ inline void mf_kloop(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<BN>& sm, c
       }
     }
   };
-  MfStage<FMT, BN, RB> st[NS];
+  Stage st[NS];
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i) fetch(st[i], i);
 #pragma unroll 1
@@ -913,7 +987,7 @@ __device__ void mfma_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int m
   constexpr int RB = MF_UP_RB<BN>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c = lane & 31;
-  mfma_tables(a, it, sm);
+  mfma_tables<FMT, true>(a, it, sm);
   __syncthreads();
   QMat q[RB];
   size_t wrow[RB];
@@ -927,8 +1001,9 @@ __device__ void mfma_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int m
   }
   const int xtok = sm.tok[min(tid / MF_XT<BN>, it.cnt - 1)];
   const uint16_t* xsrc = a.x + (size_t)xtok * D_MODEL + MF_XK<BN> * (tid % MF_XT<BN>);
+  const float xscale = OPER_F16<FMT> ? a.xsc[xtok] : 1.f;
   f32x16 acc[RB][MF_TT<BN>] = {};
-  mf_kloop<FMT, BN, RB, MF_NS_UP<FMT, BN>>(acc, sm, q, wrow, xsrc, true, D_MODEL);
+  mf_kloop<FMT, BN, RB, MF_NS_UP<FMT, BN>>(acc, sm, q, wrow, xsrc, xscale, D_MODEL);
   // acc[b][tt][4i+j] = row 8i + 4h + j of block b, token 32tt + c.  The gate
   // value of a lane's output (block 0 / rows below 16) sits at gi, its up at ui.
   const float tsg = (FMT == FMT_NVFP4) ? G.ts[mat] : 1.f;
@@ -937,21 +1012,36 @@ __device__ void mfma_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int m
 #pragma unroll
   for (int tt = 0; tt < MF_TT<BN>; ++tt) {
     const int hrow = sm.row[32 * tt + c];
-    if (hrow < 0) continue;
+    // the token's inverse activation scale folds into the tensor scales
+    const float isc = OPER_F16<FMT> ? sm.isc[32 * tt + c] : 1.f;
+    const float sg = tsg * isc, su = tsu * isc;
+    float hm = 0.f;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      uint16_t hv[4];
+      float hf[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float g = (RB == 2) ? acc[0][tt][4 * i + j] : acc[0][tt][4 * i + j];
         const float u = (RB == 2) ? acc[RB - 1][tt][4 * i + j] : acc[0][tt][4 * (i + 2) + j];
-        hv[j] = h_store<FMT>(silu_mul(g * tsg, u * tsu));
+        hf[j] = silu_mul(g * sg, u * su);
+        hm = fmaxf(hm, fabsf(hf[j]));
       }
       const int n = n0 + 32 * RB / 2 * wave + 8 * i + 4 * h;
-      uint2 pk;
-      pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
-      pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-      *reinterpret_cast<uint2*>(a.h + (size_t)hrow * D_FF + n) = pk;
+      if (hrow >= 0) {
+        if constexpr (OPER_F16<FMT>) {
+          *reinterpret_cast<float4*>(static_cast<float*>(a.h) + (size_t)hrow * D_FF + n) =
+              make_float4(hf[0], hf[1], hf[2], hf[3]);
+        } else {
+          uint2 pk;
+          pk.x = (uint32_t)f32_to_bf16(hf[0]) | ((uint32_t)f32_to_bf16(hf[1]) << 16);
+          pk.y = (uint32_t)f32_to_bf16(hf[2]) | ((uint32_t)f32_to_bf16(hf[3]) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.h) + (size_t)hrow * D_FF + n) = pk;
+        }
+      }
+    }
+    if constexpr (OPER_F16<FMT>) {  // the row's largest |h| for down: both lane halves, one atomic per wave
+      hm = fmaxf(hm, upper_half(hm));
+      if (h == 0 && hrow >= 0) atomicMax(a.hmax + hrow, __float_as_uint(hm));
     }
   }
   __syncthreads();  // tables and tiles are reused by the next item
@@ -962,20 +1052,23 @@ template <int FMT, int BN>
 __device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const ItemTok& it, int r0, FfnSmem<BN>& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c = lane & 31;
-  mfma_tables(a, it, sm);
+  mfma_tables<FMT, false>(a, it, sm);
   __syncthreads();
   const QMat q[2] = {D, D};
   const size_t wr = (size_t)mat * D_MODEL + r0 + 64 * wave + c;
   const size_t wrow[2] = {wr, wr + 32};
   const int hrow_x = sm.row[min(tid / MF_XT<BN>, it.cnt - 1)];
-  const uint16_t* xsrc = a.h + (size_t)hrow_x * D_FF + MF_XK<BN> * (tid % MF_XT<BN>);
+  const HElem<FMT>* xsrc =
+      static_cast<const HElem<FMT>*>(a.h) + (size_t)hrow_x * D_FF + MF_XK<BN> * (tid % MF_XT<BN>);
+  const float xscale = OPER_F16<FMT> ? pow2_scale(a.hmax[hrow_x]) : 1.f;
   f32x16 acc[2][MF_TT<BN>] = {};
-  mf_kloop<FMT, BN, 2, MF_NS_DN<FMT, BN>>(acc, sm, q, wrow, xsrc, false, D_FF);
-  const float ts = (FMT == FMT_NVFP4) ? D.ts[mat] : 1.f;
+  mf_kloop<FMT, BN, 2, MF_NS_DN<FMT, BN>, OPER_F16<FMT>>(acc, sm, q, wrow, xsrc, xscale, D_FF);
+  const float tsd = (FMT == FMT_NVFP4) ? D.ts[mat] : 1.f;
 #pragma unroll
   for (int tt = 0; tt < MF_TT<BN>; ++tt) {
     const int yrow = sm.row[32 * tt + c];
     if (yrow < 0) continue;
+    const float ts = OPER_F16<FMT> ? tsd * sm.isc[32 * tt + c] : tsd;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
@@ -993,11 +1086,12 @@ __device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const Item
 // ======================================================================================
 // Persistent kernels
 // ======================================================================================
-// Workgroups per CU the persistent kernels are compiled for: at least two
-// (their rings and tiles fit in half the register file).  They are launched
-// with as many workgroups as are resident at once (three per CU for the lighter
-// vector-only kernels), at most MF_WG_PER_CU per CU where tiles are possible.
-template <int FMT> constexpr int FFN_WG_PER_CU = 2;
+// Workgroups per CU the persistent kernels are compiled for: three for the
+// vector-only kernels (BN = 0: the ring fits in a third of the register file,
+// and a third workgroup keeps more of the weight stream in flight), two where
+// matrix-core tiles are possible.  They are launched with as many workgroups
+// as are resident at once, at most MF_WG_PER_CU per CU where tiles are possible.
+template <int FMT, int BN> constexpr int FFN_WG_PER_CU = (BN == 0 && FMT != FMT_BF16) ? 3 : 2;
 constexpr int MF_WG_PER_CU = 2;
 
 // LDS of the persistent kernels: the matrix-core tiles (BN tokens wide) only
@@ -1032,7 +1126,7 @@ __device__ inline int mf_item(int i, int n, int C) {
 static_assert(MFMA_MIN > VEC_SMALL_T && MFMA_MIN_WIDE > VEC_SMALL_T,
               "batches with smaller vector items have no matrix-core tiles");
 template <int FMT, int BN, int VR>
-__global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_up_kernel(LayerArgs a) {
+__global__ __launch_bounds__(256, (FFN_WG_PER_CU<FMT, BN>)) void ffn_up_kernel(LayerArgs a) {
   __shared__ FfnKernelSmem<BN> sm;
   // matrix-core items: mf_up_chunks(BN) per tile; vector-path items: D_FF / VR per tile
   const int n_all = a.ctl[CTL_N_UP], n_mf = a.ctl[CTL_N_UP_MF];
@@ -1050,7 +1144,7 @@ __global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_up_kernel(LayerAr
 }
 
 template <int FMT, int BN, int VDR>
-__global__ __launch_bounds__(256, FFN_WG_PER_CU<FMT>) void ffn_down_kernel(LayerArgs a) {
+__global__ __launch_bounds__(256, (FFN_WG_PER_CU<FMT, BN>)) void ffn_down_kernel(LayerArgs a) {
   __shared__ FfnKernelSmem<BN> sm;
   const int n_all = a.ctl[CTL_N_DN], n_mf = a.ctl[CTL_N_DN_MF];
   if constexpr (BN > 0) {
@@ -1301,6 +1395,13 @@ __global__ __launch_bounds__(256, HEAD_WG_PER_CU) void head_kernel(HeadArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) st.v[i] = ld16<false>(a.x + (size_t)t * D_MODEL + 32 * cc + 8 * i);
     }
+    st.sc = 1.f;
+    if constexpr (OPER_F16<FMT>) {  // wave t holds token t's whole row: its scale
+      uint32_t m = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = max(m, bf16_absmax8(st.v[i]));
+      st.sc = pow2_scale(wave_max_u32(m) << 16);
+    }
     mv_stage_store<FMT, true>(st, sm, 0);
   }
   __syncthreads();
@@ -1308,6 +1409,7 @@ __global__ __launch_bounds__(256, HEAD_WG_PER_CU) void head_kernel(HeadArgs a) {
   // after a pair's reduction, lanes with bit 2 clear hold row group 2 p + bit 5
   // of token 2 * bit 4 + bit 3, row j
   const int my_t = ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
+  const float tsc = OPER_F16<FMT> ? ts * sm.isc[0][my_t] : ts;  // with the token's inverse scale
 #pragma unroll 1
   for (;;) {
     const int nc = c + G_;
@@ -1338,7 +1440,7 @@ __global__ __launch_bounds__(256, HEAD_WG_PER_CU) void head_kernel(HeadArgs a) {
           s4c[0] = s4n[0];
           s4c[1] = s4n[1];
         }
-        const float v = mv_reduce8(acc[0], acc[1]) * ts;
+        const float v = mv_reduce8(acc[0], acc[1]) * tsc;
         const int row = r0 + 8 * p + 4 * ((lane >> 5) & 1) + j, t = my_t;
         if ((lane & 4) == 0 && row < a.V && t < a.T) a.logits[(size_t)t * a.V + row] = v;
       }
@@ -1374,6 +1476,7 @@ template <int FMT> constexpr int HMF_D = FMT == FMT_BF16 ? 4 : 8;
 template <int NT> constexpr int HMF_ROWS = HMF_W<NT> * 16 * HMF_RB<NT>;  // rows per item
 template <int NT> struct HeadMfSmem {
   u32x4 x[MV_CHUNKS][16 * NT][4];
+  float isc[16 * NT];  // 4-bit formats: inverse activation scale per token of the pass
 };
 
 template <int FMT> __device__ inline f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
@@ -1438,12 +1541,20 @@ __global__ __launch_bounds__(64 * HMF_W<NT>, NT == 1 ? 2 : 1) void head_mf_kerne
 #pragma unroll
     for (int k = 0; k < TT / W; ++k) {
       const int tl = t0 + W * k;
+      float sc = 1.f;
+      if constexpr (OPER_F16<FMT>) {  // the wave holds the token's whole row: its scale
+        uint32_t m = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = max(m, bf16_absmax8(v[k][i]));
+        sc = pow2_scale(wave_max_u32(m) << 16);
+        if (blk == 0) sm.isc[tl] = pow2_inv(sc);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint32_t e[4] = {v[k][i][0], v[k][i][1], v[k][i][2], v[k][i][3]}, o[4];
         if constexpr (OPER_F16<FMT>) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) e[q] = bf16x2_to_f16x2(e[q]);
+          for (int q = 0; q < 4; ++q) e[q] = bf16x2_to_f16x2(e[q], sc);
         }
         if constexpr (FMT == FMT_Q4_1) q4_order(e[0], e[1], e[2], e[3], o);
         else {
@@ -1511,7 +1622,8 @@ __global__ __launch_bounds__(64 * HMF_W<NT>, NT == 1 ? 2 : 1) void head_mf_kerne
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int t = TT * tp + 16 * tt + 4 * g + j;
-          if (row < a.V && t < a.T) a.logits[(size_t)t * a.V + row] = acc[rb][tt][j] * ts;
+          const float tsc = OPER_F16<FMT> ? ts * sm.isc[16 * tt + 4 * g + j] : ts;
+          if (row < a.V && t < a.T) a.logits[(size_t)t * a.V + row] = acc[rb][tt][j] * tsc;
         }
     }
     if (!has_next) break;

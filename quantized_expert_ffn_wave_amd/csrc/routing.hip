@@ -150,30 +150,6 @@ __device__ inline float from_ordered(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-// Lane exchange for the wave-wide maximum: step m pairs lane i with i ^ m
-// (m = 4: with 7 - i inside groups of 8, which reaches the same set).
-template <int M> __device__ inline uint32_t xchg(uint32_t v) {
-  if constexpr (M == 32) {
-    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    return (threadIdx.x & 32) ? r[0] : r[1];
-  } else if constexpr (M == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return (threadIdx.x & 16) ? r[0] : r[1];
-  } else {
-    constexpr int ctrl = (M == 8) ? 0x128 : (M == 4) ? 0x141 : (M == 2) ? 0x4E : 0xB1;
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, ctrl, 0xF, 0xF, false);
-  }
-}
-__device__ inline uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, xchg<32>(v));
-  v = max(v, xchg<16>(v));
-  v = max(v, xchg<8>(v));
-  v = max(v, xchg<4>(v));
-  v = max(v, xchg<2>(v));
-  v = max(v, xchg<1>(v));
-  return v;
-}
-
 // One wave: logits of token t (sum of the KS partials in split order + bias),
 // the top k ids and their weights.
 template <int KS>
@@ -188,6 +164,21 @@ __device__ void topk_token(const LayerArgs& a, int t, int32_t* lds_ids) {
     const int e = min(lane + 64 * i, E - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) p[i][ks] = a.logit_part[((size_t)ks * T + t) * E + e];
+  }
+  // 4-bit formats: the token's activation scale for the fp16 operands of the
+  // expert products, from the largest |x| of its row (32 elements per lane)
+  if (a.fmt != FMT_BF16) {
+    const uint4* xr = reinterpret_cast<const uint4*>(a.x + (size_t)t * D_MODEL) + 4 * lane;
+    uint32_t mx = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = xr[i];
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) mx = max(mx, max(w4[q] & 0x7FFFu, (w4[q] >> 16) & 0x7FFFu));
+    }
+    mx = wave_max_u32(mx);
+    if (lane == 0) a.xsc[t] = pow2_scale(mx << 16);
   }
   uint32_t kk[4];
   float mx = -INFINITY;
@@ -418,6 +409,11 @@ __global__ __launch_bounds__(BK_THREADS) void chunk_hist_kernel(LayerArgs a) {
   for (int e = tid; e < E; e += BK_THREADS) cnt[e] = 0;
   __syncthreads();
   for (int s = t0 * K + tid; s < t1 * K; s += BK_THREADS) atomicAdd(&cnt[a.ids[s]], 1);
+  if (a.fmt != FMT_BF16) {  // this chunk's expert-output rows (slots, then shared), raised by gate/up
+    for (int s = t0 * K + tid; s < t1 * K; s += BK_THREADS) a.hmax[s] = 0u;
+    if (a.n_shared)
+      for (int t = t0 + tid; t < t1; t += BK_THREADS) a.hmax[a.S + t] = 0u;
+  }
   __syncthreads();
   int32_t* base = chunk_table(a) + (size_t)blockIdx.x * E;
   for (int e = tid; e < E; e += BK_THREADS) base[e] = cnt[e];
@@ -554,6 +550,8 @@ __device__ void route_small(const LayerArgs& a, RouteSmallSmem& sm) {
     for (int s = tid; s < S; s += nth) sm.ids[s] = a.ids[s];
   }
   for (int i = tid; i < E * W; i += nth) sm.mask[i] = 0u;
+  if (a.fmt != FMT_BF16)  // the gate/up kernel raises these with atomic max
+    for (int i = tid; i < S + a.n_shared * T; i += nth) a.hmax[i] = 0u;
   __syncthreads();
   // per-expert token masks (a token holds at most one slot of an expert)
   for (int s = tid; s < S; s += nth) {

@@ -34,7 +34,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "synth.c")
 _LIB = os.path.join(_HERE, "libsynth.so")
 
-TAG_X, TAG_ROUTER, TAG_BIAS, TAG_EXPERT, TAG_HEAD, TAG_ATTN = 1, 2, 3, 4, 5, 6
+TAG_X, TAG_ROUTER, TAG_BIAS, TAG_EXPERT, TAG_HEAD, TAG_ATTN, TAG_EDGE = 1, 2, 3, 4, 5, 6, 7
 HEAD_VOCAB = 151552  # synthetic vocabulary of the output-head workload
 SHARED_ID = 1_000_000
 FMT_CODE = {"bf16": 0, "q4_1": 1, "nvfp4": 2}
@@ -65,6 +65,7 @@ def lib():
         L.synth_normal_f32.argtypes = [u64, dbl, vp, i64]
         L.synth_normal_bf16.argtypes = [u64, dbl, vp, i64]
         L.synth_permutation.argtypes = [u64, vp, ctypes.c_int32]
+        L.synth_bytes.argtypes = [u64, vp, i64]
         L.synth_q4_1_encode.argtypes = [vp, i64, i64, vp, vp]
         L.synth_nvfp4_encode.argtypes = [vp, i64, i64, vp, vp, vp]
         L.synth_f32_to_bf16.argtypes = [vp, vp, i64]
@@ -98,6 +99,12 @@ def normal_f32(k: int, sigma: float, n: int) -> np.ndarray:
 def normal_bf16(k: int, sigma: float, n: int) -> np.ndarray:
     out = np.empty(n, np.uint16)
     lib().synth_normal_bf16(k, sigma, _p(out), n)
+    return out
+
+
+def uniform_bytes(k: int, n: int) -> np.ndarray:
+    out = np.empty(n, np.uint8)
+    lib().synth_bytes(k, _p(out), n)
     return out
 
 
@@ -270,6 +277,139 @@ def make_attn(B: int, cap: int, seed: int = 0, HQ: int = ATTN_HQ, HK: int = ATTN
                 v_cache=bf(4, B * cap * HK * D).reshape(B, cap, HK, D),
                 q_gain=encode_bf16(g[:D]), k_gain=encode_bf16(g[D:]),
                 sinks=normal_f32(key(seed, TAG_ATTN, 6), 1.0, HQ))
+
+
+# ---- patterned weights and activations for edge cases ------------------------------------
+# Codes and scales are written directly (uniform random bytes, or bit patterns),
+# not drawn as numbers and encoded, so that every stored code occurs.
+
+# NVFP4 scale bytes: the 8 consecutive E4M3 codes from each base together cover
+# every finite code of both signs (0x7F and 0xFF are NaN and never written).
+E4M3_BASES = [8 * i for i in range(15)] + [0x77] + [0x80 | (8 * i) for i in range(15)] + [0xF7]
+Q4_1_REGIMES = ("mixed", "subnormal", "large", "normal", "small_positive")
+
+
+def _e4m3_binade(b: int) -> int:
+    """floor(log2 |value|) of an E4M3 code from its bit fields (code 0: -9)."""
+    e, m = (b >> 3) & 15, b & 7
+    if e > 0:
+        return e - 7
+    return (int(m).bit_length() - 1) - 9 if m else -9
+
+
+def edge_nvfp4_matrix(q: QMat, i: int, k: int, base: int) -> None:
+    """Matrix i of an NVFP4 set: uniform random code bytes (all 16 E2M1 codes),
+    each 16-element block's scale a random one of the 8 codes base .. base + 7,
+    and a tensor scale that brings the weights to about 0.01-0.1 in size."""
+    rows, cols = q.rows, q.cols
+    q.codes[i] = uniform_bytes(key(k, TAG_EDGE, 0), rows * cols // 2).reshape(rows, cols // 2)
+    off = uniform_bytes(key(k, TAG_EDGE, 1), rows * cols // 16) & 7
+    q.scales[i] = (base + off).astype(np.uint8).reshape(rows, cols // 16)
+    q.tensor_scale[i] = np.float32(0.01 * 2.0 ** -_e4m3_binade(base))
+
+
+def edge_q4_1_matrix(q: QMat, i: int, k: int, regime: str) -> None:
+    """Matrix i of a q4_1 set: uniform random code bytes and per-block {d, m}
+    of a regime (fp16 values, rounded to nearest even by numpy):
+      mixed          each block one of: d ~ 0.004, m ~ -7.5 d (the usual shape);
+                     d = 0 with m = +-0.02 (constant blocks); d ~ 0.004 with
+                     m > 0; d = m = 0;
+      subnormal      d and m fp16 subnormals (random bit patterns), m of either sign;
+      large          d in [100, 1000), m ~ -7.5 d (|d q + m| < 2^14);
+      normal         d ~ 0.004 (0.5 .. 1.5), m ~ -7.5 d (0.8 .. 1.2);
+      small_positive d ~ 1e-4, m = 0 (all weights >= 0)."""
+    rows, cols = q.rows, q.cols
+    nb = rows * cols // 32
+    q.codes[i] = uniform_bytes(key(k, TAG_EDGE, 0), rows * cols // 2).reshape(rows, cols // 2)
+    u = uniform_bytes(key(k, TAG_EDGE, 2), 4 * nb).reshape(4, nb).astype(np.float64) / 255.0
+    sel = uniform_bytes(key(k, TAG_EDGE, 3), nb) & 3
+    if regime == "mixed":
+        d = 0.004 * (0.5 + u[0])
+        m = np.where(sel == 0, -7.5 * d * (0.8 + 0.4 * u[1]),
+                     np.where(sel == 1, 0.02 * (2 * u[1] - 1), np.where(sel == 2, 0.01 * u[1], 0.0)))
+        d = np.where((sel == 1) | (sel == 3), 0.0, d)
+        dm = np.stack([d.astype(np.float16).view(np.uint16), m.astype(np.float16).view(np.uint16)], -1)
+    elif regime == "subnormal":
+        db = uniform_bytes(key(k, TAG_EDGE, 4), 2 * nb).view(np.uint16) & 0x03FF
+        sign = (sel.astype(np.uint16) & 1) << 15
+        mb = (uniform_bytes(key(k, TAG_EDGE, 5), 2 * nb).view(np.uint16) & 0x03FF) | sign
+        dm = np.stack([np.maximum(db, 1).astype(np.uint16), mb.astype(np.uint16)], -1)
+    elif regime == "large":
+        d = 100.0 + 900.0 * u[0]
+        m = -7.5 * d * (0.9 + 0.2 * u[1])
+        dm = np.stack([d.astype(np.float16).view(np.uint16), m.astype(np.float16).view(np.uint16)], -1)
+    elif regime == "normal":
+        d = 0.004 * (0.5 + u[0])
+        m = -7.5 * d * (0.8 + 0.4 * u[1])
+        dm = np.stack([d.astype(np.float16).view(np.uint16), m.astype(np.float16).view(np.uint16)], -1)
+    elif regime == "small_positive":
+        d = 1e-4 * (0.5 + u[0])
+        dm = np.stack([d.astype(np.float16).view(np.uint16), np.zeros(nb, np.uint16)], -1)
+    else:
+        raise ValueError(regime)
+    q.scales[i] = dm.reshape(rows, cols // 32, 2)
+
+
+def make_edge_layer(fmt: str, seed: int = 0, E: int = 32, k: int = 2, n_shared: int = 1,
+                    regimes: tuple | None = None) -> Layer:
+    """A layer whose expert weights are patterned (N(0, 0.02) bf16 router, no
+    bias).  NVFP4: routed expert e uses scale base E4M3_BASES[e % 32], the
+    shared expert base 0x38.  q4_1: routed expert e uses regime
+    regimes[e % len(regimes)] (default Q4_1_REGIMES), the shared expert
+    'mixed'."""
+    assert fmt in ("nvfp4", "q4_1")
+    d, f = 2048, 512
+    regimes = regimes or Q4_1_REGIMES
+    router_w = normal_bf16(key(seed, TAG_ROUTER), 0.02, E * d).reshape(E, d)
+    gate, up, down = alloc_qmat(fmt, E, f, d), alloc_qmat(fmt, E, f, d), alloc_qmat(fmt, E, d, f)
+
+    def fill(qs, e, ek, sel):
+        for j, q in enumerate(qs):
+            kk = key(seed, TAG_EXPERT, ek, j)
+            if fmt == "nvfp4":
+                edge_nvfp4_matrix(q, e, kk, sel)
+            else:
+                edge_q4_1_matrix(q, e, kk, sel)
+
+    for e in range(E):
+        fill((gate, up, down), e, e, E4M3_BASES[e % 32] if fmt == "nvfp4" else regimes[e % len(regimes)])
+    L = Layer(fmt, d, E, k, f, n_shared, 1.0, 1, router_w, None, gate, up, down,
+              meta=dict(seed=seed, edge=True))
+    if n_shared:
+        L.sh_gate, L.sh_up, L.sh_down = alloc_qmat(fmt, 1, f, d), alloc_qmat(fmt, 1, f, d), alloc_qmat(fmt, 1, d, f)
+        fill((L.sh_gate, L.sh_up, L.sh_down), 0, SHARED_ID, 0x38 if fmt == "nvfp4" else "mixed")
+    return L
+
+
+def make_edge_head(V: int, fmt: str, seed: int = 0) -> QMat:
+    """Output-head matrix [V][2048] with patterned weights.  NVFP4: one tensor
+    scale for the matrix, so row v's blocks use scale codes
+    E4M3_BASES[v % 32] .. + 7 (rows differ in size by up to 2^17).  q4_1: row v
+    in regime Q4_1_REGIMES[v % 5] (rows drawn as 1-row matrices)."""
+    d = 2048
+    q = alloc_qmat(fmt, 1, V, d)
+    if fmt == "nvfp4":
+        q.codes[0] = uniform_bytes(key(seed, TAG_EDGE, 10), V * d // 2).reshape(V, d // 2)
+        off = uniform_bytes(key(seed, TAG_EDGE, 11), V * d // 16).reshape(V, d // 16) & 7
+        base = np.array([E4M3_BASES[v % 32] for v in range(V)], np.uint8)[:, None]
+        q.scales[0] = (base + off).astype(np.uint8)
+        q.tensor_scale[0] = np.float32(1.0)
+    else:
+        row = alloc_qmat(fmt, 1, 1, d)
+        for v in range(V):
+            edge_q4_1_matrix(row, 0, key(seed, TAG_EDGE, 12, v), Q4_1_REGIMES[v % 5])
+            q.codes[0, v] = row.codes[0, 0]
+            q.scales[0, v] = row.scales[0, 0]
+    return q
+
+
+def make_x_rows(T: int, sigmas, xseed: int = 0, d: int = 2048) -> np.ndarray:
+    """bf16 bits [T][d]: row t ~ bf16(fp32(N(0, sigma))) with sigma =
+    sigmas[t % len(sigmas)] (sigma 0: an all-zero row)."""
+    out = np.empty((T, d), np.uint16)
+    for t in range(T):
+        out[t] = normal_bf16(key(xseed, TAG_X, t + 1, 1), float(sigmas[t % len(sigmas)]), d)
+    return out
 
 
 def bf16_to_f32(b: np.ndarray) -> np.ndarray:

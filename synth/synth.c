@@ -176,6 +176,13 @@ void synth_normal_bf16(uint64_t key, double sigma, uint16_t* out, int64_t n) {
   if (n & 1) out[n - 1] = f32_to_bf16_rne((float)(sigma * normal_at(key, (uint64_t)(n - 1))));
 }
 
+/* out[i] = the low byte of output i of stream `key`: uniform bytes, for
+ * patterned weights that set every code and scale byte directly. */
+void synth_bytes(uint64_t key, uint8_t* out, int64_t n) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)synth_u64(key, (uint64_t)i);
+}
+
 /* Random permutation of 0..n-1 (Fisher-Yates with stream `key`). */
 void synth_permutation(uint64_t key, int32_t* perm, int32_t n) {
   for (int32_t i = 0; i < n; ++i) perm[i] = i;

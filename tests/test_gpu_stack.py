@@ -41,6 +41,7 @@ def run_stack(layers, x_bits, eps=1e-6):
         rec.append(dict(topk_ids=b["topk_ids"].cpu().numpy(), topk_w=b["topk_w"].cpu().numpy(),
                         logits=b["logits"].cpu().numpy(), counts=b["counts"].cpu().numpy(),
                         offsets=b["offsets"].cpu().numpy(), perm=b["perm"].cpu().numpy()[:T * layers[0].k],
+                        inv_perm=b["inv_perm"].cpu().numpy()[:T * layers[0].k],
                         x_in=bits_of(b["x_in"]), y_out=bits_of(b["y_out"])))
     for d in dls:
         d.close()

@@ -236,6 +236,20 @@ def test_rmsnorm_matches_numpy():
     assert np.abs(got - ref).max() > 0
 
 
+def test_rmsnorm_eps_inside_the_root_closed_forms():
+    """A constant row c has mean square c^2, so RMSNorm gives c / sqrt(c^2 + eps)
+    with eps inside the root: 1/sqrt(2) -> bf16 0.70703125 when c^2 = eps
+    (eps outside would give c / (c + eps) ~ 0.999 -> bf16 1.0); with eps = 0 it
+    is sign(c) exactly; a zero row stays zero."""
+    for c in (1e-3, -1e-3):
+        got = synth.bf16_to_f32(oracle.rmsnorm_bf16(np.full(2048, c), 1e-6))
+        assert np.all(got == np.float32(np.sign(c) * 0.70703125)), got[:4]
+    got = synth.bf16_to_f32(oracle.rmsnorm_bf16(np.full(2048, 3e-7), 0.0))
+    assert np.all(got == 1.0)
+    got = synth.bf16_to_f32(oracle.rmsnorm_bf16(np.zeros(2048), 1e-6))
+    assert np.all(got == 0.0)
+
+
 def test_stack_is_composition_of_layers():
     Ls = [small_layer(seed=s, E=8, k=2, zipf=0.8) for s in range(3)]
     x = synth.make_x(4, d=64, xseed=1)
