@@ -76,7 +76,7 @@ moe_status check_qmat(const moe_qmat& q, int fmt, const char* name) {
 }
 
 struct WsLayout {
-  size_t logit_part, logits, ids, w, counts, offsets, perm, inv_perm, tiles, ctl, h, y, xsc, hmax, total;
+  size_t logit_part, logits, ids, w, counts, offsets, perm, inv_perm, tiles, ctl, h, y, xsc, hslot, total;
   int max_tiles;
 };
 
@@ -106,7 +106,7 @@ WsLayout ws_layout(const moe_layer_desc& d, int T) {
   L.h = take((d.wfmt == MOE_W_BF16 ? sizeof(uint16_t) : sizeof(float)) * R * moe::D_FF);
   L.y = take(sizeof(float) * R * moe::D_MODEL);
   L.xsc = take(sizeof(float) * (size_t)T);
-  L.hmax = take(sizeof(uint32_t) * R);
+  L.hslot = take(sizeof(float) * moe::HSLOTS * R);
   L.total = o;
   return L;
 }
@@ -155,7 +155,7 @@ moe::LayerArgs make_args(const moe_layer* L, const void* x, int T, char* ws, con
   a.h = (void*)(ws + W.h);
   a.y = (float*)(ws + W.y);
   a.xsc = (float*)(ws + W.xsc);
-  a.hmax = (uint32_t*)(ws + W.hmax);
+  a.hslot = (float*)(ws + W.hslot);
   a.max_tiles = W.max_tiles;
   return a;
 }

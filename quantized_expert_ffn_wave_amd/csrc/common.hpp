@@ -12,6 +12,7 @@ constexpr int D_FF = 512;      // expert width (routed and shared)
 constexpr int MAX_E = 256;     // routed experts
 constexpr int MAX_K = 8;       // experts per token
 constexpr int SHARED_ID = MAX_E;  // expert id of the shared expert in the work lists
+constexpr int HSLOTS = D_FF / 16; // slots of a row's |h| maximum (16 columns each)
 
 enum Fmt : int { FMT_BF16 = 0, FMT_Q4_1 = 1, FMT_NVFP4 = 2 };
 
@@ -117,10 +118,11 @@ struct LayerArgs {
   void* h;                  // [S + n_shared*T][D_FF] SwiGLU output: fp32 for the 4-bit formats, bf16 bits else
   float* y;                 // [S + n_shared*T][D_MODEL] expert outputs
   // 4-bit formats only (their products run on fp16 operands): the power-of-two
-  // scale of each token's activations, and the bits of each expert-output
-  // row's largest |h| (fp32; raised with atomic max by gate/up, read by down)
+  // scale of each token's activations, and per expert-output row the largest
+  // |h| of each 16 columns' slot, written by the gate/up item that computes
+  // those columns (each slot exactly once per forward) and read by down
   float* xsc;               // [T]
-  uint32_t* hmax;           // [S + n_shared*T]
+  float* hslot;             // [S + n_shared*T][HSLOTS]
   int max_tiles;
   // combine targets
   uint16_t* out;            // bf16 [T][D_MODEL] layer output (single layer), or null

@@ -353,7 +353,8 @@ struct MvKS {
 struct MvSmem {
   uint32_t x[2][GV_GROUP * MV_TOKW];
   MvKS ks[2][MV_CHUNKS];
-  float isc[2][GV_GROUP];  // 4-bit formats: inverse activation scale per token
+  float isc[2][GV_GROUP];      // 4-bit formats: inverse activation scale per token
+  float hred[2][4][GV_GROUP];  // gate/up, 4-bit formats: each wave's largest |h| per token
 };
 
 // token t of a vector-path item, from its packed ids (no indexed array)
@@ -368,7 +369,8 @@ __device__ inline int item_token(const Item& item, int t) {
 // the expert-output row).
 struct MvStage {
   u32x4 v[8];  // 32 bf16 (x, or bf16 h) in v[0..3], or 32 fp32 (h of the 4-bit formats)
-  float sc;
+  float sc;    // gate/up: the token's scale
+  u32x2 hs;    // down, 4-bit formats: the row's |h| slots 2c, 2c + 1 (the scale follows from all 32)
 };
 
 template <int FMT, bool UP>
@@ -378,6 +380,7 @@ __device__ inline void mv_stage_load(const LayerArgs& a, const Item& item, const
 #pragma unroll
   for (int i = 0; i < 4; ++i) st.v[i] = u32x4{0u, 0u, 0u, 0u};
   st.sc = 1.f;
+  st.hs = u32x2{0u, 0u};
   if (t < GV_GROUP && t < it.cnt) {
     const int tok = UP ? item_token(item, t) : 0;
     const int row = UP ? 0 : row_of(a, it, t);
@@ -391,7 +394,10 @@ __device__ inline void mv_stage_load(const LayerArgs& a, const Item& item, const
 #pragma unroll
       for (int i = 0; i < 4; ++i) st.v[i] = ld16<false>(src + 8 * i);
     }
-    if constexpr (OPER_F16<FMT>) st.sc = UP ? a.xsc[tok] : pow2_scale(a.hmax[row]);
+    if constexpr (OPER_F16<FMT>) {
+      if (UP) st.sc = a.xsc[tok];
+      else st.hs = ld8<false>(a.hslot + (size_t)row * HSLOTS + 2 * c);
+    }
   }
 }
 
@@ -404,9 +410,15 @@ __device__ inline void mv_stage_store(const MvStage& st, MvSmem& sm, int buf) {
   const int t = threadIdx.x / NCH, c = threadIdx.x % NCH;
   if (t >= GV_GROUP) return;
   uint32_t n[16], o[16];
-  if constexpr (!UP && OPER_F16<FMT>) {  // fp32 h, scaled into fp16 pairs
+  float sc = st.sc;
+  if constexpr (!UP && OPER_F16<FMT>) {  // fp32 h, scaled into fp16 pairs by the row's largest |h|:
+    // the maximum over its 32 slots, 2 per thread, reduced over the token's 16 threads (one wave)
+    float m = fmaxf(__uint_as_float(st.hs[0]), __uint_as_float(st.hs[1]));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) n[i] = f32x2_to_f16x2(st.v[i >> 1][2 * (i & 1)], st.v[i >> 1][2 * (i & 1) + 1], st.sc);
+    for (int off = 1; off < NCH; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+    sc = pow2_scale(__float_as_uint(m));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) n[i] = f32x2_to_f16x2(st.v[i >> 1][2 * (i & 1)], st.v[i >> 1][2 * (i & 1) + 1], sc);
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -415,11 +427,11 @@ __device__ inline void mv_stage_store(const MvStage& st, MvSmem& sm, int buf) {
     }
     if constexpr (OPER_F16<FMT>) {  // bf16 x, scaled into fp16
 #pragma unroll
-      for (int i = 0; i < 16; ++i) n[i] = bf16x2_to_f16x2(n[i], st.sc);
+      for (int i = 0; i < 16; ++i) n[i] = bf16x2_to_f16x2(n[i], sc);
     }
   }
   if constexpr (OPER_F16<FMT>)
-    if (c == 0) sm.isc[buf][t] = pow2_inv(st.sc);
+    if (c == 0) sm.isc[buf][t] = pow2_inv(sc);
   if constexpr (FMT == FMT_Q4_1) {
     const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
     float se = 0.f, so = 0.f;  // sums of x' over the even and the odd elements
@@ -600,6 +612,22 @@ struct VecOrder {
   }
 };
 
+// The item's largest |h| per token (over its 4 waves' partial maxima in LDS,
+// after a barrier) into the |h| slots of the item's VR columns of each token's
+// expert-output row.  Items partition a row's columns, so every slot is written
+// once per forward and down can take the row's maximum without atomics.
+template <int VR>
+__device__ inline void vec_hslots(const LayerArgs& a, const Item& item, const ItemTok& it, const MvSmem& sm, int buf) {
+  static_assert(VR % 16 == 0, "an item covers whole slots");
+  const int t = threadIdx.x;
+  if (t < it.cnt) {
+    const float m = fmaxf(fmaxf(sm.hred[buf][0][t], sm.hred[buf][1][t]), fmaxf(sm.hred[buf][2][t], sm.hred[buf][3][t]));
+    float* dst = a.hslot + (size_t)row_of(a, it, t) * HSLOTS + item_chunk(item.head) * (VR / 16);
+#pragma unroll
+    for (int i = 0; i < VR / 16; ++i) dst[i] = m;
+  }
+}
+
 // gate/up + SwiGLU over the vector-path items base + c, c in [0, n), this
 // workgroup taking its items in VecOrder.
 template <int FMT, int VR>
@@ -712,20 +740,25 @@ __device__ void up_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem&
         }
       }
     }
-    if constexpr (OPER_F16<FMT>) {  // the rows' largest |h| (a quad holds 4 rows of one token) for down
+    if constexpr (OPER_F16<FMT>) {  // the wave's largest |h| per token (a quad holds 4 rows of one token)
       hm = fmaxf(hm, dpp_partner<1>(hm));
       hm = fmaxf(hm, dpp_partner<2>(hm));
-      if (writer && (lane & 3) == 0) atomicMax(a.hmax + hrow, __float_as_uint(hm));
+      if ((lane & 39) == 0) sm.hred[buf][wave][my_t] = hm;  // lanes 0, 8, 16, 24: tokens 0..3
     }
     if (!has_next) break;
     mv_stage_store<FMT, true>(st, sm, buf ^ 1);
     __syncthreads();
+    if constexpr (OPER_F16<FMT>) vec_hslots<VR>(a, item, it, sm, buf);
     buf ^= 1;
     c = nc;
     item = nitem;
     it = nit;
     w = nw;
     r0 = nr0;
+  }
+  if constexpr (OPER_F16<FMT>) {
+    __syncthreads();
+    vec_hslots<VR>(a, item, it, sm, buf);
   }
 }
 
@@ -849,7 +882,9 @@ template <int BN> struct FfnSmem {
   uint16_t x[2][BN * TS];  // K-chunks alternate between the two, so one barrier per chunk suffices
   int tok[BN];
   int row[BN];
-  float isc[BN];           // 4-bit formats: inverse activation scale per token column
+  float sc[BN];            // 4-bit formats: activation scale per token column (down: from |h|)
+  float isc[BN];           // and its inverse
+  float hred[4][BN];       // gate/up, 4-bit formats: each wave's largest |h| per token column
 };
 
 // Store 16 activation elements (natural-order pairs src[8]) into LDS in the
@@ -877,7 +912,9 @@ __device__ inline f32x16 mfma32(u32x4 av, u32x4 bv, f32x16 c) {
                                                  0, 0);
 }
 
-// UP: the activation scale is the token's (x); down: the expert-output row's (h).
+// UP: the activation scale is the token's (x); down: the expert-output row's
+// (h), from the maximum over the row's 32 |h| slots, read by 256 / BN threads
+// per token column and reduced over them.
 template <int FMT, bool UP, int BN>
 __device__ inline void mfma_tables(const LayerArgs& a, const ItemTok& it, FfnSmem<BN>& sm) {
   const int i = threadIdx.x;
@@ -887,8 +924,33 @@ __device__ inline void mfma_tables(const LayerArgs& a, const ItemTok& it, FfnSme
     const int row = (i < it.cnt) ? row_of(a, it, i) : -1;
     sm.tok[i] = tok;
     sm.row[i] = row;
-    if constexpr (OPER_F16<FMT>)
-      sm.isc[i] = (i < it.cnt) ? pow2_inv(UP ? a.xsc[tok] : pow2_scale(a.hmax[row])) : 1.f;
+    if (UP && OPER_F16<FMT>) {
+      const float sc = (i < it.cnt) ? a.xsc[tok] : 1.f;
+      sm.sc[i] = sc;
+      sm.isc[i] = pow2_inv(sc);
+    }
+  }
+  if constexpr (!UP && OPER_F16<FMT>) {
+    constexpr int P = 256 / BN, NS = HSLOTS / P;  // threads per token column, slots per thread
+    static_assert(P == 2 || P == 4, "2 or 4 threads per column: one DPP exchange each");
+    const int col = i / P, part = i % P;
+    float m = 0.f;
+    if (col < it.cnt) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(a.hslot + (size_t)row_of(a, it, col) * HSLOTS + NS * part);
+#pragma unroll
+      for (int k = 0; k < NS / 4; ++k) {
+        const u32x4 v = src[k];
+        m = fmaxf(fmaxf(m, fmaxf(__uint_as_float(v[0]), __uint_as_float(v[1]))),
+                  fmaxf(__uint_as_float(v[2]), __uint_as_float(v[3])));
+      }
+    }
+    m = fmaxf(m, dpp_partner<1>(m));
+    if (P == 4) m = fmaxf(m, dpp_partner<2>(m));
+    if (part == 0) {
+      const float sc = pow2_scale(__float_as_uint(m));
+      sm.sc[col] = sc;
+      sm.isc[col] = pow2_inv(sc);
+    }
   }
 }
 
@@ -1039,12 +1101,26 @@ __device__ void mfma_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int m
         }
       }
     }
-    if constexpr (OPER_F16<FMT>) {  // the row's largest |h| for down: both lane halves, one atomic per wave
+    if constexpr (OPER_F16<FMT>) {  // the wave's largest |h| per token column, both lane halves
       hm = fmaxf(hm, upper_half(hm));
-      if (h == 0 && hrow >= 0) atomicMax(a.hmax + hrow, __float_as_uint(hm));
+      if (h == 0) sm.hred[wave][32 * tt + c] = hm;
     }
   }
   __syncthreads();  // tables and tiles are reused by the next item
+  if constexpr (OPER_F16<FMT>) {
+    // the item's largest |h| per token into the |h| slots of its D_FF / UC
+    // columns (items partition a row's columns: every slot once per forward)
+    constexpr int NSL = D_FF / mf_up_chunks(BN) / 16;  // slots of the item's columns
+    static_assert(NSL == 4 * RB, "4 waves x 16 RB row pairs");
+    const int i = threadIdx.x;
+    if (i < it.cnt) {
+      const float m = fmaxf(fmaxf(sm.hred[0][i], sm.hred[1][i]), fmaxf(sm.hred[2][i], sm.hred[3][i]));
+      float* dst = a.hslot + (size_t)sm.row[i] * HSLOTS + n0 / 16;
+#pragma unroll
+      for (int k = 0; k < NSL / 4; ++k) *reinterpret_cast<float4*>(dst + 4 * k) = make_float4(m, m, m, m);
+    }
+    __syncthreads();  // the LDS is taken over by the next item (or the vector path)
+  }
 }
 
 // down item: DN_ROWS rows (r0 ..) x BN tokens, K = 512.
@@ -1060,7 +1136,7 @@ __device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const Item
   const int hrow_x = sm.row[min(tid / MF_XT<BN>, it.cnt - 1)];
   const HElem<FMT>* xsrc =
       static_cast<const HElem<FMT>*>(a.h) + (size_t)hrow_x * D_FF + MF_XK<BN> * (tid % MF_XT<BN>);
-  const float xscale = OPER_F16<FMT> ? pow2_scale(a.hmax[hrow_x]) : 1.f;
+  const float xscale = OPER_F16<FMT> ? sm.sc[min(tid / MF_XT<BN>, it.cnt - 1)] : 1.f;
   f32x16 acc[2][MF_TT<BN>] = {};
   mf_kloop<FMT, BN, 2, MF_NS_DN<FMT, BN>, OPER_F16<FMT>>(acc, sm, q, wrow, xsrc, xscale, D_FF);
   const float tsd = (FMT == FMT_NVFP4) ? D.ts[mat] : 1.f;

@@ -409,11 +409,6 @@ __global__ __launch_bounds__(BK_THREADS) void chunk_hist_kernel(LayerArgs a) {
   for (int e = tid; e < E; e += BK_THREADS) cnt[e] = 0;
   __syncthreads();
   for (int s = t0 * K + tid; s < t1 * K; s += BK_THREADS) atomicAdd(&cnt[a.ids[s]], 1);
-  if (a.fmt != FMT_BF16) {  // this chunk's expert-output rows (slots, then shared), raised by gate/up
-    for (int s = t0 * K + tid; s < t1 * K; s += BK_THREADS) a.hmax[s] = 0u;
-    if (a.n_shared)
-      for (int t = t0 + tid; t < t1; t += BK_THREADS) a.hmax[a.S + t] = 0u;
-  }
   __syncthreads();
   int32_t* base = chunk_table(a) + (size_t)blockIdx.x * E;
   for (int e = tid; e < E; e += BK_THREADS) base[e] = cnt[e];
@@ -550,8 +545,6 @@ __device__ void route_small(const LayerArgs& a, RouteSmallSmem& sm) {
     for (int s = tid; s < S; s += nth) sm.ids[s] = a.ids[s];
   }
   for (int i = tid; i < E * W; i += nth) sm.mask[i] = 0u;
-  if (a.fmt != FMT_BF16)  // the gate/up kernel raises these with atomic max
-    for (int i = tid; i < S + a.n_shared * T; i += nth) a.hmax[i] = 0u;
   __syncthreads();
   // per-expert token masks (a token holds at most one slot of an expert)
   for (int s = tid; s < S; s += nth) {
