@@ -177,6 +177,29 @@ moe_status moe_layer_forward_staged(const moe_layer* layer, const void* x, int32
                                     const moe_route_out* route, void* workspace, size_t workspace_bytes,
                                     void* stream, void* const* events, int32_t n_events);
 
+/* moe_layer_forward without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * workspace is a static array of MOE_NOALLOC_MAX_WORKSPACE bytes in the
+ * library's code object, one copy per GPU, held until the process ends; its
+ * address is taken once per device, on the first call with that device
+ * current.  That bound covers every decode batch of up to 256 tokens of the
+ * layers this build supports (moe_layer_workspace_size says what a forward
+ * needs).
+ *   layer, x, T, y, route, stream: as for moe_layer_forward; the layer's
+ *            device must be current.
+ * Errors: MOE_ERR_WORKSPACE when the forward of T tokens needs more than
+ * MOE_NOALLOC_MAX_WORKSPACE bytes; MOE_ERR_INVALID_ARG for another current
+ * device or the arguments moe_layer_forward rejects; MOE_ERR_HIP if the
+ * scratch address cannot be taken.  All are returned before anything is
+ * enqueued.  Every call on one GPU uses the same scratch and leaves its
+ * contents there (nothing in it needs clearing: each forward writes what it
+ * reads): calls whose execution overlaps on one GPU -- on two streams, or from
+ * two threads -- race and give undefined results; order them on one stream. */
+#define MOE_NOALLOC_MAX_WORKSPACE (32u << 20)
+moe_status moe_layer_forward_noalloc(const moe_layer* layer, const void* x, int32_t T, void* y,
+                                     const moe_route_out* route, void* stream);
+
 /* Workspace bytes for moe_stack_forward over these layers at T tokens. */
 moe_status moe_stack_workspace_size(const moe_layer* const* layers, int32_t n_layers, int32_t T, size_t* bytes);
 

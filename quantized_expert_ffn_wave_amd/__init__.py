@@ -21,7 +21,8 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
                 4: "MOE_ERR_HIP"}
 WFMT = {"bf16": 0, "q4_1": 1, "nvfp4": 2}
 EXPORTED = ["moe_layer_create", "moe_layer_destroy", "moe_layer_workspace_size", "moe_desc_workspace_size",
-            "moe_layer_forward", "moe_layer_forward_staged", "moe_stack_workspace_size", "moe_stack_forward",
+            "moe_layer_forward", "moe_layer_forward_staged", "moe_layer_forward_noalloc",
+            "moe_stack_workspace_size", "moe_stack_forward",
             "moe_head_forward", "moe_attn_workspace_size", "moe_attn_decode", "moe_stream_read", "moe_last_error",
             "moe_version"]
 ATTN_HQ, ATTN_HK, ATTN_D = 32, 4, 128
@@ -84,6 +85,8 @@ _lib.moe_layer_forward.restype = ctypes.c_int
 _lib.moe_layer_forward_staged.argtypes = [_vp, _vp, _i32, _vp, ctypes.POINTER(moe_route_out), _vp, _sz, _vp,
                                           ctypes.POINTER(_vp), _i32]
 _lib.moe_layer_forward_staged.restype = ctypes.c_int
+_lib.moe_layer_forward_noalloc.argtypes = [_vp, _vp, _i32, _vp, ctypes.POINTER(moe_route_out), _vp]
+_lib.moe_layer_forward_noalloc.restype = ctypes.c_int
 _lib.moe_stack_workspace_size.argtypes = [ctypes.POINTER(_vp), _i32, _i32, ctypes.POINTER(_sz)]
 _lib.moe_stack_workspace_size.restype = ctypes.c_int
 _lib.moe_stack_forward.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _i32, ctypes.c_float,
@@ -162,6 +165,15 @@ def moe_layer_forward_staged(handle: int, x_ptr: int, T: int, y_ptr: int, route:
     arr = (_vp * len(events))(*events)
     _check(_lib.moe_layer_forward_staged(handle, x_ptr, T, y_ptr, ctypes.byref(route) if route is not None else None,
                                          ws_ptr, ws_bytes, stream, arr, len(events)), "moe_layer_forward_staged")
+
+
+def moe_layer_forward_noalloc(handle: int, x_ptr: int, T: int, y_ptr: int, route: moe_route_out | None,
+                              stream: int) -> None:
+    _check(_lib.moe_layer_forward_noalloc(handle, x_ptr, T, y_ptr, ctypes.byref(route) if route is not None else None,
+                                          stream), "moe_layer_forward_noalloc")
+
+
+NOALLOC_MAX_WORKSPACE = 32 << 20
 
 
 def moe_stack_workspace_size(handles, T: int) -> int:

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "common.hpp"
@@ -328,6 +329,54 @@ static moe_status layer_forward_impl(const moe_layer* L, const void* x, int32_t 
 moe_status moe_layer_forward(const moe_layer* L, const void* x, int32_t T, void* y, const moe_route_out* route,
                              void* ws, size_t ws_bytes, void* stream) {
   return layer_forward_impl(L, x, T, y, route, ws, ws_bytes, stream, nullptr);
+}
+
+// Workspace of moe_layer_forward_noalloc: one copy per GPU, held by the loaded
+// code object until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: kernels and copies get the device address
+// that hipGetSymbolAddress returns for the current device (scratch_ptr).
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_MAX_WORKSPACE];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once taken
+
+// The device address of `scratch` on device dev, which must be current.
+moe_status scratch_ptr(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_layer_forward_noalloc(const moe_layer* L, const void* x, int32_t T, void* y,
+                                     const moe_route_out* route, void* stream) {
+  if (!L) return fail(MOE_ERR_INVALID_ARG, "layer is NULL");
+  if (T < 0 || T > L->desc.max_tokens)
+    return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, max_tokens=%d]", T, L->desc.max_tokens);
+  if (T == 0) return MOE_OK;
+  const size_t need = ws_layout(L->desc, T).total;
+  if (need > (size_t)MOE_NOALLOC_MAX_WORKSPACE)
+    return fail(MOE_ERR_WORKSPACE, "T=%d needs %zu workspace bytes; the static scratch holds %zu", T, need,
+                (size_t)MOE_NOALLOC_MAX_WORKSPACE);
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != L->device)
+    return fail(MOE_ERR_INVALID_ARG, "device %d is current; the layer was created on device %d", dev, L->device);
+  void* ws = nullptr;
+  const moe_status st = scratch_ptr(dev, &ws);
+  if (st != MOE_OK) return st;
+  return layer_forward_impl(L, x, T, y, route, ws, (size_t)MOE_NOALLOC_MAX_WORKSPACE, stream, nullptr);
 }
 
 moe_status moe_layer_forward_staged(const moe_layer* L, const void* x, int32_t T, void* y,
