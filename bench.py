@@ -799,6 +799,34 @@ def bench_attn(args, moe, synth, torch, np):
     }
 
 
+def bench_mfma_rate(args, moe, torch):
+    """Attainable matrix-core rate per instruction kind (moe_mfma_rate): the
+    reference against which the tile path's matrix-core utilisation is read."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(256, dtype=torch.float32, device="cuda")
+    stream = moe.current_stream()
+    grid, iters, reps = 2 * n_cu, 4096, max(3, args.steps // 20)
+    rates = {}
+    for kind, (name, flop) in moe.MFMA_KINDS.items():
+        moe.moe_mfma_rate(kind, iters, grid, sink.data_ptr(), stream)  # warm-up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            moe.moe_mfma_rate(kind, iters, grid, sink.data_ptr(), stream)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tflops = grid * 4 * iters * 4 * flop / (ms * 1e-3) / 1e12
+        rates[name] = {"tflops": round(tflops, 1), "ms_per_launch": round(ms, 4)}
+        log(f"{name}: {tflops:.1f} TFLOP/s ({ms:.3f} ms per launch)")
+    f16 = rates[moe.MFMA_KINDS[0][0]]["tflops"]
+    for v in rates.values():
+        v["vs_f16"] = round(v["tflops"] / f16, 3)
+    return {"metric": "matrix-core instruction rate (measurement helper, not the layer)", "unit": "TFLOP/s",
+            "workgroups": grid, "waves_per_simd": 2, "instructions_per_wave": 4 * iters, "rates": rates,
+            "published_dense_peaks_tflops": {"f16/bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -812,6 +840,8 @@ def main() -> int:
     ap.add_argument("--no-stream-reference", action="store_true", help="skip the 4 GiB streaming-read reference")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--mfma-rate", action="store_true",
+                    help="only time the matrix-core rate helper per instruction kind (f16, bf16, fp8, scaled fp4)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -828,7 +858,9 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
-    if args.workload in synth.HEAD_CONFIGS:
+    if args.mfma_rate:
+        out = bench_mfma_rate(args, moe, torch)
+    elif args.workload in synth.HEAD_CONFIGS:
         out = bench_head(args, moe, synth, torch, np)
     elif args.workload in synth.ATTN_CONFIGS:
         out = bench_attn(args, moe, synth, torch, np)

@@ -242,6 +242,22 @@ moe_status moe_head_forward(const void* x, int32_t T, const moe_qmat* w, int32_t
  * Invalid arguments return MOE_ERR_INVALID_ARG before anything is enqueued. */
 moe_status moe_stream_read(const void* src, size_t bytes, void* sink, int32_t grid, void* stream);
 
+/* Measurement helper, not part of the layer: grid workgroups of 256 threads
+ * issue only matrix-core instructions of one kind, iters x 4 per wave in four
+ * independent accumulator chains over operands held in registers:
+ *   kind 0: v_mfma_f32_32x32x16_f16   (32768 flop each)
+ *   kind 1: v_mfma_f32_32x32x16_bf16  (32768 flop each)
+ *   kind 2: v_mfma_f32_32x32x16_fp8_fp8, E4M3 operands (32768 flop each)
+ *   kind 3: v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 E2M1 operands and unit
+ *           block scales (131072 flop each)
+ * Timed by the caller, it gives the attainable rate of each kind, against which
+ * the tile path's matrix-core utilisation is read; the FP4-class instruction is
+ * the one the review's NVFP4 files ("What actually shipped") invite.  sink:
+ * caller-owned device memory of 256 floats that the kernel overwrites (values
+ * meaningless).  Bad arguments return MOE_ERR_INVALID_ARG before anything is
+ * enqueued. */
+moe_status moe_mfma_rate(int32_t kind, int32_t iters, int32_t grid, float* sink, void* stream);
+
 /* ---- decode attention ----------------------------------------------------------
  * One new token per sequence through one attention layer of the layout in the
  * review's section "The architecture is an argument about memory bandwidth":

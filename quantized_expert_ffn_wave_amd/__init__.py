@@ -23,7 +23,8 @@ WFMT = {"bf16": 0, "q4_1": 1, "nvfp4": 2}
 EXPORTED = ["moe_layer_create", "moe_layer_destroy", "moe_layer_workspace_size", "moe_desc_workspace_size",
             "moe_layer_forward", "moe_layer_forward_staged", "moe_layer_forward_noalloc",
             "moe_stack_workspace_size", "moe_stack_forward",
-            "moe_head_forward", "moe_attn_workspace_size", "moe_attn_decode", "moe_stream_read", "moe_last_error",
+            "moe_head_forward", "moe_attn_workspace_size", "moe_attn_decode", "moe_stream_read", "moe_mfma_rate",
+            "moe_last_error",
             "moe_version"]
 ATTN_HQ, ATTN_HK, ATTN_D = 32, 4, 128
 HEAD_MAX_VOCAB = 1048576
@@ -101,6 +102,8 @@ _lib.moe_attn_decode.argtypes = [ctypes.POINTER(moe_attn_desc), _i32, _i32, _vp,
 _lib.moe_attn_decode.restype = ctypes.c_int
 _lib.moe_stream_read.argtypes = [_vp, _sz, _vp, _i32, _vp]
 _lib.moe_stream_read.restype = ctypes.c_int
+_lib.moe_mfma_rate.argtypes = [_i32, _i32, _i32, _vp, _vp]
+_lib.moe_mfma_rate.restype = ctypes.c_int
 _lib.moe_last_error.restype = ctypes.c_char_p
 _lib.moe_version.restype = ctypes.c_char_p
 
@@ -202,6 +205,14 @@ def moe_head_forward(x_ptr: int, T: int, w: moe_qmat, wfmt: int, vocab: int, d_m
 
 def moe_stream_read(src_ptr: int, nbytes: int, sink_ptr: int, grid: int, stream: int) -> None:
     _check(_lib.moe_stream_read(src_ptr, nbytes, sink_ptr, grid, stream), "moe_stream_read")
+
+
+MFMA_KINDS = {0: ("v_mfma_f32_32x32x16_f16", 32768), 1: ("v_mfma_f32_32x32x16_bf16", 32768),
+              2: ("v_mfma_f32_32x32x16_fp8_fp8", 32768), 3: ("v_mfma_scale_f32_32x32x64_f8f6f4 (fp4)", 131072)}
+
+
+def moe_mfma_rate(kind: int, iters: int, grid: int, sink_ptr: int, stream: int) -> None:
+    _check(_lib.moe_mfma_rate(kind, iters, grid, sink_ptr, stream), "moe_mfma_rate")
 
 
 # ---- torch-level helpers -----------------------------------------------------------------

@@ -487,6 +487,16 @@ moe_status moe_stream_read(const void* src, size_t bytes, void* sink, int32_t gr
   return MOE_OK;
 }
 
+moe_status moe_mfma_rate(int32_t kind, int32_t iters, int32_t grid, float* sink, void* stream) {
+  if (kind < 0 || kind > 3) return fail(MOE_ERR_INVALID_ARG, "kind must be 0..3, got %d", kind);
+  if (iters < 1 || iters > (1 << 24)) return fail(MOE_ERR_INVALID_ARG, "iters must be in [1, 2^24], got %d", iters);
+  if (grid < 1 || grid > 65536) return fail(MOE_ERR_INVALID_ARG, "grid must be in [1, 65536], got %d", grid);
+  if (!sink || !aligned(sink, 4)) return fail(MOE_ERR_INVALID_ARG, "sink must be a 4 B aligned device pointer");
+  const hipError_t e = moe::launch_mfma_rate(kind, iters, grid, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "matrix-core rate launch");
+  return MOE_OK;
+}
+
 const char* moe_last_error(void) { return g_err.c_str(); }
 
 const char* moe_version(void) { return "moe_ffn gfx950 0.1"; }

@@ -207,4 +207,7 @@ hipError_t launch_stack_init(const uint16_t* x, float* r, uint16_t* xn, int T, f
 hipError_t launch_head(const HeadArgs& a, int n_cu, hipStream_t s);
 // plain streaming read of bytes (a multiple of 16) from src on grid workgroups
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int grid, hipStream_t s);
+// matrix-core instructions of one kind (0 f16, 1 bf16, 2 fp8, 3 scaled fp4) only:
+// iters x 4 per wave on grid workgroups of 256 threads
+hipError_t launch_mfma_rate(int kind, int iters, int grid, float* sink, hipStream_t s);
 }  // namespace moe

@@ -364,13 +364,12 @@ __device__ inline int item_token(const Item& item, int t) {
 }
 
 // One thread per (token, chunk): the chunk's 32 activation elements and, for
-// the 4-bit formats, the token's activation scale (gate/up: from the top-k's
-// per-token maximum of x; down: from the gate/up kernel's maximum of |h| on
-// the expert-output row).
+// down with the 4-bit formats, two of the row's |h| slots.  The activation
+// scale follows at the store: gate/up from the row's largest |x| (a token's 64
+// chunks are one wave), down from the largest of the row's 32 |h| slots.
 struct MvStage {
   u32x4 v[8];  // 32 bf16 (x, or bf16 h) in v[0..3], or 32 fp32 (h of the 4-bit formats)
-  float sc;    // gate/up: the token's scale
-  u32x2 hs;    // down, 4-bit formats: the row's |h| slots 2c, 2c + 1 (the scale follows from all 32)
+  u32x2 hs;    // down, 4-bit formats: the row's |h| slots 2c, 2c + 1
 };
 
 template <int FMT, bool UP>
@@ -379,7 +378,6 @@ __device__ inline void mv_stage_load(const LayerArgs& a, const Item& item, const
   const int t = threadIdx.x / NCH, c = threadIdx.x % NCH;
 #pragma unroll
   for (int i = 0; i < 4; ++i) st.v[i] = u32x4{0u, 0u, 0u, 0u};
-  st.sc = 1.f;
   st.hs = u32x2{0u, 0u};
   if (t < GV_GROUP && t < it.cnt) {
     const int tok = UP ? item_token(item, t) : 0;
@@ -394,10 +392,7 @@ __device__ inline void mv_stage_load(const LayerArgs& a, const Item& item, const
 #pragma unroll
       for (int i = 0; i < 4; ++i) st.v[i] = ld16<false>(src + 8 * i);
     }
-    if constexpr (OPER_F16<FMT>) {
-      if (UP) st.sc = a.xsc[tok];
-      else st.hs = ld8<false>(a.hslot + (size_t)row * HSLOTS + 2 * c);
-    }
+    if constexpr (!UP && OPER_F16<FMT>) st.hs = ld8<false>(a.hslot + (size_t)row * HSLOTS + 2 * c);
   }
 }
 
@@ -410,7 +405,7 @@ __device__ inline void mv_stage_store(const MvStage& st, MvSmem& sm, int buf) {
   const int t = threadIdx.x / NCH, c = threadIdx.x % NCH;
   if (t >= GV_GROUP) return;
   uint32_t n[16], o[16];
-  float sc = st.sc;
+  float sc = 1.f;
   if constexpr (!UP && OPER_F16<FMT>) {  // fp32 h, scaled into fp16 pairs by the row's largest |h|:
     // the maximum over its 32 slots, 2 per thread, reduced over the token's 16 threads (one wave)
     float m = fmaxf(__uint_as_float(st.hs[0]), __uint_as_float(st.hs[1]));
@@ -425,7 +420,12 @@ __device__ inline void mv_stage_store(const MvStage& st, MvSmem& sm, int buf) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) n[4 * i + e] = st.v[i][e];
     }
-    if constexpr (OPER_F16<FMT>) {  // bf16 x, scaled into fp16
+    if constexpr (OPER_F16<FMT>) {  // bf16 x, scaled into fp16 by its row's largest |x| (the wave's)
+      static_assert(!UP || NCH == 64, "a token's chunks fill one wave");
+      uint32_t m = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = max(m, bf16_absmax8(st.v[i]));
+      sc = pow2_scale(wave_max_u32(m) << 16);
 #pragma unroll
       for (int i = 0; i < 16; ++i) n[i] = bf16x2_to_f16x2(n[i], sc);
     }
@@ -699,8 +699,8 @@ __device__ void up_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem&
     }
     const bool writer = (lane & 36) == 0 && my_t < it.cnt;
     const int hrow = row_of(a, it, 0) + my_t;
-    HElem<FMT>* hdst = static_cast<HElem<FMT>*>(a.h) + (size_t)hrow * D_FF + item_chunk(item.head) * VR +
-                       wave * (VR / 4) + j;
+    // the lane's h elements, as a 32-bit offset from the uniform base (one VGPR, not a 64-bit pointer)
+    const uint32_t hoff = (uint32_t)(hrow * D_FF + item_chunk(item.head) * VR + wave * (VR / 4) + j);
     const float isc = OPER_F16<FMT> ? sm.isc[buf][my_t] : 1.f;  // undoes the token's activation scale
     float hm = 0.f;                                             // largest |h| this lane writes
     f32x4 acc[2] = {}, negK = {}, S = {};
@@ -734,8 +734,8 @@ __device__ void up_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem&
         const float up = upper_half(v);
         const float hv = silu_mul(v, up);
         if (writer) {
-          if constexpr (OPER_F16<FMT>) hdst[4 * g] = hv;
-          else hdst[4 * g] = f32_to_bf16(hv);
+          if constexpr (OPER_F16<FMT>) static_cast<float*>(a.h)[hoff + 4 * g] = hv;
+          else static_cast<uint16_t*>(a.h)[hoff + 4 * g] = f32_to_bf16(hv);
           hm = fmaxf(hm, fabsf(hv));
         }
       }
@@ -815,8 +815,9 @@ __device__ void down_stream(const LayerArgs& a, int base, int n, int n_mf, MvSme
     }
     const bool writer = (lane & 4) == 0 && my_t < it.cnt;
     const float isc = OPER_F16<FMT> ? sm.isc[buf][my_t] : 1.f;  // undoes the row's h scale
-    float* ydst = a.y + (size_t)(row_of(a, it, 0) + my_t) * D_MODEL + item_chunk(item.head) * VDR + wave * (VDR / 4) +
-                  4 * ((lane >> 5) & 1) + j;
+    // the lane's y elements, as a 32-bit offset from the uniform base
+    const uint32_t yoff = (uint32_t)((row_of(a, it, 0) + my_t) * D_MODEL + item_chunk(item.head) * VDR +
+                                     wave * (VDR / 4) + 4 * ((lane >> 5) & 1) + j);
     uint32_t xq[16];
     f32x4 negK = {}, S = {};
     mv_acts<FMT>(sm, buf, b, j, xq, negK, S);
@@ -832,7 +833,7 @@ __device__ void down_stream(const LayerArgs& a, int base, int n, int n_mf, MvSme
         float v = mv_reduce8(acc[0], acc[1]);
         if (FMT == FMT_NVFP4) v *= w.tsg;
         if constexpr (OPER_F16<FMT>) v *= isc;
-        if (writer) ydst[4 * (u - 1)] = v;
+        if (writer) a.y[yoff + 4 * (u - 1)] = v;
       }
     }
     if (!has_next) break;
@@ -1471,14 +1472,7 @@ __global__ __launch_bounds__(256, HEAD_WG_PER_CU) void head_kernel(HeadArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) st.v[i] = ld16<false>(a.x + (size_t)t * D_MODEL + 32 * cc + 8 * i);
     }
-    st.sc = 1.f;
-    if constexpr (OPER_F16<FMT>) {  // wave t holds token t's whole row: its scale
-      uint32_t m = 0u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) m = max(m, bf16_absmax8(st.v[i]));
-      st.sc = pow2_scale(wave_max_u32(m) << 16);
-    }
-    mv_stage_store<FMT, true>(st, sm, 0);
+    mv_stage_store<FMT, true>(st, sm, 0);  // wave t holds token t's whole row: its scale too
   }
   __syncthreads();
   const float ts = (FMT == FMT_NVFP4) ? a.w.ts[0] : 1.f;

@@ -33,3 +33,14 @@ def test_stream_read_rejects_bad_sizes_on_the_device():
         moe.moe_stream_read(src.data_ptr(), 4095, sink.data_ptr(), 0, moe.current_stream())
     with pytest.raises(moe.MoeError):
         moe.moe_stream_read(src.data_ptr() + 8, 4080, sink.data_ptr(), 0, moe.current_stream())
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2, 3])
+def test_mfma_rate_helper_runs(kind):
+    """The matrix-core rate helper launches each instruction kind and writes its sink."""
+    sink = torch.full((256,), float("nan"), dtype=torch.float32, device="cuda")
+    moe.moe_mfma_rate(kind, 16, 8, sink.data_ptr(), moe.current_stream())
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(sink).all())
+    with pytest.raises(moe.MoeError):
+        moe.moe_mfma_rate(4, 16, 8, sink.data_ptr(), moe.current_stream())
