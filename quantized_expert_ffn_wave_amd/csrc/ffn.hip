@@ -1035,6 +1035,10 @@ __device__ inline void mf_kloop(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<BN>& sm, c
   for (int ck0 = 0; ck0 < nc; ck0 += NS) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
+      // Keep each chunk's work in its place: left free, the scheduler hoists the
+      // weight decodes of all NS chunks to the top of the unrolled body, and
+      // their wait drains every load in flight (the prefetch then buys nothing).
+      __builtin_amdgcn_sched_barrier(0);
       stage(st[j], sm.x[j & 1]);
       fetch(st[(j + NS - 1) % NS], ck0 + j + NS - 1);
       __syncthreads();
