@@ -207,8 +207,8 @@ def bench_layer(args, moe, synth, torch, np):
     def step(i, events=None, on=None):
         dl = dls[i % NL]
         if events is None:
-            moe.moe_layer_forward(dl.handle, x.data_ptr(), T, y.data_ptr(), None, ws.data_ptr(), ws.numel(),
-                                  stream if on is None else on)
+            fwd = moe.moe_layer_forward_persistent if args.persistent else moe.moe_layer_forward
+            fwd(dl.handle, x.data_ptr(), T, y.data_ptr(), None, ws.data_ptr(), ws.numel(), stream if on is None else on)
         else:
             moe.moe_layer_forward_staged(dl.handle, x.data_ptr(), T, y.data_ptr(), None, ws.data_ptr(), ws.numel(),
                                          stream, events)
@@ -291,9 +291,11 @@ def bench_layer(args, moe, synth, torch, np):
             tb = [touched_bytes(dl, xt, ws_all) for dl in dls]
             g = torch.cuda.CUDAGraph()  # every instance in turn, as for the timed steps above
             with torch.cuda.graph(g):
+                fwd = (moe.moe_layer_forward_persistent if args.persistent and t <= moe.PERSISTENT_MAX_T
+                       else moe.moe_layer_forward)
                 for dl in dls:
-                    moe.moe_layer_forward(dl.handle, xt.data_ptr(), t, yt.data_ptr(), None, ws_all.data_ptr(),
-                                          ws_all.numel(), moe.current_stream())
+                    fwd(dl.handle, xt.data_ptr(), t, yt.data_ptr(), None, ws_all.data_ptr(), ws_all.numel(),
+                        moe.current_stream())
             for _ in range(max(1, args.warmup // NL)):
                 g.replay()
             torch.cuda.synchronize()
@@ -359,7 +361,7 @@ def bench_layer(args, moe, synth, torch, np):
                    "top_k": K, "shared_experts": 1, "d_expert": 512, "weights": fmt, "router_bias_zipf": cfg["zipf"],
                    "layer_instances": NL, "touched_experts_mean": round(float(np.mean(touched)), 1),
                    "expert_weight_bytes_per_step": int(w_bytes), "router_bytes_per_step": router_b,
-                   "launch": "hip_graph_replay" if graph_ms is not None else "plain",
+                   "launch": ("hip_graph_replay" if graph_ms is not None else "plain") + (", persistent" if args.persistent else ""),
                    "plain_launch_ms_per_step": round(ms, 5), "graph_replay_ms": spread, "stage_ms": stage_means},
         "roofline": {"bound": "hbm", "kernel": "ffn_up_kernel (gate/up + SwiGLU)",
                      "achieved": round(up_achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -406,7 +408,8 @@ def bench_stack(args, moe, synth, torch, np):
     log(f"touched experts per layer: mean {np.mean(touched):.1f}; expert bytes per step {w_bytes / 1e6:.1f} MB")
 
     def run(on):
-        moe.moe_stack_forward(handles, x.data_ptr(), T, STACK_EPS, None, ws.data_ptr(), ws.numel(), on)
+        moe.moe_stack_forward(handles, x.data_ptr(), T, STACK_EPS, None, ws.data_ptr(), ws.numel(), on,
+                              persistent=args.persistent)
 
     for _ in range(args.warmup):
         x.copy_(x0)
@@ -525,7 +528,7 @@ def bench_stack(args, moe, synth, torch, np):
                    "router_bias_zipf": cfg["zipf"], "rms_eps": STACK_EPS,
                    "touched_experts_mean": round(float(np.mean(touched)), 1),
                    "expert_weight_bytes_per_step": int(w_bytes), "router_bytes_per_step": NLAY * E * 2048 * 2,
-                   "launch": "hip_graph_replay" if graph_ms is not None else "plain",
+                   "launch": ("hip_graph_replay" if graph_ms is not None else "plain") + (", persistent" if args.persistent else ""),
                    "plain_launch_ms_per_step": round(ms, 5), "graph_replay_ms": spread,
                    "per_layer_stage_ms": stage_means},
         "roofline": {"bound": "hbm", "kernel": "ffn_up_kernel (gate/up + SwiGLU), every layer of the stack",
@@ -840,6 +843,9 @@ def main() -> int:
     ap.add_argument("--no-stream-reference", action="store_true", help="skip the 4 GiB streaming-read reference")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--persistent", action="store_true",
+                    help="time the persistent decode path (moe_layer_forward_persistent / moe_stack_forward_persistent);"
+                         " the roofline's per-kernel timing stays on the kernel chain")
     ap.add_argument("--mfma-rate", action="store_true",
                     help="only time the matrix-core rate helper per instruction kind (f16, bf16, fp8, scaled fp4)")
     args = ap.parse_args()

@@ -200,6 +200,25 @@ moe_status moe_layer_forward_staged(const moe_layer* layer, const void* x, int32
 moe_status moe_layer_forward_noalloc(const moe_layer* layer, const void* x, int32_t T, void* y,
                                      const moe_route_out* route, void* stream);
 
+/* moe_layer_forward as a persistent decode kernel, for batches of 1..64
+ * tokens (those with no matrix-core tile): the review's section "The
+ * quantisation recipe is the most transferable part" describes fusing the whole
+ * decode pass into one dispatch.  Here it is two launches on the caller's
+ * stream: the router (which also writes the shared expert's work items and
+ * clears the hand-off words in the workspace), then one kernel with one
+ * workgroup per compute unit (all resident at once) that runs top-k, buckets, gate/up,
+ * down and the combine, handing results between its workgroups with
+ * agent-scope release/acquire and counters in the workspace.  Results are
+ * bit-identical to moe_layer_forward's.  Arguments, workspace size and errors
+ * as for moe_layer_forward; T above 64 returns MOE_ERR_UNSUPPORTED.  Each
+ * in-kernel wait is bounded: if the GPU cannot keep every workgroup of the
+ * kernel resident (another kernel occupying compute units), the waits time out
+ * and the outputs are undefined, so run it on an otherwise idle device or
+ * stream order. */
+moe_status moe_layer_forward_persistent(const moe_layer* layer, const void* x, int32_t T, void* y,
+                                        const moe_route_out* route, void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
 /* Workspace bytes for moe_stack_forward over these layers at T tokens. */
 moe_status moe_stack_workspace_size(const moe_layer* const* layers, int32_t n_layers, int32_t T, size_t* bytes);
 
@@ -208,6 +227,12 @@ moe_status moe_stack_workspace_size(const moe_layer* const* layers, int32_t n_la
  * of n_layers moe_route_out (each entry's pointers may be NULL). */
 moe_status moe_stack_forward(const moe_layer* const* layers, int32_t n_layers, void* x, int32_t T, float rms_eps,
                              const moe_route_out* routes, void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_stack_forward with every layer on the persistent decode path of
+ * moe_layer_forward_persistent (two launches per layer; 1..64 tokens). */
+moe_status moe_stack_forward_persistent(const moe_layer* const* layers, int32_t n_layers, void* x, int32_t T,
+                                        float rms_eps, const moe_route_out* routes, void* workspace,
+                                        size_t workspace_bytes, void* stream);
 
 /* Output head (the step after the last MoE layer of a decode pass): logits
  * over the vocabulary,

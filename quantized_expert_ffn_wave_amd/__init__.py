@@ -22,7 +22,8 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
 WFMT = {"bf16": 0, "q4_1": 1, "nvfp4": 2}
 EXPORTED = ["moe_layer_create", "moe_layer_destroy", "moe_layer_workspace_size", "moe_desc_workspace_size",
             "moe_layer_forward", "moe_layer_forward_staged", "moe_layer_forward_noalloc",
-            "moe_stack_workspace_size", "moe_stack_forward",
+            "moe_layer_forward_persistent", "moe_stack_workspace_size", "moe_stack_forward",
+            "moe_stack_forward_persistent",
             "moe_head_forward", "moe_attn_workspace_size", "moe_attn_decode", "moe_stream_read", "moe_mfma_rate",
             "moe_last_error",
             "moe_version"]
@@ -93,6 +94,10 @@ _lib.moe_stack_workspace_size.restype = ctypes.c_int
 _lib.moe_stack_forward.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _i32, ctypes.c_float,
                                    ctypes.POINTER(moe_route_out), _vp, _sz, _vp]
 _lib.moe_stack_forward.restype = ctypes.c_int
+_lib.moe_stack_forward_persistent.argtypes = _lib.moe_stack_forward.argtypes
+_lib.moe_stack_forward_persistent.restype = ctypes.c_int
+_lib.moe_layer_forward_persistent.argtypes = _lib.moe_layer_forward.argtypes
+_lib.moe_layer_forward_persistent.restype = ctypes.c_int
 _lib.moe_head_forward.argtypes = [_vp, _i32, ctypes.POINTER(moe_qmat), _i32, _i32, _i32, _vp, _vp]
 _lib.moe_head_forward.restype = ctypes.c_int
 _lib.moe_attn_workspace_size.argtypes = [ctypes.POINTER(moe_attn_desc), _i32, _i32, ctypes.POINTER(_sz)]
@@ -162,6 +167,15 @@ def moe_layer_forward(handle: int, x_ptr: int, T: int, y_ptr: int, route: moe_ro
                                   ws_ptr, ws_bytes, stream), "moe_layer_forward")
 
 
+def moe_layer_forward_persistent(handle: int, x_ptr: int, T: int, y_ptr: int, route: moe_route_out | None,
+                                 ws_ptr: int, ws_bytes: int, stream: int) -> None:
+    _check(_lib.moe_layer_forward_persistent(handle, x_ptr, T, y_ptr, ctypes.byref(route) if route is not None
+                                             else None, ws_ptr, ws_bytes, stream), "moe_layer_forward_persistent")
+
+
+PERSISTENT_MAX_T = 64
+
+
 def moe_layer_forward_staged(handle: int, x_ptr: int, T: int, y_ptr: int, route: moe_route_out | None, ws_ptr: int,
                              ws_bytes: int, stream: int, events) -> None:
     """events: N_STAGE_EVENTS raw hipEvent_t handles (ints)."""
@@ -187,13 +201,14 @@ def moe_stack_workspace_size(handles, T: int) -> int:
 
 
 def moe_stack_forward(handles, x_ptr: int, T: int, eps: float, routes, ws_ptr: int, ws_bytes: int,
-                      stream: int) -> None:
+                      stream: int, persistent: bool = False) -> None:
     arr = (_vp * len(handles))(*handles)
     rarr = None
     if routes is not None:
         rarr = (moe_route_out * len(routes))(*routes)
-    _check(_lib.moe_stack_forward(arr, len(handles), x_ptr, T, eps, rarr, ws_ptr, ws_bytes, stream),
-           "moe_stack_forward")
+    f = _lib.moe_stack_forward_persistent if persistent else _lib.moe_stack_forward
+    _check(f(arr, len(handles), x_ptr, T, eps, rarr, ws_ptr, ws_bytes, stream),
+           "moe_stack_forward_persistent" if persistent else "moe_stack_forward")
 
 
 
@@ -408,8 +423,10 @@ def current_stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def layer_forward(layer: DeviceLayer, x, y=None, route: moe_route_out | None = None, workspace=None):
-    """y = MoE(x) for a bf16 torch tensor x [T][d] on the device."""
+def layer_forward(layer: DeviceLayer, x, y=None, route: moe_route_out | None = None, workspace=None,
+                  persistent: bool = False):
+    """y = MoE(x) for a bf16 torch tensor x [T][d] on the device (persistent:
+    through moe_layer_forward_persistent)."""
     import torch
     T = x.shape[0]
     if y is None:
@@ -417,12 +434,12 @@ def layer_forward(layer: DeviceLayer, x, y=None, route: moe_route_out | None = N
     nbytes = layer.workspace_size(T)
     if workspace is None:
         workspace = alloc_workspace(nbytes, x.device)
-    moe_layer_forward(layer.handle, x.data_ptr(), T, y.data_ptr(), route, workspace.data_ptr(), workspace.numel(),
-                      current_stream())
+    f = moe_layer_forward_persistent if persistent else moe_layer_forward
+    f(layer.handle, x.data_ptr(), T, y.data_ptr(), route, workspace.data_ptr(), workspace.numel(), current_stream())
     return y
 
 
-def stack_forward(layers, x, eps: float = 1e-6, routes=None, workspace=None):
+def stack_forward(layers, x, eps: float = 1e-6, routes=None, workspace=None, persistent: bool = False):
     """In-place pre-norm residual stack over bf16 x [T][d]."""
     handles = [l.handle for l in layers]
     T = x.shape[0]
@@ -430,5 +447,5 @@ def stack_forward(layers, x, eps: float = 1e-6, routes=None, workspace=None):
     if workspace is None:
         workspace = alloc_workspace(nbytes, x.device)
     moe_stack_forward(handles, x.data_ptr(), T, eps, routes, workspace.data_ptr(), workspace.numel(),
-                      current_stream())
+                      current_stream(), persistent=persistent)
     return x

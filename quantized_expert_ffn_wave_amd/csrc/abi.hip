@@ -77,7 +77,7 @@ moe_status check_qmat(const moe_qmat& q, int fmt, const char* name) {
 }
 
 struct WsLayout {
-  size_t logit_part, logits, ids, w, counts, offsets, perm, inv_perm, tiles, ctl, h, y, xsc, hslot, total;
+  size_t logit_part, logits, ids, w, counts, offsets, perm, inv_perm, tiles, ctl, h, y, xsc, hslot, sync, total;
   int max_tiles;
 };
 
@@ -108,6 +108,7 @@ WsLayout ws_layout(const moe_layer_desc& d, int T) {
   L.y = take(sizeof(float) * R * moe::D_MODEL);
   L.xsc = take(sizeof(float) * (size_t)T);
   L.hslot = take(sizeof(float) * moe::HSLOTS * R);
+  L.sync = take(sizeof(uint32_t) * moe::DEC_SYNC_WORDS);
   L.total = o;
   return L;
 }
@@ -175,10 +176,31 @@ hipError_t mark(void* const* ev, int i, hipStream_t s) {
 // (except the output) are enqueued before the combine, which in a stack
 // overwrites the layer input.  ev (optional): stage records.
 moe_status run_layer(const moe_layer* L, moe::LayerArgs& a, const WsLayout& W, const moe_route_out* route,
-                     hipStream_t s, void* const* ev) {
+                     hipStream_t s, void* const* ev, char* ws = nullptr, bool persistent = false) {
   hipError_t e;
   a.write_logits = (route && route->logits) ? 1 : 0;
   if (a.write_logits) a.logits = route->logits;
+  if (persistent) {
+    // two launches: router (+ shared work items, hand-off words cleared), then
+    // one persistent kernel for top-k, buckets, gate/up, down and combine; the
+    // route copies of the layer input go first (a stack's combine overwrites it)
+    if (route && (e = copy_async(route->x_in, a.x, (size_t)a.T * moe::D_MODEL * 2, s)) != hipSuccess)
+      return hip_fail(e, "route copy");
+    if ((e = moe::launch_decode(a, reinterpret_cast<uint32_t*>(ws + W.sync), L->n_cu, s)) != hipSuccess)
+      return hip_fail(e, "persistent decode launch");
+    if (route) {
+      const size_t S = (size_t)a.S;
+      const int E = a.E;
+      if ((e = copy_async(route->topk_ids, a.ids, S * 4, s)) != hipSuccess ||
+          (e = copy_async(route->topk_w, a.w, S * 4, s)) != hipSuccess ||
+          (e = copy_async(route->counts, a.counts, (size_t)E * 4, s)) != hipSuccess ||
+          (e = copy_async(route->offsets, a.offsets, (size_t)(E + 1) * 4, s)) != hipSuccess ||
+          (e = copy_async(route->perm, a.perm, S * 4, s)) != hipSuccess ||
+          (e = copy_async(route->inv_perm, a.inv_perm, S * 4, s)) != hipSuccess)
+        return hip_fail(e, "route copy");
+    }
+    return MOE_OK;
+  }
   if ((e = mark(ev, 0, s)) != hipSuccess) return hip_fail(e, "event record");
   if ((e = moe::launch_router(a, s)) != hipSuccess) return hip_fail(e, "router launch");
   if ((e = mark(ev, 1, s)) != hipSuccess) return hip_fail(e, "event record");
@@ -304,7 +326,7 @@ moe_status moe_layer_workspace_size(const moe_layer* layer, int32_t T, size_t* b
 
 static moe_status layer_forward_impl(const moe_layer* L, const void* x, int32_t T, void* y,
                                      const moe_route_out* route, void* ws, size_t ws_bytes, void* stream,
-                                     void* const* ev) {
+                                     void* const* ev, bool persistent = false) {
   if (!L) return fail(MOE_ERR_INVALID_ARG, "layer is NULL");
   if (T < 0 || T > L->desc.max_tokens)
     return fail(MOE_ERR_INVALID_ARG, "T=%d outside [0, max_tokens=%d]", T, L->desc.max_tokens);
@@ -318,9 +340,11 @@ static moe_status layer_forward_impl(const moe_layer* L, const void* x, int32_t 
   moe_status st = check_ws(ws, ws_bytes, W.total);
   if (st != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
+  if (persistent && !moe::decode_supported(T))
+    return fail(MOE_ERR_UNSUPPORTED, "the persistent decode path covers 1..64 tokens (T=%d)", T);
   moe::LayerArgs a = make_args(L, x, T, (char*)ws, W);
   a.out = (uint16_t*)y;
-  if ((st = run_layer(L, a, W, route, s, ev)) != MOE_OK) return st;
+  if ((st = run_layer(L, a, W, route, s, ev, (char*)ws, persistent)) != MOE_OK) return st;
   hipError_t e;
   if (route && (e = copy_async(route->y_out, y, xb, s)) != hipSuccess) return hip_fail(e, "route copy");
   return MOE_OK;
@@ -379,6 +403,11 @@ moe_status moe_layer_forward_noalloc(const moe_layer* L, const void* x, int32_t 
   return layer_forward_impl(L, x, T, y, route, ws, (size_t)MOE_NOALLOC_MAX_WORKSPACE, stream, nullptr);
 }
 
+moe_status moe_layer_forward_persistent(const moe_layer* L, const void* x, int32_t T, void* y,
+                                        const moe_route_out* route, void* ws, size_t ws_bytes, void* stream) {
+  return layer_forward_impl(L, x, T, y, route, ws, ws_bytes, stream, nullptr, true);
+}
+
 moe_status moe_layer_forward_staged(const moe_layer* L, const void* x, int32_t T, void* y,
                                     const moe_route_out* route, void* ws, size_t ws_bytes, void* stream,
                                     void* const* events, int32_t n_events) {
@@ -404,12 +433,15 @@ moe_status moe_stack_workspace_size(const moe_layer* const* layers, int32_t n, i
   return MOE_OK;
 }
 
-moe_status moe_stack_forward(const moe_layer* const* layers, int32_t n, void* x, int32_t T, float eps,
-                             const moe_route_out* routes, void* ws, size_t ws_bytes, void* stream) {
+static moe_status stack_forward_impl(const moe_layer* const* layers, int32_t n, void* x, int32_t T, float eps,
+                                     const moe_route_out* routes, void* ws, size_t ws_bytes, void* stream,
+                                     bool persistent) {
   size_t need = 0;
   moe_status st = moe_stack_workspace_size(layers, n, T, &need);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
+  if (persistent && !moe::decode_supported(T))
+    return fail(MOE_ERR_UNSUPPORTED, "the persistent decode path covers 1..64 tokens (T=%d)", T);
   if (!x || !aligned(x, 16)) return fail(MOE_ERR_INVALID_ARG, "x is NULL or not 16-byte aligned");
   if (!(eps >= 0.f)) return fail(MOE_ERR_INVALID_ARG, "rms_eps must be >= 0");
   if ((st = check_ws(ws, ws_bytes, need)) != MOE_OK) return st;
@@ -435,9 +467,19 @@ moe_status moe_stack_forward(const moe_layer* const* layers, int32_t n, void* x,
     a.y_rec = route ? (uint16_t*)route->y_out : nullptr;
     a.xn_next = last ? nullptr : xn;
     a.x_final = last ? (uint16_t*)x : nullptr;
-    if ((st = run_layer(L, a, W, route, s, nullptr)) != MOE_OK) return st;
+    if ((st = run_layer(L, a, W, route, s, nullptr, base, persistent)) != MOE_OK) return st;
   }
   return MOE_OK;
+}
+
+moe_status moe_stack_forward(const moe_layer* const* layers, int32_t n, void* x, int32_t T, float eps,
+                             const moe_route_out* routes, void* ws, size_t ws_bytes, void* stream) {
+  return stack_forward_impl(layers, n, x, T, eps, routes, ws, ws_bytes, stream, false);
+}
+
+moe_status moe_stack_forward_persistent(const moe_layer* const* layers, int32_t n, void* x, int32_t T, float eps,
+                                        const moe_route_out* routes, void* ws, size_t ws_bytes, void* stream) {
+  return stack_forward_impl(layers, n, x, T, eps, routes, ws, ws_bytes, stream, true);
 }
 
 moe_status moe_head_forward(const void* x, int32_t T, const moe_qmat* w, int32_t wfmt, int32_t vocab,

@@ -53,14 +53,14 @@ __host__ __device__ inline int mfma_bn(int T) { return T > MFMA_WIDE_T ? 128 : 6
 // 128-token tiles, 64 for 64-token ones
 __host__ __device__ constexpr int mf_up_chunks(int bn) { return bn == 128 ? 4 : 8; }
 // path and token groups/tiles of a bucket of m tokens in a batch of T tokens
-__host__ __device__ inline int mfma_min(int T) { return T > MFMA_MID_T ? MFMA_MIN_WIDE : MFMA_MIN; }
-__host__ __device__ inline bool bucket_mfma(int m, int T) { return m >= mfma_min(T); }
+__host__ __device__ constexpr int mfma_min(int T) { return T > MFMA_MID_T ? MFMA_MIN_WIDE : MFMA_MIN; }
+__host__ __device__ constexpr bool bucket_mfma(int m, int T) { return m >= mfma_min(T); }
 __host__ __device__ inline int bucket_tiles(int m, int T) {
   return m <= 0 ? 0 : (bucket_mfma(m, T) ? ceil_div(m, mfma_bn(T)) : ceil_div(m, GV_GROUP));
 }
 // The shared expert (all T tokens) takes tiles from MFMA_MIN tokens on at every
 // batch size: a tile holding a few dozen tokens is slower than its vector groups.
-__host__ __device__ inline bool shared_mfma(int T) { return T >= MFMA_MIN; }
+__host__ __device__ constexpr bool shared_mfma(int T) { return T >= MFMA_MIN; }
 __host__ __device__ inline int shared_tiles(int T) {
   return T <= 0 ? 0 : (shared_mfma(T) ? ceil_div(T, mfma_bn(T)) : ceil_div(T, GV_GROUP));
 }
@@ -88,6 +88,9 @@ __device__ inline bool item_mfma(uint32_t h) { return (h & ITEM_MFMA) != 0; }
 
 // ---- control block ------------------------------------------------------------------
 enum Ctl : int { CTL_N_UP = 0, CTL_N_DN = 1, CTL_N_UP_MF = 2, CTL_N_DN_MF = 3, CTL_WORDS = 16 };
+// hand-off words of the persistent decode path (workspace; cleared by its first launch)
+enum DecSync : int { DEC_SYNC_TOPK = 0, DEC_SYNC_B1 = 1, DEC_SYNC_B2 = 2, DEC_SYNC_B3 = 3, DEC_SYNC_TIMEOUT = 15,
+                     DEC_SYNC_WORDS = 16 };
 
 struct QMat {
   const uint8_t* codes;   // q4_1/nvfp4 nibbles or bf16 elements
@@ -203,6 +206,9 @@ hipError_t launch_combine(const LayerArgs& a, hipStream_t s);
 // max_wgs workgroups, else as many as are resident on n_cu CUs at once
 hipError_t launch_ffn(const LayerArgs& a, bool up, int n_cu, int max_wgs, hipStream_t s);
 hipError_t launch_stack_init(const uint16_t* x, float* r, uint16_t* xn, int T, float eps, hipStream_t s);
+// persistent decode layer (two launches) for batches of decode_supported(T) tokens
+bool decode_supported(int T);
+hipError_t launch_decode(const LayerArgs& a, uint32_t* sync, int n_cu, hipStream_t s);
 // output head over n_cu compute units
 hipError_t launch_head(const HeadArgs& a, int n_cu, hipStream_t s);
 // plain streaming read of bytes (a multiple of 16) from src on grid workgroups

@@ -591,22 +591,22 @@ __device__ inline float upper_half(float v) {
 // round-robin to the other G - m workgroups only (R rounds), the rest to all
 // workgroups round-robin.  With no matrix-core items this is c = blockIdx.x,
 // + G, ...
+// The walkers are workgroups wid = 0 .. nwg - 1 (the whole grid, or a part of
+// a persistent one).
 struct VecOrder {
-  int G, m, P;
-  __device__ VecOrder(int n_mf) {
-    G = (int)gridDim.x;
+  int G, m, P, w;
+  __device__ VecOrder(int n_mf, int wid, int nwg) {
+    G = nwg;
+    w = wid;
     m = min(n_mf, G);
     const int R = (n_mf > 0 && m < G) ? 2 * ceil_div(n_mf, G) : 0;
     P = R * (G - m);
   }
-  __device__ int first() const {
-    const int w = (int)blockIdx.x;
-    return (w >= m && P > 0) ? w - m : P + w;
-  }
+  __device__ int first() const { return (w >= m && P > 0) ? w - m : P + w; }
   __device__ int next(int c) const {
     if (c < P) {
       const int nc = c + (G - m);
-      return nc < P ? nc : P + (int)blockIdx.x;
+      return nc < P ? nc : P + w;
     }
     return c + G;
   }
@@ -631,13 +631,13 @@ __device__ inline void vec_hslots(const LayerArgs& a, const Item& item, const It
 // gate/up + SwiGLU over the vector-path items base + c, c in [0, n), this
 // workgroup taking its items in VecOrder.
 template <int FMT, int VR>
-__device__ void up_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem& sm) {
+__device__ void up_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem& sm, int wid, int nwg) {
   using G = GV<FMT>;
   constexpr int CH = D_FF / VR;
   constexpr int D = MV_UP_RING<FMT>, NU = MV_UP_UNITS<VR>;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 3, b = lane >> 2;
-  const VecOrder order(n_mf);
+  const VecOrder order(n_mf, wid, nwg);
   int c = order.first();
   if (c >= n) return;
   Item item = fetch_item(a.tiles, base + c, CH);
@@ -765,13 +765,13 @@ __device__ void up_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem&
 // down over vector-path chunks, ordered and loaded as in up_stream: load u of a
 // chunk covers rows first_row + 4 u + j over the whole K = 512 (chunk b per lane)
 template <int FMT, int VDR>
-__device__ void down_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem& sm) {
+__device__ void down_stream(const LayerArgs& a, int base, int n, int n_mf, MvSmem& sm, int wid, int nwg) {
   using G = GV<FMT>;
   constexpr int CH = D_MODEL / VDR;
   constexpr int D = MV_DN_RING<FMT>, NU = MV_DN_UNITS<VDR>;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 3, b = lane >> 2;
-  const VecOrder order(n_mf);
+  const VecOrder order(n_mf, wid, nwg);
   int c = order.first();
   if (c >= n) return;
   Item item = fetch_item(a.tiles, base + c, CH);
@@ -1221,7 +1221,7 @@ __global__ __launch_bounds__(256, (FFN_WG_PER_CU<FMT, BN>)) void ffn_up_kernel(L
                        item_tokens(item), item_chunk(item.head) * (D_FF / UC), sm.mf);
     }
   }
-  up_stream<FMT, VR>(a, base, n_all - base, n_mf, sm.gv);
+  up_stream<FMT, VR>(a, base, n_all - base, n_mf, sm.gv, blockIdx.x, gridDim.x);
 }
 
 template <int FMT, int BN, int VDR>
@@ -1237,7 +1237,7 @@ __global__ __launch_bounds__(256, (FFN_WG_PER_CU<FMT, BN>)) void ffn_down_kernel
     }
   }
   const int base = (n_mf / N_DN_CHUNKS) * (D_MODEL / VDR);
-  down_stream<FMT, VDR>(a, base, n_all - base, n_mf, sm.gv);
+  down_stream<FMT, VDR>(a, base, n_all - base, n_mf, sm.gv, blockIdx.x, gridDim.x);
 }
 
 // Workgroups of `kernel` that fit on one CU at once (the persistent kernels are
@@ -1330,8 +1330,8 @@ __device__ inline void rmsnorm_store(const float* v, uint16_t* dst, float eps) {
 // then the shared expert, rounded once to bf16.  Single layer: written to
 // a.out.  Stack: recorded to a.y_rec (if any), r += out, then the next
 // layer's input bf16(RMSNorm(r)) or, after the last layer, bf16(r).
-__global__ __launch_bounds__(256) void combine_kernel(LayerArgs a) {
-  const int t = blockIdx.x, K = a.K;
+__device__ inline void combine_token(const LayerArgs& a, int t) {
+  const int K = a.K;
   const int i0 = 8 * threadIdx.x;
   // every load is issued before the first sum: the slots' rows, then the rows
   int pos[MAX_K];
@@ -1383,6 +1383,8 @@ __global__ __launch_bounds__(256) void combine_kernel(LayerArgs a) {
   if (a.x_final) store_bf16x8(a.x_final + (size_t)t * D_MODEL + i0, rv);
   if (a.xn_next) rmsnorm_store(rv, a.xn_next + (size_t)t * D_MODEL + i0, a.eps);
 }
+
+__global__ __launch_bounds__(256) void combine_kernel(LayerArgs a) { combine_token(a, blockIdx.x); }
 
 hipError_t launch_combine(const LayerArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(combine_kernel, dim3(a.T), dim3(256), 0, s, a);

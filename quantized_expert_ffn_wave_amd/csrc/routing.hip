@@ -38,16 +38,15 @@ __host__ __device__ inline int router_splits(int T) { return T <= ROUTER_SMALL_T
 // Decode-sized T: one wave per (16-token tile, 16-expert tile, K-split); the
 // workgroup's 4 waves take 4 consecutive expert tiles.  grid (ceil(T/16) *
 // ceil(E/64), ROUTER_KS).  MFMA 16x16x32 bf16: A = x rows, B = router rows.
-__global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __restrict__ x,
-                                                           const uint16_t* __restrict__ wr,
-                                                           const float* __restrict__ bias, float* __restrict__ part,
-                                                           int T, int E) {
+// (bx, ks): the workgroup's (token tile x expert group, K-split) indices
+__device__ inline void router_small_tile(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                                         const float* __restrict__ bias, float* __restrict__ part, int T, int E,
+                                         int bx, int ks) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int egroups = (E + 63) / 64;
-  const int t0 = (blockIdx.x / egroups) * 16;
-  const int e0 = ((blockIdx.x % egroups) * 4 + wave) * 16;
+  const int t0 = (bx / egroups) * 16;
+  const int e0 = ((bx % egroups) * 4 + wave) * 16;
   if (e0 >= E) return;
-  const int ks = blockIdx.y;
   const int kbase = ks * ROUTER_KR + 8 * (lane >> 4);
   const int col = lane & 15;
   const int t = t0 + col;
@@ -69,6 +68,13 @@ __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __res
     const int tt = t0 + 4 * (lane >> 4) + j;
     if (tt < T) part[((size_t)ks * T + tt) * E + e0 + col] = acc[j] + bz;
   }
+}
+
+__global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ wr,
+                                                           const float* __restrict__ bias, float* __restrict__ part,
+                                                           int T, int E) {
+  router_small_tile(x, wr, bias, part, T, E, blockIdx.x, blockIdx.y);
 }
 
 // Larger T: one 1024-thread workgroup per (64-token group, K-split of 512).
@@ -508,6 +514,23 @@ struct RouteSmallSmem {
   int wtot[4][3];        // per wave of experts: sizes, matrix-core tiles, vector tiles
 };
 
+// Tile i of the shared expert, which takes every token: bn-token matrix-core
+// tiles (mf), or groups of GV_GROUP tokens with their ids.
+__device__ inline Item shared_tile(int T, int i, bool mf, int bn) {
+  const int per = mf ? bn : GV_GROUP;
+  const int p0 = i * per, cnt = min(per, T - p0);
+  uint32_t tk[GV_GROUP] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < GV_GROUP; ++j)
+    if (!mf && j < cnt) tk[j] = (uint32_t)(p0 + j);
+  Item it;
+  it.head = item_head(SHARED_ID, 0, cnt, mf);
+  it.p0 = (uint32_t)p0;
+  it.t01 = tk[0] | (tk[1] << 16);
+  it.t23 = tk[2] | (tk[3] << 16);
+  return it;
+}
+
 // inclusive prefix sum over the wave's lanes
 __device__ inline int wave_inclusive(int v) {
   const int lane = threadIdx.x & 63;
@@ -646,22 +669,12 @@ __device__ void route_small(const LayerArgs& a, RouteSmallSmem& sm) {
       a.tiles[ti] = it;
     }
   }
-  // the shared expert's tiles, on the threads past the experts
+  // the shared expert's tiles, on the threads past the experts (a 256-thread
+  // caller writes them itself: they do not depend on the routing)
   for (int i = tid - 256; i >= 0 && i < sh_tiles; i += nth - 256) {
     const int ti = (sh_mf ? tiles_m : mf_tiles) + i;
     if (ti >= n_tiles) break;
-    const int per = sh_mf ? bn : GV_GROUP;
-    const int p0 = i * per, cnt = min(per, T - p0);
-    uint32_t tk[GV_GROUP] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < GV_GROUP; ++j)
-      if (!sh_mf && j < cnt) tk[j] = (uint32_t)(p0 + j);
-    Item it;
-    it.head = item_head(SHARED_ID, 0, cnt, sh_mf);
-    it.p0 = (uint32_t)p0;
-    it.t01 = tk[0] | (tk[1] << 16);
-    it.t23 = tk[2] | (tk[3] << 16);
-    a.tiles[ti] = it;
+    a.tiles[ti] = shared_tile(T, i, sh_mf, bn);
   }
 }
 

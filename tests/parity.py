@@ -47,11 +47,11 @@ def row_rel_err(y: np.ndarray, r: np.ndarray) -> np.ndarray:
     return np.abs(y - r).max(1) / den
 
 
-def gpu_forward(dl: moe.DeviceLayer, x_bits: np.ndarray, E: int, k: int):
+def gpu_forward(dl: moe.DeviceLayer, x_bits: np.ndarray, E: int, k: int, persistent: bool = False):
     T = x_bits.shape[0]
     route, bufs = moe.route_buffers(T, k, E)
     x = x_to_dev(x_bits)
-    y = moe.layer_forward(dl, x, route=route)
+    y = moe.layer_forward(dl, x, route=route, persistent=persistent)
     torch.cuda.synchronize()
     out = {n: t.cpu().numpy() for n, t in bufs.items() if n not in ("x_in", "y_out")}
     out["perm"] = out["perm"][:T * k]
@@ -103,11 +103,12 @@ def check_routing(g: dict, o: dict, E: int, k: int, scale: np.ndarray | None = N
 
 
 def check_layer(host, x_bits: np.ndarray, dl: moe.DeviceLayer | None = None, sample=None, tol: float = OUT_TOL,
-                threads: int = 0) -> dict:
-    """Run the GPU layer and compare it with the oracle under the rules above."""
+                threads: int = 0, persistent: bool = False) -> dict:
+    """Run the GPU layer (persistent: the persistent decode path) and compare it
+    with the oracle under the rules above."""
     if dl is None:
         dl = moe.DeviceLayer(host, max_tokens=max(x_bits.shape[0], 1))
-    g = gpu_forward(dl, x_bits, host.E, host.k)
+    g = gpu_forward(dl, x_bits, host.E, host.k, persistent=persistent)
     assert np.array_equal(g["x_in_bits"], x_bits)
     assert np.array_equal(g["y_out_bits"], g["y_bits"])
     o = oracle.route(host, x_bits, threads=threads)
@@ -119,5 +120,5 @@ def check_layer(host, x_bits: np.ndarray, dl: moe.DeviceLayer | None = None, sam
     err = row_rel_err(y, ref["out"])
     assert np.all(np.isfinite(y))
     assert err.max() <= tol, (err.max(), int(err.argmax()))
-    info.update(max_err=float(err.max()), mean_err=float(err.mean()), counts=g["counts"])
+    info.update(max_err=float(err.max()), mean_err=float(err.mean()), counts=g["counts"], gpu=g)
     return info
