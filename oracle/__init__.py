@@ -17,7 +17,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+_LIB = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")  # override: an instrumented build
 _FMT = {"bf16": 0, "q4_1": 1, "nvfp4": 2}
 
 _lib = None

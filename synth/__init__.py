@@ -32,7 +32,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "synth.c")
-_LIB = os.path.join(_HERE, "libsynth.so")
+_LIB = os.environ.get("MOE_SYNTH_LIB") or os.path.join(_HERE, "libsynth.so")  # override: an instrumented build
 
 TAG_X, TAG_ROUTER, TAG_BIAS, TAG_EXPERT, TAG_HEAD, TAG_ATTN, TAG_EDGE = 1, 2, 3, 4, 5, 6, 7
 HEAD_VOCAB = 151552  # synthetic vocabulary of the output-head workload
