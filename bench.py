@@ -14,8 +14,9 @@ stream (event records inside a captured graph do not time kernels).  The default
 workload is the 64-token decode layer with q4_1 experts (256 routed + 1 shared,
 width 512, d_model 2048, top-6, near-uniform routing).  Steps rotate over
 `--layers` independently drawn layer instances (3.9 GB of packed weights for 8)
-so that every step reads its expert weights from HBM, not from the 256 MB
-last-level cache.
+and, for small batches, over several token sets per instance, so that one
+cycle of steps reads at least 1 GiB of expert weights and every step reads its
+weights from HBM, not from the 256 MB last-level cache.
 
 The 47-layer workload (`--workload stack47_decode_t32_q4_1_zipf0.8`) times the
 pre-norm residual stack instead: a step is 32 tokens through all 47 layers
@@ -59,6 +60,12 @@ HBM_PEAK_GBPS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 STREAM_BYTES = 4 << 30
 SWEEP_T = [1, 2, 4, 8, 16, 32, 64, 128, 256]
+# One cycle of timed forwards reads at least this many bytes of expert weights
+# (four times the chip's 256 MB last-level cache), so that no step finds its
+# weights still cached from the previous cycle; small batches get more token
+# sets per layer instance to reach it.
+CYCLE_MIN_BYTES = 1 << 30
+MAX_X_SETS = 16
 STACK_EPS = 1e-6
 
 
@@ -69,7 +76,8 @@ def log(msg: str) -> None:
 def kernel_source_hash(kernel: str = "ffn_up") -> str:
     """Hash of the sources of the kernel a traffic summary was taken on."""
     h = hashlib.sha256()
-    files = ("attention.hip", "attention.hpp", "common.hpp") if kernel == "attn" else ("ffn.hip", "common.hpp")
+    files = (("attention.hip", "attention.hpp", "common.hpp") if kernel == "attn" else
+             ("layer.hip", "routing.hip", "ffn.hip", "decode.hip", "common.hpp"))
     for f in files:
         with open(os.path.join(ROOT, "quantized_expert_ffn_wave_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
@@ -196,21 +204,32 @@ def bench_layer(args, moe, synth, torch, np):
         # (fp32 for the 4-bit formats, bf16 for bf16 weights)
         return U, (U + 1) * exp_b, (U + 1) * gu_b + n * 2048 * 2 + (n * K + n) * 512 * h_elem
 
+    # the timed forwards cycle over (layer instance, token set) pairs; token
+    # set 0 is x, the others are drawn with further seeds, as many as a cycle
+    # needs to read CYCLE_MIN_BYTES of expert weights
+    first_w = [touched_bytes(dl, x, ws)[1] for dl in dls]
+    R = min(MAX_X_SETS, max(1, -(-CYCLE_MIN_BYTES // int(sum(first_w)))))
+    xs = [x] + [torch.from_numpy(synth.make_x(T, xseed=r).view(np.int16)).cuda().view(torch.bfloat16)
+                for r in range(1, R)]
+    pairs = [(l, r) for r in range(R) for l in range(NL)]
+    P = len(pairs)
     touched, step_w_bytes, up_bytes = [], [], []
-    for dl in dls:
-        U, wb, ub = touched_bytes(dl, x, ws)
+    for l, r in pairs:
+        U, wb, ub = touched_bytes(dls[l], xs[r], ws)
         touched.append(U)
         step_w_bytes.append(wb)
         up_bytes.append(ub)
+    log(f"{R} token set(s) per instance: {P} forwards, {sum(step_w_bytes) / 1e9:.2f} GB of expert weights per cycle")
     router_b = E * 2048 * 2
 
     def step(i, events=None, on=None):
-        dl = dls[i % NL]
+        l, r = pairs[i % P]
+        dl, xr = dls[l], xs[r]
         if events is None:
             fwd = moe.moe_layer_forward_persistent if args.persistent else moe.moe_layer_forward
-            fwd(dl.handle, x.data_ptr(), T, y.data_ptr(), None, ws.data_ptr(), ws.numel(), stream if on is None else on)
+            fwd(dl.handle, xr.data_ptr(), T, y.data_ptr(), None, ws.data_ptr(), ws.numel(), stream if on is None else on)
         else:
-            moe.moe_layer_forward_staged(dl.handle, x.data_ptr(), T, y.data_ptr(), None, ws.data_ptr(), ws.numel(),
+            moe.moe_layer_forward_staged(dl.handle, xr.data_ptr(), T, y.data_ptr(), None, ws.data_ptr(), ws.numel(),
                                          stream, events)
 
     log(f"warmup {args.warmup} steps")
@@ -238,20 +257,21 @@ def bench_layer(args, moe, synth, torch, np):
 
     graph_ms, spread = None, None
     if not args.no_graph:
-        # One graph holds a forward of every layer instance in turn, as a decode
-        # loop captures its whole step rather than one graph per layer (a graph
-        # launch costs about 5 us of idle GPU between graphs); a second graph
-        # holds the first K % NL instances, so that exactly K steps are timed.
+        # One graph holds a forward of every (instance, token set) pair in
+        # turn, as a decode loop captures its whole step rather than one graph
+        # per layer (a graph launch costs about 5 us of idle GPU between
+        # graphs); a second graph holds the first K % P pairs, so that exactly
+        # K steps are timed.
         def capture(n):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for i in range(n):
                     step(i, on=moe.current_stream())
             return g
-        n_full, n_rest = divmod(args.steps, NL)
-        g_all = capture(NL)
+        n_full, n_rest = divmod(args.steps, P)
+        g_all = capture(P)
         g_rest = capture(n_rest) if n_rest else None
-        for _ in range(max(1, args.warmup // NL)):
+        for _ in range(max(1, args.warmup // P)):
             g_all.replay()
         torch.cuda.synchronize()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -264,18 +284,18 @@ def bench_layer(args, moe, synth, torch, np):
         torch.cuda.synchronize()
         graph_ms = g0.elapsed_time(g1) / args.steps
         log(f"graph replay: {graph_ms * 1e3:.1f} us per step")
-        sp = [v / NL for v in replay_spread(torch, lambda i: g_all.replay(), max(n_full, 10))]
-        spread = {"p10": pct(sp, 10), "p50": pct(sp, 50), "p90": pct(sp, 90), "steps_per_replay": NL}
+        sp = [v / P for v in replay_spread(torch, lambda i: g_all.replay(), max(n_full, 10))]
+        spread = {"p10": pct(sp, 10), "p50": pct(sp, 50), "p90": pct(sp, 90), "steps_per_replay": P}
         del g_all, g_rest
 
     stage_ms = np.array([[row[j].elapsed_time(row[j + 1]) for j in range(moe.N_STAGE_EVENTS - 1)] for row in evs])
-    idx = [(args.warmup + i) % NL for i in range(args.steps)]
+    idx = [(args.warmup + i) % P for i in range(args.steps)]
     up_ms = stage_ms[:, moe.STAGES.index("gate_up")]
     up_achieved = sum(up_bytes[j] for j in idx) / (up_ms.sum() * 1e-3) / 1e9
     step_ms = graph_ms if graph_ms is not None else ms
-    # the timed steps: instances 0, 1, ... in the graph, warmup, warmup + 1, ... in plain launches
+    # the timed steps: pairs 0, 1, ... in the graph, warmup, warmup + 1, ... in plain launches
     first = 0 if graph_ms is not None else args.warmup
-    w_bytes = float(np.mean([step_w_bytes[(first + i) % NL] for i in range(args.steps)]))
+    w_bytes = float(np.mean([step_w_bytes[(first + i) % P] for i in range(args.steps)]))
     gbps = w_bytes / (step_ms * 1e-3) / 1e9
     traffic = read_traffic(args.workload)
     stage_means = {n: round(float(v), 4) for n, v in zip(moe.STAGES, stage_ms.mean(0))}
@@ -287,30 +307,38 @@ def bench_layer(args, moe, synth, torch, np):
         x_all = torch.from_numpy(synth.make_x(SWEEP_T[-1]).view(np.int16)).cuda().view(torch.bfloat16)
         ws_all = moe.alloc_workspace(max(dls[0].workspace_size(t) for t in SWEEP_T))
         for t in SWEEP_T:
-            xt, yt = x_all[:t].contiguous(), torch.empty((t, 2048), dtype=torch.bfloat16, device="cuda")
-            tb = [touched_bytes(dl, xt, ws_all) for dl in dls]
-            g = torch.cuda.CUDAGraph()  # every instance in turn, as for the timed steps above
+            # token sets: disjoint row windows of x_all, as many as a cycle over
+            # the instances needs to read CYCLE_MIN_BYTES (see the timed steps)
+            yt = torch.empty((t, 2048), dtype=torch.bfloat16, device="cuda")
+            tb0 = [touched_bytes(dl, x_all[:t].contiguous(), ws_all)[1] for dl in dls]
+            Rt = min(MAX_X_SETS, SWEEP_T[-1] // t, max(1, -(-CYCLE_MIN_BYTES // int(sum(tb0)))))
+            xts = [x_all[r * t:(r + 1) * t].contiguous() for r in range(Rt)]
+            tb = [touched_bytes(dl, xr, ws_all) for xr in xts for dl in dls]
+            g = torch.cuda.CUDAGraph()  # every (token set, instance) pair in turn, as for the timed steps
             with torch.cuda.graph(g):
                 fwd = (moe.moe_layer_forward_persistent if args.persistent and t <= moe.PERSISTENT_MAX_T
                        else moe.moe_layer_forward)
-                for dl in dls:
-                    fwd(dl.handle, xt.data_ptr(), t, yt.data_ptr(), None, ws_all.data_ptr(), ws_all.numel(),
-                        moe.current_stream())
-            for _ in range(max(1, args.warmup // NL)):
+                for xr in xts:
+                    for dl in dls:
+                        fwd(dl.handle, xr.data_ptr(), t, yt.data_ptr(), None, ws_all.data_ptr(), ws_all.numel(),
+                            moe.current_stream())
+            n_fwd = Rt * NL
+            for _ in range(max(1, args.warmup // n_fwd)):
                 g.replay()
             torch.cuda.synchronize()
-            reps = max(2, args.steps // (2 * NL))
+            reps = max(2, args.steps // (2 * n_fwd))
             a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a0.record()
             for _ in range(reps):
                 g.replay()
             a1.record()
             torch.cuda.synchronize()
-            t_ms = a0.elapsed_time(a1) / (reps * NL)
+            t_ms = a0.elapsed_time(a1) / (reps * n_fwd)
             wb = float(np.mean([b for _, b, _ in tb]))
             sweep.append({"tokens": t, "us_per_step": round(t_ms * 1e3, 2), "tokens_per_s": round(t / (t_ms * 1e-3), 1),
                           "touched_experts_mean": round(float(np.mean([u for u, _, _ in tb])), 1),
-                          "hbm_gbps_expert_weights": round(wb / (t_ms * 1e-3) / 1e9, 1)})
+                          "hbm_gbps_expert_weights": round(wb / (t_ms * 1e-3) / 1e9, 1),
+                          "token_sets": Rt, "weight_bytes_per_cycle": int(sum(b for _, b, _ in tb))})
             log(f"sweep T={t}: {t_ms * 1e3:.1f} us, {sweep[-1]['hbm_gbps_expert_weights']} GB/s")
             del g
         del x_all, ws_all
@@ -359,7 +387,7 @@ def bench_layer(args, moe, synth, torch, np):
         "stream_read": stream_ref,
         "config": {"workload": f"moe_layer_{args.workload}", "tokens": T, "d_model": 2048, "routed_experts": E,
                    "top_k": K, "shared_experts": 1, "d_expert": 512, "weights": fmt, "router_bias_zipf": cfg["zipf"],
-                   "layer_instances": NL, "touched_experts_mean": round(float(np.mean(touched)), 1),
+                   "layer_instances": NL, "token_sets": R, "touched_experts_mean": round(float(np.mean(touched)), 1),
                    "expert_weight_bytes_per_step": int(w_bytes), "router_bytes_per_step": router_b,
                    "launch": ("hip_graph_replay" if graph_ms is not None else "plain") + (", persistent" if args.persistent else ""),
                    "plain_launch_ms_per_step": round(ms, 5), "graph_replay_ms": spread, "stage_ms": stage_means},

@@ -105,7 +105,9 @@ WsLayout ws_layout(const moe_layer_desc& d, int T) {
   // SwiGLU output: fp32 for the 4-bit formats (scaled into fp16 by the down
   // kernel with the row's largest |h|), bf16 for bf16 weights
   L.h = take((d.wfmt == MOE_W_BF16 ? sizeof(uint16_t) : sizeof(float)) * R * moe::D_FF);
-  L.y = take(sizeof(float) * R * moe::D_MODEL);
+  // expert outputs: fp32 for the 4-bit formats, bf16 for bf16 weights (the
+  // prefill volume: 7 rows of 2048 per token)
+  L.y = take((d.wfmt == MOE_W_BF16 ? sizeof(uint16_t) : sizeof(float)) * R * moe::D_MODEL);
   L.xsc = take(sizeof(float) * (size_t)T);
   L.hslot = take(sizeof(float) * moe::HSLOTS * R);
   L.sync = take(sizeof(uint32_t) * moe::DEC_SYNC_WORDS);
@@ -155,7 +157,7 @@ moe::LayerArgs make_args(const moe_layer* L, const void* x, int T, char* ws, con
   a.tiles = (moe::Item*)(ws + W.tiles);
   a.ctl = (int32_t*)(ws + W.ctl);
   a.h = (void*)(ws + W.h);
-  a.y = (float*)(ws + W.y);
+  a.y = (void*)(ws + W.y);
   a.xsc = (float*)(ws + W.xsc);
   a.hslot = (float*)(ws + W.hslot);
   a.max_tiles = W.max_tiles;

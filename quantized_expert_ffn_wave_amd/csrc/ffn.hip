@@ -126,6 +126,13 @@ template <int FMT> constexpr bool OPER_F16 = FMT != FMT_BF16;
 // scaled fp16 operands (the scale is found from the whole row, after every
 // gate/up item has written it), bf16 for bf16 weights.
 template <int FMT> using HElem = std::conditional_t<OPER_F16<FMT>, float, uint16_t>;
+// Element of the expert outputs y: fp32 for the 4-bit formats, bf16 bits for
+// bf16 weights (rounded once, RNE; the combine sums 7 of them in fp32).
+template <int FMT> using YElem = std::conditional_t<OPER_F16<FMT>, float, uint16_t>;
+template <int FMT> __device__ inline void store_y(const LayerArgs& a, uint32_t off, float v) {
+  if constexpr (OPER_F16<FMT>) static_cast<float*>(a.y)[off] = v;
+  else static_cast<uint16_t*>(a.y)[off] = f32_to_bf16(v);
+}
 
 // ======================================================================================
 // Per-format chunk of a weight row: 32 consecutive elements of one row, the
@@ -833,7 +840,7 @@ __device__ void down_stream(const LayerArgs& a, int base, int n, int n_mf, MvSme
         float v = mv_reduce8(acc[0], acc[1]);
         if (FMT == FMT_NVFP4) v *= w.tsg;
         if constexpr (OPER_F16<FMT>) v *= isc;
-        if (writer) a.y[yoff + 4 * (u - 1)] = v;
+        if (writer) store_y<FMT>(a, yoff + 4 * (u - 1), v);
       }
     }
     if (!has_next) break;
@@ -1155,9 +1162,17 @@ __device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const Item
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = r0 + 64 * wave + 32 * b + 8 * i + 4 * h;
-        *reinterpret_cast<float4*>(a.y + (size_t)yrow * D_MODEL + r) =
-            make_float4(acc[b][tt][4 * i] * ts, acc[b][tt][4 * i + 1] * ts, acc[b][tt][4 * i + 2] * ts,
-                        acc[b][tt][4 * i + 3] * ts);
+        const size_t off = (size_t)yrow * D_MODEL + r;
+        if constexpr (OPER_F16<FMT>) {
+          *reinterpret_cast<float4*>(static_cast<float*>(a.y) + off) =
+              make_float4(acc[b][tt][4 * i] * ts, acc[b][tt][4 * i + 1] * ts, acc[b][tt][4 * i + 2] * ts,
+                          acc[b][tt][4 * i + 3] * ts);
+        } else {
+          uint2 pk;
+          pk.x = (uint32_t)f32_to_bf16(acc[b][tt][4 * i] * ts) | ((uint32_t)f32_to_bf16(acc[b][tt][4 * i + 1] * ts) << 16);
+          pk.y = (uint32_t)f32_to_bf16(acc[b][tt][4 * i + 2] * ts) | ((uint32_t)f32_to_bf16(acc[b][tt][4 * i + 3] * ts) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.y) + off) = pk;
+        }
       }
     }
   }
@@ -1345,14 +1360,25 @@ __device__ inline void combine_token(const LayerArgs& a, int t) {
       wj[j] = a.w[(size_t)t * K + j];
     }
   }
+  // (fp32 rows, or bf16 rows for bf16 weights: the branch is uniform)
+  const bool ybf = a.fmt == FMT_BF16;
   float4 v[MAX_K + 1][2];
 #pragma unroll
   for (int j = 0; j <= MAX_K; ++j) {
     const bool sh = (j == MAX_K);
     if (sh ? a.n_shared != 0 : j < K) {
-      const float4* p = reinterpret_cast<const float4*>(a.y + (size_t)(sh ? a.S + t : pos[j]) * D_MODEL + i0);
-      v[j][0] = p[0];
-      v[j][1] = p[1];
+      const size_t off = (size_t)(sh ? a.S + t : pos[j]) * D_MODEL + i0;
+      if (ybf) {
+        const u32x4 q = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.y) + off);
+        v[j][0] = make_float4(__uint_as_float(q[0] << 16), __uint_as_float(q[0] & 0xFFFF0000u),
+                              __uint_as_float(q[1] << 16), __uint_as_float(q[1] & 0xFFFF0000u));
+        v[j][1] = make_float4(__uint_as_float(q[2] << 16), __uint_as_float(q[2] & 0xFFFF0000u),
+                              __uint_as_float(q[3] << 16), __uint_as_float(q[3] & 0xFFFF0000u));
+      } else {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.y) + off);
+        v[j][0] = p[0];
+        v[j][1] = p[1];
+      }
     }
   }
   float o[8];
