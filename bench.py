@@ -57,6 +57,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense f16 / bf16 matrix-core peak
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 STREAM_BYTES = 4 << 30
 SWEEP_T = [1, 2, 4, 8, 16, 32, 64, 128, 256]
@@ -84,22 +85,33 @@ def kernel_source_hash(kernel: str = "ffn_up") -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str, kernel: str = "ffn_up"):
-    """HBM bytes per launch of the roofline kernel (gate/up, or the head) from the
-    committed counter summary, if it was taken on the current kernel source
-    (else None)."""
+def read_counter_summary(workload: str, kernel: str = "ffn_up") -> dict:
+    """Fields of the committed counter summary of the roofline kernel (gate/up,
+    or the head), if it was taken on the current kernel source (else {})."""
     path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
-        return None
+        return {}
     kv = {}
     for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha") != kernel_source_hash(kernel):
-        return None
+    return kv if kv.get("kernel_source_sha") == kernel_source_hash(kernel) else {}
+
+
+def read_traffic(workload: str, kernel: str = "ffn_up"):
+    """HBM bytes per launch of the roofline kernel from the counter summary (or None)."""
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(read_counter_summary(workload, kernel)["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def read_mfma_busy(workload: str, kernel: str = "ffn_up"):
+    """Matrix-core busy fraction of the roofline kernel from the counter summary
+    (SQ_VALU_MFMA_BUSY_CYCLES over the SIMD cycles of GRBM_GUI_ACTIVE), or None."""
+    try:
+        return float(read_counter_summary(workload, kernel)["mfma_busy"])
     except (KeyError, ValueError):
         return None
 
@@ -291,6 +303,7 @@ def bench_layer(args, moe, synth, torch, np):
     stage_ms = np.array([[row[j].elapsed_time(row[j + 1]) for j in range(moe.N_STAGE_EVENTS - 1)] for row in evs])
     idx = [(args.warmup + i) % P for i in range(args.steps)]
     up_ms = stage_ms[:, moe.STAGES.index("gate_up")]
+    up_flops = 2.0 * (T * K + T) * 2 * 512 * 2048  # gate and up products of every slot
     up_achieved = sum(up_bytes[j] for j in idx) / (up_ms.sum() * 1e-3) / 1e9
     step_ms = graph_ms if graph_ms is not None else ms
     # the timed steps: pairs 0, 1, ... in the graph, warmup, warmup + 1, ... in plain launches
@@ -396,6 +409,14 @@ def bench_layer(args, moe, synth, torch, np):
                      "frac": round(up_achieved / HBM_PEAK_GBPS, 4),
                      "frac_of_stream_read": round(up_achieved / stream_ref["gbps"], 4) if stream_ref else None,
                      "traffic": traffic},
+        # the same kernel against the matrix cores: algorithmic products (both
+        # matrices over every slot, routed and shared) per event-timed launch,
+        # and the busy fraction the committed counter summary measured
+        "mfma": {"kernel": "ffn_up_kernel", "operands": "bf16" if fmt == "bf16" else "f16",
+                 "achieved_tflops": round(up_flops * len(idx) / (up_ms.sum() * 1e-3) / 1e12, 2),
+                 "peak_tflops": MFMA_PEAK_TFLOPS,
+                 "frac": round(up_flops * len(idx) / (up_ms.sum() * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+                 "mfma_util": read_mfma_busy(args.workload)},
         "cpu_baseline": cpu,
     }
     if sweep is not None:
@@ -505,6 +526,7 @@ def bench_stack(args, moe, synth, torch, np):
     torch.cuda.synchronize()
     stage_ms = np.array([[row[j].elapsed_time(row[j + 1]) for j in range(moe.N_STAGE_EVENTS - 1)] for row in evs])
     up_ms = stage_ms[:, moe.STAGES.index("gate_up")]
+    up_flops = 2.0 * (T * K + T) * 2 * 512 * 2048  # gate and up products of every slot
     up_achieved = n_rep * sum(up_bytes) / (up_ms.sum() * 1e-3) / 1e9
     stage_means = {n: round(float(v), 4) for n, v in zip(moe.STAGES, stage_ms.mean(0))}
     log(f"per-layer stage means (ms): {stage_means}")
@@ -532,6 +554,8 @@ def bench_stack(args, moe, synth, torch, np):
         d.close()
     del dls, ws, wsl, x, x0, y, xin, rb
     torch.cuda.empty_cache()
+    if args.copy_calibration:
+        copy_calibration(torch)
     stream_ref = None if args.no_stream_reference else stream_reference(moe, torch)
 
     return {
