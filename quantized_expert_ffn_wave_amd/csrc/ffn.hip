@@ -886,8 +886,12 @@ static_assert(MF_XK<64> % 16 == 0 && MF_XK<128> % 16 == 0, "activations are stag
 static_assert(DN_ROWS == 4 * 64, "down items: 4 waves x 2 row blocks of 32 rows");
 static_assert(D_MODEL % (64 * 4) == 0 && D_FF % (64 * 4) == 0, "the chunk loop is unrolled by up to 4");
 
-template <int BN> struct FfnSmem {
+// bf16 weights reach the matrix cores through LDS (mf_kloop_bf16): a block of
+// 64 rows x one K-chunk per wave (single-buffered: only its own wave uses it).
+template <int FMT> constexpr int MF_WL_ROWS = (FMT == FMT_BF16) ? 64 : 1;
+template <int FMT, int BN> struct FfnSmem {
   uint16_t x[2][BN * TS];  // K-chunks alternate between the two, so one barrier per chunk suffices
+  uint16_t w[4][MF_WL_ROWS<FMT> * TS];  // bf16 weights: each wave's rows of the current K-chunk
   int tok[BN];
   int row[BN];
   float sc[BN];            // 4-bit formats: activation scale per token column (down: from |h|)
@@ -924,7 +928,7 @@ __device__ inline f32x16 mfma32(u32x4 av, u32x4 bv, f32x16 c) {
 // (h), from the maximum over the row's 32 |h| slots, read by 256 / BN threads
 // per token column and reduced over them.
 template <int FMT, bool UP, int BN>
-__device__ inline void mfma_tables(const LayerArgs& a, const ItemTok& it, FfnSmem<BN>& sm) {
+__device__ inline void mfma_tables(const LayerArgs& a, const ItemTok& it, FfnSmem<FMT, BN>& sm) {
   const int i = threadIdx.x;
   if (i < BN) {
     // matrix-core tiles are shared-expert tiles or routed buckets (tokens via perm)
@@ -976,7 +980,7 @@ template <int FMT, int BN, int RB, bool XF32> struct MfStage {
 // column only meets its own activations); xscale: that row's activation scale
 // (4-bit formats).
 template <int FMT, int BN, int RB, int NS, bool XF32 = false>
-__device__ inline void mf_kloop(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<BN>& sm, const QMat (&q)[RB],
+__device__ inline void mf_kloop(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<FMT, BN>& sm, const QMat (&q)[RB],
                                 const size_t (&wrow)[RB], const void* xsrc, float xscale, int kdim) {
   using Stage = MfStage<FMT, BN, RB, XF32>;
   constexpr int NX = MF_XK<BN> / (XF32 ? 4 : 8);  // 16-byte activation loads per thread and chunk
@@ -1054,10 +1058,90 @@ __device__ inline void mf_kloop(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<BN>& sm, c
   }
 }
 
+// bf16 weights: acc[b][tt] += W_block_b x X over K = kdim with both operands
+// staged in LDS.  Every global load is line-friendly: a lane loads 16 bytes and 8
+// lanes cover one 128-byte piece (64 K-elements) of a row, so one load
+// instruction reads 8 whole cache lines: 8 of the wave's 32 RB weight rows, or 8
+// of the tile's tokens.  (Loading each lane's own MFMA operand instead touches
+// 32 rows per instruction, which streams from HBM at half the rate.)  The
+// weights are regrouped into the A layout through the wave's LDS block, the
+// activations through the shared tile as in mf_kloop; chunk j's global loads are
+// issued NS - 1 chunks ahead.  xbase + xrow[t] * kdim: the bf16 row of tile
+// token t (xrow in LDS, rows past cnt repeat a valid one; their columns are
+// never stored).  The wave's 32 RB weight rows are two halves of 16 RB
+// consecutive rows each, starting at rows wh[0] and wh[1] (gate and up rows of
+// the same outputs, or two blocks of down rows); wave row r sits in LDS row r,
+// so block b of the A operand is LDS rows 32 b ..
+template <int BN, int RB, int NS>
+__device__ inline void mf_kloop_bf16(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<FMT_BF16, BN>& sm,
+                                     const uint16_t* const (&wh)[2], const uint16_t* xbase, const int* xrow, int cnt,
+                                     int kdim) {
+  constexpr int NW = 4 * RB;   // weight loads per lane and chunk: wave rows 8 i + lane / 8
+  constexpr int HR = 16 * RB;  // rows per half
+  constexpr int NX = BN / 32;  // activation loads per thread and chunk: tokens 32 i + 8 wave + lane / 8
+  static_assert(NS % 2 == 0, "chunk j uses activation buffer j % 2");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, c = lane & 31, sub = lane >> 3, part = lane & 7;
+  const int nc = kdim / 64;
+  uint16_t* wl = sm.w[wave];
+  const uint16_t* wp[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) wp[g] = wh[g] + (size_t)sub * kdim + 8 * part;
+  uint32_t xo[NX];
+#pragma unroll
+  for (int i = 0; i < NX; ++i) xo[i] = (uint32_t)xrow[min(32 * i + 8 * wave + sub, cnt - 1)] * (uint32_t)kdim + 8u * part;
+  struct Stage {
+    u32x4 w[NW];
+    u32x4 x[NX];
+  };
+  auto fetch = [&](Stage& st, int ck) {
+    ck = min(ck, nc - 1);  // past the last chunk the last one is loaded again (exact wait counts)
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+      st.w[i] = ld16<true>(wp[(8 * i) / HR] + (size_t)((8 * i) % HR) * kdim + 64 * ck);
+#pragma unroll
+    for (int i = 0; i < NX; ++i) st.x[i] = ld16<false>(xbase + xo[i] + 64 * ck);
+  };
+  auto stage = [&](const Stage& st, uint16_t* buf) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) *reinterpret_cast<u32x4*>(wl + (8 * i + sub) * TS + 8 * part) = st.w[i];
+#pragma unroll
+    for (int i = 0; i < NX; ++i) *reinterpret_cast<u32x4*>(buf + (32 * i + 8 * wave + sub) * TS + 8 * part) = st.x[i];
+  };
+  auto multiply = [&](const uint16_t* buf) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 av[RB];
+#pragma unroll
+      for (int b = 0; b < RB; ++b) av[b] = *reinterpret_cast<const u32x4*>(wl + (32 * b + c) * TS + 32 * h + 8 * s);
+#pragma unroll
+      for (int tt = 0; tt < MF_TT<BN>; ++tt) {
+        const u32x4 bv = *reinterpret_cast<const u32x4*>(buf + (32 * tt + c) * TS + 32 * h + 8 * s);
+#pragma unroll
+        for (int b = 0; b < RB; ++b) acc[b][tt] = mfma32<FMT_BF16>(av[b], bv, acc[b][tt]);
+      }
+    }
+  };
+  Stage st[NS];
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) fetch(st[i], i);
+#pragma unroll 1
+  for (int ck0 = 0; ck0 < nc; ck0 += NS) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      __builtin_amdgcn_sched_barrier(0);
+      stage(st[j], sm.x[j & 1]);
+      fetch(st[(j + NS - 1) % NS], ck0 + j + NS - 1);
+      __syncthreads();
+      multiply(sm.x[j & 1]);
+    }
+  }
+}
+
 // gate/up item: 32 MF_UP_RB row pairs per wave (n0 ..) x BN tokens.
 template <int FMT, int BN>
 __device__ void mfma_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int mat, const ItemTok& it, int n0,
-                        FfnSmem<BN>& sm) {
+                        FfnSmem<FMT, BN>& sm) {
   constexpr int RB = MF_UP_RB<BN>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c = lane & 31;
@@ -1077,7 +1161,15 @@ __device__ void mfma_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int m
   const uint16_t* xsrc = a.x + (size_t)xtok * D_MODEL + MF_XK<BN> * (tid % MF_XT<BN>);
   const float xscale = OPER_F16<FMT> ? a.xsc[xtok] : 1.f;
   f32x16 acc[RB][MF_TT<BN>] = {};
-  mf_kloop<FMT, BN, RB, MF_NS_UP<FMT, BN>>(acc, sm, q, wrow, xsrc, xscale, D_MODEL);
+  if constexpr (FMT == FMT_BF16) {
+    // the wave's gate rows and up rows of the same outputs
+    const size_t r = (size_t)mat * D_FF + n0 + 16 * RB * wave;
+    const uint16_t* const wh[2] = {reinterpret_cast<const uint16_t*>(G.codes) + r * D_MODEL,
+                                   reinterpret_cast<const uint16_t*>(Uq.codes) + r * D_MODEL};
+    mf_kloop_bf16<BN, RB, MF_NS_UP<FMT, BN>>(acc, sm, wh, a.x, sm.tok, it.cnt, D_MODEL);
+  } else {
+    mf_kloop<FMT, BN, RB, MF_NS_UP<FMT, BN>>(acc, sm, q, wrow, xsrc, xscale, D_MODEL);
+  }
   // acc[b][tt][4i+j] = row 8i + 4h + j of block b, token 32tt + c.  The gate
   // value of a lane's output (block 0 / rows below 16) sits at gi, its up at ui.
   const float tsg = (FMT == FMT_NVFP4) ? G.ts[mat] : 1.f;
@@ -1137,7 +1229,8 @@ __device__ void mfma_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int m
 
 // down item: DN_ROWS rows (r0 ..) x BN tokens, K = 512.
 template <int FMT, int BN>
-__device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const ItemTok& it, int r0, FfnSmem<BN>& sm) {
+__device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const ItemTok& it, int r0,
+                          FfnSmem<FMT, BN>& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c = lane & 31;
   mfma_tables<FMT, false>(a, it, sm);
@@ -1150,7 +1243,13 @@ __device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const Item
       static_cast<const HElem<FMT>*>(a.h) + (size_t)hrow_x * D_FF + MF_XK<BN> * (tid % MF_XT<BN>);
   const float xscale = OPER_F16<FMT> ? sm.sc[min(tid / MF_XT<BN>, it.cnt - 1)] : 1.f;
   f32x16 acc[2][MF_TT<BN>] = {};
-  mf_kloop<FMT, BN, 2, MF_NS_DN<FMT, BN>, OPER_F16<FMT>>(acc, sm, q, wrow, xsrc, xscale, D_FF);
+  if constexpr (FMT == FMT_BF16) {
+    const uint16_t* w0 = reinterpret_cast<const uint16_t*>(D.codes) + (wr - (size_t)c) * D_FF;
+    const uint16_t* const wh[2] = {w0, w0 + (size_t)32 * D_FF};
+    mf_kloop_bf16<BN, 2, MF_NS_DN<FMT, BN>>(acc, sm, wh, static_cast<const uint16_t*>(a.h), sm.row, it.cnt, D_FF);
+  } else {
+    mf_kloop<FMT, BN, 2, MF_NS_DN<FMT, BN>, OPER_F16<FMT>>(acc, sm, q, wrow, xsrc, xscale, D_FF);
+  }
   const float tsd = (FMT == FMT_NVFP4) ? D.ts[mat] : 1.f;
 #pragma unroll
   for (int tt = 0; tt < MF_TT<BN>; ++tt) {
@@ -1193,13 +1292,13 @@ constexpr int MF_WG_PER_CU = 2;
 // LDS of the persistent kernels: the matrix-core tiles (BN tokens wide) only
 // where the batch can have them (BN > 0: T >= mfma_min(T)), since their double
 // buffer would otherwise cost the vector path occupancy.
-template <int BN> struct FfnKernelSmem {
+template <int FMT, int BN> struct FfnKernelSmem {
   union {
-    FfnSmem<BN> mf;
+    FfnSmem<FMT, BN> mf;
     MvSmem gv;
   };
 };
-template <> struct FfnKernelSmem<0> {
+template <int FMT> struct FfnKernelSmem<FMT, 0> {
   MvSmem gv;
 };
 
@@ -1223,7 +1322,7 @@ static_assert(MFMA_MIN > VEC_SMALL_T && MFMA_MIN_WIDE > VEC_SMALL_T,
               "batches with smaller vector items have no matrix-core tiles");
 template <int FMT, int BN, int VR>
 __global__ __launch_bounds__(256, (FFN_WG_PER_CU<FMT, BN>)) void ffn_up_kernel(LayerArgs a) {
-  __shared__ FfnKernelSmem<BN> sm;
+  __shared__ FfnKernelSmem<FMT, BN> sm;
   // matrix-core items: mf_up_chunks(BN) per tile; vector-path items: D_FF / VR per tile
   const int n_all = a.ctl[CTL_N_UP], n_mf = a.ctl[CTL_N_UP_MF];
   constexpr int UC = (BN > 0) ? mf_up_chunks(BN) : 1;
@@ -1241,7 +1340,7 @@ __global__ __launch_bounds__(256, (FFN_WG_PER_CU<FMT, BN>)) void ffn_up_kernel(L
 
 template <int FMT, int BN, int VDR>
 __global__ __launch_bounds__(256, (FFN_WG_PER_CU<FMT, BN>)) void ffn_down_kernel(LayerArgs a) {
-  __shared__ FfnKernelSmem<BN> sm;
+  __shared__ FfnKernelSmem<FMT, BN> sm;
   const int n_all = a.ctl[CTL_N_DN], n_mf = a.ctl[CTL_N_DN_MF];
   if constexpr (BN > 0) {
     for (int i = blockIdx.x; i < n_mf; i += gridDim.x) {
