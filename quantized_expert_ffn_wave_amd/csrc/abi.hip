@@ -77,7 +77,7 @@ moe_status check_qmat(const moe_qmat& q, int fmt, const char* name) {
 }
 
 struct WsLayout {
-  size_t logit_part, logits, ids, w, counts, offsets, perm, inv_perm, tiles, ctl, h, y, xsc, hslot, sync, total;
+  size_t logit_part, logits, ids, w, counts, offsets, perm, inv_perm, tiles, ctl, h, y, xsc, xq, hslot, sync, total;
   int max_tiles;
 };
 
@@ -109,6 +109,8 @@ WsLayout ws_layout(const moe_layer_desc& d, int T) {
   // prefill volume: 7 rows of 2048 per token)
   L.y = take((d.wfmt == MOE_W_BF16 ? sizeof(uint16_t) : sizeof(float)) * R * moe::D_MODEL);
   L.xsc = take(sizeof(float) * (size_t)T);
+  // 4-bit formats: the scaled fp16 activations the matrix-core tiles read
+  L.xq = take(d.wfmt == MOE_W_BF16 ? 0 : sizeof(uint16_t) * (size_t)T * moe::D_MODEL);
   L.hslot = take(sizeof(float) * moe::HSLOTS * R);
   L.sync = take(sizeof(uint32_t) * moe::DEC_SYNC_WORDS);
   L.total = o;
@@ -159,6 +161,7 @@ moe::LayerArgs make_args(const moe_layer* L, const void* x, int T, char* ws, con
   a.h = (void*)(ws + W.h);
   a.y = (void*)(ws + W.y);
   a.xsc = (float*)(ws + W.xsc);
+  a.xq = (uint16_t*)(ws + W.xq);
   a.hslot = (float*)(ws + W.hslot);
   a.max_tiles = W.max_tiles;
   return a;

@@ -126,6 +126,7 @@ struct LayerArgs {
   // |h| of each 16 columns' slot, written by the gate/up item that computes
   // those columns (each slot exactly once per forward) and read by down
   float* xsc;               // [T]
+  uint16_t* xq;             // [T][D_MODEL] fp16 bits: x times xsc, in the weights' k order (matrix-core tiles)
   float* hslot;             // [S + n_shared*T][HSLOTS]
   int max_tiles;
   // combine targets

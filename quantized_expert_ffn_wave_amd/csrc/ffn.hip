@@ -886,9 +886,10 @@ static_assert(MF_XK<64> % 16 == 0 && MF_XK<128> % 16 == 0, "activations are stag
 static_assert(DN_ROWS == 4 * 64, "down items: 4 waves x 2 row blocks of 32 rows");
 static_assert(D_MODEL % (64 * 4) == 0 && D_FF % (64 * 4) == 0, "the chunk loop is unrolled by up to 4");
 
-// bf16 weights reach the matrix cores through LDS (mf_kloop_bf16): a block of
-// 64 rows x one K-chunk per wave (single-buffered: only its own wave uses it).
-template <int FMT> constexpr int MF_WL_ROWS = (FMT == FMT_BF16) ? 64 : 1;
+// Weights reach the matrix cores through LDS (mf_kloop_bf16, mf_kloop_q): a
+// block of 64 rows x 128 bytes per wave (one K-chunk of bf16, four of the 4-bit
+// codes), single-buffered: only its own wave uses it.
+template <int FMT> constexpr int MF_WL_ROWS = 64;
 template <int FMT, int BN> struct FfnSmem {
   uint16_t x[2][BN * TS];  // K-chunks alternate between the two, so one barrier per chunk suffices
   uint16_t w[4][MF_WL_ROWS<FMT> * TS];  // bf16 weights: each wave's rows of the current K-chunk
@@ -1138,6 +1139,114 @@ __device__ inline void mf_kloop_bf16(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<FMT_B
   }
 }
 
+// 4-bit weights, gate/up: the same scheme as mf_kloop_bf16 for the codes and
+// the activations.  The activations come pre-scaled in fp16 and in the weights'
+// k order (xq), so they are copied as they are.  The codes move in groups of
+// four K-chunks (128 bytes of a row, one line-friendly load per 8 rows and
+// lane), each group staged into the wave's LDS block while the next one is
+// loaded; a lane then reads its 16 bytes of a chunk from there and decodes them
+// as mf_kloop does.  The block scales are loaded per lane, 3 chunks ahead.
+// q[b], wrow[b]: the lane's matrix and row of block b (for its scales).
+template <int FMT, int BN, int RB, int NSX>
+__device__ inline void mf_kloop_q(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<FMT, BN>& sm, const QMat (&q)[RB],
+                                  const size_t (&wrow)[RB], const uint8_t* const (&wh)[2], const uint16_t* xbase,
+                                  const int* xrow, int cnt) {
+  constexpr int kdim = D_MODEL;
+  constexpr int RBYTES = kdim / 2;  // codes per row
+  constexpr int NW = 4 * RB;        // code loads per lane and group: wave rows 8 i + lane / 8
+  constexpr int HR = 16 * RB;       // rows per half
+  constexpr int NX = BN / 32;       // activation loads per thread and chunk
+  constexpr int NC = kdim / 64, NG = NC / 4;
+  static_assert(NSX == 2 || NSX == 4, "activation ring of 2 or 4 chunks");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, c = lane & 31, sub = lane >> 3, part = lane & 7;
+  uint8_t* wl = reinterpret_cast<uint8_t*>(sm.w[wave]);
+  constexpr int WS = TS * 2;  // LDS bytes per weight row
+  const uint8_t* wp[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) wp[g] = wh[g] + (size_t)sub * RBYTES + 16 * part;
+  uint32_t xo[NX];
+#pragma unroll
+  for (int i = 0; i < NX; ++i) xo[i] = (uint32_t)xrow[min(32 * i + 8 * wave + sub, cnt - 1)] * (uint32_t)kdim + 8u * part;
+  u32x4 wst[NW];
+  u32x4 xst[NSX][NX];
+  uint32_t sst[4][RB];
+  auto fetch_w = [&](int g) {
+    g = min(g, NG - 1);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) wst[i] = ld16<true>(wp[(8 * i) / HR] + (size_t)((8 * i) % HR) * RBYTES + 128 * g);
+  };
+  auto stage_w = [&]() {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) *reinterpret_cast<u32x4*>(wl + (8 * i + sub) * WS + 16 * part) = wst[i];
+  };
+  auto fetch_x = [&](u32x4 (&st)[NX], int ck) {
+    ck = min(ck, NC - 1);
+#pragma unroll
+    for (int i = 0; i < NX; ++i) st[i] = ld16<false>(xbase + xo[i] + 64 * ck);
+  };
+  auto stage_x = [&](const u32x4 (&st)[NX], uint16_t* buf) {
+#pragma unroll
+    for (int i = 0; i < NX; ++i) *reinterpret_cast<u32x4*>(buf + (32 * i + 8 * wave + sub) * TS + 8 * part) = st[i];
+  };
+  auto fetch_s = [&](uint32_t (&st)[RB], int ck) {
+    ck = min(ck, NC - 1);
+    // block 2 ck + h of a row of 2048: stored at 8 (ck mod 8) + 4 h + ck / 8
+    const uint32_t slot = 8u * (uint32_t)(ck & 7) + 4u * (uint32_t)h + (uint32_t)(ck >> 3);
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      if constexpr (FMT == FMT_Q4_1)
+        st[b] = ld4<false>(reinterpret_cast<const uint32_t*>(q[b].scales) + wrow[b] * (kdim / 32) + slot);
+      else
+        st[b] = ld2<false>(reinterpret_cast<const uint8_t*>(q[b].scales) + wrow[b] * (kdim / 16) + 2 * slot);
+    }
+  };
+  auto multiply = [&](int cg, const uint32_t (&sc)[RB], const uint16_t* buf) {
+    uint32_t wv[RB][16];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      typename GV<FMT>::Raw r;
+      r.c = *reinterpret_cast<const u32x4*>(wl + (32 * b + c) * WS + 32 * cg + 16 * h);
+      if constexpr (FMT == FMT_Q4_1) r.dm = sc[b];
+      else r.s = sc[b];
+      GV<FMT>::decode(r, wv[b]);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int tt = 0; tt < MF_TT<BN>; ++tt) {
+        const u32x4 bv = *reinterpret_cast<const u32x4*>(buf + (32 * tt + c) * TS + 32 * h + 8 * s);
+#pragma unroll
+        for (int b = 0; b < RB; ++b)
+          acc[b][tt] = mfma32<FMT>(u32x4{wv[b][4 * s], wv[b][4 * s + 1], wv[b][4 * s + 2], wv[b][4 * s + 3]}, bv,
+                                   acc[b][tt]);
+      }
+    }
+  };
+  fetch_w(0);
+#pragma unroll
+  for (int i = 0; i < NSX - 1; ++i) fetch_x(xst[i], i);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) fetch_s(sst[i], i);
+#pragma unroll 1
+  for (int g = 0; g < NG; ++g) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ck = 4 * g + j;
+      __builtin_amdgcn_sched_barrier(0);
+      if (j == 0) {
+        stage_w();      // the previous group's chunks are multiplied (this wave, in order)
+        fetch_w(g + 1);
+      }
+      stage_x(xst[j % NSX], sm.x[j & 1]);
+      fetch_x(xst[(j + NSX - 1) % NSX], ck + NSX - 1);
+      fetch_s(sst[(j + 3) % 4], ck + 3);
+      __syncthreads();
+      multiply(j, sst[j], sm.x[j & 1]);
+    }
+  }
+}
+
 // gate/up item: 32 MF_UP_RB row pairs per wave (n0 ..) x BN tokens.
 template <int FMT, int BN>
 __device__ void mfma_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int mat, const ItemTok& it, int n0,
@@ -1167,7 +1276,12 @@ __device__ void mfma_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int m
     const uint16_t* const wh[2] = {reinterpret_cast<const uint16_t*>(G.codes) + r * D_MODEL,
                                    reinterpret_cast<const uint16_t*>(Uq.codes) + r * D_MODEL};
     mf_kloop_bf16<BN, RB, MF_NS_UP<FMT, BN>>(acc, sm, wh, a.x, sm.tok, it.cnt, D_MODEL);
+  } else if constexpr (BN == 64) {
+    const size_t r = (size_t)mat * D_FF + n0 + 16 * RB * wave;
+    const uint8_t* const wh[2] = {G.codes + r * (D_MODEL / 2), Uq.codes + r * (D_MODEL / 2)};
+    mf_kloop_q<FMT, BN, RB, 4>(acc, sm, q, wrow, wh, a.xq, sm.tok, it.cnt);
   } else {
+    // (128-token tiles: the staged loop's registers do not fit two waves per SIMD)
     mf_kloop<FMT, BN, RB, MF_NS_UP<FMT, BN>>(acc, sm, q, wrow, xsrc, xscale, D_MODEL);
   }
   // acc[b][tt][4i+j] = row 8i + 4h + j of block b, token 32tt + c.  The gate

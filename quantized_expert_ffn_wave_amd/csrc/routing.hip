@@ -172,19 +172,38 @@ __device__ void topk_token(const LayerArgs& a, int t, int32_t* lds_ids) {
     for (int ks = 0; ks < KS; ++ks) p[i][ks] = a.logit_part[((size_t)ks * T + t) * E + e];
   }
   // 4-bit formats: the token's activation scale for the fp16 operands of the
-  // expert products, from the largest |x| of its row (32 elements per lane)
+  // expert products, from the largest |x| of its row (32 elements per lane),
+  // and the row scaled into fp16 for the matrix-core tiles, in the weights' k
+  // order: natural for NVFP4; for q4_1, within each group of 8 elements the
+  // order 0 4 1 5 2 6 3 7 in which its nibble decode delivers the weights
   if (a.fmt != FMT_BF16) {
     const uint4* xr = reinterpret_cast<const uint4*>(a.x + (size_t)t * D_MODEL) + 4 * lane;
+    uint4 xv[4];
     uint32_t mx = 0u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint4 v = xr[i];
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+      xv[i] = xr[i];
+      const uint32_t w4[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) mx = max(mx, max(w4[q] & 0x7FFFu, (w4[q] >> 16) & 0x7FFFu));
     }
     mx = wave_max_u32(mx);
-    if (lane == 0) a.xsc[t] = pow2_scale(mx << 16);
+    const float sc = pow2_scale(mx << 16);
+    if (lane == 0) a.xsc[t] = sc;
+    uint4* dst = reinterpret_cast<uint4*>(a.xq + (size_t)t * D_MODEL) + 4 * lane;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w4[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+      uint32_t n[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        n[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w4[q] << 16) * sc,
+                                                                     __uint_as_float(w4[q] & 0xFFFF0000u) * sc));
+      if (a.fmt == FMT_Q4_1)
+        dst[i] = make_uint4(__builtin_amdgcn_perm(n[2], n[0], 0x05040100u), __builtin_amdgcn_perm(n[2], n[0], 0x07060302u),
+                            __builtin_amdgcn_perm(n[3], n[1], 0x05040100u), __builtin_amdgcn_perm(n[3], n[1], 0x07060302u));
+      else dst[i] = make_uint4(n[0], n[1], n[2], n[3]);
+    }
   }
   uint32_t kk[4];
   float mx = -INFINITY;
