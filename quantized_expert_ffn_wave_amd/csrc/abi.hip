@@ -164,7 +164,6 @@ moe::LayerArgs make_args(const moe_layer* L, const void* x, int T, char* ws, con
   a.xq = (uint16_t*)(ws + W.xq);
   a.hslot = (float*)(ws + W.hslot);
   a.max_tiles = W.max_tiles;
-  a.sync = (uint32_t*)(ws + W.sync);
   return a;
 }
 

@@ -88,11 +88,9 @@ __device__ inline bool item_mfma(uint32_t h) { return (h & ITEM_MFMA) != 0; }
 
 // ---- control block ------------------------------------------------------------------
 enum Ctl : int { CTL_N_UP = 0, CTL_N_DN = 1, CTL_N_UP_MF = 2, CTL_N_DN_MF = 3, CTL_WORDS = 16 };
-// hand-off words (workspace): the persistent decode path's (cleared by its
-// first launch) and the kernel chain's top-k arrival counter (cleared by the
-// router launch before it)
-enum DecSync : int { DEC_SYNC_TOPK = 0, DEC_SYNC_B1 = 1, DEC_SYNC_B2 = 2, DEC_SYNC_B3 = 3, DEC_SYNC_CHAIN_TOPK = 4,
-                     DEC_SYNC_TIMEOUT = 15, DEC_SYNC_WORDS = 16 };
+// hand-off words of the persistent decode path (workspace; cleared by its first launch)
+enum DecSync : int { DEC_SYNC_TOPK = 0, DEC_SYNC_B1 = 1, DEC_SYNC_B2 = 2, DEC_SYNC_B3 = 3, DEC_SYNC_TIMEOUT = 15,
+                     DEC_SYNC_WORDS = 16 };
 
 struct QMat {
   const uint8_t* codes;   // q4_1/nvfp4 nibbles or bf16 elements
@@ -131,7 +129,6 @@ struct LayerArgs {
   uint16_t* xq;             // [T][D_MODEL] fp16 bits: x times xsc, in the weights' k order (matrix-core tiles)
   float* hslot;             // [S + n_shared*T][HSLOTS]
   int max_tiles;
-  uint32_t* sync;           // [DEC_SYNC_WORDS] hand-off words
   // combine targets
   uint16_t* out;            // bf16 [T][D_MODEL] layer output (single layer), or null
   float* r;                 // fp32 [T][D_MODEL] residual (stack), or null

@@ -37,6 +37,28 @@ static_assert(!bucket_mfma(DEC_MAX_T, DEC_MAX_T) && !shared_mfma(DEC_MAX_T) && s
               "the persistent path covers exactly the batches without matrix-core tiles");
 constexpr int DEC_SPIN_LIMIT = 1 << 18;  // polls of about 1 us: a wait gives up after about 0.3 s
 
+// This wave's stores are complete, then the workgroup meets: afterwards one
+// thread's agent-scope release covers the whole workgroup's stores.
+__device__ inline void wg_drain() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// The workgroup counts itself into ctr (n arrivals expected); true in every
+// thread of the last workgroup to arrive, after its acquire.
+__device__ inline bool last_arrival(uint32_t* ctr, uint32_t n) {
+  __shared__ uint32_t last;
+  wg_drain();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = (old == n - 1) ? 1u : 0u;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  return last != 0u;
+}
+
 // All n workgroups meet at counter ctr.
 __device__ inline void grid_barrier(uint32_t* ctr, uint32_t n, uint32_t* timeout) {
   wg_drain();
@@ -77,7 +99,7 @@ __global__ __launch_bounds__(256, (FFN_WG_PER_CU<FMT, 0>)) void decode_layer_ker
   if (w < n_tk) {
     const int t = 4 * w + wave;
     if (t < a.T) topk_token<ROUTER_KS>(a, t, nullptr);
-    if (last_arrival(sync + DEC_SYNC_TOPK, (uint32_t)n_tk)) route_small<false, false>(a, sm.rs);
+    if (last_arrival(sync + DEC_SYNC_TOPK, (uint32_t)n_tk)) route_small<false>(a, sm.rs);
   } else if (n_sh > 0) {
     up_stream<FMT, VR>(a, 0, n_sh, 0, sm.gv, w - n_tk, G - n_tk);
   }

@@ -70,13 +70,11 @@ __device__ inline void router_small_tile(const uint16_t* __restrict__ x, const u
   }
 }
 
-// (ctr: the top-k arrival counter of the next launch, cleared here)
 __global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ wr,
                                                            const float* __restrict__ bias, float* __restrict__ part,
-                                                           int T, int E, uint32_t* ctr) {
+                                                           int T, int E) {
   router_small_tile(x, wr, bias, part, T, E, blockIdx.x, blockIdx.y);
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *ctr = 0u;
 }
 
 // Larger T: one 1024-thread workgroup per (64-token group, K-split of 512).
@@ -131,8 +129,7 @@ __global__ __launch_bounds__(1024) void router_large_kernel(const uint16_t* __re
 hipError_t launch_router(const LayerArgs& a, hipStream_t s) {
   if (a.T <= ROUTER_SMALL_T) {
     dim3 grid(ceil_div(a.T, 16) * ceil_div(a.E, 64), ROUTER_KS);
-    hipLaunchKernelGGL(router_small_kernel, grid, dim3(256), 0, s, a.x, a.router_w, a.router_b, a.logit_part, a.T, a.E,
-                       a.sync + DEC_SYNC_CHAIN_TOPK);
+    hipLaunchKernelGGL(router_small_kernel, grid, dim3(256), 0, s, a.x, a.router_w, a.router_b, a.logit_part, a.T, a.E);
   } else {
     dim3 grid(ceil_div(a.T, ROUTER_TG), ROUTER_KS_L);
     hipLaunchKernelGGL(router_large_kernel, grid, dim3(1024), 0, s, a.x, a.router_w, a.router_b, a.logit_part, a.T,
@@ -405,31 +402,6 @@ __device__ void write_lists(const LayerArgs& a, const int* bcnt, const int* boff
   }
 }
 
-// This wave's stores are complete, then the workgroup meets: afterwards one
-// thread's agent-scope release covers the whole workgroup's stores.
-__device__ inline void wg_drain() {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-}
-
-// The workgroup counts itself into ctr (n arrivals expected); true in every
-// thread of the last workgroup to arrive, after its acquire.  (An agent-scope
-// release costs the workgroup an L2 write-back, and the releases of one XCD
-// queue behind each other: worth it for a handful of workgroups, not for a
-// grid.)
-__device__ inline bool last_arrival(uint32_t* ctr, uint32_t n) {
-  __shared__ uint32_t last;
-  wg_drain();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last = (old == n - 1) ? 1u : 0u;
-    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  }
-  __syncthreads();
-  return last != 0u;
-}
-
 // KS: the router's partial splits for this batch size (router_splits(T))
 template <int KS>
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(LayerArgs a) {
@@ -550,7 +522,6 @@ __global__ __launch_bounds__(BK_THREADS) void chunk_perm_kernel(LayerArgs a) {
 constexpr int RS_THREADS = 1024;
 constexpr int RS_MAX_T = 256;
 constexpr int RS_FUSED_T = RS_THREADS / 64;
-constexpr int RS_HANDOFF_T = 64;  // largest batch whose top-k hands the buckets to its last workgroup
 constexpr int RS_WORDS = RS_MAX_T / 32;
 
 struct RouteSmallSmem {
@@ -605,10 +576,7 @@ __device__ inline int wave_inclusive(int v) {
 // take the matrix-core items first; the shared expert's vector items, which
 // mostly read its weights from L2, go before the routed ones so that they do
 // not fall into the last, partial round).
-// SH256: a 256-thread caller that also writes the shared expert's tiles
-// (after the routed ones, with the same threads); otherwise threads 256.. write
-// them, or, with 256 threads, the caller has.
-template <bool TOPK, bool SH256>
+template <bool TOPK>
 __device__ void route_small(const LayerArgs& a, RouteSmallSmem& sm) {
   const int tid = threadIdx.x, nth = blockDim.x, wave = tid >> 6, lane = tid & 63;
   const int E = a.E, K = a.K, T = a.T, S = a.S;
@@ -722,18 +690,10 @@ __device__ void route_small(const LayerArgs& a, RouteSmallSmem& sm) {
   }
   // the shared expert's tiles, on the threads past the experts (a 256-thread
   // caller writes them itself: they do not depend on the routing)
-  if (SH256) {
-    for (int i = tid; i < sh_tiles; i += nth) {
-      const int ti = (sh_mf ? tiles_m : mf_tiles) + i;
-      if (ti >= n_tiles) break;
-      a.tiles[ti] = shared_tile(T, i, sh_mf, bn);
-    }
-  } else {
-    for (int i = tid - 256; i >= 0 && i < sh_tiles; i += nth - 256) {
-      const int ti = (sh_mf ? tiles_m : mf_tiles) + i;
-      if (ti >= n_tiles) break;
-      a.tiles[ti] = shared_tile(T, i, sh_mf, bn);
-    }
+  for (int i = tid - 256; i >= 0 && i < sh_tiles; i += nth - 256) {
+    const int ti = (sh_mf ? tiles_m : mf_tiles) + i;
+    if (ti >= n_tiles) break;
+    a.tiles[ti] = shared_tile(T, i, sh_mf, bn);
   }
 }
 
@@ -741,37 +701,21 @@ template <bool TOPK>
 __global__ __launch_bounds__(RS_THREADS) void route_small_kernel(LayerArgs a) {
   __shared__ RouteSmallSmem sm;
   static_assert(RS_THREADS > 256 && MAX_E <= 256, "experts on the first four waves, shared tiles on the rest");
-  route_small<TOPK, false>(a, sm);
-}
-
-// Batches of RS_FUSED_T + 1 .. RS_HANDOFF_T tokens: the top-k (a wave per
-// token) and the buckets in one launch.  Each workgroup publishes its tokens'
-// ids and counts itself in; the last one to arrive builds the buckets and work
-// lists.  Measured against a top-k launch and a bucket launch: 64 tokens 9.7 ->
-// 8.4 us; at 256 tokens (64 workgroups releasing, the buckets on 256 threads)
-// it lost 2 us, so larger batches keep the two launches.
-__global__ __launch_bounds__(TK_THREADS) void topk_route_kernel(LayerArgs a) {
-  __shared__ RouteSmallSmem sm;
-  static_assert(TK_THREADS == 256 && MAX_E <= 256, "one thread per expert in the bucket phases");
-  const int t = blockIdx.x * (TK_THREADS / 64) + (threadIdx.x >> 6);
-  if (t < a.T) topk_token<ROUTER_KS>(a, t, nullptr);
-  if (last_arrival(a.sync + DEC_SYNC_CHAIN_TOPK, gridDim.x)) route_small<false, true>(a, sm);
+  route_small<TOPK>(a, sm);
 }
 
 // top-k (with the buckets too, for up to RS_FUSED_T tokens)
 hipError_t launch_topk(const LayerArgs& a, hipStream_t s) {
   if (a.T <= RS_FUSED_T) hipLaunchKernelGGL(route_small_kernel<true>, dim3(1), dim3(RS_THREADS), 0, s, a);
-  else if (a.T <= RS_HANDOFF_T)
-    hipLaunchKernelGGL(topk_route_kernel, dim3(ceil_div(a.T, TK_THREADS / 64)), dim3(TK_THREADS), 0, s, a);
   else if (router_splits(a.T) == ROUTER_KS)
     hipLaunchKernelGGL(topk_kernel<ROUTER_KS>, dim3(ceil_div(a.T, TK_THREADS / 64)), dim3(TK_THREADS), 0, s, a);
   else hipLaunchKernelGGL(topk_kernel<ROUTER_KS_L>, dim3(ceil_div(a.T, TK_THREADS / 64)), dim3(TK_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
-// buckets and work lists (up to RS_HANDOFF_T tokens the top-k launch builds them)
+// buckets and work lists (done by the top-k launch for up to RS_FUSED_T tokens)
 hipError_t launch_bucket(const LayerArgs& a, hipStream_t s) {
-  if (a.T <= RS_HANDOFF_T) return hipSuccess;
+  if (a.T <= RS_FUSED_T) return hipSuccess;
   if (a.T <= RS_MAX_T) {
     hipLaunchKernelGGL(route_small_kernel<false>, dim3(1), dim3(RS_THREADS), 0, s, a);
     return hipGetLastError();
