@@ -882,6 +882,63 @@ def bench_mfma_rate(args, moe, torch):
             "published_dense_peaks_tflops": {"f16/bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}}
 
 
+def bench_read_patterns(args, moe, torch):
+    """HBM read rate per access pattern (moe_read_pattern): a 1 GiB buffer read
+    in regions of rows of 1 KB (4-bit rows of 2048) and 4 KB (bf16 rows), on
+    2 and 4 workgroups per CU, best of the two, 5 launches each."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(3)
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    stream = moe.current_stream()
+    res = {}
+    for row_bytes in (1024, 4096):
+        for p, (name, rows) in moe.READ_PATTERNS.items():
+            best = None
+            for grid in (2 * n_cu, 4 * n_cu):
+                moe.moe_read_pattern(p, src.data_ptr(), nbytes, row_bytes, grid, sink.data_ptr(), stream)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(5):
+                    moe.moe_read_pattern(p, src.data_ptr(), nbytes, row_bytes, grid, sink.data_ptr(), stream)
+                e1.record()
+                torch.cuda.synchronize()
+                gbps = nbytes * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+                best = max(best or 0.0, gbps)
+            res[f"{name}, rows of {row_bytes} B"] = round(best, 1)
+            log(f"pattern {p} ({name}), rows of {row_bytes} B: {best:.0f} GB/s")
+    del src
+    return {"metric": "HBM read rate per load-instruction access pattern (measurement helper, not the layer)",
+            "unit": "GB/s", "bytes": nbytes, "loads_in_flight_per_lane": 8, "rates": res}
+
+
+def bench_release_cost(args, moe, torch):
+    """Cost of agent-scope releases at the end of every workgroup
+    (moe_release_cost): us per launch for each mode, grid and data size."""
+    stream = moe.current_stream()
+    grids, pts = (512, 2048, 8192), (4, 16)
+    data = torch.zeros(max(grids) * 256 * max(pts), dtype=torch.float32, device="cuda")
+    ctr = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    res = []
+    for grid in grids:
+        for pt in pts:
+            row = {"workgroups": grid, "kib_written_per_workgroup": pt}
+            for mode, name in moe.RELEASE_MODES.items():
+                moe.moe_release_cost(mode, data.data_ptr(), ctr.data_ptr(), grid, pt, stream)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(20):
+                    moe.moe_release_cost(mode, data.data_ptr(), ctr.data_ptr(), grid, pt, stream)
+                e1.record()
+                torch.cuda.synchronize()
+                row[name] = round(e0.elapsed_time(e1) * 1e3 / 20, 2)
+            log(f"{row}")
+            res.append(row)
+    return {"metric": "agent-scope release cost (measurement helper, not the layer)", "unit": "us per launch",
+            "table": res}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -900,6 +957,10 @@ def main() -> int:
                          " the roofline's per-kernel timing stays on the kernel chain")
     ap.add_argument("--mfma-rate", action="store_true",
                     help="only time the matrix-core rate helper per instruction kind (f16, bf16, fp8, scaled fp4)")
+    ap.add_argument("--read-patterns", action="store_true",
+                    help="only time the HBM read rate of each load-instruction access pattern")
+    ap.add_argument("--release-cost", action="store_true",
+                    help="only time agent-scope releases at the end of every workgroup")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -918,6 +979,10 @@ def main() -> int:
         return 2
     if args.mfma_rate:
         out = bench_mfma_rate(args, moe, torch)
+    elif args.read_patterns:
+        out = bench_read_patterns(args, moe, torch)
+    elif args.release_cost:
+        out = bench_release_cost(args, moe, torch)
     elif args.workload in synth.HEAD_CONFIGS:
         out = bench_head(args, moe, synth, torch, np)
     elif args.workload in synth.ATTN_CONFIGS:

@@ -283,6 +283,42 @@ moe_status moe_stream_read(const void* src, size_t bytes, void* sink, int32_t gr
  * enqueued. */
 moe_status moe_mfma_rate(int32_t kind, int32_t iters, int32_t grid, float* sink, void* stream);
 
+/* Measurement helper, not part of the layer: the HBM read rate of one
+ * per-instruction access pattern.  The review's section "The architecture is an
+ * argument about memory bandwidth" makes the weight stream the bound; this
+ * shows how the choice of bytes one load instruction touches moves that
+ * stream.  The `bytes` bytes at src are split into regions of R rows of
+ * row_bytes bytes, one region per wave at a time, each streamed with eight
+ * 16-byte loads per lane in flight; a load instruction touches:
+ *   pattern 0: 1 KB contiguous                  (R = 32)
+ *   pattern 1: 32 rows x 32 bytes               (R = 32; per-lane operands of a 4-bit tile)
+ *   pattern 2: 32 rows x 64 + 64 bytes          (R = 32; per-lane operands of a bf16 tile)
+ *   pattern 3: 4 rows x 256 bytes               (R = 4; the vector path)
+ *   pattern 4: 8 rows x 128 bytes               (R = 8; the tile loops' staged loads)
+ * row_bytes: a positive multiple of 256; bytes: a positive multiple of
+ * R x row_bytes; src 16 B aligned; grid workgroups of 256 threads; sink:
+ * caller-owned device memory of 256 uint32 (contents meaningless).  Bad
+ * arguments return MOE_ERR_INVALID_ARG before anything is enqueued. */
+moe_status moe_read_pattern(int32_t pattern, const void* src, size_t bytes, size_t row_bytes, int32_t grid,
+                            void* sink, void* stream);
+
+/* Measurement helper, not part of the layer: the cost of the agent-scope
+ * release that a hand-off between workgroups on different XCDs needs (the
+ * alternative to a kernel boundary between the steps of the review's decode
+ * pass, section "The quantisation recipe is the most transferable part").
+ * grid workgroups of 256 threads each write per_thread floats per thread into
+ * data (workgroup b owns floats [b * 256 * per_thread, (b + 1) * 256 *
+ * per_thread)), then their first thread:
+ *   mode 0: nothing more;  1: release fence + agent-scope atomic add of 1 to
+ *   counters[16 (b mod 256)];  2: the atomic add only;  3: the release only;
+ *   4: release, atomic add, acquire fence.
+ * No workgroup waits for another.  data must hold grid * 256 * per_thread
+ * floats and counters 4096 uint32 (caller-owned device memory; the counters are
+ * incremented, not cleared).  grid in [1, 65536], per_thread in [1, 64]; bad
+ * arguments return MOE_ERR_INVALID_ARG before anything is enqueued. */
+moe_status moe_release_cost(int32_t mode, float* data, uint32_t* counters, int32_t grid, int32_t per_thread,
+                            void* stream);
+
 /* ---- decode attention ----------------------------------------------------------
  * One new token per sequence through one attention layer of the layout in the
  * review's section "The architecture is an argument about memory bandwidth":

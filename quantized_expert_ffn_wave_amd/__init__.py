@@ -25,6 +25,7 @@ EXPORTED = ["moe_layer_create", "moe_layer_destroy", "moe_layer_workspace_size",
             "moe_layer_forward_persistent", "moe_stack_workspace_size", "moe_stack_forward",
             "moe_stack_forward_persistent",
             "moe_head_forward", "moe_attn_workspace_size", "moe_attn_decode", "moe_stream_read", "moe_mfma_rate",
+            "moe_read_pattern", "moe_release_cost",
             "moe_last_error",
             "moe_version"]
 ATTN_HQ, ATTN_HK, ATTN_D = 32, 4, 128
@@ -109,6 +110,10 @@ _lib.moe_stream_read.argtypes = [_vp, _sz, _vp, _i32, _vp]
 _lib.moe_stream_read.restype = ctypes.c_int
 _lib.moe_mfma_rate.argtypes = [_i32, _i32, _i32, _vp, _vp]
 _lib.moe_mfma_rate.restype = ctypes.c_int
+_lib.moe_read_pattern.argtypes = [_i32, _vp, _sz, _sz, _i32, _vp, _vp]
+_lib.moe_read_pattern.restype = ctypes.c_int
+_lib.moe_release_cost.argtypes = [_i32, _vp, _vp, _i32, _i32, _vp]
+_lib.moe_release_cost.restype = ctypes.c_int
 _lib.moe_last_error.restype = ctypes.c_char_p
 _lib.moe_version.restype = ctypes.c_char_p
 
@@ -228,6 +233,23 @@ MFMA_KINDS = {0: ("v_mfma_f32_32x32x16_f16", 32768), 1: ("v_mfma_f32_32x32x16_bf
 
 def moe_mfma_rate(kind: int, iters: int, grid: int, sink_ptr: int, stream: int) -> None:
     _check(_lib.moe_mfma_rate(kind, iters, grid, sink_ptr, stream), "moe_mfma_rate")
+
+
+READ_PATTERNS = {0: ("contiguous 1 KB", 32), 1: ("32 rows x 32 B", 32), 2: ("32 rows x 64+64 B", 32),
+                 3: ("4 rows x 256 B", 4), 4: ("8 rows x 128 B", 8)}  # name, rows per region
+
+
+def moe_read_pattern(pattern: int, src_ptr: int, nbytes: int, row_bytes: int, grid: int, sink_ptr: int,
+                     stream: int) -> None:
+    _check(_lib.moe_read_pattern(pattern, src_ptr, nbytes, row_bytes, grid, sink_ptr, stream), "moe_read_pattern")
+
+
+RELEASE_MODES = {0: "stores only", 1: "release + atomic", 2: "atomic only", 3: "release only",
+                 4: "release + atomic + acquire"}
+
+
+def moe_release_cost(mode: int, data_ptr: int, counters_ptr: int, grid: int, per_thread: int, stream: int) -> None:
+    _check(_lib.moe_release_cost(mode, data_ptr, counters_ptr, grid, per_thread, stream), "moe_release_cost")
 
 
 # ---- torch-level helpers -----------------------------------------------------------------

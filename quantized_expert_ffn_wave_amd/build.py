@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_ffn.so")
-SOURCES = ["abi.hip", "layer.hip", "stream_read.hip", "mfma_rate.hip", "attention.hip"]
+SOURCES = ["abi.hip", "layer.hip", "stream_read.hip", "mfma_rate.hip", "probes.hip", "attention.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

@@ -11,6 +11,7 @@
 
 #include "common.hpp"
 #include "attention.hpp"
+#include "probes.hpp"
 #include "moe_ffn.h"
 
 // Handle: the checked descriptor and the borrowed weights (no GPU resources).
@@ -541,6 +542,35 @@ moe_status moe_mfma_rate(int32_t kind, int32_t iters, int32_t grid, float* sink,
   if (!sink || !aligned(sink, 4)) return fail(MOE_ERR_INVALID_ARG, "sink must be a 4 B aligned device pointer");
   const hipError_t e = moe::launch_mfma_rate(kind, iters, grid, sink, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "matrix-core rate launch");
+  return MOE_OK;
+}
+
+moe_status moe_read_pattern(int32_t pattern, const void* src, size_t bytes, size_t row_bytes, int32_t grid,
+                            void* sink, void* stream) {
+  if (!moe::read_pattern_shape_ok(pattern, bytes, row_bytes))
+    return fail(MOE_ERR_INVALID_ARG,
+                "pattern must be 0..4, row_bytes a positive multiple of 256, and bytes a positive multiple of the "
+                "pattern's rows (32, 32, 32, 4, 8) times row_bytes (pattern %d, bytes %zu, row_bytes %zu)",
+                pattern, bytes, row_bytes);
+  if (!src || !aligned(src, 16)) return fail(MOE_ERR_INVALID_ARG, "src must be a 16 B aligned device pointer");
+  if (!sink || !aligned(sink, 4)) return fail(MOE_ERR_INVALID_ARG, "sink must be a 4 B aligned device pointer");
+  if (grid < 1 || grid > 65536) return fail(MOE_ERR_INVALID_ARG, "grid must be in [1, 65536], got %d", grid);
+  const hipError_t e = moe::launch_read_pattern(pattern, src, bytes, row_bytes, grid, static_cast<uint32_t*>(sink),
+                                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "read-pattern launch");
+  return MOE_OK;
+}
+
+moe_status moe_release_cost(int32_t mode, float* data, uint32_t* counters, int32_t grid, int32_t per_thread,
+                            void* stream) {
+  if (mode < 0 || mode > 4) return fail(MOE_ERR_INVALID_ARG, "mode must be 0..4, got %d", mode);
+  if (grid < 1 || grid > 65536) return fail(MOE_ERR_INVALID_ARG, "grid must be in [1, 65536], got %d", grid);
+  if (per_thread < 1 || per_thread > 64)
+    return fail(MOE_ERR_INVALID_ARG, "per_thread must be in [1, 64], got %d", per_thread);
+  if (!data || !aligned(data, 4)) return fail(MOE_ERR_INVALID_ARG, "data must be a 4 B aligned device pointer");
+  if (!counters || !aligned(counters, 4)) return fail(MOE_ERR_INVALID_ARG, "counters must be a 4 B aligned device pointer");
+  const hipError_t e = moe::launch_release_cost(mode, data, counters, grid, per_thread, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "release-cost launch");
   return MOE_OK;
 }
 

@@ -224,3 +224,26 @@ def test_one_hip_runtime_per_process():
     assert r.returncode == 0, r.stderr
     n = int(r.stdout.split()[0])
     assert n == 1, r.stdout
+
+
+def test_measurement_helpers_check_arguments_before_the_device():
+    """moe_read_pattern / moe_release_cost reject bad shapes and pointers
+    without touching a device."""
+    lib = moe.lib()
+    inv = moe.MOE_ERR_INVALID_ARG
+    src, sink = 0x100000, 0x2000
+    rp = lambda p, nbytes, rb, grid=256, s=src, k=sink: lib.moe_read_pattern(p, s, nbytes, rb, grid, k, None)
+    assert rp(5, 32 * 1024, 1024) == inv                # unknown pattern
+    assert rp(0, 32 * 1024, 1000) == inv                # row_bytes not a multiple of 256
+    assert rp(0, 31 * 1024, 1024) == inv                # not whole 32-row regions
+    assert rp(3, 6 * 1024, 1024) == inv                 # not whole 4-row regions
+    assert rp(4, 0, 1024) == inv
+    assert rp(0, 32 * 1024, 1024, s=src + 8) == inv     # src not 16 B aligned
+    assert rp(0, 32 * 1024, 1024, k=None) == inv
+    assert rp(0, 32 * 1024, 1024, grid=0) == inv
+    rc = lambda m, grid=64, pt=4, d=0x4000, c=0x8000: lib.moe_release_cost(m, d, c, grid, pt, None)
+    assert rc(5) == inv and rc(-1) == inv
+    assert rc(1, grid=0) == inv and rc(1, grid=65537) == inv
+    assert rc(1, pt=0) == inv and rc(1, pt=65) == inv
+    assert rc(1, d=None) == inv and rc(1, c=0x8002) == inv
+    assert "counters" in moe.last_error()

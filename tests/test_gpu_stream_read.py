@@ -44,3 +44,35 @@ def test_mfma_rate_helper_runs(kind):
     assert bool(torch.isfinite(sink).all())
     with pytest.raises(moe.MoeError):
         moe.moe_mfma_rate(4, 16, 8, sink.data_ptr(), moe.current_stream())
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("pattern", [0, 1, 2, 3, 4])
+def test_read_pattern_helper_runs(pattern):
+    """The access-pattern helper reads ragged region counts and leaves its sink
+    untouched (the kernel stores only when the XOR of what it read is its
+    keep-alive constant, which equal bytes never give)."""
+    rows = moe.READ_PATTERNS[pattern][1]
+    for row_bytes, regions in ((256, 3), (1024, 37)):
+        nbytes = rows * row_bytes * regions
+        src = torch.full((nbytes,), 7, dtype=torch.uint8, device="cuda")
+        sink = torch.full((256,), 7, dtype=torch.int32, device="cuda")
+        moe.moe_read_pattern(pattern, src.data_ptr(), nbytes, row_bytes, 8, sink.data_ptr(), moe.current_stream())
+        torch.cuda.synchronize()
+        assert bool((sink == 7).all())
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("mode", [0, 1, 2, 3, 4])
+def test_release_cost_helper_counts_and_writes(mode):
+    grid, pt = 300, 3
+    data = torch.zeros(grid * 256 * pt, dtype=torch.float32, device="cuda")
+    ctr = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    moe.moe_release_cost(mode, data.data_ptr(), ctr.data_ptr(), grid, pt, moe.current_stream())
+    torch.cuda.synchronize()
+    b = torch.arange(grid, device="cuda").repeat_interleave(256 * pt)
+    i = torch.arange(pt, device="cuda").repeat_interleave(256).repeat(grid)
+    assert torch.equal(data, (b + i).float())
+    counted = int(ctr.view(256, 16)[:, 0].sum())
+    assert counted == (grid if mode in (1, 2, 4) else 0)
+    assert int(ctr.view(256, 16)[:, 1:].abs().sum()) == 0

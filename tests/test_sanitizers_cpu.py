@@ -22,8 +22,19 @@ OBJS = os.path.join(CSRC, "_build")
 CLANG = "/opt/rocm/lib/llvm/bin/clang"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+
+def library_sources():
+    """The library's source list, from its build script (loaded by path)."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_moe_build", os.path.join(ROOT, "quantized_expert_ffn_wave_amd",
+                                                                             "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.SOURCES
+
+
 # the kernel objects linked beside the instrumented abi.hip (all but abi.o)
-KERNEL_OBJS = ["layer.o", "stream_read.o", "mfma_rate.o", "attention.o"]
+KERNEL_OBJS = [s.replace(".hip", ".o") for s in library_sources() if s != "abi.hip"]
 # the one test whose full-size routing sweep takes most of a minute serially
 SLOW = "test_full_size_uniform_routing_touches_expected_expert_count"
 
