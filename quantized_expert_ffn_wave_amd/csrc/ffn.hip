@@ -1145,23 +1145,33 @@ __device__ inline void mf_kloop_bf16(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<FMT_B
 // four K-chunks (128 bytes of a row, one line-friendly load per 8 rows and
 // lane), each group staged into the wave's LDS block while the next one is
 // loaded; a lane then reads its 16 bytes of a chunk from there and decodes them
-// as mf_kloop does.  The block scales are loaded per lane, 3 chunks ahead.
-// q[b], wrow[b]: the lane's matrix and row of block b (for its scales).
+// as mf_kloop does.  The block scales: q4_1 loaded per lane, 3 chunks ahead;
+// NVFP4 (a row's scales for all of K are one 128-byte line) staged once per
+// item into the unused upper half of the wave's LDS block, with line-friendly
+// loads like the codes, and read from there per chunk.  (Per-lane scale loads
+// touch 32 rows per instruction; on the 256-token NVFP4 layer they cost about
+// as much as the whole decode.)
+// q[b], wrow[b]: the lane's matrix and row of block b (for its scales); sh: the
+// scale rows of the two halves (NVFP4).
 template <int FMT, int BN, int RB, int NSX>
 __device__ inline void mf_kloop_q(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<FMT, BN>& sm, const QMat (&q)[RB],
-                                  const size_t (&wrow)[RB], const uint8_t* const (&wh)[2], const uint16_t* xbase,
-                                  const int* xrow, int cnt) {
+                                  const size_t (&wrow)[RB], const uint8_t* const (&wh)[2],
+                                  const uint8_t* const (&sh)[2], const uint16_t* xbase, const int* xrow, int cnt) {
   constexpr int kdim = D_MODEL;
   constexpr int RBYTES = kdim / 2;  // codes per row
   constexpr int NW = 4 * RB;        // code loads per lane and group: wave rows 8 i + lane / 8
   constexpr int HR = 16 * RB;       // rows per half
   constexpr int NX = BN / 32;       // activation loads per thread and chunk
   constexpr int NC = kdim / 64, NG = NC / 4;
-  static_assert(NSX == 2 || NSX == 4, "activation ring of 2 or 4 chunks");
+  static_assert(NSX == 4, "activation ring of 4 chunks, as deep as the scales'");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c = lane & 31, sub = lane >> 3, part = lane & 7;
   uint8_t* wl = reinterpret_cast<uint8_t*>(sm.w[wave]);
   constexpr int WS = TS * 2;  // LDS bytes per weight row
+  constexpr bool SL = FMT == FMT_NVFP4;  // scales through LDS
+  constexpr int SBYTES = kdim / 16;      // NVFP4 scale bytes per row
+  static_assert(!SL || (RB == 1 && 2 * 32 * WS <= MF_WL_ROWS<FMT> * TS * 2 && SBYTES == 128),
+                "NVFP4: 32 rows of codes and 32 rows of 128 scale bytes in the wave's LDS block");
   const uint8_t* wp[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) wp[g] = wh[g] + (size_t)sub * RBYTES + 16 * part;
@@ -1170,7 +1180,7 @@ __device__ inline void mf_kloop_q(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<FMT, BN>
   for (int i = 0; i < NX; ++i) xo[i] = (uint32_t)xrow[min(32 * i + 8 * wave + sub, cnt - 1)] * (uint32_t)kdim + 8u * part;
   u32x4 wst[NW];
   u32x4 xst[NSX][NX];
-  uint32_t sst[4][RB];
+  uint32_t sst[4][RB] = {};  // (q4_1)
   auto fetch_w = [&](int g) {
     g = min(g, NG - 1);
 #pragma unroll
@@ -1194,21 +1204,24 @@ __device__ inline void mf_kloop_q(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<FMT, BN>
     // block 2 ck + h of a row of 2048: stored at 8 (ck mod 8) + 4 h + ck / 8
     const uint32_t slot = 8u * (uint32_t)(ck & 7) + 4u * (uint32_t)h + (uint32_t)(ck >> 3);
 #pragma unroll
-    for (int b = 0; b < RB; ++b) {
-      if constexpr (FMT == FMT_Q4_1)
-        st[b] = ld4<false>(reinterpret_cast<const uint32_t*>(q[b].scales) + wrow[b] * (kdim / 32) + slot);
-      else
-        st[b] = ld2<false>(reinterpret_cast<const uint8_t*>(q[b].scales) + wrow[b] * (kdim / 16) + 2 * slot);
-    }
+    for (int b = 0; b < RB; ++b)
+      st[b] = ld4<false>(reinterpret_cast<const uint32_t*>(q[b].scales) + wrow[b] * (kdim / 32) + slot);
   };
-  auto multiply = [&](int cg, const uint32_t (&sc)[RB], const uint16_t* buf) {
+  auto multiply = [&](int ck, const uint32_t (&sc)[RB], const uint16_t* buf) {
+    const int cg = ck & 3;
     uint32_t wv[RB][16];
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
       typename GV<FMT>::Raw r;
       r.c = *reinterpret_cast<const u32x4*>(wl + (32 * b + c) * WS + 32 * cg + 16 * h);
-      if constexpr (FMT == FMT_Q4_1) r.dm = sc[b];
-      else r.s = sc[b];
+      if constexpr (FMT == FMT_Q4_1) {
+        r.dm = sc[b];
+      } else {
+        // the aligned 4 bytes holding slot 8 (ck mod 8) + 4 h + ck / 8 (2 bytes
+        // each), from the lane's scale row
+        const uint32_t w4 = 4u * (uint32_t)(ck & 7) + 2u * (uint32_t)h + (uint32_t)(ck >> 4);
+        r.s = *reinterpret_cast<const uint32_t*>(wl + (32 + c) * WS + 4 * w4) >> (16 * ((ck >> 3) & 1));
+      }
       GV<FMT>::decode(r, wv[b]);
     }
 #pragma unroll
@@ -1223,11 +1236,29 @@ __device__ inline void mf_kloop_q(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<FMT, BN>
       }
     }
   };
-  fetch_w(0);
+  if constexpr (SL) {
+    // wave rows 8 i + lane / 8 of the two halves, 16 bytes per lane; written
+    // once the codes and activations of the first chunks are on their way
+    u32x4 sl[4];
 #pragma unroll
-  for (int i = 0; i < NSX - 1; ++i) fetch_x(xst[i], i);
+    for (int i = 0; i < 4; ++i) sl[i] = ld16<false>(sh[(8 * i) / 16] + (size_t)((8 * i) % 16 + sub) * SBYTES + 16 * part);
+    fetch_w(0);
 #pragma unroll
-  for (int i = 0; i < 3; ++i) fetch_s(sst[i], i);
+    for (int i = 0; i < 3; ++i) fetch_x(xst[i], i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(wl + (32 + 8 * i + sub) * WS + 16 * part) = sl[i];
+  } else {
+    // the prologue issues its loads in the loop's order (activations, then
+    // scales, chunk by chunk): the wait counts at the loop top hold for both
+    // ways in, so they stay those of the steady state
+    fetch_w(0);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      fetch_x(xst[i], i);
+      fetch_s(sst[i], i);
+    }
+  }
 #pragma unroll 1
   for (int g = 0; g < NG; ++g) {
 #pragma unroll
@@ -1240,9 +1271,9 @@ __device__ inline void mf_kloop_q(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<FMT, BN>
       }
       stage_x(xst[j % NSX], sm.x[j & 1]);
       fetch_x(xst[(j + NSX - 1) % NSX], ck + NSX - 1);
-      fetch_s(sst[(j + 3) % 4], ck + 3);
+      if constexpr (!SL) fetch_s(sst[(j + 3) % 4], ck + 3);
       __syncthreads();
-      multiply(j, sst[j], sm.x[j & 1]);
+      multiply(ck, sst[j], sm.x[j & 1]);
     }
   }
 }
@@ -1279,7 +1310,9 @@ __device__ void mfma_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int m
   } else if constexpr (BN == 64) {
     const size_t r = (size_t)mat * D_FF + n0 + 16 * RB * wave;
     const uint8_t* const wh[2] = {G.codes + r * (D_MODEL / 2), Uq.codes + r * (D_MODEL / 2)};
-    mf_kloop_q<FMT, BN, RB, 4>(acc, sm, q, wrow, wh, a.xq, sm.tok, it.cnt);
+    const uint8_t* const sh[2] = {static_cast<const uint8_t*>(G.scales) + r * (D_MODEL / 16),
+                                  static_cast<const uint8_t*>(Uq.scales) + r * (D_MODEL / 16)};
+    mf_kloop_q<FMT, BN, RB, 4>(acc, sm, q, wrow, wh, sh, a.xq, sm.tok, it.cnt);
   } else {
     // (128-token tiles: the staged loop's registers do not fit two waves per SIMD)
     mf_kloop<FMT, BN, RB, MF_NS_UP<FMT, BN>>(acc, sm, q, wrow, xsrc, xscale, D_MODEL);
