@@ -890,6 +890,12 @@ static_assert(D_MODEL % (64 * 4) == 0 && D_FF % (64 * 4) == 0, "the chunk loop i
 // block of 64 rows x 128 bytes per wave (one K-chunk of bf16, four of the 4-bit
 // codes), single-buffered: only its own wave uses it.
 template <int FMT> constexpr int MF_WL_ROWS = 64;
+// Down items, 4-bit formats: the block scales of each wave's 64 rows, one row
+// (D_FF / 32 blocks: 64 bytes q4_1, 32 NVFP4) per DN_SW words, padded by a word
+// so that the 32 lanes reading one word of 32 rows hit 32 banks.
+template <int FMT> constexpr int DN_SW = (FMT == FMT_Q4_1) ? D_FF / 32 + 1 : (FMT == FMT_NVFP4) ? D_FF / 64 + 1 : 1;
+// (64-token tiles only: the 128-token tiles keep the per-lane loop, and their LDS two workgroups per CU)
+template <int FMT, int BN> constexpr int DN_SWORDS = (FMT != FMT_BF16 && BN == 64) ? 64 * DN_SW<FMT> : 1;
 template <int FMT, int BN> struct FfnSmem {
   uint16_t x[2][BN * TS];  // K-chunks alternate between the two, so one barrier per chunk suffices
   uint16_t w[4][MF_WL_ROWS<FMT> * TS];  // bf16 weights: each wave's rows of the current K-chunk
@@ -898,6 +904,7 @@ template <int FMT, int BN> struct FfnSmem {
   float sc[BN];            // 4-bit formats: activation scale per token column (down: from |h|)
   float isc[BN];           // and its inverse
   float hred[4][BN];       // gate/up, 4-bit formats: each wave's largest |h| per token column
+  uint32_t ds[4][DN_SWORDS<FMT, BN>];  // down, 4-bit formats: each wave's block scales
 };
 
 // Store 16 activation elements (natural-order pairs src[8]) into LDS in the
@@ -1000,7 +1007,18 @@ __device__ inline void mf_kloop(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<FMT, BN>& 
     const uint32_t slot = (kdim == D_MODEL) ? 8u * (uint32_t)(ck & 7) + 4u * (uint32_t)h + (uint32_t)(ck >> 3)
                                             : 2u * (uint32_t)ck + (uint32_t)h;
 #pragma unroll
-    for (int b = 0; b < RB; ++b) st.w[b] = GV<FMT>::template load_slot<false>(q[b], wrow[b], 0u, 2 * ck + h, slot, kdim);
+    for (int b = 0; b < RB; ++b) {
+      if constexpr (FMT == FMT_NVFP4 && BN == 64) {
+        // the aligned 4 bytes holding the slot's 2, shifted into place at the
+        // decode: a 16-bit load result is narrowed and widened again at the
+        // top of the loop, and that wait drains every load in flight (not for
+        // 128-token tiles, whose registers are full)
+        st.w[b] = GV<FMT>::template load_codes<false>(q[b], wrow[b], 0u, 2 * ck + h, kdim);
+        st.w[b].s = ld4<false>(static_cast<const uint8_t*>(q[b].scales) + wrow[b] * (kdim / 16) + 4 * (slot >> 1));
+      } else {
+        st.w[b] = GV<FMT>::template load_slot<false>(q[b], wrow[b], 0u, 2 * ck + h, slot, kdim);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < NX; ++i)
       st.x[i] = ld16<false>(static_cast<const uint8_t*>(xsrc) + (XF32 ? 4 : 2) * 64 * ck + 16 * i);
@@ -1024,10 +1042,16 @@ __device__ inline void mf_kloop(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<FMT, BN>& 
       stage_x16<FMT>(buf + xt * TS + MF_XK<BN> * xs + 16 * g, xv);
     }
   };
-  auto multiply = [&](const Stage& st, const uint16_t* buf) {
+  auto multiply = [&](const Stage& st, int ck, const uint16_t* buf) {
     uint32_t wv[RB][16];
+    // NVFP4: which half of the scale dword is the lane's (slot mod 2, as in fetch)
+    const int shift = 16 * ((kdim == D_MODEL) ? ((ck >> 3) & 1) : h);
 #pragma unroll
-    for (int b = 0; b < RB; ++b) GV<FMT>::decode(st.w[b], wv[b]);
+    for (int b = 0; b < RB; ++b) {
+      typename GV<FMT>::Raw r = st.w[b];
+      if constexpr (FMT == FMT_NVFP4 && BN == 64) r.s >>= shift;
+      GV<FMT>::decode(r, wv[b]);
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -1054,7 +1078,7 @@ __device__ inline void mf_kloop(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<FMT, BN>& 
       stage(st[j], sm.x[j & 1]);
       fetch(st[(j + NS - 1) % NS], ck0 + j + NS - 1);
       __syncthreads();
-      multiply(st[j], sm.x[j & 1]);
+      multiply(st[j], ck0 + j, sm.x[j & 1]);
     }
   }
 }
@@ -1278,6 +1302,168 @@ __device__ inline void mf_kloop_q(f32x16 (&acc)[RB][MF_TT<BN>], FfnSmem<FMT, BN>
   }
 }
 
+// 4-bit weights, down (K = D_FF: 8 K-chunks, two groups of four), tables
+// included.  The codes move as in mf_kloop_q: line-friendly loads of a group
+// of four K-chunks staged through the wave's LDS block.  The block scales of
+// the wave's 64 rows are contiguous in storage; they are read once per item
+// with contiguous loads and kept in LDS (the per-lane loads they replace touch
+// 32 rows per instruction, as did the per-lane code loads).  The tables (the
+// down half of mfma_tables: rows, and each row's activation scale from its |h|
+// slots) read the slots first, then the first group of codes and the scales
+// are requested, so that the tables' wait is for the slots alone and the
+// codes' latency overlaps it.  The activations (h,
+// fp32) are read line-friendly too: 16 threads take a token's 256 bytes of a
+// chunk (4 floats each), 16 tokens per round, and convert and store them as
+// mf_kloop does (q4_1: the two halves of each 8-element group trade a pair of
+// values between neighbouring lanes to reach the weights' k order), 2 chunks
+// ahead.  Same products in the same order as mf_kloop with fp32 activations.
+template <int FMT, int BN>
+__device__ inline void mf_down_q(const LayerArgs& a, const QMat& D, int mat, const ItemTok& it, int r0,
+                                 FfnSmem<FMT, BN>& sm, f32x16 (&acc)[2][MF_TT<BN>]) {
+  static_assert(FMT != FMT_BF16 && BN == 64, "4-bit formats, 64-token tiles");
+  constexpr int kdim = D_FF, RBYTES = kdim / 2, NC = kdim / 64, NG = NC / 4;
+  constexpr int SB = (FMT == FMT_Q4_1) ? kdim / 32 * 4 : kdim / 16;  // scale bytes per row
+  constexpr int SW = DN_SW<FMT>;
+  constexpr int NSL = 64 * SB / 1024;  // 16-byte scale loads per lane
+  constexpr int NXR = BN / 16;         // activation loads per thread and chunk
+  constexpr int NSX = 3;               // activation chunks in registers
+  constexpr int WS = TS * 2;           // LDS bytes per weight row
+  static_assert(NG == 2 && 64 * SB % 1024 == 0 && SW * 4 == SB + 4, "rows of 512: two groups, whole scale rows");
+  static_assert(MF_WL_ROWS<FMT> == 64, "the wave's 64 code rows of a group fill its LDS block");
+  static_assert(DN_SWORDS<FMT, BN> == 64 * SW, "scale rows of the wave's 64 rows");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, c = lane & 31, sub = lane >> 3, part = lane & 7;
+  uint8_t* wl = reinterpret_cast<uint8_t*>(sm.w[wave]);
+  uint32_t* sl = sm.ds[wave];
+  const size_t w0 = (size_t)mat * D_MODEL + r0 + 64 * wave;  // the wave's first row
+  const uint8_t* wp = D.codes + (w0 + sub) * RBYTES + 16 * part;
+  u32x4 wst[8];
+  auto fetch_w = [&](int g) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wst[i] = ld16<true>(wp + (size_t)(8 * i) * RBYTES + 128 * g);
+  };
+  auto stage_w = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(wl + (8 * i + sub) * WS + 16 * part) = wst[i];
+  };
+  // |h| slots of column tid / P (P threads per column; past the count a valid
+  // row, ignored), then the codes and scales
+  constexpr int P = 256 / BN, NSH = HSLOTS / P;
+  static_assert(P == 4 && NSH % 4 == 0, "4 threads per token column: two DPP exchanges");
+  const int col = tid / P, pt = tid % P;
+  u32x4 hv[NSH / 4];
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.hslot + (size_t)row_of(a, it, min(col, it.cnt - 1)) * HSLOTS +
+                                                      NSH * pt);
+#pragma unroll
+    for (int k = 0; k < NSH / 4; ++k) hv[k] = src[k];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 sst[NSL];
+#pragma unroll
+  for (int i = 0; i < NSL; ++i)
+    sst[i] = ld16<false>(static_cast<const uint8_t*>(D.scales) + w0 * SB + 1024 * i + 16 * lane);
+  fetch_w(0);
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < NSH / 4; ++k)
+      m = fmaxf(fmaxf(m, fmaxf(__uint_as_float(hv[k][0]), __uint_as_float(hv[k][1]))),
+                fmaxf(__uint_as_float(hv[k][2]), __uint_as_float(hv[k][3])));
+    if (col >= it.cnt) m = 0.f;
+    m = fmaxf(m, dpp_partner<1>(m));
+    m = fmaxf(m, dpp_partner<2>(m));
+    if (pt == 0) {
+      const float sc = pow2_scale(__float_as_uint(m));
+      sm.sc[col] = sc;
+      sm.isc[col] = pow2_inv(sc);
+    }
+    if (tid < BN) sm.row[tid] = (tid < it.cnt) ? row_of(a, it, tid) : -1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NSL; ++i) {
+    const int o = 1024 * i + 16 * lane;  // byte of the wave's scales
+#pragma unroll
+    for (int d = 0; d < 4; ++d) sl[(o / SB) * SW + (o % SB) / 4 + d] = sst[i][d];
+  }
+  // thread: 4 floats (elements 4 q ..) of tokens 16 i + tid / 16 of each chunk
+  const int q = tid & 15;
+  uint32_t xo[NXR];
+  float xs[NXR];
+#pragma unroll
+  for (int i = 0; i < NXR; ++i) {
+    const int t = min(16 * i + (tid >> 4), it.cnt - 1);  // past the count: a valid row, never stored
+    xo[i] = (uint32_t)sm.row[t] * (uint32_t)kdim + 4u * (uint32_t)q;
+    xs[i] = sm.sc[t];
+  }
+  const float* hb = static_cast<const float*>(a.h);
+  u32x4 xst[NSX][NXR];
+  auto fetch_x = [&](u32x4 (&st)[NXR], int ck) {
+#pragma unroll
+    for (int i = 0; i < NXR; ++i) st[i] = ld16<false>(hb + xo[i] + 64 * ck);
+  };
+  auto stage_x = [&](const u32x4 (&st)[NXR], uint16_t* buf) {
+#pragma unroll
+    for (int i = 0; i < NXR; ++i) {
+      uint32_t p0 = f32x2_to_f16x2(st[i][0], st[i][1], xs[i]);
+      uint32_t p1 = f32x2_to_f16x2(st[i][2], st[i][3], xs[i]);
+      if constexpr (FMT == FMT_Q4_1) {
+        // even q holds elements 0-3 of an 8-group, odd q 4-7; order 0 4 1 5 | 2 6 3 7
+        const bool even = (q & 1) == 0;
+        const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)(even ? p1 : p0), 0xB1, 0xF, 0xF, false);
+        const uint32_t lo = even ? p0 : got, hi = even ? got : p1;
+        p0 = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        p1 = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+      }
+      *reinterpret_cast<u32x2*>(buf + (16 * i + (tid >> 4)) * TS + 4 * q) = u32x2{p0, p1};
+    }
+  };
+  auto multiply = [&](int ck, const uint16_t* buf) {
+    const int cg = ck & 3;
+    uint32_t wv[2][16];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      typename GV<FMT>::Raw r;
+      r.c = *reinterpret_cast<const u32x4*>(wl + (32 * b + c) * WS + 32 * cg + 16 * h);
+      // block 2 ck + h of the row: q4_1 word 2 ck + h; NVFP4 half h of word ck
+      if constexpr (FMT == FMT_Q4_1) r.dm = sl[(32 * b + c) * SW + 2 * ck + h];
+      else r.s = sl[(32 * b + c) * SW + ck] >> (16 * h);
+      GV<FMT>::decode(r, wv[b]);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int tt = 0; tt < MF_TT<BN>; ++tt) {
+        const u32x4 bv = *reinterpret_cast<const u32x4*>(buf + (32 * tt + c) * TS + 32 * h + 8 * s);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[b][tt] = mfma32<FMT>(u32x4{wv[b][4 * s], wv[b][4 * s + 1], wv[b][4 * s + 2], wv[b][4 * s + 3]}, bv,
+                                   acc[b][tt]);
+      }
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < NSX - 1; ++i) fetch_x(xst[i], i);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ck = 4 * g + j;
+      __builtin_amdgcn_sched_barrier(0);
+      if (j == 0) {
+        stage_w();  // the previous group's chunks are multiplied (this wave, in order)
+        if (g + 1 < NG) fetch_w(g + 1);
+      }
+      stage_x(xst[ck % NSX], sm.x[ck & 1]);
+      if (ck + NSX - 1 < NC) fetch_x(xst[(ck + NSX - 1) % NSX], ck + NSX - 1);
+      __syncthreads();
+      multiply(ck, sm.x[ck & 1]);
+    }
+  }
+}
+
 // gate/up item: 32 MF_UP_RB row pairs per wave (n0 ..) x BN tokens.
 template <int FMT, int BN>
 __device__ void mfma_up(const LayerArgs& a, const QMat& G, const QMat& Uq, int mat, const ItemTok& it, int n0,
@@ -1380,22 +1566,26 @@ __device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const Item
                           FfnSmem<FMT, BN>& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, c = lane & 31;
-  mfma_tables<FMT, false>(a, it, sm);
-  __syncthreads();
-  const QMat q[2] = {D, D};
-  const size_t wr = (size_t)mat * D_MODEL + r0 + 64 * wave + c;
-  const size_t wrow[2] = {wr, wr + 32};
-  const int hrow_x = sm.row[min(tid / MF_XT<BN>, it.cnt - 1)];
-  const HElem<FMT>* xsrc =
-      static_cast<const HElem<FMT>*>(a.h) + (size_t)hrow_x * D_FF + MF_XK<BN> * (tid % MF_XT<BN>);
-  const float xscale = OPER_F16<FMT> ? sm.sc[min(tid / MF_XT<BN>, it.cnt - 1)] : 1.f;
   f32x16 acc[2][MF_TT<BN>] = {};
-  if constexpr (FMT == FMT_BF16) {
-    const uint16_t* w0 = reinterpret_cast<const uint16_t*>(D.codes) + (wr - (size_t)c) * D_FF;
-    const uint16_t* const wh[2] = {w0, w0 + (size_t)32 * D_FF};
-    mf_kloop_bf16<BN, 2, MF_NS_DN<FMT, BN>>(acc, sm, wh, static_cast<const uint16_t*>(a.h), sm.row, it.cnt, D_FF);
+  if constexpr (FMT != FMT_BF16 && BN == 64) {
+    mf_down_q<FMT, BN>(a, D, mat, it, r0, sm, acc);
   } else {
-    mf_kloop<FMT, BN, 2, MF_NS_DN<FMT, BN>, OPER_F16<FMT>>(acc, sm, q, wrow, xsrc, xscale, D_FF);
+    mfma_tables<FMT, false>(a, it, sm);
+    __syncthreads();
+    const QMat q[2] = {D, D};
+    const size_t wr = (size_t)mat * D_MODEL + r0 + 64 * wave + c;
+    const size_t wrow[2] = {wr, wr + 32};
+    if constexpr (FMT == FMT_BF16) {
+      const uint16_t* w0 = reinterpret_cast<const uint16_t*>(D.codes) + (wr - (size_t)c) * D_FF;
+      const uint16_t* const wh[2] = {w0, w0 + (size_t)32 * D_FF};
+      mf_kloop_bf16<BN, 2, MF_NS_DN<FMT, BN>>(acc, sm, wh, static_cast<const uint16_t*>(a.h), sm.row, it.cnt, D_FF);
+    } else {
+      const int hrow_x = sm.row[min(tid / MF_XT<BN>, it.cnt - 1)];
+      const HElem<FMT>* xsrc =
+          static_cast<const HElem<FMT>*>(a.h) + (size_t)hrow_x * D_FF + MF_XK<BN> * (tid % MF_XT<BN>);
+      const float xscale = sm.sc[min(tid / MF_XT<BN>, it.cnt - 1)];
+      mf_kloop<FMT, BN, 2, MF_NS_DN<FMT, BN>, OPER_F16<FMT>>(acc, sm, q, wrow, xsrc, xscale, D_FF);
+    }
   }
   const float tsd = (FMT == FMT_NVFP4) ? D.ts[mat] : 1.f;
 #pragma unroll
