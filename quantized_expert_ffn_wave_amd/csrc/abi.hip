@@ -111,7 +111,8 @@ WsLayout ws_layout(const moe_layer_desc& d, int T) {
   L.y = take((d.wfmt == MOE_W_BF16 ? sizeof(uint16_t) : sizeof(float)) * R * moe::D_MODEL);
   L.xsc = take(sizeof(float) * (size_t)T);
   // 4-bit formats: the scaled fp16 activations the matrix-core tiles read
-  L.xq = take(d.wfmt == MOE_W_BF16 ? 0 : sizeof(uint16_t) * (size_t)T * moe::D_MODEL);
+  // (none where the batch has no tile)
+  L.xq = take(d.wfmt == MOE_W_BF16 || !moe::batch_mfma(T) ? 0 : sizeof(uint16_t) * (size_t)T * moe::D_MODEL);
   L.hslot = take(sizeof(float) * moe::HSLOTS * R);
   L.sync = take(sizeof(uint32_t) * moe::DEC_SYNC_WORDS);
   L.total = o;
@@ -162,7 +163,7 @@ moe::LayerArgs make_args(const moe_layer* L, const void* x, int T, char* ws, con
   a.h = (void*)(ws + W.h);
   a.y = (void*)(ws + W.y);
   a.xsc = (float*)(ws + W.xsc);
-  a.xq = (uint16_t*)(ws + W.xq);
+  a.xq = (a.fmt != moe::FMT_BF16 && moe::batch_mfma(a.T)) ? (uint16_t*)(ws + W.xq) : nullptr;
   a.hslot = (float*)(ws + W.hslot);
   a.max_tiles = W.max_tiles;
   return a;

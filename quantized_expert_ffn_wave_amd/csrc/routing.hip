@@ -190,19 +190,21 @@ __device__ void topk_token(const LayerArgs& a, int t, int32_t* lds_ids) {
     mx = wave_max_u32(mx);
     const float sc = pow2_scale(mx << 16);
     if (lane == 0) a.xsc[t] = sc;
-    uint4* dst = reinterpret_cast<uint4*>(a.xq + (size_t)t * D_MODEL) + 4 * lane;
+    if (a.xq != nullptr) {  // (none where the batch has no tile)
+      uint4* dst = reinterpret_cast<uint4*>(a.xq + (size_t)t * D_MODEL) + 4 * lane;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t w4[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-      uint32_t n[4];
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w4[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+        uint32_t n[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        n[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w4[q] << 16) * sc,
-                                                                     __uint_as_float(w4[q] & 0xFFFF0000u) * sc));
-      if (a.fmt == FMT_Q4_1)
-        dst[i] = make_uint4(__builtin_amdgcn_perm(n[2], n[0], 0x05040100u), __builtin_amdgcn_perm(n[2], n[0], 0x07060302u),
-                            __builtin_amdgcn_perm(n[3], n[1], 0x05040100u), __builtin_amdgcn_perm(n[3], n[1], 0x07060302u));
-      else dst[i] = make_uint4(n[0], n[1], n[2], n[3]);
+        for (int q = 0; q < 4; ++q)
+          n[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w4[q] << 16) * sc,
+                                                                       __uint_as_float(w4[q] & 0xFFFF0000u) * sc));
+        if (a.fmt == FMT_Q4_1)
+          dst[i] = make_uint4(__builtin_amdgcn_perm(n[2], n[0], 0x05040100u), __builtin_amdgcn_perm(n[2], n[0], 0x07060302u),
+                              __builtin_amdgcn_perm(n[3], n[1], 0x05040100u), __builtin_amdgcn_perm(n[3], n[1], 0x07060302u));
+        else dst[i] = make_uint4(n[0], n[1], n[2], n[3]);
+      }
     }
   }
   uint32_t kk[4];
