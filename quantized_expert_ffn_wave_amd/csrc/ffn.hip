@@ -1652,6 +1652,19 @@ __device__ inline int mf_item(int i, int n, int C) {
   return (8 * g + tl) * C + ch;
 }
 
+// Workgroups that take down items of the matrix-core path: with more items
+// than workgroups, the fewest that keep the same number of rounds (a multiple
+// of 8, so that item i still runs on XCD i % 8), so that the last round does
+// not run half empty.  At 4096 tokens the 2304 down items take 464 of 512
+// workgroups for 5 rounds (down 175 -> 172 us).  Not for gate/up: its 1152
+// items on 384 workgroups took 268 against 239 us on 512, since an item's
+// length is set by its K-loop's latency, not by its share of HBM.
+__device__ inline int mf_grid(int n, int g) {
+  if (n <= g) return g;
+  const int rounds = ceil_div(n, g);
+  return min(g, (ceil_div(n, rounds) + 7) & ~7);
+}
+
 // Items of the matrix-core path come first; the vector-path chunks follow.
 // VR, VDR: rows of the vector-path gate/up and down items (vec_up_rows and
 // vec_dn_rows of the batch size).
@@ -1680,7 +1693,8 @@ __global__ __launch_bounds__(256, (FFN_WG_PER_CU<FMT, BN>)) void ffn_down_kernel
   __shared__ FfnKernelSmem<FMT, BN> sm;
   const int n_all = a.ctl[CTL_N_DN], n_mf = a.ctl[CTL_N_DN_MF];
   if constexpr (BN > 0) {
-    for (int i = blockIdx.x; i < n_mf; i += gridDim.x) {
+    const int G = mf_grid(n_mf, gridDim.x);
+    for (int i = blockIdx.x; i < n_mf && (int)blockIdx.x < G; i += G) {
       const Item item = fetch_item(a.tiles, mf_item(i, n_mf, N_DN_CHUNKS), N_DN_CHUNKS);
       const bool sh = item_shared(item.head);
       mfma_down<FMT, BN>(a, sel_qmat(sh, a.sh_down, a.down), sh ? 0 : item_expert(item.head), item_tokens(item),
