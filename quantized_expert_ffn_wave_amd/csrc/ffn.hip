@@ -1615,6 +1615,137 @@ __device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const Item
   __syncthreads();
 }
 
+// bf16 down items, one workgroup's sequence idx = i0, i0 + stride, ... < n, as
+// one K-loop: the chunk after an item's last one is the next item's first, so
+// its loads are in flight during the last chunk's products and the y stores
+// instead of after them (an item has only 8 K-chunks, and the first one's
+// latency, paid once per item, was about a tenth of it).  No tables: an item's
+// h rows are its bucket positions (routed) or tokens (shared), contiguous,
+// and they are its y rows too.  Same loads, LDS layout and products in the
+// same order as mfma_down through mf_kloop_bf16.
+__device__ inline int mf_item(int i, int n, int C);
+template <int BN>
+__device__ void mfma_down_bf16_seq(const LayerArgs& a, int i0, int stride, int n, FfnSmem<FMT_BF16, BN>& sm) {
+  constexpr int NW = 8;               // weight loads per lane and chunk: wave rows 8 i + lane / 8
+  constexpr int NX = BN / 32;         // h loads per thread and chunk: tokens 32 i + 8 wave + lane / 8
+  constexpr int kdim = D_FF, NC = kdim / 64;
+  static_assert(MF_NS_DN<FMT_BF16, BN> == 2 && NC % 2 == 0, "two stages, chunk j in LDS buffer j % 2");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, c = lane & 31, sub = lane >> 3, part = lane & 7;
+  uint16_t* wl = sm.w[wave];
+  const uint16_t* hb = static_cast<const uint16_t*>(a.h);
+  struct Src {
+    const uint16_t* wp;  // the lane's first weight row piece of the wave's 64 rows
+    uint32_t xo[NX];     // the thread's h row offsets (elements)
+    int mat, r0, p0, cnt, shared;
+  };
+  // item idx of the sequence is entry mf_item(idx) of the list (row chunk mf_item(idx) % N_DN_CHUNKS)
+  auto prep = [&](const Item& raw, int idx) {
+    Item item = raw;
+    item.head |= (uint32_t)(mf_item(idx, n, N_DN_CHUNKS) % N_DN_CHUNKS) << 9;
+    item.head = __builtin_amdgcn_readfirstlane(item.head);
+    item.p0 = __builtin_amdgcn_readfirstlane(item.p0);
+    const ItemTok it = item_tokens(item);
+    Src s;
+    s.shared = it.shared;
+    s.mat = it.shared ? 0 : item_expert(item.head);
+    s.r0 = item_chunk(item.head) * DN_ROWS;
+    s.p0 = it.p0;
+    s.cnt = it.cnt;
+    const uint16_t* codes = reinterpret_cast<const uint16_t*>(it.shared ? a.sh_down.codes : a.down.codes);
+    s.wp = codes + ((size_t)s.mat * D_MODEL + s.r0 + 64 * wave + sub) * kdim + 8 * part;
+#pragma unroll
+    for (int i = 0; i < NX; ++i) s.xo[i] = (uint32_t)row_of(a, it, min(32 * i + 8 * wave + sub, it.cnt - 1)) * kdim + 8u * part;
+    return s;
+  };
+  auto load_item = [&](int idx) { return a.tiles[mf_item(idx, n, N_DN_CHUNKS) / N_DN_CHUNKS]; };
+  struct Stage {
+    u32x4 w[NW];
+    u32x4 x[NX];
+  };
+  auto fetch = [&](Stage& st, const Src& s, int ck) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) st.w[i] = ld16<true>(s.wp + (size_t)(8 * i) * kdim + 64 * ck);
+#pragma unroll
+    for (int i = 0; i < NX; ++i) st.x[i] = ld16<false>(hb + s.xo[i] + 64 * ck);
+  };
+  auto stage = [&](const Stage& st, uint16_t* buf) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) *reinterpret_cast<u32x4*>(wl + (8 * i + sub) * TS + 8 * part) = st.w[i];
+#pragma unroll
+    for (int i = 0; i < NX; ++i) *reinterpret_cast<u32x4*>(buf + (32 * i + 8 * wave + sub) * TS + 8 * part) = st.x[i];
+  };
+  f32x16 acc[2][MF_TT<BN>];
+  auto multiply = [&](const uint16_t* buf) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 av[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) av[b] = *reinterpret_cast<const u32x4*>(wl + (32 * b + c) * TS + 32 * h + 8 * s);
+#pragma unroll
+      for (int tt = 0; tt < MF_TT<BN>; ++tt) {
+        const u32x4 bv = *reinterpret_cast<const u32x4*>(buf + (32 * tt + c) * TS + 32 * h + 8 * s);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[b][tt] = mfma32<FMT_BF16>(av[b], bv, acc[b][tt]);
+      }
+    }
+  };
+  int idx = i0;
+  if (idx >= n) return;
+  Src cur = prep(load_item(idx), idx);
+  Stage st[2];
+  fetch(st[0], cur, 0);
+  for (;;) {
+    const int nidx = idx + stride;
+    const bool more = nidx < n;
+    // the next item's entry, read now and used at the last chunk
+    const Item nraw = load_item(more ? nidx : idx);
+#pragma unroll
+    for (int tt = 0; tt < MF_TT<BN>; ++tt) acc[0][tt] = acc[1][tt] = f32x16{};
+    Src nxt = cur;
+#pragma unroll 1
+    for (int ck0 = 0; ck0 < NC; ck0 += 2) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int ck = ck0 + j;
+        __builtin_amdgcn_sched_barrier(0);
+        stage(st[j], sm.x[j]);
+        if (ck + 1 < NC) {
+          fetch(st[j ^ 1], cur, ck + 1);
+        } else {
+          // past the sequence's last item its last chunk is loaded again (exact wait counts)
+          if (more) nxt = prep(nraw, nidx);
+          fetch(st[j ^ 1], nxt, more ? 0 : NC - 1);
+        }
+        __syncthreads();
+        multiply(sm.x[j]);
+      }
+    }
+    // y rows: acc[b][tt][4 i + j] = row 64 wave + 32 b + 8 i + 4 h + j, token 32 tt + c
+#pragma unroll
+    for (int tt = 0; tt < MF_TT<BN>; ++tt) {
+      const int col = 32 * tt + c;
+      if (col >= cur.cnt) continue;
+      const size_t yrow = (size_t)(cur.shared ? a.S + cur.p0 + col : cur.p0 + col);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = cur.r0 + 64 * wave + 32 * b + 8 * i + 4 * h;
+          uint2 pk;
+          pk.x = (uint32_t)f32_to_bf16(acc[b][tt][4 * i]) | ((uint32_t)f32_to_bf16(acc[b][tt][4 * i + 1]) << 16);
+          pk.y = (uint32_t)f32_to_bf16(acc[b][tt][4 * i + 2]) | ((uint32_t)f32_to_bf16(acc[b][tt][4 * i + 3]) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.y) + yrow * D_MODEL + r) = pk;
+        }
+      }
+    }
+    if (!more) break;
+    idx = nidx;
+    cur = nxt;
+  }
+  __syncthreads();  // the LDS is taken over by the vector path
+}
+
 // ======================================================================================
 // Persistent kernels
 // ======================================================================================
@@ -1692,7 +1823,10 @@ template <int FMT, int BN, int VDR>
 __global__ __launch_bounds__(256, (FFN_WG_PER_CU<FMT, BN>)) void ffn_down_kernel(LayerArgs a) {
   __shared__ FfnKernelSmem<FMT, BN> sm;
   const int n_all = a.ctl[CTL_N_DN], n_mf = a.ctl[CTL_N_DN_MF];
-  if constexpr (BN > 0) {
+  if constexpr (BN > 0 && FMT == FMT_BF16) {
+    const int G = mf_grid(n_mf, gridDim.x);
+    if ((int)blockIdx.x < G) mfma_down_bf16_seq<BN>(a, blockIdx.x, G, n_mf, sm.mf);
+  } else if constexpr (BN > 0) {
     const int G = mf_grid(n_mf, gridDim.x);
     for (int i = blockIdx.x; i < n_mf && (int)blockIdx.x < G; i += G) {
       const Item item = fetch_item(a.tiles, mf_item(i, n_mf, N_DN_CHUNKS), N_DN_CHUNKS);
