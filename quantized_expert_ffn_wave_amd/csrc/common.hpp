@@ -119,7 +119,8 @@ struct LayerArgs {
   Item* tiles;              // work list: one entry per token tile (row chunk 0)
   int32_t* ctl;             // [CTL_WORDS]
   void* h;                  // [S + n_shared*T][D_FF] SwiGLU output: fp32 for the 4-bit formats, bf16 bits else
-  void* y;                  // [S + n_shared*T][D_MODEL] expert outputs: fp32 for the 4-bit formats, bf16 bits
+  void* y;                  // [S + n_shared*T][D_MODEL] expert outputs, row t K + j for slot j of token t
+                            // (S + t for the shared expert): fp32 for the 4-bit formats, bf16 bits
                             // for bf16 weights (whose layer output is bf16 of a 7-term sum of them)
   // 4-bit formats only (their products run on fp16 operands): the power-of-two
   // scale of each token's activations, and per expert-output row the largest

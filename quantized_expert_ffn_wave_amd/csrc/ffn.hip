@@ -804,6 +804,13 @@ __device__ void down_stream(const LayerArgs& a, int base, int n, int n_mf, MvSme
   // after a reduction over two row groups, lanes with bit 2 clear hold row
   // group (2 p + bit 5)'s sum for token 2 * bit 4 + bit 3
   const int my_t = ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
+  // the lane's y row: token my_t's slot (from perm), or S + token (shared);
+  // the next item's is read just before the ring's first load of that item,
+  // so that waiting for it waits for no load of the next item
+  auto y_row = [&](const ItemTok& x) {
+    return x.shared ? a.S + x.p0 + my_t : a.perm[x.p0 + min(my_t, x.cnt - 1)];
+  };
+  int yrow = y_row(it);
 #pragma unroll 1
   for (;;) {
     const int nc = order.next(c);
@@ -812,6 +819,7 @@ __device__ void down_stream(const LayerArgs& a, int base, int n, int n_mf, MvSme
     ItemTok nit = it;
     ChunkW nw = w;
     size_t nr0 = r0;
+    int nyrow = yrow;
     MvStage st;
     if (has_next) {
       nitem = fetch_item(a.tiles, base + nc, CH);
@@ -823,7 +831,7 @@ __device__ void down_stream(const LayerArgs& a, int base, int n, int n_mf, MvSme
     const bool writer = (lane & 4) == 0 && my_t < it.cnt;
     const float isc = OPER_F16<FMT> ? sm.isc[buf][my_t] : 1.f;  // undoes the row's h scale
     // the lane's y elements, as a 32-bit offset from the uniform base
-    const uint32_t yoff = (uint32_t)((row_of(a, it, 0) + my_t) * D_MODEL + item_chunk(item.head) * VDR +
+    const uint32_t yoff = (uint32_t)(yrow * D_MODEL + item_chunk(item.head) * VDR +
                                      wave * (VDR / 4) + 4 * ((lane >> 5) & 1) + j);
     uint32_t xq[16];
     f32x4 negK = {}, S = {};
@@ -832,8 +840,12 @@ __device__ void down_stream(const LayerArgs& a, int base, int n, int n_mf, MvSme
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const typename G::Raw cur = ring[u % D];
-      if (u + D < NU) ring[u % D] = load_unit(w, r0, u + D);
-      else if (has_next) ring[u % D] = load_unit(nw, nr0, u + D - NU);
+      if (u + D < NU) {
+        ring[u % D] = load_unit(w, r0, u + D);
+      } else if (has_next) {
+        if (u + D == NU) nyrow = y_row(nit);
+        ring[u % D] = load_unit(nw, nr0, u + D - NU);
+      }
       acc[u & 1] = f32x4{0.f, 0.f, 0.f, 0.f};
       MV<FMT>::unit(cur, xq, negK, S, acc[u & 1]);
       if (u & 1) {
@@ -852,6 +864,7 @@ __device__ void down_stream(const LayerArgs& a, int base, int n, int n_mf, MvSme
     it = nit;
     w = nw;
     r0 = nr0;
+    yrow = nyrow;
   }
 }
 
@@ -900,7 +913,8 @@ template <int FMT, int BN> struct FfnSmem {
   uint16_t x[2][BN * TS];  // K-chunks alternate between the two, so one barrier per chunk suffices
   uint16_t w[4][MF_WL_ROWS<FMT> * TS];  // bf16 weights: each wave's rows of the current K-chunk
   int tok[BN];
-  int row[BN];
+  int row[BN];             // h rows (bucket positions; shared: S + token)
+  int yrow[BN];            // y rows (slots t K + j; shared: S + token)
   float sc[BN];            // 4-bit formats: activation scale per token column (down: from |h|)
   float isc[BN];           // and its inverse
   float hred[4][BN];       // gate/up, 4-bit formats: each wave's largest |h| per token column
@@ -940,10 +954,12 @@ __device__ inline void mfma_tables(const LayerArgs& a, const ItemTok& it, FfnSme
   const int i = threadIdx.x;
   if (i < BN) {
     // matrix-core tiles are shared-expert tiles or routed buckets (tokens via perm)
-    const int tok = (i < it.cnt) ? (it.shared ? it.p0 + i : a.perm[it.p0 + i] / a.K) : -1;
+    const int slot = (i < it.cnt && !it.shared) ? a.perm[it.p0 + i] : 0;
+    const int tok = (i < it.cnt) ? (it.shared ? it.p0 + i : slot / a.K) : -1;
     const int row = (i < it.cnt) ? row_of(a, it, i) : -1;
     sm.tok[i] = tok;
     sm.row[i] = row;
+    sm.yrow[i] = (i < it.cnt) ? (it.shared ? row : slot) : -1;
     if (UP && OPER_F16<FMT>) {
       const float sc = (i < it.cnt) ? a.xsc[tok] : 1.f;
       sm.sc[i] = sc;
@@ -1351,6 +1367,7 @@ __device__ inline void mf_down_q(const LayerArgs& a, const QMat& D, int mat, con
   constexpr int P = 256 / BN, NSH = HSLOTS / P;
   static_assert(P == 4 && NSH % 4 == 0, "4 threads per token column: two DPP exchanges");
   const int col = tid / P, pt = tid % P;
+  const int yslot = (tid < it.cnt && !it.shared) ? a.perm[it.p0 + tid] : 0;  // y row of token column tid
   u32x4 hv[NSH / 4];
   {
     const u32x4* src = reinterpret_cast<const u32x4*>(a.hslot + (size_t)row_of(a, it, min(col, it.cnt - 1)) * HSLOTS +
@@ -1379,7 +1396,10 @@ __device__ inline void mf_down_q(const LayerArgs& a, const QMat& D, int mat, con
       sm.sc[col] = sc;
       sm.isc[col] = pow2_inv(sc);
     }
-    if (tid < BN) sm.row[tid] = (tid < it.cnt) ? row_of(a, it, tid) : -1;
+    if (tid < BN) {
+      sm.row[tid] = (tid < it.cnt) ? row_of(a, it, tid) : -1;
+      sm.yrow[tid] = (tid < it.cnt) ? (it.shared ? row_of(a, it, tid) : yslot) : -1;
+    }
   }
   __syncthreads();
 #pragma unroll
@@ -1590,7 +1610,7 @@ __device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const Item
   const float tsd = (FMT == FMT_NVFP4) ? D.ts[mat] : 1.f;
 #pragma unroll
   for (int tt = 0; tt < MF_TT<BN>; ++tt) {
-    const int yrow = sm.row[32 * tt + c];
+    const int yrow = sm.yrow[32 * tt + c];
     if (yrow < 0) continue;
     const float ts = OPER_F16<FMT> ? tsd * sm.isc[32 * tt + c] : tsd;
 #pragma unroll
@@ -1620,8 +1640,8 @@ __device__ void mfma_down(const LayerArgs& a, const QMat& D, int mat, const Item
 // its loads are in flight during the last chunk's products and the y stores
 // instead of after them (an item has only 8 K-chunks, and the first one's
 // latency, paid once per item, was about a tenth of it).  No tables: an item's
-// h rows are its bucket positions (routed) or tokens (shared), contiguous,
-// and they are its y rows too.  Same loads, LDS layout and products in the
+// h rows are its bucket positions (routed) or S + its tokens (shared),
+// contiguous, and its y rows are read from perm with the item.  Same loads, LDS layout and products in the
 // same order as mfma_down through mf_kloop_bf16.
 __device__ inline int mf_item(int i, int n, int C);
 template <int BN>
@@ -1637,7 +1657,8 @@ __device__ void mfma_down_bf16_seq(const LayerArgs& a, int i0, int stride, int n
   struct Src {
     const uint16_t* wp;  // the lane's first weight row piece of the wave's 64 rows
     uint32_t xo[NX];     // the thread's h row offsets (elements)
-    int mat, r0, p0, cnt, shared;
+    int yr[MF_TT<BN>];   // the lane's y rows (token columns 32 tt + c; -1 past the count)
+    int mat, r0;
   };
   // item idx of the sequence is entry mf_item(idx) of the list (row chunk mf_item(idx) % N_DN_CHUNKS)
   auto prep = [&](const Item& raw, int idx) {
@@ -1647,11 +1668,13 @@ __device__ void mfma_down_bf16_seq(const LayerArgs& a, int i0, int stride, int n
     item.p0 = __builtin_amdgcn_readfirstlane(item.p0);
     const ItemTok it = item_tokens(item);
     Src s;
-    s.shared = it.shared;
     s.mat = it.shared ? 0 : item_expert(item.head);
     s.r0 = item_chunk(item.head) * DN_ROWS;
-    s.p0 = it.p0;
-    s.cnt = it.cnt;
+#pragma unroll
+    for (int tt = 0; tt < MF_TT<BN>; ++tt) {
+      const int col = 32 * tt + c;
+      s.yr[tt] = col >= it.cnt ? -1 : it.shared ? a.S + it.p0 + col : a.perm[it.p0 + col];
+    }
     const uint16_t* codes = reinterpret_cast<const uint16_t*>(it.shared ? a.sh_down.codes : a.down.codes);
     s.wp = codes + ((size_t)s.mat * D_MODEL + s.r0 + 64 * wave + sub) * kdim + 8 * part;
 #pragma unroll
@@ -1721,12 +1744,11 @@ __device__ void mfma_down_bf16_seq(const LayerArgs& a, int i0, int stride, int n
         multiply(sm.x[j]);
       }
     }
-    // y rows: acc[b][tt][4 i + j] = row 64 wave + 32 b + 8 i + 4 h + j, token 32 tt + c
+    // y: acc[b][tt][4 i + j] = output row 64 wave + 32 b + 8 i + 4 h + j, token column 32 tt + c
 #pragma unroll
     for (int tt = 0; tt < MF_TT<BN>; ++tt) {
-      const int col = 32 * tt + c;
-      if (col >= cur.cnt) continue;
-      const size_t yrow = (size_t)(cur.shared ? a.S + cur.p0 + col : cur.p0 + col);
+      if (cur.yr[tt] < 0) continue;
+      const size_t yrow = (size_t)cur.yr[tt];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
 #pragma unroll
@@ -1932,17 +1954,14 @@ __device__ inline void rmsnorm_store(const float* v, uint16_t* dst, float eps) {
 __device__ inline void combine_token(const LayerArgs& a, int t) {
   const int K = a.K;
   const int i0 = 8 * threadIdx.x;
-  // every load is issued before the first sum: the slots' rows, then the rows
+  // every load is issued before the first sum: the weights and the rows (y
+  // rows are slots, t K + j, so that no lookup of bucket positions comes first)
   int pos[MAX_K];
   float wj[MAX_K];
 #pragma unroll
   for (int j = 0; j < MAX_K; ++j) {
-    pos[j] = 0;
-    wj[j] = 0.f;
-    if (j < K) {
-      pos[j] = a.inv_perm[(size_t)t * K + j];
-      wj[j] = a.w[(size_t)t * K + j];
-    }
+    pos[j] = t * K + j;
+    wj[j] = (j < K) ? a.w[(size_t)t * K + j] : 0.f;
   }
   // (fp32 rows, or bf16 rows for bf16 weights: the branch is uniform)
   const bool ybf = a.fmt == FMT_BF16;
