@@ -277,8 +277,9 @@ template <int M> __device__ inline float halve_step(float a, float b) {
   }
 }
 // Tokens of an item: bucket positions p0 .. p0+cnt-1 of a routed expert
-// (expert-output row p), or tokens p0 .. p0+cnt-1 of the shared expert
-// (expert-output row S + t).  Vector-path items carry their token ids.
+// (expert-output row p: the row of h and of its |h| slots; y is written at the
+// position's slot perm[p] instead), or tokens p0 .. p0+cnt-1 of the shared
+// expert (row S + t of h and of y).  Vector-path items carry their token ids.
 struct ItemTok {
   int p0, cnt;
   bool shared, mfma;
