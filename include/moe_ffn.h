@@ -18,16 +18,18 @@
  *   E_e(x) = Wd_e (silu(Wg_e x) * (Wu_e x))  (SwiGLU, silu(g) = g/(1+e^-g))
  *   y      = sum_j w_j E_{ids_j}(x) + shared_scale * E_shared(x)   -> bf16
  *
- * Arithmetic: router logits accumulate in fp32 from bf16 operands; the SwiGLU
- * output h is rounded to bf16 between the two expert products; expert outputs
- * are summed in fp32 in the order j = 0..k-1, then the shared expert, and the
- * result is rounded once to bf16.  With 4-bit weights both expert products run
- * on fp16 operands (every q4_1 weight d*q + m rounded once to fp16, every
- * NVFP4 E2M1 x E4M3 product exact in fp16, the tensor scale applied in fp32),
- * and each token's activations (x, and h per expert-output row) enter them
- * multiplied by a power of two that puts the row's largest magnitude in
- * [2^14, 2^15), undone in fp32 afterwards: the size of a token row is then
- * limited only by fp32, not by fp16's range.
+ * Arithmetic: router logits accumulate in fp32 from bf16 operands; expert
+ * outputs are summed in fp32 in the order j = 0..k-1, then the shared expert,
+ * and the result is rounded once to bf16.  With bf16 weights both expert
+ * products run on bf16 operands, the SwiGLU output h is rounded to bf16
+ * between them, and each expert output is rounded to bf16 (RNE) before the
+ * sum.  With 4-bit weights both expert products run on fp16 operands (every
+ * q4_1 weight d*q + m rounded once to fp16, every NVFP4 E2M1 x E4M3 product
+ * exact in fp16, the tensor scale applied in fp32), h and the expert outputs
+ * stay fp32, and each token's activations (x, and h per expert-output row)
+ * enter the products multiplied by a power of two that puts the row's largest
+ * magnitude in [2^14, 2^15), undone in fp32 afterwards: the size of a token
+ * row is then limited only by fp32, not by fp16's range.
  * Supported inputs: finite x (NaN and infinity are outside the contract);
  * finite weights with every q4_1 block satisfying |d*q + m| <= 65504 for
  * q = 0..15; results whose intermediate values (logits, gate/up products, h,
