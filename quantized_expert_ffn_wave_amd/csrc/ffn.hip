@@ -1769,6 +1769,150 @@ __device__ void mfma_down_bf16_seq(const LayerArgs& a, int i0, int stride, int n
   __syncthreads();  // the LDS is taken over by the vector path
 }
 
+// bf16 gate/up items of 128-token tiles, one workgroup's sequence idx = i0,
+// i0 + stride, ... < n, as one K-loop (as mfma_down_bf16_seq): the next item's
+// entry is read when an item starts, its token ids (from perm) halfway through
+// its chunks, and its first chunk is loaded during the last chunk's products and
+// the SwiGLU stores, instead of a table round trip and a pipeline fill per item.
+// No LDS tables: the h rows of an item's token columns are its bucket positions
+// (or S + token).  Same loads, LDS layout and products in the same order as
+// mfma_up through mf_kloop_bf16.
+template <int BN>
+__device__ void mfma_up_bf16_seq(const LayerArgs& a, int i0, int stride, int n, FfnSmem<FMT_BF16, BN>& sm) {
+  static_assert(BN == 128 && MF_UP_RB<BN> == 2 && MF_NS_UP<FMT_BF16, BN> == 2, "2 row blocks, 2 stages");
+  constexpr int UC = mf_up_chunks(BN);  // items per tile (128 row pairs each)
+  constexpr int NX = BN / 32;           // x loads per thread and chunk: tokens 32 i + 8 wave + lane / 8
+  constexpr int kdim = D_MODEL, NC = kdim / 64;
+  static_assert(NC % 2 == 0, "chunk j in LDS buffer j % 2");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, c = lane & 31, sub = lane >> 3, part = lane & 7;
+  uint16_t* wl = sm.w[wave];
+  struct Cur {
+    int p0, cnt, shared, n0;
+    size_t wrow;  // the wave's first gate (and up) row in its matrix
+  };
+  auto decode_item = [&](const Item& raw, int idx) {
+    const int m = mf_item(idx, n, UC);
+    Cur r;
+    const uint32_t head = __builtin_amdgcn_readfirstlane(raw.head);
+    r.p0 = (int)__builtin_amdgcn_readfirstlane(raw.p0);
+    r.cnt = item_count(head);
+    r.shared = item_shared(head);
+    r.n0 = (m % UC) * (D_FF / UC);
+    r.wrow = (size_t)(r.shared ? 0 : item_expert(head)) * D_FF + r.n0 + 32 * wave;
+    return r;
+  };
+  auto load_item = [&](int idx) { return a.tiles[mf_item(idx, n, UC) / UC]; };
+  // the thread's token of x load i, clamped into the item's count
+  auto tok_slot = [&](const Cur& r, int i) { return min(32 * i + 8 * wave + sub, r.cnt - 1); };
+  struct Stage {
+    u32x4 w[8];
+    u32x4 x[NX];
+  };
+  auto fetch = [&](Stage& st, const Cur& r, const uint32_t (&xo)[NX], int ck) {
+    const uint16_t* wg = reinterpret_cast<const uint16_t*>(r.shared ? a.sh_gate.codes : a.gate.codes);
+    const uint16_t* wu = reinterpret_cast<const uint16_t*>(r.shared ? a.sh_up.codes : a.up.codes);
+    const size_t off = (r.wrow + sub) * kdim + 8 * part + 64 * ck;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.w[i] = ld16<true>(wg + off + (size_t)(8 * i) * kdim);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.w[4 + i] = ld16<true>(wu + off + (size_t)(8 * i) * kdim);
+#pragma unroll
+    for (int i = 0; i < NX; ++i) st.x[i] = ld16<false>(a.x + xo[i] + 64 * ck);
+  };
+  auto stage = [&](const Stage& st, uint16_t* buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(wl + (8 * i + sub) * TS + 8 * part) = st.w[i];
+#pragma unroll
+    for (int i = 0; i < NX; ++i) *reinterpret_cast<u32x4*>(buf + (32 * i + 8 * wave + sub) * TS + 8 * part) = st.x[i];
+  };
+  f32x16 acc[2][MF_TT<BN>];
+  auto multiply = [&](const uint16_t* buf) {
+#pragma unroll
+    for (int s_ = 0; s_ < 4; ++s_) {
+      u32x4 av[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) av[b] = *reinterpret_cast<const u32x4*>(wl + (32 * b + c) * TS + 32 * h + 8 * s_);
+#pragma unroll
+      for (int tt = 0; tt < MF_TT<BN>; ++tt) {
+        const u32x4 bv = *reinterpret_cast<const u32x4*>(buf + (32 * tt + c) * TS + 32 * h + 8 * s_);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[b][tt] = mfma32<FMT_BF16>(av[b], bv, acc[b][tt]);
+      }
+    }
+  };
+  int idx = i0;
+  if (idx >= n) return;
+  Cur cur = decode_item(load_item(idx), idx);
+  uint32_t xo[NX];
+#pragma unroll
+  for (int i = 0; i < NX; ++i) {
+    const int j = tok_slot(cur, i);
+    xo[i] = (uint32_t)(cur.shared ? cur.p0 + j : a.perm[cur.p0 + j] / a.K) * (uint32_t)kdim + 8u * part;
+  }
+  Stage st[2];
+  fetch(st[0], cur, xo, 0);
+  for (;;) {
+    const int nidx = idx + stride;
+    const bool more = nidx < n;
+    const Item nraw = load_item(more ? nidx : idx);  // used halfway through
+    Cur nxt = cur;
+    int pv[NX];
+#pragma unroll
+    for (int tt = 0; tt < MF_TT<BN>; ++tt) acc[0][tt] = acc[1][tt] = f32x16{};
+#pragma unroll 1
+    for (int ck0 = 0; ck0 < NC; ck0 += 2) {
+      if (ck0 == NC / 2) {
+        // the next item's tokens, read half an item ahead of their use
+        nxt = more ? decode_item(nraw, nidx) : cur;
+#pragma unroll
+        for (int i = 0; i < NX; ++i) pv[i] = nxt.shared ? 0 : a.perm[nxt.p0 + tok_slot(nxt, i)];
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int ck = ck0 + j;
+        __builtin_amdgcn_sched_barrier(0);
+        stage(st[j], sm.x[j]);
+        if (ck + 1 < NC) {
+          fetch(st[j ^ 1], cur, xo, ck + 1);
+        } else {
+          // past the sequence's last item its last chunk is loaded again (exact wait counts)
+          if (more) {
+#pragma unroll
+            for (int i = 0; i < NX; ++i)
+              xo[i] = (uint32_t)(nxt.shared ? nxt.p0 + tok_slot(nxt, i) : pv[i] / a.K) * (uint32_t)kdim + 8u * part;
+          }
+          fetch(st[j ^ 1], more ? nxt : cur, xo, more ? 0 : NC - 1);
+        }
+        __syncthreads();
+        multiply(sm.x[j]);
+      }
+    }
+    // SwiGLU: acc[b][tt][4 i + j] = row pair n0 + 32 wave + 8 i + 4 h + j (b = 0 gate, 1 up), token column 32 tt + c
+#pragma unroll
+    for (int tt = 0; tt < MF_TT<BN>; ++tt) {
+      const int col = 32 * tt + c;
+      if (col >= cur.cnt) continue;
+      const size_t hrow = (size_t)(cur.shared ? a.S + cur.p0 + col : cur.p0 + col);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float hf[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hf[e] = silu_mul(acc[0][tt][4 * i + e], acc[1][tt][4 * i + e]);
+        const int nn = cur.n0 + 32 * wave + 8 * i + 4 * h;
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(hf[0]) | ((uint32_t)f32_to_bf16(hf[1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16(hf[2]) | ((uint32_t)f32_to_bf16(hf[3]) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.h) + hrow * D_FF + nn) = pk;
+      }
+    }
+    if (!more) break;
+    idx = nidx;
+    cur = nxt;
+  }
+  __syncthreads();  // the LDS is taken over by the vector path
+}
+
 // ======================================================================================
 // Persistent kernels
 // ======================================================================================
@@ -1831,7 +1975,9 @@ __global__ __launch_bounds__(256, (FFN_WG_PER_CU<FMT, BN>)) void ffn_up_kernel(L
   const int n_all = a.ctl[CTL_N_UP], n_mf = a.ctl[CTL_N_UP_MF];
   constexpr int UC = (BN > 0) ? mf_up_chunks(BN) : 1;
   const int base = (n_mf / UC) * (D_FF / VR);
-  if constexpr (BN > 0) {
+  if constexpr (BN == 128 && FMT == FMT_BF16) {
+    mfma_up_bf16_seq<BN>(a, blockIdx.x, gridDim.x, n_mf, sm.mf);
+  } else if constexpr (BN > 0) {
     for (int i = blockIdx.x; i < n_mf; i += gridDim.x) {
       const Item item = fetch_item(a.tiles, mf_item(i, n_mf, UC), UC);
       const bool sh = item_shared(item.head);
